@@ -1,0 +1,18 @@
+"""CPU oracle of the batch-1 MLA + MoE decode step (float64, numpy).
+
+TEST INFRASTRUCTURE ONLY. This package is the independent reference that the
+HIP engine is checked against. Only the tests, the smoke check of the package
+entry point and the benchmark's CPU-baseline leg may import or run it; the
+engine's own code path never does, and the oracle shares no code with the
+engine (the seeded input generators under `synth` are the only common part).
+
+Every function states the passage of the TileRT pages it follows, or the
+reading chosen where the pages are silent. Parity pins (tests under tests/
+marked "not gpu") tie each function to closed forms, library routines,
+brute force or invariants. No function here is "parity unpinned".
+"""
+from . import numerics, model  # noqa: F401
+from .numerics import E4M3, bf16_round, bf16_bits_to_f64, dequant_fp8, e4m3_decode  # noqa: F401
+from .model import (OracleWeights, DecodeState, decode_step, forward_full, prefill,  # noqa: F401
+                    rmsnorm, rope, softmax, route, topk_indices, mla_absorbed, mla_naive,
+                    split_wkv_b)

@@ -1,0 +1,71 @@
+"""Number formats of the decode step, written out from their definitions.
+
+TEST INFRASTRUCTURE (see the package docstring): only tests, the smoke check
+and the benchmark's CPU-baseline leg may import this module.
+
+* OCP FP8 E4M3 ("e4m3fn"): 1 sign bit, 4 exponent bits with bias 7, 3 mantissa
+  bits; exponent field 0 encodes subnormals m/8 * 2^-6; codes 0x7F and 0xFF are
+  NaN; there is no infinity, so the largest finite magnitude is 1.75 * 2^8 = 448.
+  The TileRT pages name FP8 as the precision of their results (SemiAnalysis
+  "Ultra-High Interactivity on NVIDIA GPUs? - TileRT InferenceX", results
+  section) without fixing the variant; the OCP variant is the one with hardware
+  conversions on the target GPU.
+* bfloat16: the upper 16 bits of an IEEE binary32 value; rounding to it is
+  round-to-nearest, ties to even, on an 8-bit significand.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+BLOCK = 128
+
+
+def _e4m3_table() -> np.ndarray:
+    t = np.empty(256, dtype=np.float64)
+    for code in range(256):
+        sign = -1.0 if code & 0x80 else 1.0
+        exp = (code >> 3) & 0xF
+        man = code & 0x7
+        if exp == 0xF and man == 0x7:
+            t[code] = np.nan
+        elif exp == 0:
+            t[code] = sign * (man / 8.0) * 2.0 ** -6
+        else:
+            t[code] = sign * (1.0 + man / 8.0) * 2.0 ** (exp - 7)
+    return t
+
+
+E4M3 = _e4m3_table()
+
+
+def e4m3_decode(codes: np.ndarray) -> np.ndarray:
+    """Values of e4m3 codes (uint8 array) as float64."""
+    return E4M3[np.asarray(codes, dtype=np.uint8)]
+
+
+def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns (uint16) to their exact float64 values."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16
+    return b.view(np.float32).astype(np.float64)
+
+
+def bf16_round(x: np.ndarray) -> np.ndarray:
+    """Round float64 values to the nearest bfloat16 value (ties to even).
+
+    x = m * 2^e with 0.5 <= |m| < 1; a bf16 normal number keeps 8 significant
+    bits, so m * 2^8 is rounded to an integer (half to even) and scaled back.
+    Values below the bf16 normal range keep the subnormal spacing 2^-133.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    m, e = np.frexp(x)
+    e = np.maximum(e, -125)          # smallest normal bf16 is 2^-126 = 0.5 * 2^-125
+    q = np.rint(np.ldexp(x, 8 - e))  # np.rint rounds half to even
+    return np.ldexp(q, e - 8)
+
+
+def dequant_fp8(codes: np.ndarray, scale_bits: np.ndarray) -> np.ndarray:
+    """W[i, j] = e4m3(code[i, j]) * scale[i // 128, j // 128] in float64."""
+    n, k = codes.shape
+    s = bf16_bits_to_f64(scale_bits)
+    s_full = np.repeat(np.repeat(s, BLOCK, axis=0)[:n], BLOCK, axis=1)[:, :k]
+    return e4m3_decode(codes) * s_full
