@@ -1,0 +1,1273 @@
+// Persistent decode engine kernel for gfx950.
+//
+// One launch runs one batch-1 decode step of the MLA + MoE stack. The grid is
+// one 512-thread workgroup per compute unit; every workgroup walks the same
+// ordered stage list (the plan) and takes a fixed share of each stage. Stages
+// are ordered by striped arrival counters in device memory: a workgroup
+// finishing a stage bumps one counter, a workgroup starting a stage that reads
+// another stage's output spins until that stage's counters reach epoch * count.
+// This replaces kernel boundaries between operators, the central idea of the
+// TileRT engine kernel (SemiAnalysis, "Ultra-High Interactivity on NVIDIA
+// GPUs? - TileRT InferenceX", how-it-works section: one persistent kernel,
+// operators as tile tasks, no per-operator launch or teardown).
+//
+// Cross-workgroup data (activations, the new cache row, counters) moves only
+// through agent-coherent loads and stores (sc1: they bypass the per-XCD L2s'
+// non-coherent copies), so no L2 writeback or invalidate is needed per stage.
+// Weights and older cache rows are immutable during a launch and use ordinary
+// cached loads.
+//
+// GEMV stages (every weight product at batch 1 is a matrix-vector product)
+// stream FP8 e4m3 weights with 16-byte loads per lane, convert them in
+// registers with the hardware OCP-FP8 conversion, multiply by fp32
+// activations staged in LDS and reduce with DPP cross-lane adds. M = 1 is not
+// a dense contraction, so MFMA is not used there.
+#include <hip/hip_runtime.h>
+
+#include "pdm_internal.h"
+#include "engine.h"
+
+namespace pdm {
+namespace {
+
+constexpr int kUnroll = 8;  // 1 KB units in flight per wave and buffer
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+struct __align__(16) Smem {
+  float x[kXMax];                 // staged input vector(s) of the current stage
+  float part[kWaves][kRowChunk];  // per-wave row partial sums
+  const uint8_t* slot_codes[kMaxSlots];
+  const uint16_t* slot_scales[kMaxSlots];
+  float slot_w[kMaxSlots];
+  int slot_act[kMaxSlots];        // act offset of each slot
+  int route_idx[kMaxSlots];       // top-k experts of the current MoE layer
+  float route_w[kMaxSlots];       // their normalised weights
+  float red[2 * kWaves];
+  int ired[2 * kWaves];
+  uint64_t t_enter, t_ready;
+  int abort;
+};
+
+// ------------------------------------------------------------------ helpers
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+
+__device__ __forceinline__ float ld_coh(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int ld_coh_i(const int* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t ld_coh_u(const uint32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_coh(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_coh_i(int* p, int v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_coh_u(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Wait until every memory operation this thread issued has completed.
+__device__ __forceinline__ void mem_done() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
+__device__ __forceinline__ float bf16_val(uint16_t b) { return __builtin_bit_cast(float, (uint32_t)b << 16); }
+
+// Round an fp32 value to the nearest bf16 value (ties to even), kept in fp32.
+__device__ __forceinline__ float round_bf16(float v) {
+  uint32_t u = __builtin_bit_cast(uint32_t, v);
+  u = (u + 0x7fffu + ((u >> 16) & 1u)) & 0xffff0000u;
+  return __builtin_bit_cast(float, u);
+}
+__device__ __forceinline__ uint16_t bf16_bits(float v) {
+  return (uint16_t)(__builtin_bit_cast(uint32_t, round_bf16(v)) >> 16);
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+// xor 1, xor 2 (quad_perm), then mirror within 8 and within 16 lanes
+constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140;
+
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp<kDppXor1>(v);
+  v += dpp<kDppXor2>(v);
+  v += dpp<kDppHalfMirror>(v);
+  v += dpp<kDppMirror>(v);
+  return v;
+}
+// sum over the 64 lanes, returned uniform
+__device__ __forceinline__ float wave_sum(float v) {
+  v = row16_sum(v);
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0)) +
+         __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 16)) +
+         __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32)) +
+         __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 48));
+}
+__device__ __forceinline__ float wave_max(float v) {
+  v = fmaxf(v, dpp<kDppXor1>(v));
+  v = fmaxf(v, dpp<kDppXor2>(v));
+  v = fmaxf(v, dpp<kDppHalfMirror>(v));
+  v = fmaxf(v, dpp<kDppMirror>(v));
+  float a = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
+  float b = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 16));
+  float c = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
+  float d = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 48));
+  return fmaxf(fmaxf(a, b), fmaxf(c, d));
+}
+// sum within aligned groups of `gs` lanes (gs a power of two <= 64); every lane gets its group sum
+__device__ __forceinline__ float group_sum(float v, int gs) {
+  if (gs >= 2) v += dpp<kDppXor1>(v);
+  if (gs >= 4) v += dpp<kDppXor2>(v);
+  if (gs >= 8) v += dpp<kDppHalfMirror>(v);
+  if (gs >= 16) v += dpp<kDppMirror>(v);
+  if (gs >= 32) v += __shfl_xor(v, 16);
+  if (gs >= 64) v += __shfl_xor(v, 32);
+  return v;
+}
+
+// block-wide sum (all 512 threads participate); result in every thread
+__device__ float block_sum(Smem& sm, float v) {
+  float w = wave_sum(v);
+  if (lane_id() == 0) sm.red[wave_id()] = w;
+  __syncthreads();
+  float t = 0.f;
+#pragma unroll
+  for (int i = 0; i < kWaves; ++i) t += sm.red[i];
+  __syncthreads();
+  return t;
+}
+
+__device__ __forceinline__ float silu(float g) { return g / (1.0f + __expf(-g)); }
+
+// ------------------------------------------------------------------ sync
+
+struct Ctx {
+  const Plan* P;
+  LaunchArgs A;
+  int G;
+  int wg;
+};
+
+__device__ __forceinline__ int* counter_ptr(const Ctx& c, int stage, int stripe) {
+  return reinterpret_cast<int*>(c.P->counters) + ((size_t)stage * kStripes + stripe) * kCounterStride;
+}
+__device__ __forceinline__ int stripe_count(int G, int stripe) { return (G - stripe + kStripes - 1) / kStripes; }
+
+__device__ void set_watchdog(const Ctx& c, int stage, int observed) {
+  unsigned long long* st = reinterpret_cast<unsigned long long*>(c.P->status);
+  unsigned long long mine = ((unsigned long long)c.A.epoch << 32) | (unsigned)(-PDM_ERR_WATCHDOG);
+  unsigned long long cur = __hip_atomic_load(st, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if ((uint32_t)(cur >> 32) != c.A.epoch || (uint32_t)cur == 0u) {
+    if (__hip_atomic_compare_exchange_strong(st, &cur, mine, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT)) {
+      int* det = reinterpret_cast<int*>(c.P->status) + 4;
+      st_coh_i(det + 0, stage);
+      st_coh_i(det + 1, c.wg);
+      st_coh_i(det + 2, observed);
+    }
+  }
+}
+
+// Wait until stage `s` is complete in every workgroup. Returns false when the
+// step was aborted (watchdog). All threads of the workgroup must call it.
+__device__ bool wait_stage(const Ctx& c, Smem& sm, int s, int my_stage) {
+  if (threadIdx.x == 0) {
+    sm.abort = 0;
+    if (c.A.trace) sm.t_enter = wall_clock64();
+  }
+  if (s >= 0 && threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    const int* ctr = counter_ptr(c, s, lane & (kStripes - 1));
+    const int target = (int)c.A.epoch * stripe_count(c.G, lane & (kStripes - 1));
+    const unsigned long long* st = reinterpret_cast<const unsigned long long*>(c.P->status);
+    const bool poll_ctr = lane < kStripes && lane < c.G;
+    int spins = 0;
+    while (true) {
+      bool ok = true;
+      int seen = 0;
+      if (poll_ctr) { seen = ld_coh_i(ctr); ok = seen >= target; }
+      bool abort = false;
+      if (lane == kStripes) {
+        unsigned long long v = __hip_atomic_load(st, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        abort = (uint32_t)(v >> 32) == c.A.epoch && (uint32_t)v != 0u;
+      }
+      if (__any(abort)) { if (lane == 0) sm.abort = 1; break; }
+      if (__all(ok)) break;
+      if (++spins > c.A.spin_limit) {
+        if (!ok) set_watchdog(c, my_stage, seen);
+        if (lane == 0) sm.abort = 1;
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x == 0 && c.A.trace) sm.t_ready = wall_clock64();
+  return sm.abort == 0;
+}
+
+__device__ void signal_stage(const Ctx& c, Smem& sm, int s) {
+  mem_done();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    if (!(s == c.A.skip_stage && c.wg == 0))
+      __hip_atomic_fetch_add(counter_ptr(c, s, c.wg & (kStripes - 1)), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (c.A.trace) {
+      uint64_t* t = reinterpret_cast<uint64_t*>(c.A.trace) + ((size_t)s * c.G + c.wg) * kTraceWords;
+      t[0] = sm.t_enter;
+      t[1] = sm.t_ready;
+      t[2] = wall_clock64();
+      t[3] = c.A.epoch;
+    }
+  }
+}
+
+// ------------------------------------------------------------------ GEMV core
+
+// Addressing of one GEMV stage. A "matrix" may be split into slots: row slots
+// (rows [j << lg, (j+1) << lg) come from slot j's matrix) or K slots (bytes
+// [j << lg, (j+1) << lg) of every row come from slot j's matrix).
+struct Gemv {
+  const uint8_t* codes;     // slot-less matrix
+  const uint16_t* scales;
+  int Kb;                   // bytes per logical row (all slots concatenated for K slots)
+  int nkb;                  // scale blocks per row of one (slot) matrix
+  int slot_mode;            // 0 none, 1 row slots, 2 K slots
+  int lg_slot;
+  int slot_Kb;              // bytes per row of one slot matrix
+  int lg_rpv;               // rows per input vector = 1 << lg_rpv (31: one shared vector)
+  int vbase;                // first staged vector
+  int xK;                   // floats per staged vector
+};
+
+// Address of the 16 bytes a lane reads for (row, byte offset b) and its scale.
+template <int EB>
+__device__ __forceinline__ void unit_ptr(const Gemv& g, const Smem& sm, int row, int b,
+                                         const uint8_t*& cp, const uint16_t*& sp) {
+  if (g.slot_mode == 0) {
+    cp = g.codes + (size_t)row * g.Kb + b;
+    if (EB == 1) sp = g.scales + (size_t)(row >> 3) * g.nkb + (b >> 7);
+  } else if (g.slot_mode == 1) {
+    int j = row >> g.lg_slot;
+    int rr = row & ((1 << g.lg_slot) - 1);
+    cp = sm.slot_codes[j] + (size_t)rr * g.slot_Kb + b;
+    if (EB == 1) sp = sm.slot_scales[j] + (size_t)(rr >> 3) * g.nkb + (b >> 7);
+  } else {
+    int j = b >> g.lg_slot;
+    int bb = b & ((1 << g.lg_slot) - 1);
+    cp = sm.slot_codes[j] + (size_t)row * g.slot_Kb + bb;
+    if (EB == 1) sp = sm.slot_scales[j] + (size_t)(row >> 3) * g.nkb + (bb >> 7);
+  }
+}
+
+// dot of one lane's 16 bytes with the staged input
+template <int EB>
+__device__ __forceinline__ float unit_dot(const u32x4& w, const float* xs) {
+  const float4* x4 = reinterpret_cast<const float4*>(xs);
+  float acc = 0.f;
+  if constexpr (EB == 1) {
+    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)ws[i], false);
+      auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)ws[i], true);
+      float4 xv = x4[i];
+      acc = fmaf(lo[0], xv.x, acc);
+      acc = fmaf(lo[1], xv.y, acc);
+      acc = fmaf(hi[0], xv.z, acc);
+      acc = fmaf(hi[1], xv.w, acc);
+    }
+  } else {
+    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      float4 xv = x4[i];
+      acc = fmaf(bf16_lo(ws[2 * i]), xv.x, acc);
+      acc = fmaf(bf16_hi(ws[2 * i]), xv.y, acc);
+      acc = fmaf(bf16_lo(ws[2 * i + 1]), xv.z, acc);
+      acc = fmaf(bf16_hi(ws[2 * i + 1]), xv.w, acc);
+    }
+  }
+  return acc;
+}
+
+// Runs the units of rows [ra, rb) of a GEMV (ra, rb multiples of the unit
+// row count) split over the 8 waves; writes per-wave row partials to
+// sm.part[w][row - ra]. `prep` is called once by every wave after its first
+// batch of weight loads has been issued and before any input is used; it
+// must contain a workgroup barrier (it waits on the dependency and stages the
+// input). Returns false if prep reported an abort.
+template <int EB, class Prep>
+__device__ bool gemv_rows(const Gemv& g, Smem& sm, int ra, int rb, bool call_prep, bool early, Prep&& prep) {
+  const int lane = lane_id();
+  const int w = wave_id();
+  const int kb = g.Kb;
+  const bool small = kb < 1024 && (1024 % kb) == 0;
+  // units
+  int S = 1, m = 1, lg_lpr = 0;
+  int nunits;
+  if (small) {
+    m = 1024 / kb;
+    lg_lpr = 31 - __builtin_clz(kb >> 4);
+    nunits = (rb - ra) / m;
+  } else {
+    S = (kb + 1023) >> 10;
+    nunits = (rb - ra) * S;
+  }
+  const int u0 = (int)((int64_t)nunits * w / kWaves);
+  const int u1 = (int)((int64_t)nunits * (w + 1) / kWaves);
+
+  u32x4 wa[kUnroll], wb[kUnroll];
+  float sa[kUnroll], sb[kUnroll];
+  int ra_row[kUnroll], rb_row[kUnroll], ra_b[kUnroll], rb_b[kUnroll];
+
+  auto issue = [&](u32x4* W, float* Sc, int* R, int* B, int ub) {
+#pragma unroll
+    for (int j = 0; j < kUnroll; ++j) {
+      int u = ub + j;
+      int row, b;
+      if (small) {
+        row = ra + u * m + (lane >> lg_lpr);
+        b = (lane & ((1 << lg_lpr) - 1)) << 4;
+      } else {
+        int r = u / S;
+        row = ra + r;
+        b = ((u - r * S) << 10) + (lane << 4);
+      }
+      R[j] = row;
+      B[j] = b;
+      bool ok = u < u1 && b < kb;
+      u32x4 v = {0u, 0u, 0u, 0u};
+      float sc = 0.f;
+      if (ok) {
+        const uint8_t* cp;
+        const uint16_t* sp = nullptr;
+        unit_ptr<EB>(g, sm, row, b, cp, sp);
+        v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(cp));
+        if constexpr (EB == 1) sc = bf16_val(*sp);
+      }
+      W[j] = v;
+      Sc[j] = sc;
+    }
+  };
+
+  int cur_row = -1;
+  float acc = 0.f;
+  auto flush = [&]() {
+    if (cur_row >= 0) {
+      float t = wave_sum(acc);
+      if (lane == 0) sm.part[w][cur_row - ra] = t;
+    }
+    acc = 0.f;
+  };
+  auto compute = [&](const u32x4* W, const float* Sc, const int* R, const int* B, int ub) {
+#pragma unroll
+    for (int j = 0; j < kUnroll; ++j) {
+      int u = ub + j;
+      if (u >= u1) break;
+      int row = R[j];
+      int b = B[j];
+      int k0 = (EB == 1) ? b : (b >> 1);
+      int xoff = (g.lg_rpv >= 31) ? 0 : ((row >> g.lg_rpv) - g.vbase) * g.xK;
+      float d = 0.f;
+      if (b < kb) d = unit_dot<EB>(W[j], sm.x + xoff + k0);
+      if constexpr (EB == 1) d *= Sc[j];
+      if (small) {
+        float t = group_sum(d, 1 << lg_lpr);
+        if ((lane & ((1 << lg_lpr) - 1)) == 0) sm.part[w][row - ra] = t;
+      } else {
+        int rowu = __builtin_amdgcn_readfirstlane(row);
+        if (rowu != cur_row) { flush(); cur_row = rowu; }
+        acc += d;
+      }
+    }
+  };
+
+  // Weight addresses that do not depend on this step's data are issued before
+  // the dependency wait, so the loads are in flight while the wait spins.
+  if (early) issue(wa, sa, ra_row, ra_b, u0);
+  if (call_prep) {
+    if (!prep()) return false;
+  }
+  if (!early) issue(wa, sa, ra_row, ra_b, u0);
+  for (int ub = u0; ub < u1; ub += 2 * kUnroll) {
+    if (ub + kUnroll < u1) issue(wb, sb, rb_row, rb_b, ub + kUnroll);
+    compute(wa, sa, ra_row, ra_b, ub);
+    if (ub + kUnroll >= u1) break;
+    if (ub + 2 * kUnroll < u1) issue(wa, sa, ra_row, ra_b, ub + 2 * kUnroll);
+    compute(wb, sb, rb_row, rb_b, ub + kUnroll);
+  }
+  if (!small) flush();
+  return true;
+}
+
+// Balanced contiguous share of `rows` (in groups of `gran`) for workgroup wg.
+__device__ __forceinline__ void my_rows(int rows, int gran, int G, int wg, int& ra, int& rb) {
+  int ng = rows / gran;
+  ra = (int)((int64_t)ng * wg / G) * gran;
+  rb = (int)((int64_t)ng * (wg + 1) / G) * gran;
+}
+
+// Sum the per-wave partials of rows [0, n) of the chunk into part[0][*].
+__device__ __forceinline__ void combine_rows(Smem& sm, int n) {
+  for (int t = threadIdx.x; t < n; t += kThreads) {
+    float y = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) y += sm.part[w][t];
+    sm.part[0][t] = y;
+  }
+}
+
+__device__ __forceinline__ void zero_part(Smem& sm) {
+  float* p = &sm.part[0][0];
+  for (int i = threadIdx.x; i < kWaves * kRowChunk; i += kThreads) p[i] = 0.f;
+}
+
+// Stage an input vector with fused RMSNorm: x_lds[k] = v[k] * g[k] / sqrt(mean(v^2) + eps).
+// `get(k)` returns v[k]. Contains barriers; all threads call it.
+template <class Get>
+__device__ void stage_rmsnorm(Smem& sm, int K, const float* gain, float eps, Get&& get) {
+  float ss = 0.f;
+  for (int k = threadIdx.x; k < K; k += kThreads) {
+    float v = get(k);
+    sm.x[k] = v;
+    ss += v * v;
+  }
+  float tot = block_sum(sm, ss);
+  float rs = 1.0f / sqrtf(tot / (float)K + eps);
+  for (int k = threadIdx.x; k < K; k += kThreads) sm.x[k] = sm.x[k] * rs * gain[k];
+  __syncthreads();
+}
+
+template <class Get>
+__device__ void stage_plain(Smem& sm, int K, Get&& get) {
+  for (int k = threadIdx.x; k < K; k += kThreads) sm.x[k] = get(k);
+  __syncthreads();
+}
+
+// ------------------------------------------------------------------ stage bodies
+
+struct StageEnv {
+  Ctx c;
+  const StagePlan* st;
+  int s;
+};
+
+__device__ __forceinline__ const LayerPlan& layer_of(const Ctx& c, int l) { return c.P->layers[l]; }
+
+// input of layer l: embedding row / external hidden vector for l == 0, else previous layer output
+__device__ __forceinline__ float layer_input(const Ctx& c, int l, int k) {
+  if (l > 0) return ld_coh(reinterpret_cast<const float*>(layer_of(c, l - 1).xo) + k);
+  if (c.P->dims.vocab > 0) {
+    const uint16_t* e = reinterpret_cast<const uint16_t*>(c.P->embed) + (size_t)c.A.token * c.P->dims.hidden;
+    return bf16_val(e[k]);
+  }
+  return bf16_val(c.A.x_in[k]);
+}
+
+__device__ Gemv gemv_of(const Fp8Mat& m, const char* base_unused = nullptr) {
+  (void)base_unused;
+  Gemv g{};
+  g.codes = reinterpret_cast<const uint8_t*>(m.codes);
+  g.scales = reinterpret_cast<const uint16_t*>(m.scales);
+  g.Kb = m.K;
+  g.nkb = m.nkb;
+  g.slot_mode = 0;
+  g.lg_rpv = 31;
+  return g;
+}
+
+// Generic single-chunk-loop driver: processes the workgroup's rows in chunks;
+// `prep` (wait + staging) runs before the first chunk; `epi(ra_chunk, n)`
+// consumes part[0][0..n) after combine.
+template <int EB, class Prep, class Epi>
+__device__ bool run_gemv(const StageEnv& E, Smem& sm, const Gemv& g, int ra, int rb, bool early, Prep&& prep, Epi&& epi) {
+  bool first = true;
+  if (ra >= rb) {
+    // no rows: still take part in the dependency wait so barriers match
+    return prep();
+  }
+  for (int ca = ra; ca < rb; ca += kRowChunk) {
+    int cb = min(rb, ca + kRowChunk);
+    if (!first) { zero_part(sm); __syncthreads(); }
+    bool ok = gemv_rows<EB>(g, sm, ca, cb, first, early, [&]() {
+      zero_part(sm);
+      return prep();
+    });
+    if (!ok) return false;
+    first = false;
+    __syncthreads();
+    combine_rows(sm, cb - ca);
+    __syncthreads();
+    epi(ca, cb - ca);
+    __syncthreads();
+  }
+  return true;
+}
+
+// --- QKV: [W_DQ ; W_DKV] * RMSNorm(x)
+__device__ bool stage_qkv(const StageEnv& E, Smem& sm) {
+  const Ctx& c = E.c;
+  const int l = E.st->layer;
+  const LayerPlan& L = layer_of(c, l);
+  const int D = c.P->dims.hidden;
+  Gemv g = gemv_of(L.qkv);
+  int ra, rb;
+  my_rows(E.st->rows, E.st->gran, c.G, c.wg, ra, rb);
+  float* out = reinterpret_cast<float*>(L.qkv_raw);
+  return run_gemv<1>(E, sm, g, ra, rb, true,
+      [&]() {
+        if (!wait_stage(c, sm, E.st->wait, E.s)) return false;
+        stage_rmsnorm(sm, D, reinterpret_cast<const float*>(L.attn_norm), c.P->dims.rms_eps,
+                      [&](int k) { return layer_input(c, l, k); });
+        if (l == 0 && c.wg == 0) {
+          float* x0 = reinterpret_cast<float*>(c.P->x0);
+          for (int k = threadIdx.x; k < D; k += kThreads) st_coh(x0 + k, layer_input(c, 0, k));
+        }
+        return true;
+      },
+      [&](int ca, int n) {
+        for (int t = threadIdx.x; t < n; t += kThreads) st_coh(out + ca + t, sm.part[0][t]);
+      });
+}
+
+// --- QB: W_UQ * RMSNorm(c_q) with RoPE on the rotary rows; the last workgroup appends the cache row
+__device__ bool stage_qb(const StageEnv& E, Smem& sm) {
+  const Ctx& c = E.c;
+  const pdm_dims& d = c.P->dims;
+  const int l = E.st->layer;
+  const LayerPlan& L = layer_of(c, l);
+  const float* raw = reinterpret_cast<const float*>(L.qkv_raw);
+  const float* tab = reinterpret_cast<const float*>(c.P->rope_tab) + (size_t)c.A.pos * d.rope;  // (cos, sin) pairs
+  const int qkh = d.qk_nope + d.rope;
+  Gemv g = gemv_of(L.qb);
+  int ra, rb;
+  my_rows(E.st->rows, E.st->gran, c.G, c.wg, ra, rb);
+  float* out = reinterpret_cast<float*>(L.q);
+  bool ok = run_gemv<1>(E, sm, g, ra, rb, true,
+      [&]() {
+        if (!wait_stage(c, sm, E.st->wait, E.s)) return false;
+        stage_rmsnorm(sm, d.q_lora, reinterpret_cast<const float*>(L.q_norm), d.rms_eps,
+                      [&](int k) { return ld_coh(raw + k); });
+        return true;
+      },
+      [&](int ca, int n) {
+        for (int t = threadIdx.x; t < n; t += kThreads) {
+          int r = ca + t;
+          int j = r % qkh;
+          float y = sm.part[0][t];
+          if (j >= d.qk_nope) {
+            int i = (j - d.qk_nope) >> 1;
+            float cs = tab[2 * i], sn = tab[2 * i + 1];
+            float other = sm.part[0][t ^ 1];
+            y = (j - d.qk_nope) & 1 ? other * sn + y * cs : y * cs - other * sn;
+          }
+          st_coh(out + r, y);
+        }
+      });
+  if (!ok) return false;
+  if (c.wg == c.G - 1) {
+    // cache row: [RMSNorm(kv latent) ; RoPE(rotary key)] in bf16 at position pos
+    const float* kvr = raw + d.q_lora;
+    float ss = 0.f;
+    for (int k = threadIdx.x; k < d.kv_lora; k += kThreads) { float v = ld_coh(kvr + k); ss += v * v; }
+    float tot = block_sum(sm, ss);
+    float rs = 1.0f / sqrtf(tot / (float)d.kv_lora + d.rms_eps);
+    const float* gk = reinterpret_cast<const float*>(L.kv_norm);
+    uint32_t* row = reinterpret_cast<uint32_t*>(reinterpret_cast<uint16_t*>(L.kv) + (size_t)c.A.pos * (d.kv_lora + d.rope));
+    const int npairs = (d.kv_lora + d.rope) / 2;
+    for (int p = threadIdx.x; p < npairs; p += kThreads) {
+      float a, b;
+      int k = 2 * p;
+      if (k < d.kv_lora) {
+        a = ld_coh(kvr + k) * rs * gk[k];
+        b = ld_coh(kvr + k + 1) * rs * gk[k + 1];
+      } else {
+        int i = (k - d.kv_lora) >> 1;
+        float x0 = ld_coh(kvr + k), x1 = ld_coh(kvr + k + 1);
+        float cs = tab[2 * i], sn = tab[2 * i + 1];
+        a = x0 * cs - x1 * sn;
+        b = x0 * sn + x1 * cs;
+      }
+      st_coh_u(row + p, (uint32_t)bf16_bits(a) | ((uint32_t)bf16_bits(b) << 16));
+    }
+  }
+  return true;
+}
+
+// --- ABSORB: q_lat[h] = W_UK[h]^T q_nope[h]  (rows (h, c), K = d_n, per-head input)
+__device__ bool stage_absorb(const StageEnv& E, Smem& sm) {
+  const Ctx& c = E.c;
+  const pdm_dims& d = c.P->dims;
+  const LayerPlan& L = layer_of(c, E.st->layer);
+  const int qkh = d.qk_nope + d.rope;
+  const float* q = reinterpret_cast<const float*>(L.q);
+  Gemv g = gemv_of(L.ukT);
+  int ra, rb;
+  my_rows(E.st->rows, E.st->gran, c.G, c.wg, ra, rb);
+  g.lg_rpv = 31 - __builtin_clz(d.kv_lora);
+  g.vbase = ra / d.kv_lora;
+  g.xK = d.qk_nope;
+  float* out = reinterpret_cast<float*>(L.ql);
+  return run_gemv<1>(E, sm, g, ra, rb, true,
+      [&]() {
+        if (!wait_stage(c, sm, E.st->wait, E.s)) return false;
+        int h0 = ra / d.kv_lora, h1 = (rb - 1) / d.kv_lora;
+        int n = (h1 - h0 + 1) * d.qk_nope;
+        stage_plain(sm, n, [&](int k) {
+          int h = h0 + k / d.qk_nope;
+          return ld_coh(q + (size_t)h * qkh + (k % d.qk_nope));
+        });
+        return true;
+      },
+      [&](int ca, int n) {
+        for (int t = threadIdx.x; t < n; t += kThreads) st_coh(out + ca + t, sm.part[0][t]);
+      });
+}
+
+// --- ATTN: split-KV MLA attention partials (m, l, acc) per (head, position chunk)
+template <int DPL>
+__device__ bool stage_attn(const StageEnv& E, Smem& sm) {
+  const Ctx& c = E.c;
+  const pdm_dims& d = c.P->dims;
+  const LayerPlan& L = layer_of(c, E.st->layer);
+  const int nch = c.P->nch, hg = c.P->hg;
+  const int units = c.P->n_hg * nch;
+  if (c.wg >= units) return wait_stage(c, sm, -1, E.s);  // no share of this stage
+  const int grp = c.wg / nch, ch = c.wg % nch;
+  const int pos = c.A.pos, ctx = pos + 1;
+  const int chunk = (ctx + nch - 1) / nch;
+  const int t0 = min(ctx, ch * chunk), t1 = min(ctx, t0 + chunk);
+  const int dc = d.kv_lora, dr = d.rope, kvr = dc + dr;
+  const int qkh = d.qk_nope + d.rope;
+  const float tau = 1.0f / sqrtf((float)qkh);
+  if (!wait_stage(c, sm, E.st->wait, E.s)) return false;
+  // stage q (scaled by tau): per head [q_lat (dc) ; q_rope (dr)], and the current row
+  float* qs = sm.x;                      // [hg][kvr]
+  float* cur = sm.x + hg * kvr;          // [kvr]
+  const float* ql = reinterpret_cast<const float*>(L.ql);
+  const float* qf = reinterpret_cast<const float*>(L.q);
+  for (int i = threadIdx.x; i < hg * kvr; i += kThreads) {
+    int hh = i / kvr, k = i % kvr;
+    int h = grp * hg + hh;
+    float v = k < dc ? ld_coh(ql + (size_t)h * dc + k) : ld_coh(qf + (size_t)h * qkh + d.qk_nope + (k - dc));
+    qs[i] = v * tau;
+  }
+  const uint16_t* cache = reinterpret_cast<const uint16_t*>(L.kv);
+  const bool has_cur = pos >= t0 && pos < t1;
+  if (has_cur) {
+    const uint32_t* rowp = reinterpret_cast<const uint32_t*>(cache + (size_t)pos * kvr);
+    for (int p = threadIdx.x; p < kvr / 2; p += kThreads) {
+      uint32_t u = ld_coh_u(rowp + p);
+      cur[2 * p] = bf16_lo(u);
+      cur[2 * p + 1] = bf16_hi(u);
+    }
+  }
+  __syncthreads();
+
+  const int lane = lane_id();
+  const int w = wave_id();
+  constexpr int HPW_MAX = kHeadGroup / kWaves;  // 2
+  const int hpw = hg / kWaves;                  // 1 or 2
+  float m[HPW_MAX], lsum[HPW_MAX], acc[HPW_MAX][DPL];
+#pragma unroll
+  for (int i = 0; i < HPW_MAX; ++i) {
+    m[i] = -INFINITY; lsum[i] = 0.f;
+#pragma unroll
+    for (int k = 0; k < DPL; ++k) acc[i][k] = 0.f;
+  }
+  const int tmain = min(t1, pos);  // rows before pos come from the cache through cached loads
+  for (int tb = t0; tb < tmain; tb += 64) {
+    const int t = tb + lane;
+    const bool valid = t < tmain;
+    float s[HPW_MAX] = {0.f, 0.f};
+    const uint4* rp = reinterpret_cast<const uint4*>(cache + (size_t)(valid ? t : t0) * kvr);
+    // latent part: dc/8 loads of 8 bf16
+#pragma unroll 4
+    for (int q8 = 0; q8 < kvr / 8; ++q8) {
+      uint4 v = rp[q8];
+      float f[8] = {bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y),
+                    bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w)};
+#pragma unroll
+      for (int i = 0; i < HPW_MAX; ++i) {
+        if (i < hpw) {
+          const float4* qv = reinterpret_cast<const float4*>(qs + (w * hpw + i) * kvr + q8 * 8);
+          float4 a = qv[0], b = qv[1];
+          s[i] += a.x * f[0] + a.y * f[1] + a.z * f[2] + a.w * f[3] + b.x * f[4] + b.y * f[5] + b.z * f[6] + b.w * f[7];
+        }
+      }
+    }
+    float p[HPW_MAX];
+#pragma unroll
+    for (int i = 0; i < HPW_MAX; ++i) {
+      if (i < hpw) {
+        float sv = valid ? s[i] : -INFINITY;
+        float mb = wave_max(sv);
+        float mn = fmaxf(m[i], mb);
+        float alpha = __expf(m[i] - mn);
+        p[i] = valid ? __expf(sv - mn) : 0.f;
+        lsum[i] = lsum[i] * alpha + wave_sum(p[i]);
+#pragma unroll
+        for (int k = 0; k < DPL; ++k) acc[i][k] *= alpha;
+        m[i] = mn;
+      }
+    }
+    const int nv = min(64, tmain - tb);
+    for (int j = 0; j < nv; ++j) {
+      const uint16_t* r = cache + (size_t)(tb + j) * kvr + lane * DPL;
+      float cv[DPL];
+      if constexpr (DPL == 8) {
+        uint4 v = *reinterpret_cast<const uint4*>(r);
+        cv[0] = bf16_lo(v.x); cv[1] = bf16_hi(v.x); cv[2] = bf16_lo(v.y); cv[3] = bf16_hi(v.y);
+        cv[4] = bf16_lo(v.z); cv[5] = bf16_hi(v.z); cv[6] = bf16_lo(v.w); cv[7] = bf16_hi(v.w);
+      } else if constexpr (DPL == 4) {
+        uint2 v = *reinterpret_cast<const uint2*>(r);
+        cv[0] = bf16_lo(v.x); cv[1] = bf16_hi(v.x); cv[2] = bf16_lo(v.y); cv[3] = bf16_hi(v.y);
+      } else {
+        uint32_t v = *reinterpret_cast<const uint32_t*>(r);
+        cv[0] = bf16_lo(v); cv[1] = bf16_hi(v);
+      }
+#pragma unroll
+      for (int i = 0; i < HPW_MAX; ++i) {
+        if (i < hpw) {
+          float pj = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, p[i]), j));
+#pragma unroll
+          for (int k = 0; k < DPL; ++k) acc[i][k] = fmaf(pj, cv[k], acc[i][k]);
+        }
+      }
+    }
+  }
+  if (has_cur) {
+#pragma unroll
+    for (int i = 0; i < HPW_MAX; ++i) {
+      if (i < hpw) {
+        const float* qh = qs + (w * hpw + i) * kvr;
+        float part = 0.f;
+        for (int k = lane; k < kvr; k += 64) part += qh[k] * cur[k];
+        float sv = wave_sum(part);
+        float mn = fmaxf(m[i], sv);
+        float alpha = __expf(m[i] - mn);
+        float pv = __expf(sv - mn);
+        lsum[i] = lsum[i] * alpha + pv;
+#pragma unroll
+        for (int k = 0; k < DPL; ++k) acc[i][k] = acc[i][k] * alpha + pv * cur[lane * DPL + k];
+        m[i] = mn;
+      }
+    }
+  }
+  float* part = reinterpret_cast<float*>(L.attn_part);
+#pragma unroll
+  for (int i = 0; i < HPW_MAX; ++i) {
+    if (i < hpw) {
+      int h = grp * hg + w * hpw + i;
+      float* dst = part + ((size_t)h * nch + ch) * (dc + 2);
+#pragma unroll
+      for (int k = 0; k < DPL; ++k) st_coh(dst + lane * DPL + k, acc[i][k]);
+      if (lane == 0) { st_coh(dst + dc, m[i]); st_coh(dst + dc + 1, lsum[i]); }
+    }
+  }
+  return true;
+}
+
+// --- UV: merge the attention partials of each head, o[h] = W_UV[h] o_lat[h]
+__device__ bool stage_uv(const StageEnv& E, Smem& sm) {
+  const Ctx& c = E.c;
+  const pdm_dims& d = c.P->dims;
+  const LayerPlan& L = layer_of(c, E.st->layer);
+  const int nch = c.P->nch, dc = d.kv_lora;
+  const float* part = reinterpret_cast<const float*>(L.attn_part);
+  Gemv g = gemv_of(L.uv);
+  int ra, rb;
+  my_rows(E.st->rows, E.st->gran, c.G, c.wg, ra, rb);
+  g.lg_rpv = 31 - __builtin_clz(d.v_head);
+  g.vbase = ra / d.v_head;
+  g.xK = dc;
+  float* out = reinterpret_cast<float*>(L.o);
+  return run_gemv<1>(E, sm, g, ra, rb, true,
+      [&]() {
+        if (!wait_stage(c, sm, E.st->wait, E.s)) return false;
+        int h0 = ra / d.v_head, h1 = (rb - 1) / d.v_head;
+        float* fac = sm.x + kXMax - 2 * kRowChunk;  // per-chunk max, then merge weights
+        for (int h = h0; h <= h1; ++h) {
+          const float* ph = part + (size_t)h * nch * (dc + 2);
+          for (int i = threadIdx.x; i < nch; i += kThreads) {
+            fac[i] = ld_coh(ph + (size_t)i * (dc + 2) + dc);
+            fac[kRowChunk + i] = ld_coh(ph + (size_t)i * (dc + 2) + dc + 1);
+          }
+          __syncthreads();
+          float mx = -INFINITY;
+          for (int i = 0; i < nch; ++i) mx = fmaxf(mx, fac[i]);
+          float den = 0.f;
+          for (int i = 0; i < nch; ++i) den += fac[i] == -INFINITY ? 0.f : fac[kRowChunk + i] * __expf(fac[i] - mx);
+          __syncthreads();
+          for (int i = threadIdx.x; i < nch; i += kThreads) fac[i] = fac[i] == -INFINITY ? 0.f : __expf(fac[i] - mx) / den;
+          __syncthreads();
+          for (int k = threadIdx.x; k < dc; k += kThreads) {
+            float num = 0.f;
+            for (int i = 0; i < nch; ++i) num += ld_coh(ph + (size_t)i * (dc + 2) + k) * fac[i];
+            sm.x[(h - h0) * dc + k] = num;
+          }
+          __syncthreads();
+        }
+        return true;
+      },
+      [&](int ca, int n) {
+        for (int t = threadIdx.x; t < n; t += kThreads) st_coh(out + ca + t, sm.part[0][t]);
+      });
+}
+
+// --- WO: x_attn = x + W_O o
+__device__ bool stage_wo(const StageEnv& E, Smem& sm) {
+  const Ctx& c = E.c;
+  const pdm_dims& d = c.P->dims;
+  const int l = E.st->layer;
+  const LayerPlan& L = layer_of(c, l);
+  const float* o = reinterpret_cast<const float*>(L.o);
+  Gemv g = gemv_of(L.wo);
+  int ra, rb;
+  my_rows(E.st->rows, E.st->gran, c.G, c.wg, ra, rb);
+  float* out = reinterpret_cast<float*>(L.xa);
+  return run_gemv<1>(E, sm, g, ra, rb, true,
+      [&]() {
+        if (!wait_stage(c, sm, E.st->wait, E.s)) return false;
+        stage_plain(sm, d.n_heads * d.v_head, [&](int k) { return ld_coh(o + k); });
+        return true;
+      },
+      [&](int ca, int n) {
+        for (int t = threadIdx.x; t < n; t += kThreads) st_coh(out + ca + t, layer_input(c, l, ca + t) + sm.part[0][t]);
+      });
+}
+
+// --- ROUTER: z = W_r * RMSNorm(x_attn)   (bf16 weights)
+__device__ bool stage_router(const StageEnv& E, Smem& sm) {
+  const Ctx& c = E.c;
+  const pdm_dims& d = c.P->dims;
+  const LayerPlan& L = layer_of(c, E.st->layer);
+  const float* xa = reinterpret_cast<const float*>(L.xa);
+  Gemv g{};
+  g.codes = reinterpret_cast<const uint8_t*>(L.router);
+  g.Kb = d.hidden * 2;
+  g.lg_rpv = 31;
+  int ra, rb;
+  my_rows(E.st->rows, E.st->gran, c.G, c.wg, ra, rb);
+  float* out = reinterpret_cast<float*>(L.router_logits);
+  return run_gemv<2>(E, sm, g, ra, rb, true,
+      [&]() {
+        if (!wait_stage(c, sm, E.st->wait, E.s)) return false;
+        stage_rmsnorm(sm, d.hidden, reinterpret_cast<const float*>(L.ffn_norm), d.rms_eps,
+                      [&](int k) { return ld_coh(xa + k); });
+        return true;
+      },
+      [&](int ca, int n) {
+        for (int t = threadIdx.x; t < n; t += kThreads) st_coh(out + ca + t, sm.part[0][t]);
+      });
+}
+
+// Top-k of the router logits by one wave (ties to the lower index), written to
+// the slot tables with sigmoid weights normalised over the chosen experts.
+// Must be called by all threads; contains barriers.
+__device__ void route_topk(const Ctx& c, Smem& sm, const LayerPlan& L, bool write_tap) {
+  const pdm_dims& d = c.P->dims;
+  const float* z = reinterpret_cast<const float*>(L.router_logits);
+  const int E = d.n_experts, k = d.top_k;
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    float v[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      int e = lane + 64 * i;
+      v[i] = e < E ? ld_coh(z + e) : -INFINITY;
+    }
+    float wsum = 0.f;
+    for (int j = 0; j < k; ++j) {
+      // lane-local best (lowest index among equal values: scan in increasing index order)
+      float bv = -INFINITY;
+      int bi = 0x7fffffff;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        int e = lane + 64 * i;
+        if (e < E && (v[i] > bv || (v[i] == bv && e < bi))) { bv = v[i]; bi = e; }
+      }
+      // wave argmax
+      for (int off = 1; off < 64; off <<= 1) {
+        float ov = __shfl_xor(bv, off);
+        int oi = __shfl_xor(bi, off);
+        if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
+      }
+      if (bi >= E) bi = 0;  // only when no finite logit is left (never for finite inputs)
+      // remove it
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if (lane + 64 * i == bi) v[i] = -INFINITY;
+      float sg = 1.0f / (1.0f + __expf(-bv));
+      if (lane == 0) { sm.route_idx[j] = bi; sm.route_w[j] = sg; }
+      wsum += sg;
+    }
+    if (lane == 0) {
+      for (int j = 0; j < k; ++j) sm.route_w[j] /= wsum;
+    }
+  }
+  __syncthreads();
+  if (write_tap && threadIdx.x < k) {
+    reinterpret_cast<int*>(L.topk_idx)[threadIdx.x] = sm.route_idx[threadIdx.x];
+    reinterpret_cast<float*>(L.topk_w)[threadIdx.x] = sm.route_w[threadIdx.x];
+  }
+}
+
+// Slot tables of an MoE stage: expert block pointers (gate/up or down part),
+// weights and act offsets. Routed slots use the layer's top-k in LDS.
+__device__ void set_slots(const pdm_dims& d, const LayerPlan& L, Smem& sm, bool routed, bool down) {
+  const int t = threadIdx.x;
+  const int n = down ? d.top_k + d.n_shared : (routed ? d.top_k : d.n_shared);
+  if (t < n) {
+    int e, act;
+    float w;
+    if (down) {
+      e = t < d.top_k ? sm.route_idx[t] : d.n_experts + (t - d.top_k);
+      w = 1.f;
+      act = t * d.moe_ffn;
+    } else if (routed) {
+      e = sm.route_idx[t];
+      w = sm.route_w[t];
+      act = t * d.moe_ffn;
+    } else {
+      e = d.n_experts + t;
+      w = 1.f;
+      act = (d.top_k + t) * d.moe_ffn;
+    }
+    const uint8_t* base = reinterpret_cast<const uint8_t*>(L.expert_base) + (size_t)e * L.expert_stride;
+    const Fp8Mat& m = down ? L.edown : L.egu;
+    sm.slot_codes[t] = base + m.codes;
+    sm.slot_scales[t] = reinterpret_cast<const uint16_t*>(base + m.scales);
+    sm.slot_w[t] = w;
+    sm.slot_act[t] = act;
+  }
+}
+
+// --- GU: SwiGLU gate/up of dense FFN, shared experts, or routed experts
+__device__ bool stage_gu(const StageEnv& E, Smem& sm, bool routed) {
+  const Ctx& c = E.c;
+  const pdm_dims& d = c.P->dims;
+  const LayerPlan& L = layer_of(c, E.st->layer);
+  const float* xa = reinterpret_cast<const float*>(L.xa);
+  float* act = reinterpret_cast<float*>(L.act);
+  Gemv g{};
+  g.lg_rpv = 31;
+  g.Kb = d.hidden;
+  int F;  // intermediate per slot
+  if (!L.is_moe) {
+    g = gemv_of(L.gu);
+    F = d.ffn;
+  } else {
+    g.slot_mode = 1;
+    g.lg_slot = 31 - __builtin_clz(2 * d.moe_ffn);
+    g.slot_Kb = d.hidden;
+    g.nkb = L.egu.nkb;
+    F = d.moe_ffn;
+  }
+  int ra, rb;
+  my_rows(E.st->rows, E.st->gran, c.G, c.wg, ra, rb);
+  // shared-expert and dense pointers are static: set them before the early
+  // weight loads; routed pointers need the router output (after the wait)
+  if (L.is_moe && !routed) {
+    set_slots(d, L, sm, false, false);
+    __syncthreads();
+  }
+  return run_gemv<1>(E, sm, g, ra, rb, !routed,
+      [&]() {
+        if (!wait_stage(c, sm, E.st->wait, E.s)) return false;
+        if (routed) {
+          route_topk(c, sm, L, c.wg == 0);
+          set_slots(d, L, sm, true, false);
+        }
+        stage_rmsnorm(sm, d.hidden, reinterpret_cast<const float*>(L.ffn_norm), d.rms_eps,
+                      [&](int k) { return ld_coh(xa + k); });
+        return true;
+      },
+      [&](int ca, int n) {
+        // rows are gate/up interleaved in groups of 8: [gate 8 ; up 8]
+        for (int t = threadIdx.x; t < n / 2; t += kThreads) {
+          int grp = t >> 3, r = t & 7;
+          float gt = sm.part[0][grp * 16 + r];
+          float up = sm.part[0][grp * 16 + 8 + r];
+          int pr = (ca >> 1) + t;  // pair row across all slots
+          float a = silu(gt) * up;
+          int dst;
+          if (L.is_moe) {
+            int j = pr / F, f = pr - j * F;
+            a *= sm.slot_w[j];
+            dst = sm.slot_act[j] + f;
+          } else {
+            dst = pr;
+          }
+          st_coh(act + dst, a);
+        }
+      });
+}
+
+// --- DOWN: x_out = bf16(x_attn + sum_slots W_down[slot] act[slot])
+__device__ bool stage_down(const StageEnv& E, Smem& sm) {
+  const Ctx& c = E.c;
+  const pdm_dims& d = c.P->dims;
+  const LayerPlan& L = layer_of(c, E.st->layer);
+  const float* xa = reinterpret_cast<const float*>(L.xa);
+  const float* act = reinterpret_cast<const float*>(L.act);
+  float* out = reinterpret_cast<float*>(L.xo);
+  Gemv g{};
+  int K;
+  if (!L.is_moe) {
+    g = gemv_of(L.down);
+    K = d.ffn;
+  } else {
+    K = (d.top_k + d.n_shared) * d.moe_ffn;
+    g.Kb = K;
+    g.slot_mode = 2;
+    g.lg_slot = 31 - __builtin_clz(d.moe_ffn);
+    g.slot_Kb = d.moe_ffn;
+    g.nkb = L.edown.nkb;
+    g.lg_rpv = 31;
+  }
+  int ra, rb;
+  my_rows(E.st->rows, E.st->gran, c.G, c.wg, ra, rb);
+  // the layer's routing is already in LDS (set by the routed gate/up stage)
+  if (L.is_moe) {
+    set_slots(d, L, sm, true, true);
+    __syncthreads();
+  }
+  return run_gemv<1>(E, sm, g, ra, rb, true,
+      [&]() {
+        if (!wait_stage(c, sm, E.st->wait, E.s)) return false;
+        stage_plain(sm, K, [&](int k) { return ld_coh(act + k); });
+        return true;
+      },
+      [&](int ca, int n) {
+        for (int t = threadIdx.x; t < n; t += kThreads)
+          st_coh(out + ca + t, round_bf16(ld_coh(xa + ca + t) + sm.part[0][t]));
+      });
+}
+
+// --- LM: logits = W_lm * RMSNorm(x), argmax over the vocabulary
+__device__ bool stage_lm(const StageEnv& E, Smem& sm) {
+  const Ctx& c = E.c;
+  const pdm_dims& d = c.P->dims;
+  const float* x = reinterpret_cast<const float*>(layer_of(c, d.n_layers - 1).xo);
+  float* logits = c.A.logits ? c.A.logits : reinterpret_cast<float*>(c.P->logits_internal);
+  Gemv g{};
+  g.codes = reinterpret_cast<const uint8_t*>(c.P->lm_head);
+  g.Kb = d.hidden * 2;
+  g.lg_rpv = 31;
+  int ra, rb;
+  my_rows(E.st->rows, E.st->gran, c.G, c.wg, ra, rb);
+  float bestv = -INFINITY;
+  int besti = 0x7fffffff;
+  bool ok = run_gemv<2>(E, sm, g, ra, rb, true,
+      [&]() {
+        if (!wait_stage(c, sm, E.st->wait, E.s)) return false;
+        stage_rmsnorm(sm, d.hidden, reinterpret_cast<const float*>(c.P->final_norm), d.rms_eps,
+                      [&](int k) { return ld_coh(x + k); });
+        return true;
+      },
+      [&](int ca, int n) {
+        for (int t = threadIdx.x; t < n; t += kThreads) {
+          float v = sm.part[0][t];
+          logits[ca + t] = v;
+          if (v > bestv || (v == bestv && ca + t < besti)) { bestv = v; besti = ca + t; }
+        }
+      });
+  if (!ok) return false;
+  // workgroup argmax
+  for (int off = 1; off < 64; off <<= 1) {
+    float ov = __shfl_xor(bestv, off);
+    int oi = __shfl_xor(besti, off);
+    if (ov > bestv || (ov == bestv && oi < besti)) { bestv = ov; besti = oi; }
+  }
+  if (lane_id() == 0) { sm.red[wave_id()] = bestv; sm.ired[wave_id()] = besti; }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int w = 1; w < kWaves; ++w)
+      if (sm.red[w] > bestv || (sm.red[w] == bestv && sm.ired[w] < besti)) { bestv = sm.red[w]; besti = sm.ired[w]; }
+    float* best = reinterpret_cast<float*>(c.P->lm_best) + 2 * c.wg;
+    st_coh(best, bestv);
+    st_coh_i(reinterpret_cast<int*>(best + 1), besti);
+    mem_done();
+    // the last workgroup to arrive reduces the per-workgroup maxima
+    int* done = counter_ptr(c, c.P->n_stages, 0);
+    int old = __hip_atomic_fetch_add(done, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (old == (int)c.A.epoch * c.G - 1) {
+      float bv = -INFINITY;
+      int bi = 0x7fffffff;
+      for (int w = 0; w < c.G; ++w) {
+        const float* bw = reinterpret_cast<const float*>(c.P->lm_best) + 2 * w;
+        float v = ld_coh(bw);
+        int i = ld_coh_i(reinterpret_cast<const int*>(bw + 1));
+        if (v > bv || (v == bv && i < bi)) { bv = v; bi = i; }
+      }
+      if (c.A.argmax) *c.A.argmax = bi;
+    }
+  }
+  return true;
+}
+
+}  // namespace
+
+__global__ void __launch_bounds__(kThreads, 1) engine_kernel(const Plan* __restrict__ P, LaunchArgs A) {
+  __shared__ Smem sm;
+  Ctx c;
+  c.P = P;
+  c.A = A;
+  c.G = P->G;
+  c.wg = blockIdx.x;
+  const int n = P->n_stages;
+  const int dpl = P->dims.kv_lora / 64;
+  for (int s = 0; s < n; ++s) {
+    StageEnv E{c, &P->stages[s], s};
+    bool ok;
+    switch (P->stages[s].type) {
+      case PDM_ST_QKV: ok = stage_qkv(E, sm); break;
+      case PDM_ST_QB: ok = stage_qb(E, sm); break;
+      case PDM_ST_ABSORB: ok = stage_absorb(E, sm); break;
+      case PDM_ST_ATTN:
+        ok = dpl == 8 ? stage_attn<8>(E, sm) : dpl == 4 ? stage_attn<4>(E, sm) : stage_attn<2>(E, sm);
+        break;
+      case PDM_ST_UV: ok = stage_uv(E, sm); break;
+      case PDM_ST_WO: ok = stage_wo(E, sm); break;
+      case PDM_ST_ROUTER: ok = stage_router(E, sm); break;
+      case PDM_ST_GU: ok = stage_gu(E, sm, false); break;
+      case PDM_ST_GU_ROUTED: ok = stage_gu(E, sm, true); break;
+      case PDM_ST_DOWN: ok = stage_down(E, sm); break;
+      case PDM_ST_LM: ok = stage_lm(E, sm); break;
+      default: ok = false; break;
+    }
+    if (!ok) return;  // watchdog abort: every workgroup leaves at its next wait
+    signal_stage(c, sm, s);
+  }
+}
+
+// ------------------------------------------------------------------ setup kernels
+
+// cos/sin table for RoPE: tab[t][i] = (cos, sin) of t * base^(-2i/d), computed in float64.
+__global__ void rope_table_kernel(float* tab, int max_ctx, int rope, double base) {
+  const int half = rope / 2;
+  const size_t n = (size_t)max_ctx * half;
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) {
+    int t = (int)(i / half), j = (int)(i % half);
+    double inv = pow(base, -2.0 * j / rope);
+    double a = (double)t * inv;
+    tab[2 * i] = (float)cos(a);
+    tab[2 * i + 1] = (float)sin(a);
+  }
+}
+
+// Offline packer: logical FP8 matrix (codes [N][K], scales [ceil(N/128)][ceil(K/128)])
+// into a packed matrix (codes [rows][Kp], scales [rows/8][nkb]) by a row/column map.
+//   mode 0: packed row r = logical row (r - row0) for r in [row0, row0 + N), same columns
+//   mode 1 (W_UK transpose): packed row (h, c), column n  <- logical (h*(dn+dv) + n, c)
+//   mode 2 (W_UV extract):   packed row (h, v), column c  <- logical (h*(dn+dv) + dn + v, c)
+//   mode 3 (gate/up interleave): packed row 16*i + j (j < 8) <- gate row 8*i + j (a0 = 0),
+//                                packed row 16*i + 8 + j     <- up row 8*i + j (a0 = 1)
+
+__device__ __forceinline__ bool pack_src(const PackMap& m, int r, int k, int& sr, int& sc) {
+  switch (m.mode) {
+    case 0:
+      if (r < m.row0 || r >= m.row0 + m.N) return false;
+      sr = r - m.row0; sc = k; return true;
+    case 1: {
+      int h = r / m.dc, cc = r % m.dc;
+      sr = h * (m.dn + m.dv) + k; sc = cc; return true;
+    }
+    case 2: {
+      int h = r / m.dv, v = r % m.dv;
+      sr = h * (m.dn + m.dv) + m.dn + v; sc = k; return true;
+    }
+    default: {
+      int i = r >> 4, j = r & 15;
+      if ((j >= 8) != (m.which == 1)) return false;
+      sr = 8 * i + (j & 7); sc = k; return true;
+    }
+  }
+}
+
+__global__ void pack_codes_kernel(const uint8_t* __restrict__ src, uint8_t* __restrict__ dst, PackMap m) {
+  const size_t n = (size_t)m.rows * m.Kp;
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) {
+    int r = (int)(i / m.Kp), k = (int)(i % m.Kp);
+    int sr, sc;
+    if (pack_src(m, r, k, sr, sc)) dst[i] = src[(size_t)sr * m.K + sc];
+  }
+}
+
+// One scale per (8 packed rows, 128 packed columns): the logical block holding
+// the tile's first element. The host checks at plan time that every tile lies
+// inside one logical 128x128 block.
+__global__ void pack_scales_kernel(const uint16_t* __restrict__ src, uint16_t* __restrict__ dst, PackMap m) {
+  const int skb = (m.K + 127) / 128;
+  const size_t n = (size_t)(m.rows / 8) * m.nkb;
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) {
+    int rg = (int)(i / m.nkb), kb = (int)(i % m.nkb);
+    int sr, sc;
+    if (!pack_src(m, rg * 8, kb * 128, sr, sc)) continue;
+    dst[i] = src[(size_t)(sr / 128) * skb + (sc / 128)];
+  }
+}
+
+}  // namespace pdm
+
+namespace pdm {
+
+hipError_t launch_engine(const Plan* plan_dev, const LaunchArgs& a, int G, hipStream_t stream, bool cooperative) {
+  if (cooperative) {
+    const Plan* p = plan_dev;
+    LaunchArgs args = a;
+    void* kargs[] = {(void*)&p, (void*)&args};
+    return hipLaunchCooperativeKernel((const void*)engine_kernel, dim3(G), dim3(kThreads), kargs, 0, stream);
+  }
+  hipLaunchKernelGGL(engine_kernel, dim3(G), dim3(kThreads), 0, stream, plan_dev, a);
+  return hipGetLastError();
+}
+
+__global__ void zero_words_kernel(uint32_t* p, size_t n) {
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) p[i] = 0u;
+}
+
+hipError_t launch_zero(void* p, size_t bytes, hipStream_t stream) {
+  size_t n = bytes / 4;
+  int blocks = (int)std::min<size_t>(1024, (n + 255) / 256);
+  if (blocks < 1) return hipSuccess;
+  hipLaunchKernelGGL(zero_words_kernel, dim3(blocks), dim3(256), 0, stream, reinterpret_cast<uint32_t*>(p), n);
+  return hipGetLastError();
+}
+
+hipError_t launch_rope_table(float* tab, int max_ctx, int rope, double base, hipStream_t stream) {
+  size_t n = (size_t)max_ctx * (rope / 2);
+  int blocks = (int)std::min<size_t>(4096, (n + 255) / 256);
+  hipLaunchKernelGGL(rope_table_kernel, dim3(blocks), dim3(256), 0, stream, tab, max_ctx, rope, base);
+  return hipGetLastError();
+}
+
+hipError_t launch_pack(const uint8_t* src_codes, const uint16_t* src_scales, uint8_t* dst_codes,
+                       uint16_t* dst_scales, const PackMap& m, hipStream_t stream) {
+  size_t n = (size_t)m.rows * m.Kp;
+  int blocks = (int)std::min<size_t>(8192, (n + 255) / 256);
+  hipLaunchKernelGGL(pack_codes_kernel, dim3(blocks), dim3(256), 0, stream, src_codes, dst_codes, m);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  size_t ns = (size_t)(m.rows / 8) * m.nkb;
+  int sblocks = (int)std::min<size_t>(4096, (ns + 255) / 256);
+  hipLaunchKernelGGL(pack_scales_kernel, dim3(sblocks), dim3(256), 0, stream, src_scales, dst_scales, m);
+  return hipGetLastError();
+}
+
+}  // namespace pdm

