@@ -1,0 +1,219 @@
+#!/usr/bin/env python3
+"""Batch-1 decode benchmark of the persistent engine on one MI355X.
+
+Workload (default): the DeepSeek-V3-shaped stack of 3 dense + 8 MoE MLA
+layers with a bf16 LM head (vocabulary 129,280), FP8-e4m3 weights with
+128x128 bf16 block scales, batch 1, a 1024-position latent cache (synthetic
+N(0,1) latents) and 1024 teacher-forced decode steps, so the cache grows from
+1025 to 2048 rows. Weights, latents and tokens are seeded synthetic data.
+
+One step is one persistent-kernel launch (the whole decode step). The timed
+region is K back-to-back steps with HIP events on the launch stream; inputs
+are resident in HBM. Prints one JSON line with tokens/s/user, TPOT, the HBM
+roofline fraction of the engine kernel and the CPU oracle baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+
+def log(msg):
+    print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
+
+
+def engine_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in ("engine.hip", "pdm_internal.h", "planner.cpp"):
+        with open(os.path.join(ROOT, "persistent_decode_megakernel_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload: str):
+    """HBM traffic per launch from the committed rocprofv3 counter summary, if
+    it was taken on the current kernel source."""
+    p = os.path.join(ROOT, "profiles", f"engine_{workload}_traffic.json")
+    if not os.path.exists(p):
+        return None
+    d = json.load(open(p))
+    if d.get("engine_source_hash") != engine_source_hash():
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(cfg, store, seed, pos):
+    """Time the CPU oracle on a bounded sample of one decode step: one dense
+    layer, one MoE layer and 1/16 of the LM head rows, then scale to a whole
+    token (3 dense + 8 MoE layers + the full LM head)."""
+    import numpy as np
+    import oracle as O
+    from oracle import model as M
+    from synth import gen
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        threads = 1
+    W = O.OracleWeights(store, cache_limit_bytes=0)
+    st = O.DecodeState.empty(cfg, pos + 1)
+    dense_l = cfg.layers.index("dense")
+    moe_l = cfg.layers.index("moe")
+    for l in (dense_l, moe_l):
+        rows = gen.latent_rows(cfg, l, pos, seed, device=store.device).cpu().numpy().view(np.uint16)
+        st.cache[l][:pos] = O.bf16_bits_to_f64(rows)
+    x = W.bf16_row("embed", gen.decode_token(cfg, 0, 0, seed))
+    t = {}
+    for name, l in (("dense", dense_l), ("moe", moe_l)):
+        t0 = time.perf_counter()
+        x = M.attention_decode(W, cfg, l, x, pos, st, True)
+        x = O.bf16_round(M.ffn_decode(W, cfg, l, x))
+        t[name] = time.perf_counter() - t0
+        log(f"cpu baseline: oracle {name} layer {t[name]:.2f} s")
+    t0 = time.perf_counter()
+    lm = store.numpy("lm_head")["data"]
+    rows = lm.shape[0] // 16
+    hf = O.rmsnorm(x, W("final_norm"), cfg.rms_eps)
+    _ = O.bf16_bits_to_f64(lm[:rows]) @ hf
+    t["lm_sixteenth"] = time.perf_counter() - t0
+    n_dense, n_moe = cfg.layers.count("dense"), cfg.layers.count("moe")
+    per_token = n_dense * t["dense"] + n_moe * t["moe"] + 16 * t["lm_sixteenth"]
+    return {"value": 1.0 / per_token, "unit": "tok/s/user", "cores": threads, "kind": "oracle",
+            "sample": (f"float64 numpy oracle timed on one dense layer ({t['dense']:.2f} s), one MoE layer "
+                       f"({t['moe']:.2f} s) and 1/16 of the LM head rows ({t['lm_sixteenth']:.2f} s) of one "
+                       f"decode step at context {pos + 1}; scaled to {n_dense} dense + {n_moe} MoE layers + the "
+                       f"full LM head = {per_token:.1f} s per token")}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=1024)
+    ap.add_argument("--warmup", type=int, default=8)
+    ap.add_argument("--workload", default="dsv3_stack_1k")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this engine runs batch-1 decode on one GPU; multi-GPU runs are not "
+                                   "part of it (see DESIGN.md for how the path would shard)",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+    import torch
+    from persistent_decode_megakernel_amd import Engine, roofline as R
+    from synth import configs, gen
+
+    cfg = configs.get(args.workload)
+    P, K, Wm = cfg.prompt_len, args.steps, args.warmup
+    if K < 1 or P + max(K, Wm) > P + cfg.decode_steps:
+        raise SystemExit(f"--steps and --warmup must be within 1..{cfg.decode_steps}")
+    max_ctx = P + cfg.decode_steps
+    log(f"workload {cfg.name}: {cfg.n_layers} layers, prompt {P}, {K} timed steps")
+    eng = Engine(cfg, max_ctx=max_ctx, device=0)
+    log(f"buffers: weights {eng.sizes.weight_bytes / 1e9:.2f} GB, kv {eng.sizes.kv_bytes / 1e6:.1f} MB, "
+        f"{eng.sizes.n_stages} stages, {eng.sizes.n_workgroups} workgroups")
+    store = gen.LogicalWeights(cfg, args.seed, "cuda", cache=False)
+    t0 = time.time()
+    specs = store.specs()
+    for i, spec in enumerate(specs):
+        eng.load_tensor(spec, store.get(spec.name, spec.layer, spec.expert))
+        if (i + 1) % 256 == 0:
+            torch.cuda.synchronize()
+            log(f"packed {i + 1}/{len(specs)} tensors ({time.time() - t0:.0f} s)")
+    torch.cuda.synchronize()
+    log(f"weights generated and packed in {time.time() - t0:.0f} s")
+    lat = [gen.latent_rows(cfg, l, P, args.seed, device="cuda") for l in range(cfg.n_layers)]
+
+    def fill_cache():
+        eng.reset()
+        for l in range(cfg.n_layers):
+            eng.import_kv(l, 0, lat[l])
+
+    tokens = [gen.decode_token(cfg, j, 0, args.seed) for j in range(max(K, Wm))]
+    x_in = None
+    if cfg.vocab == 0:
+        x_in = [gen.layer_input(cfg, j, 0, args.seed, device="cuda") for j in range(max(K, Wm))]
+
+    def step(j):
+        if x_in is None:
+            eng.decode(P + j, token=tokens[j])
+        else:
+            eng.decode(P + j, x_in=x_in[j])
+
+    fill_cache()
+    for j in range(Wm):
+        step(j)
+    rc, st = eng.status()
+    if rc != 0:
+        raise SystemExit(f"warm-up step failed: status {rc} stage {st.stage}")
+    log(f"warm-up {Wm} steps ok")
+    fill_cache()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
+    ev[0].record(stream)
+    for j in range(K):
+        step(j)
+        ev[j + 1].record(stream)
+    torch.cuda.synchronize()
+    rc, st = eng.status()
+    if rc != 0:
+        raise SystemExit(f"timed step failed: status {rc} stage {st.stage}")
+    per = [ev[j].elapsed_time(ev[j + 1]) for j in range(K)]     # ms, one launch each
+    total_ms = ev[0].elapsed_time(ev[K])
+    tpot = total_ms / K / 1e3
+    per_sorted = sorted(per)
+    p50, p99 = per_sorted[K // 2], per_sorted[min(K - 1, int(0.99 * K))]
+    bytes_mean = R.mean_bytes_per_token(cfg, P, K)
+    achieved = bytes_mean / tpot
+    log(f"TPOT {tpot * 1e3:.3f} ms ({1 / tpot:.1f} tok/s/user), {achieved / 1e9:.0f} GB/s = "
+        f"{achieved / R.HBM_PEAK_BYTES_PER_S * 100:.1f}% of 8 TB/s")
+    traffic = load_traffic(cfg.name)
+    out = {
+        "metric": "batch-1 decode tokens/s/user",
+        "value": round(1.0 / tpot, 3),
+        "unit": "tok/s/user",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": Wm,
+        "ms_per_step": round(tpot * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": (f"{cfg.name}: {cfg.layers.count('dense')} dense + {cfg.layers.count('moe')} MoE MLA layers"
+                         f"{' + bf16 LM head' if cfg.vocab else ''}, DeepSeek-V3 shapes, batch 1, "
+                         f"{P}-position latent cache, {K} teacher-forced decode steps"),
+            "weights": "fp8-e4m3 + bf16 128x128 block scales; router and LM head bf16",
+            "prompt_positions": P,
+            "context_range": [P + 1, P + K],
+            "batch": 1,
+        },
+        "tpot_ms": {"mean": round(tpot * 1e3, 4), "p50": round(p50, 4), "p99": round(p99, 4)},
+        "hbm": {"bytes_per_token": int(bytes_mean), "achieved_GBps": round(achieved / 1e9, 1),
+                "frac_of_8TBps": round(achieved / R.HBM_PEAK_BYTES_PER_S, 4),
+                "roofline_tok_s": round(R.roofline_tokens_per_s(R.HBM_PEAK_BYTES_PER_S, bytes_mean), 1)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved / 1e9, 1), "peak": 8000.0, "unit": "GB/s",
+                     "frac": round(achieved / R.HBM_PEAK_BYTES_PER_S, 4), "traffic": traffic,
+                     "kernel": "pdm::engine_kernel (one launch per decode step)",
+                     "algorithmic_bytes_per_launch": int(bytes_mean)},
+    }
+    if not args.no_cpu_baseline:
+        try:
+            out["cpu_baseline"] = cpu_baseline(cfg, store, args.seed, P)
+        except Exception as exc:  # the baseline is reported, never required
+            out["cpu_baseline"] = {"error": repr(exc)}
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

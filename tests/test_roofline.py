@@ -1,0 +1,55 @@
+"""Pins of the roofline arithmetic against the pages' printed figures and
+against the byte counts of the model shapes."""
+import json
+import os
+
+import pytest
+
+from persistent_decode_megakernel_amd import roofline as R
+from synth import configs
+
+GOLD = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "pages_roofline.json")))
+
+
+def test_pages_nvfp4_roofline():
+    g = GOLD["nvfp4_b200_roofline"]
+    v = R.roofline_tokens_per_s(g["bandwidth_bytes_per_s"], g["bytes_per_token"])
+    assert int(v) == g["printed_tokens_per_s"]
+
+
+def test_pages_mxfp8_roofline_rounds_to_printed():
+    g = GOLD["mxfp8_h200_roofline"]
+    v = R.roofline_tokens_per_s(g["bandwidth_bytes_per_s"], g["bytes_per_token"])
+    assert 900 < v < 1000 and round(v, -3) == g["printed_tokens_per_s_rounded"]
+
+
+def test_pages_interactivity_is_inverse_tpot():
+    g = GOLD["decode_tail_8k1k"]
+    v = R.interactivity(g["seconds"] / g["tokens"])
+    assert round(v) == g["printed_tokens_per_s"]
+    # 494.2 tok/s/user means a 2.02 ms time per output token
+    assert abs(1e3 / GOLD["interactivity_1k1k"]["printed_tokens_per_s"] - 2.0235) < 1e-3
+
+
+def test_stack_bytes_per_token():
+    cfg = configs.get("dsv3_stack_1k")
+    w = R.weight_bytes(cfg)
+    # attention per layer, dense FFN, 9 active experts + router, LM head
+    attn = 2112 * 7168 + 24576 * 1536 + 32768 * 512 + 7168 * 16384
+    assert attn == 187_105_280
+    assert w["fp8_codes"] + w["bf16"] == 11 * attn + 3 * 3 * 18432 * 7168 + 8 * (9 * 3 * 2048 * 7168 + 256 * 7168 * 2) + 129280 * 7168 * 2
+    assert w["fp8_codes"] + w["bf16"] == 8_300_855_296
+    assert w["block_scales"] == 784_080
+    # KV: 11 layers x ctx rows x 576 bf16
+    assert R.kv_bytes(cfg, 1025) == 11 * 1025 * 1152
+    mean = R.mean_bytes_per_token(cfg, 1024, 1024)
+    assert abs(mean / 1e9 - 8.3211) < 5e-4
+    mean8k = R.mean_bytes_per_token(configs.get("dsv3_stack_8k"), 8192, 1024)
+    assert abs(mean8k / 1e9 - 8.4119) < 5e-4
+
+
+def test_single_layer_bytes():
+    d = configs.get("dsv3_dense_layer")
+    m = configs.get("dsv3_moe_layer")
+    assert abs(R.bytes_per_token(d, 1025) / 1e6 - 584.7) < 0.1
+    assert abs(R.bytes_per_token(m, 1025) / 1e6 - 588.4) < 0.1
