@@ -116,7 +116,8 @@ def main():
         raise SystemExit(f"--steps and --warmup must be within 1..{cfg.decode_steps}")
     max_ctx = P + cfg.decode_steps
     log(f"workload {cfg.name}: {cfg.n_layers} layers, prompt {P}, {K} timed steps")
-    eng = Engine(cfg, max_ctx=max_ctx, device=0)
+    eng = Engine(cfg, max_ctx=max_ctx, device=0, trace=True)
+    eng.set_trace(False)
     log(f"buffers: weights {eng.sizes.weight_bytes / 1e9:.2f} GB, kv {eng.sizes.kv_bytes / 1e6:.1f} MB, "
         f"{eng.sizes.n_stages} stages, {eng.sizes.n_workgroups} workgroups")
     store = gen.LogicalWeights(cfg, args.seed, "cuda", cache=False)
@@ -176,6 +177,19 @@ def main():
     log(f"TPOT {tpot * 1e3:.3f} ms ({1 / tpot:.1f} tok/s/user), {achieved / 1e9:.0f} GB/s = "
         f"{achieved / R.HBM_PEAK_BYTES_PER_S * 100:.1f}% of 8 TB/s")
     traffic = load_traffic(cfg.name)
+    # a few traced steps after the timed region: per-stage spans and idle time
+    from persistent_decode_megakernel_amd import describe_plan, trace as T
+    plan = describe_plan(cfg, max_ctx, eng.sizes.n_workgroups)
+    fill_cache()
+    eng.set_trace(True)
+    sums = []
+    for j in range(4):
+        step(j)
+        eng.status()
+        sums.append(T.summarize(eng.taps()["trace"].cpu().numpy(), plan))
+    eng.set_trace(False)
+    best = min(sums, key=lambda x: x["total_us"])
+    log("traced step (per stage type):\n" + T.format_table(best))
     out = {
         "metric": "batch-1 decode tokens/s/user",
         "value": round(1.0 / tpot, 3),
@@ -207,6 +221,8 @@ def main():
                      "kernel": "pdm::engine_kernel (one launch per decode step)",
                      "algorithmic_bytes_per_launch": int(bytes_mean)},
     }
+    out["trace"] = {"idle_frac": round(best["idle_frac"], 4), "step_us": round(best["total_us"], 1),
+                    "by_type_us": {k: round(v["span_us"], 1) for k, v in T.by_type(best).items()}}
     if not args.no_cpu_baseline:
         try:
             out["cpu_baseline"] = cpu_baseline(cfg, store, args.seed, P)

@@ -264,6 +264,12 @@ int pdm_cache_length(const pdm_engine* e, int32_t* out);
  * skip signalling that stage, which must trip the watchdog. */
 int pdm_set_debug(pdm_engine* e, int32_t spin_limit, int32_t skip_signal_stage);
 
+/* Record per-stage timestamps (wall clock, 100 MHz on MI355X) of the
+ * following steps into the bound trace buffer: on != 0 enables, 0 disables.
+ * Requires a trace buffer at bind time. Records: [stage][workgroup] x
+ * {entered, dependency satisfied, signalled, epoch}. */
+int pdm_set_trace(pdm_engine* e, int32_t on);
+
 int pdm_destroy(pdm_engine* e);
 
 const char* pdm_strerror(int code);

@@ -81,6 +81,7 @@ _SIGS = {
     "pdm_get_taps": (C.c_int, [_P, C.POINTER(Taps)]),
     "pdm_cache_length": (C.c_int, [_P, C.POINTER(C.c_int32)]),
     "pdm_set_debug": (C.c_int, [_P, C.c_int32, C.c_int32]),
+    "pdm_set_trace": (C.c_int, [_P, C.c_int32]),
     "pdm_destroy": (C.c_int, [_P]),
     "pdm_strerror": (C.c_char_p, [C.c_int]),
 }

@@ -34,6 +34,7 @@ struct pdm_engine {
   int32_t spin_limit = 1 << 22;
   int32_t skip_stage = -1;
   bool cooperative = false;
+  bool trace_on = true;
 };
 
 namespace {
@@ -392,7 +393,7 @@ int pdm_decode_step(pdm_engine* e, int32_t token, int32_t pos, const uint16_t* x
   a.x_in = x_in_dev;
   a.logits = d.vocab > 0 ? logits_dev : nullptr;
   a.argmax = d.vocab > 0 ? argmax_dev : nullptr;
-  a.trace = e->trace;
+  a.trace = e->trace_on ? e->trace : nullptr;
   DeviceGuard g(e->device);
   hipError_t err = launch_engine(e->plan_dev, a, e->G, (hipStream_t)stream, e->cooperative);
   if (err != hipSuccess) return PDM_ERR_LAUNCH;
@@ -451,6 +452,13 @@ int pdm_set_debug(pdm_engine* e, int32_t spin_limit, int32_t skip_signal_stage) 
   if (!e || spin_limit < 0) return PDM_ERR_ARG;
   e->spin_limit = spin_limit > 0 ? spin_limit : kDefaultSpin;
   e->skip_stage = skip_signal_stage >= 0 ? skip_signal_stage : -1;
+  return PDM_OK;
+}
+
+int pdm_set_trace(pdm_engine* e, int32_t on) {
+  if (!e) return PDM_ERR_ARG;
+  if (on && !e->trace) return PDM_ERR_UNBOUND;
+  e->trace_on = on != 0;
   return PDM_OK;
 }
 

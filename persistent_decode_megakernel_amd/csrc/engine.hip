@@ -33,10 +33,38 @@ namespace {
 constexpr int kUnroll = 8;  // 1 KB units in flight per wave and buffer
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// Every device pointer of the plan is global memory. Accessing it through an
+// address_space(1) pointer makes the compiler emit global (not flat) memory
+// instructions, which only count against vmcnt; flat ones also count against
+// lgkmcnt and would make every LDS read wait for all weight loads in flight.
+#define GLOBAL_AS __attribute__((address_space(1)))
+template <class T>
+__device__ __forceinline__ const GLOBAL_AS T* gp(const T* p) { return (const GLOBAL_AS T*)p; }
+template <class T>
+__device__ __forceinline__ GLOBAL_AS T* gpw(T* p) { return (GLOBAL_AS T*)p; }
+template <class T>
+__device__ __forceinline__ T gld(const T* p) { return *gp(p); }
+// Copy a plan struct out of global memory word by word (C++ copy constructors
+// cannot bind address-space-qualified objects); unused words are dropped.
+template <class T>
+__device__ __forceinline__ T load_plan(const GLOBAL_AS T* p) {
+  static_assert(sizeof(T) % 4 == 0, "plan structs are word-sized");
+  T v;
+  const GLOBAL_AS uint32_t* src = reinterpret_cast<const GLOBAL_AS uint32_t*>(p);
+  uint32_t* dst = reinterpret_cast<uint32_t*>(&v);
+#pragma unroll
+  for (int i = 0; i < (int)(sizeof(T) / 4); ++i) dst[i] = src[i];
+  return v;
+}
+template <class T>
+__device__ __forceinline__ void gst(T* p, T v) { *gpw(p) = v; }
 
 struct __align__(16) Smem {
   float x[kXMax];                 // staged input vector(s) of the current stage
   float part[kWaves][kRowChunk];  // per-wave row partial sums
+  uint16_t sc[kScMax];            // block scales of the current row chunk
   const uint8_t* slot_codes[kMaxSlots];
   const uint16_t* slot_scales[kMaxSlots];
   float slot_w[kMaxSlots];
@@ -55,22 +83,22 @@ __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
 __device__ __forceinline__ float ld_coh(const float* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return __hip_atomic_load(gp(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ int ld_coh_i(const int* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return __hip_atomic_load(gp(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ uint32_t ld_coh_u(const uint32_t* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return __hip_atomic_load(gp(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ void st_coh(float* p, float v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(gpw(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ void st_coh_i(int* p, int v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(gpw(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ void st_coh_u(uint32_t* p, uint32_t v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(gpw(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Wait until every memory operation this thread issued has completed.
@@ -139,7 +167,7 @@ __device__ __forceinline__ float group_sum(float v, int gs) {
 }
 
 // block-wide sum (all 512 threads participate); result in every thread
-__device__ float block_sum(Smem& sm, float v) {
+__device__ __forceinline__ float block_sum(Smem& sm, float v) {
   float w = wave_sum(v);
   if (lane_id() == 0) sm.red[wave_id()] = w;
   __syncthreads();
@@ -155,7 +183,7 @@ __device__ __forceinline__ float silu(float g) { return g / (1.0f + __expf(-g));
 // ------------------------------------------------------------------ sync
 
 struct Ctx {
-  const Plan* P;
+  const GLOBAL_AS Plan* P;  // plan in global memory: uniform reads become scalar loads
   LaunchArgs A;
   int G;
   int wg;
@@ -166,8 +194,8 @@ __device__ __forceinline__ int* counter_ptr(const Ctx& c, int stage, int stripe)
 }
 __device__ __forceinline__ int stripe_count(int G, int stripe) { return (G - stripe + kStripes - 1) / kStripes; }
 
-__device__ void set_watchdog(const Ctx& c, int stage, int observed) {
-  unsigned long long* st = reinterpret_cast<unsigned long long*>(c.P->status);
+__device__ __noinline__ void set_watchdog(const Ctx& c, int stage, int observed) {
+  GLOBAL_AS unsigned long long* st = gpw(reinterpret_cast<unsigned long long*>(c.P->status));
   unsigned long long mine = ((unsigned long long)c.A.epoch << 32) | (unsigned)(-PDM_ERR_WATCHDOG);
   unsigned long long cur = __hip_atomic_load(st, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   if ((uint32_t)(cur >> 32) != c.A.epoch || (uint32_t)cur == 0u) {
@@ -183,7 +211,7 @@ __device__ void set_watchdog(const Ctx& c, int stage, int observed) {
 
 // Wait until stage `s` is complete in every workgroup. Returns false when the
 // step was aborted (watchdog). All threads of the workgroup must call it.
-__device__ bool wait_stage(const Ctx& c, Smem& sm, int s, int my_stage) {
+__device__ __forceinline__ bool wait_stage(const Ctx& c, Smem& sm, int s, int my_stage) {
   if (threadIdx.x == 0) {
     sm.abort = 0;
     if (c.A.trace) sm.t_enter = wall_clock64();
@@ -192,7 +220,7 @@ __device__ bool wait_stage(const Ctx& c, Smem& sm, int s, int my_stage) {
     const int lane = threadIdx.x;
     const int* ctr = counter_ptr(c, s, lane & (kStripes - 1));
     const int target = (int)c.A.epoch * stripe_count(c.G, lane & (kStripes - 1));
-    const unsigned long long* st = reinterpret_cast<const unsigned long long*>(c.P->status);
+    const GLOBAL_AS unsigned long long* st = gp(reinterpret_cast<const unsigned long long*>(c.P->status));
     const bool poll_ctr = lane < kStripes && lane < c.G;
     int spins = 0;
     while (true) {
@@ -219,14 +247,14 @@ __device__ bool wait_stage(const Ctx& c, Smem& sm, int s, int my_stage) {
   return sm.abort == 0;
 }
 
-__device__ void signal_stage(const Ctx& c, Smem& sm, int s) {
+__device__ __forceinline__ void signal_stage(const Ctx& c, Smem& sm, int s) {
   mem_done();
   __syncthreads();
   if (threadIdx.x == 0) {
     if (!(s == c.A.skip_stage && c.wg == 0))
-      __hip_atomic_fetch_add(counter_ptr(c, s, c.wg & (kStripes - 1)), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_fetch_add(gpw(counter_ptr(c, s, c.wg & (kStripes - 1))), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (c.A.trace) {
-      uint64_t* t = reinterpret_cast<uint64_t*>(c.A.trace) + ((size_t)s * c.G + c.wg) * kTraceWords;
+      GLOBAL_AS uint64_t* t = gpw(reinterpret_cast<uint64_t*>(c.A.trace) + ((size_t)s * c.G + c.wg) * kTraceWords);
       t[0] = sm.t_enter;
       t[1] = sm.t_ready;
       t[2] = wall_clock64();
@@ -304,19 +332,57 @@ __device__ __forceinline__ float unit_dot(const u32x4& w, const float* xs) {
   return acc;
 }
 
+// Scale table of rows [ra, rb) in LDS: sm.sc[((row >> 3) - (ra >> 3)) * nkbt + (b >> 7)],
+// nkbt = ceil(Kb / 128). The loads are issued here; the values are written to
+// LDS by store_scales() so that the caller can issue weight loads in between.
+constexpr int kScPerThread = (kScMax + kThreads - 1) / kThreads;
+
+template <int EB>
+__device__ __forceinline__ void load_scales(const Gemv& g, const Smem& sm, int ra, int rb, uint16_t* v) {
+  if constexpr (EB != 1) return;
+  const int nkbt = (g.Kb + 127) >> 7;
+  const int g0 = ra >> 3;
+  const int n = (((rb - 1) >> 3) - g0 + 1) * nkbt;
+#pragma unroll
+  for (int j = 0; j < kScPerThread; ++j) {
+    int i = threadIdx.x + j * kThreads;
+    v[j] = 0;
+    if (i < n) {
+      int gl = i / nkbt, kbi = i - gl * nkbt;
+      int row = max(ra, (g0 + gl) << 3);
+      const uint8_t* cp;
+      const uint16_t* sp = nullptr;
+      unit_ptr<1>(g, sm, row, kbi << 7, cp, sp);
+      v[j] = gld(sp);
+    }
+  }
+}
+
+template <int EB>
+__device__ __forceinline__ void store_scales(const Gemv& g, Smem& sm, int ra, int rb, const uint16_t* v) {
+  if constexpr (EB != 1) return;
+  const int nkbt = (g.Kb + 127) >> 7;
+  const int n = (((rb - 1) >> 3) - (ra >> 3) + 1) * nkbt;
+#pragma unroll
+  for (int j = 0; j < kScPerThread; ++j) {
+    int i = threadIdx.x + j * kThreads;
+    if (i < n) sm.sc[i] = v[j];
+  }
+}
+
 // Runs the units of rows [ra, rb) of a GEMV (ra, rb multiples of the unit
 // row count) split over the 8 waves; writes per-wave row partials to
-// sm.part[w][row - ra]. `prep` is called once by every wave after its first
-// batch of weight loads has been issued and before any input is used; it
-// must contain a workgroup barrier (it waits on the dependency and stages the
-// input). Returns false if prep reported an abort.
+// sm.part[w][row - ra]. A unit is one 16-byte load per lane: 1 KB of one row
+// (rows of 1 KB or more) or 1024 / Kb whole rows (shorter power-of-two rows).
+// `prep` is called once by every thread after the scale loads and the first
+// batch of weight loads have been issued (when `early`) and before any input
+// is used; it must end with a workgroup barrier. Returns false on abort.
 template <int EB, class Prep>
-__device__ bool gemv_rows(const Gemv& g, Smem& sm, int ra, int rb, bool call_prep, bool early, Prep&& prep) {
+__device__ __forceinline__ bool gemv_rows(const Gemv& g, Smem& sm, int ra, int rb, bool call_prep, bool early, Prep&& prep) {
   const int lane = lane_id();
   const int w = wave_id();
   const int kb = g.Kb;
   const bool small = kb < 1024 && (1024 % kb) == 0;
-  // units
   int S = 1, m = 1, lg_lpr = 0;
   int nunits;
   if (small) {
@@ -329,38 +395,40 @@ __device__ bool gemv_rows(const Gemv& g, Smem& sm, int ra, int rb, bool call_pre
   }
   const int u0 = (int)((int64_t)nunits * w / kWaves);
   const int u1 = (int)((int64_t)nunits * (w + 1) / kWaves);
+  const int nkbt = (kb + 127) >> 7;
+  const int g0 = ra >> 3;
+
+  // (row, segment) of unit u in the large-row mode, advanced incrementally
+  int i_row = 0, i_seg = 0;
+  if (!small) { i_row = u0 / S; i_seg = u0 - i_row * S; }
+  int c_row = i_row, c_seg = i_seg;
+
+  auto unit_of = [&](int u, int& row, int& b, int& r_it, int& s_it) {
+    if (small) {
+      row = ra + u * m + (lane >> lg_lpr);
+      b = (lane & ((1 << lg_lpr) - 1)) << 4;
+    } else {
+      row = ra + r_it;
+      b = (s_it << 10) + (lane << 4);
+      if (++s_it == S) { s_it = 0; ++r_it; }
+    }
+  };
 
   u32x4 wa[kUnroll], wb[kUnroll];
-  float sa[kUnroll], sb[kUnroll];
-  int ra_row[kUnroll], rb_row[kUnroll], ra_b[kUnroll], rb_b[kUnroll];
-
-  auto issue = [&](u32x4* W, float* Sc, int* R, int* B, int ub) {
+  auto issue = [&](u32x4* W, int ub) {
 #pragma unroll
     for (int j = 0; j < kUnroll; ++j) {
       int u = ub + j;
       int row, b;
-      if (small) {
-        row = ra + u * m + (lane >> lg_lpr);
-        b = (lane & ((1 << lg_lpr) - 1)) << 4;
-      } else {
-        int r = u / S;
-        row = ra + r;
-        b = ((u - r * S) << 10) + (lane << 4);
-      }
-      R[j] = row;
-      B[j] = b;
-      bool ok = u < u1 && b < kb;
+      unit_of(u, row, b, i_row, i_seg);
       u32x4 v = {0u, 0u, 0u, 0u};
-      float sc = 0.f;
-      if (ok) {
+      if (u < u1 && b < kb) {
         const uint8_t* cp;
         const uint16_t* sp = nullptr;
         unit_ptr<EB>(g, sm, row, b, cp, sp);
-        v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(cp));
-        if constexpr (EB == 1) sc = bf16_val(*sp);
+        v = __builtin_nontemporal_load(gp(reinterpret_cast<const u32x4*>(cp)));
       }
       W[j] = v;
-      Sc[j] = sc;
     }
   };
 
@@ -373,18 +441,20 @@ __device__ bool gemv_rows(const Gemv& g, Smem& sm, int ra, int rb, bool call_pre
     }
     acc = 0.f;
   };
-  auto compute = [&](const u32x4* W, const float* Sc, const int* R, const int* B, int ub) {
+  auto compute = [&](const u32x4* W, int ub) {
 #pragma unroll
     for (int j = 0; j < kUnroll; ++j) {
       int u = ub + j;
       if (u >= u1) break;
-      int row = R[j];
-      int b = B[j];
+      int row, b;
+      unit_of(u, row, b, c_row, c_seg);
       int k0 = (EB == 1) ? b : (b >> 1);
       int xoff = (g.lg_rpv >= 31) ? 0 : ((row >> g.lg_rpv) - g.vbase) * g.xK;
       float d = 0.f;
-      if (b < kb) d = unit_dot<EB>(W[j], sm.x + xoff + k0);
-      if constexpr (EB == 1) d *= Sc[j];
+      if (b < kb) {
+        d = unit_dot<EB>(W[j], sm.x + xoff + k0);
+        if constexpr (EB == 1) d *= bf16_val(sm.sc[((row >> 3) - g0) * nkbt + (b >> 7)]);
+      }
       if (small) {
         float t = group_sum(d, 1 << lg_lpr);
         if ((lane & ((1 << lg_lpr) - 1)) == 0) sm.part[w][row - ra] = t;
@@ -396,19 +466,30 @@ __device__ bool gemv_rows(const Gemv& g, Smem& sm, int ra, int rb, bool call_pre
     }
   };
 
-  // Weight addresses that do not depend on this step's data are issued before
-  // the dependency wait, so the loads are in flight while the wait spins.
-  if (early) issue(wa, sa, ra_row, ra_b, u0);
+  // Weight and scale addresses that do not depend on this step's data are
+  // issued before the dependency wait, so the loads are in flight while the
+  // wait spins.
+  uint16_t scv[kScPerThread];
+  if (early) {
+    load_scales<EB>(g, sm, ra, rb, scv);
+    issue(wa, u0);
+    store_scales<EB>(g, sm, ra, rb, scv);
+  }
   if (call_prep) {
     if (!prep()) return false;
   }
-  if (!early) issue(wa, sa, ra_row, ra_b, u0);
+  if (!early) {
+    load_scales<EB>(g, sm, ra, rb, scv);
+    issue(wa, u0);
+    store_scales<EB>(g, sm, ra, rb, scv);
+    __syncthreads();
+  }
   for (int ub = u0; ub < u1; ub += 2 * kUnroll) {
-    if (ub + kUnroll < u1) issue(wb, sb, rb_row, rb_b, ub + kUnroll);
-    compute(wa, sa, ra_row, ra_b, ub);
+    if (ub + kUnroll < u1) issue(wb, ub + kUnroll);
+    compute(wa, ub);
     if (ub + kUnroll >= u1) break;
-    if (ub + 2 * kUnroll < u1) issue(wa, sa, ra_row, ra_b, ub + 2 * kUnroll);
-    compute(wb, sb, rb_row, rb_b, ub + kUnroll);
+    if (ub + 2 * kUnroll < u1) issue(wa, ub + 2 * kUnroll);
+    compute(wb, ub + kUnroll);
   }
   if (!small) flush();
   return true;
@@ -436,25 +517,45 @@ __device__ __forceinline__ void zero_part(Smem& sm) {
   for (int i = threadIdx.x; i < kWaves * kRowChunk; i += kThreads) p[i] = 0.f;
 }
 
+// Copy K values get(k) into sm.x with all loads of a batch in flight at once
+// (a load-then-store loop would wait for each load in turn). Returns this
+// thread's sum of squares.
+constexpr int kStageBatch = 16;
+
+template <class Get>
+__device__ __forceinline__ float stage_values(Smem& sm, int K, Get&& get) {
+  float ss = 0.f;
+  for (int k0 = threadIdx.x; k0 < K; k0 += kStageBatch * kThreads) {
+    float v[kStageBatch];
+#pragma unroll
+    for (int i = 0; i < kStageBatch; ++i) {
+      int k = k0 + i * kThreads;
+      v[i] = k < K ? get(k) : 0.f;
+    }
+#pragma unroll
+    for (int i = 0; i < kStageBatch; ++i) {
+      int k = k0 + i * kThreads;
+      if (k < K) sm.x[k] = v[i];
+      ss += v[i] * v[i];
+    }
+  }
+  return ss;
+}
+
 // Stage an input vector with fused RMSNorm: x_lds[k] = v[k] * g[k] / sqrt(mean(v^2) + eps).
 // `get(k)` returns v[k]. Contains barriers; all threads call it.
 template <class Get>
-__device__ void stage_rmsnorm(Smem& sm, int K, const float* gain, float eps, Get&& get) {
-  float ss = 0.f;
-  for (int k = threadIdx.x; k < K; k += kThreads) {
-    float v = get(k);
-    sm.x[k] = v;
-    ss += v * v;
-  }
+__device__ __forceinline__ void stage_rmsnorm(Smem& sm, int K, const float* gain, float eps, Get&& get) {
+  float ss = stage_values(sm, K, get);
   float tot = block_sum(sm, ss);
   float rs = 1.0f / sqrtf(tot / (float)K + eps);
-  for (int k = threadIdx.x; k < K; k += kThreads) sm.x[k] = sm.x[k] * rs * gain[k];
+  for (int k = threadIdx.x; k < K; k += kThreads) sm.x[k] = sm.x[k] * rs * gld(gain + k);
   __syncthreads();
 }
 
 template <class Get>
-__device__ void stage_plain(Smem& sm, int K, Get&& get) {
-  for (int k = threadIdx.x; k < K; k += kThreads) sm.x[k] = get(k);
+__device__ __forceinline__ void stage_plain(Smem& sm, int K, Get&& get) {
+  stage_values(sm, K, get);
   __syncthreads();
 }
 
@@ -462,23 +563,35 @@ __device__ void stage_plain(Smem& sm, int K, Get&& get) {
 
 struct StageEnv {
   Ctx c;
-  const StagePlan* st;
+  StagePlan st;
   int s;
 };
 
-__device__ __forceinline__ const LayerPlan& layer_of(const Ctx& c, int l) { return c.P->layers[l]; }
+__device__ __forceinline__ LayerPlan layer_of(const Ctx& c, int l) { return load_plan(&c.P->layers[l]); }
 
-// input of layer l: embedding row / external hidden vector for l == 0, else previous layer output
-__device__ __forceinline__ float layer_input(const Ctx& c, int l, int k) {
-  if (l > 0) return ld_coh(reinterpret_cast<const float*>(layer_of(c, l - 1).xo) + k);
-  if (c.P->dims.vocab > 0) {
-    const uint16_t* e = reinterpret_cast<const uint16_t*>(c.P->embed) + (size_t)c.A.token * c.P->dims.hidden;
-    return bf16_val(e[k]);
+// Input of layer l: the embedding row or external hidden vector for l == 0,
+// else the previous layer's output (written this step: coherent loads).
+struct LayerInput {
+  const float* prev;     // previous layer output, or null
+  const uint16_t* bf16;  // embedding row / x_in
+  __device__ __forceinline__ float operator()(int k) const {
+    return prev ? ld_coh(prev + k) : bf16_val(gld(bf16 + k));
   }
-  return bf16_val(c.A.x_in[k]);
+};
+
+__device__ __forceinline__ LayerInput layer_input(const Ctx& c, int l) {
+  LayerInput in{nullptr, nullptr};
+  if (l > 0) {
+    in.prev = reinterpret_cast<const float*>(c.P->layers[l - 1].xo);
+  } else if (c.P->dims.vocab > 0) {
+    in.bf16 = reinterpret_cast<const uint16_t*>(c.P->embed) + (size_t)c.A.token * c.P->dims.hidden;
+  } else {
+    in.bf16 = c.A.x_in;
+  }
+  return in;
 }
 
-__device__ Gemv gemv_of(const Fp8Mat& m, const char* base_unused = nullptr) {
+__device__ __forceinline__ Gemv gemv_of(const Fp8Mat& m, const char* base_unused = nullptr) {
   (void)base_unused;
   Gemv g{};
   g.codes = reinterpret_cast<const uint8_t*>(m.codes);
@@ -494,19 +607,30 @@ __device__ Gemv gemv_of(const Fp8Mat& m, const char* base_unused = nullptr) {
 // `prep` (wait + staging) runs before the first chunk; `epi(ra_chunk, n)`
 // consumes part[0][0..n) after combine.
 template <int EB, class Prep, class Epi>
-__device__ bool run_gemv(const StageEnv& E, Smem& sm, const Gemv& g, int ra, int rb, bool early, Prep&& prep, Epi&& epi) {
-  bool first = true;
+__device__ __forceinline__ bool run_gemv(const StageEnv& E, Smem& sm, const Gemv& g, int ra, int rb, bool early,
+                                         Prep&& prep, Epi&& epi) {
   if (ra >= rb) {
     // no rows: still take part in the dependency wait so barriers match
     return prep();
   }
+  bool first = true;
   for (int ca = ra; ca < rb; ca += kRowChunk) {
     int cb = min(rb, ca + kRowChunk);
-    if (!first) { zero_part(sm); __syncthreads(); }
-    bool ok = gemv_rows<EB>(g, sm, ca, cb, first, early, [&]() {
+    bool ok;
+    if (first) {
+      ok = gemv_rows<EB>(g, sm, ca, cb, true, early, [&]() {
+        zero_part(sm);
+        return prep();
+      });
+    } else {
       zero_part(sm);
-      return prep();
-    });
+      // the early path stores the scale table before the barrier in prep;
+      // later chunks need it (and the zeroed partials) visible before use
+      ok = gemv_rows<EB>(g, sm, ca, cb, true, true, [&]() {
+        __syncthreads();
+        return true;
+      });
+    }
     if (!ok) return false;
     first = false;
     __syncthreads();
@@ -519,23 +643,23 @@ __device__ bool run_gemv(const StageEnv& E, Smem& sm, const Gemv& g, int ra, int
 }
 
 // --- QKV: [W_DQ ; W_DKV] * RMSNorm(x)
-__device__ bool stage_qkv(const StageEnv& E, Smem& sm) {
+__device__ __forceinline__ bool stage_qkv(const StageEnv& E, Smem& sm) {
   const Ctx& c = E.c;
-  const int l = E.st->layer;
-  const LayerPlan& L = layer_of(c, l);
+  const int l = E.st.layer;
+  const LayerPlan L = layer_of(c, l);
   const int D = c.P->dims.hidden;
   Gemv g = gemv_of(L.qkv);
   int ra, rb;
-  my_rows(E.st->rows, E.st->gran, c.G, c.wg, ra, rb);
+  my_rows(E.st.rows, E.st.gran, c.G, c.wg, ra, rb);
   float* out = reinterpret_cast<float*>(L.qkv_raw);
   return run_gemv<1>(E, sm, g, ra, rb, true,
       [&]() {
-        if (!wait_stage(c, sm, E.st->wait, E.s)) return false;
-        stage_rmsnorm(sm, D, reinterpret_cast<const float*>(L.attn_norm), c.P->dims.rms_eps,
-                      [&](int k) { return layer_input(c, l, k); });
+        if (!wait_stage(c, sm, E.st.wait, E.s)) return false;
+        const LayerInput in = layer_input(c, l);
+        stage_rmsnorm(sm, D, reinterpret_cast<const float*>(L.attn_norm), c.P->dims.rms_eps, in);
         if (l == 0 && c.wg == 0) {
           float* x0 = reinterpret_cast<float*>(c.P->x0);
-          for (int k = threadIdx.x; k < D; k += kThreads) st_coh(x0 + k, layer_input(c, 0, k));
+          for (int k = threadIdx.x; k < D; k += kThreads) st_coh(x0 + k, in(k));
         }
         return true;
       },
@@ -545,21 +669,21 @@ __device__ bool stage_qkv(const StageEnv& E, Smem& sm) {
 }
 
 // --- QB: W_UQ * RMSNorm(c_q) with RoPE on the rotary rows; the last workgroup appends the cache row
-__device__ bool stage_qb(const StageEnv& E, Smem& sm) {
+__device__ __forceinline__ bool stage_qb(const StageEnv& E, Smem& sm) {
   const Ctx& c = E.c;
-  const pdm_dims& d = c.P->dims;
-  const int l = E.st->layer;
-  const LayerPlan& L = layer_of(c, l);
+  const pdm_dims d = load_plan(&c.P->dims);
+  const int l = E.st.layer;
+  const LayerPlan L = layer_of(c, l);
   const float* raw = reinterpret_cast<const float*>(L.qkv_raw);
   const float* tab = reinterpret_cast<const float*>(c.P->rope_tab) + (size_t)c.A.pos * d.rope;  // (cos, sin) pairs
   const int qkh = d.qk_nope + d.rope;
   Gemv g = gemv_of(L.qb);
   int ra, rb;
-  my_rows(E.st->rows, E.st->gran, c.G, c.wg, ra, rb);
+  my_rows(E.st.rows, E.st.gran, c.G, c.wg, ra, rb);
   float* out = reinterpret_cast<float*>(L.q);
   bool ok = run_gemv<1>(E, sm, g, ra, rb, true,
       [&]() {
-        if (!wait_stage(c, sm, E.st->wait, E.s)) return false;
+        if (!wait_stage(c, sm, E.st.wait, E.s)) return false;
         stage_rmsnorm(sm, d.q_lora, reinterpret_cast<const float*>(L.q_norm), d.rms_eps,
                       [&](int k) { return ld_coh(raw + k); });
         return true;
@@ -571,7 +695,7 @@ __device__ bool stage_qb(const StageEnv& E, Smem& sm) {
           float y = sm.part[0][t];
           if (j >= d.qk_nope) {
             int i = (j - d.qk_nope) >> 1;
-            float cs = tab[2 * i], sn = tab[2 * i + 1];
+            float cs = gld(tab + 2 * i), sn = gld(tab + 2 * i + 1);
             float other = sm.part[0][t ^ 1];
             y = (j - d.qk_nope) & 1 ? other * sn + y * cs : y * cs - other * sn;
           }
@@ -593,12 +717,12 @@ __device__ bool stage_qb(const StageEnv& E, Smem& sm) {
       float a, b;
       int k = 2 * p;
       if (k < d.kv_lora) {
-        a = ld_coh(kvr + k) * rs * gk[k];
-        b = ld_coh(kvr + k + 1) * rs * gk[k + 1];
+        a = ld_coh(kvr + k) * rs * gld(gk + k);
+        b = ld_coh(kvr + k + 1) * rs * gld(gk + k + 1);
       } else {
         int i = (k - d.kv_lora) >> 1;
         float x0 = ld_coh(kvr + k), x1 = ld_coh(kvr + k + 1);
-        float cs = tab[2 * i], sn = tab[2 * i + 1];
+        float cs = gld(tab + 2 * i), sn = gld(tab + 2 * i + 1);
         a = x0 * cs - x1 * sn;
         b = x0 * sn + x1 * cs;
       }
@@ -609,22 +733,22 @@ __device__ bool stage_qb(const StageEnv& E, Smem& sm) {
 }
 
 // --- ABSORB: q_lat[h] = W_UK[h]^T q_nope[h]  (rows (h, c), K = d_n, per-head input)
-__device__ bool stage_absorb(const StageEnv& E, Smem& sm) {
+__device__ __forceinline__ bool stage_absorb(const StageEnv& E, Smem& sm) {
   const Ctx& c = E.c;
-  const pdm_dims& d = c.P->dims;
-  const LayerPlan& L = layer_of(c, E.st->layer);
+  const pdm_dims d = load_plan(&c.P->dims);
+  const LayerPlan L = layer_of(c, E.st.layer);
   const int qkh = d.qk_nope + d.rope;
   const float* q = reinterpret_cast<const float*>(L.q);
   Gemv g = gemv_of(L.ukT);
   int ra, rb;
-  my_rows(E.st->rows, E.st->gran, c.G, c.wg, ra, rb);
+  my_rows(E.st.rows, E.st.gran, c.G, c.wg, ra, rb);
   g.lg_rpv = 31 - __builtin_clz(d.kv_lora);
   g.vbase = ra / d.kv_lora;
   g.xK = d.qk_nope;
   float* out = reinterpret_cast<float*>(L.ql);
   return run_gemv<1>(E, sm, g, ra, rb, true,
       [&]() {
-        if (!wait_stage(c, sm, E.st->wait, E.s)) return false;
+        if (!wait_stage(c, sm, E.st.wait, E.s)) return false;
         int h0 = ra / d.kv_lora, h1 = (rb - 1) / d.kv_lora;
         int n = (h1 - h0 + 1) * d.qk_nope;
         stage_plain(sm, n, [&](int k) {
@@ -640,10 +764,10 @@ __device__ bool stage_absorb(const StageEnv& E, Smem& sm) {
 
 // --- ATTN: split-KV MLA attention partials (m, l, acc) per (head, position chunk)
 template <int DPL>
-__device__ bool stage_attn(const StageEnv& E, Smem& sm) {
+__device__ __forceinline__ bool stage_attn(const StageEnv& E, Smem& sm) {
   const Ctx& c = E.c;
-  const pdm_dims& d = c.P->dims;
-  const LayerPlan& L = layer_of(c, E.st->layer);
+  const pdm_dims d = load_plan(&c.P->dims);
+  const LayerPlan L = layer_of(c, E.st.layer);
   const int nch = c.P->nch, hg = c.P->hg;
   const int units = c.P->n_hg * nch;
   if (c.wg >= units) return wait_stage(c, sm, -1, E.s);  // no share of this stage
@@ -654,18 +778,18 @@ __device__ bool stage_attn(const StageEnv& E, Smem& sm) {
   const int dc = d.kv_lora, dr = d.rope, kvr = dc + dr;
   const int qkh = d.qk_nope + d.rope;
   const float tau = 1.0f / sqrtf((float)qkh);
-  if (!wait_stage(c, sm, E.st->wait, E.s)) return false;
+  if (!wait_stage(c, sm, E.st.wait, E.s)) return false;
   // stage q (scaled by tau): per head [q_lat (dc) ; q_rope (dr)], and the current row
   float* qs = sm.x;                      // [hg][kvr]
   float* cur = sm.x + hg * kvr;          // [kvr]
   const float* ql = reinterpret_cast<const float*>(L.ql);
   const float* qf = reinterpret_cast<const float*>(L.q);
-  for (int i = threadIdx.x; i < hg * kvr; i += kThreads) {
-    int hh = i / kvr, k = i % kvr;
+  stage_values(sm, hg * kvr, [&](int i) {
+    int hh = i / kvr, k = i - hh * kvr;
     int h = grp * hg + hh;
     float v = k < dc ? ld_coh(ql + (size_t)h * dc + k) : ld_coh(qf + (size_t)h * qkh + d.qk_nope + (k - dc));
-    qs[i] = v * tau;
-  }
+    return v * tau;
+  });
   const uint16_t* cache = reinterpret_cast<const uint16_t*>(L.kv);
   const bool has_cur = pos >= t0 && pos < t1;
   if (has_cur) {
@@ -694,11 +818,11 @@ __device__ bool stage_attn(const StageEnv& E, Smem& sm) {
     const int t = tb + lane;
     const bool valid = t < tmain;
     float s[HPW_MAX] = {0.f, 0.f};
-    const uint4* rp = reinterpret_cast<const uint4*>(cache + (size_t)(valid ? t : t0) * kvr);
+    const u32x4* rp = reinterpret_cast<const u32x4*>(cache + (size_t)(valid ? t : t0) * kvr);
     // latent part: dc/8 loads of 8 bf16
 #pragma unroll 4
     for (int q8 = 0; q8 < kvr / 8; ++q8) {
-      uint4 v = rp[q8];
+      u32x4 v = gld(rp + q8);
       float f[8] = {bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y),
                     bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w)};
 #pragma unroll
@@ -730,14 +854,14 @@ __device__ bool stage_attn(const StageEnv& E, Smem& sm) {
       const uint16_t* r = cache + (size_t)(tb + j) * kvr + lane * DPL;
       float cv[DPL];
       if constexpr (DPL == 8) {
-        uint4 v = *reinterpret_cast<const uint4*>(r);
+        u32x4 v = gld(reinterpret_cast<const u32x4*>(r));
         cv[0] = bf16_lo(v.x); cv[1] = bf16_hi(v.x); cv[2] = bf16_lo(v.y); cv[3] = bf16_hi(v.y);
         cv[4] = bf16_lo(v.z); cv[5] = bf16_hi(v.z); cv[6] = bf16_lo(v.w); cv[7] = bf16_hi(v.w);
       } else if constexpr (DPL == 4) {
-        uint2 v = *reinterpret_cast<const uint2*>(r);
+        u32x2 v = gld(reinterpret_cast<const u32x2*>(r));
         cv[0] = bf16_lo(v.x); cv[1] = bf16_hi(v.x); cv[2] = bf16_lo(v.y); cv[3] = bf16_hi(v.y);
       } else {
-        uint32_t v = *reinterpret_cast<const uint32_t*>(r);
+        uint32_t v = gld(reinterpret_cast<const uint32_t*>(r));
         cv[0] = bf16_lo(v); cv[1] = bf16_hi(v);
       }
 #pragma unroll
@@ -783,24 +907,24 @@ __device__ bool stage_attn(const StageEnv& E, Smem& sm) {
 }
 
 // --- UV: merge the attention partials of each head, o[h] = W_UV[h] o_lat[h]
-__device__ bool stage_uv(const StageEnv& E, Smem& sm) {
+__device__ __forceinline__ bool stage_uv(const StageEnv& E, Smem& sm) {
   const Ctx& c = E.c;
-  const pdm_dims& d = c.P->dims;
-  const LayerPlan& L = layer_of(c, E.st->layer);
+  const pdm_dims d = load_plan(&c.P->dims);
+  const LayerPlan L = layer_of(c, E.st.layer);
   const int nch = c.P->nch, dc = d.kv_lora;
   const float* part = reinterpret_cast<const float*>(L.attn_part);
   Gemv g = gemv_of(L.uv);
   int ra, rb;
-  my_rows(E.st->rows, E.st->gran, c.G, c.wg, ra, rb);
+  my_rows(E.st.rows, E.st.gran, c.G, c.wg, ra, rb);
   g.lg_rpv = 31 - __builtin_clz(d.v_head);
   g.vbase = ra / d.v_head;
   g.xK = dc;
   float* out = reinterpret_cast<float*>(L.o);
   return run_gemv<1>(E, sm, g, ra, rb, true,
       [&]() {
-        if (!wait_stage(c, sm, E.st->wait, E.s)) return false;
+        if (!wait_stage(c, sm, E.st.wait, E.s)) return false;
         int h0 = ra / d.v_head, h1 = (rb - 1) / d.v_head;
-        float* fac = sm.x + kXMax - 2 * kRowChunk;  // per-chunk max, then merge weights
+        float* fac = sm.x + kXMax - 2 * kRowChunk;  // per-chunk max and sum, then merge weights
         for (int h = h0; h <= h1; ++h) {
           const float* ph = part + (size_t)h * nch * (dc + 2);
           for (int i = threadIdx.x; i < nch; i += kThreads) {
@@ -817,7 +941,15 @@ __device__ bool stage_uv(const StageEnv& E, Smem& sm) {
           __syncthreads();
           for (int k = threadIdx.x; k < dc; k += kThreads) {
             float num = 0.f;
-            for (int i = 0; i < nch; ++i) num += ld_coh(ph + (size_t)i * (dc + 2) + k) * fac[i];
+            for (int i0 = 0; i0 < nch; i0 += kStageBatch) {
+              float v[kStageBatch];
+#pragma unroll
+              for (int b = 0; b < kStageBatch; ++b)
+                v[b] = i0 + b < nch ? ld_coh(ph + (size_t)(i0 + b) * (dc + 2) + k) : 0.f;
+#pragma unroll
+              for (int b = 0; b < kStageBatch; ++b)
+                if (i0 + b < nch) num += v[b] * fac[i0 + b];
+            }
             sm.x[(h - h0) * dc + k] = num;
           }
           __syncthreads();
@@ -830,43 +962,44 @@ __device__ bool stage_uv(const StageEnv& E, Smem& sm) {
 }
 
 // --- WO: x_attn = x + W_O o
-__device__ bool stage_wo(const StageEnv& E, Smem& sm) {
+__device__ __forceinline__ bool stage_wo(const StageEnv& E, Smem& sm) {
   const Ctx& c = E.c;
-  const pdm_dims& d = c.P->dims;
-  const int l = E.st->layer;
-  const LayerPlan& L = layer_of(c, l);
+  const pdm_dims d = load_plan(&c.P->dims);
+  const int l = E.st.layer;
+  const LayerPlan L = layer_of(c, l);
   const float* o = reinterpret_cast<const float*>(L.o);
   Gemv g = gemv_of(L.wo);
   int ra, rb;
-  my_rows(E.st->rows, E.st->gran, c.G, c.wg, ra, rb);
+  my_rows(E.st.rows, E.st.gran, c.G, c.wg, ra, rb);
   float* out = reinterpret_cast<float*>(L.xa);
   return run_gemv<1>(E, sm, g, ra, rb, true,
       [&]() {
-        if (!wait_stage(c, sm, E.st->wait, E.s)) return false;
+        if (!wait_stage(c, sm, E.st.wait, E.s)) return false;
         stage_plain(sm, d.n_heads * d.v_head, [&](int k) { return ld_coh(o + k); });
         return true;
       },
       [&](int ca, int n) {
-        for (int t = threadIdx.x; t < n; t += kThreads) st_coh(out + ca + t, layer_input(c, l, ca + t) + sm.part[0][t]);
+        const LayerInput in = layer_input(c, l);
+        for (int t = threadIdx.x; t < n; t += kThreads) st_coh(out + ca + t, in(ca + t) + sm.part[0][t]);
       });
 }
 
 // --- ROUTER: z = W_r * RMSNorm(x_attn)   (bf16 weights)
-__device__ bool stage_router(const StageEnv& E, Smem& sm) {
+__device__ __forceinline__ bool stage_router(const StageEnv& E, Smem& sm) {
   const Ctx& c = E.c;
-  const pdm_dims& d = c.P->dims;
-  const LayerPlan& L = layer_of(c, E.st->layer);
+  const pdm_dims d = load_plan(&c.P->dims);
+  const LayerPlan L = layer_of(c, E.st.layer);
   const float* xa = reinterpret_cast<const float*>(L.xa);
   Gemv g{};
   g.codes = reinterpret_cast<const uint8_t*>(L.router);
   g.Kb = d.hidden * 2;
   g.lg_rpv = 31;
   int ra, rb;
-  my_rows(E.st->rows, E.st->gran, c.G, c.wg, ra, rb);
+  my_rows(E.st.rows, E.st.gran, c.G, c.wg, ra, rb);
   float* out = reinterpret_cast<float*>(L.router_logits);
   return run_gemv<2>(E, sm, g, ra, rb, true,
       [&]() {
-        if (!wait_stage(c, sm, E.st->wait, E.s)) return false;
+        if (!wait_stage(c, sm, E.st.wait, E.s)) return false;
         stage_rmsnorm(sm, d.hidden, reinterpret_cast<const float*>(L.ffn_norm), d.rms_eps,
                       [&](int k) { return ld_coh(xa + k); });
         return true;
@@ -879,8 +1012,8 @@ __device__ bool stage_router(const StageEnv& E, Smem& sm) {
 // Top-k of the router logits by one wave (ties to the lower index), written to
 // the slot tables with sigmoid weights normalised over the chosen experts.
 // Must be called by all threads; contains barriers.
-__device__ void route_topk(const Ctx& c, Smem& sm, const LayerPlan& L, bool write_tap) {
-  const pdm_dims& d = c.P->dims;
+__device__ __forceinline__ void route_topk(const Ctx& c, Smem& sm, const LayerPlan& L, bool write_tap) {
+  const pdm_dims d = load_plan(&c.P->dims);
   const float* z = reinterpret_cast<const float*>(L.router_logits);
   const int E = d.n_experts, k = d.top_k;
   if (threadIdx.x < 64) {
@@ -922,14 +1055,14 @@ __device__ void route_topk(const Ctx& c, Smem& sm, const LayerPlan& L, bool writ
   }
   __syncthreads();
   if (write_tap && threadIdx.x < k) {
-    reinterpret_cast<int*>(L.topk_idx)[threadIdx.x] = sm.route_idx[threadIdx.x];
-    reinterpret_cast<float*>(L.topk_w)[threadIdx.x] = sm.route_w[threadIdx.x];
+    gst(reinterpret_cast<int*>(L.topk_idx) + threadIdx.x, sm.route_idx[threadIdx.x]);
+    gst(reinterpret_cast<float*>(L.topk_w) + threadIdx.x, sm.route_w[threadIdx.x]);
   }
 }
 
 // Slot tables of an MoE stage: expert block pointers (gate/up or down part),
 // weights and act offsets. Routed slots use the layer's top-k in LDS.
-__device__ void set_slots(const pdm_dims& d, const LayerPlan& L, Smem& sm, bool routed, bool down) {
+__device__ __forceinline__ void set_slots(const pdm_dims& d, const LayerPlan& L, Smem& sm, bool routed, bool down) {
   const int t = threadIdx.x;
   const int n = down ? d.top_k + d.n_shared : (routed ? d.top_k : d.n_shared);
   if (t < n) {
@@ -958,10 +1091,10 @@ __device__ void set_slots(const pdm_dims& d, const LayerPlan& L, Smem& sm, bool 
 }
 
 // --- GU: SwiGLU gate/up of dense FFN, shared experts, or routed experts
-__device__ bool stage_gu(const StageEnv& E, Smem& sm, bool routed) {
+__device__ __forceinline__ bool stage_gu(const StageEnv& E, Smem& sm, bool routed) {
   const Ctx& c = E.c;
-  const pdm_dims& d = c.P->dims;
-  const LayerPlan& L = layer_of(c, E.st->layer);
+  const pdm_dims d = load_plan(&c.P->dims);
+  const LayerPlan L = layer_of(c, E.st.layer);
   const float* xa = reinterpret_cast<const float*>(L.xa);
   float* act = reinterpret_cast<float*>(L.act);
   Gemv g{};
@@ -979,7 +1112,7 @@ __device__ bool stage_gu(const StageEnv& E, Smem& sm, bool routed) {
     F = d.moe_ffn;
   }
   int ra, rb;
-  my_rows(E.st->rows, E.st->gran, c.G, c.wg, ra, rb);
+  my_rows(E.st.rows, E.st.gran, c.G, c.wg, ra, rb);
   // shared-expert and dense pointers are static: set them before the early
   // weight loads; routed pointers need the router output (after the wait)
   if (L.is_moe && !routed) {
@@ -988,7 +1121,7 @@ __device__ bool stage_gu(const StageEnv& E, Smem& sm, bool routed) {
   }
   return run_gemv<1>(E, sm, g, ra, rb, !routed,
       [&]() {
-        if (!wait_stage(c, sm, E.st->wait, E.s)) return false;
+        if (!wait_stage(c, sm, E.st.wait, E.s)) return false;
         if (routed) {
           route_topk(c, sm, L, c.wg == 0);
           set_slots(d, L, sm, true, false);
@@ -1019,10 +1152,10 @@ __device__ bool stage_gu(const StageEnv& E, Smem& sm, bool routed) {
 }
 
 // --- DOWN: x_out = bf16(x_attn + sum_slots W_down[slot] act[slot])
-__device__ bool stage_down(const StageEnv& E, Smem& sm) {
+__device__ __forceinline__ bool stage_down(const StageEnv& E, Smem& sm) {
   const Ctx& c = E.c;
-  const pdm_dims& d = c.P->dims;
-  const LayerPlan& L = layer_of(c, E.st->layer);
+  const pdm_dims d = load_plan(&c.P->dims);
+  const LayerPlan L = layer_of(c, E.st.layer);
   const float* xa = reinterpret_cast<const float*>(L.xa);
   const float* act = reinterpret_cast<const float*>(L.act);
   float* out = reinterpret_cast<float*>(L.xo);
@@ -1041,7 +1174,7 @@ __device__ bool stage_down(const StageEnv& E, Smem& sm) {
     g.lg_rpv = 31;
   }
   int ra, rb;
-  my_rows(E.st->rows, E.st->gran, c.G, c.wg, ra, rb);
+  my_rows(E.st.rows, E.st.gran, c.G, c.wg, ra, rb);
   // the layer's routing is already in LDS (set by the routed gate/up stage)
   if (L.is_moe) {
     set_slots(d, L, sm, true, true);
@@ -1049,7 +1182,7 @@ __device__ bool stage_down(const StageEnv& E, Smem& sm) {
   }
   return run_gemv<1>(E, sm, g, ra, rb, true,
       [&]() {
-        if (!wait_stage(c, sm, E.st->wait, E.s)) return false;
+        if (!wait_stage(c, sm, E.st.wait, E.s)) return false;
         stage_plain(sm, K, [&](int k) { return ld_coh(act + k); });
         return true;
       },
@@ -1060,9 +1193,9 @@ __device__ bool stage_down(const StageEnv& E, Smem& sm) {
 }
 
 // --- LM: logits = W_lm * RMSNorm(x), argmax over the vocabulary
-__device__ bool stage_lm(const StageEnv& E, Smem& sm) {
+__device__ __forceinline__ bool stage_lm(const StageEnv& E, Smem& sm) {
   const Ctx& c = E.c;
-  const pdm_dims& d = c.P->dims;
+  const pdm_dims d = load_plan(&c.P->dims);
   const float* x = reinterpret_cast<const float*>(layer_of(c, d.n_layers - 1).xo);
   float* logits = c.A.logits ? c.A.logits : reinterpret_cast<float*>(c.P->logits_internal);
   Gemv g{};
@@ -1070,12 +1203,12 @@ __device__ bool stage_lm(const StageEnv& E, Smem& sm) {
   g.Kb = d.hidden * 2;
   g.lg_rpv = 31;
   int ra, rb;
-  my_rows(E.st->rows, E.st->gran, c.G, c.wg, ra, rb);
+  my_rows(E.st.rows, E.st.gran, c.G, c.wg, ra, rb);
   float bestv = -INFINITY;
   int besti = 0x7fffffff;
   bool ok = run_gemv<2>(E, sm, g, ra, rb, true,
       [&]() {
-        if (!wait_stage(c, sm, E.st->wait, E.s)) return false;
+        if (!wait_stage(c, sm, E.st.wait, E.s)) return false;
         stage_rmsnorm(sm, d.hidden, reinterpret_cast<const float*>(c.P->final_norm), d.rms_eps,
                       [&](int k) { return ld_coh(x + k); });
         return true;
@@ -1083,7 +1216,7 @@ __device__ bool stage_lm(const StageEnv& E, Smem& sm) {
       [&](int ca, int n) {
         for (int t = threadIdx.x; t < n; t += kThreads) {
           float v = sm.part[0][t];
-          logits[ca + t] = v;
+          gst(logits + ca + t, v);
           if (v > bestv || (v == bestv && ca + t < besti)) { bestv = v; besti = ca + t; }
         }
       });
@@ -1105,7 +1238,7 @@ __device__ bool stage_lm(const StageEnv& E, Smem& sm) {
     mem_done();
     // the last workgroup to arrive reduces the per-workgroup maxima
     int* done = counter_ptr(c, c.P->n_stages, 0);
-    int old = __hip_atomic_fetch_add(done, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    int old = __hip_atomic_fetch_add(gpw(done), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (old == (int)c.A.epoch * c.G - 1) {
       float bv = -INFINITY;
       int bi = 0x7fffffff;
@@ -1115,7 +1248,7 @@ __device__ bool stage_lm(const StageEnv& E, Smem& sm) {
         int i = ld_coh_i(reinterpret_cast<const int*>(bw + 1));
         if (v > bv || (v == bv && i < bi)) { bv = v; bi = i; }
       }
-      if (c.A.argmax) *c.A.argmax = bi;
+      if (c.A.argmax) gst(c.A.argmax, bi);
     }
   }
   return true;
@@ -1126,16 +1259,16 @@ __device__ bool stage_lm(const StageEnv& E, Smem& sm) {
 __global__ void __launch_bounds__(kThreads, 1) engine_kernel(const Plan* __restrict__ P, LaunchArgs A) {
   __shared__ Smem sm;
   Ctx c;
-  c.P = P;
+  c.P = (const GLOBAL_AS Plan*)P;
   c.A = A;
-  c.G = P->G;
+  c.G = c.P->G;
   c.wg = blockIdx.x;
-  const int n = P->n_stages;
-  const int dpl = P->dims.kv_lora / 64;
+  const int n = c.P->n_stages;
+  const int dpl = c.P->dims.kv_lora / 64;
   for (int s = 0; s < n; ++s) {
-    StageEnv E{c, &P->stages[s], s};
+    StageEnv E{c, load_plan(&c.P->stages[s]), s};
     bool ok;
-    switch (P->stages[s].type) {
+    switch (E.st.type) {
       case PDM_ST_QKV: ok = stage_qkv(E, sm); break;
       case PDM_ST_QB: ok = stage_qb(E, sm); break;
       case PDM_ST_ABSORB: ok = stage_absorb(E, sm); break;

@@ -17,9 +17,10 @@ constexpr int kThreads = 512;         // 8 waves of 64 lanes per workgroup
 constexpr int kWaves = kThreads / 64;
 constexpr int kStripes = 16;          // arrival counters per stage
 constexpr int kCounterStride = 32;    // ints between counters (128 B)
-constexpr int kRowChunk = 512;        // rows combined per LDS pass
-constexpr int kXMax = 24576;          // floats of staged activation per workgroup (96 KB)
+constexpr int kRowChunk = 256;        // rows combined per LDS pass
+constexpr int kXMax = 32768;          // floats of staged activation per workgroup (128 KB)
 constexpr int kMaxSlots = 16;         // expert slots of one MoE stage
+constexpr int kScMax = 5120;          // LDS block-scale entries of one GEMV row chunk
 constexpr int kMaxStages = PDM_MAX_LAYERS * 12 + 4;
 constexpr int kHeadGroup = 16;        // attention heads per work unit (at most)
 constexpr uint32_t kMagic = 0x57444d50u;  // "PDMW"

@@ -127,6 +127,9 @@ class Engine:
     def set_debug(self, spin_limit: int = 0, skip_signal_stage: int = -1):
         L.check("pdm_set_debug", self.lib.pdm_set_debug(self.h, spin_limit, skip_signal_stage))
 
+    def set_trace(self, on: bool):
+        L.check("pdm_set_trace", self.lib.pdm_set_trace(self.h, 1 if on else 0))
+
     def taps(self) -> dict:
         """Views of the last step's taps inside the scratch buffer."""
         t = L.Taps()

@@ -1,0 +1,60 @@
+"""Per-stage timing from the engine's in-kernel trace records.
+
+A monolithic persistent kernel hides per-operator time from kernel-level
+profilers (SemiAnalysis TileRT page, challenges section). The engine
+therefore records, for every stage and workgroup, when the workgroup entered
+the stage, when its dependency wait ended and when it signalled completion
+(wall clock, 100 MHz). This module turns those records into per-stage spans,
+work and wait times and the idle fraction of the step.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+WALLCLOCK_HZ = 100e6
+
+
+def summarize(trace: np.ndarray, plan: list, hz: float = WALLCLOCK_HZ) -> dict:
+    """trace: int64 [n_stages, n_workgroups, 4] of one step; plan: describe_plan() list."""
+    t = trace.astype(np.float64)
+    enter, ready, done = t[:, :, 0], t[:, :, 1], t[:, :, 2]
+    t0 = enter.min()
+    us = 1e6 / hz
+    rows = []
+    prev_end = t0
+    for s, st in enumerate(plan):
+        start, end = enter[s].min(), done[s].max()
+        work = (done[s] - ready[s]) * us
+        wait = (ready[s] - enter[s]) * us
+        span = (end - prev_end) * us  # critical-path increment of this stage
+        rows.append({
+            "stage": s, "type": st["type"], "layer": st["layer"], "weight_bytes": st["weight_bytes"],
+            "end_us": (end - t0) * us, "span_us": span, "work_us_mean": float(work.mean()),
+            "work_us_max": float(work.max()), "wait_us_mean": float(wait.mean()),
+            "GBps": st["weight_bytes"] / max(span, 1e-3) / 1e3 if st["weight_bytes"] else 0.0,
+        })
+        prev_end = max(prev_end, end)
+    total = (done.max() - t0) * us
+    busy = ((done - ready) * us).sum()
+    G = trace.shape[1]
+    return {"total_us": total, "idle_frac": 1.0 - busy / (total * G), "stages": rows}
+
+
+def by_type(summary: dict) -> dict:
+    agg = {}
+    for r in summary["stages"]:
+        a = agg.setdefault(r["type"], {"span_us": 0.0, "weight_bytes": 0, "count": 0})
+        a["span_us"] += r["span_us"]
+        a["weight_bytes"] += r["weight_bytes"]
+        a["count"] += 1
+    for a in agg.values():
+        a["GBps"] = a["weight_bytes"] / max(a["span_us"], 1e-3) / 1e3
+    return agg
+
+
+def format_table(summary: dict) -> str:
+    lines = [f"step {summary['total_us']:.1f} us, idle fraction {summary['idle_frac']:.3f}",
+             f"{'type':>10} {'count':>5} {'span_us':>9} {'MB':>9} {'GB/s':>7}"]
+    for k, a in sorted(by_type(summary).items(), key=lambda kv: -kv[1]["span_us"]):
+        lines.append(f"{k:>10} {a['count']:>5} {a['span_us']:>9.1f} {a['weight_bytes'] / 1e6:>9.1f} {a['GBps']:>7.0f}")
+    return "\n".join(lines)
