@@ -194,16 +194,19 @@ __device__ __forceinline__ int* counter_ptr(const Ctx& c, int stage, int stripe)
 }
 __device__ __forceinline__ int stripe_count(int G, int stripe) { return (G - stripe + kStripes - 1) / kStripes; }
 
-__device__ __noinline__ void set_watchdog(const Ctx& c, int stage, int observed) {
-  GLOBAL_AS unsigned long long* st = gpw(reinterpret_cast<unsigned long long*>(c.P->status));
-  unsigned long long mine = ((unsigned long long)c.A.epoch << 32) | (unsigned)(-PDM_ERR_WATCHDOG);
+// Record a dependency-wait timeout in the status word (first one wins).
+// Scalar arguments only: a by-reference argument of a non-inlined call would
+// force the caller's structs into scratch memory.
+__device__ __noinline__ void set_watchdog(uint64_t status, uint32_t epoch, int wg, int stage, int observed) {
+  GLOBAL_AS unsigned long long* st = (GLOBAL_AS unsigned long long*)status;
+  unsigned long long mine = ((unsigned long long)epoch << 32) | (unsigned)(-PDM_ERR_WATCHDOG);
   unsigned long long cur = __hip_atomic_load(st, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  if ((uint32_t)(cur >> 32) != c.A.epoch || (uint32_t)cur == 0u) {
+  if ((uint32_t)(cur >> 32) != epoch || (uint32_t)cur == 0u) {
     if (__hip_atomic_compare_exchange_strong(st, &cur, mine, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
                                              __HIP_MEMORY_SCOPE_AGENT)) {
-      int* det = reinterpret_cast<int*>(c.P->status) + 4;
+      int* det = reinterpret_cast<int*>(status) + 4;
       st_coh_i(det + 0, stage);
-      st_coh_i(det + 1, c.wg);
+      st_coh_i(det + 1, wg);
       st_coh_i(det + 2, observed);
     }
   }
@@ -235,7 +238,7 @@ __device__ __forceinline__ bool wait_stage(const Ctx& c, Smem& sm, int s, int my
       if (__any(abort)) { if (lane == 0) sm.abort = 1; break; }
       if (__all(ok)) break;
       if (++spins > c.A.spin_limit) {
-        if (!ok) set_watchdog(c, my_stage, seen);
+        if (!ok) set_watchdog(c.P->status, c.A.epoch, c.wg, my_stage, seen);
         if (lane == 0) sm.abort = 1;
         break;
       }
@@ -282,13 +285,13 @@ struct Gemv {
 };
 
 // Address of the 16 bytes a lane reads for (row, byte offset b) and its scale.
-template <int EB>
-__device__ __forceinline__ void unit_ptr(const Gemv& g, const Smem& sm, int row, int b,
-                                         const uint8_t*& cp, const uint16_t*& sp) {
-  if (g.slot_mode == 0) {
+template <int EB, int SLOT>
+__device__ __forceinline__ void unit_ptr_t(const Gemv& g, const Smem& sm, int row, int b,
+                                           const uint8_t*& cp, const uint16_t*& sp) {
+  if constexpr (SLOT == 0) {
     cp = g.codes + (size_t)row * g.Kb + b;
     if (EB == 1) sp = g.scales + (size_t)(row >> 3) * g.nkb + (b >> 7);
-  } else if (g.slot_mode == 1) {
+  } else if constexpr (SLOT == 1) {
     int j = row >> g.lg_slot;
     int rr = row & ((1 << g.lg_slot) - 1);
     cp = sm.slot_codes[j] + (size_t)rr * g.slot_Kb + b;
@@ -299,6 +302,14 @@ __device__ __forceinline__ void unit_ptr(const Gemv& g, const Smem& sm, int row,
     cp = sm.slot_codes[j] + (size_t)row * g.slot_Kb + bb;
     if (EB == 1) sp = sm.slot_scales[j] + (size_t)(row >> 3) * g.nkb + (bb >> 7);
   }
+}
+
+template <int EB>
+__device__ __forceinline__ void unit_ptr(const Gemv& g, const Smem& sm, int row, int b,
+                                         const uint8_t*& cp, const uint16_t*& sp) {
+  if (g.slot_mode == 0) unit_ptr_t<EB, 0>(g, sm, row, b, cp, sp);
+  else if (g.slot_mode == 1) unit_ptr_t<EB, 1>(g, sm, row, b, cp, sp);
+  else unit_ptr_t<EB, 2>(g, sm, row, b, cp, sp);
 }
 
 // dot of one lane's 16 bytes with the staged input
@@ -370,22 +381,37 @@ __device__ __forceinline__ void store_scales(const Gemv& g, Smem& sm, int ra, in
   }
 }
 
+// Sum within aligned groups of 2^lg lanes (lg <= 6) without branches.
+__device__ __forceinline__ float group_sum_lg(float v, int lg) {
+  v += lg >= 1 ? dpp<kDppXor1>(v) : 0.f;
+  v += lg >= 2 ? dpp<kDppXor2>(v) : 0.f;
+  v += lg >= 3 ? dpp<kDppHalfMirror>(v) : 0.f;
+  v += lg >= 4 ? dpp<kDppMirror>(v) : 0.f;
+  v += lg >= 5 ? __shfl_xor(v, 16) : 0.f;
+  v += lg >= 6 ? __shfl_xor(v, 32) : 0.f;
+  return v;
+}
+
 // Runs the units of rows [ra, rb) of a GEMV (ra, rb multiples of the unit
 // row count) split over the 8 waves; writes per-wave row partials to
 // sm.part[w][row - ra]. A unit is one 16-byte load per lane: 1 KB of one row
-// (rows of 1 KB or more) or 1024 / Kb whole rows (shorter power-of-two rows).
-// `prep` is called once by every thread after the scale loads and the first
-// batch of weight loads have been issued (when `early`) and before any input
-// is used; it must end with a workgroup barrier. Returns false on abort.
-template <int EB, class Prep>
-__device__ __forceinline__ bool gemv_rows(const Gemv& g, Smem& sm, int ra, int rb, bool call_prep, bool early, Prep&& prep) {
+// (LONG: rows of 1 KB or more) or 1024 / Kb whole rows (short power-of-two
+// rows). `prep` is called once by every thread after the scale loads and the
+// first batch of weight loads have been issued (when `early`) and before any
+// input is used; it must end with a workgroup barrier. Returns false on abort.
+//
+// Every unit of an unrolled batch issues its load unconditionally (units past
+// the wave's range read a valid address and are dropped): with no branch
+// around the loads the compiler waits only for the batch being consumed, so
+// the next batch stays in flight.
+template <int EB, bool LONG, int SLOT, class Prep>
+__device__ __forceinline__ bool gemv_rows_t(const Gemv& g, Smem& sm, int ra, int rb, bool early, Prep&& prep) {
   const int lane = lane_id();
   const int w = wave_id();
   const int kb = g.Kb;
-  const bool small = kb < 1024 && (1024 % kb) == 0;
   int S = 1, m = 1, lg_lpr = 0;
   int nunits;
-  if (small) {
+  if constexpr (!LONG) {
     m = 1024 / kb;
     lg_lpr = 31 - __builtin_clz(kb >> 4);
     nunits = (rb - ra) / m;
@@ -397,71 +423,75 @@ __device__ __forceinline__ bool gemv_rows(const Gemv& g, Smem& sm, int ra, int r
   const int u1 = (int)((int64_t)nunits * (w + 1) / kWaves);
   const int nkbt = (kb + 127) >> 7;
   const int g0 = ra >> 3;
+  const int lpr_mask = (1 << lg_lpr) - 1;
 
-  // (row, segment) of unit u in the large-row mode, advanced incrementally
+  // (row, segment) of the next unit to issue / to compute (LONG mode)
   int i_row = 0, i_seg = 0;
-  if (!small) { i_row = u0 / S; i_seg = u0 - i_row * S; }
+  if constexpr (LONG) { i_row = u0 / S; i_seg = u0 - i_row * S; }
   int c_row = i_row, c_seg = i_seg;
-
-  auto unit_of = [&](int u, int& row, int& b, int& r_it, int& s_it) {
-    if (small) {
-      row = ra + u * m + (lane >> lg_lpr);
-      b = (lane & ((1 << lg_lpr) - 1)) << 4;
-    } else {
-      row = ra + r_it;
-      b = (s_it << 10) + (lane << 4);
-      if (++s_it == S) { s_it = 0; ++r_it; }
-    }
-  };
 
   u32x4 wa[kUnroll], wb[kUnroll];
   auto issue = [&](u32x4* W, int ub) {
 #pragma unroll
     for (int j = 0; j < kUnroll; ++j) {
-      int u = ub + j;
+      const int u = ub + j;
       int row, b;
-      unit_of(u, row, b, i_row, i_seg);
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (u < u1 && b < kb) {
-        const uint8_t* cp;
-        const uint16_t* sp = nullptr;
-        unit_ptr<EB>(g, sm, row, b, cp, sp);
-        v = __builtin_nontemporal_load(gp(reinterpret_cast<const u32x4*>(cp)));
+      if constexpr (LONG) {
+        row = ra + i_row;
+        b = (i_seg << 10) + (lane << 4);
+        const bool wrap = i_seg + 1 == S;
+        i_row += wrap ? 1 : 0;
+        i_seg = wrap ? 0 : i_seg + 1;
+      } else {
+        row = ra + u * m + (lane >> lg_lpr);
+        b = (lane & lpr_mask) << 4;
       }
-      W[j] = v;
+      const bool ok = u < u1 && b < kb;
+      const uint8_t* cp;
+      const uint16_t* sp = nullptr;
+      unit_ptr_t<EB, SLOT>(g, sm, ok ? row : ra, ok ? b : 0, cp, sp);
+      W[j] = __builtin_nontemporal_load(gp(reinterpret_cast<const u32x4*>(cp)));
     }
   };
 
-  int cur_row = -1;
+  int cur_row = LONG ? ra + c_row : -1;
   float acc = 0.f;
-  auto flush = [&]() {
-    if (cur_row >= 0) {
-      float t = wave_sum(acc);
-      if (lane == 0) sm.part[w][cur_row - ra] = t;
-    }
-    acc = 0.f;
-  };
   auto compute = [&](const u32x4* W, int ub) {
 #pragma unroll
     for (int j = 0; j < kUnroll; ++j) {
-      int u = ub + j;
-      if (u >= u1) break;
+      const int u = ub + j;
+      const bool uok = u < u1;
       int row, b;
-      unit_of(u, row, b, c_row, c_seg);
-      int k0 = (EB == 1) ? b : (b >> 1);
-      int xoff = (g.lg_rpv >= 31) ? 0 : ((row >> g.lg_rpv) - g.vbase) * g.xK;
-      float d = 0.f;
-      if (b < kb) {
-        d = unit_dot<EB>(W[j], sm.x + xoff + k0);
-        if constexpr (EB == 1) d *= bf16_val(sm.sc[((row >> 3) - g0) * nkbt + (b >> 7)]);
-      }
-      if (small) {
-        float t = group_sum(d, 1 << lg_lpr);
-        if ((lane & ((1 << lg_lpr) - 1)) == 0) sm.part[w][row - ra] = t;
+      if constexpr (LONG) {
+        row = ra + c_row;
+        b = (c_seg << 10) + (lane << 4);
+        const bool wrap = c_seg + 1 == S;
+        c_row += wrap ? 1 : 0;
+        c_seg = wrap ? 0 : c_seg + 1;
       } else {
-        int rowu = __builtin_amdgcn_readfirstlane(row);
-        if (rowu != cur_row) { flush(); cur_row = rowu; }
+        row = ra + u * m + (lane >> lg_lpr);
+        b = (lane & lpr_mask) << 4;
+      }
+      const bool ok = uok && b < kb;
+      const int bq = ok ? b : 0;
+      const int rq = ok ? row : ra;
+      const int k0 = (EB == 1) ? bq : (bq >> 1);
+      const int xoff = (g.lg_rpv >= 31) ? 0 : ((rq >> g.lg_rpv) - g.vbase) * g.xK;
+      float d = unit_dot<EB>(W[j], sm.x + xoff + k0);
+      if constexpr (EB == 1) d *= bf16_val(sm.sc[((rq >> 3) - g0) * nkbt + (bq >> 7)]);
+      d = ok ? d : 0.f;
+      if constexpr (LONG) {
+        // rows change at most once per unit; flushing is a uniform branch
+        if (uok && row != cur_row) {
+          float t = wave_sum(acc);
+          if (lane == 0) sm.part[w][cur_row - ra] = t;
+          acc = 0.f;
+          cur_row = row;
+        }
         acc += d;
+      } else {
+        float t = group_sum_lg(d, lg_lpr);
+        if (uok && (lane & lpr_mask) == 0) sm.part[w][row - ra] = t;
       }
     }
   };
@@ -474,11 +504,9 @@ __device__ __forceinline__ bool gemv_rows(const Gemv& g, Smem& sm, int ra, int r
     load_scales<EB>(g, sm, ra, rb, scv);
     issue(wa, u0);
     store_scales<EB>(g, sm, ra, rb, scv);
-  }
-  if (call_prep) {
     if (!prep()) return false;
-  }
-  if (!early) {
+  } else {
+    if (!prep()) return false;
     load_scales<EB>(g, sm, ra, rb, scv);
     issue(wa, u0);
     store_scales<EB>(g, sm, ra, rb, scv);
@@ -491,8 +519,20 @@ __device__ __forceinline__ bool gemv_rows(const Gemv& g, Smem& sm, int ra, int r
     if (ub + 2 * kUnroll < u1) issue(wa, ub + 2 * kUnroll);
     compute(wb, ub + kUnroll);
   }
-  if (!small) flush();
+  if constexpr (LONG) {
+    if (u0 < u1) {
+      float t = wave_sum(acc);
+      if (lane == 0) sm.part[w][cur_row - ra] = t;
+    }
+  }
   return true;
+}
+
+template <int EB, int SLOT, class Prep>
+__device__ __forceinline__ bool gemv_rows(const Gemv& g, Smem& sm, int ra, int rb, bool early, Prep&& prep) {
+  const bool small = g.Kb < 1024 && (1024 % g.Kb) == 0;
+  return small ? gemv_rows_t<EB, false, SLOT>(g, sm, ra, rb, early, prep)
+               : gemv_rows_t<EB, true, SLOT>(g, sm, ra, rb, early, prep);
 }
 
 // Balanced contiguous share of `rows` (in groups of `gran`) for workgroup wg.
@@ -606,7 +646,7 @@ __device__ __forceinline__ Gemv gemv_of(const Fp8Mat& m, const char* base_unused
 // Generic single-chunk-loop driver: processes the workgroup's rows in chunks;
 // `prep` (wait + staging) runs before the first chunk; `epi(ra_chunk, n)`
 // consumes part[0][0..n) after combine.
-template <int EB, class Prep, class Epi>
+template <int EB, int SLOT, class Prep, class Epi>
 __device__ __forceinline__ bool run_gemv(const StageEnv& E, Smem& sm, const Gemv& g, int ra, int rb, bool early,
                                          Prep&& prep, Epi&& epi) {
   if (ra >= rb) {
@@ -618,7 +658,7 @@ __device__ __forceinline__ bool run_gemv(const StageEnv& E, Smem& sm, const Gemv
     int cb = min(rb, ca + kRowChunk);
     bool ok;
     if (first) {
-      ok = gemv_rows<EB>(g, sm, ca, cb, true, early, [&]() {
+      ok = gemv_rows<EB, SLOT>(g, sm, ca, cb, early, [&]() {
         zero_part(sm);
         return prep();
       });
@@ -626,7 +666,7 @@ __device__ __forceinline__ bool run_gemv(const StageEnv& E, Smem& sm, const Gemv
       zero_part(sm);
       // the early path stores the scale table before the barrier in prep;
       // later chunks need it (and the zeroed partials) visible before use
-      ok = gemv_rows<EB>(g, sm, ca, cb, true, true, [&]() {
+      ok = gemv_rows<EB, SLOT>(g, sm, ca, cb, true, [&]() {
         __syncthreads();
         return true;
       });
@@ -652,7 +692,7 @@ __device__ __forceinline__ bool stage_qkv(const StageEnv& E, Smem& sm) {
   int ra, rb;
   my_rows(E.st.rows, E.st.gran, c.G, c.wg, ra, rb);
   float* out = reinterpret_cast<float*>(L.qkv_raw);
-  return run_gemv<1>(E, sm, g, ra, rb, true,
+  return run_gemv<1, 0>(E, sm, g, ra, rb, true,
       [&]() {
         if (!wait_stage(c, sm, E.st.wait, E.s)) return false;
         const LayerInput in = layer_input(c, l);
@@ -681,7 +721,7 @@ __device__ __forceinline__ bool stage_qb(const StageEnv& E, Smem& sm) {
   int ra, rb;
   my_rows(E.st.rows, E.st.gran, c.G, c.wg, ra, rb);
   float* out = reinterpret_cast<float*>(L.q);
-  bool ok = run_gemv<1>(E, sm, g, ra, rb, true,
+  bool ok = run_gemv<1, 0>(E, sm, g, ra, rb, true,
       [&]() {
         if (!wait_stage(c, sm, E.st.wait, E.s)) return false;
         stage_rmsnorm(sm, d.q_lora, reinterpret_cast<const float*>(L.q_norm), d.rms_eps,
@@ -746,7 +786,7 @@ __device__ __forceinline__ bool stage_absorb(const StageEnv& E, Smem& sm) {
   g.vbase = ra / d.kv_lora;
   g.xK = d.qk_nope;
   float* out = reinterpret_cast<float*>(L.ql);
-  return run_gemv<1>(E, sm, g, ra, rb, true,
+  return run_gemv<1, 0>(E, sm, g, ra, rb, true,
       [&]() {
         if (!wait_stage(c, sm, E.st.wait, E.s)) return false;
         int h0 = ra / d.kv_lora, h1 = (rb - 1) / d.kv_lora;
@@ -920,7 +960,7 @@ __device__ __forceinline__ bool stage_uv(const StageEnv& E, Smem& sm) {
   g.vbase = ra / d.v_head;
   g.xK = dc;
   float* out = reinterpret_cast<float*>(L.o);
-  return run_gemv<1>(E, sm, g, ra, rb, true,
+  return run_gemv<1, 0>(E, sm, g, ra, rb, true,
       [&]() {
         if (!wait_stage(c, sm, E.st.wait, E.s)) return false;
         int h0 = ra / d.v_head, h1 = (rb - 1) / d.v_head;
@@ -972,7 +1012,7 @@ __device__ __forceinline__ bool stage_wo(const StageEnv& E, Smem& sm) {
   int ra, rb;
   my_rows(E.st.rows, E.st.gran, c.G, c.wg, ra, rb);
   float* out = reinterpret_cast<float*>(L.xa);
-  return run_gemv<1>(E, sm, g, ra, rb, true,
+  return run_gemv<1, 0>(E, sm, g, ra, rb, true,
       [&]() {
         if (!wait_stage(c, sm, E.st.wait, E.s)) return false;
         stage_plain(sm, d.n_heads * d.v_head, [&](int k) { return ld_coh(o + k); });
@@ -997,7 +1037,7 @@ __device__ __forceinline__ bool stage_router(const StageEnv& E, Smem& sm) {
   int ra, rb;
   my_rows(E.st.rows, E.st.gran, c.G, c.wg, ra, rb);
   float* out = reinterpret_cast<float*>(L.router_logits);
-  return run_gemv<2>(E, sm, g, ra, rb, true,
+  return run_gemv<2, 0>(E, sm, g, ra, rb, true,
       [&]() {
         if (!wait_stage(c, sm, E.st.wait, E.s)) return false;
         stage_rmsnorm(sm, d.hidden, reinterpret_cast<const float*>(L.ffn_norm), d.rms_eps,
@@ -1119,8 +1159,7 @@ __device__ __forceinline__ bool stage_gu(const StageEnv& E, Smem& sm, bool route
     set_slots(d, L, sm, false, false);
     __syncthreads();
   }
-  return run_gemv<1>(E, sm, g, ra, rb, !routed,
-      [&]() {
+  auto prep = [&]() {
         if (!wait_stage(c, sm, E.st.wait, E.s)) return false;
         if (routed) {
           route_topk(c, sm, L, c.wg == 0);
@@ -1129,8 +1168,8 @@ __device__ __forceinline__ bool stage_gu(const StageEnv& E, Smem& sm, bool route
         stage_rmsnorm(sm, d.hidden, reinterpret_cast<const float*>(L.ffn_norm), d.rms_eps,
                       [&](int k) { return ld_coh(xa + k); });
         return true;
-      },
-      [&](int ca, int n) {
+      };
+  auto epi = [&](int ca, int n) {
         // rows are gate/up interleaved in groups of 8: [gate 8 ; up 8]
         for (int t = threadIdx.x; t < n / 2; t += kThreads) {
           int grp = t >> 3, r = t & 7;
@@ -1148,7 +1187,9 @@ __device__ __forceinline__ bool stage_gu(const StageEnv& E, Smem& sm, bool route
           }
           st_coh(act + dst, a);
         }
-      });
+      };
+  if (L.is_moe) return run_gemv<1, 1>(E, sm, g, ra, rb, !routed, prep, epi);
+  return run_gemv<1, 0>(E, sm, g, ra, rb, true, prep, epi);
 }
 
 // --- DOWN: x_out = bf16(x_attn + sum_slots W_down[slot] act[slot])
@@ -1180,16 +1221,17 @@ __device__ __forceinline__ bool stage_down(const StageEnv& E, Smem& sm) {
     set_slots(d, L, sm, true, true);
     __syncthreads();
   }
-  return run_gemv<1>(E, sm, g, ra, rb, true,
-      [&]() {
+  auto prep = [&]() {
         if (!wait_stage(c, sm, E.st.wait, E.s)) return false;
         stage_plain(sm, K, [&](int k) { return ld_coh(act + k); });
         return true;
-      },
-      [&](int ca, int n) {
+      };
+  auto epi = [&](int ca, int n) {
         for (int t = threadIdx.x; t < n; t += kThreads)
           st_coh(out + ca + t, round_bf16(ld_coh(xa + ca + t) + sm.part[0][t]));
-      });
+      };
+  if (L.is_moe) return run_gemv<1, 2>(E, sm, g, ra, rb, true, prep, epi);
+  return run_gemv<1, 0>(E, sm, g, ra, rb, true, prep, epi);
 }
 
 // --- LM: logits = W_lm * RMSNorm(x), argmax over the vocabulary
@@ -1206,7 +1248,7 @@ __device__ __forceinline__ bool stage_lm(const StageEnv& E, Smem& sm) {
   my_rows(E.st.rows, E.st.gran, c.G, c.wg, ra, rb);
   float bestv = -INFINITY;
   int besti = 0x7fffffff;
-  bool ok = run_gemv<2>(E, sm, g, ra, rb, true,
+  bool ok = run_gemv<2, 0>(E, sm, g, ra, rb, true,
       [&]() {
         if (!wait_stage(c, sm, E.st.wait, E.s)) return false;
         stage_rmsnorm(sm, d.hidden, reinterpret_cast<const float*>(c.P->final_norm), d.rms_eps,
