@@ -75,6 +75,7 @@ struct __align__(16) Smem {
   int ired[2 * kWaves];
   uint64_t t_enter, t_ready;
   int abort;
+  int last;                       // this workgroup arrived last at the LM head
 };
 
 // ------------------------------------------------------------------ helpers
@@ -803,7 +804,31 @@ __device__ __forceinline__ bool stage_absorb(const StageEnv& E, Smem& sm) {
 }
 
 // --- ATTN: split-KV MLA attention partials (m, l, acc) per (head, position chunk)
-template <int DPL>
+//
+// Attention is the one dense contraction of the step: 16 heads share every
+// latent cache row, so a work unit (16 heads x a chunk of positions) runs its
+// two products on the matrix cores with v_mfma_f32_16x16x32_bf16:
+//   scores  S^T[t][h] = sum_d K[t][d] Q[h][d]   (A = cache rows, B = queries)
+//   values  O[h][c]   = sum_t P[h][t] V[t][c]   (A = probabilities, B = cache rows)
+// K and V are the bf16 cache rows themselves. The fp32 operands (the scaled
+// queries and the probabilities) enter as a bf16 high part plus a bf16
+// residual, two MFMAs each, which keeps both products accurate to about
+// 2^-16 relative: the result matches fp32 arithmetic, not bf16 rounding.
+// Operand layout (lane l, g = l / 16): A holds A[l % 16][8g .. 8g + 7],
+// B holds B[8g .. 8g + 7][l % 16], C holds C[4g .. 4g + 3][l % 16].
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+constexpr int kAttnBlock = 64;    // positions staged per round
+constexpr int kMH = 16;           // heads per MFMA tile (unit heads padded to 16)
+
+__device__ __forceinline__ void split_bf16(float v, __bf16& hi, __bf16& lo) {
+  hi = (__bf16)v;
+  lo = (__bf16)(v - (float)hi);
+}
+
+__device__ __forceinline__ bf16x8 u32x4_as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+template <int DTILES>  // latent dim tiles of 16 per wave: kv_lora / 128
 __device__ __forceinline__ bool stage_attn(const StageEnv& E, Smem& sm) {
   const Ctx& c = E.c;
   const pdm_dims d = load_plan(&c.P->dims);
@@ -817,131 +842,182 @@ __device__ __forceinline__ bool stage_attn(const StageEnv& E, Smem& sm) {
   const int t0 = min(ctx, ch * chunk), t1 = min(ctx, t0 + chunk);
   const int dc = d.kv_lora, dr = d.rope, kvr = dc + dr;
   const int qkh = d.qk_nope + d.rope;
+  const int q8n = kvr / 8;              // 16-byte pieces per cache row
+  const int nkb = kvr / 32;             // MFMA k-blocks of a score
+  const int kstr = kvr / 2 + 4;         // LDS cache-row stride in u32 (padded)
+  const int qstr = kvr + 8;             // LDS query-row stride in bf16 (padded)
+  constexpr int pstr = kAttnBlock + 4;  // LDS probability-row stride in floats
   const float tau = 1.0f / sqrtf((float)qkh);
   if (!wait_stage(c, sm, E.st.wait, E.s)) return false;
-  // stage q (scaled by tau): per head [q_lat (dc) ; q_rope (dr)], and the current row
-  float* qs = sm.x;                      // [hg][kvr]
-  float* cur = sm.x + hg * kvr;          // [kvr]
-  const float* ql = reinterpret_cast<const float*>(L.ql);
+
+  // LDS: query hi/lo [16][qstr] bf16, cache rows [64][kstr] u32, two score
+  // partials [2][16][pstr] f32, per-head max / sum / rescale
+  __bf16* qh = reinterpret_cast<__bf16*>(sm.x);
+  __bf16* ql = qh + kMH * qstr;
+  uint32_t* kvs = reinterpret_cast<uint32_t*>(ql + kMH * qstr);
+  float* sp = reinterpret_cast<float*>(kvs + kAttnBlock * kstr);
+  float* hm = sp + 2 * kMH * pstr;  // running max per head
+  float* hl = hm + kMH;             // running sum per head
+  float* ha = hl + kMH;             // rescale of the accumulators this round
+
+  const float* qlat = reinterpret_cast<const float*>(L.ql);
   const float* qf = reinterpret_cast<const float*>(L.q);
-  stage_values(sm, hg * kvr, [&](int i) {
-    int hh = i / kvr, k = i - hh * kvr;
-    int h = grp * hg + hh;
-    float v = k < dc ? ld_coh(ql + (size_t)h * dc + k) : ld_coh(qf + (size_t)h * qkh + d.qk_nope + (k - dc));
-    return v * tau;
-  });
-  const uint16_t* cache = reinterpret_cast<const uint16_t*>(L.kv);
-  const bool has_cur = pos >= t0 && pos < t1;
-  if (has_cur) {
-    const uint32_t* rowp = reinterpret_cast<const uint32_t*>(cache + (size_t)pos * kvr);
-    for (int p = threadIdx.x; p < kvr / 2; p += kThreads) {
-      uint32_t u = ld_coh_u(rowp + p);
-      cur[2 * p] = bf16_lo(u);
-      cur[2 * p + 1] = bf16_hi(u);
+  {
+    // scaled queries split into bf16 high and residual parts; heads >= hg are zero
+    const int n = kMH * kvr;
+    for (int i0 = threadIdx.x; i0 < n; i0 += kStageBatch * kThreads) {
+      float v[kStageBatch];
+#pragma unroll
+      for (int b = 0; b < kStageBatch; ++b) {
+        int i = min(i0 + b * kThreads, n - 1);
+        int hh = i / kvr, k = i - hh * kvr;
+        int h = grp * hg + min(hh, hg - 1);
+        const float* src = k < dc ? qlat + (size_t)h * dc + k : qf + (size_t)h * qkh + d.qk_nope + (k - dc);
+        v[b] = ld_coh(src);
+      }
+#pragma unroll
+      for (int b = 0; b < kStageBatch; ++b) {
+        int i = i0 + b * kThreads;
+        if (i < n) {
+          int hh = i / kvr, k = i - hh * kvr;
+          __bf16 hi, lo;
+          split_bf16(hh < hg ? v[b] * tau : 0.f, hi, lo);
+          qh[hh * qstr + k] = hi;
+          ql[hh * qstr + k] = lo;
+        }
+      }
     }
+    if (threadIdx.x < kMH) { hm[threadIdx.x] = -INFINITY; hl[threadIdx.x] = 0.f; }
   }
-  __syncthreads();
 
   const int lane = lane_id();
   const int w = wave_id();
-  constexpr int HPW_MAX = kHeadGroup / kWaves;  // 2
-  const int hpw = hg / kWaves;                  // 1 or 2
-  float m[HPW_MAX], lsum[HPW_MAX], acc[HPW_MAX][DPL];
+  const int lr = lane & 15, lg = lane >> 4;
+  const uint16_t* cache = reinterpret_cast<const uint16_t*>(L.kv);
+  f32x4 acc[DTILES];
 #pragma unroll
-  for (int i = 0; i < HPW_MAX; ++i) {
-    m[i] = -INFINITY; lsum[i] = 0.f;
+  for (int i = 0; i < DTILES; ++i) acc[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
+
+  for (int tb = t0; tb < t1; tb += kAttnBlock) {
+    const int nb = min(kAttnBlock, t1 - tb);
+    // ---- stage rows [tb, tb + nb) (zeros beyond nb); the row of pos was
+    // written this step by another workgroup and is read coherently
+    {
+      constexpr int kPer = (kAttnBlock * 80 + kThreads - 1) / kThreads;
+      const int nmain = max(0, min(nb, pos - tb)) * q8n;
+      u32x4 v[kPer];
 #pragma unroll
-    for (int k = 0; k < DPL; ++k) acc[i][k] = 0.f;
-  }
-  const int tmain = min(t1, pos);  // rows before pos come from the cache through cached loads
-  for (int tb = t0; tb < tmain; tb += 64) {
-    const int t = tb + lane;
-    const bool valid = t < tmain;
-    float s[HPW_MAX] = {0.f, 0.f};
-    const u32x4* rp = reinterpret_cast<const u32x4*>(cache + (size_t)(valid ? t : t0) * kvr);
-    // latent part: dc/8 loads of 8 bf16
-#pragma unroll 4
-    for (int q8 = 0; q8 < kvr / 8; ++q8) {
-      u32x4 v = gld(rp + q8);
-      float f[8] = {bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y),
-                    bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w)};
+      for (int r = 0; r < kPer; ++r) {
+        int i = threadIdx.x + r * kThreads;
+        int row = i / q8n, col = i - row * q8n;
+        int ok = i < nmain;
+        v[r] = gld(reinterpret_cast<const u32x4*>(cache + (size_t)(tb + (ok ? row : 0)) * kvr) + (ok ? col : 0));
+      }
+      const bool cur_here = pos >= tb && pos < tb + nb;
+      uint32_t cv = 0;
+      if (cur_here && threadIdx.x < kvr / 2)
+        cv = ld_coh_u(reinterpret_cast<const uint32_t*>(cache + (size_t)pos * kvr) + threadIdx.x);
+      __syncthreads();  // the previous round's readers are done with kvs and sp
 #pragma unroll
-      for (int i = 0; i < HPW_MAX; ++i) {
-        if (i < hpw) {
-          const float4* qv = reinterpret_cast<const float4*>(qs + (w * hpw + i) * kvr + q8 * 8);
-          float4 a = qv[0], b = qv[1];
-          s[i] += a.x * f[0] + a.y * f[1] + a.z * f[2] + a.w * f[3] + b.x * f[4] + b.y * f[5] + b.z * f[6] + b.w * f[7];
+      for (int r = 0; r < kPer; ++r) {
+        int i = threadIdx.x + r * kThreads;
+        if (i < kAttnBlock * q8n) {
+          int row = i / q8n, col = i - row * q8n;
+          u32x4 z = {0u, 0u, 0u, 0u};
+          *reinterpret_cast<u32x4*>(kvs + row * kstr + col * 4) = i < nmain ? v[r] : z;
+        }
+      }
+      __syncthreads();
+      if (cur_here && threadIdx.x < kvr / 2) kvs[(pos - tb) * kstr + threadIdx.x] = cv;
+      __syncthreads();
+    }
+    // ---- scores: waves 0-3 take position tiles 0-3 over the first half of
+    // the k-blocks, waves 4-7 the same tiles over the second half
+    {
+      const int tile = w & 3, half = w >> 2;
+      const int kb0 = half ? nkb / 2 : 0, kb1 = half ? nkb : nkb / 2;
+      f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+      if (tile * 16 < nb) {
+        const uint32_t* arow = kvs + (tile * 16 + lr) * kstr + lg * 4;
+        const __bf16* bh = qh + lr * qstr + lg * 8;
+        const __bf16* bl = ql + lr * qstr + lg * 8;
+        for (int kb = kb0; kb < kb1; ++kb) {
+          bf16x8 a = u32x4_as_bf16x8(*reinterpret_cast<const u32x4*>(arow + kb * 16));
+          bf16x8 b1 = *reinterpret_cast<const bf16x8*>(bh + kb * 32);
+          bf16x8 b2 = *reinterpret_cast<const bf16x8*>(bl + kb * 32);
+          sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b1, sc, 0, 0, 0);
+          sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b2, sc, 0, 0, 0);
+        }
+      }
+      // sc[r] = S^T[tile*16 + 4*lg + r][lr] = score of head lr at that position
+      float* dst = sp + half * kMH * pstr + lr * pstr + tile * 16 + 4 * lg;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) dst[r] = sc[r];
+    }
+    __syncthreads();
+    // ---- online softmax: wave w owns heads 2w and 2w+1, lanes are positions
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int h = 2 * w + q;
+      const bool valid = lane < nb;
+      float sv = valid ? sp[h * pstr + lane] + sp[kMH * pstr + h * pstr + lane] : -INFINITY;
+      float mold = hm[h];
+      float mn = fmaxf(mold, wave_max(sv));
+      float alpha = __expf(mold - mn);  // 0 on the first round (mold = -inf)
+      float pv = valid ? __expf(sv - mn) : 0.f;
+      float ps = wave_sum(pv);
+      sp[h * pstr + lane] = pv;          // probabilities replace the first partial
+      if (lane == 0) { hm[h] = mn; hl[h] = hl[h] * alpha + ps; ha[h] = alpha; }
+    }
+    __syncthreads();
+    // ---- values: wave w owns latent dim tiles [w * DTILES, w * DTILES + DTILES)
+    {
+#pragma unroll
+      for (int i = 0; i < DTILES; ++i) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[i][r] *= ha[4 * lg + r];
+      }
+      for (int pb = 0; pb < (nb + 31) / 32; ++pb) {
+        // A = P[head lr][pb*32 + 8*lg + 0..7], split hi / lo
+        const float* prow = sp + lr * pstr + pb * 32 + 8 * lg;
+        bf16x8 ah, al;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          __bf16 hi, lo;
+          split_bf16(prow[e], hi, lo);
+          ah[e] = hi;
+          al[e] = lo;
+        }
+#pragma unroll
+        for (int i = 0; i < DTILES; ++i) {
+          // B = V[pb*32 + 8*lg + e][dim tile*16 + lr]: one bf16 from each of 8 rows
+          const int col = (w * DTILES + i) * 16 + lr;
+          const uint16_t* vcol = reinterpret_cast<const uint16_t*>(kvs) + (pb * 32 + 8 * lg) * (2 * kstr) + col;
+          bf16x8 b;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) b[e] = __builtin_bit_cast(__bf16, vcol[e * 2 * kstr]);
+          acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, b, acc[i], 0, 0, 0);
+          acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, b, acc[i], 0, 0, 0);
         }
       }
     }
-    float p[HPW_MAX];
-#pragma unroll
-    for (int i = 0; i < HPW_MAX; ++i) {
-      if (i < hpw) {
-        float sv = valid ? s[i] : -INFINITY;
-        float mb = wave_max(sv);
-        float mn = fmaxf(m[i], mb);
-        float alpha = __expf(m[i] - mn);
-        p[i] = valid ? __expf(sv - mn) : 0.f;
-        lsum[i] = lsum[i] * alpha + wave_sum(p[i]);
-#pragma unroll
-        for (int k = 0; k < DPL; ++k) acc[i][k] *= alpha;
-        m[i] = mn;
-      }
-    }
-    const int nv = min(64, tmain - tb);
-    for (int j = 0; j < nv; ++j) {
-      const uint16_t* r = cache + (size_t)(tb + j) * kvr + lane * DPL;
-      float cv[DPL];
-      if constexpr (DPL == 8) {
-        u32x4 v = gld(reinterpret_cast<const u32x4*>(r));
-        cv[0] = bf16_lo(v.x); cv[1] = bf16_hi(v.x); cv[2] = bf16_lo(v.y); cv[3] = bf16_hi(v.y);
-        cv[4] = bf16_lo(v.z); cv[5] = bf16_hi(v.z); cv[6] = bf16_lo(v.w); cv[7] = bf16_hi(v.w);
-      } else if constexpr (DPL == 4) {
-        u32x2 v = gld(reinterpret_cast<const u32x2*>(r));
-        cv[0] = bf16_lo(v.x); cv[1] = bf16_hi(v.x); cv[2] = bf16_lo(v.y); cv[3] = bf16_hi(v.y);
-      } else {
-        uint32_t v = gld(reinterpret_cast<const uint32_t*>(r));
-        cv[0] = bf16_lo(v); cv[1] = bf16_hi(v);
-      }
-#pragma unroll
-      for (int i = 0; i < HPW_MAX; ++i) {
-        if (i < hpw) {
-          float pj = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, p[i]), j));
-#pragma unroll
-          for (int k = 0; k < DPL; ++k) acc[i][k] = fmaf(pj, cv[k], acc[i][k]);
-        }
-      }
-    }
   }
-  if (has_cur) {
-#pragma unroll
-    for (int i = 0; i < HPW_MAX; ++i) {
-      if (i < hpw) {
-        const float* qh = qs + (w * hpw + i) * kvr;
-        float part = 0.f;
-        for (int k = lane; k < kvr; k += 64) part += qh[k] * cur[k];
-        float sv = wave_sum(part);
-        float mn = fmaxf(m[i], sv);
-        float alpha = __expf(m[i] - mn);
-        float pv = __expf(sv - mn);
-        lsum[i] = lsum[i] * alpha + pv;
-#pragma unroll
-        for (int k = 0; k < DPL; ++k) acc[i][k] = acc[i][k] * alpha + pv * cur[lane * DPL + k];
-        m[i] = mn;
-      }
-    }
-  }
+  __syncthreads();
+  // ---- partials: acc[i][r] = O[head 4*lg + r][dim (w*DTILES + i)*16 + lr]
   float* part = reinterpret_cast<float*>(L.attn_part);
 #pragma unroll
-  for (int i = 0; i < HPW_MAX; ++i) {
-    if (i < hpw) {
-      int h = grp * hg + w * hpw + i;
-      float* dst = part + ((size_t)h * nch + ch) * (dc + 2);
+  for (int r = 0; r < 4; ++r) {
+    const int hh = 4 * lg + r;
+    if (hh < hg) {
+      float* dst = part + ((size_t)(grp * hg + hh) * nch + ch) * (dc + 2);
 #pragma unroll
-      for (int k = 0; k < DPL; ++k) st_coh(dst + lane * DPL + k, acc[i][k]);
-      if (lane == 0) { st_coh(dst + dc, m[i]); st_coh(dst + dc + 1, lsum[i]); }
+      for (int i = 0; i < DTILES; ++i) st_coh(dst + (w * DTILES + i) * 16 + lr, acc[i][r]);
     }
+  }
+  if (threadIdx.x < hg) {
+    float* dst = part + ((size_t)(grp * hg + threadIdx.x) * nch + ch) * (dc + 2);
+    st_coh(dst + dc, hm[threadIdx.x]);
+    st_coh(dst + dc + 1, hl[threadIdx.x]);
   }
   return true;
 }
@@ -1271,6 +1347,7 @@ __device__ __forceinline__ bool stage_lm(const StageEnv& E, Smem& sm) {
   }
   if (lane_id() == 0) { sm.red[wave_id()] = bestv; sm.ired[wave_id()] = besti; }
   __syncthreads();
+  // workgroup result, then the last workgroup to arrive reduces all of them
   if (threadIdx.x == 0) {
     for (int w = 1; w < kWaves; ++w)
       if (sm.red[w] > bestv || (sm.red[w] == bestv && sm.ired[w] < besti)) { bestv = sm.red[w]; besti = sm.ired[w]; }
@@ -1278,20 +1355,36 @@ __device__ __forceinline__ bool stage_lm(const StageEnv& E, Smem& sm) {
     st_coh(best, bestv);
     st_coh_i(reinterpret_cast<int*>(best + 1), besti);
     mem_done();
-    // the last workgroup to arrive reduces the per-workgroup maxima
     int* done = counter_ptr(c, c.P->n_stages, 0);
     int old = __hip_atomic_fetch_add(gpw(done), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (old == (int)c.A.epoch * c.G - 1) {
-      float bv = -INFINITY;
-      int bi = 0x7fffffff;
-      for (int w = 0; w < c.G; ++w) {
-        const float* bw = reinterpret_cast<const float*>(c.P->lm_best) + 2 * w;
-        float v = ld_coh(bw);
-        int i = ld_coh_i(reinterpret_cast<const int*>(bw + 1));
-        if (v > bv || (v == bv && i < bi)) { bv = v; bi = i; }
+    sm.last = old == (int)c.A.epoch * c.G - 1;
+  }
+  __syncthreads();
+  if (sm.last && threadIdx.x < 64) {
+    // one wave: every lane loads its share of the per-workgroup maxima at once
+    const int lane = threadIdx.x;
+    float bv = -INFINITY;
+    int bi = 0x7fffffff;
+    for (int w0 = 0; w0 < c.G; w0 += 64 * 4) {
+      float v[4];
+      int ix[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        int wg = w0 + r * 64 + lane;
+        const float* bw = reinterpret_cast<const float*>(c.P->lm_best) + 2 * (wg < c.G ? wg : 0);
+        v[r] = wg < c.G ? ld_coh(bw) : -INFINITY;
+        ix[r] = wg < c.G ? ld_coh_i(reinterpret_cast<const int*>(bw + 1)) : 0x7fffffff;
       }
-      if (c.A.argmax) gst(c.A.argmax, bi);
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (v[r] > bv || (v[r] == bv && ix[r] < bi)) { bv = v[r]; bi = ix[r]; }
     }
+    for (int off = 1; off < 64; off <<= 1) {
+      float ov = __shfl_xor(bv, off);
+      int oi = __shfl_xor(bi, off);
+      if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
+    }
+    if (lane == 0 && c.A.argmax) gst(c.A.argmax, bi);
   }
   return true;
 }
@@ -1315,7 +1408,7 @@ __global__ void __launch_bounds__(kThreads, 1) engine_kernel(const Plan* __restr
       case PDM_ST_QB: ok = stage_qb(E, sm); break;
       case PDM_ST_ABSORB: ok = stage_absorb(E, sm); break;
       case PDM_ST_ATTN:
-        ok = dpl == 8 ? stage_attn<8>(E, sm) : dpl == 4 ? stage_attn<4>(E, sm) : stage_attn<2>(E, sm);
+        ok = dpl == 8 ? stage_attn<4>(E, sm) : dpl == 4 ? stage_attn<2>(E, sm) : stage_attn<1>(E, sm);
         break;
       case PDM_ST_UV: ok = stage_uv(E, sm); break;
       case PDM_ST_WO: ok = stage_wo(E, sm); break;

@@ -105,7 +105,11 @@ int build_plan(const pdm_dims& d, int32_t max_ctx, int32_t G, Plan* p, Layout* l
     p->nch = std::min(by_wg, by_ctx);
   }
   p->nch = std::min(p->nch, kRowChunk);
-  if (p->hg * kvr > kXMax) return PDM_ERR_CONFIG;
+  // attention LDS: query hi/lo rows [16][kvr + 8] bf16, 64 staged cache rows
+  // [64][kvr / 2 + 4] u32, two score partials [2][16][68] f32, 48 head scalars
+  if (kvr % 32 != 0 || p->hg > 16) return PDM_ERR_CONFIG;
+  if (2LL * 16 * (kvr + 8) * 2 + 64LL * (kvr / 2 + 4) * 4 + 2LL * 16 * 68 * 4 + 48 * 4 > (int64_t)kXMax * 4)
+    return PDM_ERR_CONFIG;
   // every packed 8-row x 128-column scale tile of W_UK^T and W_UV must lie in one logical block
   for (int h = 0; h < H; ++h) {
     const int base = h * (d.qk_nope + d.v_head);
