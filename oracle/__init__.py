@@ -15,4 +15,4 @@ from . import numerics, model  # noqa: F401
 from .numerics import E4M3, bf16_round, bf16_bits_to_f64, dequant_fp8, e4m3_decode  # noqa: F401
 from .model import (OracleWeights, DecodeState, decode_step, forward_full, prefill,  # noqa: F401
                     rmsnorm, rope, softmax, route, topk_indices, mla_absorbed, mla_naive,
-                    split_wkv_b)
+                    split_wkv_b, attention_decode, ffn_decode, lm_logits)

@@ -233,6 +233,16 @@ def ffn_decode(W, cfg, l: int, x: np.ndarray, taps: Optional[dict] = None):
     return x + y
 
 
+def lm_logits(W: OracleWeights, cfg, x: np.ndarray, rows_per_block: int = 8192) -> np.ndarray:
+    """Final RMSNorm and LM head product, taken a block of vocabulary rows at a
+    time so that a 129,280-row bf16 head never sits in memory as one float64
+    matrix. Row i of the result is the same dot product as in decode_step."""
+    hf = rmsnorm(x, W("final_norm"), cfg.rms_eps)
+    data = W.store.numpy("lm_head")["data"]
+    return np.concatenate([bf16_bits_to_f64(data[i:i + rows_per_block]) @ hf
+                           for i in range(0, data.shape[0], rows_per_block)])
+
+
 def decode_step(W: OracleWeights, state: DecodeState, pos: int, token: Optional[int] = None,
                 x_in: Optional[np.ndarray] = None, parity: bool = True, absorbed: bool = True):
     """One decode step at position pos == state.length.

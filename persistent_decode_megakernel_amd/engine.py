@@ -158,6 +158,8 @@ class Engine:
         if getattr(self, "h", None) is not None:
             self.lib.pdm_destroy(self.h)
             self.h = None
+        # the buffers are useless without the handle: let torch reuse the memory
+        self.weights = self.kv = self.scratch = self.trace = None
 
     def __del__(self):
         try:

@@ -114,3 +114,16 @@ def test_bare_layer_stack_input(tiny_cfg, tiny_store):
     assert "logits" not in out and len(out["hidden"]) == cfg.n_layers
     full = O.forward_full(W, xs=x[None, :], parity=True)
     assert _rel(out["hidden"][-1], full["hidden"][-1][0]) < 1e-12
+
+
+def test_blocked_lm_head_matches_step_logits(tiny_cfg, tiny_store):
+    """The row-blocked LM head equals the step's LM head for any block size,
+    including blocks that do not divide the vocabulary."""
+    W = O.OracleWeights(tiny_store)
+    st = O.DecodeState.empty(tiny_cfg, 4)
+    out = O.decode_step(W, st, 0, token=5)
+    x = out["hidden"][-1]
+    for rows in (7, 300, 2048, 5000):
+        got = O.lm_logits(W, tiny_cfg, x, rows_per_block=rows)
+        assert got.shape == out["logits"].shape
+        assert _rel(got, out["logits"]) < 1e-13
