@@ -99,7 +99,7 @@ typedef struct pdm_sizes {
   uint64_t weight_bytes;   /* packed weight arena (= the packed blob) */
   uint64_t kv_bytes;       /* latent KV cache, n_layers x max_ctx x (kv_lora+rope) bf16 */
   uint64_t scratch_bytes;  /* plan, counters, activations, taps */
-  uint64_t trace_bytes;    /* optional per-stage timestamps, 32 B per stage and workgroup */
+  uint64_t trace_bytes;    /* optional per-stage timestamps, 64 B per stage and workgroup */
   uint64_t alignment;      /* required alignment of every buffer (256) */
   int32_t n_stages;        /* stages of one decode step */
   int32_t n_workgroups;    /* persistent workgroups the sizes were computed for */
@@ -143,7 +143,7 @@ typedef struct pdm_taps {
   const int32_t* router_idx_dev; /* [n_layers, top_k]; rows of dense layers unused */
   const float* router_w_dev;     /* [n_layers, top_k] normalised routing weights */
   const float* logits_dev;       /* [vocab] when no logits buffer was passed */
-  const uint64_t* trace_dev;     /* [n_stages, n_workgroups, 4] or null when unbound */
+  const uint64_t* trace_dev;     /* [n_stages, n_workgroups, 8] or null when unbound */
   int32_t n_stages, n_workgroups;
   uint32_t epoch;                /* epoch of the last launched step */
 } pdm_taps;
@@ -267,7 +267,8 @@ int pdm_set_debug(pdm_engine* e, int32_t spin_limit, int32_t skip_signal_stage);
 /* Record per-stage timestamps (wall clock, 100 MHz on MI355X) of the
  * following steps into the bound trace buffer: on != 0 enables, 0 disables.
  * Requires a trace buffer at bind time. Records: [stage][workgroup] x
- * {entered, dependency satisfied, signalled, epoch}. */
+ * {entered, dependency satisfied, signalled, epoch, input staged, weights
+ * consumed, epilogue done, 0}; a mark a stage does not pass through is 0. */
 int pdm_set_trace(pdm_engine* e, int32_t on);
 
 int pdm_destroy(pdm_engine* e);

@@ -1,7 +1,9 @@
 """Build the HIP engine library for gfx950 with hipcc (in-tree, no JIT cache)."""
 from __future__ import annotations
 
+import json
 import os
+import re
 import shutil
 import subprocess
 
@@ -24,17 +26,39 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
+USAGE = os.path.join(OUT_DIR, "resource_usage.json")
+
+
+def parse_resource_usage(text: str) -> dict:
+    """Per-kernel register, spill, scratch and LDS figures from hipcc's
+    kernel-resource-usage remarks."""
+    usage, cur = {}, None
+    for line in text.splitlines():
+        m = re.search(r"remark: Function Name: (\S+)", line)
+        if m:
+            cur = usage.setdefault(m.group(1), {})
+            continue
+        m = re.search(r"remark:\s+([A-Za-z][A-Za-z /\[\]]*?):\s+(-?\d+)", line)
+        if m and cur is not None:
+            cur[m.group(1).strip()] = int(m.group(2))
+    return usage
+
+
 def build_library(verbose: bool = False) -> str:
     os.makedirs(OUT_DIR, exist_ok=True)
     tmp = OUT + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"), "-o", tmp,
-           *[os.path.join(CSRC, s) for s in SOURCES]]
+    cmd = [hipcc(), *HIPCC_FLAGS, "-Rpass-analysis=kernel-resource-usage", "-I", os.path.join(ROOT, "include"),
+           "-o", tmp, *[os.path.join(CSRC, s) for s in SOURCES]]
     r = subprocess.run(cmd, capture_output=True, text=True)
-    msgs = "\n".join(l for l in (r.stdout + r.stderr).splitlines() if "packed-fp32-ops" not in l)
+    text = r.stdout + r.stderr
+    msgs = "\n".join(l for l in text.splitlines() if "packed-fp32-ops" not in l and "remark:" not in l
+                     and not l.lstrip().startswith(("|", "^")) and not re.match(r"^\s*\d+ \|", l))
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed ({r.returncode}):\n{msgs}")
     if verbose and msgs.strip():
         print(msgs)
+    with open(USAGE, "w") as f:
+        json.dump(parse_resource_usage(text), f, indent=1, sort_keys=True)
     os.replace(tmp, OUT)
     return OUT
 

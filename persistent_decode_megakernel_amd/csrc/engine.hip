@@ -74,6 +74,7 @@ struct __align__(16) Smem {
   float red[2 * kWaves];
   int ired[2 * kWaves];
   uint64_t t_enter, t_ready;
+  uint64_t t_mark[3];             // input staged, weights consumed, epilogue done
   int abort;
   int last;                       // this workgroup arrived last at the LM head
 };
@@ -218,7 +219,10 @@ __device__ __noinline__ void set_watchdog(uint64_t status, uint32_t epoch, int w
 __device__ __forceinline__ bool wait_stage(const Ctx& c, Smem& sm, int s, int my_stage) {
   if (threadIdx.x == 0) {
     sm.abort = 0;
-    if (c.A.trace) sm.t_enter = wall_clock64();
+    if (c.A.trace) {
+      sm.t_enter = wall_clock64();
+      sm.t_mark[0] = sm.t_mark[1] = sm.t_mark[2] = 0;
+    }
   }
   if (s >= 0 && threadIdx.x < 64) {
     const int lane = threadIdx.x;
@@ -251,6 +255,12 @@ __device__ __forceinline__ bool wait_stage(const Ctx& c, Smem& sm, int s, int my
   return sm.abort == 0;
 }
 
+// Intra-stage trace mark i (1 weights consumed, 2 epilogue done; the input
+// staged mark is carried in a register and written with mark 1).
+__device__ __forceinline__ void mark(const Ctx& c, Smem& sm, int i) {
+  if (c.A.trace && threadIdx.x == 0) sm.t_mark[i] = wall_clock64();
+}
+
 __device__ __forceinline__ void signal_stage(const Ctx& c, Smem& sm, int s) {
   mem_done();
   __syncthreads();
@@ -263,6 +273,10 @@ __device__ __forceinline__ void signal_stage(const Ctx& c, Smem& sm, int s) {
       t[1] = sm.t_ready;
       t[2] = wall_clock64();
       t[3] = c.A.epoch;
+      t[4] = sm.t_mark[0];
+      t[5] = sm.t_mark[1];
+      t[6] = sm.t_mark[2];
+      t[7] = 0;
     }
   }
 }
@@ -584,13 +598,30 @@ __device__ __forceinline__ float stage_values(Smem& sm, int K, Get&& get) {
 }
 
 // Stage an input vector with fused RMSNorm: x_lds[k] = v[k] * g[k] / sqrt(mean(v^2) + eps).
-// `get(k)` returns v[k]. Contains barriers; all threads call it.
+// `get(k)` returns v[k]. The gains are loaded in the same batches as the
+// input, so the whole staging costs one memory round trip per batch.
+// Contains barriers; all threads call it.
 template <class Get>
 __device__ __forceinline__ void stage_rmsnorm(Smem& sm, int K, const float* gain, float eps, Get&& get) {
-  float ss = stage_values(sm, K, get);
+  float ss = 0.f;
+  for (int k0 = threadIdx.x; k0 < K; k0 += kStageBatch * kThreads) {
+    float v[kStageBatch], gv[kStageBatch];
+#pragma unroll
+    for (int i = 0; i < kStageBatch; ++i) {
+      int k = k0 + i * kThreads;
+      v[i] = k < K ? get(k) : 0.f;
+      gv[i] = gld(gain + min(k, K - 1));
+    }
+#pragma unroll
+    for (int i = 0; i < kStageBatch; ++i) {
+      int k = k0 + i * kThreads;
+      if (k < K) sm.x[k] = v[i] * gv[i];
+      ss += v[i] * v[i];
+    }
+  }
   float tot = block_sum(sm, ss);
   float rs = 1.0f / sqrtf(tot / (float)K + eps);
-  for (int k = threadIdx.x; k < K; k += kThreads) sm.x[k] = sm.x[k] * rs * gld(gain + k);
+  for (int k = threadIdx.x; k < K; k += kThreads) sm.x[k] *= rs;
   __syncthreads();
 }
 
@@ -655,13 +686,16 @@ __device__ __forceinline__ bool run_gemv(const StageEnv& E, Smem& sm, const Gemv
     return prep();
   }
   bool first = true;
+  uint64_t t_staged = 0;
   for (int ca = ra; ca < rb; ca += kRowChunk) {
     int cb = min(rb, ca + kRowChunk);
     bool ok;
     if (first) {
       ok = gemv_rows<EB, SLOT>(g, sm, ca, cb, early, [&]() {
         zero_part(sm);
-        return prep();
+        const bool r = prep();
+        if (E.c.A.trace) t_staged = wall_clock64();
+        return r;
       });
     } else {
       zero_part(sm);
@@ -674,11 +708,14 @@ __device__ __forceinline__ bool run_gemv(const StageEnv& E, Smem& sm, const Gemv
     }
     if (!ok) return false;
     first = false;
+    mark(E.c, sm, 1);
+    if (E.c.A.trace && threadIdx.x == 0 && t_staged) sm.t_mark[0] = t_staged;
     __syncthreads();
     combine_rows(sm, cb - ca);
     __syncthreads();
     epi(ca, cb - ca);
     __syncthreads();
+    mark(E.c, sm, 2);
   }
   return true;
 }
@@ -848,6 +885,25 @@ __device__ __forceinline__ bool stage_attn(const StageEnv& E, Smem& sm) {
   const int qstr = kvr + 8;             // LDS query-row stride in bf16 (padded)
   constexpr int pstr = kAttnBlock + 4;  // LDS probability-row stride in floats
   const float tau = 1.0f / sqrtf((float)qkh);
+  const uint16_t* cache = reinterpret_cast<const uint16_t*>(L.kv);
+
+  // Cache rows of a block before pos were written by earlier steps: their
+  // loads need no dependency, so the first block is issued before the wait
+  // and each later block while the previous one is being computed.
+  constexpr int kPer = (kAttnBlock * 80 + kThreads - 1) / kThreads;
+  u32x4 v[kPer];
+  auto issue_block = [&](int tb) {
+    const int nb = min(kAttnBlock, t1 - tb);
+    const int nmain = max(0, min(nb, pos - tb)) * q8n;
+#pragma unroll
+    for (int r = 0; r < kPer; ++r) {
+      int i = threadIdx.x + r * kThreads;
+      int row = i / q8n, col = i - row * q8n;
+      int ok = i < nmain;
+      v[r] = gld(reinterpret_cast<const u32x4*>(cache + (size_t)(tb + (ok ? row : 0)) * kvr) + (ok ? col : 0));
+    }
+  };
+  if (t0 < t1) issue_block(t0);
   if (!wait_stage(c, sm, E.st.wait, E.s)) return false;
 
   // LDS: query hi/lo [16][qstr] bf16, cache rows [64][kstr] u32, two score
@@ -865,23 +921,24 @@ __device__ __forceinline__ bool stage_attn(const StageEnv& E, Smem& sm) {
   {
     // scaled queries split into bf16 high and residual parts; heads >= hg are zero
     const int n = kMH * kvr;
-    for (int i0 = threadIdx.x; i0 < n; i0 += kStageBatch * kThreads) {
-      float v[kStageBatch];
+    constexpr int kQB = 24;  // 16 heads x 576 values in one batch of loads per thread
+    for (int i0 = threadIdx.x; i0 < n; i0 += kQB * kThreads) {
+      float qv[kQB];
 #pragma unroll
-      for (int b = 0; b < kStageBatch; ++b) {
+      for (int b = 0; b < kQB; ++b) {
         int i = min(i0 + b * kThreads, n - 1);
         int hh = i / kvr, k = i - hh * kvr;
         int h = grp * hg + min(hh, hg - 1);
         const float* src = k < dc ? qlat + (size_t)h * dc + k : qf + (size_t)h * qkh + d.qk_nope + (k - dc);
-        v[b] = ld_coh(src);
+        qv[b] = ld_coh(src);
       }
 #pragma unroll
-      for (int b = 0; b < kStageBatch; ++b) {
+      for (int b = 0; b < kQB; ++b) {
         int i = i0 + b * kThreads;
         if (i < n) {
           int hh = i / kvr, k = i - hh * kvr;
           __bf16 hi, lo;
-          split_bf16(hh < hg ? v[b] * tau : 0.f, hi, lo);
+          split_bf16(hh < hg ? qv[b] * tau : 0.f, hi, lo);
           qh[hh * qstr + k] = hi;
           ql[hh * qstr + k] = lo;
         }
@@ -893,7 +950,6 @@ __device__ __forceinline__ bool stage_attn(const StageEnv& E, Smem& sm) {
   const int lane = lane_id();
   const int w = wave_id();
   const int lr = lane & 15, lg = lane >> 4;
-  const uint16_t* cache = reinterpret_cast<const uint16_t*>(L.kv);
   f32x4 acc[DTILES];
 #pragma unroll
   for (int i = 0; i < DTILES; ++i) acc[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
@@ -903,16 +959,7 @@ __device__ __forceinline__ bool stage_attn(const StageEnv& E, Smem& sm) {
     // ---- stage rows [tb, tb + nb) (zeros beyond nb); the row of pos was
     // written this step by another workgroup and is read coherently
     {
-      constexpr int kPer = (kAttnBlock * 80 + kThreads - 1) / kThreads;
       const int nmain = max(0, min(nb, pos - tb)) * q8n;
-      u32x4 v[kPer];
-#pragma unroll
-      for (int r = 0; r < kPer; ++r) {
-        int i = threadIdx.x + r * kThreads;
-        int row = i / q8n, col = i - row * q8n;
-        int ok = i < nmain;
-        v[r] = gld(reinterpret_cast<const u32x4*>(cache + (size_t)(tb + (ok ? row : 0)) * kvr) + (ok ? col : 0));
-      }
       const bool cur_here = pos >= tb && pos < tb + nb;
       uint32_t cv = 0;
       if (cur_here && threadIdx.x < kvr / 2)
@@ -927,6 +974,7 @@ __device__ __forceinline__ bool stage_attn(const StageEnv& E, Smem& sm) {
           *reinterpret_cast<u32x4*>(kvs + row * kstr + col * 4) = i < nmain ? v[r] : z;
         }
       }
+      if (tb + kAttnBlock < t1) issue_block(tb + kAttnBlock);
       __syncthreads();
       if (cur_here && threadIdx.x < kvr / 2) kvs[(pos - tb) * kstr + threadIdx.x] = cv;
       __syncthreads();
@@ -1023,6 +1071,7 @@ __device__ __forceinline__ bool stage_attn(const StageEnv& E, Smem& sm) {
 }
 
 // --- UV: merge the attention partials of each head, o[h] = W_UV[h] o_lat[h]
+constexpr int kMergeBatch = 32;  // chunk accumulators in flight per thread
 __device__ __forceinline__ bool stage_uv(const StageEnv& E, Smem& sm) {
   const Ctx& c = E.c;
   const pdm_dims d = load_plan(&c.P->dims);
@@ -1039,37 +1088,37 @@ __device__ __forceinline__ bool stage_uv(const StageEnv& E, Smem& sm) {
   return run_gemv<1, 0>(E, sm, g, ra, rb, true,
       [&]() {
         if (!wait_stage(c, sm, E.st.wait, E.s)) return false;
-        int h0 = ra / d.v_head, h1 = (rb - 1) / d.v_head;
-        float* fac = sm.x + kXMax - 2 * kRowChunk;  // per-chunk max and sum, then merge weights
+        // Thread k merges latent column k of a head: the chunk maxima and sums
+        // (chunk i in lane i of every wave) and the chunk accumulators of its
+        // column are all loaded before any is used.
+        const int h0 = ra / d.v_head, h1 = (rb - 1) / d.v_head;
+        const int lane = lane_id();
+        const int k = min((int)threadIdx.x, dc - 1);
+        const bool lane_ch = lane < nch;
         for (int h = h0; h <= h1; ++h) {
           const float* ph = part + (size_t)h * nch * (dc + 2);
-          for (int i = threadIdx.x; i < nch; i += kThreads) {
-            fac[i] = ld_coh(ph + (size_t)i * (dc + 2) + dc);
-            fac[kRowChunk + i] = ld_coh(ph + (size_t)i * (dc + 2) + dc + 1);
-          }
-          __syncthreads();
-          float mx = -INFINITY;
-          for (int i = 0; i < nch; ++i) mx = fmaxf(mx, fac[i]);
-          float den = 0.f;
-          for (int i = 0; i < nch; ++i) den += fac[i] == -INFINITY ? 0.f : fac[kRowChunk + i] * __expf(fac[i] - mx);
-          __syncthreads();
-          for (int i = threadIdx.x; i < nch; i += kThreads) fac[i] = fac[i] == -INFINITY ? 0.f : __expf(fac[i] - mx) / den;
-          __syncthreads();
-          for (int k = threadIdx.x; k < dc; k += kThreads) {
-            float num = 0.f;
-            for (int i0 = 0; i0 < nch; i0 += kStageBatch) {
-              float v[kStageBatch];
+          const float* pl = ph + (size_t)(lane_ch ? lane : 0) * (dc + 2) + dc;
+          const float mi = ld_coh(pl), si = ld_coh(pl + 1);
+          float fac = 0.f, num = 0.f;
+          for (int i0 = 0; i0 < nch; i0 += kMergeBatch) {
+            float v[kMergeBatch];
 #pragma unroll
-              for (int b = 0; b < kStageBatch; ++b)
-                v[b] = i0 + b < nch ? ld_coh(ph + (size_t)(i0 + b) * (dc + 2) + k) : 0.f;
-#pragma unroll
-              for (int b = 0; b < kStageBatch; ++b)
-                if (i0 + b < nch) num += v[b] * fac[i0 + b];
+            for (int b = 0; b < kMergeBatch; ++b) v[b] = ld_coh(ph + (size_t)min(i0 + b, nch - 1) * (dc + 2) + k);
+            if (i0 == 0) {
+              const float m = lane_ch ? mi : -INFINITY;
+              const float mx = wave_max(m);
+              const float e = m == -INFINITY ? 0.f : __expf(m - mx);
+              fac = e / wave_sum(e * (lane_ch ? si : 0.f));
             }
-            sm.x[(h - h0) * dc + k] = num;
+#pragma unroll
+            for (int b = 0; b < kMergeBatch; ++b) {
+              const float f = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, fac), (i0 + b) & 63));
+              num += i0 + b < nch ? v[b] * f : 0.f;
+            }
           }
-          __syncthreads();
+          if ((int)threadIdx.x < dc) sm.x[(h - h0) * dc + threadIdx.x] = num;
         }
+        __syncthreads();
         return true;
       },
       [&](int ca, int n) {
@@ -1088,15 +1137,21 @@ __device__ __forceinline__ bool stage_wo(const StageEnv& E, Smem& sm) {
   int ra, rb;
   my_rows(E.st.rows, E.st.gran, c.G, c.wg, ra, rb);
   float* out = reinterpret_cast<float*>(L.xa);
+  const LayerInput in = layer_input(c, l);
+  // the residual (this layer's input) is complete before this stage's
+  // dependency: load the workgroup's share before waiting
+  float res = 0.f;
+  const bool res_pre = rb - ra <= kRowChunk;  // one chunk: thread t holds row ra + t
   return run_gemv<1, 0>(E, sm, g, ra, rb, true,
       [&]() {
+        if (res_pre && (int)threadIdx.x < rb - ra) res = in(ra + threadIdx.x);
         if (!wait_stage(c, sm, E.st.wait, E.s)) return false;
         stage_plain(sm, d.n_heads * d.v_head, [&](int k) { return ld_coh(o + k); });
         return true;
       },
       [&](int ca, int n) {
-        const LayerInput in = layer_input(c, l);
-        for (int t = threadIdx.x; t < n; t += kThreads) st_coh(out + ca + t, in(ca + t) + sm.part[0][t]);
+        for (int t = threadIdx.x; t < n; t += kThreads)
+          st_coh(out + ca + t, (res_pre ? res : in(ca + t)) + sm.part[0][t]);
       });
 }
 
@@ -1297,14 +1352,19 @@ __device__ __forceinline__ bool stage_down(const StageEnv& E, Smem& sm) {
     set_slots(d, L, sm, true, true);
     __syncthreads();
   }
+  // the residual x_attn is complete before this stage's dependency (the
+  // gate/up stage this workgroup already passed waited for it)
+  float res = 0.f;
+  const bool res_pre = rb - ra <= kRowChunk;  // one chunk: thread t holds row ra + t
   auto prep = [&]() {
+        if (res_pre && (int)threadIdx.x < rb - ra) res = ld_coh(xa + ra + threadIdx.x);
         if (!wait_stage(c, sm, E.st.wait, E.s)) return false;
         stage_plain(sm, K, [&](int k) { return ld_coh(act + k); });
         return true;
       };
   auto epi = [&](int ca, int n) {
         for (int t = threadIdx.x; t < n; t += kThreads)
-          st_coh(out + ca + t, round_bf16(ld_coh(xa + ca + t) + sm.part[0][t]));
+          st_coh(out + ca + t, round_bf16((res_pre ? res : ld_coh(xa + ca + t)) + sm.part[0][t]));
       };
   if (L.is_moe) return run_gemv<1, 2>(E, sm, g, ra, rb, true, prep, epi);
   return run_gemv<1, 0>(E, sm, g, ra, rb, true, prep, epi);
@@ -1419,7 +1479,10 @@ __global__ void __launch_bounds__(kThreads, 1) engine_kernel(const Plan* __restr
       case PDM_ST_LM: ok = stage_lm(E, sm); break;
       default: ok = false; break;
     }
-    if (!ok) return;  // watchdog abort: every workgroup leaves at its next wait
+    if (!ok) {  // watchdog abort: every workgroup leaves at its next wait
+      mem_done();
+      return;
+    }
     signal_stage(c, sm, s);
   }
 }

@@ -23,9 +23,10 @@ constexpr int kMaxSlots = 16;         // expert slots of one MoE stage
 constexpr int kScMax = 5120;          // LDS block-scale entries of one GEMV row chunk
 constexpr int kMaxStages = PDM_MAX_LAYERS * 12 + 4;
 constexpr int kHeadGroup = 16;        // attention heads per work unit (at most)
+constexpr int kMaxChunks = 64;        // attention position chunks per head (one per lane when merged)
 constexpr uint32_t kMagic = 0x57444d50u;  // "PDMW"
 constexpr int kHeaderBytes = 256;
-constexpr int kTraceWords = 4;        // u64 words per (stage, workgroup) trace record
+constexpr int kTraceWords = 8;        // u64 words per (stage, workgroup) trace record
 
 // Packed FP8 matrix: e4m3 codes [rows][K] row-major, then bf16 scales
 // [rows / 8][nkb] with nkb = ceil(K / 128). A scale entry covers 8 packed rows

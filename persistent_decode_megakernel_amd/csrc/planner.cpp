@@ -104,7 +104,7 @@ int build_plan(const pdm_dims& d, int32_t max_ctx, int32_t G, Plan* p, Layout* l
     int by_ctx = (int)std::max<int64_t>(1, ceil_div(max_ctx, 16));
     p->nch = std::min(by_wg, by_ctx);
   }
-  p->nch = std::min(p->nch, kRowChunk);
+  p->nch = std::min(p->nch, kMaxChunks);
   // attention LDS: query hi/lo rows [16][kvr + 8] bf16, 64 staged cache rows
   // [64][kvr / 2 + 4] u32, two score partials [2][16][68] f32, 48 head scalars
   if (kvr % 32 != 0 || p->hg > 16) return PDM_ERR_CONFIG;

@@ -151,7 +151,7 @@ class Engine:
             "n_stages": t.n_stages, "n_workgroups": t.n_workgroups, "epoch": t.epoch,
         }
         if self.trace is not None:
-            out["trace"] = self.trace.view(torch.int64).view(t.n_stages, t.n_workgroups, 4)
+            out["trace"] = self.trace.view(torch.int64).view(t.n_stages, t.n_workgroups, 8)
         return out
 
     def close(self):

@@ -4,7 +4,8 @@ A monolithic persistent kernel hides per-operator time from kernel-level
 profilers (SemiAnalysis TileRT page, challenges section). The engine
 therefore records, for every stage and workgroup, when the workgroup entered
 the stage, when its dependency wait ended and when it signalled completion
-(wall clock, 100 MHz). This module turns those records into per-stage spans,
+(wall clock, 100 MHz), plus marks inside the stage: input staged, weights
+consumed, epilogue done (0 where a stage has no such point). This module turns those records into per-stage spans,
 work and wait times and the idle fraction of the step.
 """
 from __future__ import annotations
@@ -15,7 +16,7 @@ WALLCLOCK_HZ = 100e6
 
 
 def summarize(trace: np.ndarray, plan: list, hz: float = WALLCLOCK_HZ) -> dict:
-    """trace: int64 [n_stages, n_workgroups, 4] of one step; plan: describe_plan() list."""
+    """trace: int64 [n_stages, n_workgroups, 8] of one step; plan: describe_plan() list."""
     t = trace.astype(np.float64)
     enter, ready, done = t[:, :, 0], t[:, :, 1], t[:, :, 2]
     t0 = enter.min()

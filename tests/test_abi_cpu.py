@@ -139,3 +139,21 @@ def test_plan_weight_bytes_match_active_parameters(lib):
     moe = 3 * D * cfg.moe_ffn * (cfg.top_k + cfg.n_shared) + cfg.n_experts * D * 2
     codes = 11 * attn + 3 * dense + 8 * moe + cfg.vocab * D * 2
     assert codes <= tot <= codes * 1.003 + 11 * 4 * (2 * D + cfg.q_lora + cfg.kv_lora) + 4 * D
+
+
+def test_engine_kernel_resource_usage():
+    """The persistent kernel keeps one 512-thread workgroup per CU and does not
+    fall off a spill cliff: register spills turn into scratch traffic that every
+    stage's completion wait then has to drain."""
+    import json
+    from persistent_decode_megakernel_amd import build
+    if not os.path.exists(build.USAGE):
+        pytest.skip("library not built")
+    usage = json.load(open(build.USAGE))
+    k = [v for n, v in usage.items() if "engine_kernel" in n]
+    assert len(k) == 1
+    k = k[0]
+    assert k["Occupancy [waves/SIMD]"] >= 2
+    assert k["LDS Size [bytes/block]"] <= 160 * 1024
+    assert k["ScratchSize [bytes/lane]"] <= 512, k
+    assert k["VGPRs Spill"] <= 128, k

@@ -171,3 +171,9 @@ def test_trace_records(tiny_case):
     tr = taps["trace"].cpu().numpy()
     assert (tr[:, :, 3] == taps["epoch"]).all()
     assert (tr[:, :, 2] >= tr[:, :, 1]).all() and (tr[:, :, 1] >= tr[:, :, 0]).all()
+    # intra-stage marks: 0 where a stage has none, else ordered inside [ready, done]
+    for i in (4, 5, 6):
+        m = tr[:, :, i]
+        has = m != 0
+        assert (m[has] >= tr[:, :, 1][has]).all() and (m[has] <= tr[:, :, 2][has]).all()
+    assert (tr[:, :, 7] == 0).all()
