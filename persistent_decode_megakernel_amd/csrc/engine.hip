@@ -31,6 +31,8 @@ namespace pdm {
 namespace {
 
 constexpr int kUnroll = 8;  // 1 KB units in flight per wave and buffer
+constexpr int kEarlyBatches = 1;       // unit batches per wave issued before a stage's dependency wait
+constexpr bool kScalesAfterWait = false;  // write the LDS scale table after the wait (else before)
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -76,6 +78,7 @@ struct __align__(16) Smem {
   uint64_t t_enter, t_ready;
   uint64_t t_mark[3];             // input staged, weights consumed, epilogue done
   int abort;
+  int claim;                      // next free unit batch of the current GEMV row chunk
   int last;                       // this workgroup arrived last at the LM head
 };
 
@@ -319,14 +322,6 @@ __device__ __forceinline__ void unit_ptr_t(const Gemv& g, const Smem& sm, int ro
   }
 }
 
-template <int EB>
-__device__ __forceinline__ void unit_ptr(const Gemv& g, const Smem& sm, int row, int b,
-                                         const uint8_t*& cp, const uint16_t*& sp) {
-  if (g.slot_mode == 0) unit_ptr_t<EB, 0>(g, sm, row, b, cp, sp);
-  else if (g.slot_mode == 1) unit_ptr_t<EB, 1>(g, sm, row, b, cp, sp);
-  else unit_ptr_t<EB, 2>(g, sm, row, b, cp, sp);
-}
-
 // dot of one lane's 16 bytes with the staged input
 template <int EB>
 __device__ __forceinline__ float unit_dot(const u32x4& w, const float* xs) {
@@ -363,24 +358,31 @@ __device__ __forceinline__ float unit_dot(const u32x4& w, const float* xs) {
 // LDS by store_scales() so that the caller can issue weight loads in between.
 constexpr int kScPerThread = (kScMax + kThreads - 1) / kThreads;
 
-template <int EB>
+template <int EB, int SLOT>
 __device__ __forceinline__ void load_scales(const Gemv& g, const Smem& sm, int ra, int rb, uint16_t* v) {
   if constexpr (EB != 1) return;
   const int nkbt = (g.Kb + 127) >> 7;
   const int g0 = ra >> 3;
   const int n = (((rb - 1) >> 3) - g0 + 1) * nkbt;
+  // entry i = (group gl, block kbi) with i = threadIdx.x + j * kThreads,
+  // stepped without a division per entry
+  const int qs = kThreads / nkbt, rs = kThreads - qs * nkbt;
+  int gl = (int)threadIdx.x / nkbt;
+  int kbi = (int)threadIdx.x - gl * nkbt;
 #pragma unroll
   for (int j = 0; j < kScPerThread; ++j) {
-    int i = threadIdx.x + j * kThreads;
+    const int i = threadIdx.x + j * kThreads;
     v[j] = 0;
     if (i < n) {
-      int gl = i / nkbt, kbi = i - gl * nkbt;
       int row = max(ra, (g0 + gl) << 3);
       const uint8_t* cp;
       const uint16_t* sp = nullptr;
-      unit_ptr<1>(g, sm, row, kbi << 7, cp, sp);
+      unit_ptr_t<1, SLOT>(g, sm, row, kbi << 7, cp, sp);
       v[j] = gld(sp);
     }
+    gl += qs;
+    kbi += rs;
+    if (kbi >= nkbt) { kbi -= nkbt; ++gl; }
   }
 }
 
@@ -434,19 +436,27 @@ __device__ __forceinline__ bool gemv_rows_t(const Gemv& g, Smem& sm, int ra, int
     S = (kb + 1023) >> 10;
     nunits = (rb - ra) * S;
   }
-  const int u0 = (int)((int64_t)nunits * w / kWaves);
-  const int u1 = (int)((int64_t)nunits * (w + 1) / kWaves);
+  // Units go out in batches of kUnroll. Wave w takes batch w first (issued
+  // before the dependency wait when early); later batches are claimed from an
+  // LDS counter, so waves whose loads return sooner stream more of the rows.
+  const int nbat = (nunits + kUnroll - 1) / kUnroll;
   const int nkbt = (kb + 127) >> 7;
   const int g0 = ra >> 3;
   const int lpr_mask = (1 << lg_lpr) - 1;
-
-  // (row, segment) of the next unit to issue / to compute (LONG mode)
-  int i_row = 0, i_seg = 0;
-  if constexpr (LONG) { i_row = u0 / S; i_seg = u0 - i_row * S; }
-  int c_row = i_row, c_seg = i_seg;
+  // u / S by multiply-high (exact for u < 2^32 / S)
+  const uint32_t magic = S == 1 ? 0u : 0xFFFFFFFFu / (uint32_t)S + 1u;
+  auto div_s = [&](int u) { return S == 1 ? u : (int)__umulhi((uint32_t)u, magic); };
+  auto claim = [&]() {
+    int v = 0;
+    if (lane == 0) v = __hip_atomic_fetch_add(&sm.claim, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    return __builtin_amdgcn_readlane(v, 0);
+  };
 
   u32x4 wa[kUnroll], wb[kUnroll];
-  auto issue = [&](u32x4* W, int ub) {
+  auto issue = [&](u32x4* W, int bt) {
+    const int ub = bt * kUnroll;
+    int i_row = 0, i_seg = 0;
+    if constexpr (LONG) { i_row = div_s(ub); i_seg = ub - i_row * S; }
 #pragma unroll
     for (int j = 0; j < kUnroll; ++j) {
       const int u = ub + j;
@@ -461,7 +471,7 @@ __device__ __forceinline__ bool gemv_rows_t(const Gemv& g, Smem& sm, int ra, int
         row = ra + u * m + (lane >> lg_lpr);
         b = (lane & lpr_mask) << 4;
       }
-      const bool ok = u < u1 && b < kb;
+      const bool ok = u < nunits && b < kb;
       const uint8_t* cp;
       const uint16_t* sp = nullptr;
       unit_ptr_t<EB, SLOT>(g, sm, ok ? row : ra, ok ? b : 0, cp, sp);
@@ -469,13 +479,18 @@ __device__ __forceinline__ bool gemv_rows_t(const Gemv& g, Smem& sm, int ra, int
     }
   };
 
-  int cur_row = LONG ? ra + c_row : -1;
-  float acc = 0.f;
-  auto compute = [&](const u32x4* W, int ub) {
+  // LONG rows span several units and possibly several batches (and waves):
+  // each wave adds its share of a row into its own partial.
+  auto compute = [&](const u32x4* W, int bt) {
+    const int ub = bt * kUnroll;
+    int c_row = 0, c_seg = 0;
+    if constexpr (LONG) { c_row = div_s(ub); c_seg = ub - c_row * S; }
+    int cur_row = ra + c_row;
+    float acc = 0.f;
 #pragma unroll
     for (int j = 0; j < kUnroll; ++j) {
       const int u = ub + j;
-      const bool uok = u < u1;
+      const bool uok = u < nunits;
       int row, b;
       if constexpr (LONG) {
         row = ra + c_row;
@@ -499,7 +514,7 @@ __device__ __forceinline__ bool gemv_rows_t(const Gemv& g, Smem& sm, int ra, int
         // rows change at most once per unit; flushing is a uniform branch
         if (uok && row != cur_row) {
           float t = wave_sum(acc);
-          if (lane == 0) sm.part[w][cur_row - ra] = t;
+          if (lane == 0) sm.part[w][cur_row - ra] += t;
           acc = 0.f;
           cur_row = row;
         }
@@ -509,36 +524,53 @@ __device__ __forceinline__ bool gemv_rows_t(const Gemv& g, Smem& sm, int ra, int
         if (uok && (lane & lpr_mask) == 0) sm.part[w][row - ra] = t;
       }
     }
+    if constexpr (LONG) {
+      float t = wave_sum(acc);
+      if (lane == 0) sm.part[w][cur_row - ra] += t;
+    }
   };
 
   // Weight and scale addresses that do not depend on this step's data are
   // issued before the dependency wait, so the loads are in flight while the
   // wait spins.
+  // The first two batches of each wave are static (w and w + kWaves); with
+  // `early` both are in flight during the wait. The scale table reaches LDS
+  // after the wait, when its loads have long returned.
+  // Without `early` (routed experts) the slot tables the weight and scale
+  // addresses come from are only set inside prep.
   uint16_t scv[kScPerThread];
+  int bA = w, bB = kEarlyBatches == 2 ? w + kWaves : 0;
   if (early) {
-    load_scales<EB>(g, sm, ra, rb, scv);
-    issue(wa, u0);
-    store_scales<EB>(g, sm, ra, rb, scv);
+    load_scales<EB, SLOT>(g, sm, ra, rb, scv);
+    if (bA < nbat) issue(wa, bA);
+    if (kEarlyBatches == 2 && bB < nbat) issue(wb, bB);
+    if (!kScalesAfterWait) store_scales<EB>(g, sm, ra, rb, scv);
     if (!prep()) return false;
   } else {
     if (!prep()) return false;
-    load_scales<EB>(g, sm, ra, rb, scv);
-    issue(wa, u0);
-    store_scales<EB>(g, sm, ra, rb, scv);
+    load_scales<EB, SLOT>(g, sm, ra, rb, scv);
+    if (bA < nbat) issue(wa, bA);
+    if (kEarlyBatches == 2 && bB < nbat) issue(wb, bB);
+    if (!kScalesAfterWait) store_scales<EB>(g, sm, ra, rb, scv);
+  }
+  if (kScalesAfterWait || !early) {
+    if (kScalesAfterWait) store_scales<EB>(g, sm, ra, rb, scv);
     __syncthreads();
   }
-  for (int ub = u0; ub < u1; ub += 2 * kUnroll) {
-    if (ub + kUnroll < u1) issue(wb, ub + kUnroll);
-    compute(wa, ub);
-    if (ub + kUnroll >= u1) break;
-    if (ub + 2 * kUnroll < u1) issue(wa, ub + 2 * kUnroll);
-    compute(wb, ub + kUnroll);
+  if (kEarlyBatches == 1) {
+    bB = claim();
+    if (bB < nbat) issue(wb, bB);
   }
-  if constexpr (LONG) {
-    if (u0 < u1) {
-      float t = wave_sum(acc);
-      if (lane == 0) sm.part[w][cur_row - ra] = t;
-    }
+  // Claims increase monotonically, so the batch in A is always older than the
+  // one in B and a failed claim means every later claim fails too.
+  while (bA < nbat) {
+    compute(wa, bA);
+    bA = claim();
+    if (bA < nbat) issue(wa, bA);
+    if (bB >= nbat) break;
+    compute(wb, bB);
+    bB = claim();
+    if (bB < nbat) issue(wb, bB);
   }
   return true;
 }
@@ -552,9 +584,9 @@ __device__ __forceinline__ bool gemv_rows(const Gemv& g, Smem& sm, int ra, int r
 
 // Balanced contiguous share of `rows` (in groups of `gran`) for workgroup wg.
 __device__ __forceinline__ void my_rows(int rows, int gran, int G, int wg, int& ra, int& rb) {
-  int ng = rows / gran;
-  ra = (int)((int64_t)ng * wg / G) * gran;
-  rb = (int)((int64_t)ng * (wg + 1) / G) * gran;
+  const int ng = rows / gran;  // ng * G < 2^31 for every plan shape
+  ra = ng * wg / G * gran;
+  rb = ng * (wg + 1) / G * gran;
 }
 
 // Sum the per-wave partials of rows [0, n) of the chunk into part[0][*].
@@ -567,9 +599,12 @@ __device__ __forceinline__ void combine_rows(Smem& sm, int n) {
   }
 }
 
+// Zero the per-wave partials and reset the batch counter (the first
+// kEarlyBatches batches of every wave are taken statically).
 __device__ __forceinline__ void zero_part(Smem& sm) {
   float* p = &sm.part[0][0];
   for (int i = threadIdx.x; i < kWaves * kRowChunk; i += kThreads) p[i] = 0.f;
+  if (threadIdx.x == 0) sm.claim = kEarlyBatches * kWaves;
 }
 
 // Copy K values get(k) into sm.x with all loads of a batch in flight at once
@@ -699,8 +734,8 @@ __device__ __forceinline__ bool run_gemv(const StageEnv& E, Smem& sm, const Gemv
       });
     } else {
       zero_part(sm);
-      // the early path stores the scale table before the barrier in prep;
-      // later chunks need it (and the zeroed partials) visible before use
+      // later chunks need the zeroed partials and batch counter visible
+      // before their first claim
       ok = gemv_rows<EB, SLOT>(g, sm, ca, cb, true, [&]() {
         __syncthreads();
         return true;
