@@ -33,6 +33,11 @@ namespace {
 constexpr int kUnroll = 8;  // 1 KB units in flight per wave and buffer
 constexpr int kEarlyBatches = 1;       // unit batches per wave issued before a stage's dependency wait
 constexpr bool kScalesAfterWait = false;  // write the LDS scale table after the wait (else before)
+// The last wave of a workgroup polls the dependency counters and issues no
+// load before the wait: loads complete in order per wave, so a poll issued
+// behind a batch of weight loads would only return after them.
+constexpr int kPollWave = kWaves - 1;
+constexpr int kPreThreads = kPollWave * 64;  // threads that may issue loads before a wait
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -227,8 +232,8 @@ __device__ __forceinline__ bool wait_stage(const Ctx& c, Smem& sm, int s, int my
       sm.t_mark[0] = sm.t_mark[1] = sm.t_mark[2] = 0;
     }
   }
-  if (s >= 0 && threadIdx.x < 64) {
-    const int lane = threadIdx.x;
+  if (s >= 0 && wave_id() == kPollWave) {
+    const int lane = lane_id();
     const int* ctr = counter_ptr(c, s, lane & (kStripes - 1));
     const int target = (int)c.A.epoch * stripe_count(c.G, lane & (kStripes - 1));
     const GLOBAL_AS unsigned long long* st = gp(reinterpret_cast<const unsigned long long*>(c.P->status));
@@ -258,8 +263,9 @@ __device__ __forceinline__ bool wait_stage(const Ctx& c, Smem& sm, int s, int my
   return sm.abort == 0;
 }
 
-// Intra-stage trace mark i (1 weights consumed, 2 epilogue done; the input
-// staged mark is carried in a register and written with mark 1).
+// Intra-stage trace mark i (0 input staged, 1 weights consumed (attention:
+// blocks done), 2 epilogue done). GEMV stages carry the staged time in a
+// register and write it with mark 1.
 __device__ __forceinline__ void mark(const Ctx& c, Smem& sm, int i) {
   if (c.A.trace && threadIdx.x == 0) sm.t_mark[i] = wall_clock64();
 }
@@ -356,7 +362,8 @@ __device__ __forceinline__ float unit_dot(const u32x4& w, const float* xs) {
 // Scale table of rows [ra, rb) in LDS: sm.sc[((row >> 3) - (ra >> 3)) * nkbt + (b >> 7)],
 // nkbt = ceil(Kb / 128). The loads are issued here; the values are written to
 // LDS by store_scales() so that the caller can issue weight loads in between.
-constexpr int kScPerThread = (kScMax + kThreads - 1) / kThreads;
+constexpr int kScThreads = kPreThreads;  // the polling wave loads none of the table
+constexpr int kScPerThread = (kScMax + kScThreads - 1) / kScThreads;
 
 template <int EB, int SLOT>
 __device__ __forceinline__ void load_scales(const Gemv& g, const Smem& sm, int ra, int rb, uint16_t* v) {
@@ -364,14 +371,15 @@ __device__ __forceinline__ void load_scales(const Gemv& g, const Smem& sm, int r
   const int nkbt = (g.Kb + 127) >> 7;
   const int g0 = ra >> 3;
   const int n = (((rb - 1) >> 3) - g0 + 1) * nkbt;
-  // entry i = (group gl, block kbi) with i = threadIdx.x + j * kThreads,
+  if ((int)threadIdx.x >= kScThreads) return;
+  // entry i = (group gl, block kbi) with i = threadIdx.x + j * kScThreads,
   // stepped without a division per entry
-  const int qs = kThreads / nkbt, rs = kThreads - qs * nkbt;
+  const int qs = kScThreads / nkbt, rs = kScThreads - qs * nkbt;
   int gl = (int)threadIdx.x / nkbt;
   int kbi = (int)threadIdx.x - gl * nkbt;
 #pragma unroll
   for (int j = 0; j < kScPerThread; ++j) {
-    const int i = threadIdx.x + j * kThreads;
+    const int i = threadIdx.x + j * kScThreads;
     v[j] = 0;
     if (i < n) {
       int row = max(ra, (g0 + gl) << 3);
@@ -389,11 +397,12 @@ __device__ __forceinline__ void load_scales(const Gemv& g, const Smem& sm, int r
 template <int EB>
 __device__ __forceinline__ void store_scales(const Gemv& g, Smem& sm, int ra, int rb, const uint16_t* v) {
   if constexpr (EB != 1) return;
+  if ((int)threadIdx.x >= kScThreads) return;
   const int nkbt = (g.Kb + 127) >> 7;
   const int n = (((rb - 1) >> 3) - (ra >> 3) + 1) * nkbt;
 #pragma unroll
   for (int j = 0; j < kScPerThread; ++j) {
-    int i = threadIdx.x + j * kThreads;
+    int i = threadIdx.x + j * kScThreads;
     if (i < n) sm.sc[i] = v[j];
   }
 }
@@ -539,7 +548,8 @@ __device__ __forceinline__ bool gemv_rows_t(const Gemv& g, Smem& sm, int ra, int
   // Without `early` (routed experts) the slot tables the weight and scale
   // addresses come from are only set inside prep.
   uint16_t scv[kScPerThread];
-  int bA = w, bB = kEarlyBatches == 2 ? w + kWaves : 0;
+  constexpr int kStat = kWaves - 1;  // waves with static batches (not the polling wave)
+  int bA = w < kStat ? w : nbat, bB = kEarlyBatches == 2 && w < kStat ? w + kStat : nbat;
   if (early) {
     load_scales<EB, SLOT>(g, sm, ra, rb, scv);
     if (bA < nbat) issue(wa, bA);
@@ -557,7 +567,11 @@ __device__ __forceinline__ bool gemv_rows_t(const Gemv& g, Smem& sm, int ra, int
     if (kScalesAfterWait) store_scales<EB>(g, sm, ra, rb, scv);
     __syncthreads();
   }
-  if (kEarlyBatches == 1) {
+  if (w == kPollWave) {  // no static batch: claim the first one too
+    bA = claim();
+    if (bA < nbat) issue(wa, bA);
+  }
+  if (kEarlyBatches == 1 || w == kPollWave) {
     bB = claim();
     if (bB < nbat) issue(wb, bB);
   }
@@ -600,11 +614,11 @@ __device__ __forceinline__ void combine_rows(Smem& sm, int n) {
 }
 
 // Zero the per-wave partials and reset the batch counter (the first
-// kEarlyBatches batches of every wave are taken statically).
+// kEarlyBatches batches of every wave but the polling wave are static).
 __device__ __forceinline__ void zero_part(Smem& sm) {
   float* p = &sm.part[0][0];
   for (int i = threadIdx.x; i < kWaves * kRowChunk; i += kThreads) p[i] = 0.f;
-  if (threadIdx.x == 0) sm.claim = kEarlyBatches * kWaves;
+  if (threadIdx.x == 0) sm.claim = kEarlyBatches * (kWaves - 1);
 }
 
 // Copy K values get(k) into sm.x with all loads of a batch in flight at once
@@ -925,14 +939,17 @@ __device__ __forceinline__ bool stage_attn(const StageEnv& E, Smem& sm) {
   // Cache rows of a block before pos were written by earlier steps: their
   // loads need no dependency, so the first block is issued before the wait
   // and each later block while the previous one is being computed.
-  constexpr int kPer = (kAttnBlock * 80 + kThreads - 1) / kThreads;
+  // (threads of the polling wave load none of them)
+  constexpr int kPer = (kAttnBlock * 80 + kPreThreads - 1) / kPreThreads;
   u32x4 v[kPer];
+  const bool loader = (int)threadIdx.x < kPreThreads;
   auto issue_block = [&](int tb) {
+    if (!loader) return;
     const int nb = min(kAttnBlock, t1 - tb);
     const int nmain = max(0, min(nb, pos - tb)) * q8n;
 #pragma unroll
     for (int r = 0; r < kPer; ++r) {
-      int i = threadIdx.x + r * kThreads;
+      int i = threadIdx.x + r * kPreThreads;
       int row = i / q8n, col = i - row * q8n;
       int ok = i < nmain;
       v[r] = gld(reinterpret_cast<const u32x4*>(cache + (size_t)(tb + (ok ? row : 0)) * kvr) + (ok ? col : 0));
@@ -980,6 +997,7 @@ __device__ __forceinline__ bool stage_attn(const StageEnv& E, Smem& sm) {
       }
     }
     if (threadIdx.x < kMH) { hm[threadIdx.x] = -INFINITY; hl[threadIdx.x] = 0.f; }
+    mark(c, sm, 0);
   }
 
   const int lane = lane_id();
@@ -1002,8 +1020,8 @@ __device__ __forceinline__ bool stage_attn(const StageEnv& E, Smem& sm) {
       __syncthreads();  // the previous round's readers are done with kvs and sp
 #pragma unroll
       for (int r = 0; r < kPer; ++r) {
-        int i = threadIdx.x + r * kThreads;
-        if (i < kAttnBlock * q8n) {
+        int i = threadIdx.x + r * kPreThreads;
+        if (loader && i < kAttnBlock * q8n) {
           int row = i / q8n, col = i - row * q8n;
           u32x4 z = {0u, 0u, 0u, 0u};
           *reinterpret_cast<u32x4*>(kvs + row * kstr + col * 4) = i < nmain ? v[r] : z;
@@ -1086,6 +1104,7 @@ __device__ __forceinline__ bool stage_attn(const StageEnv& E, Smem& sm) {
     }
   }
   __syncthreads();
+  mark(c, sm, 1);
   // ---- partials: acc[i][r] = O[head 4*lg + r][dim (w*DTILES + i)*16 + lr]
   float* part = reinterpret_cast<float*>(L.attn_part);
 #pragma unroll
@@ -1102,6 +1121,7 @@ __device__ __forceinline__ bool stage_attn(const StageEnv& E, Smem& sm) {
     st_coh(dst + dc, hm[threadIdx.x]);
     st_coh(dst + dc + 1, hl[threadIdx.x]);
   }
+  mark(c, sm, 2);
   return true;
 }
 
