@@ -100,6 +100,8 @@ def main():
     ap.add_argument("--workload", default="dsv3_stack_1k")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--trace-detail", action="store_true",
+                    help="also print the per-stage phase breakdown of the fastest traced step (stderr)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this engine runs batch-1 decode on one GPU; multi-GPU runs are not "
@@ -182,14 +184,18 @@ def main():
     plan = describe_plan(cfg, max_ctx, eng.sizes.n_workgroups)
     fill_cache()
     eng.set_trace(True)
-    sums = []
+    sums, traces = [], []
     for j in range(4):
         step(j)
         eng.status()
-        sums.append(T.summarize(eng.taps()["trace"].cpu().numpy(), plan))
+        traces.append(eng.taps()["trace"].cpu().numpy().copy())
+        sums.append(T.summarize(traces[-1], plan))
     eng.set_trace(False)
-    best = min(sums, key=lambda x: x["total_us"])
+    best_i = min(range(len(sums)), key=lambda i: sums[i]["total_us"])
+    best = sums[best_i]
     log("traced step (per stage type):\n" + T.format_table(best))
+    if args.trace_detail:
+        log("traced step (per stage):\n" + T.format_phases(T.phases(traces[best_i], plan)))
     out = {
         "metric": "batch-1 decode tokens/s/user",
         "value": round(1.0 / tpot, 3),

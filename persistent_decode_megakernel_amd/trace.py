@@ -59,3 +59,46 @@ def format_table(summary: dict) -> str:
     for k, a in sorted(by_type(summary).items(), key=lambda kv: -kv[1]["span_us"]):
         lines.append(f"{k:>10} {a['count']:>5} {a['span_us']:>9.1f} {a['weight_bytes'] / 1e6:>9.1f} {a['GBps']:>7.0f}")
     return "\n".join(lines)
+
+
+def phases(trace: np.ndarray, plan: list, hz: float = WALLCLOCK_HZ) -> list:
+    """Per-stage breakdown of one step from the 8-word records: mean and max
+    over workgroups of wait (entered -> dependency satisfied), stage (-> input
+    staged), stream (-> weights consumed), epi (-> epilogue done), ack (->
+    signalled) and gap (signalled -> entered the next stage). Phases a stage
+    does not mark are None."""
+    t = trace.astype(np.float64) * (1e6 / hz)
+    enter, ready, done = t[:, :, 0], t[:, :, 1], t[:, :, 2]
+    m0, m1, m2 = t[:, :, 4], t[:, :, 5], t[:, :, 6]
+    has = (trace[:, :, 4] != 0) & (trace[:, :, 5] != 0) & (trace[:, :, 6] != 0)
+    t0 = enter.min()
+    out = []
+    prev_end = t0
+    for s, st in enumerate(plan):
+        def mm(v, sel=None):
+            v = v if sel is None else v[sel]
+            return None if v.size == 0 else (float(v.mean()), float(v.max()))
+        h = has[s]
+        row = {"stage": s, "type": st["type"], "layer": st["layer"],
+               "span_us": float(done[s].max() - prev_end), "start_us": float(enter[s].min() - t0),
+               "wait": mm(ready[s] - enter[s]),
+               "stage_in": mm(m0[s] - ready[s], h), "stream": mm(m1[s] - m0[s], h),
+               "epi": mm(m2[s] - m1[s], h), "ack": mm(done[s] - m2[s], h),
+               "gap": mm(enter[s + 1] - done[s]) if s + 1 < len(plan) else None}
+        out.append(row)
+        prev_end = max(prev_end, done[s].max())
+    return out
+
+
+def format_phases(rows: list) -> str:
+    def f(v):
+        return f"{'-':>11}" if v is None else f"{v[0]:5.1f}[{v[1]:4.1f}]"
+    lines = ["per stage, mean[max] over workgroups (us): wait = entered -> dependency satisfied, stage = -> input "
+             "staged, stream = -> weights consumed, epi = -> epilogue done, ack = -> signalled, gap = -> next "
+             "stage entered",
+             f"{'st':>3} {'type':>9} {'L':>2} {'span':>6} {'start':>7} {'wait':>11} {'stage':>11} {'stream':>11} "
+             f"{'epi':>11} {'ack':>11} {'gap':>11}"]
+    for r in rows:
+        lines.append(f"{r['stage']:>3} {r['type']:>9} {r['layer']:>2} {r['span_us']:>6.1f} {r['start_us']:>7.1f} "
+                     f"{f(r['wait'])} {f(r['stage_in'])} {f(r['stream'])} {f(r['epi'])} {f(r['ack'])} {f(r['gap'])}")
+    return "\n".join(lines)
