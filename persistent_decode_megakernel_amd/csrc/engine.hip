@@ -680,6 +680,26 @@ __device__ __forceinline__ void stage_plain(Smem& sm, int K, Get&& get) {
   __syncthreads();
 }
 
+// LDS DMA copy by the calling wave of `nbytes` (a multiple of 16) from a
+// 16-byte aligned global address into LDS: 16 bytes per lane and 1 KB per
+// instruction, no registers held. Lanes past the end re-read the last 16
+// bytes and write up to 1 KB - 16 bytes past the end of `dst` (callers leave
+// that much LDS slack). A coherent copy uses the sc1 cache policy, as a
+// relaxed agent-scope atomic load does, for data written this step by other
+// workgroups. The caller waits for completion (vmcnt) before using the data.
+constexpr unsigned kCpolSc1 = 16;
+
+__device__ __forceinline__ void dma_to_lds(void* dst, const void* src, int nbytes) {
+  const int lane = lane_id();
+  const char* sb = reinterpret_cast<const char*>(src);
+  char* db = reinterpret_cast<char*>(dst);
+  for (int off = 0; off < nbytes; off += 1024) {
+    const int o = min(off + lane * 16, nbytes - 16);
+    __builtin_amdgcn_global_load_lds((const GLOBAL_AS void*)(sb + o),
+                                     (__attribute__((address_space(3))) void*)(db + off), 16, 0, kCpolSc1);
+  }
+}
+
 // ------------------------------------------------------------------ stage bodies
 
 struct StageEnv {
@@ -971,30 +991,36 @@ __device__ __forceinline__ bool stage_attn(const StageEnv& E, Smem& sm) {
   const float* qlat = reinterpret_cast<const float*>(L.ql);
   const float* qf = reinterpret_cast<const float*>(L.q);
   {
+    // The polling wave, which has no cache-row loads queued ahead of it,
+    // copies the head group's queries into the (not yet used) cache-row area:
+    // q_lat [hg][dc] in one piece, then the rotary parts [hg][dr] (one piece
+    // per head, several pieces per DMA instruction).
+    float* raw = reinterpret_cast<float*>(kvs);
+    const int qbytes = hg * dc * 4;
+    float* rawpe = raw + ((qbytes + 1023) & ~1023) / 4;
+    if (wave_id() == kPollWave) {
+      dma_to_lds(raw, qlat + (size_t)grp * hg * dc, qbytes);
+      const int lpp = dr / 4;       // lanes per rotary piece (16 bytes each)
+      const int ppi = 64 / lpp;     // pieces per instruction
+      const int lane = lane_id();
+      for (int p0 = 0; p0 < hg; p0 += ppi) {
+        const int p = min(p0 + lane / lpp, hg - 1);
+        const float* src = qf + (size_t)(grp * hg + p) * qkh + d.qk_nope + (lane % lpp) * 4;
+        __builtin_amdgcn_global_load_lds((const GLOBAL_AS void*)src,
+                                         (__attribute__((address_space(3))) void*)(rawpe + p0 * dr), 16, 0, kCpolSc1);
+      }
+      mem_done();
+    }
+    __syncthreads();
     // scaled queries split into bf16 high and residual parts; heads >= hg are zero
     const int n = kMH * kvr;
-    constexpr int kQB = 24;  // 16 heads x 576 values in one batch of loads per thread
-    for (int i0 = threadIdx.x; i0 < n; i0 += kQB * kThreads) {
-      float qv[kQB];
-#pragma unroll
-      for (int b = 0; b < kQB; ++b) {
-        int i = min(i0 + b * kThreads, n - 1);
-        int hh = i / kvr, k = i - hh * kvr;
-        int h = grp * hg + min(hh, hg - 1);
-        const float* src = k < dc ? qlat + (size_t)h * dc + k : qf + (size_t)h * qkh + d.qk_nope + (k - dc);
-        qv[b] = ld_coh(src);
-      }
-#pragma unroll
-      for (int b = 0; b < kQB; ++b) {
-        int i = i0 + b * kThreads;
-        if (i < n) {
-          int hh = i / kvr, k = i - hh * kvr;
-          __bf16 hi, lo;
-          split_bf16(hh < hg ? qv[b] * tau : 0.f, hi, lo);
-          qh[hh * qstr + k] = hi;
-          ql[hh * qstr + k] = lo;
-        }
-      }
+    for (int i = threadIdx.x; i < n; i += kThreads) {
+      const int hh = i / kvr, k = i - hh * kvr;
+      const float q = hh < hg ? (k < dc ? raw[hh * dc + k] : rawpe[hh * dr + (k - dc)]) : 0.f;
+      __bf16 hi, lo;
+      split_bf16(q * tau, hi, lo);
+      qh[hh * qstr + k] = hi;
+      ql[hh * qstr + k] = lo;
     }
     if (threadIdx.x < kMH) { hm[threadIdx.x] = -INFINITY; hl[threadIdx.x] = 0.f; }
     mark(c, sm, 0);
@@ -1143,11 +1169,40 @@ __device__ __forceinline__ bool stage_uv(const StageEnv& E, Smem& sm) {
   return run_gemv<1, 0>(E, sm, g, ra, rb, true,
       [&]() {
         if (!wait_stage(c, sm, E.st.wait, E.s)) return false;
-        // Thread k merges latent column k of a head: the chunk maxima and sums
-        // (chunk i in lane i of every wave) and the chunk accumulators of its
-        // column are all loaded before any is used.
         const int h0 = ra / d.v_head, h1 = (rb - 1) / d.v_head;
         const int lane = lane_id();
+        const int hbytes = nch * (dc + 2) * 4;  // partials of one head
+        if (h0 == h1 && (hbytes & 15) == 0 && 4096 + hbytes + 1024 <= kXMax * 4) {
+          // One head: the polling wave (no weight loads queued ahead of it)
+          // copies its partials into LDS with coherent DMA; thread k then
+          // merges latent column k from LDS (chunk i's maximum and sum in
+          // lane i of every wave).
+          const float* ph = part + (size_t)h0 * nch * (dc + 2);
+          float* pr = sm.x + 1024;
+          if (wave_id() == kPollWave) {
+            dma_to_lds(pr, ph, hbytes);
+            mem_done();
+          }
+          __syncthreads();
+          const bool lane_ch = lane < nch;
+          const float m = lane_ch ? pr[lane * (dc + 2) + dc] : -INFINITY;
+          const float sv = lane_ch ? pr[lane * (dc + 2) + dc + 1] : 0.f;
+          const float mx = wave_max(m);
+          const float e = m == -INFINITY ? 0.f : __expf(m - mx);
+          const float fac = e / wave_sum(e * sv);
+          if ((int)threadIdx.x < dc) {
+            float num = 0.f;
+            for (int i = 0; i < nch; ++i)
+              num += pr[i * (dc + 2) + threadIdx.x] *
+                     __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, fac), i));
+            sm.x[threadIdx.x] = num;
+          }
+          __syncthreads();
+          return true;
+        }
+        // Several heads: thread k merges latent column k of each head, with
+        // the chunk maxima and sums (chunk i in lane i of every wave) and the
+        // chunk accumulators of its column all loaded before any is used.
         const int k = min((int)threadIdx.x, dc - 1);
         const bool lane_ch = lane < nch;
         for (int h = h0; h <= h1; ++h) {
