@@ -165,6 +165,15 @@ __device__ __forceinline__ float wave_max(float v) {
   float d = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 48));
   return fmaxf(fmaxf(a, b), fmaxf(c, d));
 }
+// minimum over the 64 lanes of an int, returned uniform
+__device__ __forceinline__ int wave_min_i(int v) {
+  v = min(v, __builtin_amdgcn_update_dpp(0, v, kDppXor1, 0xF, 0xF, false));
+  v = min(v, __builtin_amdgcn_update_dpp(0, v, kDppXor2, 0xF, 0xF, false));
+  v = min(v, __builtin_amdgcn_update_dpp(0, v, kDppHalfMirror, 0xF, 0xF, false));
+  v = min(v, __builtin_amdgcn_update_dpp(0, v, kDppMirror, 0xF, 0xF, false));
+  return min(min(__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 16)),
+             min(__builtin_amdgcn_readlane(v, 32), __builtin_amdgcn_readlane(v, 48)));
+}
 // sum within aligned groups of `gs` lanes (gs a power of two <= 64); every lane gets its group sum
 __device__ __forceinline__ float group_sum(float v, int gs) {
   if (gs >= 2) v += dpp<kDppXor1>(v);
@@ -1307,27 +1316,25 @@ __device__ __forceinline__ void route_topk(const Ctx& c, Smem& sm, const LayerPl
     }
     float wsum = 0.f;
     for (int j = 0; j < k; ++j) {
-      // lane-local best (lowest index among equal values: scan in increasing index order)
+      // lane-local best: scanning in increasing index order with a strict
+      // compare keeps the lowest index among equal values
       float bv = -INFINITY;
       int bi = 0x7fffffff;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         int e = lane + 64 * i;
-        if (e < E && (v[i] > bv || (v[i] == bv && e < bi))) { bv = v[i]; bi = e; }
+        if (e < E && v[i] > bv) { bv = v[i]; bi = e; }
       }
-      // wave argmax
-      for (int off = 1; off < 64; off <<= 1) {
-        float ov = __shfl_xor(bv, off);
-        int oi = __shfl_xor(bi, off);
-        if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
-      }
-      if (bi >= E) bi = 0;  // only when no finite logit is left (never for finite inputs)
+      // wave maximum, then the lowest index holding it (DPP reductions)
+      const float gm = wave_max(bv);
+      int bw = wave_min_i(bv == gm ? bi : 0x7fffffff);
+      if (bw >= E) bw = 0;  // only when no finite logit is left (never for finite inputs)
       // remove it
 #pragma unroll
       for (int i = 0; i < 16; ++i)
-        if (lane + 64 * i == bi) v[i] = -INFINITY;
-      float sg = 1.0f / (1.0f + __expf(-bv));
-      if (lane == 0) { sm.route_idx[j] = bi; sm.route_w[j] = sg; }
+        if (lane + 64 * i == bw) v[i] = -INFINITY;
+      float sg = 1.0f / (1.0f + __expf(-gm));
+      if (lane == 0) { sm.route_idx[j] = bw; sm.route_w[j] = sg; }
       wsum += sg;
     }
     if (lane == 0) {
