@@ -1407,14 +1407,22 @@ __device__ __forceinline__ bool stage_gu(const StageEnv& E, Smem& sm, bool route
     set_slots(d, L, sm, false, false);
     __syncthreads();
   }
+  // With x_staged the normalised input is still in LDS from the router stage
+  // this workgroup ran before (which waited for x_attn); the routed stage
+  // still waits for the router logits.
+  const bool reuse = E.st.x_staged != 0;
   auto prep = [&]() {
-        if (!wait_stage(c, sm, E.st.wait, E.s)) return false;
+        if (!wait_stage(c, sm, reuse && !routed ? -1 : E.st.wait, E.s)) return false;
         if (routed) {
           route_topk(c, sm, L, c.wg == 0);
           set_slots(d, L, sm, true, false);
         }
-        stage_rmsnorm(sm, d.hidden, reinterpret_cast<const float*>(L.ffn_norm), d.rms_eps,
-                      [&](int k) { return ld_coh(xa + k); });
+        if (reuse) {
+          __syncthreads();  // slot tables
+        } else {
+          stage_rmsnorm(sm, d.hidden, reinterpret_cast<const float*>(L.ffn_norm), d.rms_eps,
+                        [&](int k) { return ld_coh(xa + k); });
+        }
         return true;
       };
   auto epi = [&](int ca, int n) {

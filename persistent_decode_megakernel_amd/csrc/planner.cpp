@@ -180,9 +180,15 @@ int build_plan(const pdm_dims& d, int32_t max_ctx, int32_t G, Plan* p, Layout* l
       int s_gu = add(PDM_ST_GU, l, s_wo, 2 * d.ffn, D, std::max(16, unit_rows(D, 1)));
       last = add(PDM_ST_DOWN, l, s_gu, D, d.ffn, unit_rows(d.ffn, 1));
     } else {
+      // router, shared and routed gate/up all read RMSNorm(x_attn): the router
+      // stage stages it and the two gate/up stages reuse it from LDS
       int s_rt = add(PDM_ST_ROUTER, l, s_wo, d.n_experts, D, unit_rows(D, 2));
-      if (d.n_shared > 0) add(PDM_ST_GU, l, s_wo, 2 * d.moe_ffn * d.n_shared, D, std::max(16, unit_rows(D, 1)));
+      if (d.n_shared > 0) {
+        int s_sh = add(PDM_ST_GU, l, s_wo, 2 * d.moe_ffn * d.n_shared, D, std::max(16, unit_rows(D, 1)));
+        p->stages[s_sh].x_staged = 1;
+      }
       int s_gr = add(PDM_ST_GU_ROUTED, l, s_rt, 2 * d.moe_ffn * d.top_k, D, std::max(16, unit_rows(D, 1)));
+      p->stages[s_gr].x_staged = 1;
       int kslots = (d.top_k + d.n_shared) * d.moe_ffn;
       last = add(PDM_ST_DOWN, l, s_gr, D, kslots, unit_rows(kslots, 1));
     }
