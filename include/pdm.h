@@ -168,8 +168,8 @@ enum pdm_stage_type {
   PDM_ST_UV = 4,       /* merge partials, o[h] = W_UV[h] o_lat[h] */
   PDM_ST_WO = 5,       /* x += W_O o */
   PDM_ST_ROUTER = 6,   /* router logits W_r * RMSNorm(x) */
-  PDM_ST_GU = 7,       /* SwiGLU gate/up of the dense FFN or of the shared experts */
-  PDM_ST_GU_ROUTED = 8,/* SwiGLU gate/up of the top-k routed experts */
+  PDM_ST_GU = 7,       /* SwiGLU gate/up of the dense FFN */
+  PDM_ST_GU_ROUTED = 8,/* top-k routing, SwiGLU gate/up of the shared and the routed experts */
   PDM_ST_DOWN = 9,     /* x += sum of down projections (weighted), bf16 layer output */
   PDM_ST_LM = 10       /* logits = W_lm * RMSNorm(x), argmax */
 };

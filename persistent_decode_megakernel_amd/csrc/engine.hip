@@ -32,7 +32,6 @@ namespace {
 
 constexpr int kUnroll = 8;  // 1 KB units in flight per wave and buffer
 constexpr int kEarlyBatches = 1;       // unit batches per wave issued before a stage's dependency wait
-constexpr bool kScalesAfterWait = false;  // write the LDS scale table after the wait (else before)
 // The last wave of a workgroup polls the dependency counters and issues no
 // load before the wait: loads complete in order per wave, so a poll issued
 // behind a batch of weight loads would only return after them.
@@ -315,6 +314,11 @@ struct Gemv {
   int lg_rpv;               // rows per input vector = 1 << lg_rpv (31: one shared vector)
   int vbase;                // first staged vector
   int xK;                   // floats per staged vector
+  // two-segment row map (SLOT 3): local rows [0, seg_n1) are row slot rows
+  // seg_p1 + r, the rest seg_p2 + (r - seg_n1); with `split` only the first
+  // segment's addresses are known before prep
+  int seg_n1, seg_p1, seg_p2;
+  int split;
 };
 
 // Address of the 16 bytes a lane reads for (row, byte offset b) and its scale.
@@ -324,9 +328,11 @@ __device__ __forceinline__ void unit_ptr_t(const Gemv& g, const Smem& sm, int ro
   if constexpr (SLOT == 0) {
     cp = g.codes + (size_t)row * g.Kb + b;
     if (EB == 1) sp = g.scales + (size_t)(row >> 3) * g.nkb + (b >> 7);
-  } else if constexpr (SLOT == 1) {
-    int j = row >> g.lg_slot;
-    int rr = row & ((1 << g.lg_slot) - 1);
+  } else if constexpr (SLOT == 1 || SLOT == 3) {
+    int pr = row;
+    if constexpr (SLOT == 3) pr = row < g.seg_n1 ? g.seg_p1 + row : g.seg_p2 + (row - g.seg_n1);
+    int j = pr >> g.lg_slot;
+    int rr = pr & ((1 << g.lg_slot) - 1);
     cp = sm.slot_codes[j] + (size_t)rr * g.slot_Kb + b;
     if (EB == 1) sp = sm.slot_scales[j] + (size_t)(rr >> 3) * g.nkb + (b >> 7);
   } else {
@@ -548,34 +554,37 @@ __device__ __forceinline__ bool gemv_rows_t(const Gemv& g, Smem& sm, int ra, int
     }
   };
 
-  // Weight and scale addresses that do not depend on this step's data are
-  // issued before the dependency wait, so the loads are in flight while the
-  // wait spins.
-  // The first two batches of each wave are static (w and w + kWaves); with
-  // `early` both are in flight during the wait. The scale table reaches LDS
-  // after the wait, when its loads have long returned.
-  // Without `early` (routed experts) the slot tables the weight and scale
-  // addresses come from are only set inside prep.
+  // With `early`, weight and scale addresses do not depend on this step's
+  // data: the scale table goes to LDS and each static wave's first batch is
+  // in flight before prep (the dependency wait). Without it (slot tables set
+  // inside prep) everything follows prep. With g.split only the batches
+  // inside the first row segment go out before prep, and the scale table is
+  // loaded after it.
   uint16_t scv[kScPerThread];
   constexpr int kStat = kWaves - 1;  // waves with static batches (not the polling wave)
   int bA = w < kStat ? w : nbat, bB = kEarlyBatches == 2 && w < kStat ? w + kStat : nbat;
+  const bool early_s = early && !g.split;
+  const int ebat = !g.split ? nbat : min(nbat, (LONG ? g.seg_n1 * S : g.seg_n1 / m) / kUnroll);
   if (early) {
-    load_scales<EB, SLOT>(g, sm, ra, rb, scv);
-    if (bA < nbat) issue(wa, bA);
-    if (kEarlyBatches == 2 && bB < nbat) issue(wb, bB);
-    if (!kScalesAfterWait) store_scales<EB>(g, sm, ra, rb, scv);
+    if (early_s) load_scales<EB, SLOT>(g, sm, ra, rb, scv);
+    if (bA < ebat) issue(wa, bA);
+    if (kEarlyBatches == 2 && bB < ebat) issue(wb, bB);
+    if (early_s) store_scales<EB>(g, sm, ra, rb, scv);
     if (!prep()) return false;
+    if (!early_s) {
+      load_scales<EB, SLOT>(g, sm, ra, rb, scv);
+      if (bA >= ebat && bA < nbat) issue(wa, bA);
+      if (kEarlyBatches == 2 && bB >= ebat && bB < nbat) issue(wb, bB);
+      store_scales<EB>(g, sm, ra, rb, scv);
+    }
   } else {
     if (!prep()) return false;
     load_scales<EB, SLOT>(g, sm, ra, rb, scv);
     if (bA < nbat) issue(wa, bA);
     if (kEarlyBatches == 2 && bB < nbat) issue(wb, bB);
-    if (!kScalesAfterWait) store_scales<EB>(g, sm, ra, rb, scv);
+    store_scales<EB>(g, sm, ra, rb, scv);
   }
-  if (kScalesAfterWait || !early) {
-    if (kScalesAfterWait) store_scales<EB>(g, sm, ra, rb, scv);
-    __syncthreads();
-  }
+  if (!early_s) __syncthreads();  // scale table
   if (w == kPollWave) {  // no static batch: claim the first one too
     bA = claim();
     if (bA < nbat) issue(wa, bA);
@@ -1300,14 +1309,15 @@ __device__ __forceinline__ bool stage_router(const StageEnv& E, Smem& sm) {
 }
 
 // Top-k of the router logits by one wave (ties to the lower index), written to
-// the slot tables with sigmoid weights normalised over the chosen experts.
+// LDS with sigmoid weights normalised over the chosen experts.
 // Must be called by all threads; contains barriers.
 __device__ __forceinline__ void route_topk(const Ctx& c, Smem& sm, const LayerPlan& L, bool write_tap) {
   const pdm_dims d = load_plan(&c.P->dims);
   const float* z = reinterpret_cast<const float*>(L.router_logits);
   const int E = d.n_experts, k = d.top_k;
-  if (threadIdx.x < 64) {
-    const int lane = threadIdx.x;
+  // the polling wave: it has no weight loads queued ahead of the logits
+  if (wave_id() == kPollWave) {
+    const int lane = lane_id();
     float v[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
@@ -1348,75 +1358,94 @@ __device__ __forceinline__ void route_topk(const Ctx& c, Smem& sm, const LayerPl
   }
 }
 
-// Slot tables of an MoE stage: expert block pointers (gate/up or down part),
-// weights and act offsets. Routed slots use the layer's top-k in LDS.
-__device__ __forceinline__ void set_slots(const pdm_dims& d, const LayerPlan& L, Smem& sm, bool routed, bool down) {
+// Slot tables of a MoE stage: expert matrix pointers, gate weights and act
+// offsets. Gate/up (row slots): shared experts in slots [0, n_shared) (which
+// need no routing), routed experts in [n_shared, n_shared + top_k). Down
+// (K slots, in act order): routed experts first, then the shared ones. Routed
+// slots use the layer's top-k in LDS.
+__device__ __forceinline__ void set_slots(const pdm_dims& d, const LayerPlan& L, Smem& sm, bool shared, bool routed,
+                                          bool down) {
   const int t = threadIdx.x;
-  const int n = down ? d.top_k + d.n_shared : (routed ? d.top_k : d.n_shared);
-  if (t < n) {
-    int e, act;
-    float w;
-    if (down) {
-      e = t < d.top_k ? sm.route_idx[t] : d.n_experts + (t - d.top_k);
-      w = 1.f;
-      act = t * d.moe_ffn;
-    } else if (routed) {
-      e = sm.route_idx[t];
-      w = sm.route_w[t];
-      act = t * d.moe_ffn;
-    } else {
-      e = d.n_experts + t;
-      w = 1.f;
-      act = (d.top_k + t) * d.moe_ffn;
-    }
+  const int ns = d.n_shared, k = d.top_k;
+  if (t < ns + k) {
+    const bool is_shared = down ? t >= k : t < ns;
+    if (is_shared ? !shared : !routed) return;
+    const int i = down ? (is_shared ? t - k : t) : (is_shared ? t : t - ns);  // index among its kind
+    const int e = is_shared ? d.n_experts + i : sm.route_idx[i];
     const uint8_t* base = reinterpret_cast<const uint8_t*>(L.expert_base) + (size_t)e * L.expert_stride;
     const Fp8Mat& m = down ? L.edown : L.egu;
     sm.slot_codes[t] = base + m.codes;
     sm.slot_scales[t] = reinterpret_cast<const uint16_t*>(base + m.scales);
-    sm.slot_w[t] = w;
-    sm.slot_act[t] = act;
+    sm.slot_w[t] = down || is_shared ? 1.f : sm.route_w[i];
+    sm.slot_act[t] = (is_shared ? k + i : i) * d.moe_ffn;
   }
 }
 
-// --- GU: SwiGLU gate/up of dense FFN, shared experts, or routed experts
-__device__ __forceinline__ bool stage_gu(const StageEnv& E, Smem& sm, bool routed) {
+// --- GU: SwiGLU gate/up of the dense FFN (rows gate/up interleaved in groups of 8)
+__device__ __forceinline__ bool stage_gu(const StageEnv& E, Smem& sm) {
   const Ctx& c = E.c;
   const pdm_dims d = load_plan(&c.P->dims);
   const LayerPlan L = layer_of(c, E.st.layer);
   const float* xa = reinterpret_cast<const float*>(L.xa);
   float* act = reinterpret_cast<float*>(L.act);
+  Gemv g = gemv_of(L.gu);
+  int ra, rb;
+  my_rows(E.st.rows, E.st.gran, c.G, c.wg, ra, rb);
+  return run_gemv<1, 0>(E, sm, g, ra, rb, true,
+      [&]() {
+        if (!wait_stage(c, sm, E.st.wait, E.s)) return false;
+        stage_rmsnorm(sm, d.hidden, reinterpret_cast<const float*>(L.ffn_norm), d.rms_eps,
+                      [&](int k) { return ld_coh(xa + k); });
+        return true;
+      },
+      [&](int ca, int n) {
+        // rows [gate 8 ; up 8] per group of 16: pair row (ca >> 1) + t
+        for (int t = threadIdx.x; t < n / 2; t += kThreads) {
+          int grp = t >> 3, r = t & 7;
+          float gt = sm.part[0][grp * 16 + r];
+          float up = sm.part[0][grp * 16 + 8 + r];
+          st_coh(act + (ca >> 1) + t, silu(gt) * up);
+        }
+      });
+}
+
+// --- GU (MoE): SwiGLU gate/up of the shared and the top-k routed experts in
+// one stage. Each workgroup takes a share of the shared-expert rows and a
+// share of the routed rows; the shared rows come first, so their weight loads
+// go out before the wait for the router logits and stream while this
+// workgroup computes the top-k. The router stage this workgroup ran last
+// already staged RMSNorm(x_attn) in LDS (kStXStaged).
+__device__ __forceinline__ bool stage_gu_moe(const StageEnv& E, Smem& sm) {
+  const Ctx& c = E.c;
+  const pdm_dims d = load_plan(&c.P->dims);
+  const LayerPlan L = layer_of(c, E.st.layer);
+  const float* xa = reinterpret_cast<const float*>(L.xa);
+  float* act = reinterpret_cast<float*>(L.act);
+  const int F = d.moe_ffn;
+  const int rows_sh = 2 * F * d.n_shared;  // row slots [0, n_shared) hold the shared experts
   Gemv g{};
   g.lg_rpv = 31;
   g.Kb = d.hidden;
-  int F;  // intermediate per slot
-  if (!L.is_moe) {
-    g = gemv_of(L.gu);
-    F = d.ffn;
-  } else {
-    g.slot_mode = 1;
-    g.lg_slot = 31 - __builtin_clz(2 * d.moe_ffn);
-    g.slot_Kb = d.hidden;
-    g.nkb = L.egu.nkb;
-    F = d.moe_ffn;
-  }
-  int ra, rb;
-  my_rows(E.st.rows, E.st.gran, c.G, c.wg, ra, rb);
-  // shared-expert and dense pointers are static: set them before the early
-  // weight loads; routed pointers need the router output (after the wait)
-  if (L.is_moe && !routed) {
-    set_slots(d, L, sm, false, false);
-    __syncthreads();
-  }
-  // With x_staged the normalised input is still in LDS from the router stage
-  // this workgroup ran before (which waited for x_attn); the routed stage
-  // still waits for the router logits.
-  const bool reuse = E.st.x_staged != 0;
-  auto prep = [&]() {
-        if (!wait_stage(c, sm, reuse && !routed ? -1 : E.st.wait, E.s)) return false;
-        if (routed) {
-          route_topk(c, sm, L, c.wg == 0);
-          set_slots(d, L, sm, true, false);
-        }
+  g.slot_mode = 1;
+  g.lg_slot = 31 - __builtin_clz(2 * F);
+  g.slot_Kb = d.hidden;
+  g.nkb = L.egu.nkb;
+  int p1, e1, p2, e2;
+  my_rows(rows_sh, E.st.gran, c.G, c.wg, p1, e1);
+  my_rows(2 * F * d.top_k, E.st.gran, c.G, c.wg, p2, e2);
+  g.seg_n1 = e1 - p1;
+  g.seg_p1 = p1;
+  g.seg_p2 = rows_sh + p2;
+  g.split = 1;
+  const int n = (e1 - p1) + (e2 - p2);
+  const bool reuse = (E.st.flags & kStXStaged) != 0;
+  set_slots(d, L, sm, true, false, false);
+  __syncthreads();
+  return run_gemv<1, 3>(E, sm, g, 0, n, true,
+      [&]() {
+        if (!wait_stage(c, sm, E.st.wait, E.s)) return false;
+        route_topk(c, sm, L, c.wg == 0);
+        set_slots(d, L, sm, false, true, false);
         if (reuse) {
           __syncthreads();  // slot tables
         } else {
@@ -1424,28 +1453,20 @@ __device__ __forceinline__ bool stage_gu(const StageEnv& E, Smem& sm, bool route
                         [&](int k) { return ld_coh(xa + k); });
         }
         return true;
-      };
-  auto epi = [&](int ca, int n) {
-        // rows are gate/up interleaved in groups of 8: [gate 8 ; up 8]
-        for (int t = threadIdx.x; t < n / 2; t += kThreads) {
+      },
+      [&](int ca, int nr) {
+        for (int t = threadIdx.x; t < nr / 2; t += kThreads) {
           int grp = t >> 3, r = t & 7;
           float gt = sm.part[0][grp * 16 + r];
           float up = sm.part[0][grp * 16 + 8 + r];
-          int pr = (ca >> 1) + t;  // pair row across all slots
-          float a = silu(gt) * up;
-          int dst;
-          if (L.is_moe) {
-            int j = pr / F, f = pr - j * F;
-            a *= sm.slot_w[j];
-            dst = sm.slot_act[j] + f;
-          } else {
-            dst = pr;
-          }
-          st_coh(act + dst, a);
+          // local gate row -> row-slot row -> pair row across all slots
+          const int lr = ca + grp * 16 + r;
+          const int pr = lr < g.seg_n1 ? g.seg_p1 + lr : g.seg_p2 + (lr - g.seg_n1);
+          const int pair = (pr >> 4) * 8 + (pr & 7);
+          const int j = pair / F, f = pair - j * F;
+          st_coh(act + sm.slot_act[j] + f, silu(gt) * up * sm.slot_w[j]);
         }
-      };
-  if (L.is_moe) return run_gemv<1, 1>(E, sm, g, ra, rb, !routed, prep, epi);
-  return run_gemv<1, 0>(E, sm, g, ra, rb, true, prep, epi);
+      });
 }
 
 // --- DOWN: x_out = bf16(x_attn + sum_slots W_down[slot] act[slot])
@@ -1472,9 +1493,9 @@ __device__ __forceinline__ bool stage_down(const StageEnv& E, Smem& sm) {
   }
   int ra, rb;
   my_rows(E.st.rows, E.st.gran, c.G, c.wg, ra, rb);
-  // the layer's routing is already in LDS (set by the routed gate/up stage)
+  // the layer's routing is already in LDS (computed by the gate/up stage)
   if (L.is_moe) {
-    set_slots(d, L, sm, true, true);
+    set_slots(d, L, sm, true, true, true);
     __syncthreads();
   }
   // the residual x_attn is complete before this stage's dependency (the
@@ -1598,8 +1619,8 @@ __global__ void __launch_bounds__(kThreads, 1) engine_kernel(const Plan* __restr
       case PDM_ST_UV: ok = stage_uv(E, sm); break;
       case PDM_ST_WO: ok = stage_wo(E, sm); break;
       case PDM_ST_ROUTER: ok = stage_router(E, sm); break;
-      case PDM_ST_GU: ok = stage_gu(E, sm, false); break;
-      case PDM_ST_GU_ROUTED: ok = stage_gu(E, sm, true); break;
+      case PDM_ST_GU: ok = stage_gu(E, sm); break;
+      case PDM_ST_GU_ROUTED: ok = stage_gu_moe(E, sm); break;
       case PDM_ST_DOWN: ok = stage_down(E, sm); break;
       case PDM_ST_LM: ok = stage_lm(E, sm); break;
       default: ok = false; break;

@@ -81,10 +81,12 @@ struct StagePlan {
   int32_t rows;
   int32_t K;
   int32_t gran;    // row-split granularity
-  int32_t x_staged;  // 1: the input vector the previous stage staged in LDS is this stage's input too
-                     //    (same workgroup, so a wait this stage's input alone would need is skipped)
+  int32_t flags;   // kSt* bits below
   int32_t pad;
 };
+
+// StagePlan flags. Consecutive stages of one workgroup share LDS:
+constexpr int kStXStaged = 1;  // the input the previous stage staged in LDS is this stage's input
 
 struct Plan {
   pdm_dims dims;

@@ -180,15 +180,12 @@ int build_plan(const pdm_dims& d, int32_t max_ctx, int32_t G, Plan* p, Layout* l
       int s_gu = add(PDM_ST_GU, l, s_wo, 2 * d.ffn, D, std::max(16, unit_rows(D, 1)));
       last = add(PDM_ST_DOWN, l, s_gu, D, d.ffn, unit_rows(d.ffn, 1));
     } else {
-      // router, shared and routed gate/up all read RMSNorm(x_attn): the router
-      // stage stages it and the two gate/up stages reuse it from LDS
+      // Router and gate/up both read RMSNorm(x_attn): the router stage stages
+      // it and the gate/up stage (shared and routed experts) reuses it from LDS.
       int s_rt = add(PDM_ST_ROUTER, l, s_wo, d.n_experts, D, unit_rows(D, 2));
-      if (d.n_shared > 0) {
-        int s_sh = add(PDM_ST_GU, l, s_wo, 2 * d.moe_ffn * d.n_shared, D, std::max(16, unit_rows(D, 1)));
-        p->stages[s_sh].x_staged = 1;
-      }
-      int s_gr = add(PDM_ST_GU_ROUTED, l, s_rt, 2 * d.moe_ffn * d.top_k, D, std::max(16, unit_rows(D, 1)));
-      p->stages[s_gr].x_staged = 1;
+      int s_gr = add(PDM_ST_GU_ROUTED, l, s_rt, 2 * d.moe_ffn * (d.n_shared + d.top_k), D,
+                     std::max(16, unit_rows(D, 1)));
+      p->stages[s_gr].flags = kStXStaged;
       int kslots = (d.top_k + d.n_shared) * d.moe_ffn;
       last = add(PDM_ST_DOWN, l, s_gr, D, kslots, unit_rows(kslots, 1));
     }
@@ -289,11 +286,10 @@ void stage_info(const Plan& p, int s, pdm_stage_info* o) {
       o->weight_bytes = (uint64_t)d.n_experts * d.hidden * 2 + (uint64_t)d.hidden * 4; break;
     case PDM_ST_GU:
       o->reads[0] = id(PDM_BUF_XATTN, l); o->writes[0] = id(PDM_BUF_ACT, l);
-      o->weight_bytes = L.is_moe ? fp8b(L.egu) * d.n_shared : fp8b(L.gu);
-      break;
+      o->weight_bytes = fp8b(L.gu); break;
     case PDM_ST_GU_ROUTED:
       o->reads[0] = id(PDM_BUF_XATTN, l); o->reads[1] = id(PDM_BUF_ROUTER, l); o->writes[0] = id(PDM_BUF_ACT, l);
-      o->weight_bytes = fp8b(L.egu) * d.top_k; break;
+      o->weight_bytes = fp8b(L.egu) * (d.top_k + d.n_shared); break;
     case PDM_ST_DOWN:
       o->reads[0] = id(PDM_BUF_ACT, l); o->reads[1] = id(PDM_BUF_XATTN, l); o->writes[0] = id(PDM_BUF_XOUT, l);
       if (L.is_moe) o->reads[2] = id(PDM_BUF_ROUTER, l);

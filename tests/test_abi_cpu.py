@@ -112,7 +112,7 @@ def test_stage_plan_is_a_valid_dag(lib, name):
     cfg = configs.get(name)
     plan = describe_plan(cfg, cfg.prompt_len + cfg.decode_steps)
     _validate_dag(plan, cfg)
-    per_layer = {"dense": 8, "moe": 9 + (1 if cfg.n_shared else 0)}
+    per_layer = {"dense": 8, "moe": 9}
     assert len(plan) == sum(per_layer[k] for k in cfg.layers) + (1 if cfg.vocab else 0)
 
 
