@@ -37,6 +37,7 @@ constexpr int kEarlyBatches = 1;       // unit batches per wave issued before a 
 // behind a batch of weight loads would only return after them.
 constexpr int kPollWave = kWaves - 1;
 constexpr int kPreThreads = kPollWave * 64;  // threads that may issue loads before a wait
+static_assert((512 + 128) / 2 <= kPreThreads, "cache-row pairs fit the loading threads");
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -846,11 +847,57 @@ __device__ __forceinline__ bool stage_qb(const StageEnv& E, Smem& sm) {
   int ra, rb;
   my_rows(E.st.rows, E.st.gran, c.G, c.wg, ra, rb);
   float* out = reinterpret_cast<float*>(L.q);
+  // The last workgroup also appends this step's cache row
+  // [RMSNorm(kv latent) ; RoPE(rotary key)] (bf16, at position pos). Thread p
+  // owns the value pair 2p, 2p + 1: its gains or rotation come from static
+  // data and are loaded before the wait, its latent values are loaded with
+  // the query staging (one round trip for both), and the row is written
+  // before the weights are consumed.
+  const bool app = c.wg == c.G - 1;
+  const int npairs = (d.kv_lora + d.rope) / 2;  // <= kPreThreads: the polling wave holds none
+  const int p = threadIdx.x;
+  const bool own = app && p < npairs;
+  const bool is_lat = 2 * p < d.kv_lora;
+  float ga = 0.f, gb = 0.f;  // gains (latent pairs) or (cos, sin) (rotary pairs)
+  const float* kvr = raw + d.q_lora;
   bool ok = run_gemv<1, 0>(E, sm, g, ra, rb, true,
       [&]() {
+        if (own) {
+          if (is_lat) {
+            const float* gk = reinterpret_cast<const float*>(L.kv_norm) + 2 * p;
+            ga = gld(gk);
+            gb = gld(gk + 1);
+          } else {
+            const int i = p - d.kv_lora / 2;
+            ga = gld(tab + 2 * i);
+            gb = gld(tab + 2 * i + 1);
+          }
+        }
         if (!wait_stage(c, sm, E.st.wait, E.s)) return false;
+        float x0 = 0.f, x1 = 0.f;
+        if (own) {
+          x0 = ld_coh(kvr + 2 * p);
+          x1 = ld_coh(kvr + 2 * p + 1);
+        }
         stage_rmsnorm(sm, d.q_lora, reinterpret_cast<const float*>(L.q_norm), d.rms_eps,
                       [&](int k) { return ld_coh(raw + k); });
+        if (app) {
+          const float tot = block_sum(sm, own && is_lat ? x0 * x0 + x1 * x1 : 0.f);
+          const float rs = 1.0f / sqrtf(tot / (float)d.kv_lora + d.rms_eps);
+          if (own) {
+            float a, b;
+            if (is_lat) {
+              a = x0 * rs * ga;
+              b = x1 * rs * gb;
+            } else {
+              a = x0 * ga - x1 * gb;
+              b = x0 * gb + x1 * ga;
+            }
+            uint32_t* row = reinterpret_cast<uint32_t*>(reinterpret_cast<uint16_t*>(L.kv) +
+                                                        (size_t)c.A.pos * (d.kv_lora + d.rope));
+            st_coh_u(row + p, (uint32_t)bf16_bits(a) | ((uint32_t)bf16_bits(b) << 16));
+          }
+        }
         return true;
       },
       [&](int ca, int n) {
@@ -867,34 +914,7 @@ __device__ __forceinline__ bool stage_qb(const StageEnv& E, Smem& sm) {
           st_coh(out + r, y);
         }
       });
-  if (!ok) return false;
-  if (c.wg == c.G - 1) {
-    // cache row: [RMSNorm(kv latent) ; RoPE(rotary key)] in bf16 at position pos
-    const float* kvr = raw + d.q_lora;
-    float ss = 0.f;
-    for (int k = threadIdx.x; k < d.kv_lora; k += kThreads) { float v = ld_coh(kvr + k); ss += v * v; }
-    float tot = block_sum(sm, ss);
-    float rs = 1.0f / sqrtf(tot / (float)d.kv_lora + d.rms_eps);
-    const float* gk = reinterpret_cast<const float*>(L.kv_norm);
-    uint32_t* row = reinterpret_cast<uint32_t*>(reinterpret_cast<uint16_t*>(L.kv) + (size_t)c.A.pos * (d.kv_lora + d.rope));
-    const int npairs = (d.kv_lora + d.rope) / 2;
-    for (int p = threadIdx.x; p < npairs; p += kThreads) {
-      float a, b;
-      int k = 2 * p;
-      if (k < d.kv_lora) {
-        a = ld_coh(kvr + k) * rs * gld(gk + k);
-        b = ld_coh(kvr + k + 1) * rs * gld(gk + k + 1);
-      } else {
-        int i = (k - d.kv_lora) >> 1;
-        float x0 = ld_coh(kvr + k), x1 = ld_coh(kvr + k + 1);
-        float cs = gld(tab + 2 * i), sn = gld(tab + 2 * i + 1);
-        a = x0 * cs - x1 * sn;
-        b = x0 * sn + x1 * cs;
-      }
-      st_coh_u(row + p, (uint32_t)bf16_bits(a) | ((uint32_t)bf16_bits(b) << 16));
-    }
-  }
-  return true;
+  return ok;
 }
 
 // --- ABSORB: q_lat[h] = W_UK[h]^T q_nope[h]  (rows (h, c), K = d_n, per-head input)
