@@ -71,7 +71,6 @@ __device__ __forceinline__ void gst(T* p, T v) { *gpw(p) = v; }
 struct __align__(16) Smem {
   float x[kXMax];                 // staged input vector(s) of the current stage
   float part[kWaves][kRowChunk];  // per-wave row partial sums
-  uint16_t sc[kScMax];            // block scales of the current row chunk
   const uint8_t* slot_codes[kMaxSlots];
   const uint16_t* slot_scales[kMaxSlots];
   float slot_w[kMaxSlots];
@@ -375,53 +374,6 @@ __device__ __forceinline__ float unit_dot(const u32x4& w, const float* xs) {
   return acc;
 }
 
-// Scale table of rows [ra, rb) in LDS: sm.sc[((row >> 3) - (ra >> 3)) * nkbt + (b >> 7)],
-// nkbt = ceil(Kb / 128). The loads are issued here; the values are written to
-// LDS by store_scales() so that the caller can issue weight loads in between.
-constexpr int kScThreads = kPreThreads;  // the polling wave loads none of the table
-constexpr int kScPerThread = (kScMax + kScThreads - 1) / kScThreads;
-
-template <int EB, int SLOT>
-__device__ __forceinline__ void load_scales(const Gemv& g, const Smem& sm, int ra, int rb, uint16_t* v) {
-  if constexpr (EB != 1) return;
-  const int nkbt = (g.Kb + 127) >> 7;
-  const int g0 = ra >> 3;
-  const int n = (((rb - 1) >> 3) - g0 + 1) * nkbt;
-  if ((int)threadIdx.x >= kScThreads) return;
-  // entry i = (group gl, block kbi) with i = threadIdx.x + j * kScThreads,
-  // stepped without a division per entry
-  const int qs = kScThreads / nkbt, rs = kScThreads - qs * nkbt;
-  int gl = (int)threadIdx.x / nkbt;
-  int kbi = (int)threadIdx.x - gl * nkbt;
-#pragma unroll
-  for (int j = 0; j < kScPerThread; ++j) {
-    const int i = threadIdx.x + j * kScThreads;
-    v[j] = 0;
-    if (i < n) {
-      int row = max(ra, (g0 + gl) << 3);
-      const uint8_t* cp;
-      const uint16_t* sp = nullptr;
-      unit_ptr_t<1, SLOT>(g, sm, row, kbi << 7, cp, sp);
-      v[j] = gld(sp);
-    }
-    gl += qs;
-    kbi += rs;
-    if (kbi >= nkbt) { kbi -= nkbt; ++gl; }
-  }
-}
-
-template <int EB>
-__device__ __forceinline__ void store_scales(const Gemv& g, Smem& sm, int ra, int rb, const uint16_t* v) {
-  if constexpr (EB != 1) return;
-  if ((int)threadIdx.x >= kScThreads) return;
-  const int nkbt = (g.Kb + 127) >> 7;
-  const int n = (((rb - 1) >> 3) - (ra >> 3) + 1) * nkbt;
-#pragma unroll
-  for (int j = 0; j < kScPerThread; ++j) {
-    int i = threadIdx.x + j * kScThreads;
-    if (i < n) sm.sc[i] = v[j];
-  }
-}
 
 // Sum within aligned groups of 2^lg lanes (lg <= 6) without branches.
 __device__ __forceinline__ float group_sum_lg(float v, int lg) {
@@ -465,8 +417,6 @@ __device__ __forceinline__ bool gemv_rows_t(const Gemv& g, Smem& sm, int ra, int
   // before the dependency wait when early); later batches are claimed from an
   // LDS counter, so waves whose loads return sooner stream more of the rows.
   const int nbat = (nunits + kUnroll - 1) / kUnroll;
-  const int nkbt = (kb + 127) >> 7;
-  const int g0 = ra >> 3;
   const int lpr_mask = (1 << lg_lpr) - 1;
   // u / S by multiply-high (exact for u < 2^32 / S)
   const uint32_t magic = S == 1 ? 0u : 0xFFFFFFFFu / (uint32_t)S + 1u;
@@ -477,8 +427,12 @@ __device__ __forceinline__ bool gemv_rows_t(const Gemv& g, Smem& sm, int ra, int
     return __builtin_amdgcn_readlane(v, 0);
   };
 
+  // A batch: each lane's 16 code bytes of kUnroll units and, for FP8, the
+  // block scale each 16 bytes belong to, loaded alongside (the scale lines of
+  // a row group are shared by its 8 rows and come from cache after the first).
   u32x4 wa[kUnroll], wb[kUnroll];
-  auto issue = [&](u32x4* W, int bt) {
+  uint32_t sa[kUnroll], sb[kUnroll];
+  auto issue = [&](u32x4* W, uint32_t* SC, int bt) {
     const int ub = bt * kUnroll;
     int i_row = 0, i_seg = 0;
     if constexpr (LONG) { i_row = div_s(ub); i_seg = ub - i_row * S; }
@@ -501,12 +455,13 @@ __device__ __forceinline__ bool gemv_rows_t(const Gemv& g, Smem& sm, int ra, int
       const uint16_t* sp = nullptr;
       unit_ptr_t<EB, SLOT>(g, sm, ok ? row : ra, ok ? b : 0, cp, sp);
       W[j] = __builtin_nontemporal_load(gp(reinterpret_cast<const u32x4*>(cp)));
+      if constexpr (EB == 1) SC[j] = gld(sp);
     }
   };
 
   // LONG rows span several units and possibly several batches (and waves):
   // each wave adds its share of a row into its own partial.
-  auto compute = [&](const u32x4* W, int bt) {
+  auto compute = [&](const u32x4* W, const uint32_t* SC, int bt) {
     const int ub = bt * kUnroll;
     int c_row = 0, c_seg = 0;
     if constexpr (LONG) { c_row = div_s(ub); c_seg = ub - c_row * S; }
@@ -533,7 +488,7 @@ __device__ __forceinline__ bool gemv_rows_t(const Gemv& g, Smem& sm, int ra, int
       const int k0 = (EB == 1) ? bq : (bq >> 1);
       const int xoff = (g.lg_rpv >= 31) ? 0 : ((rq >> g.lg_rpv) - g.vbase) * g.xK;
       float d = unit_dot<EB>(W[j], sm.x + xoff + k0);
-      if constexpr (EB == 1) d *= bf16_val(sm.sc[((rq >> 3) - g0) * nkbt + (bq >> 7)]);
+      if constexpr (EB == 1) d *= bf16_val((uint16_t)SC[j]);
       d = ok ? d : 0.f;
       if constexpr (LONG) {
         // rows change at most once per unit; flushing is a uniform branch
@@ -556,54 +511,36 @@ __device__ __forceinline__ bool gemv_rows_t(const Gemv& g, Smem& sm, int ra, int
   };
 
   // With `early`, weight and scale addresses do not depend on this step's
-  // data: the scale table goes to LDS and each static wave's first batch is
-  // in flight before prep (the dependency wait). Without it (slot tables set
-  // inside prep) everything follows prep. With g.split only the batches
-  // inside the first row segment go out before prep, and the scale table is
-  // loaded after it.
-  uint16_t scv[kScPerThread];
+  // data: each static wave's first batch is in flight before prep (the
+  // dependency wait). Without it (slot tables set inside prep) everything
+  // follows prep. With g.split only the batches inside the first row segment
+  // go out before prep.
   constexpr int kStat = kWaves - 1;  // waves with static batches (not the polling wave)
   int bA = w < kStat ? w : nbat, bB = kEarlyBatches == 2 && w < kStat ? w + kStat : nbat;
-  const bool early_s = early && !g.split;
-  const int ebat = !g.split ? nbat : min(nbat, (LONG ? g.seg_n1 * S : g.seg_n1 / m) / kUnroll);
-  if (early) {
-    if (early_s) load_scales<EB, SLOT>(g, sm, ra, rb, scv);
-    if (bA < ebat) issue(wa, bA);
-    if (kEarlyBatches == 2 && bB < ebat) issue(wb, bB);
-    if (early_s) store_scales<EB>(g, sm, ra, rb, scv);
-    if (!prep()) return false;
-    if (!early_s) {
-      load_scales<EB, SLOT>(g, sm, ra, rb, scv);
-      if (bA >= ebat && bA < nbat) issue(wa, bA);
-      if (kEarlyBatches == 2 && bB >= ebat && bB < nbat) issue(wb, bB);
-      store_scales<EB>(g, sm, ra, rb, scv);
-    }
-  } else {
-    if (!prep()) return false;
-    load_scales<EB, SLOT>(g, sm, ra, rb, scv);
-    if (bA < nbat) issue(wa, bA);
-    if (kEarlyBatches == 2 && bB < nbat) issue(wb, bB);
-    store_scales<EB>(g, sm, ra, rb, scv);
-  }
-  if (!early_s) __syncthreads();  // scale table
+  const int ebat = !early ? 0 : !g.split ? nbat : min(nbat, (LONG ? g.seg_n1 * S : g.seg_n1 / m) / kUnroll);
+  if (bA < ebat) issue(wa, sa, bA);
+  if (kEarlyBatches == 2 && bB < ebat) issue(wb, sb, bB);
+  if (!prep()) return false;
+  if (bA >= ebat && bA < nbat) issue(wa, sa, bA);
+  if (kEarlyBatches == 2 && bB >= ebat && bB < nbat) issue(wb, sb, bB);
   if (w == kPollWave) {  // no static batch: claim the first one too
     bA = claim();
-    if (bA < nbat) issue(wa, bA);
+    if (bA < nbat) issue(wa, sa, bA);
   }
   if (kEarlyBatches == 1 || w == kPollWave) {
     bB = claim();
-    if (bB < nbat) issue(wb, bB);
+    if (bB < nbat) issue(wb, sb, bB);
   }
   // Claims increase monotonically, so the batch in A is always older than the
   // one in B and a failed claim means every later claim fails too.
   while (bA < nbat) {
-    compute(wa, bA);
+    compute(wa, sa, bA);
     bA = claim();
-    if (bA < nbat) issue(wa, bA);
+    if (bA < nbat) issue(wa, sa, bA);
     if (bB >= nbat) break;
-    compute(wb, bB);
+    compute(wb, sb, bB);
     bB = claim();
-    if (bB < nbat) issue(wb, bB);
+    if (bB < nbat) issue(wb, sb, bB);
   }
   return true;
 }

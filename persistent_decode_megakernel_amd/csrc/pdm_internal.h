@@ -20,7 +20,6 @@ constexpr int kCounterStride = 32;    // ints between counters (128 B)
 constexpr int kRowChunk = 256;        // rows combined per LDS pass
 constexpr int kXMax = 32768;          // floats of staged activation per workgroup (128 KB)
 constexpr int kMaxSlots = 16;         // expert slots of one MoE stage
-constexpr int kScMax = 5120;          // LDS block-scale entries of one GEMV row chunk
 constexpr int kMaxStages = PDM_MAX_LAYERS * 12 + 4;
 constexpr int kHeadGroup = 16;        // attention heads per work unit (at most)
 constexpr int kMaxChunks = 64;        // attention position chunks per head (one per lane when merged)

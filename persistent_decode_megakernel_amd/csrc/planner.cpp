@@ -41,13 +41,6 @@ int validate_dims(const pdm_dims& d, int32_t max_ctx) {
   if (d.qk_nope < 1024 && (!is_pow2(d.qk_nope) || 1024 / d.qk_nope > d.kv_lora)) return PDM_ERR_CONFIG;
   if (d.kv_lora < 1024 && 1024 / d.kv_lora > d.v_head) return PDM_ERR_CONFIG;
   if (!(d.rms_eps >= 0.f) || !(d.rope_base > 1.f)) return PDM_ERR_CONFIG;
-  // a row chunk's block-scale table must fit the engine's LDS table
-  {
-    int64_t kmax = std::max<int64_t>({d.hidden, d.q_lora, (int64_t)d.n_heads * d.v_head, d.kv_lora, d.qk_nope});
-    if (any_dense) kmax = std::max<int64_t>(kmax, d.ffn);
-    if (any_moe) kmax = std::max<int64_t>(kmax, (int64_t)(d.top_k + d.n_shared) * d.moe_ffn);
-    if ((kRowChunk / 8 + 1) * ceil_div(kmax, 128) > kScMax) return PDM_ERR_CONFIG;
-  }
   return PDM_OK;
 }
 
