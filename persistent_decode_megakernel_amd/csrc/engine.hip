@@ -83,6 +83,7 @@ struct __align__(16) Smem {
   uint64_t t_mark[3];             // input staged, weights consumed, epilogue done
   int abort;
   int claim;                      // next free unit batch of the current GEMV row chunk
+  int slots_ready;                // the routed slot tables of the current MoE gate/up stage are set
   int last;                       // this workgroup arrived last at the LM head
 };
 
@@ -398,8 +399,14 @@ __device__ __forceinline__ float group_sum_lg(float v, int lg) {
 // the wave's range read a valid address and are dropped): with no branch
 // around the loads the compiler waits only for the batch being consumed, so
 // the next batch stays in flight.
-template <int EB, bool LONG, int SLOT, class Prep>
-__device__ __forceinline__ bool gemv_rows_t(const Gemv& g, Smem& sm, int ra, int rb, bool early, Prep&& prep) {
+// Work that only the polling wave does after prep (none by default).
+struct NoLate {
+  __device__ __forceinline__ void operator()() const {}
+};
+
+template <int EB, bool LONG, int SLOT, class Prep, class Late>
+__device__ __forceinline__ bool gemv_rows_t(const Gemv& g, Smem& sm, int ra, int rb, bool early, Prep&& prep,
+                                            Late&& late) {
   const int lane = lane_id();
   const int w = wave_id();
   const int kb = g.Kb;
@@ -521,7 +528,24 @@ __device__ __forceinline__ bool gemv_rows_t(const Gemv& g, Smem& sm, int ra, int
   if (bA < ebat) issue(wa, sa, bA);
   if (kEarlyBatches == 2 && bB < ebat) issue(wb, sb, bB);
   if (!prep()) return false;
+  // With g.split the polling wave sets up the second segment (late) while the
+  // other waves stream the first; a batch beyond the first segment waits for
+  // its LDS flag. The flag stays set for later row chunks of the stage.
+  bool ready = !g.split;
+  if (g.split && w == kPollWave) {
+    late();
+    __hip_atomic_store(&sm.slots_ready, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+    ready = true;
+  }
+  auto gate = [&](int bt) {
+    if (ready || bt < ebat || bt >= nbat) return;
+    while (__hip_atomic_load(&sm.slots_ready, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) == 0)
+      __builtin_amdgcn_s_sleep(1);
+    ready = true;
+  };
+  gate(bA);
   if (bA >= ebat && bA < nbat) issue(wa, sa, bA);
+  gate(bB);
   if (kEarlyBatches == 2 && bB >= ebat && bB < nbat) issue(wb, sb, bB);
   if (w == kPollWave) {  // no static batch: claim the first one too
     bA = claim();
@@ -529,6 +553,7 @@ __device__ __forceinline__ bool gemv_rows_t(const Gemv& g, Smem& sm, int ra, int
   }
   if (kEarlyBatches == 1 || w == kPollWave) {
     bB = claim();
+    gate(bB);
     if (bB < nbat) issue(wb, sb, bB);
   }
   // Claims increase monotonically, so the batch in A is always older than the
@@ -536,20 +561,23 @@ __device__ __forceinline__ bool gemv_rows_t(const Gemv& g, Smem& sm, int ra, int
   while (bA < nbat) {
     compute(wa, sa, bA);
     bA = claim();
+    gate(bA);
     if (bA < nbat) issue(wa, sa, bA);
     if (bB >= nbat) break;
     compute(wb, sb, bB);
     bB = claim();
+    gate(bB);
     if (bB < nbat) issue(wb, sb, bB);
   }
   return true;
 }
 
-template <int EB, int SLOT, class Prep>
-__device__ __forceinline__ bool gemv_rows(const Gemv& g, Smem& sm, int ra, int rb, bool early, Prep&& prep) {
+template <int EB, int SLOT, class Prep, class Late>
+__device__ __forceinline__ bool gemv_rows(const Gemv& g, Smem& sm, int ra, int rb, bool early, Prep&& prep,
+                                          Late&& late) {
   const bool small = g.Kb < 1024 && (1024 % g.Kb) == 0;
-  return small ? gemv_rows_t<EB, false, SLOT>(g, sm, ra, rb, early, prep)
-               : gemv_rows_t<EB, true, SLOT>(g, sm, ra, rb, early, prep);
+  return small ? gemv_rows_t<EB, false, SLOT>(g, sm, ra, rb, early, prep, late)
+               : gemv_rows_t<EB, true, SLOT>(g, sm, ra, rb, early, prep, late);
 }
 
 // Balanced contiguous share of `rows` (in groups of `gran`) for workgroup wg.
@@ -703,12 +731,16 @@ __device__ __forceinline__ Gemv gemv_of(const Fp8Mat& m, const char* base_unused
 // Generic single-chunk-loop driver: processes the workgroup's rows in chunks;
 // `prep` (wait + staging) runs before the first chunk; `epi(ra_chunk, n)`
 // consumes part[0][0..n) after combine.
-template <int EB, int SLOT, class Prep, class Epi>
+// `late` (g.split only) runs on the polling wave once, after prep, while the
+// other waves already stream the first row segment.
+template <int EB, int SLOT, class Prep, class Epi, class Late = NoLate>
 __device__ __forceinline__ bool run_gemv(const StageEnv& E, Smem& sm, const Gemv& g, int ra, int rb, bool early,
-                                         Prep&& prep, Epi&& epi) {
+                                         Prep&& prep, Epi&& epi, Late&& late = Late{}) {
   if (ra >= rb) {
     // no rows: still take part in the dependency wait so barriers match
-    return prep();
+    const bool r = prep();
+    if (r && wave_id() == kPollWave) late();
+    return r;
   }
   bool first = true;
   uint64_t t_staged = 0;
@@ -721,7 +753,7 @@ __device__ __forceinline__ bool run_gemv(const StageEnv& E, Smem& sm, const Gemv
         const bool r = prep();
         if (E.c.A.trace) t_staged = wall_clock64();
         return r;
-      });
+      }, late);
     } else {
       zero_part(sm);
       // later chunks need the zeroed partials and batch counter visible
@@ -729,7 +761,7 @@ __device__ __forceinline__ bool run_gemv(const StageEnv& E, Smem& sm, const Gemv
       ok = gemv_rows<EB, SLOT>(g, sm, ca, cb, true, [&]() {
         __syncthreads();
         return true;
-      });
+      }, NoLate{});
     }
     if (!ok) return false;
     first = false;
@@ -1265,53 +1297,59 @@ __device__ __forceinline__ bool stage_router(const StageEnv& E, Smem& sm) {
       });
 }
 
-// Top-k of the router logits by one wave (ties to the lower index), written to
-// LDS with sigmoid weights normalised over the chosen experts.
-// Must be called by all threads; contains barriers.
-__device__ __forceinline__ void route_topk(const Ctx& c, Smem& sm, const LayerPlan& L, bool write_tap) {
-  const pdm_dims d = load_plan(&c.P->dims);
+// Top-k of the router logits by the calling wave (ties to the lower index),
+// with sigmoid weights normalised over the chosen experts: into LDS, and the
+// routed slot tables of the gate/up stage (slots n_shared + j) set from them.
+// Lane j keeps the j-th choice, so nothing is read back from LDS.
+__device__ __forceinline__ void route_wave(const pdm_dims& d, Smem& sm, const LayerPlan& L, bool write_tap) {
   const float* z = reinterpret_cast<const float*>(L.router_logits);
   const int E = d.n_experts, k = d.top_k;
-  // the polling wave: it has no weight loads queued ahead of the logits
-  if (wave_id() == kPollWave) {
-    const int lane = lane_id();
-    float v[16];
+  const int lane = lane_id();
+  float v[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    int e = lane + 64 * i;
+    v[i] = e < E ? ld_coh(z + e) : -INFINITY;
+  }
+  float wsum = 0.f;
+  int my_e = 0;
+  float my_w = 0.f;
+  for (int j = 0; j < k; ++j) {
+    // lane-local best: scanning in increasing index order with a strict
+    // compare keeps the lowest index among equal values
+    float bv = -INFINITY;
+    int bi = 0x7fffffff;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       int e = lane + 64 * i;
-      v[i] = e < E ? ld_coh(z + e) : -INFINITY;
+      if (e < E && v[i] > bv) { bv = v[i]; bi = e; }
     }
-    float wsum = 0.f;
-    for (int j = 0; j < k; ++j) {
-      // lane-local best: scanning in increasing index order with a strict
-      // compare keeps the lowest index among equal values
-      float bv = -INFINITY;
-      int bi = 0x7fffffff;
+    // wave maximum, then the lowest index holding it (DPP reductions)
+    const float gm = wave_max(bv);
+    int bw = wave_min_i(bv == gm ? bi : 0x7fffffff);
+    if (bw >= E) bw = 0;  // only when no finite logit is left (never for finite inputs)
+    // remove it
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        int e = lane + 64 * i;
-        if (e < E && v[i] > bv) { bv = v[i]; bi = e; }
-      }
-      // wave maximum, then the lowest index holding it (DPP reductions)
-      const float gm = wave_max(bv);
-      int bw = wave_min_i(bv == gm ? bi : 0x7fffffff);
-      if (bw >= E) bw = 0;  // only when no finite logit is left (never for finite inputs)
-      // remove it
-#pragma unroll
-      for (int i = 0; i < 16; ++i)
-        if (lane + 64 * i == bw) v[i] = -INFINITY;
-      float sg = 1.0f / (1.0f + __expf(-gm));
-      if (lane == 0) { sm.route_idx[j] = bw; sm.route_w[j] = sg; }
-      wsum += sg;
-    }
-    if (lane == 0) {
-      for (int j = 0; j < k; ++j) sm.route_w[j] /= wsum;
-    }
+    for (int i = 0; i < 16; ++i)
+      if (lane + 64 * i == bw) v[i] = -INFINITY;
+    const float sg = 1.0f / (1.0f + __expf(-gm));
+    if (lane == j) { my_e = bw; my_w = sg; }
+    wsum += sg;
   }
-  __syncthreads();
-  if (write_tap && threadIdx.x < k) {
-    gst(reinterpret_cast<int*>(L.topk_idx) + threadIdx.x, sm.route_idx[threadIdx.x]);
-    gst(reinterpret_cast<float*>(L.topk_w) + threadIdx.x, sm.route_w[threadIdx.x]);
+  if (lane < k) {
+    my_w /= wsum;
+    sm.route_idx[lane] = my_e;
+    sm.route_w[lane] = my_w;
+    if (write_tap) {
+      gst(reinterpret_cast<int*>(L.topk_idx) + lane, my_e);
+      gst(reinterpret_cast<float*>(L.topk_w) + lane, my_w);
+    }
+    const int t = d.n_shared + lane;
+    const uint8_t* base = reinterpret_cast<const uint8_t*>(L.expert_base) + (size_t)my_e * L.expert_stride;
+    sm.slot_codes[t] = base + L.egu.codes;
+    sm.slot_scales[t] = reinterpret_cast<const uint16_t*>(base + L.egu.scales);
+    sm.slot_w[t] = my_w;
+    sm.slot_act[t] = lane * d.moe_ffn;
   }
 }
 
@@ -1397,18 +1435,14 @@ __device__ __forceinline__ bool stage_gu_moe(const StageEnv& E, Smem& sm) {
   const int n = (e1 - p1) + (e2 - p2);
   const bool reuse = (E.st.flags & kStXStaged) != 0;
   set_slots(d, L, sm, true, false, false);
+  if (threadIdx.x == 0) sm.slots_ready = 0;
   __syncthreads();
   return run_gemv<1, 3>(E, sm, g, 0, n, true,
       [&]() {
         if (!wait_stage(c, sm, E.st.wait, E.s)) return false;
-        route_topk(c, sm, L, c.wg == 0);
-        set_slots(d, L, sm, false, true, false);
-        if (reuse) {
-          __syncthreads();  // slot tables
-        } else {
+        if (!reuse)
           stage_rmsnorm(sm, d.hidden, reinterpret_cast<const float*>(L.ffn_norm), d.rms_eps,
                         [&](int k) { return ld_coh(xa + k); });
-        }
         return true;
       },
       [&](int ca, int nr) {
@@ -1423,7 +1457,8 @@ __device__ __forceinline__ bool stage_gu_moe(const StageEnv& E, Smem& sm) {
           const int j = pair / F, f = pair - j * F;
           st_coh(act + sm.slot_act[j] + f, silu(gt) * up * sm.slot_w[j]);
         }
-      });
+      },
+      [&]() { route_wave(d, sm, L, c.wg == 0); });
 }
 
 // --- DOWN: x_out = bf16(x_attn + sum_slots W_down[slot] act[slot])
