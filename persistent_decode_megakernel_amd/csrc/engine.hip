@@ -122,6 +122,35 @@ __device__ __forceinline__ float bf16_lo(uint32_t w) { return __builtin_bit_cast
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
 __device__ __forceinline__ float bf16_val(uint16_t b) { return __builtin_bit_cast(float, (uint32_t)b << 16); }
 
+// v as a bf16 high part plus the bf16 of the remainder
+__device__ __forceinline__ void split_bf16(float v, __bf16& hi, __bf16& lo) {
+  hi = (__bf16)v;
+  lo = (__bf16)(v - (float)hi);
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(__bf16 a, __bf16 b) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+}
+
+// Attention-ready queries of a layer: [head group][high, residual][kMH][kvr + 8]
+// bf16 of q * tau (tau = 1 / sqrt(d_qk)): columns [0, d_c) are q_lat (written
+// by the absorb stage), [d_c, d_c + d_r) the rotated rotary part (by the qb
+// stage); the attention stage copies a head group's image into LDS as is.
+constexpr int kMH = kHeadGroup;  // heads per MFMA tile (unit heads padded to kMH)
+// u32 index of the column pair (col, col + 1), col even, of head h
+__device__ __forceinline__ size_t qatt_pair(int h, int col, int hg, int kvr, int part) {
+  const int grp = h / hg, hh = h - grp * hg;
+  return ((((size_t)grp * 2 + part) * kMH + hh) * (kvr + 8) + col) >> 1;
+}
+// stores q-pair (a, b) of head h at columns (col, col + 1)
+__device__ __forceinline__ void store_qatt(uint32_t* qa, int h, int col, int hg, int kvr, float tau, float a,
+                                           float b) {
+  __bf16 ah, al, bh, bl;
+  split_bf16(a * tau, ah, al);
+  split_bf16(b * tau, bh, bl);
+  st_coh_u(qa + qatt_pair(h, col, hg, kvr, 0), pack_bf16x2(ah, bh));
+  st_coh_u(qa + qatt_pair(h, col, hg, kvr, 1), pack_bf16x2(al, bl));
+}
+
 // Round an fp32 value to the nearest bf16 value (ties to even), kept in fp32.
 __device__ __forceinline__ float round_bf16(float v) {
   uint32_t u = __builtin_bit_cast(uint32_t, v);
@@ -816,6 +845,9 @@ __device__ __forceinline__ bool stage_qb(const StageEnv& E, Smem& sm) {
   int ra, rb;
   my_rows(E.st.rows, E.st.gran, c.G, c.wg, ra, rb);
   float* out = reinterpret_cast<float*>(L.q);
+  uint32_t* qa = reinterpret_cast<uint32_t*>(L.ql);
+  const int hg = c.P->hg, kvw = d.kv_lora + d.rope;
+  const float tau = 1.0f / sqrtf((float)qkh);
   // The last workgroup also appends this step's cache row
   // [RMSNorm(kv latent) ; RoPE(rotary key)] (bf16, at position pos). Thread p
   // owns the value pair 2p, 2p + 1: its gains or rotation come from static
@@ -870,17 +902,19 @@ __device__ __forceinline__ bool stage_qb(const StageEnv& E, Smem& sm) {
         return true;
       },
       [&](int ca, int n) {
+        // q_nope rows to the fp32 buffer (the absorb stage's input); rotary
+        // pairs (adjacent rows, starting even) rotated into the attention layout
         for (int t = threadIdx.x; t < n; t += kThreads) {
-          int r = ca + t;
-          int j = r % qkh;
-          float y = sm.part[0][t];
-          if (j >= d.qk_nope) {
-            int i = (j - d.qk_nope) >> 1;
-            float cs = gld(tab + 2 * i), sn = gld(tab + 2 * i + 1);
-            float other = sm.part[0][t ^ 1];
-            y = (j - d.qk_nope) & 1 ? other * sn + y * cs : y * cs - other * sn;
+          const int r = ca + t;
+          const int h = r / qkh, j = r - h * qkh;
+          if (j < d.qk_nope) {
+            st_coh(out + r, sm.part[0][t]);
+          } else if (((j - d.qk_nope) & 1) == 0) {
+            const int i = (j - d.qk_nope) >> 1;
+            const float cs = gld(tab + 2 * i), sn = gld(tab + 2 * i + 1);
+            const float x0 = sm.part[0][t], x1 = sm.part[0][t + 1];
+            store_qatt(qa, h, d.kv_lora + (j - d.qk_nope), hg, kvw, tau, x0 * cs - x1 * sn, x0 * sn + x1 * cs);
           }
-          st_coh(out + r, y);
         }
       });
   return ok;
@@ -899,7 +933,9 @@ __device__ __forceinline__ bool stage_absorb(const StageEnv& E, Smem& sm) {
   g.lg_rpv = 31 - __builtin_clz(d.kv_lora);
   g.vbase = ra / d.kv_lora;
   g.xK = d.qk_nope;
-  float* out = reinterpret_cast<float*>(L.ql);
+  uint32_t* qa = reinterpret_cast<uint32_t*>(L.ql);
+  const int hg = c.P->hg, kvr = d.kv_lora + d.rope;
+  const float tau = 1.0f / sqrtf((float)qkh);
   return run_gemv<1, 0>(E, sm, g, ra, rb, true,
       [&]() {
         if (!wait_stage(c, sm, E.st.wait, E.s)) return false;
@@ -912,7 +948,12 @@ __device__ __forceinline__ bool stage_absorb(const StageEnv& E, Smem& sm) {
         return true;
       },
       [&](int ca, int n) {
-        for (int t = threadIdx.x; t < n; t += kThreads) st_coh(out + ca + t, sm.part[0][t]);
+        // rows (h, c) in pairs of adjacent latent columns (chunks start and end even)
+        for (int t = threadIdx.x; t < n / 2; t += kThreads) {
+          const int r = ca + 2 * t;
+          const int h = r >> g.lg_rpv, col = r & (d.kv_lora - 1);
+          store_qatt(qa, h, col, hg, kvr, tau, sm.part[0][2 * t], sm.part[0][2 * t + 1]);
+        }
       });
 }
 
@@ -932,12 +973,7 @@ __device__ __forceinline__ bool stage_absorb(const StageEnv& E, Smem& sm) {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr int kAttnBlock = 64;    // positions staged per round
-constexpr int kMH = 16;           // heads per MFMA tile (unit heads padded to 16)
 
-__device__ __forceinline__ void split_bf16(float v, __bf16& hi, __bf16& lo) {
-  hi = (__bf16)v;
-  lo = (__bf16)(v - (float)hi);
-}
 
 __device__ __forceinline__ bf16x8 u32x4_as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
@@ -954,13 +990,11 @@ __device__ __forceinline__ bool stage_attn(const StageEnv& E, Smem& sm) {
   const int chunk = (ctx + nch - 1) / nch;
   const int t0 = min(ctx, ch * chunk), t1 = min(ctx, t0 + chunk);
   const int dc = d.kv_lora, dr = d.rope, kvr = dc + dr;
-  const int qkh = d.qk_nope + d.rope;
   const int q8n = kvr / 8;              // 16-byte pieces per cache row
   const int nkb = kvr / 32;             // MFMA k-blocks of a score
   const int kstr = kvr / 2 + 4;         // LDS cache-row stride in u32 (padded)
   const int qstr = kvr + 8;             // LDS query-row stride in bf16 (padded)
   constexpr int pstr = kAttnBlock + 4;  // LDS probability-row stride in floats
-  const float tau = 1.0f / sqrtf((float)qkh);
   const uint16_t* cache = reinterpret_cast<const uint16_t*>(L.kv);
 
   // Cache rows of a block before pos were written by earlier steps: their
@@ -995,39 +1029,26 @@ __device__ __forceinline__ bool stage_attn(const StageEnv& E, Smem& sm) {
   float* hl = hm + kMH;             // running sum per head
   float* ha = hl + kMH;             // rescale of the accumulators this round
 
-  const float* qlat = reinterpret_cast<const float*>(L.ql);
-  const float* qf = reinterpret_cast<const float*>(L.q);
   {
     // The polling wave, which has no cache-row loads queued ahead of it,
-    // copies the head group's queries into the (not yet used) cache-row area:
-    // q_lat [hg][dc] in one piece, then the rotary parts [hg][dr] (one piece
-    // per head, several pieces per DMA instruction).
-    float* raw = reinterpret_cast<float*>(kvs);
-    const int qbytes = hg * dc * 4;
-    float* rawpe = raw + ((qbytes + 1023) & ~1023) / 4;
+    // copies the head group's attention-ready queries (scaled, split into
+    // bf16 high and residual rows by their producers) straight into LDS;
+    // rows of heads >= hg are zero.
+    const uint16_t* qa = reinterpret_cast<const uint16_t*>(L.ql) + (size_t)grp * 2 * kMH * qstr;
+    const int rbytes = hg * qstr * 2;
     if (wave_id() == kPollWave) {
-      dma_to_lds(raw, qlat + (size_t)grp * hg * dc, qbytes);
-      const int lpp = dr / 4;       // lanes per rotary piece (16 bytes each)
-      const int ppi = 64 / lpp;     // pieces per instruction
-      const int lane = lane_id();
-      for (int p0 = 0; p0 < hg; p0 += ppi) {
-        const int p = min(p0 + lane / lpp, hg - 1);
-        const float* src = qf + (size_t)(grp * hg + p) * qkh + d.qk_nope + (lane % lpp) * 4;
-        __builtin_amdgcn_global_load_lds((const GLOBAL_AS void*)src,
-                                         (__attribute__((address_space(3))) void*)(rawpe + p0 * dr), 16, 0, kCpolSc1);
+      if (hg == kMH) {
+        dma_to_lds(qh, qa, 2 * rbytes);
+      } else {
+        dma_to_lds(qh, qa, rbytes);
+        dma_to_lds(ql, qa + kMH * qstr, rbytes);
       }
       mem_done();
     }
     __syncthreads();
-    // scaled queries split into bf16 high and residual parts; heads >= hg are zero
-    const int n = kMH * kvr;
-    for (int i = threadIdx.x; i < n; i += kThreads) {
-      const int hh = i / kvr, k = i - hh * kvr;
-      const float q = hh < hg ? (k < dc ? raw[hh * dc + k] : rawpe[hh * dr + (k - dc)]) : 0.f;
-      __bf16 hi, lo;
-      split_bf16(q * tau, hi, lo);
-      qh[hh * qstr + k] = hi;
-      ql[hh * qstr + k] = lo;
+    for (int i = threadIdx.x; i < (kMH - hg) * qstr; i += kThreads) {
+      qh[hg * qstr + i] = (__bf16)0.f;
+      ql[hg * qstr + i] = (__bf16)0.f;
     }
     if (threadIdx.x < kMH) { hm[threadIdx.x] = -INFINITY; hl[threadIdx.x] = 0.f; }
     mark(c, sm, 0);

@@ -62,7 +62,7 @@ struct LayerPlan {
   // activations (scratch), f32 unless noted
   uint64_t qkv_raw;    // [d_q + d_c + d_r]
   uint64_t q;          // [H][d_n + d_r], rotary part rotated
-  uint64_t ql;         // [H][d_c]
+  uint64_t ql;         // attention-ready queries: bf16 [n_hg][high, residual][kHeadGroup][d_c + d_r + 8]
   uint64_t attn_part;  // [H][nch][d_c + 2]: acc, max, sum
   uint64_t o;          // [H * d_v]
   uint64_t xa;         // [D] residual after attention

@@ -221,7 +221,7 @@ int build_plan(const pdm_dims& d, int32_t max_ctx, int32_t G, Plan* p, Layout* l
     L.topk_w = tw_all + (uint64_t)l * kk * 4;
     L.qkv_raw = s.take((uint64_t)L.qkv.rows * 4);
     L.q = s.take((uint64_t)H * qkh * 4);
-    L.ql = s.take((uint64_t)H * d.kv_lora * 4);
+    L.ql = s.take((uint64_t)p->n_hg * 2 * kHeadGroup * (kvr + 8) * 2);
     L.attn_part = s.take((uint64_t)H * p->nch * (d.kv_lora + 2) * 4);
     L.o = s.take((uint64_t)H * d.v_head * 4);
     int64_t act = L.is_moe ? (int64_t)(d.top_k + d.n_shared) * d.moe_ffn : d.ffn;
