@@ -293,7 +293,6 @@ __device__ __forceinline__ bool wait_stage(const Ctx& c, Smem& sm, int s, int my
         if (lane == 0) sm.abort = 1;
         break;
       }
-      __builtin_amdgcn_s_sleep(1);
     }
   }
   __syncthreads();
