@@ -1003,18 +1003,22 @@ __device__ __forceinline__ bool stage_attn(const StageEnv& E, Smem& sm) {
   constexpr int kPer = (kAttnBlock * 80 + kPreThreads - 1) / kPreThreads;
   u32x4 v[kPer];
   const bool loader = (int)threadIdx.x < kPreThreads;
+  // piece i of a block is 16-byte piece i of the block's contiguous rows
   auto issue_block = [&](int tb) {
     if (!loader) return;
     const int nb = min(kAttnBlock, t1 - tb);
     const int nmain = max(0, min(nb, pos - tb)) * q8n;
+    const u32x4* src = reinterpret_cast<const u32x4*>(cache + (size_t)tb * kvr);
 #pragma unroll
     for (int r = 0; r < kPer; ++r) {
-      int i = threadIdx.x + r * kPreThreads;
-      int row = i / q8n, col = i - row * q8n;
-      int ok = i < nmain;
-      v[r] = gld(reinterpret_cast<const u32x4*>(cache + (size_t)(tb + (ok ? row : 0)) * kvr) + (ok ? col : 0));
+      const int i = threadIdx.x + r * kPreThreads;
+      v[r] = gld(src + (i < nmain ? i : 0));
     }
   };
+  // LDS position of piece i: (row, col) = (i / q8n, i % q8n), stepped per r
+  // from the thread's first piece without a division per piece
+  const int row0 = (int)threadIdx.x / q8n, col0 = (int)threadIdx.x - row0 * q8n;
+  const int drow = kPreThreads / q8n, dcol = kPreThreads - drow * q8n;
   if (t0 < t1) issue_block(t0);
   if (!wait_stage(c, sm, E.st.wait, E.s)) return false;
 
@@ -1071,14 +1075,17 @@ __device__ __forceinline__ bool stage_attn(const StageEnv& E, Smem& sm) {
       if (cur_here && threadIdx.x < kvr / 2)
         cv = ld_coh_u(reinterpret_cast<const uint32_t*>(cache + (size_t)pos * kvr) + threadIdx.x);
       __syncthreads();  // the previous round's readers are done with kvs and sp
+      int row = row0, col = col0;
 #pragma unroll
       for (int r = 0; r < kPer; ++r) {
-        int i = threadIdx.x + r * kPreThreads;
+        const int i = threadIdx.x + r * kPreThreads;
         if (loader && i < kAttnBlock * q8n) {
-          int row = i / q8n, col = i - row * q8n;
           u32x4 z = {0u, 0u, 0u, 0u};
           *reinterpret_cast<u32x4*>(kvs + row * kstr + col * 4) = i < nmain ? v[r] : z;
         }
+        col += dcol;
+        row += drow;
+        if (col >= q8n) { col -= q8n; ++row; }
       }
       if (tb + kAttnBlock < t1) issue_block(tb + kAttnBlock);
       __syncthreads();
