@@ -615,14 +615,13 @@ __device__ __forceinline__ void my_rows(int rows, int gran, int G, int wg, int& 
   rb = ng * (wg + 1) / G * gran;
 }
 
-// Sum the per-wave partials of rows [0, n) of the chunk into part[0][*].
-__device__ __forceinline__ void combine_rows(Smem& sm, int n) {
-  for (int t = threadIdx.x; t < n; t += kThreads) {
-    float y = 0.f;
+// A chunk row's result: the sum of the waves' partials (each wave adds only
+// the units it claimed; the others' entries stay zero).
+__device__ __forceinline__ float part_sum(const Smem& sm, int t) {
+  float y = 0.f;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) y += sm.part[w][t];
-    sm.part[0][t] = y;
-  }
+  for (int w = 0; w < kWaves; ++w) y += sm.part[w][t];
+  return y;
 }
 
 // Zero the per-wave partials and reset the batch counter (the first
@@ -758,7 +757,7 @@ __device__ __forceinline__ Gemv gemv_of(const Fp8Mat& m, const char* base_unused
 
 // Generic single-chunk-loop driver: processes the workgroup's rows in chunks;
 // `prep` (wait + staging) runs before the first chunk; `epi(ra_chunk, n)`
-// consumes part[0][0..n) after combine.
+// reads the chunk's row results through part_sum.
 // `late` (g.split only) runs on the polling wave once, after prep, while the
 // other waves already stream the first row segment.
 template <int EB, int SLOT, class Prep, class Epi, class Late = NoLate>
@@ -796,8 +795,6 @@ __device__ __forceinline__ bool run_gemv(const StageEnv& E, Smem& sm, const Gemv
     mark(E.c, sm, 1);
     if (E.c.A.trace && threadIdx.x == 0 && t_staged) sm.t_mark[0] = t_staged;
     __syncthreads();
-    combine_rows(sm, cb - ca);
-    __syncthreads();
     epi(ca, cb - ca);
     __syncthreads();
     mark(E.c, sm, 2);
@@ -827,7 +824,7 @@ __device__ __forceinline__ bool stage_qkv(const StageEnv& E, Smem& sm) {
         return true;
       },
       [&](int ca, int n) {
-        for (int t = threadIdx.x; t < n; t += kThreads) st_coh(out + ca + t, sm.part[0][t]);
+        for (int t = threadIdx.x; t < n; t += kThreads) st_coh(out + ca + t, part_sum(sm, t));
       });
 }
 
@@ -907,11 +904,11 @@ __device__ __forceinline__ bool stage_qb(const StageEnv& E, Smem& sm) {
           const int r = ca + t;
           const int h = r / qkh, j = r - h * qkh;
           if (j < d.qk_nope) {
-            st_coh(out + r, sm.part[0][t]);
+            st_coh(out + r, part_sum(sm, t));
           } else if (((j - d.qk_nope) & 1) == 0) {
             const int i = (j - d.qk_nope) >> 1;
             const float cs = gld(tab + 2 * i), sn = gld(tab + 2 * i + 1);
-            const float x0 = sm.part[0][t], x1 = sm.part[0][t + 1];
+            const float x0 = part_sum(sm, t), x1 = part_sum(sm, t + 1);
             store_qatt(qa, h, d.kv_lora + (j - d.qk_nope), hg, kvw, tau, x0 * cs - x1 * sn, x0 * sn + x1 * cs);
           }
         }
@@ -951,7 +948,7 @@ __device__ __forceinline__ bool stage_absorb(const StageEnv& E, Smem& sm) {
         for (int t = threadIdx.x; t < n / 2; t += kThreads) {
           const int r = ca + 2 * t;
           const int h = r >> g.lg_rpv, col = r & (d.kv_lora - 1);
-          store_qatt(qa, h, col, hg, kvr, tau, sm.part[0][2 * t], sm.part[0][2 * t + 1]);
+          store_qatt(qa, h, col, hg, kvr, tau, part_sum(sm, 2 * t), part_sum(sm, 2 * t + 1));
         }
       });
 }
@@ -1266,7 +1263,7 @@ __device__ __forceinline__ bool stage_uv(const StageEnv& E, Smem& sm) {
         return true;
       },
       [&](int ca, int n) {
-        for (int t = threadIdx.x; t < n; t += kThreads) st_coh(out + ca + t, sm.part[0][t]);
+        for (int t = threadIdx.x; t < n; t += kThreads) st_coh(out + ca + t, part_sum(sm, t));
       });
 }
 
@@ -1295,7 +1292,7 @@ __device__ __forceinline__ bool stage_wo(const StageEnv& E, Smem& sm) {
       },
       [&](int ca, int n) {
         for (int t = threadIdx.x; t < n; t += kThreads)
-          st_coh(out + ca + t, (res_pre ? res : in(ca + t)) + sm.part[0][t]);
+          st_coh(out + ca + t, (res_pre ? res : in(ca + t)) + part_sum(sm, t));
       });
 }
 
@@ -1320,7 +1317,7 @@ __device__ __forceinline__ bool stage_router(const StageEnv& E, Smem& sm) {
         return true;
       },
       [&](int ca, int n) {
-        for (int t = threadIdx.x; t < n; t += kThreads) st_coh(out + ca + t, sm.part[0][t]);
+        for (int t = threadIdx.x; t < n; t += kThreads) st_coh(out + ca + t, part_sum(sm, t));
       });
 }
 
@@ -1424,8 +1421,8 @@ __device__ __forceinline__ bool stage_gu(const StageEnv& E, Smem& sm) {
         // rows [gate 8 ; up 8] per group of 16: pair row (ca >> 1) + t
         for (int t = threadIdx.x; t < n / 2; t += kThreads) {
           int grp = t >> 3, r = t & 7;
-          float gt = sm.part[0][grp * 16 + r];
-          float up = sm.part[0][grp * 16 + 8 + r];
+          float gt = part_sum(sm, grp * 16 + r);
+          float up = part_sum(sm, grp * 16 + 8 + r);
           st_coh(act + (ca >> 1) + t, silu(gt) * up);
         }
       });
@@ -1475,8 +1472,8 @@ __device__ __forceinline__ bool stage_gu_moe(const StageEnv& E, Smem& sm) {
       [&](int ca, int nr) {
         for (int t = threadIdx.x; t < nr / 2; t += kThreads) {
           int grp = t >> 3, r = t & 7;
-          float gt = sm.part[0][grp * 16 + r];
-          float up = sm.part[0][grp * 16 + 8 + r];
+          float gt = part_sum(sm, grp * 16 + r);
+          float up = part_sum(sm, grp * 16 + 8 + r);
           // local gate row -> row-slot row -> pair row across all slots
           const int lr = ca + grp * 16 + r;
           const int pr = lr < g.seg_n1 ? g.seg_p1 + lr : g.seg_p2 + (lr - g.seg_n1);
@@ -1529,7 +1526,7 @@ __device__ __forceinline__ bool stage_down(const StageEnv& E, Smem& sm) {
       };
   auto epi = [&](int ca, int n) {
         for (int t = threadIdx.x; t < n; t += kThreads)
-          st_coh(out + ca + t, round_bf16((res_pre ? res : ld_coh(xa + ca + t)) + sm.part[0][t]));
+          st_coh(out + ca + t, round_bf16((res_pre ? res : ld_coh(xa + ca + t)) + part_sum(sm, t)));
       };
   if (L.is_moe) return run_gemv<1, 2>(E, sm, g, ra, rb, true, prep, epi);
   return run_gemv<1, 0>(E, sm, g, ra, rb, true, prep, epi);
@@ -1558,7 +1555,7 @@ __device__ __forceinline__ bool stage_lm(const StageEnv& E, Smem& sm) {
       },
       [&](int ca, int n) {
         for (int t = threadIdx.x; t < n; t += kThreads) {
-          float v = sm.part[0][t];
+          float v = part_sum(sm, t);
           gst(logits + ca + t, v);
           if (v > bestv || (v == bestv && ca + t < besti)) { bestv = v; besti = ca + t; }
         }
