@@ -42,6 +42,10 @@ static_assert((512 + 128) / 2 <= kPreThreads, "cache-row pairs fit the loading t
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
+// Cache-policy operand of loads: sc1, the policy of a relaxed agent-scope
+// atomic load, for data written this step by other workgroups.
+constexpr unsigned kCpolSc1 = 16;
+
 // Every device pointer of the plan is global memory. Accessing it through an
 // address_space(1) pointer makes the compiler emit global (not flat) memory
 // instructions, which only count against vmcnt; flat ones also count against
@@ -691,6 +695,63 @@ __device__ __forceinline__ void stage_plain(Smem& sm, int K, Get&& get) {
   __syncthreads();
 }
 
+// Contiguous fp32 vectors written this step by other workgroups (K a multiple
+// of 4) are staged with 16-byte buffer loads under the sc1 policy, so every
+// vector of up to kStageVec * 4 * kThreads floats costs one round trip. The
+// buffer descriptor's bound makes loads past the end read zero.
+constexpr int kBufDword3 = 0x00020000;  // raw (untyped) buffer descriptor, gfx9
+constexpr int kStageVec = 10;           // 16-byte loads per thread in flight
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t vec_rsrc(const float* p, int n) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(p), 0, n * 4, kBufDword3);
+}
+template <unsigned CPOL>
+__device__ __forceinline__ float4 ld_vec4(__amdgpu_buffer_rsrc_t r, int i4) {
+  return __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(r, i4 * 16, 0, CPOL));
+}
+
+// x_lds = v (gain null) or v * gain, v = src[0, K) loaded coherently. Returns
+// this thread's sum of squares of v. Whether a batch slot has any element is
+// the same for the whole workgroup, so only the loads a vector needs are issued.
+__device__ __forceinline__ float stage_vec(Smem& sm, int K, const float* src, const float* gain) {
+  const __amdgpu_buffer_rsrc_t rv = vec_rsrc(src, K);
+  const __amdgpu_buffer_rsrc_t rg = vec_rsrc(gain ? gain : src, K);
+  const int n4 = K / 4;
+  float ss = 0.f;
+  for (int b0 = 0; b0 < n4; b0 += kStageVec * kThreads) {
+    float4 v[kStageVec], g[kStageVec];
+#pragma unroll
+    for (int i = 0; i < kStageVec; ++i) {
+      v[i] = g[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (b0 + i * kThreads < n4) {
+        v[i] = ld_vec4<kCpolSc1>(rv, b0 + i * kThreads + threadIdx.x);
+        if (gain) g[i] = ld_vec4<0>(rg, b0 + i * kThreads + threadIdx.x);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kStageVec; ++i) {
+      const int i4 = b0 + i * kThreads + threadIdx.x;
+      float4 y = v[i];
+      if (gain) { y.x *= g[i].x; y.y *= g[i].y; y.z *= g[i].z; y.w *= g[i].w; }
+      if (i4 < n4) *reinterpret_cast<float4*>(sm.x + 4 * i4) = y;
+      ss += v[i].x * v[i].x + v[i].y * v[i].y + v[i].z * v[i].z + v[i].w * v[i].w;
+    }
+  }
+  return ss;
+}
+
+// stage_rmsnorm / stage_plain of a contiguous coherent vector
+__device__ __forceinline__ void stage_rmsnorm_vec(Smem& sm, int K, const float* gain, float eps, const float* src) {
+  const float tot = block_sum(sm, stage_vec(sm, K, src, gain));
+  const float rs = 1.0f / sqrtf(tot / (float)K + eps);
+  for (int k = threadIdx.x; k < K; k += kThreads) sm.x[k] *= rs;
+  __syncthreads();
+}
+__device__ __forceinline__ void stage_plain_vec(Smem& sm, int K, const float* src) {
+  stage_vec(sm, K, src, nullptr);
+  __syncthreads();
+}
+
 // LDS DMA copy by the calling wave of `nbytes` (a multiple of 16) from a
 // 16-byte aligned global address into LDS: 16 bytes per lane and 1 KB per
 // instruction, no registers held. Lanes past the end re-read the last 16
@@ -698,7 +759,6 @@ __device__ __forceinline__ void stage_plain(Smem& sm, int K, Get&& get) {
 // that much LDS slack). A coherent copy uses the sc1 cache policy, as a
 // relaxed agent-scope atomic load does, for data written this step by other
 // workgroups. The caller waits for completion (vmcnt) before using the data.
-constexpr unsigned kCpolSc1 = 16;
 
 __device__ __forceinline__ void dma_to_lds(void* dst, const void* src, int nbytes) {
   const int lane = lane_id();
@@ -816,7 +876,10 @@ __device__ __forceinline__ bool stage_qkv(const StageEnv& E, Smem& sm) {
       [&]() {
         if (!wait_stage(c, sm, E.st.wait, E.s)) return false;
         const LayerInput in = layer_input(c, l);
-        stage_rmsnorm(sm, D, reinterpret_cast<const float*>(L.attn_norm), c.P->dims.rms_eps, in);
+        if (in.prev)
+          stage_rmsnorm_vec(sm, D, reinterpret_cast<const float*>(L.attn_norm), c.P->dims.rms_eps, in.prev);
+        else
+          stage_rmsnorm(sm, D, reinterpret_cast<const float*>(L.attn_norm), c.P->dims.rms_eps, in);
         if (l == 0 && c.wg == 0) {
           float* x0 = reinterpret_cast<float*>(c.P->x0);
           for (int k = threadIdx.x; k < D; k += kThreads) st_coh(x0 + k, in(k));
@@ -876,8 +939,7 @@ __device__ __forceinline__ bool stage_qb(const StageEnv& E, Smem& sm) {
           x0 = ld_coh(kvr + 2 * p);
           x1 = ld_coh(kvr + 2 * p + 1);
         }
-        stage_rmsnorm(sm, d.q_lora, reinterpret_cast<const float*>(L.q_norm), d.rms_eps,
-                      [&](int k) { return ld_coh(raw + k); });
+        stage_rmsnorm_vec(sm, d.q_lora, reinterpret_cast<const float*>(L.q_norm), d.rms_eps, raw);
         if (app) {
           const float tot = block_sum(sm, own && is_lat ? x0 * x0 + x1 * x1 : 0.f);
           const float rs = 1.0f / sqrtf(tot / (float)d.kv_lora + d.rms_eps);
@@ -1287,7 +1349,7 @@ __device__ __forceinline__ bool stage_wo(const StageEnv& E, Smem& sm) {
       [&]() {
         if (res_pre && (int)threadIdx.x < rb - ra) res = in(ra + threadIdx.x);
         if (!wait_stage(c, sm, E.st.wait, E.s)) return false;
-        stage_plain(sm, d.n_heads * d.v_head, [&](int k) { return ld_coh(o + k); });
+        stage_plain_vec(sm, d.n_heads * d.v_head, o);
         return true;
       },
       [&](int ca, int n) {
@@ -1312,8 +1374,7 @@ __device__ __forceinline__ bool stage_router(const StageEnv& E, Smem& sm) {
   return run_gemv<2, 0>(E, sm, g, ra, rb, true,
       [&]() {
         if (!wait_stage(c, sm, E.st.wait, E.s)) return false;
-        stage_rmsnorm(sm, d.hidden, reinterpret_cast<const float*>(L.ffn_norm), d.rms_eps,
-                      [&](int k) { return ld_coh(xa + k); });
+        stage_rmsnorm_vec(sm, d.hidden, reinterpret_cast<const float*>(L.ffn_norm), d.rms_eps, xa);
         return true;
       },
       [&](int ca, int n) {
@@ -1413,8 +1474,7 @@ __device__ __forceinline__ bool stage_gu(const StageEnv& E, Smem& sm) {
   return run_gemv<1, 0>(E, sm, g, ra, rb, true,
       [&]() {
         if (!wait_stage(c, sm, E.st.wait, E.s)) return false;
-        stage_rmsnorm(sm, d.hidden, reinterpret_cast<const float*>(L.ffn_norm), d.rms_eps,
-                      [&](int k) { return ld_coh(xa + k); });
+        stage_rmsnorm_vec(sm, d.hidden, reinterpret_cast<const float*>(L.ffn_norm), d.rms_eps, xa);
         return true;
       },
       [&](int ca, int n) {
@@ -1465,8 +1525,7 @@ __device__ __forceinline__ bool stage_gu_moe(const StageEnv& E, Smem& sm) {
       [&]() {
         if (!wait_stage(c, sm, E.st.wait, E.s)) return false;
         if (!reuse)
-          stage_rmsnorm(sm, d.hidden, reinterpret_cast<const float*>(L.ffn_norm), d.rms_eps,
-                        [&](int k) { return ld_coh(xa + k); });
+          stage_rmsnorm_vec(sm, d.hidden, reinterpret_cast<const float*>(L.ffn_norm), d.rms_eps, xa);
         return true;
       },
       [&](int ca, int nr) {
@@ -1521,7 +1580,7 @@ __device__ __forceinline__ bool stage_down(const StageEnv& E, Smem& sm) {
   auto prep = [&]() {
         if (res_pre && (int)threadIdx.x < rb - ra) res = ld_coh(xa + ra + threadIdx.x);
         if (!wait_stage(c, sm, E.st.wait, E.s)) return false;
-        stage_plain(sm, K, [&](int k) { return ld_coh(act + k); });
+        stage_plain_vec(sm, K, act);
         return true;
       };
   auto epi = [&](int ca, int n) {
@@ -1549,8 +1608,7 @@ __device__ __forceinline__ bool stage_lm(const StageEnv& E, Smem& sm) {
   bool ok = run_gemv<2, 0>(E, sm, g, ra, rb, true,
       [&]() {
         if (!wait_stage(c, sm, E.st.wait, E.s)) return false;
-        stage_rmsnorm(sm, d.hidden, reinterpret_cast<const float*>(c.P->final_norm), d.rms_eps,
-                      [&](int k) { return ld_coh(x + k); });
+        stage_rmsnorm_vec(sm, d.hidden, reinterpret_cast<const float*>(c.P->final_norm), d.rms_eps, x);
         return true;
       },
       [&](int ca, int n) {
