@@ -82,6 +82,7 @@ struct __align__(16) Smem {
   int route_idx[kMaxSlots];       // top-k experts of the current MoE layer
   float route_w[kMaxSlots];       // their normalised weights
   float red[2 * kWaves];
+  float nred[kWaves];             // per-wave sums of squares of the last normalised staging
   int ired[2 * kWaves];
   uint64_t t_enter, t_ready;
   uint64_t t_mark[3];             // input staged, weights consumed, epilogue done
@@ -740,13 +741,23 @@ __device__ __forceinline__ float stage_vec(Smem& sm, int K, const float* src, co
   return ss;
 }
 
-// stage_rmsnorm / stage_plain of a contiguous coherent vector
-__device__ __forceinline__ void stage_rmsnorm_vec(Smem& sm, int K, const float* gain, float eps, const float* src) {
-  const float tot = block_sum(sm, stage_vec(sm, K, src, gain));
-  const float rs = 1.0f / sqrtf(tot / (float)K + eps);
-  for (int k = threadIdx.x; k < K; k += kThreads) sm.x[k] *= rs;
+// Fused RMSNorm of a contiguous coherent vector, applied to the product: the
+// stage holds gain * v in LDS and multiplies its rows' results by 1 / rms (the
+// GEMV is linear in its input), so the staging needs one barrier and no
+// second pass over LDS. The per-wave sums of squares stay in sm.nred for
+// rms_scale(), also in the next stage when it reuses the staged input.
+__device__ __forceinline__ void stage_norm_vec(Smem& sm, int K, const float* gain, const float* src) {
+  const float w = wave_sum(stage_vec(sm, K, src, gain));
+  if (lane_id() == 0) sm.nred[wave_id()] = w;
   __syncthreads();
 }
+__device__ __forceinline__ float rms_scale(const Smem& sm, int K, float eps) {
+  float t = 0.f;
+#pragma unroll
+  for (int i = 0; i < kWaves; ++i) t += sm.nred[i];
+  return 1.0f / sqrtf(t / (float)K + eps);
+}
+// stage_plain of a contiguous coherent vector
 __device__ __forceinline__ void stage_plain_vec(Smem& sm, int K, const float* src) {
   stage_vec(sm, K, src, nullptr);
   __syncthreads();
@@ -872,14 +883,17 @@ __device__ __forceinline__ bool stage_qkv(const StageEnv& E, Smem& sm) {
   int ra, rb;
   my_rows(E.st.rows, E.st.gran, c.G, c.wg, ra, rb);
   float* out = reinterpret_cast<float*>(L.qkv_raw);
+  float rs = 1.f;  // 1 / rms of the input when the staging leaves it to the product
   return run_gemv<1, 0>(E, sm, g, ra, rb, true,
       [&]() {
         if (!wait_stage(c, sm, E.st.wait, E.s)) return false;
         const LayerInput in = layer_input(c, l);
-        if (in.prev)
-          stage_rmsnorm_vec(sm, D, reinterpret_cast<const float*>(L.attn_norm), c.P->dims.rms_eps, in.prev);
-        else
+        if (in.prev) {
+          stage_norm_vec(sm, D, reinterpret_cast<const float*>(L.attn_norm), in.prev);
+          rs = rms_scale(sm, D, c.P->dims.rms_eps);
+        } else {
           stage_rmsnorm(sm, D, reinterpret_cast<const float*>(L.attn_norm), c.P->dims.rms_eps, in);
+        }
         if (l == 0 && c.wg == 0) {
           float* x0 = reinterpret_cast<float*>(c.P->x0);
           for (int k = threadIdx.x; k < D; k += kThreads) st_coh(x0 + k, in(k));
@@ -887,7 +901,7 @@ __device__ __forceinline__ bool stage_qkv(const StageEnv& E, Smem& sm) {
         return true;
       },
       [&](int ca, int n) {
-        for (int t = threadIdx.x; t < n; t += kThreads) st_coh(out + ca + t, part_sum(sm, t));
+        for (int t = threadIdx.x; t < n; t += kThreads) st_coh(out + ca + t, part_sum(sm, t) * rs);
       });
 }
 
@@ -920,6 +934,7 @@ __device__ __forceinline__ bool stage_qb(const StageEnv& E, Smem& sm) {
   const bool is_lat = 2 * p < d.kv_lora;
   float ga = 0.f, gb = 0.f;  // gains (latent pairs) or (cos, sin) (rotary pairs)
   const float* kvr = raw + d.q_lora;
+  float rs = 1.f;  // 1 / rms of c_q, applied to the product
   bool ok = run_gemv<1, 0>(E, sm, g, ra, rb, true,
       [&]() {
         if (own) {
@@ -939,7 +954,8 @@ __device__ __forceinline__ bool stage_qb(const StageEnv& E, Smem& sm) {
           x0 = ld_coh(kvr + 2 * p);
           x1 = ld_coh(kvr + 2 * p + 1);
         }
-        stage_rmsnorm_vec(sm, d.q_lora, reinterpret_cast<const float*>(L.q_norm), d.rms_eps, raw);
+        stage_norm_vec(sm, d.q_lora, reinterpret_cast<const float*>(L.q_norm), raw);
+        rs = rms_scale(sm, d.q_lora, d.rms_eps);
         if (app) {
           const float tot = block_sum(sm, own && is_lat ? x0 * x0 + x1 * x1 : 0.f);
           const float rs = 1.0f / sqrtf(tot / (float)d.kv_lora + d.rms_eps);
@@ -966,11 +982,11 @@ __device__ __forceinline__ bool stage_qb(const StageEnv& E, Smem& sm) {
           const int r = ca + t;
           const int h = r / qkh, j = r - h * qkh;
           if (j < d.qk_nope) {
-            st_coh(out + r, part_sum(sm, t));
+            st_coh(out + r, part_sum(sm, t) * rs);
           } else if (((j - d.qk_nope) & 1) == 0) {
             const int i = (j - d.qk_nope) >> 1;
             const float cs = gld(tab + 2 * i), sn = gld(tab + 2 * i + 1);
-            const float x0 = part_sum(sm, t), x1 = part_sum(sm, t + 1);
+            const float x0 = part_sum(sm, t) * rs, x1 = part_sum(sm, t + 1) * rs;
             store_qatt(qa, h, d.kv_lora + (j - d.qk_nope), hg, kvw, tau, x0 * cs - x1 * sn, x0 * sn + x1 * cs);
           }
         }
@@ -1371,14 +1387,16 @@ __device__ __forceinline__ bool stage_router(const StageEnv& E, Smem& sm) {
   int ra, rb;
   my_rows(E.st.rows, E.st.gran, c.G, c.wg, ra, rb);
   float* out = reinterpret_cast<float*>(L.router_logits);
+  float rs = 1.f;  // 1 / rms of x_attn, applied to the product
   return run_gemv<2, 0>(E, sm, g, ra, rb, true,
       [&]() {
         if (!wait_stage(c, sm, E.st.wait, E.s)) return false;
-        stage_rmsnorm_vec(sm, d.hidden, reinterpret_cast<const float*>(L.ffn_norm), d.rms_eps, xa);
+        stage_norm_vec(sm, d.hidden, reinterpret_cast<const float*>(L.ffn_norm), xa);
+        rs = rms_scale(sm, d.hidden, d.rms_eps);
         return true;
       },
       [&](int ca, int n) {
-        for (int t = threadIdx.x; t < n; t += kThreads) st_coh(out + ca + t, part_sum(sm, t));
+        for (int t = threadIdx.x; t < n; t += kThreads) st_coh(out + ca + t, part_sum(sm, t) * rs);
       });
 }
 
@@ -1471,18 +1489,20 @@ __device__ __forceinline__ bool stage_gu(const StageEnv& E, Smem& sm) {
   Gemv g = gemv_of(L.gu);
   int ra, rb;
   my_rows(E.st.rows, E.st.gran, c.G, c.wg, ra, rb);
+  float rs = 1.f;  // 1 / rms of x_attn, applied to the product
   return run_gemv<1, 0>(E, sm, g, ra, rb, true,
       [&]() {
         if (!wait_stage(c, sm, E.st.wait, E.s)) return false;
-        stage_rmsnorm_vec(sm, d.hidden, reinterpret_cast<const float*>(L.ffn_norm), d.rms_eps, xa);
+        stage_norm_vec(sm, d.hidden, reinterpret_cast<const float*>(L.ffn_norm), xa);
+        rs = rms_scale(sm, d.hidden, d.rms_eps);
         return true;
       },
       [&](int ca, int n) {
         // rows [gate 8 ; up 8] per group of 16: pair row (ca >> 1) + t
         for (int t = threadIdx.x; t < n / 2; t += kThreads) {
           int grp = t >> 3, r = t & 7;
-          float gt = part_sum(sm, grp * 16 + r);
-          float up = part_sum(sm, grp * 16 + 8 + r);
+          float gt = part_sum(sm, grp * 16 + r) * rs;
+          float up = part_sum(sm, grp * 16 + 8 + r) * rs;
           st_coh(act + (ca >> 1) + t, silu(gt) * up);
         }
       });
@@ -1521,18 +1541,19 @@ __device__ __forceinline__ bool stage_gu_moe(const StageEnv& E, Smem& sm) {
   set_slots(d, L, sm, true, false, false);
   if (threadIdx.x == 0) sm.slots_ready = 0;
   __syncthreads();
+  float rs = 1.f;  // 1 / rms of x_attn, applied to the product
   return run_gemv<1, 3>(E, sm, g, 0, n, true,
       [&]() {
         if (!wait_stage(c, sm, E.st.wait, E.s)) return false;
-        if (!reuse)
-          stage_rmsnorm_vec(sm, d.hidden, reinterpret_cast<const float*>(L.ffn_norm), d.rms_eps, xa);
+        if (!reuse) stage_norm_vec(sm, d.hidden, reinterpret_cast<const float*>(L.ffn_norm), xa);
+        rs = rms_scale(sm, d.hidden, d.rms_eps);  // with reuse: the router stage's sums
         return true;
       },
       [&](int ca, int nr) {
         for (int t = threadIdx.x; t < nr / 2; t += kThreads) {
           int grp = t >> 3, r = t & 7;
-          float gt = part_sum(sm, grp * 16 + r);
-          float up = part_sum(sm, grp * 16 + 8 + r);
+          float gt = part_sum(sm, grp * 16 + r) * rs;
+          float up = part_sum(sm, grp * 16 + 8 + r) * rs;
           // local gate row -> row-slot row -> pair row across all slots
           const int lr = ca + grp * 16 + r;
           const int pr = lr < g.seg_n1 ? g.seg_p1 + lr : g.seg_p2 + (lr - g.seg_n1);
@@ -1605,15 +1626,17 @@ __device__ __forceinline__ bool stage_lm(const StageEnv& E, Smem& sm) {
   my_rows(E.st.rows, E.st.gran, c.G, c.wg, ra, rb);
   float bestv = -INFINITY;
   int besti = 0x7fffffff;
+  float rs = 1.f;  // 1 / rms of the final hidden state, applied to the product
   bool ok = run_gemv<2, 0>(E, sm, g, ra, rb, true,
       [&]() {
         if (!wait_stage(c, sm, E.st.wait, E.s)) return false;
-        stage_rmsnorm_vec(sm, d.hidden, reinterpret_cast<const float*>(c.P->final_norm), d.rms_eps, x);
+        stage_norm_vec(sm, d.hidden, reinterpret_cast<const float*>(c.P->final_norm), x);
+        rs = rms_scale(sm, d.hidden, d.rms_eps);
         return true;
       },
       [&](int ca, int n) {
         for (int t = threadIdx.x; t < n; t += kThreads) {
-          float v = part_sum(sm, t);
+          float v = part_sum(sm, t) * rs;
           gst(logits + ca + t, v);
           if (v > bestv || (v == bestv && ca + t < besti)) { bestv = v; besti = ca + t; }
         }
