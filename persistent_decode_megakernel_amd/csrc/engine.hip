@@ -1031,6 +1031,16 @@ __device__ __forceinline__ bool stage_absorb(const StageEnv& E, Smem& sm) {
       });
 }
 
+// Position chunks per head group this step: about 128 positions per attention
+// unit (its 64-position blocks run one after another), at least 16 chunks
+// (fewer leave the merge cheaper but the units longer) and at most the
+// planned count, which sizes the partial buffer. The attention and W_UV
+// stages derive the same count from the position.
+__device__ __forceinline__ int attn_chunks(const Ctx& c, int ctx) {
+  const int np = c.P->nch;
+  return min(np, max(min(16, np), (ctx + 127) / 128));
+}
+
 // --- ATTN: split-KV MLA attention partials (m, l, acc) per (head, position chunk)
 //
 // Attention is the one dense contraction of the step: 16 heads share every
@@ -1056,7 +1066,7 @@ __device__ __forceinline__ bool stage_attn(const StageEnv& E, Smem& sm) {
   const Ctx& c = E.c;
   const pdm_dims d = load_plan(&c.P->dims);
   const LayerPlan L = layer_of(c, E.st.layer);
-  const int nch = c.P->nch, hg = c.P->hg;
+  const int nch = attn_chunks(c, c.A.pos + 1), hg = c.P->hg;
   const int units = c.P->n_hg * nch;
   if (c.wg >= units) return wait_stage(c, sm, -1, E.s);  // no share of this stage
   const int grp = c.wg / nch, ch = c.wg % nch;
@@ -1266,7 +1276,7 @@ __device__ __forceinline__ bool stage_uv(const StageEnv& E, Smem& sm) {
   const Ctx& c = E.c;
   const pdm_dims d = load_plan(&c.P->dims);
   const LayerPlan L = layer_of(c, E.st.layer);
-  const int nch = c.P->nch, dc = d.kv_lora;
+  const int nch = attn_chunks(c, c.A.pos + 1), dc = d.kv_lora;
   const float* part = reinterpret_cast<const float*>(L.attn_part);
   Gemv g = gemv_of(L.uv);
   int ra, rb;

@@ -63,7 +63,7 @@ struct LayerPlan {
   uint64_t qkv_raw;    // [d_q + d_c + d_r]
   uint64_t q;          // [H][d_n + d_r], rotary part rotated
   uint64_t ql;         // attention-ready queries: bf16 [n_hg][high, residual][kHeadGroup][d_c + d_r + 8]
-  uint64_t attn_part;  // [H][nch][d_c + 2]: acc, max, sum
+  uint64_t attn_part;  // [H][chunks][d_c + 2]: acc, max, sum (chunks <= nch, chosen per step)
   uint64_t o;          // [H * d_v]
   uint64_t xa;         // [D] residual after attention
   uint64_t act;        // [slots * F_e] or [F]: weighted SwiGLU activations
@@ -92,7 +92,7 @@ struct Plan {
   int32_t G;          // persistent workgroups
   int32_t n_stages;
   int32_t max_ctx;
-  int32_t nch;        // attention position chunks per head group
+  int32_t nch;        // most attention position chunks per head group (the count is chosen per step)
   int32_t hg;         // heads per attention unit
   int32_t n_hg;       // head groups
   int32_t pad[2];
