@@ -72,11 +72,16 @@ __device__ __forceinline__ T load_plan(const GLOBAL_AS T* p) {
 template <class T>
 __device__ __forceinline__ void gst(T* p, T v) { *gpw(p) = v; }
 
+// Weight matrix of one expert slot: FP8 codes and their block scales.
+struct __align__(16) SlotRef {
+  const uint8_t* codes;
+  const uint16_t* scales;
+};
+
 struct __align__(16) Smem {
   float x[kXMax];                 // staged input vector(s) of the current stage
   float part[kWaves][kRowChunk];  // per-wave row partial sums
-  const uint8_t* slot_codes[kMaxSlots];
-  const uint16_t* slot_scales[kMaxSlots];
+  SlotRef slot[kMaxSlots];        // weight matrices of the expert slots (one 16-byte LDS read each)
   float slot_w[kMaxSlots];
   int slot_act[kMaxSlots];        // act offset of each slot
   int route_idx[kMaxSlots];       // top-k experts of the current MoE layer
@@ -367,13 +372,15 @@ __device__ __forceinline__ void unit_ptr_t(const Gemv& g, const Smem& sm, int ro
     if constexpr (SLOT == 3) pr = row < g.seg_n1 ? g.seg_p1 + row : g.seg_p2 + (row - g.seg_n1);
     int j = pr >> g.lg_slot;
     int rr = pr & ((1 << g.lg_slot) - 1);
-    cp = sm.slot_codes[j] + (size_t)rr * g.slot_Kb + b;
-    if (EB == 1) sp = sm.slot_scales[j] + (size_t)(rr >> 3) * g.nkb + (b >> 7);
+    const SlotRef sr = sm.slot[j];
+    cp = sr.codes + (size_t)rr * g.slot_Kb + b;
+    if (EB == 1) sp = sr.scales + (size_t)(rr >> 3) * g.nkb + (b >> 7);
   } else {
     int j = b >> g.lg_slot;
     int bb = b & ((1 << g.lg_slot) - 1);
-    cp = sm.slot_codes[j] + (size_t)row * g.slot_Kb + bb;
-    if (EB == 1) sp = sm.slot_scales[j] + (size_t)(row >> 3) * g.nkb + (bb >> 7);
+    const SlotRef sr = sm.slot[j];
+    cp = sr.codes + (size_t)row * g.slot_Kb + bb;
+    if (EB == 1) sp = sr.scales + (size_t)(row >> 3) * g.nkb + (bb >> 7);
   }
 }
 
@@ -1459,8 +1466,7 @@ __device__ __forceinline__ void route_wave(const pdm_dims& d, Smem& sm, const La
     }
     const int t = d.n_shared + lane;
     const uint8_t* base = reinterpret_cast<const uint8_t*>(L.expert_base) + (size_t)my_e * L.expert_stride;
-    sm.slot_codes[t] = base + L.egu.codes;
-    sm.slot_scales[t] = reinterpret_cast<const uint16_t*>(base + L.egu.scales);
+    sm.slot[t] = SlotRef{base + L.egu.codes, reinterpret_cast<const uint16_t*>(base + L.egu.scales)};
     sm.slot_w[t] = my_w;
     sm.slot_act[t] = lane * d.moe_ffn;
   }
@@ -1482,8 +1488,7 @@ __device__ __forceinline__ void set_slots(const pdm_dims& d, const LayerPlan& L,
     const int e = is_shared ? d.n_experts + i : sm.route_idx[i];
     const uint8_t* base = reinterpret_cast<const uint8_t*>(L.expert_base) + (size_t)e * L.expert_stride;
     const Fp8Mat& m = down ? L.edown : L.egu;
-    sm.slot_codes[t] = base + m.codes;
-    sm.slot_scales[t] = reinterpret_cast<const uint16_t*>(base + m.scales);
+    sm.slot[t] = SlotRef{base + m.codes, reinterpret_cast<const uint16_t*>(base + m.scales)};
     sm.slot_w[t] = down || is_shared ? 1.f : sm.route_w[i];
     sm.slot_act[t] = (is_shared ? k + i : i) * d.moe_ffn;
   }
