@@ -384,7 +384,25 @@ __device__ __forceinline__ void unit_ptr_t(const Gemv& g, const Smem& sm, int ro
   }
 }
 
-// dot of one lane's 16 bytes with the staged input
+// A staged input vector sits in LDS permuted within each block of 1024
+// floats: float k (k = 16 l + 4 i + e in its block) is stored at float
+// 256 i + 4 l + e. The 16 floats a lane multiplies with its 16 FP8 weight
+// bytes are then four float4 reads 1 KB apart, and the lanes of a wave read
+// consecutive float4s (no LDS bank conflicts; with the plain order the lanes'
+// float4s were 64 bytes apart). Vectors of K floats occupy K rounded up to a
+// multiple of 1024; groups of 16 (FP8) or 8 (bf16) floats stay together.
+__device__ __forceinline__ int xperm(int k) {
+  return (k & ~1023) | (((k >> 2) & 3) << 8) | (((k >> 4) & 63) << 2) | (k & 3);
+}
+// xperm of a group start: k a multiple of 16 (FP8 units) or of 8 (bf16 units)
+template <int EB>
+__device__ __forceinline__ int xperm_group(int k) {
+  if constexpr (EB == 1) return (k & ~1023) | ((k >> 2) & 252);
+  else return (k & ~1023) | ((k & 8) << 6) | ((k >> 2) & 252);
+}
+
+// dot of one lane's 16 bytes with the staged input; xs = sm.x + xperm(k0)
+// for the lane's first input float k0
 template <int EB>
 __device__ __forceinline__ float unit_dot(const u32x4& w, const float* xs) {
   const float4* x4 = reinterpret_cast<const float4*>(xs);
@@ -395,7 +413,7 @@ __device__ __forceinline__ float unit_dot(const u32x4& w, const float* xs) {
     for (int i = 0; i < 4; ++i) {
       auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)ws[i], false);
       auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)ws[i], true);
-      float4 xv = x4[i];
+      float4 xv = x4[64 * i];
       acc = fmaf(lo[0], xv.x, acc);
       acc = fmaf(lo[1], xv.y, acc);
       acc = fmaf(hi[0], xv.z, acc);
@@ -405,7 +423,7 @@ __device__ __forceinline__ float unit_dot(const u32x4& w, const float* xs) {
     const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      float4 xv = x4[i];
+      float4 xv = x4[64 * i];
       acc = fmaf(bf16_lo(ws[2 * i]), xv.x, acc);
       acc = fmaf(bf16_hi(ws[2 * i]), xv.y, acc);
       acc = fmaf(bf16_lo(ws[2 * i + 1]), xv.z, acc);
@@ -534,14 +552,18 @@ __device__ __forceinline__ bool gemv_rows_t(const Gemv& g, Smem& sm, int ra, int
       const int rq = ok ? row : ra;
       const int k0 = (EB == 1) ? bq : (bq >> 1);
       const int xoff = (g.lg_rpv >= 31) ? 0 : ((rq >> g.lg_rpv) - g.vbase) * g.xK;
-      float d = unit_dot<EB>(W[j], sm.x + xoff + k0);
+      float d = unit_dot<EB>(W[j], sm.x + xperm_group<EB>(xoff + k0));
       if constexpr (EB == 1) d *= bf16_val((uint16_t)SC[j]);
       d = ok ? d : 0.f;
       if constexpr (LONG) {
-        // rows change at most once per unit; flushing is a uniform branch
+        // rows change at most once per unit; flushing is a uniform branch.
+        // A flush adds the four 16-lane row sums into the wave's partial
+        // with LDS atomics (no read-back wait; a wave's adds to one row stay
+        // in program order)
         if (uok && row != cur_row) {
-          float t = wave_sum(acc);
-          if (lane == 0) sm.part[w][cur_row - ra] += t;
+          const float t = row16_sum(acc);
+          if ((lane & 15) == 0)
+            __hip_atomic_fetch_add(&sm.part[w][cur_row - ra], t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
           acc = 0.f;
           cur_row = row;
         }
@@ -552,8 +574,9 @@ __device__ __forceinline__ bool gemv_rows_t(const Gemv& g, Smem& sm, int ra, int
       }
     }
     if constexpr (LONG) {
-      float t = wave_sum(acc);
-      if (lane == 0) sm.part[w][cur_row - ra] += t;
+      const float t = row16_sum(acc);
+      if ((lane & 15) == 0)
+        __hip_atomic_fetch_add(&sm.part[w][cur_row - ra], t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     }
   };
 
@@ -662,7 +685,7 @@ __device__ __forceinline__ float stage_values(Smem& sm, int K, Get&& get) {
 #pragma unroll
     for (int i = 0; i < kStageBatch; ++i) {
       int k = k0 + i * kThreads;
-      if (k < K) sm.x[k] = v[i];
+      if (k < K) sm.x[xperm(k)] = v[i];
       ss += v[i] * v[i];
     }
   }
@@ -687,13 +710,13 @@ __device__ __forceinline__ void stage_rmsnorm(Smem& sm, int K, const float* gain
 #pragma unroll
     for (int i = 0; i < kStageBatch; ++i) {
       int k = k0 + i * kThreads;
-      if (k < K) sm.x[k] = v[i] * gv[i];
+      if (k < K) sm.x[xperm(k)] = v[i] * gv[i];
       ss += v[i] * v[i];
     }
   }
   float tot = block_sum(sm, ss);
   float rs = 1.0f / sqrtf(tot / (float)K + eps);
-  for (int k = threadIdx.x; k < K; k += kThreads) sm.x[k] *= rs;
+  for (int k = threadIdx.x; k < K; k += kThreads) sm.x[xperm(k)] *= rs;
   __syncthreads();
 }
 
@@ -741,7 +764,7 @@ __device__ __forceinline__ float stage_vec(Smem& sm, int K, const float* src, co
       const int i4 = b0 + i * kThreads + threadIdx.x;
       float4 y = v[i];
       if (gain) { y.x *= g[i].x; y.y *= g[i].y; y.z *= g[i].z; y.w *= g[i].w; }
-      if (i4 < n4) *reinterpret_cast<float4*>(sm.x + 4 * i4) = y;
+      if (i4 < n4) *reinterpret_cast<float4*>(sm.x + xperm(4 * i4)) = y;
       ss += v[i].x * v[i].x + v[i].y * v[i].y + v[i].z * v[i].z + v[i].w * v[i].w;
     }
   }
@@ -1321,7 +1344,7 @@ __device__ __forceinline__ bool stage_uv(const StageEnv& E, Smem& sm) {
             for (int i = 0; i < nch; ++i)
               num += pr[i * (dc + 2) + threadIdx.x] *
                      __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, fac), i));
-            sm.x[threadIdx.x] = num;
+            sm.x[xperm(threadIdx.x)] = num;
           }
           __syncthreads();
           return true;
@@ -1352,7 +1375,7 @@ __device__ __forceinline__ bool stage_uv(const StageEnv& E, Smem& sm) {
               num += i0 + b < nch ? v[b] * f : 0.f;
             }
           }
-          if ((int)threadIdx.x < dc) sm.x[(h - h0) * dc + threadIdx.x] = num;
+          if ((int)threadIdx.x < dc) sm.x[xperm((h - h0) * dc + threadIdx.x)] = num;
         }
         __syncthreads();
         return true;
