@@ -14,9 +14,12 @@ OUT_DIR = os.path.join(HERE, "_lib")
 OUT = os.path.join(OUT_DIR, "libpdm.so")
 SOURCES = ["engine.hip", "api.cpp", "planner.cpp"]
 
-# Packed FP32 VALU forms stay off: plain float code only.
+# Packed FP32 VALU forms stay off: plain float code only. The atomic
+# optimizer (which turns a few lanes' LDS or global atomics into a lane loop
+# plus one atomic) is off: the engine's atomics come from one to four lanes.
 HIPCC_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
-               "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+               "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+               "-mllvm", "-amdgpu-atomic-optimizer-strategy=None"]
 
 
 def hipcc() -> str:

@@ -462,9 +462,14 @@ struct NoLate {
   __device__ __forceinline__ void operator()() const {}
 };
 
-template <int EB, bool LONG, int SLOT, class Prep, class Late>
+// FULL (LONG only): rows are whole KB (K a multiple of 1024) and there is one
+// input vector, so a unit's validity is the same for all lanes and its input
+// floats are at a lane-fixed LDS offset: every per-unit address term but the
+// lane's own is uniform (scalar arithmetic).
+template <int EB, bool LONG, int SLOT, bool FULL, class Prep, class Late>
 __device__ __forceinline__ bool gemv_rows_t(const Gemv& g, Smem& sm, int ra, int rb, bool early, Prep&& prep,
                                             Late&& late) {
+  static_assert(LONG || !FULL, "whole-KB rows are long rows");
   const int lane = lane_id();
   const int w = wave_id();
   const int kb = g.Kb;
@@ -515,7 +520,7 @@ __device__ __forceinline__ bool gemv_rows_t(const Gemv& g, Smem& sm, int ra, int
         row = ra + u * m + (lane >> lg_lpr);
         b = (lane & lpr_mask) << 4;
       }
-      const bool ok = u < nunits && b < kb;
+      const bool ok = u < nunits && (FULL || b < kb);
       const uint8_t* cp;
       const uint16_t* sp = nullptr;
       unit_ptr_t<EB, SLOT>(g, sm, ok ? row : ra, ok ? b : 0, cp, sp);
@@ -537,6 +542,7 @@ __device__ __forceinline__ bool gemv_rows_t(const Gemv& g, Smem& sm, int ra, int
       const int u = ub + j;
       const bool uok = u < nunits;
       int row, b;
+      const int seg = c_seg;
       if constexpr (LONG) {
         row = ra + c_row;
         b = (c_seg << 10) + (lane << 4);
@@ -547,12 +553,20 @@ __device__ __forceinline__ bool gemv_rows_t(const Gemv& g, Smem& sm, int ra, int
         row = ra + u * m + (lane >> lg_lpr);
         b = (lane & lpr_mask) << 4;
       }
-      const bool ok = uok && b < kb;
-      const int bq = ok ? b : 0;
-      const int rq = ok ? row : ra;
-      const int k0 = (EB == 1) ? bq : (bq >> 1);
-      const int xoff = (g.lg_rpv >= 31) ? 0 : ((rq >> g.lg_rpv) - g.vbase) * g.xK;
-      float d = unit_dot<EB>(W[j], sm.x + xperm_group<EB>(xoff + k0));
+      const bool ok = uok && (FULL || b < kb);
+      const float* xs;
+      if constexpr (FULL) {
+        // xperm_group of (seg * 1024 + 16 * lane) (FP8) or (seg * 512 + 8 * lane) (bf16)
+        xs = sm.x + (EB == 1 ? (seg << 10) + (lane << 2)
+                             : ((seg >> 1) << 10) + ((lane & 1) << 9) + ((seg & 1) << 7) + ((lane >> 1) << 2));
+      } else {
+        const int bq = ok ? b : 0;
+        const int rq = ok ? row : ra;
+        const int k0 = (EB == 1) ? bq : (bq >> 1);
+        const int xoff = (g.lg_rpv >= 31) ? 0 : ((rq >> g.lg_rpv) - g.vbase) * g.xK;
+        xs = sm.x + xperm_group<EB>(xoff + k0);
+      }
+      float d = unit_dot<EB>(W[j], xs);
       if constexpr (EB == 1) d *= bf16_val((uint16_t)SC[j]);
       d = ok ? d : 0.f;
       if constexpr (LONG) {
@@ -639,8 +653,9 @@ template <int EB, int SLOT, class Prep, class Late>
 __device__ __forceinline__ bool gemv_rows(const Gemv& g, Smem& sm, int ra, int rb, bool early, Prep&& prep,
                                           Late&& late) {
   const bool small = g.Kb < 1024 && (1024 % g.Kb) == 0;
-  return small ? gemv_rows_t<EB, false, SLOT>(g, sm, ra, rb, early, prep, late)
-               : gemv_rows_t<EB, true, SLOT>(g, sm, ra, rb, early, prep, late);
+  if (small) return gemv_rows_t<EB, false, SLOT, false>(g, sm, ra, rb, early, prep, late);
+  if ((g.Kb & 1023) == 0 && g.lg_rpv >= 31) return gemv_rows_t<EB, true, SLOT, true>(g, sm, ra, rb, early, prep, late);
+  return gemv_rows_t<EB, true, SLOT, false>(g, sm, ra, rb, early, prep, late);
 }
 
 // Balanced contiguous share of `rows` (in groups of `gran`) for workgroup wg.
