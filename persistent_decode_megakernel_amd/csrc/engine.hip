@@ -1459,13 +1459,14 @@ __device__ __forceinline__ bool stage_router(const StageEnv& E, Smem& sm) {
 // with sigmoid weights normalised over the chosen experts: into LDS, and the
 // routed slot tables of the gate/up stage (slots n_shared + j) set from them.
 // Lane j keeps the j-th choice, so nothing is read back from LDS.
-__device__ __forceinline__ void route_wave(const pdm_dims& d, Smem& sm, const LayerPlan& L, bool write_tap) {
+template <int NV>  // logits per lane: experts lane + 64 i, i < NV (NV * 64 >= n_experts)
+__device__ __forceinline__ void route_wave_t(const pdm_dims& d, Smem& sm, const LayerPlan& L, bool write_tap) {
   const float* z = reinterpret_cast<const float*>(L.router_logits);
   const int E = d.n_experts, k = d.top_k;
   const int lane = lane_id();
-  float v[16];
+  float v[NV];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
+  for (int i = 0; i < NV; ++i) {
     int e = lane + 64 * i;
     v[i] = e < E ? ld_coh(z + e) : -INFINITY;
   }
@@ -1478,7 +1479,7 @@ __device__ __forceinline__ void route_wave(const pdm_dims& d, Smem& sm, const La
     float bv = -INFINITY;
     int bi = 0x7fffffff;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
+    for (int i = 0; i < NV; ++i) {
       int e = lane + 64 * i;
       if (e < E && v[i] > bv) { bv = v[i]; bi = e; }
     }
@@ -1488,7 +1489,7 @@ __device__ __forceinline__ void route_wave(const pdm_dims& d, Smem& sm, const La
     if (bw >= E) bw = 0;  // only when no finite logit is left (never for finite inputs)
     // remove it
 #pragma unroll
-    for (int i = 0; i < 16; ++i)
+    for (int i = 0; i < NV; ++i)
       if (lane + 64 * i == bw) v[i] = -INFINITY;
     const float sg = 1.0f / (1.0f + __expf(-gm));
     if (lane == j) { my_e = bw; my_w = sg; }
@@ -1508,6 +1509,11 @@ __device__ __forceinline__ void route_wave(const pdm_dims& d, Smem& sm, const La
     sm.slot_w[t] = my_w;
     sm.slot_act[t] = lane * d.moe_ffn;
   }
+}
+
+__device__ __forceinline__ void route_wave(const pdm_dims& d, Smem& sm, const LayerPlan& L, bool write_tap) {
+  if (d.n_experts <= 256) route_wave_t<4>(d, sm, L, write_tap);
+  else route_wave_t<16>(d, sm, L, write_tap);
 }
 
 // Slot tables of a MoE stage: expert matrix pointers, gate weights and act
