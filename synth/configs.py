@@ -72,6 +72,14 @@ CONFIGS = {
         rope=32, v_head=32, ffn=1024, n_experts=16, moe_ffn=256, top_k=2,
         n_shared=1, vocab=2048, layers=("dense", "moe"), prompt_len=256,
         decode_steps=64),
+    # three layers with ragged shapes: rows that are not whole KB (partial
+    # units), 24 heads (head groups of 8), two shared experts, top-3 of 12,
+    # a vocabulary and a prompt that fill no tile exactly
+    "ragged": ModelConfig(
+        name="ragged", hidden=1040, n_heads=24, q_lora=176, kv_lora=128, qk_nope=32,
+        rope=32, v_head=32, ffn=1072, n_experts=12, moe_ffn=64, top_k=3,
+        n_shared=2, vocab=1000, layers=("dense", "moe", "moe"), prompt_len=100,
+        decode_steps=16),
     # one dense layer at DeepSeek-V3 shape, fed by an N(0,1) hidden vector
     "dsv3_dense_layer": ModelConfig(
         name="dsv3_dense_layer", **_DSV3_ATTN, **_DSV3_FFN, vocab=0,

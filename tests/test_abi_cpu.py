@@ -52,7 +52,7 @@ def test_create_without_gpu_reports_device_error(lib):
     assert lib.pdm_create(C.byref(d), 64, 0, C.byref(h)) == L.ERR_DEVICE
 
 
-@pytest.mark.parametrize("name", configs.CONFIG_ORDER)
+@pytest.mark.parametrize("name", configs.CONFIG_ORDER + ("ragged",))
 def test_sizes(lib, name):
     from persistent_decode_megakernel_amd import query_sizes
     cfg = configs.get(name)
@@ -106,7 +106,7 @@ def _validate_dag(plan, cfg):
     assert kinds.count("lm") == (1 if cfg.vocab else 0)
 
 
-@pytest.mark.parametrize("name", configs.CONFIG_ORDER)
+@pytest.mark.parametrize("name", configs.CONFIG_ORDER + ("ragged",))
 def test_stage_plan_is_a_valid_dag(lib, name):
     from persistent_decode_megakernel_amd import describe_plan
     cfg = configs.get(name)
