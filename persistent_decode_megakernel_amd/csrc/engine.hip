@@ -30,7 +30,7 @@
 namespace pdm {
 namespace {
 
-constexpr int kUnroll = 6;  // 1 KB units in flight per wave and buffer
+constexpr int kUnroll = 5;  // 1 KB units in flight per wave and buffer
 constexpr int kEarlyBatches = 1;       // unit batches per wave issued before a stage's dependency wait
 // The last wave of a workgroup polls the dependency counters and issues no
 // load before the wait: loads complete in order per wave, so a poll issued
