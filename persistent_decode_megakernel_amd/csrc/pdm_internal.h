@@ -15,7 +15,7 @@ namespace pdm {
 
 constexpr int kThreads = 512;         // 8 waves of 64 lanes per workgroup
 constexpr int kWaves = kThreads / 64;
-constexpr int kStripes = 16;          // arrival counters per stage
+constexpr int kStripes = 32;          // arrival counters per stage (power of two, < 64)
 constexpr int kCounterStride = 32;    // ints between counters (128 B)
 constexpr int kRowChunk = 256;        // rows combined per LDS pass
 constexpr int kXMax = 32768;          // floats of staged activation per workgroup (128 KB)
