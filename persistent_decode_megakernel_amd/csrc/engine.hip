@@ -912,7 +912,9 @@ __device__ __forceinline__ bool run_gemv(const StageEnv& E, Smem& sm, const Gemv
     if (E.c.A.trace && threadIdx.x == 0 && t_staged) sm.t_mark[0] = t_staged;
     __syncthreads();
     epi(ca, cb - ca);
-    __syncthreads();
+    // The next chunk reuses the partials; after the last chunk the stage's
+    // signal (a workgroup barrier) orders the epilogue before any later LDS use.
+    if (cb < rb) __syncthreads();
     mark(E.c, sm, 2);
   }
   return true;
