@@ -931,20 +931,22 @@ __device__ __forceinline__ bool stage_qkv(const StageEnv& E, Smem& sm) {
   my_rows(E.st.rows, E.st.gran, c.G, c.wg, ra, rb);
   float* out = reinterpret_cast<float*>(L.qkv_raw);
   float rs = 1.f;  // 1 / rms of the input when the staging leaves it to the product
+  // The step input tap (layer 0): every workgroup copies its slice, loaded
+  // before the dependency wait (the input does not depend on this step's work).
+  const LayerInput in = layer_input(c, l);
+  const int tk0 = D * c.wg / c.G, tn = D * (c.wg + 1) / c.G - tk0;
+  const bool tapper = l == 0 && (int)threadIdx.x < tn;
+  const float tap = tapper ? in(tk0 + threadIdx.x) : 0.f;
   return run_gemv<1, 0>(E, sm, g, ra, rb, true,
       [&]() {
         if (!wait_stage(c, sm, E.st.wait, E.s)) return false;
-        const LayerInput in = layer_input(c, l);
         if (in.prev) {
           stage_norm_vec(sm, D, reinterpret_cast<const float*>(L.attn_norm), in.prev);
           rs = rms_scale(sm, D, c.P->dims.rms_eps);
         } else {
           stage_rmsnorm(sm, D, reinterpret_cast<const float*>(L.attn_norm), c.P->dims.rms_eps, in);
         }
-        if (l == 0 && c.wg == 0) {
-          float* x0 = reinterpret_cast<float*>(c.P->x0);
-          for (int k = threadIdx.x; k < D; k += kThreads) st_coh(x0 + k, in(k));
-        }
+        if (tapper) st_coh(reinterpret_cast<float*>(c.P->x0) + tk0 + threadIdx.x, tap);
         return true;
       },
       [&](int ca, int n) {
