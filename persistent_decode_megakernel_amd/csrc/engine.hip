@@ -391,6 +391,7 @@ __device__ __forceinline__ void unit_ptr_t(const Gemv& g, const Smem& sm, int ro
 // consecutive float4s (no LDS bank conflicts; with the plain order the lanes'
 // float4s were 64 bytes apart). Vectors of K floats occupy K rounded up to a
 // multiple of 1024; groups of 16 (FP8) or 8 (bf16) floats stay together.
+static_assert(kXMax % 1024 == 0, "staged vectors occupy whole 1024-float blocks");
 __device__ __forceinline__ int xperm(int k) {
   return (k & ~1023) | (((k >> 2) & 3) << 8) | (((k >> 4) & 63) << 2) | (k & 3);
 }

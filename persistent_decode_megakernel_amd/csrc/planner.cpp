@@ -195,7 +195,8 @@ int build_plan(const pdm_dims& d, int32_t max_ctx, int32_t G, Plan* p, Layout* l
     int64_t ng = st.rows / st.gran;
     int64_t per = ceil_div(ng, G) * st.gran;
     int64_t heads = ceil_div(per, rpv) + 1;
-    if (heads * st.K > kXMax) return PDM_ERR_CONFIG;
+    // staged vectors occupy whole 1024-float blocks of the permuted LDS layout
+    if (align_up((uint64_t)(heads * st.K), 1024) > (uint64_t)kXMax) return PDM_ERR_CONFIG;
   }
 
   // ---------------- scratch
