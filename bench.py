@@ -105,7 +105,8 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this engine runs batch-1 decode on one GPU; multi-GPU runs are not "
-                                   "part of it (see DESIGN.md for how the path would shard)",
+                                   "part of it (a sharded path would split GEMV rows, heads, expert rows "
+                                   "and the vocabulary over GPUs)",
                           "n_gpus": args.gpus}))
         sys.exit(2)
     import torch
