@@ -197,6 +197,84 @@ def test_moe_one_expert_equals_dense():
     np.testing.assert_allclose(dense - x, ref, rtol=1e-12)
 
 
+# --------------------------------------------------------------------------- MoE combination, closed forms
+#
+# The routed experts enter with their sigmoid scores normalised over the
+# chosen set, every shared expert with weight 1 ("What is TileRT" section 5.2:
+# routed experts with a few active per token; the combination rule itself is
+# a reading). Router rows are built so that the logits take chosen values:
+# with x = c * 1 and unit gains, h = RMSNorm(x) is the constant vector
+# c / sqrt(c^2 + eps), and a router row t_e * u with u . h = 1 gives z_e = t_e.
+
+def _swiglu_torch(g, u, dn, h):
+    """down(silu(gate h) * (up h)), composed from torch's SiLU."""
+    return (F.silu(torch.from_numpy(g @ h)) * torch.from_numpy(u @ h)).numpy() @ dn.T
+
+
+def _moe_case(n_exp, top_k, n_shared, logits, D=32, Fe=12, seed=5):
+    from synth import configs
+    rng = np.random.default_rng(seed)
+    cfg = configs.get("tiny").with_(hidden=D, moe_ffn=Fe, n_experts=n_exp, top_k=top_k,
+                                    n_shared=n_shared, layers=("moe",))
+    c = 0.7
+    x = np.full(D, c)
+    h = np.full(D, c / np.sqrt(c * c + cfg.rms_eps))
+    u = h / (h @ h)
+    ws = {("ffn_norm", 0, -1): np.ones(D),
+          ("router", 0, -1): np.asarray(logits, dtype=np.float64)[:, None] * u[None, :]}
+    mats = {}
+    for e in range(n_exp + n_shared):
+        mats[e] = (rng.standard_normal((Fe, D)) * 0.3, rng.standard_normal((Fe, D)) * 0.3,
+                   rng.standard_normal((D, Fe)) * 0.3)
+    return cfg, ws, mats, x, h
+
+
+def _put(ws, mats):
+    for e, (g, u, dn) in mats.items():
+        ws[("w_gate", 0, e)], ws[("w_up", 0, e)], ws[("w_down", 0, e)] = g, u, dn
+    return ws
+
+
+def pin_moe_combination():
+    sig = lambda t: 1.0 / (1.0 + np.exp(-np.asarray(t, dtype=np.float64)))
+    # (1) top-1 with one shared expert whose weights equal the chosen routed
+    #     expert's: the routed weight normalises to 1, the shared one is 1, so
+    #     the FFN adds exactly twice that expert's SwiGLU
+    cfg, ws, mats, x, h = _moe_case(4, 1, 1, [0.1, 2.0, -1.0, 0.5])
+    mats[4] = mats[1]
+    W = _DictW(_put(ws, mats), cfg)
+    taps = {}
+    y = M.ffn_decode(W, cfg, 0, x, taps) - x
+    assert [int(i) for i in taps["router_idx"][0]] == [1]
+    np.testing.assert_allclose(y, 2.0 * _swiglu_torch(*mats[1], h), rtol=1e-12, atol=1e-14)
+    # (2) two routed experts with equal logits and no shared expert: 1/2 each
+    cfg, ws, mats, x, h = _moe_case(5, 2, 0, [0.3, 1.25, -2.0, 1.25, 0.9])
+    W = _DictW(_put(ws, mats), cfg)
+    y = M.ffn_decode(W, cfg, 0, x) - x
+    np.testing.assert_allclose(y, 0.5 * _swiglu_torch(*mats[1], h) + 0.5 * _swiglu_torch(*mats[3], h),
+                               rtol=1e-12, atol=1e-14)
+    # (3) general case: top-3 of 6 with two shared experts, unequal logits;
+    #     weights sigma(t_i) / sum over the chosen three, shared with weight 1
+    t = [0.2, -0.4, 1.7, 0.9, -1.1, 1.3]
+    cfg, ws, mats, x, h = _moe_case(6, 3, 2, t)
+    W = _DictW(_put(ws, mats), cfg)
+    taps = {}
+    y = M.ffn_decode(W, cfg, 0, x, taps) - x
+    chosen = [2, 5, 3]
+    assert [int(i) for i in taps["router_idx"][0]] == chosen
+    w = sig([t[i] for i in chosen])
+    w = w / w.sum()
+    want = _swiglu_torch(*mats[6], h) + _swiglu_torch(*mats[7], h)
+    for wi, e in zip(w, chosen):
+        want = want + wi * _swiglu_torch(*mats[e], h)
+    np.testing.assert_allclose(y, want, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(taps["router_w"][0], w, rtol=1e-14)
+
+
+def test_moe_combination_closed_forms():
+    pin_moe_combination()
+
+
 # --------------------------------------------------------------------------- planted mistakes
 
 def _expect_pin_failure(monkeypatch, target, attr, bad, pin):
@@ -246,3 +324,35 @@ def test_planted_mistakes_are_caught(monkeypatch):
     with monkeypatch.context() as mp:
         _expect_pin_failure(mp, O, "softmax", lambda s, axis=-1: np.exp(s) / np.exp(s).sum(axis=axis, keepdims=True) * 1.01,
                             pin_softmax)
+
+    # MoE combination mistakes: shared expert dropped, shared expert scaled by
+    # the first routed weight, routed weights left unnormalised
+    good_ffn = M.ffn_decode
+
+    def ffn_variant(shared_w, normalise):
+        def ffn(W, cfg, l, x, taps=None):
+            h2 = M.rmsnorm(x, W("ffn_norm", l), cfg.rms_eps)
+            z = W("router", l) @ h2
+            s = M.sigmoid(z)
+            idx = M.topk_indices(s, cfg.top_k)
+            w = s[idx] / np.sum(s[idx]) if normalise else s[idx]
+            y = np.zeros_like(x)
+            for j in range(cfg.n_shared):
+                y = y + shared_w(w) * M.swiglu(W, l, cfg.n_experts + j, h2)
+            for e, we in zip(idx, w):
+                y = y + we * M.swiglu(W, l, int(e), h2)
+            if taps is not None:
+                taps.setdefault("router_logits", []).append(z)
+                taps.setdefault("router_idx", []).append(idx)
+                taps.setdefault("router_w", []).append(w)
+            return x + y
+        return ffn
+    # the variant with the reading's own choices passes (the harness is sound)
+    with monkeypatch.context() as mp:
+        mp.setattr(M, "ffn_decode", ffn_variant(lambda w: 1.0, True))
+        pin_moe_combination()
+    for bad in (ffn_variant(lambda w: 0.0, True), ffn_variant(lambda w: w[0], True),
+                ffn_variant(lambda w: 1.0, False)):
+        with monkeypatch.context() as mp:
+            _expect_pin_failure(mp, M, "ffn_decode", bad, pin_moe_combination)
+    assert M.ffn_decode is good_ffn
