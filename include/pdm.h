@@ -42,7 +42,7 @@ extern "C" {
 typedef struct ihipStream_t* pdm_stream_t; /* a hipStream_t; 0 is the null stream */
 
 #define PDM_MAX_LAYERS 128
-#define PDM_ABI_VERSION 1
+#define PDM_ABI_VERSION 2
 
 /* Error codes */
 enum {
@@ -162,22 +162,21 @@ typedef struct pdm_stage_info {
 
 enum pdm_stage_type {
   PDM_ST_QKV = 0,      /* [W_DQ ; W_DKV] * RMSNorm(x): query and key/value latents */
-  PDM_ST_QB = 1,       /* W_UQ * RMSNorm(c_q), RoPE on the rotary rows; cache row append */
-  PDM_ST_ABSORB = 2,   /* q_lat[h] = W_UK[h]^T q_nope[h] */
-  PDM_ST_ATTN = 3,     /* split-KV MLA attention partials over the latent cache */
-  PDM_ST_UV = 4,       /* merge partials, o[h] = W_UV[h] o_lat[h] */
-  PDM_ST_WO = 5,       /* x += W_O o */
-  PDM_ST_ROUTER = 6,   /* router logits W_r * RMSNorm(x) */
-  PDM_ST_GU = 7,       /* SwiGLU gate/up of the dense FFN */
-  PDM_ST_GU_ROUTED = 8,/* top-k routing, SwiGLU gate/up of the shared and the routed experts */
-  PDM_ST_DOWN = 9,     /* x += sum of down projections (weighted), bf16 layer output */
-  PDM_ST_LM = 10       /* logits = W_lm * RMSNorm(x), argmax */
+  PDM_ST_QB = 1,       /* W_UQ * RMSNorm(c_q), RoPE on the rotary rows; partial q_lat = W_UK^T q_nope */
+  PDM_ST_ATTN = 2,     /* split-KV MLA attention partials over the latent cache; cache row append */
+  PDM_ST_UV = 3,       /* merge partials, o[h] = W_UV[h] o_lat[h] */
+  PDM_ST_WO = 4,       /* x += W_O o */
+  PDM_ST_ROUTER = 5,   /* router logits W_r * RMSNorm(x) */
+  PDM_ST_GU = 6,       /* SwiGLU gate/up of the dense FFN */
+  PDM_ST_GU_ROUTED = 7,/* top-k routing, SwiGLU gate/up of the shared and the routed experts */
+  PDM_ST_DOWN = 8,     /* x += sum of down projections (weighted), bf16 layer output */
+  PDM_ST_LM = 9        /* logits = W_lm * RMSNorm(x), argmax */
 };
 
 enum pdm_buffer_id {
-  PDM_BUF_INPUT = 0, PDM_BUF_QKV = 1, PDM_BUF_Q = 2, PDM_BUF_QLAT = 3, PDM_BUF_ATTN = 4,
-  PDM_BUF_O = 5, PDM_BUF_XATTN = 6, PDM_BUF_ROUTER = 7, PDM_BUF_ACT = 8, PDM_BUF_XOUT = 9,
-  PDM_BUF_LOGITS = 10, PDM_BUF_KV = 11
+  PDM_BUF_INPUT = 0, PDM_BUF_QKV = 1, PDM_BUF_QLAT = 2, PDM_BUF_ATTN = 3, PDM_BUF_O = 4,
+  PDM_BUF_XATTN = 5, PDM_BUF_ROUTER = 6, PDM_BUF_ACT = 7, PDM_BUF_XOUT = 8, PDM_BUF_LOGITS = 9,
+  PDM_BUF_KV = 10
 };
 /* Buffer ids are per layer: id + 16 * layer (the LM head uses layer n_layers). */
 
@@ -267,8 +266,9 @@ int pdm_set_debug(pdm_engine* e, int32_t spin_limit, int32_t skip_signal_stage);
 /* Record per-stage timestamps (wall clock, 100 MHz on MI355X) of the
  * following steps into the bound trace buffer: on != 0 enables, 0 disables.
  * Requires a trace buffer at bind time. Records: [stage][workgroup] x
- * {entered, dependency satisfied, signalled, epoch, input staged, weights
- * consumed, epilogue done, 0}; a mark a stage does not pass through is 0. */
+ * {dependency wait entered, dependency satisfied, signalled, epoch, input
+ * staged, weights consumed, epilogue done, stage entered (before its set-up
+ * and early loads)}; a mark a stage does not pass through is 0. */
 int pdm_set_trace(pdm_engine* e, int32_t on);
 
 int pdm_destroy(pdm_engine* e);

@@ -5,7 +5,7 @@ import ctypes as C
 import os
 
 MAX_LAYERS = 128
-ABI_VERSION = 1
+ABI_VERSION = 2
 
 LIB_DIR = os.path.join(os.path.dirname(os.path.abspath(__file__)), "_lib")
 LIB_PATH = os.path.join(LIB_DIR, "libpdm.so")
@@ -25,9 +25,9 @@ TENSOR_IDS = {
 }
 
 # stage types and buffer ids
-ST_NAMES = ["qkv", "qb", "absorb", "attn", "uv", "wo", "router", "gu", "gu_routed", "down", "lm"]
-BUF_INPUT, BUF_QKV, BUF_Q, BUF_QLAT, BUF_ATTN, BUF_O, BUF_XATTN, BUF_ROUTER = range(8)
-BUF_ACT, BUF_XOUT, BUF_LOGITS, BUF_KV = range(8, 12)
+ST_NAMES = ["qkv", "qb", "attn", "uv", "wo", "router", "gu", "gu_routed", "down", "lm"]
+BUF_INPUT, BUF_QKV, BUF_QLAT, BUF_ATTN, BUF_O, BUF_XATTN, BUF_ROUTER = range(7)
+BUF_ACT, BUF_XOUT, BUF_LOGITS, BUF_KV = range(7, 11)
 
 
 class Dims(C.Structure):

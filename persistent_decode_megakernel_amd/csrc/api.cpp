@@ -85,16 +85,16 @@ void absolutize(const pdm_engine& e, Plan* a) {
   auto fm = [&](Fp8Mat& m) { m.codes += W; m.scales += W; };
   auto fs = [&](uint64_t& v) { v += S; };
   if (e.dims.vocab > 0) { fw(a->embed); fw(a->final_norm); fw(a->lm_head); }
-  fs(a->rope_tab); fs(a->counters); fs(a->status); fs(a->lm_best); fs(a->logits_internal); fs(a->x0);
+  fs(a->rope_tab); fs(a->counters); fs(a->flags); fs(a->status); fs(a->lm_best); fs(a->logits_internal); fs(a->x0);
   a->trace = reinterpret_cast<uint64_t>(e.trace);
   for (int l = 0; l < e.dims.n_layers; ++l) {
     LayerPlan& L = a->layers[l];
     fw(L.attn_norm); fw(L.q_norm); fw(L.kv_norm); fw(L.ffn_norm);
-    fm(L.qkv); fm(L.qb); fm(L.ukT); fm(L.uv); fm(L.wo);
+    fm(L.qkv); fm(L.qb); fm(L.uk); fm(L.uv); fm(L.wo);
     if (!L.is_moe) { fm(L.gu); fm(L.down); }
     else { fw(L.router); fw(L.expert_base); }  // egu / edown stay relative to an expert block
     L.kv += K;
-    fs(L.qkv_raw); fs(L.q); fs(L.ql); fs(L.attn_part); fs(L.o); fs(L.xa); fs(L.act);
+    fs(L.qkv_raw); fs(L.qlat_part); fs(L.qrope); fs(L.attn_part); fs(L.o); fs(L.xa); fs(L.act);
     fs(L.router_logits); fs(L.xo); fs(L.topk_idx); fs(L.topk_w);
   }
 }
@@ -260,8 +260,8 @@ int pdm_load_fp8(pdm_engine* e, int32_t tensor, int32_t layer, int32_t expert, c
     case PDM_T_WKV_A: set(0, kvr, D, L.qkv, d.q_lora, 0); return into(L.qkv, zero);
     case PDM_T_WQ_B: set(0, H * qkh, d.q_lora, L.qb, 0, 0); return into(L.qb, zero);
     case PDM_T_WKV_B: {
-      set(1, H * (d.qk_nope + d.v_head), d.kv_lora, L.ukT, 0, 0);
-      rc = into(L.ukT, zero);
+      set(1, H * (d.qk_nope + d.v_head), d.kv_lora, L.uk, 0, 0);
+      rc = into(L.uk, zero);
       if (rc) return rc;
       set(2, H * (d.qk_nope + d.v_head), d.kv_lora, L.uv, 0, 0);
       return into(L.uv, zero);

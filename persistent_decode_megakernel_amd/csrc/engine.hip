@@ -89,7 +89,7 @@ struct __align__(16) Smem {
   float red[2 * kWaves];
   float nred[kWaves];             // per-wave sums of squares of the last normalised staging
   int ired[2 * kWaves];
-  uint64_t t_enter, t_ready;
+  uint64_t t_entry, t_enter, t_ready;  // stage entered, dependency wait entered, wait done
   uint64_t t_mark[3];             // input staged, weights consumed, epilogue done
   int abort;
   int claim;                      // next free unit batch of the current GEMV row chunk
@@ -141,25 +141,7 @@ __device__ __forceinline__ uint32_t pack_bf16x2(__bf16 a, __bf16 b) {
   return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
 }
 
-// Attention-ready queries of a layer: [head group][high, residual][kMH][kvr + 8]
-// bf16 of q * tau (tau = 1 / sqrt(d_qk)): columns [0, d_c) are q_lat (written
-// by the absorb stage), [d_c, d_c + d_r) the rotated rotary part (by the qb
-// stage); the attention stage copies a head group's image into LDS as is.
 constexpr int kMH = kHeadGroup;  // heads per MFMA tile (unit heads padded to kMH)
-// u32 index of the column pair (col, col + 1), col even, of head h
-__device__ __forceinline__ size_t qatt_pair(int h, int col, int hg, int kvr, int part) {
-  const int grp = h / hg, hh = h - grp * hg;
-  return ((((size_t)grp * 2 + part) * kMH + hh) * (kvr + 8) + col) >> 1;
-}
-// stores q-pair (a, b) of head h at columns (col, col + 1)
-__device__ __forceinline__ void store_qatt(uint32_t* qa, int h, int col, int hg, int kvr, float tau, float a,
-                                           float b) {
-  __bf16 ah, al, bh, bl;
-  split_bf16(a * tau, ah, al);
-  split_bf16(b * tau, bh, bl);
-  st_coh_u(qa + qatt_pair(h, col, hg, kvr, 0), pack_bf16x2(ah, bh));
-  st_coh_u(qa + qatt_pair(h, col, hg, kvr, 1), pack_bf16x2(al, bl));
-}
 
 // Round an fp32 value to the nearest bf16 value (ties to even), kept in fp32.
 __device__ __forceinline__ float round_bf16(float v) {
@@ -283,14 +265,15 @@ __device__ __forceinline__ bool wait_stage(const Ctx& c, Smem& sm, int s, int my
   if (s >= 0 && wave_id() == kPollWave) {
     const int lane = lane_id();
     const int* ctr = counter_ptr(c, s, lane & (kStripes - 1));
-    const int target = (int)c.A.epoch * stripe_count(c.G, lane & (kStripes - 1));
+    // counters grow by stripe_count per step: compare modulo 2^32
+    const uint32_t target = c.A.epoch * (uint32_t)stripe_count(c.G, lane & (kStripes - 1));
     const GLOBAL_AS unsigned long long* st = gp(reinterpret_cast<const unsigned long long*>(c.P->status));
     const bool poll_ctr = lane < kStripes && lane < c.G;
     int spins = 0;
     while (true) {
       bool ok = true;
       int seen = 0;
-      if (poll_ctr) { seen = ld_coh_i(ctr); ok = seen >= target; }
+      if (poll_ctr) { seen = ld_coh_i(ctr); ok = (int)((uint32_t)seen - target) >= 0; }
       bool abort = false;
       if (lane == kStripes) {
         unsigned long long v = __hip_atomic_load(st, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -300,6 +283,54 @@ __device__ __forceinline__ bool wait_stage(const Ctx& c, Smem& sm, int s, int my
       if (__all(ok)) break;
       if (++spins > c.A.spin_limit) {
         if (!ok) set_watchdog(c.P->status, c.A.epoch, c.wg, my_stage, seen);
+        if (lane == 0) sm.abort = 1;
+        break;
+      }
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x == 0 && c.A.trace) sm.t_ready = wall_clock64();
+  return sm.abort == 0;
+}
+
+// Wait until workgroups [w0, w1] of G have finished stage `s` this step: each
+// workgroup's completion flag holds the epoch of the last step in which it
+// finished the stage. The polling wave samples up to 256 flags per round (4
+// per lane, loaded together) and the status word. An empty range (w0 > w1)
+// or s < 0 waits for nothing. All threads of the workgroup must call it.
+__device__ __forceinline__ bool wait_flags(const Ctx& c, Smem& sm, int s, int w0, int w1, int my_stage) {
+  if (threadIdx.x == 0) {
+    sm.abort = 0;
+    if (c.A.trace) {
+      sm.t_enter = wall_clock64();
+      sm.t_mark[0] = sm.t_mark[1] = sm.t_mark[2] = 0;
+    }
+  }
+  if (s >= 0 && w0 <= w1 && wave_id() == kPollWave) {
+    const int lane = lane_id();
+    const int n = w1 - w0 + 1;
+    const uint32_t* f = reinterpret_cast<const uint32_t*>(c.P->flags) + (size_t)s * c.G + w0;
+    const GLOBAL_AS unsigned long long* st = gp(reinterpret_cast<const unsigned long long*>(c.P->status));
+    int spins = 0;
+    while (true) {
+      uint32_t v[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) v[k] = lane + 64 * k < n ? ld_coh_u(f + lane + 64 * k) : c.A.epoch;
+      unsigned long long sv = lane == 0 ? __hip_atomic_load(st, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0ull;
+      bool ok = true;
+      uint32_t seen = c.A.epoch;
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        if ((int)(v[k] - c.A.epoch) < 0) { ok = false; seen = v[k]; }
+      for (int i = lane + 256; i < n; i += 64) {  // ranges beyond 256 workgroups
+        const uint32_t x = ld_coh_u(f + i);
+        if ((int)(x - c.A.epoch) < 0) { ok = false; seen = x; }
+      }
+      const bool abort = lane == 0 && (uint32_t)(sv >> 32) == c.A.epoch && (uint32_t)sv != 0u;
+      if (__any(abort)) { if (lane == 0) sm.abort = 1; break; }
+      if (__all(ok)) break;
+      if (++spins > c.A.spin_limit) {
+        if (!ok) set_watchdog(c.P->status, c.A.epoch, c.wg, my_stage, (int)seen);
         if (lane == 0) sm.abort = 1;
         break;
       }
@@ -321,8 +352,10 @@ __device__ __forceinline__ void signal_stage(const Ctx& c, Smem& sm, int s) {
   mem_done();
   __syncthreads();
   if (threadIdx.x == 0) {
-    if (!(s == c.A.skip_stage && c.wg == 0))
+    if (!(s == c.A.skip_stage && c.wg == 0)) {
       __hip_atomic_fetch_add(gpw(counter_ptr(c, s, c.wg & (kStripes - 1))), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      st_coh_u(reinterpret_cast<uint32_t*>(c.P->flags) + (size_t)s * c.G + c.wg, c.A.epoch);
+    }
     if (c.A.trace) {
       GLOBAL_AS uint64_t* t = gpw(reinterpret_cast<uint64_t*>(c.A.trace) + ((size_t)s * c.G + c.wg) * kTraceWords);
       t[0] = sm.t_enter;
@@ -332,7 +365,7 @@ __device__ __forceinline__ void signal_stage(const Ctx& c, Smem& sm, int s) {
       t[4] = sm.t_mark[0];
       t[5] = sm.t_mark[1];
       t[6] = sm.t_mark[2];
-      t[7] = 0;
+      t[7] = sm.t_entry;
     }
   }
 }
@@ -610,10 +643,12 @@ __device__ __forceinline__ bool gemv_rows_t(const Gemv& g, Smem& sm, int ra, int
   // other waves stream the first; a batch beyond the first segment waits for
   // its LDS flag. The flag stays set for later row chunks of the stage.
   bool ready = !g.split;
-  if (g.split && w == kPollWave) {
+  if (w == kPollWave) {
     late();
-    __hip_atomic_store(&sm.slots_ready, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
-    ready = true;
+    if (g.split) {
+      __hip_atomic_store(&sm.slots_ready, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+      ready = true;
+    }
   }
   auto gate = [&](int bt) {
     if (ready || bt < ebat || bt >= nbat) return;
@@ -817,6 +852,7 @@ __device__ __forceinline__ void stage_plain_vec(Smem& sm, int K, const float* sr
 // relaxed agent-scope atomic load does, for data written this step by other
 // workgroups. The caller waits for completion (vmcnt) before using the data.
 
+template <unsigned CPOL = kCpolSc1>
 __device__ __forceinline__ void dma_to_lds(void* dst, const void* src, int nbytes) {
   const int lane = lane_id();
   const char* sb = reinterpret_cast<const char*>(src);
@@ -824,7 +860,23 @@ __device__ __forceinline__ void dma_to_lds(void* dst, const void* src, int nbyte
   for (int off = 0; off < nbytes; off += 1024) {
     const int o = min(off + lane * 16, nbytes - 16);
     __builtin_amdgcn_global_load_lds((const GLOBAL_AS void*)(sb + o),
-                                     (__attribute__((address_space(3))) void*)(db + off), 16, 0, kCpolSc1);
+                                     (__attribute__((address_space(3))) void*)(db + off), 16, 0, CPOL);
+  }
+}
+
+// The same copy spread over all waves of the workgroup (1 KB pieces round
+// robin), for copies too large for one wave's loads in flight. Every wave
+// then waits for its own pieces (mem_done) before the barrier that publishes
+// the data; `dst` needs the same 1 KB of slack.
+template <unsigned CPOL = kCpolSc1>
+__device__ __forceinline__ void dma_to_lds_wg(void* dst, const void* src, int nbytes) {
+  const int lane = lane_id();
+  const char* sb = reinterpret_cast<const char*>(src);
+  char* db = reinterpret_cast<char*>(dst);
+  for (int off = wave_id() * 1024; off < nbytes; off += kWaves * 1024) {
+    const int o = min(off + lane * 16, nbytes - 16);
+    __builtin_amdgcn_global_load_lds((const GLOBAL_AS void*)(sb + o),
+                                     (__attribute__((address_space(3))) void*)(db + off), 16, 0, CPOL);
   }
 }
 
@@ -875,8 +927,8 @@ __device__ __forceinline__ Gemv gemv_of(const Fp8Mat& m, const char* base_unused
 // Generic single-chunk-loop driver: processes the workgroup's rows in chunks;
 // `prep` (wait + staging) runs before the first chunk; `epi(ra_chunk, n)`
 // reads the chunk's row results through part_sum.
-// `late` (g.split only) runs on the polling wave once, after prep, while the
-// other waves already stream the first row segment.
+// `late` runs on the polling wave once, after prep (with g.split: while the
+// other waves already stream the first row segment).
 template <int EB, int SLOT, class Prep, class Epi, class Late = NoLate>
 __device__ __forceinline__ bool run_gemv(const StageEnv& E, Smem& sm, const Gemv& g, int ra, int rb, bool early,
                                          Prep&& prep, Epi&& epi, Late&& late = Late{}) {
@@ -955,7 +1007,47 @@ __device__ __forceinline__ bool stage_qkv(const StageEnv& E, Smem& sm) {
       });
 }
 
-// --- QB: W_UQ * RMSNorm(c_q) with RoPE on the rotary rows; the last workgroup appends the cache row
+// --- QB: q = W_UQ * RMSNorm(c_q), with the absorbed key projection fused in.
+//
+// Rotary query pairs are rotated and stored (scaled by tau = 1 / sqrt(d_qk),
+// split into a bf16 high part and a bf16 residual) for the attention stage.
+// The q_nope values the workgroup computed stay in LDS and are multiplied by
+// the matching rows of W_UK: q_lat[h] = W_UK[h]^T q_nope[h] = sum over n of
+// q_nope[h][n] * W_UK[h][n][:], so the rows n this workgroup holds give a
+// partial sum of q_lat[h] (one per head and workgroup; the attention stage
+// adds a head's partials in a fixed order). No workgroup waits for another
+// between the query projection and the absorbed product, and the W_UK rows
+// (static weights) are copied into LDS by the polling wave while the other
+// waves stream W_UQ.
+__device__ __forceinline__ void store_qrope(uint32_t* qr, int h, int col, int hg, int dr, float tau, float a,
+                                            float b) {
+  const int grp = h / hg, hh = h - grp * hg;
+  __bf16 ah, al, bh, bl;
+  split_bf16(a * tau, ah, al);
+  split_bf16(b * tau, bh, bl);
+  st_coh_u(qr + ((((size_t)grp * 2 + 0) * hg + hh) * dr + col) / 2, pack_bf16x2(ah, bh));
+  st_coh_u(qr + ((((size_t)grp * 2 + 1) * hg + hh) * dr + col) / 2, pack_bf16x2(al, bl));
+}
+
+// LDS layout of the q_b stage (byte offsets into sm.x): the staged c_q, the
+// workgroup's q_nope values, its W_UK rows and their scale entries (both
+// copied by DMA, each followed by 1 KB of slack), the absorb reduction.
+struct QbLds {
+  int qn, wk, wsc, red, sc_pre, sc_bytes, gA;
+  __device__ __forceinline__ QbLds(int q_lora, int nq, int dc, int u0, int u1, const uint16_t* scales) {
+    const int nkb = dc / 128;
+    qn = ((q_lora + 1023) & ~1023) * 4;
+    wk = qn + ((nq + 3) & ~3) * 4;
+    gA = u0 >> 3;
+    const int gB = nq > 0 ? (u1 - 1) >> 3 : gA;
+    const uintptr_t src = reinterpret_cast<uintptr_t>(scales + (size_t)gA * nkb);
+    sc_pre = (int)(src & 15);
+    sc_bytes = ((gB - gA + 1) * nkb * 2 + sc_pre + 15) & ~15;
+    wsc = wk + nq * dc + 1024;
+    red = wsc + sc_bytes + 1024;
+  }
+};
+
 __device__ __forceinline__ bool stage_qb(const StageEnv& E, Smem& sm) {
   const Ctx& c = E.c;
   const pdm_dims d = load_plan(&c.P->dims);
@@ -963,132 +1055,114 @@ __device__ __forceinline__ bool stage_qb(const StageEnv& E, Smem& sm) {
   const LayerPlan L = layer_of(c, l);
   const float* raw = reinterpret_cast<const float*>(L.qkv_raw);
   const float* tab = reinterpret_cast<const float*>(c.P->rope_tab) + (size_t)c.A.pos * d.rope;  // (cos, sin) pairs
-  const int qkh = d.qk_nope + d.rope;
+  const int qkh = d.qk_nope + d.rope, dn = d.qk_nope, dc = d.kv_lora, dr = d.rope;
   Gemv g = gemv_of(L.qb);
   int ra, rb;
   my_rows(E.st.rows, E.st.gran, c.G, c.wg, ra, rb);
-  float* out = reinterpret_cast<float*>(L.q);
-  uint32_t* qa = reinterpret_cast<uint32_t*>(L.ql);
-  const int hg = c.P->hg, kvw = d.kv_lora + d.rope;
+  int u0, u1;
+  qb_nope_rows(d, ra, rb, u0, u1);
+  const int nq = u1 - u0;
+  const QbLds lay(d.q_lora, nq, dc, u0, u1, reinterpret_cast<const uint16_t*>(L.uk.scales));
+  char* xb = reinterpret_cast<char*>(sm.x);
+  float* qn = reinterpret_cast<float*>(xb + lay.qn);
+  const uint8_t* wk = reinterpret_cast<const uint8_t*>(xb + lay.wk);
+  const uint8_t* wsc = reinterpret_cast<const uint8_t*>(xb + lay.wsc);
+  float* red = reinterpret_cast<float*>(xb + lay.red);
+  uint32_t* qr = reinterpret_cast<uint32_t*>(L.qrope);
+  const int hg = c.P->hg;
   const float tau = 1.0f / sqrtf((float)qkh);
-  // The last workgroup also appends this step's cache row
-  // [RMSNorm(kv latent) ; RoPE(rotary key)] (bf16, at position pos). Thread p
-  // owns the value pair 2p, 2p + 1: its gains or rotation come from static
-  // data and are loaded before the wait, its latent values are loaded with
-  // the query staging (one round trip for both), and the row is written
-  // before the weights are consumed.
-  const bool app = c.wg == c.G - 1;
-  const int npairs = (d.kv_lora + d.rope) / 2;  // <= kPreThreads: the polling wave holds none
-  const int p = threadIdx.x;
-  const bool own = app && p < npairs;
-  const bool is_lat = 2 * p < d.kv_lora;
-  float ga = 0.f, gb = 0.f;  // gains (latent pairs) or (cos, sin) (rotary pairs)
-  const float* kvr = raw + d.q_lora;
   float rs = 1.f;  // 1 / rms of c_q, applied to the product
-  bool ok = run_gemv<1, 0>(E, sm, g, ra, rb, true,
+  const bool ok = run_gemv<1, 0>(E, sm, g, ra, rb, true,
       [&]() {
-        if (own) {
-          if (is_lat) {
-            const float* gk = reinterpret_cast<const float*>(L.kv_norm) + 2 * p;
-            ga = gld(gk);
-            gb = gld(gk + 1);
-          } else {
-            const int i = p - d.kv_lora / 2;
-            ga = gld(tab + 2 * i);
-            gb = gld(tab + 2 * i + 1);
-          }
-        }
         if (!wait_stage(c, sm, E.st.wait, E.s)) return false;
-        float x0 = 0.f, x1 = 0.f;
-        if (own) {
-          x0 = ld_coh(kvr + 2 * p);
-          x1 = ld_coh(kvr + 2 * p + 1);
-        }
         stage_norm_vec(sm, d.q_lora, reinterpret_cast<const float*>(L.q_norm), raw);
         rs = rms_scale(sm, d.q_lora, d.rms_eps);
-        if (app) {
-          const float tot = block_sum(sm, own && is_lat ? x0 * x0 + x1 * x1 : 0.f);
-          const float rs = 1.0f / sqrtf(tot / (float)d.kv_lora + d.rms_eps);
-          if (own) {
-            float a, b;
-            if (is_lat) {
-              a = x0 * rs * ga;
-              b = x1 * rs * gb;
-            } else {
-              a = x0 * ga - x1 * gb;
-              b = x0 * gb + x1 * ga;
-            }
-            uint32_t* row = reinterpret_cast<uint32_t*>(reinterpret_cast<uint16_t*>(L.kv) +
-                                                        (size_t)c.A.pos * (d.kv_lora + d.rope));
-            st_coh_u(row + p, (uint32_t)bf16_bits(a) | ((uint32_t)bf16_bits(b) << 16));
-          }
-        }
         return true;
       },
       [&](int ca, int n) {
-        // q_nope rows to the fp32 buffer (the absorb stage's input); rotary
-        // pairs (adjacent rows, starting even) rotated into the attention layout
+        // q_nope rows into LDS (W_UK row index h * d_n + j); rotary pairs
+        // (adjacent rows, starting even) rotated into the query store
         for (int t = threadIdx.x; t < n; t += kThreads) {
           const int r = ca + t;
           const int h = r / qkh, j = r - h * qkh;
-          if (j < d.qk_nope) {
-            st_coh(out + r, part_sum(sm, t) * rs);
-          } else if (((j - d.qk_nope) & 1) == 0) {
-            const int i = (j - d.qk_nope) >> 1;
+          if (j < dn) {
+            qn[h * dn + j - u0] = part_sum(sm, t) * rs;
+          } else if (((j - dn) & 1) == 0) {
+            const int i = (j - dn) >> 1;
             const float cs = gld(tab + 2 * i), sn = gld(tab + 2 * i + 1);
             const float x0 = part_sum(sm, t) * rs, x1 = part_sum(sm, t + 1) * rs;
-            store_qatt(qa, h, d.kv_lora + (j - d.qk_nope), hg, kvw, tau, x0 * cs - x1 * sn, x0 * sn + x1 * cs);
+            store_qrope(qr, h, j - dn, hg, dr, tau, x0 * cs - x1 * sn, x0 * sn + x1 * cs);
           }
         }
-      });
-  return ok;
-}
-
-// --- ABSORB: q_lat[h] = W_UK[h]^T q_nope[h]  (rows (h, c), K = d_n, per-head input)
-__device__ __forceinline__ bool stage_absorb(const StageEnv& E, Smem& sm) {
-  const Ctx& c = E.c;
-  const pdm_dims d = load_plan(&c.P->dims);
-  const LayerPlan L = layer_of(c, E.st.layer);
-  const int qkh = d.qk_nope + d.rope;
-  const float* q = reinterpret_cast<const float*>(L.q);
-  Gemv g = gemv_of(L.ukT);
-  int ra, rb;
-  my_rows(E.st.rows, E.st.gran, c.G, c.wg, ra, rb);
-  g.lg_rpv = 31 - __builtin_clz(d.kv_lora);
-  g.vbase = ra / d.kv_lora;
-  g.xK = d.qk_nope;
-  uint32_t* qa = reinterpret_cast<uint32_t*>(L.ql);
-  const int hg = c.P->hg, kvr = d.kv_lora + d.rope;
-  const float tau = 1.0f / sqrtf((float)qkh);
-  return run_gemv<1, 0>(E, sm, g, ra, rb, true,
-      [&]() {
-        if (!wait_stage(c, sm, E.st.wait, E.s)) return false;
-        int h0 = ra / d.kv_lora, h1 = (rb - 1) / d.kv_lora;
-        int n = (h1 - h0 + 1) * d.qk_nope;
-        stage_plain(sm, n, [&](int k) {
-          int h = h0 + k / d.qk_nope;
-          return ld_coh(q + (size_t)h * qkh + (k % d.qk_nope));
-        });
-        return true;
       },
-      [&](int ca, int n) {
-        // rows (h, c) in pairs of adjacent latent columns (chunks start and end even)
-        for (int t = threadIdx.x; t < n / 2; t += kThreads) {
-          const int r = ca + 2 * t;
-          const int h = r >> g.lg_rpv, col = r & (d.kv_lora - 1);
-          store_qatt(qa, h, col, hg, kvr, tau, part_sum(sm, 2 * t), part_sum(sm, 2 * t + 1));
+      [&]() {
+        // polling wave, after the wait: the W_UK rows and scales of this
+        // workgroup's q_nope rows into LDS (static weights, default policy)
+        if (nq > 0) {
+          dma_to_lds<0>(xb + lay.wk, reinterpret_cast<const uint8_t*>(L.uk.codes) + (size_t)u0 * dc, nq * dc);
+          const uintptr_t sa = reinterpret_cast<uintptr_t>(reinterpret_cast<const uint16_t*>(L.uk.scales) +
+                                                           (size_t)lay.gA * (dc / 128));
+          dma_to_lds<0>(xb + lay.wsc, reinterpret_cast<const void*>(sa - lay.sc_pre), lay.sc_bytes);
         }
       });
+  if (!ok) return false;
+  if (nq <= 0) return true;
+  if (wave_id() == kPollWave) mem_done();
+  __syncthreads();  // q_nope values and the copied W_UK rows are in LDS
+  // Absorbed product: thread t takes the 16 latent columns of 16-byte unit
+  // cb = t mod (d_c / 16) of every (threads per column block)-th row and
+  // keeps 16 sums; the per-thread sums of a column are then added in LDS.
+  const int cpr = dc >> 4;              // 16-byte units per W_UK row
+  const int slots = kThreads / cpr;     // threads per column block
+  const int cb = threadIdx.x & (cpr - 1), sl = threadIdx.x / cpr;
+  const int nkb = dc / 128;
+  const int maxp = c.P->qb_maxparts, gran = c.P->qb_gran;
+  float* part = reinterpret_cast<float*>(L.qlat_part);
+  const int hA = u0 / dn, hB = (u1 - 1) / dn;
+  for (int h = hA; h <= hB; ++h) {
+    const int a = max(u0, h * dn) - u0, b = min(u1, (h + 1) * dn) - u0;
+    float acc[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+    for (int r = a + sl; r < b; r += slots) {
+      const u32x4 w = *reinterpret_cast<const u32x4*>(wk + (size_t)r * dc + cb * 16);
+      const int u = u0 + r;
+      const uint16_t sb = *reinterpret_cast<const uint16_t*>(wsc + lay.sc_pre + (((u >> 3) - lay.gA) * nkb + (cb >> 3)) * 2);
+      const float q = qn[r] * bf16_val(sb);
+      const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)ws[i], false);
+        auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)ws[i], true);
+        acc[4 * i + 0] = fmaf(lo[0], q, acc[4 * i + 0]);
+        acc[4 * i + 1] = fmaf(lo[1], q, acc[4 * i + 1]);
+        acc[4 * i + 2] = fmaf(hi[0], q, acc[4 * i + 2]);
+        acc[4 * i + 3] = fmaf(hi[1], q, acc[4 * i + 3]);
+      }
+    }
+    float4* rd = reinterpret_cast<float4*>(red + sl * dc + cb * 16);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) rd[i] = make_float4(acc[4 * i], acc[4 * i + 1], acc[4 * i + 2], acc[4 * i + 3]);
+    __syncthreads();
+    const int slot = c.wg - qb_first(d, gran, c.G, h);
+    float* dst = part + ((size_t)h * maxp + slot) * dc;
+    for (int cc = threadIdx.x; cc < dc; cc += kThreads) {
+      float sum = 0.f;
+      for (int k = 0; k < slots; ++k) sum += red[k * dc + cc];
+      st_coh(dst + cc, sum);
+    }
+    __syncthreads();
+  }
+  return true;
 }
 
-// Position chunks per head group this step: about 128 positions per attention
-// unit (its 64-position blocks run one after another), at least 16 chunks
-// (fewer leave the merge cheaper but the units longer) and at most the
-// planned count, which sizes the partial buffer. The attention and W_UV
-// stages derive the same count from the position.
+// Position chunks per head group this step: at least kChunkPos positions
+// per attention unit and at most the planned count (one unit per workgroup
+// when the context allows it), which also sizes the partial buffer. The
+// attention and W_UV stages derive the same count from the position.
+constexpr int kChunkPos = 16;
 __device__ __forceinline__ int attn_chunks(const Ctx& c, int ctx) {
-  const int np = c.P->nch;
-  return min(np, max(min(16, np), (ctx + 127) / 128));
+  return min(c.P->nch, max(1, (ctx + kChunkPos - 1) / kChunkPos));
 }
 
 // --- ATTN: split-KV MLA attention partials (m, l, acc) per (head, position chunk)
@@ -1118,18 +1192,40 @@ __device__ __forceinline__ bool stage_attn(const StageEnv& E, Smem& sm) {
   const LayerPlan L = layer_of(c, E.st.layer);
   const int nch = attn_chunks(c, c.A.pos + 1), hg = c.P->hg;
   const int units = c.P->n_hg * nch;
-  if (c.wg >= units) return wait_stage(c, sm, -1, E.s);  // no share of this stage
+  if (c.wg >= units) return wait_flags(c, sm, -1, 0, -1, E.s);  // no share of this stage
   const int grp = c.wg / nch, ch = c.wg % nch;
   const int pos = c.A.pos, ctx = pos + 1;
   const int chunk = (ctx + nch - 1) / nch;
   const int t0 = min(ctx, ch * chunk), t1 = min(ctx, t0 + chunk);
-  const int dc = d.kv_lora, dr = d.rope, kvr = dc + dr;
+  const int dc = d.kv_lora, dr = d.rope, kvr = dc + dr, qkh = d.qk_nope + dr;
   const int q8n = kvr / 8;              // 16-byte pieces per cache row
   const int nkb = kvr / 32;             // MFMA k-blocks of a score
   const int kstr = kvr / 2 + 4;         // LDS cache-row stride in u32 (padded)
   const int qstr = kvr + 8;             // LDS query-row stride in bf16 (padded)
   constexpr int pstr = kAttnBlock + 4;  // LDS probability-row stride in floats
   const uint16_t* cache = reinterpret_cast<const uint16_t*>(L.kv);
+  // The unit whose chunk holds position pos builds this step's cache row
+  // [RMSNorm(latent) ; RoPE(rotary key)] itself from the key/value latent of
+  // the q_a/kv_a stage (bf16, rounding point R1); the unit of head group 0
+  // also appends it to the cache. Thread p owns the value pair (2p, 2p + 1):
+  // its gains or rotation are static and loaded before the wait.
+  const bool has_cur = pos >= t0 && pos < t1;
+  const int npairs = kvr / 2;  // <= kPreThreads
+  const int p = threadIdx.x;
+  const bool own = has_cur && p < npairs;
+  const bool is_lat = 2 * p < dc;
+  float ga = 0.f, gb = 0.f;  // gains (latent pairs) or (cos, sin) (rotary pairs)
+  if (own) {
+    if (is_lat) {
+      const float* gk = reinterpret_cast<const float*>(L.kv_norm) + 2 * p;
+      ga = gld(gk);
+      gb = gld(gk + 1);
+    } else {
+      const float* tab = reinterpret_cast<const float*>(c.P->rope_tab) + (size_t)pos * dr + 2 * (p - dc / 2);
+      ga = gld(tab);
+      gb = gld(tab + 1);
+    }
+  }
 
   // Cache rows of a block before pos were written by earlier steps: their
   // loads need no dependency, so the first block is issued before the wait
@@ -1155,40 +1251,88 @@ __device__ __forceinline__ bool stage_attn(const StageEnv& E, Smem& sm) {
   const int row0 = (int)threadIdx.x / q8n, col0 = (int)threadIdx.x - row0 * q8n;
   const int drow = kPreThreads / q8n, dcol = kPreThreads - drow * q8n;
   if (t0 < t1) issue_block(t0);
-  if (!wait_stage(c, sm, E.st.wait, E.s)) return false;
+  // wait for the q_b workgroups that produced this head group's queries
+  const int gran = c.P->qb_gran, qrows = d.n_heads * qkh;
+  const int wlo = split_owner(qrows, gran, c.G, grp * hg * qkh);
+  const int whi = split_owner(qrows, gran, c.G, (grp + 1) * hg * qkh - 1);
+  if (!wait_flags(c, sm, E.st.wait, wlo, whi, E.s)) return false;
 
   // LDS: query hi/lo [16][qstr] bf16, cache rows [64][kstr] u32, two score
-  // partials [2][16][pstr] f32, per-head max / sum / rescale
+  // partials [2][16][pstr] f32; at the end of the staging area the per-head
+  // max / sum / rescale and the new cache row [kvr / 2] u32
   __bf16* qh = reinterpret_cast<__bf16*>(sm.x);
   __bf16* ql = qh + kMH * qstr;
   uint32_t* kvs = reinterpret_cast<uint32_t*>(ql + kMH * qstr);
   float* sp = reinterpret_cast<float*>(kvs + kAttnBlock * kstr);
-  float* hm = sp + 2 * kMH * pstr;  // running max per head
-  float* hl = hm + kMH;             // running sum per head
-  float* ha = hl + kMH;             // rescale of the accumulators this round
+  uint32_t* crow = reinterpret_cast<uint32_t*>(sm.x + kXMax) - npairs;
+  float* hm = reinterpret_cast<float*>(crow) - 3 * kMH;  // running max per head
+  float* hl = hm + kMH;                                   // running sum per head
+  float* ha = hl + kMH;                                   // rescale of the accumulators this round
 
   {
-    // The polling wave, which has no cache-row loads queued ahead of it,
-    // copies the head group's attention-ready queries (scaled, split into
-    // bf16 high and residual rows by their producers) straight into LDS;
-    // rows of heads >= hg are zero.
-    const uint16_t* qa = reinterpret_cast<const uint16_t*>(L.ql) + (size_t)grp * 2 * kMH * qstr;
-    const int rbytes = hg * qstr * 2;
+    // All waves copy the head group's q_lat partials, the polling wave (no
+    // cache-row loads queued ahead of it) the rotary queries and (for the
+    // unit holding pos) the key/value latent, into the space the cache rows
+    // use later. Then the queries are assembled: latent columns = tau * the
+    // sum of the head's partials in slot order, split into bf16 high and
+    // residual parts; rotary columns as stored; rows of heads >= hg zero.
+    const int maxp = c.P->qb_maxparts;
+    float* tpart = reinterpret_cast<float*>(kvs);                    // [hg][maxp][dc]
+    uint32_t* trope = reinterpret_cast<uint32_t*>(tpart + hg * maxp * dc + 256);  // [2][hg][dr / 2]
+    float* tkv = reinterpret_cast<float*>(trope + hg * dr + 256);    // [kvr]
+    const float* raw = reinterpret_cast<const float*>(L.qkv_raw);
+    if ((int)threadIdx.x < hg) sm.ired[threadIdx.x] = qb_parts(d, gran, c.G, grp * hg + threadIdx.x);
+    dma_to_lds_wg(tpart, reinterpret_cast<const float*>(L.qlat_part) + (size_t)grp * hg * maxp * dc, hg * maxp * dc * 4);
     if (wave_id() == kPollWave) {
-      if (hg == kMH) {
-        dma_to_lds(qh, qa, 2 * rbytes);
-      } else {
-        dma_to_lds(qh, qa, rbytes);
-        dma_to_lds(ql, qa + kMH * qstr, rbytes);
-      }
-      mem_done();
+      dma_to_lds(trope, reinterpret_cast<const uint16_t*>(L.qrope) + (size_t)grp * 2 * hg * dr, 2 * hg * dr * 2);
+      if (has_cur) dma_to_lds(tkv, raw + d.q_lora, kvr * 4);
     }
+    mem_done();
     __syncthreads();
+    const float tau = 1.0f / sqrtf((float)qkh);
+    const int lgdc = 31 - __builtin_clz(dc);
+    for (int i = threadIdx.x; i < hg * dc; i += kThreads) {
+      const int hh = i >> lgdc, col = i & (dc - 1);
+      const int np = sm.ired[hh];
+      const float* pp = tpart + (size_t)hh * maxp * dc + col;
+      float sum = 0.f;
+      for (int k = 0; k < np; ++k) sum += pp[k * dc];
+      __bf16 hi, lo;
+      split_bf16(sum * tau, hi, lo);
+      qh[hh * qstr + col] = hi;
+      ql[hh * qstr + col] = lo;
+    }
+    for (int i = threadIdx.x; i < hg * (dr / 2); i += kThreads) {
+      const int hh = i / (dr / 2), cp = i - hh * (dr / 2);
+      reinterpret_cast<uint32_t*>(qh + hh * qstr + dc)[cp] = trope[i];
+      reinterpret_cast<uint32_t*>(ql + hh * qstr + dc)[cp] = trope[hg * (dr / 2) + i];
+    }
     for (int i = threadIdx.x; i < (kMH - hg) * qstr; i += kThreads) {
       qh[hg * qstr + i] = (__bf16)0.f;
       ql[hg * qstr + i] = (__bf16)0.f;
     }
     if (threadIdx.x < kMH) { hm[threadIdx.x] = -INFINITY; hl[threadIdx.x] = 0.f; }
+    if (has_cur) {
+      // every wave forms the latent's sum of squares itself (no barrier)
+      float ss = 0.f;
+      for (int k = lane_id(); k < dc; k += 64) ss += tkv[k] * tkv[k];
+      const float rsk = 1.0f / sqrtf(wave_sum(ss) / (float)dc + d.rms_eps);
+      if (own) {
+        const float x0 = tkv[2 * p], x1 = tkv[2 * p + 1];
+        float a, b;
+        if (is_lat) {
+          a = x0 * rsk * ga;
+          b = x1 * rsk * gb;
+        } else {
+          a = x0 * ga - x1 * gb;
+          b = x0 * gb + x1 * ga;
+        }
+        const uint32_t pr = (uint32_t)bf16_bits(a) | ((uint32_t)bf16_bits(b) << 16);
+        crow[p] = pr;
+        if (grp == 0)
+          st_coh_u(reinterpret_cast<uint32_t*>(const_cast<uint16_t*>(cache) + (size_t)pos * kvr) + p, pr);
+      }
+    }
     mark(c, sm, 0);
   }
 
@@ -1206,9 +1350,6 @@ __device__ __forceinline__ bool stage_attn(const StageEnv& E, Smem& sm) {
     {
       const int nmain = max(0, min(nb, pos - tb)) * q8n;
       const bool cur_here = pos >= tb && pos < tb + nb;
-      uint32_t cv = 0;
-      if (cur_here && threadIdx.x < kvr / 2)
-        cv = ld_coh_u(reinterpret_cast<const uint32_t*>(cache + (size_t)pos * kvr) + threadIdx.x);
       __syncthreads();  // the previous round's readers are done with kvs and sp
       int row = row0, col = col0;
 #pragma unroll
@@ -1224,7 +1365,7 @@ __device__ __forceinline__ bool stage_attn(const StageEnv& E, Smem& sm) {
       }
       if (tb + kAttnBlock < t1) issue_block(tb + kAttnBlock);
       __syncthreads();
-      if (cur_here && threadIdx.x < kvr / 2) kvs[(pos - tb) * kstr + threadIdx.x] = cv;
+      if (cur_here && threadIdx.x < kvr / 2) kvs[(pos - tb) * kstr + threadIdx.x] = crow[threadIdx.x];
       __syncthreads();
     }
     // ---- scores: waves 0-3 take position tiles 0-3 over the first half of
@@ -1337,21 +1478,21 @@ __device__ __forceinline__ bool stage_uv(const StageEnv& E, Smem& sm) {
   float* out = reinterpret_cast<float*>(L.o);
   return run_gemv<1, 0>(E, sm, g, ra, rb, true,
       [&]() {
-        if (!wait_stage(c, sm, E.st.wait, E.s)) return false;
+        // wait for the attention units of this workgroup's heads only
         const int h0 = ra / d.v_head, h1 = (rb - 1) / d.v_head;
+        const int hg = c.P->hg;
+        if (ra >= rb) return wait_flags(c, sm, -1, 0, -1, E.s);
+        if (!wait_flags(c, sm, E.st.wait, h0 / hg * nch, (h1 / hg + 1) * nch - 1, E.s)) return false;
         const int lane = lane_id();
         const int hbytes = nch * (dc + 2) * 4;  // partials of one head
         if (h0 == h1 && (hbytes & 15) == 0 && 4096 + hbytes + 1024 <= kXMax * 4) {
-          // One head: the polling wave (no weight loads queued ahead of it)
-          // copies its partials into LDS with coherent DMA; thread k then
-          // merges latent column k from LDS (chunk i's maximum and sum in
-          // lane i of every wave).
+          // One head: all waves copy its partials into LDS with coherent
+          // DMA; thread k then merges latent column k from LDS (chunk i's
+          // maximum and sum in lane i of every wave).
           const float* ph = part + (size_t)h0 * nch * (dc + 2);
           float* pr = sm.x + 1024;
-          if (wave_id() == kPollWave) {
-            dma_to_lds(pr, ph, hbytes);
-            mem_done();
-          }
+          dma_to_lds_wg(pr, ph, hbytes);
+          mem_done();
           __syncthreads();
           const bool lane_ch = lane < nch;
           const float m = lane_ch ? pr[lane * (dc + 2) + dc] : -INFINITY;
@@ -1724,7 +1865,7 @@ __device__ __forceinline__ bool stage_lm(const StageEnv& E, Smem& sm) {
     mem_done();
     int* done = counter_ptr(c, c.P->n_stages, 0);
     int old = __hip_atomic_fetch_add(gpw(done), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    sm.last = old == (int)c.A.epoch * c.G - 1;
+    sm.last = (uint32_t)old == c.A.epoch * (uint32_t)c.G - 1u;
   }
   __syncthreads();
   if (sm.last && threadIdx.x < 64) {
@@ -1768,12 +1909,12 @@ __global__ void __launch_bounds__(kThreads, 1) engine_kernel(const Plan* __restr
   const int n = c.P->n_stages;
   const int dpl = c.P->dims.kv_lora / 64;
   for (int s = 0; s < n; ++s) {
+    if (c.A.trace && threadIdx.x == 0) sm.t_entry = wall_clock64();
     StageEnv E{c, load_plan(&c.P->stages[s]), s};
     bool ok;
     switch (E.st.type) {
       case PDM_ST_QKV: ok = stage_qkv(E, sm); break;
       case PDM_ST_QB: ok = stage_qb(E, sm); break;
-      case PDM_ST_ABSORB: ok = stage_absorb(E, sm); break;
       case PDM_ST_ATTN:
         ok = dpl == 8 ? stage_attn<4>(E, sm) : dpl == 4 ? stage_attn<2>(E, sm) : stage_attn<1>(E, sm);
         break;
@@ -1812,7 +1953,7 @@ __global__ void rope_table_kernel(float* tab, int max_ctx, int rope, double base
 // Offline packer: logical FP8 matrix (codes [N][K], scales [ceil(N/128)][ceil(K/128)])
 // into a packed matrix (codes [rows][Kp], scales [rows/8][nkb]) by a row/column map.
 //   mode 0: packed row r = logical row (r - row0) for r in [row0, row0 + N), same columns
-//   mode 1 (W_UK transpose): packed row (h, c), column n  <- logical (h*(dn+dv) + n, c)
+//   mode 1 (W_UK extract):   packed row (h, n), column c  <- logical (h*(dn+dv) + n, c)
 //   mode 2 (W_UV extract):   packed row (h, v), column c  <- logical (h*(dn+dv) + dn + v, c)
 //   mode 3 (gate/up interleave): packed row 16*i + j (j < 8) <- gate row 8*i + j (a0 = 0),
 //                                packed row 16*i + 8 + j     <- up row 8*i + j (a0 = 1)
@@ -1823,8 +1964,8 @@ __device__ __forceinline__ bool pack_src(const PackMap& m, int r, int k, int& sr
       if (r < m.row0 || r >= m.row0 + m.N) return false;
       sr = r - m.row0; sc = k; return true;
     case 1: {
-      int h = r / m.dc, cc = r % m.dc;
-      sr = h * (m.dn + m.dv) + k; sc = cc; return true;
+      int h = r / m.dn, n = r % m.dn;
+      sr = h * (m.dn + m.dv) + n; sc = k; return true;
     }
     case 2: {
       int h = r / m.dv, v = r % m.dv;

@@ -11,6 +11,13 @@
 
 #include "../../include/pdm.h"
 
+// Functions shared by the host planner and the device code.
+#if defined(__HIPCC__)
+#define PDM_HD __host__ __device__
+#else
+#define PDM_HD
+#endif
+
 namespace pdm {
 
 constexpr int kThreads = 512;         // 8 waves of 64 lanes per workgroup
@@ -47,7 +54,7 @@ struct LayerPlan {
   uint64_t attn_norm, q_norm, kv_norm, ffn_norm;  // f32 gains
   Fp8Mat qkv;    // [W_DQ ; W_DKV]                     rows d_q + d_c + d_r, K = D
   Fp8Mat qb;     // W_UQ                               rows H*(d_n+d_r),     K = d_q
-  Fp8Mat ukT;    // W_UK transposed per head [h][c][n] rows H*d_c,           K = d_n
+  Fp8Mat uk;     // W_UK per head [h][n][c]            rows H*d_n,           K = d_c
   Fp8Mat uv;     // W_UV per head [h][v][c]            rows H*d_v,           K = d_c
   Fp8Mat wo;     // W_O                                rows D,               K = H*d_v
   Fp8Mat gu;     // dense gate/up, 8-row interleaved   rows 2F,              K = D
@@ -61,8 +68,8 @@ struct LayerPlan {
   uint64_t kv;
   // activations (scratch), f32 unless noted
   uint64_t qkv_raw;    // [d_q + d_c + d_r]
-  uint64_t q;          // [H][d_n + d_r], rotary part rotated
-  uint64_t ql;         // attention-ready queries: bf16 [n_hg][high, residual][kHeadGroup][d_c + d_r + 8]
+  uint64_t qlat_part;  // [H][qb_maxparts][d_c]: per-workgroup partials of W_UK[h]^T q_nope[h]
+  uint64_t qrope;      // bf16 [n_hg][high, residual][hg][d_r]: rotated rotary queries * tau
   uint64_t attn_part;  // [H][chunks][d_c + 2]: acc, max, sum (chunks <= nch, chosen per step)
   uint64_t o;          // [H * d_v]
   uint64_t xa;         // [D] residual after attention
@@ -95,10 +102,12 @@ struct Plan {
   int32_t nch;        // most attention position chunks per head group (the count is chosen per step)
   int32_t hg;         // heads per attention unit
   int32_t n_hg;       // head groups
-  int32_t pad[2];
+  int32_t qb_gran;    // row-split granularity of the q_b stage
+  int32_t qb_maxparts;  // most q_b workgroups holding query rows of one head
   uint64_t embed, final_norm, lm_head;  // arena
   uint64_t rope_tab;                    // scratch: f32 [max_ctx][rope/2][2] (cos, sin)
   uint64_t counters;                    // scratch: int [n_stages + 1][kStripes][kCounterStride]
+  uint64_t flags;                       // scratch: u32 [n_stages][G] epoch of each workgroup's last finished stage
   uint64_t status;                      // scratch: u64
   uint64_t lm_best;                     // scratch: [G] x {f32 value, i32 index}
   uint64_t logits_internal;             // scratch: f32 [vocab]
@@ -122,6 +131,42 @@ void stage_info(const Plan& p, int s, pdm_stage_info* out);
 uint64_t dims_hash(const pdm_dims& d);
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Balanced contiguous share of `rows` (whole groups of `gran` rows) for
+// workgroup wg of G: rows [ra, rb). Requires (rows / gran) * G < 2^31.
+PDM_HD inline void split_rows(int rows, int gran, int G, int wg, int& ra, int& rb) {
+  const int ng = rows / gran;
+  ra = ng * wg / G * gran;
+  rb = ng * (wg + 1) / G * gran;
+}
+// The workgroup whose share (split_rows) holds row r, 0 <= r < rows.
+// floor(ng * w / G) <= r / gran < floor(ng * (w + 1) / G) solves to
+// w = ceil((r / gran + 1) * G / ng) - 1.
+PDM_HD inline int split_owner(int rows, int gran, int G, int r) {
+  const int ng = rows / gran, g = r / gran;
+  return ((g + 1) * G + ng - 1) / ng - 1;
+}
+
+// The q_b stage splits the rows of W_UQ ([head][d_n nope ; d_r rotary]) over
+// the workgroups; each workgroup also multiplies the nope rows it produced by
+// the matching rows of W_UK. Partial `slot` of head h comes from workgroup
+// qb_first(h) + slot; there are qb_parts(h) of them.
+PDM_HD inline int qb_first(const pdm_dims& d, int gran, int G, int h) {
+  return split_owner(d.n_heads * (d.qk_nope + d.rope), gran, G, h * (d.qk_nope + d.rope));
+}
+PDM_HD inline int qb_parts(const pdm_dims& d, int gran, int G, int h) {
+  const int rows = d.n_heads * (d.qk_nope + d.rope);
+  return split_owner(rows, gran, G, h * (d.qk_nope + d.rope) + d.qk_nope - 1) - qb_first(d, gran, G, h) + 1;
+}
+// W_UK rows [u0, u1) (row h * d_n + n) whose q_nope values q_b rows [ra, rb) produce.
+PDM_HD inline void qb_nope_rows(const pdm_dims& d, int ra, int rb, int& u0, int& u1) {
+  const int qkh = d.qk_nope + d.rope;
+  if (ra >= rb) { u0 = u1 = 0; return; }
+  const int ha = ra / qkh, ja = ra - ha * qkh, hb = (rb - 1) / qkh, jb = rb - 1 - hb * qkh;
+  u0 = ha * d.qk_nope + (ja < d.qk_nope ? ja : d.qk_nope);
+  u1 = hb * d.qk_nope + (jb + 1 < d.qk_nope ? jb + 1 : d.qk_nope);
+  if (u1 < u0) u1 = u0;
+}
 inline uint64_t align_up(uint64_t v, uint64_t a) { return (v + a - 1) / a * a; }
 inline bool is_pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
 inline int ilog2(int64_t v) { int r = 0; while ((int64_t(1) << r) < v) ++r; return r; }

@@ -92,24 +92,52 @@ int build_plan(const pdm_dims& d, int32_t max_ctx, int32_t G, Plan* p, Layout* l
   const int H = d.n_heads, D = d.hidden, qkh = d.qk_nope + d.rope, kvr = d.kv_lora + d.rope;
   p->hg = (H % kHeadGroup == 0) ? kHeadGroup : 8;
   p->n_hg = H / p->hg;
+  // every head group needs at least one attention unit (one workgroup)
+  if (p->n_hg > G) return PDM_ERR_CONFIG;
   {
-    int by_wg = std::max(1, G / p->n_hg);
+    int by_wg = G / p->n_hg;
     int by_ctx = (int)std::max<int64_t>(1, ceil_div(max_ctx, 16));
     p->nch = std::min(by_wg, by_ctx);
   }
   p->nch = std::min(p->nch, kMaxChunks);
-  // attention LDS: query hi/lo rows [16][kvr + 8] bf16, 64 staged cache rows
-  // [64][kvr / 2 + 4] u32, two score partials [2][16][68] f32, 48 head scalars
   if (kvr % 32 != 0 || p->hg > 16) return PDM_ERR_CONFIG;
-  if (2LL * 16 * (kvr + 8) * 2 + 64LL * (kvr / 2 + 4) * 4 + 2LL * 16 * 68 * 4 + 48 * 4 > (int64_t)kXMax * 4)
-    return PDM_ERR_CONFIG;
-  // every packed 8-row x 128-column scale tile of W_UK^T and W_UV must lie in one logical block
+  // q_b row split and the number of q_lat partials per head
+  p->qb_gran = std::max(2, unit_rows(d.q_lora, 1));
+  if (((int64_t)H * qkh / p->qb_gran) * G >= (1LL << 31)) return PDM_ERR_CONFIG;
+  p->qb_maxparts = 1;
+  for (int h = 0; h < H; ++h) p->qb_maxparts = std::max(p->qb_maxparts, qb_parts(d, p->qb_gran, G, h));
+  {
+    // q_b LDS: staged c_q, the workgroup's q_nope values, its W_UK rows and
+    // their scales (each DMA'd with 1 KB of slack), the absorb reduction
+    int64_t most = 0;
+    for (int w = 0; w < G; ++w) {
+      int ra, rb, u0, u1;
+      split_rows(H * qkh, p->qb_gran, G, w, ra, rb);
+      qb_nope_rows(d, ra, rb, u0, u1);
+      most = std::max<int64_t>(most, u1 - u0);
+    }
+    const int64_t bytes = align_up(d.q_lora, 1024) * 4 + align_up(most, 4) * 4 + most * d.kv_lora + 1024 +
+                          (most / 8 + 2) * (d.kv_lora / 128) * 2 + 32 + 1024 + (int64_t)kThreads * 16 * 4;
+    if (bytes > (int64_t)kXMax * 4) return PDM_ERR_CONFIG;
+  }
+  {
+    // attention LDS: query hi/lo rows [16][kvr + 8] bf16, 64 staged cache
+    // rows [64][kvr / 2 + 4] u32, two score partials [2][16][68] f32, 48 head
+    // scalars, the current cache row [kvr / 2] u32. Before the first block is
+    // staged, the space after the queries holds the DMA'd q_lat partials,
+    // rotary queries and key/value latent (each with 1 KB of slack).
+    const int64_t qbytes = 2LL * 16 * (kvr + 8) * 2;
+    const int64_t end = (int64_t)kXMax * 4 - kvr * 2 - 48 * 4;  // head scalars and the new row at the end
+    if (qbytes + 64LL * (kvr / 2 + 4) * 4 + 2LL * 16 * 68 * 4 > end) return PDM_ERR_CONFIG;
+    const int64_t tmp = (int64_t)p->hg * p->qb_maxparts * d.kv_lora * 4 + 1024 + 2LL * p->hg * d.rope * 2 + 1024 +
+                        (int64_t)kvr * 4 + 1024;
+    if (qbytes + tmp > end) return PDM_ERR_CONFIG;
+  }
+  // every packed 8-row x 128-column scale tile of W_UK and W_UV must lie in one logical block
   for (int h = 0; h < H; ++h) {
     const int base = h * (d.qk_nope + d.v_head);
-    for (int k0 = 0; k0 < d.qk_nope; k0 += 128) {
-      int last = std::min(k0 + 127, d.qk_nope - 1);
-      if ((base + k0) / 128 != (base + last) / 128) return PDM_ERR_CONFIG;
-    }
+    for (int n0 = 0; n0 < d.qk_nope; n0 += 8)
+      if ((base + n0) / 128 != (base + n0 + 7) / 128) return PDM_ERR_CONFIG;
     for (int v0 = 0; v0 < d.v_head; v0 += 8)
       if ((base + d.qk_nope + v0) / 128 != (base + d.qk_nope + v0 + 7) / 128) return PDM_ERR_CONFIG;
   }
@@ -131,7 +159,7 @@ int build_plan(const pdm_dims& d, int32_t max_ctx, int32_t G, Plan* p, Layout* l
     L.ffn_norm = w.take((uint64_t)D * 4);
     L.qkv = fp8_mat(w, d.q_lora + kvr, D);
     L.qb = fp8_mat(w, H * qkh, d.q_lora);
-    L.ukT = fp8_mat(w, H * d.kv_lora, d.qk_nope);
+    L.uk = fp8_mat(w, H * d.qk_nope, d.kv_lora);
     L.uv = fp8_mat(w, H * d.v_head, d.kv_lora);
     L.wo = fp8_mat(w, D, H * d.v_head);
     if (!L.is_moe) {
@@ -164,9 +192,10 @@ int build_plan(const pdm_dims& d, int32_t max_ctx, int32_t G, Plan* p, Layout* l
   for (int l = 0; l < d.n_layers; ++l) {
     const LayerPlan& L = p->layers[l];
     int s_qkv = add(PDM_ST_QKV, l, last, L.qkv.rows, D, unit_rows(D, 1));
-    int s_qb = add(PDM_ST_QB, l, s_qkv, L.qb.rows, d.q_lora, std::max(2, unit_rows(d.q_lora, 1)));
-    int s_abs = add(PDM_ST_ABSORB, l, s_qb, L.ukT.rows, d.qk_nope, unit_rows(d.qk_nope, 1));
-    int s_att = add(PDM_ST_ATTN, l, s_abs, p->n_hg * p->nch, kvr, 1);
+    int s_qb = add(PDM_ST_QB, l, s_qkv, L.qb.rows, d.q_lora, p->qb_gran);
+    // attention units wait only for the q_b workgroups of their head group,
+    // W_UV workgroups only for the attention units of their heads
+    int s_att = add(PDM_ST_ATTN, l, s_qb, p->n_hg * p->nch, kvr, 1);
     int s_uv = add(PDM_ST_UV, l, s_att, L.uv.rows, d.kv_lora, unit_rows(d.kv_lora, 1));
     int s_wo = add(PDM_ST_WO, l, s_uv, D, H * d.v_head, unit_rows(H * d.v_head, 1));
     if (!L.is_moe) {
@@ -190,7 +219,7 @@ int build_plan(const pdm_dims& d, int32_t max_ctx, int32_t G, Plan* p, Layout* l
   // per-workgroup staged-input limit for the per-head GEMVs
   for (int s = 0; s < ns; ++s) {
     const StagePlan& st = p->stages[s];
-    int rpv = st.type == PDM_ST_ABSORB ? d.kv_lora : st.type == PDM_ST_UV ? d.v_head : 0;
+    int rpv = st.type == PDM_ST_UV ? d.v_head : 0;
     if (!rpv) continue;
     int64_t ng = st.rows / st.gran;
     int64_t per = ceil_div(ng, G) * st.gran;
@@ -204,6 +233,7 @@ int build_plan(const pdm_dims& d, int32_t max_ctx, int32_t G, Plan* p, Layout* l
   lay->plan_off = s.take(sizeof(Plan));
   p->rope_tab = s.take((uint64_t)max_ctx * (d.rope / 2) * 2 * 4);
   p->counters = s.take((uint64_t)(ns + 1) * kStripes * kCounterStride * 4);
+  p->flags = s.take((uint64_t)ns * G * 4);
   p->status = s.take(256);
   p->lm_best = s.take((uint64_t)G * 8);
   p->logits_internal = s.take((uint64_t)std::max(d.vocab, 1) * 4);
@@ -221,8 +251,8 @@ int build_plan(const pdm_dims& d, int32_t max_ctx, int32_t G, Plan* p, Layout* l
     L.topk_idx = ti_all + (uint64_t)l * kk * 4;
     L.topk_w = tw_all + (uint64_t)l * kk * 4;
     L.qkv_raw = s.take((uint64_t)L.qkv.rows * 4);
-    L.q = s.take((uint64_t)H * qkh * 4);
-    L.ql = s.take((uint64_t)p->n_hg * 2 * kHeadGroup * (kvr + 8) * 2);
+    L.qlat_part = s.take((uint64_t)H * p->qb_maxparts * d.kv_lora * 4);
+    L.qrope = s.take((uint64_t)p->n_hg * 2 * p->hg * d.rope * 2);
     L.attn_part = s.take((uint64_t)H * p->nch * (d.kv_lora + 2) * 4);
     L.o = s.take((uint64_t)H * d.v_head * 4);
     int64_t act = L.is_moe ? (int64_t)(d.top_k + d.n_shared) * d.moe_ffn : d.ffn;
@@ -261,14 +291,12 @@ void stage_info(const Plan& p, int s, pdm_stage_info* o) {
       o->reads[0] = input(); o->writes[0] = id(PDM_BUF_QKV, l);
       o->weight_bytes = fp8b(L.qkv) + (uint64_t)d.hidden * 4; break;
     case PDM_ST_QB:
-      o->reads[0] = id(PDM_BUF_QKV, l); o->writes[0] = id(PDM_BUF_Q, l); o->writes[1] = id(PDM_BUF_KV, l);
-      o->weight_bytes = fp8b(L.qb) + (uint64_t)(d.q_lora + d.kv_lora) * 4; break;
-    case PDM_ST_ABSORB:
-      o->reads[0] = id(PDM_BUF_Q, l); o->writes[0] = id(PDM_BUF_QLAT, l);
-      o->weight_bytes = fp8b(L.ukT); break;
+      o->reads[0] = id(PDM_BUF_QKV, l); o->writes[0] = id(PDM_BUF_QLAT, l);
+      o->weight_bytes = fp8b(L.qb) + fp8b(L.uk) + (uint64_t)d.q_lora * 4; break;
     case PDM_ST_ATTN:
-      o->reads[0] = id(PDM_BUF_QLAT, l); o->reads[1] = id(PDM_BUF_Q, l); o->reads[2] = id(PDM_BUF_KV, l);
-      o->writes[0] = id(PDM_BUF_ATTN, l); break;
+      o->reads[0] = id(PDM_BUF_QLAT, l); o->reads[1] = id(PDM_BUF_QKV, l); o->reads[2] = id(PDM_BUF_KV, l);
+      o->writes[0] = id(PDM_BUF_ATTN, l); o->writes[1] = id(PDM_BUF_KV, l);
+      o->weight_bytes = (uint64_t)d.kv_lora * 4; break;
     case PDM_ST_UV:
       o->reads[0] = id(PDM_BUF_ATTN, l); o->writes[0] = id(PDM_BUF_O, l);
       o->weight_bytes = fp8b(L.uv); break;

@@ -54,6 +54,27 @@ def teacher_forced(W, state, cfg, pos0, n_steps, seed=0, max_attempts=40, x_inpu
     return steps
 
 
+def bf16_ulps(got, want) -> np.ndarray:
+    """Distance in bf16 steps between two arrays of bf16 values (given as
+    floats): both are mapped to their 16-bit patterns, ordered so that
+    consecutive bf16 numbers are consecutive integers (+0 and -0 coincide)."""
+    def key(v):
+        v = np.asarray(v, dtype=np.float64)
+        assert np.array_equal(O.bf16_round(v), v), "values must be bf16 values"
+        b = (v.astype(np.float32).view(np.uint32) >> 16).astype(np.int64)
+        return np.where(b & 0x8000, -(b & 0x7FFF), b)
+    return np.abs(key(got) - key(want))
+
+
+def assert_bf16_rows_match(got, want, what=""):
+    """Cache rows are bf16 on both sides (rounding point R1); an element may
+    differ by one bf16 step where the fp32 value before rounding lies within
+    summation-order noise of a rounding boundary, never by more."""
+    d = bf16_ulps(got, want)
+    assert d.max() <= 1, (what, int(d.max()), int((d > 1).sum()))
+    return int((d == 1).sum())
+
+
 def cache_rows_bf16(state, layer, n):
     """The oracle's first n cache rows of a layer as bf16 bit patterns (int16 tensor)."""
     import torch

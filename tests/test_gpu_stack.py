@@ -1,18 +1,23 @@
 """GPU parity of the whole decode stack at full DeepSeek-V3 size: 3 dense + 8
 MoE MLA layers, final norm and the bf16 LM head over 129,280 tokens, in the
 benchmark's launch configuration (engine sized for prompt + 1024 decode steps,
-one persistent launch of one workgroup per CU per step).
+one persistent launch of one workgroup per CU per step, the same seeded
+teacher-forced token stream as the benchmark).
 
-The oracle runs one step at that size per case (about a minute of float64 CPU
-work) and is checked two ways:
+The engine runs every one of the workload's 1024 decode steps on its own
+appended cache (the prompt positions hold N(0, 1) bf16 latents: an oracle
+prefill of 1024 or 8192 tokens through 94 GB of experts is far beyond a CPU
+test; the bytes a step reads are the same). At sampled steps the oracle,
+given the engine's cache as it stands (every row the engine appended in the
+earlier steps included), checks the step two ways:
   * chained: the oracle's own step from the same token and cache, compared
     with every per-layer output, the logits and the argmax of the engine;
   * isolated: each oracle layer fed the engine's own input to that layer (and
     each FFN the engine's post-attention residual), so a per-layer error
     cannot hide behind the tolerance of the chain.
-The prompt cache holds N(0, 1) bf16 latents (the oracle prefill of 1024 or
-8192 tokens through 94 GB of experts is far beyond a CPU test); the bytes the
-step reads are the same.
+The new cache row of every layer is compared element by element (equal, or
+one bf16 step apart). One oracle step at this size is about 15-20 s of
+float64 CPU work.
 """
 import numpy as np
 import pytest
@@ -21,7 +26,7 @@ import torch
 import oracle as O
 from synth import configs, gen
 
-from parity_util import MARGIN, REL_TOL, rel_l2
+from parity_util import MARGIN, REL_TOL, bf16_ulps, rel_l2
 
 pytestmark = pytest.mark.gpu
 
@@ -33,11 +38,8 @@ def _gap(z, k):
     return float(s[k - 1] - s[k])
 
 
-def _engine_step(eng, cfg, lat, pos, tok):
-    eng.reset()
-    for l in range(cfg.n_layers):
-        eng.import_kv(l, 0, lat[l])
-    eng.decode(pos, token=tok)
+def _engine_outputs(eng, cfg, pos):
+    """Taps, logits, argmax and the new cache rows of the step just run at pos."""
     rc, st = eng.status()
     assert rc == 0, f"engine status {rc} at stage {st.stage}"
     t = eng.taps()
@@ -75,12 +77,12 @@ def _check_step(store, cfg, base_state, pos, tok, g):
             "attn_delta": rel_l2(g["hidden_attn"][l] - x_i, xa_i - x_i),
             "ffn": rel_l2(g["hidden"][l], xo_i),
             "chain": rel_l2(g["hidden"][l], x_c),
-            "kv_row": rel_l2(g["kv"][l], st_i.cache[l][pos]),
+            "kv_ulps": int(bf16_ulps(g["kv"][l], st_i.cache[l][pos]).max()),
         }
         report.append((l, e))
         print(f"layer {l}: " + " ".join(f"{k} {v:.2e}" for k, v in e.items()), flush=True)
         assert e["attn"] < REL_TOL and e["attn_delta"] < REL_TOL, (l, e)
-        assert e["ffn"] < REL_TOL and e["kv_row"] < REL_TOL, (l, e)
+        assert e["ffn"] < REL_TOL and e["kv_ulps"] <= 1, (l, e)
         assert e["chain"] < REL_TOL, (l, e)
         if cfg.layers[l] == "moe":
             k = cfg.top_k
@@ -107,33 +109,45 @@ def _check_step(store, cfg, base_state, pos, tok, g):
     return margin
 
 
-@pytest.mark.timeout(900)
-@pytest.mark.parametrize("name,where", [("dsv3_stack_1k", "first"), ("dsv3_stack_8k", "last")])
-def test_stack_fullsize(name, where):
+def _oracle_base(eng, cfg, pos):
+    """Oracle decode state holding the engine's cache rows [0, pos) of every layer."""
+    base = O.DecodeState.empty(cfg, pos + 1)
+    for l in range(cfg.n_layers):
+        rows = eng.export_kv(l, 0, pos).cpu().numpy().view(np.uint16)
+        base.cache[l][:pos] = O.bf16_bits_to_f64(rows)
+    base.length = pos
+    return base
+
+
+@pytest.mark.timeout(1100)
+@pytest.mark.parametrize("name,checked", [("dsv3_stack_1k", (0, 255, 1023)), ("dsv3_stack_8k", (0, 1023))])
+def test_stack_fullsize_own_cache(name, checked):
     from persistent_decode_megakernel_amd import Engine
     cfg = configs.get(name)
     P = cfg.prompt_len
-    max_ctx = P + cfg.decode_steps
-    pos = P if where == "first" else max_ctx - 1
+    K = cfg.decode_steps
+    max_ctx = P + K
     eng = Engine(cfg, max_ctx=max_ctx, device=0)
     try:
         assert eng.sizes.n_workgroups == torch.cuda.get_device_properties(0).multi_processor_count
         store = gen.LogicalWeights(cfg, SEED, "cuda", cache=False)
         eng.load_weights(store)
-        base = O.DecodeState.empty(cfg, pos + 1)
-        lat = []
+        eng.reset()
         for l in range(cfg.n_layers):
-            rows = gen.latent_rows(cfg, l, pos, SEED, device="cuda")
-            base.cache[l][:pos] = O.bf16_bits_to_f64(rows.cpu().numpy().view(np.uint16))
-            lat.append(rows)
-        base.length = pos
-        for attempt in range(4):
-            tok = gen.decode_token(cfg, pos - P, attempt, SEED)
-            g = _engine_step(eng, cfg, lat, pos, tok)
-            if _check_step(store, cfg, base, pos, tok, g) > MARGIN:
-                break
-        else:
-            pytest.fail(f"no token with router and logit margins above {MARGIN}")
+            eng.import_kv(l, 0, gen.latent_rows(cfg, l, P, SEED, device="cuda"))
+        margins = {}
+        for j in range(K):
+            tok = gen.decode_token(cfg, j, 0, SEED)
+            eng.decode(P + j, token=tok)
+            if j in checked:
+                pos = P + j
+                print(f"{name}: checking step {j} (position {pos}, token {tok})", flush=True)
+                g = _engine_outputs(eng, cfg, pos)
+                margins[j] = _check_step(store, cfg, _oracle_base(eng, cfg, pos), pos, tok, g)
+        rc, st = eng.status()
+        assert rc == 0, f"engine status {rc} at stage {st.stage}"
+        assert eng.cache_length() == max_ctx
+        print(f"{name}: decision margins at the checked steps {margins}", flush=True)
     finally:
         eng.close()
         del eng

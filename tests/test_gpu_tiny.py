@@ -8,7 +8,7 @@ import torch
 import oracle as O
 from synth import configs, gen
 
-from parity_util import REL_TOL, cache_rows_bf16, rel_l2, teacher_forced
+from parity_util import REL_TOL, assert_bf16_rows_match, cache_rows_bf16, rel_l2, teacher_forced
 
 pytestmark = pytest.mark.gpu
 
@@ -73,8 +73,8 @@ def test_tiny_cache_rows_match_oracle(tiny_case):
     for l in range(cfg.n_layers):
         got = eng.export_kv(l, P, 8).view(torch.bfloat16).float().cpu().numpy().astype(np.float64)
         want = st.cache[l][P:P + 8]
-        # a bf16 row may differ by one ulp where fp32 rounding crosses a tie
-        assert rel_l2(got, want) < 1e-2, l
+        n1 = assert_bf16_rows_match(got, want, f"layer {l}")
+        print(f"layer {l}: {n1} of {got.size} cache values one bf16 step apart")
 
 
 def test_tiny_from_empty_cache(tiny_case):
@@ -176,4 +176,5 @@ def test_trace_records(tiny_case):
         m = tr[:, :, i]
         has = m != 0
         assert (m[has] >= tr[:, :, 1][has]).all() and (m[has] <= tr[:, :, 2][has]).all()
-    assert (tr[:, :, 7] == 0).all()
+    # stage entry precedes the dependency wait
+    assert (tr[:, :, 7] > 0).all() and (tr[:, :, 7] <= tr[:, :, 0]).all()

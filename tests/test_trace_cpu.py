@@ -10,11 +10,11 @@ def _records():
     # 2 stages x 2 workgroups; ticks of 10 ns (100 MHz)
     plan = [{"type": "qkv", "layer": 0, "weight_bytes": 1000}, {"type": "attn", "layer": 0, "weight_bytes": 0}]
     tr = np.zeros((2, 2, 8), dtype=np.int64)
-    #            enter ready done  epoch staged consumed epi
-    tr[0, 0] = [100, 200, 1100, 1, 300, 900, 1000, 0]
-    tr[0, 1] = [100, 300, 1300, 1, 400, 1100, 1200, 0]
-    tr[1, 0] = [1200, 1400, 2000, 1, 1500, 1800, 1900, 0]
-    tr[1, 1] = [1400, 1500, 2100, 1, 0, 0, 0, 0]  # a workgroup without marks
+    #            enter ready done  epoch staged consumed epi  entry
+    tr[0, 0] = [100, 200, 1100, 1, 300, 900, 1000, 60]
+    tr[0, 1] = [100, 300, 1300, 1, 400, 1100, 1200, 80]
+    tr[1, 0] = [1200, 1400, 2000, 1, 1500, 1800, 1900, 1150]
+    tr[1, 1] = [1400, 1500, 2100, 1, 0, 0, 0, 1350]  # a workgroup without marks
     return tr, plan
 
 
@@ -32,12 +32,13 @@ def test_summary_spans_and_idle():
 def test_phases():
     tr, plan = _records()
     ph = T.phases(tr, plan)
+    assert ph[0]["setup"] == pytest.approx((0.3, 0.4))
     assert ph[0]["wait"] == pytest.approx((1.5, 2.0))
     assert ph[0]["stage_in"] == pytest.approx((1.0, 1.0))
     assert ph[0]["stream"] == pytest.approx((6.5, 7.0))
     assert ph[0]["epi"] == pytest.approx((1.0, 1.0))
     assert ph[0]["ack"] == pytest.approx((1.0, 1.0))
-    assert ph[0]["gap"] == pytest.approx((1.0, 1.0))
+    assert ph[0]["gap"] == pytest.approx((0.5, 0.5))  # signalled -> next stage entered
     # stage 1: only workgroup 0 carries marks
     assert ph[1]["stream"] == pytest.approx((3.0, 3.0))
     assert ph[1]["gap"] is None
