@@ -1281,7 +1281,20 @@ __device__ __forceinline__ bool stage_attn(const StageEnv& E, Smem& sm) {
     uint32_t* trope = reinterpret_cast<uint32_t*>(tpart + hg * maxp * dc + 256);  // [2][hg][dr / 2]
     float* tkv = reinterpret_cast<float*>(trope + hg * dr + 256);    // [kvr]
     const float* raw = reinterpret_cast<const float*>(L.qkv_raw);
-    if ((int)threadIdx.x < hg) sm.ired[threadIdx.x] = qb_parts(d, gran, c.G, grp * hg + threadIdx.x);
+    // slot k of head h holds a partial only if workgroup qb_first(h) + k
+    // owns rows (with fewer row groups than workgroups some own none)
+    uint64_t* qmask = reinterpret_cast<uint64_t*>(&sm.part[0][0]);
+    if ((int)threadIdx.x < hg) {
+      const int h = grp * hg + threadIdx.x, ng = qrows / gran;
+      const int first = qb_first(d, gran, c.G, h), np = qb_parts(d, gran, c.G, h);
+      uint64_t m = 0;
+      for (int k = 0; k < np; ++k) {
+        const int w = first + k;
+        if (ng * (w + 1) / c.G != ng * w / c.G) m |= 1ull << k;
+      }
+      sm.ired[threadIdx.x] = np;
+      qmask[threadIdx.x] = m;
+    }
     dma_to_lds_wg(tpart, reinterpret_cast<const float*>(L.qlat_part) + (size_t)grp * hg * maxp * dc, hg * maxp * dc * 4);
     if (wave_id() == kPollWave) {
       dma_to_lds(trope, reinterpret_cast<const uint16_t*>(L.qrope) + (size_t)grp * 2 * hg * dr, 2 * hg * dr * 2);
@@ -1294,9 +1307,11 @@ __device__ __forceinline__ bool stage_attn(const StageEnv& E, Smem& sm) {
     for (int i = threadIdx.x; i < hg * dc; i += kThreads) {
       const int hh = i >> lgdc, col = i & (dc - 1);
       const int np = sm.ired[hh];
+      const uint64_t m = qmask[hh];
       const float* pp = tpart + (size_t)hh * maxp * dc + col;
       float sum = 0.f;
-      for (int k = 0; k < np; ++k) sum += pp[k * dc];
+      for (int k = 0; k < np; ++k)
+        if ((m >> k) & 1) sum += pp[k * dc];
       __bf16 hi, lo;
       split_bf16(sum * tau, hi, lo);
       qh[hh * qstr + col] = hi;

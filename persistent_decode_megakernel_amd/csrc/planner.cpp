@@ -106,6 +106,7 @@ int build_plan(const pdm_dims& d, int32_t max_ctx, int32_t G, Plan* p, Layout* l
   if (((int64_t)H * qkh / p->qb_gran) * G >= (1LL << 31)) return PDM_ERR_CONFIG;
   p->qb_maxparts = 1;
   for (int h = 0; h < H; ++h) p->qb_maxparts = std::max(p->qb_maxparts, qb_parts(d, p->qb_gran, G, h));
+  if (p->qb_maxparts > 64) return PDM_ERR_CONFIG;  // the attention stage keeps a 64-bit slot mask per head
   {
     // q_b LDS: staged c_q, the workgroup's q_nope values, its W_UK rows and
     // their scales (each DMA'd with 1 KB of slack), the absorb reduction
@@ -244,20 +245,33 @@ int build_plan(const pdm_dims& d, int32_t max_ctx, int32_t G, Plan* p, Layout* l
   const int kk = std::max(d.top_k, 1);
   const uint64_t ti_all = s.take((uint64_t)d.n_layers * kk * 4);
   const uint64_t tw_all = s.take((uint64_t)d.n_layers * kk * 4);
+  // Working activations are shared by all layers: a layer's buffers are
+  // written again only after full barriers that every reader of the previous
+  // layer has passed (the next q_a/kv_a stage waits for all workgroups' last
+  // stage, the W_O stage for all W_UV workgroups).
+  int64_t act = 1;
+  for (int l = 0; l < d.n_layers; ++l)
+    act = std::max<int64_t>(act, d.layer_moe[l] ? (int64_t)(d.top_k + d.n_shared) * d.moe_ffn : d.ffn);
+  const uint64_t qkv_raw = s.take((uint64_t)(d.q_lora + kvr) * 4);
+  const uint64_t qlat_part = s.take((uint64_t)H * p->qb_maxparts * d.kv_lora * 4);
+  const uint64_t qrope = s.take((uint64_t)p->n_hg * 2 * p->hg * d.rope * 2);
+  const uint64_t attn_part = s.take((uint64_t)H * p->nch * (d.kv_lora + 2) * 4);
+  const uint64_t o = s.take((uint64_t)H * d.v_head * 4);
+  const uint64_t act_buf = s.take((uint64_t)act * 4);
+  const uint64_t router_logits = s.take((uint64_t)std::max(d.n_experts, 1) * 4);
   for (int l = 0; l < d.n_layers; ++l) {
     LayerPlan& L = p->layers[l];
     L.xo = xo_all + (uint64_t)l * D * 4;
     L.xa = xa_all + (uint64_t)l * D * 4;
     L.topk_idx = ti_all + (uint64_t)l * kk * 4;
     L.topk_w = tw_all + (uint64_t)l * kk * 4;
-    L.qkv_raw = s.take((uint64_t)L.qkv.rows * 4);
-    L.qlat_part = s.take((uint64_t)H * p->qb_maxparts * d.kv_lora * 4);
-    L.qrope = s.take((uint64_t)p->n_hg * 2 * p->hg * d.rope * 2);
-    L.attn_part = s.take((uint64_t)H * p->nch * (d.kv_lora + 2) * 4);
-    L.o = s.take((uint64_t)H * d.v_head * 4);
-    int64_t act = L.is_moe ? (int64_t)(d.top_k + d.n_shared) * d.moe_ffn : d.ffn;
-    L.act = s.take((uint64_t)act * 4);
-    L.router_logits = s.take((uint64_t)std::max(d.n_experts, 1) * 4);
+    L.qkv_raw = qkv_raw;
+    L.qlat_part = qlat_part;
+    L.qrope = qrope;
+    L.attn_part = attn_part;
+    L.o = o;
+    L.act = act_buf;
+    L.router_logits = router_logits;
   }
   lay->scratch_bytes = align_up(s.off, 256);
   lay->trace_bytes = (uint64_t)ns * G * kTraceWords * 8;

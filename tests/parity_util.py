@@ -66,12 +66,26 @@ def bf16_ulps(got, want) -> np.ndarray:
     return np.abs(key(got) - key(want))
 
 
+ROW_ATOL = 1e-4     # absolute slack of a bf16 cache value, in units of its row's rms
+
+
 def assert_bf16_rows_match(got, want, what=""):
-    """Cache rows are bf16 on both sides (rounding point R1); an element may
+    """Cache rows are bf16 on both sides (rounding point R1). An element may
     differ by one bf16 step where the fp32 value before rounding lies within
-    summation-order noise of a rounding boundary, never by more."""
+    summation-order noise of a rounding boundary. Near zero one bf16 step is
+    smaller than that noise itself (an fp32 dot product of ~10^3 terms against
+    the float64 one: ~10^-6 of the row's scale), so there the elements must
+    instead agree to ROW_ATOL times the row's rms. Returns the number of
+    elements one step apart."""
+    got = np.asarray(got, dtype=np.float64)
+    want = np.asarray(want, dtype=np.float64)
     d = bf16_ulps(got, want)
-    assert d.max() <= 1, (what, int(d.max()), int((d > 1).sum()))
+    rms = np.sqrt(np.mean(want * want, axis=-1, keepdims=True))
+    bad = (d > 1) & (np.abs(got - want) > ROW_ATOL * rms)
+    if bad.any():
+        i = np.argwhere(bad)[:4]
+        raise AssertionError((what, int(bad.sum()), [(tuple(int(x) for x in ix), float(got[tuple(ix)]),
+                                                      float(want[tuple(ix)]), int(d[tuple(ix)])) for ix in i]))
     return int((d == 1).sum())
 
 
@@ -81,3 +95,34 @@ def cache_rows_bf16(state, layer, n):
     vals = state.cache[layer][:n]
     assert np.array_equal(O.bf16_round(vals), vals), "cache rows must be bf16 values"
     return torch.from_numpy(vals.astype(np.float32)).to(torch.bfloat16).view(torch.int16)
+
+
+def poison_scratch(eng):
+    """Fill the part of an engine's scratch buffer that every step must write
+    before reading (logits, step-input tap, layer taps and all working
+    activations: everything from the internal logits buffer on) with 0xFF
+    bytes, a NaN pattern, so that a read of a value no stage wrote this step
+    shows up in the results instead of reading zeros."""
+    import ctypes as C
+    from persistent_decode_megakernel_amd import _lib as L
+    t = L.Taps()
+    L.check("pdm_get_taps", eng.lib.pdm_get_taps(eng.h, C.byref(t)))
+    off = t.logits_dev - eng.scratch.data_ptr()
+    assert 0 < off < eng.scratch.numel()
+    eng.scratch[off:].fill_(0xFF)
+
+
+def isolated_cache_rows(W, cfg, pos, x0, hidden, caches):
+    """The oracle's new cache row of every layer at position pos, each layer
+    fed the engine's own input to it (x0 for layer 0, the engine's output of
+    the layer before otherwise) and the engine's own cache rows [0, pos), so
+    that only summation order separates the two sides."""
+    out = []
+    for l in range(cfg.n_layers):
+        st = O.DecodeState.empty(cfg, pos + 1)
+        st.cache[l][:pos] = caches[l][:pos]
+        st.length = pos
+        x_in = x0 if l == 0 else np.asarray(hidden[l - 1], dtype=np.float64)
+        O.attention_decode(W, cfg, l, x_in, pos, st, True)
+        out.append(st.cache[l][pos].copy())
+    return out

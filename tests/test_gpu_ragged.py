@@ -13,7 +13,8 @@ import torch
 import oracle as O
 from synth import configs, gen
 
-from parity_util import REL_TOL, assert_bf16_rows_match, cache_rows_bf16, rel_l2, teacher_forced
+from parity_util import (REL_TOL, assert_bf16_rows_match, cache_rows_bf16, isolated_cache_rows, poison_scratch,
+                         rel_l2, teacher_forced)
 
 pytestmark = pytest.mark.gpu
 
@@ -43,6 +44,8 @@ def test_ragged_teacher_forced_parity(ragged_case):
     worst = {"logits": 0.0, "hidden": 0.0}
     for j, (tok, ref) in enumerate(steps):
         print(f"ragged step {j} position {P + j}", flush=True)
+        if j % 2 == 1:
+            poison_scratch(eng)  # every value a step reads must be written in that step
         am, lg = eng.decode(P + j, token=tok)
         rc, st = eng.status()
         assert rc == 0, (j, st.code, st.stage)
@@ -68,18 +71,20 @@ def test_ragged_teacher_forced_parity(ragged_case):
 
 
 def test_ragged_cache_rows_match_oracle(ragged_case):
+    """Every appended cache row against the oracle's row for the same layer
+    input (isolated per layer), element by element."""
     cfg, W, st0, steps, eng = ragged_case
     P = cfg.prompt_len
     eng.reset()
     for l in range(cfg.n_layers):
         eng.import_kv(l, 0, cache_rows_bf16(st0, l, P).cuda())
-    st = st0.copy()
-    n = 6
-    for j, (tok, _) in enumerate(steps[:n]):
-        O.decode_step(W, st, P + j, token=tok)
-        eng.decode(P + j, token=tok)
-    torch.cuda.synchronize()
-    for l in range(cfg.n_layers):
-        got = eng.export_kv(l, P, n).view(torch.bfloat16).float().cpu().numpy().astype(np.float64)
-        want = st.cache[l][P:P + n]
-        assert_bf16_rows_match(got, want, f"layer {l}")
+    for j, (tok, _) in enumerate(steps[:6]):
+        pos = P + j
+        eng.decode(pos, token=tok)
+        assert eng.status()[0] == 0
+        hid = eng.taps()["hidden"].cpu().numpy()
+        caches = [eng.export_kv(l, 0, pos + 1).view(torch.bfloat16).float().cpu().numpy().astype(np.float64)
+                  for l in range(cfg.n_layers)]
+        want = isolated_cache_rows(W, cfg, pos, W.bf16_row("embed", tok), hid, caches)
+        for l in range(cfg.n_layers):
+            assert_bf16_rows_match(caches[l][pos], want[l], f"step {j} layer {l}")

@@ -26,7 +26,7 @@ import torch
 import oracle as O
 from synth import configs, gen
 
-from parity_util import MARGIN, REL_TOL, bf16_ulps, rel_l2
+from parity_util import MARGIN, REL_TOL, assert_bf16_rows_match, bf16_ulps, rel_l2
 
 pytestmark = pytest.mark.gpu
 
@@ -54,12 +54,20 @@ def _engine_outputs(eng, cfg, pos):
 
 def _check_step(store, cfg, base_state, pos, tok, g):
     """Oracle chained and isolated passes against the engine's step `g`.
-    Returns the smallest decision margin of the chained oracle step."""
+    The isolated checks are strict at every layer. The chained oracle feeds
+    its own (bf16-rounded) layer outputs forward, which can differ from the
+    engine's by one bf16 step per element; a router decision whose top-k gap
+    is within MARGIN may then pick another expert, after which the chain is
+    a different computation. The chained comparison therefore counts only
+    while every chained router decision so far had a gap above MARGIN and
+    chose the engine's experts. Returns the smallest decision margin of the
+    chained oracle step."""
     st_c, st_i = base_state.copy(), base_state.copy()
     W0 = O.OracleWeights(store, cache_limit_bytes=0)
     x_emb = W0.bf16_row("embed", tok)
     x_c = x_emb
     margin = np.inf
+    chain_ok = True
     report = []
     for l in range(cfg.n_layers):
         W = O.OracleWeights(store, cache_limit_bytes=12 << 30)
@@ -79,14 +87,22 @@ def _check_step(store, cfg, base_state, pos, tok, g):
             "chain": rel_l2(g["hidden"][l], x_c),
             "kv_ulps": int(bf16_ulps(g["kv"][l], st_i.cache[l][pos]).max()),
         }
+        assert_bf16_rows_match(g["kv"][l], st_i.cache[l][pos], f"layer {l} cache row")
         report.append((l, e))
         print(f"layer {l}: " + " ".join(f"{k} {v:.2e}" for k, v in e.items()), flush=True)
         assert e["attn"] < REL_TOL and e["attn_delta"] < REL_TOL, (l, e)
-        assert e["ffn"] < REL_TOL and e["kv_ulps"] <= 1, (l, e)
-        assert e["chain"] < REL_TOL, (l, e)
+        assert e["ffn"] < REL_TOL, (l, e)
         if cfg.layers[l] == "moe":
             k = cfg.top_k
-            margin = min(margin, _gap(tc["router_logits"][0], k))
+            gap_c = _gap(tc["router_logits"][0], k)
+            margin = min(margin, gap_c)
+            same = [int(i) for i in tc["router_idx"][0]] == [int(i) for i in g["router_idx"][l]]
+            chain_ok = chain_ok and gap_c > MARGIN and same
+        if chain_ok:
+            assert e["chain"] < REL_TOL, (l, e)
+        else:
+            print(f"layer {l}: chained comparison not counted (a chained router gap <= {MARGIN})", flush=True)
+        if cfg.layers[l] == "moe":
             z = ti["router_logits"][0]
             got = [int(i) for i in g["router_idx"][l]]
             if _gap(z, k) > MARGIN:
@@ -100,11 +116,13 @@ def _check_step(store, cfg, base_state, pos, tok, g):
     margin = min(margin, _gap(lg_c, 1))
     e_c, e_i = rel_l2(g["logits"], lg_c), rel_l2(g["logits"], lg_i)
     print(f"pos {pos} token {tok}: logits chained {e_c:.2e} isolated {e_i:.2e}", flush=True)
-    assert e_c < REL_TOL and e_i < REL_TOL, (e_c, e_i)
+    assert e_i < REL_TOL, e_i
+    if chain_ok:
+        assert e_c < REL_TOL, e_c
     assert g["argmax"] == int(np.argmax(g["logits"]))
     if _gap(lg_i, 1) > MARGIN:
         assert g["argmax"] == int(np.argmax(lg_i))
-    if margin > MARGIN:
+    if chain_ok and margin > MARGIN:
         assert g["argmax"] == int(np.argmax(lg_c))
     return margin
 

@@ -8,7 +8,8 @@ import torch
 import oracle as O
 from synth import configs, gen
 
-from parity_util import REL_TOL, assert_bf16_rows_match, cache_rows_bf16, rel_l2, teacher_forced
+from parity_util import (REL_TOL, assert_bf16_rows_match, cache_rows_bf16, isolated_cache_rows, poison_scratch,
+                         rel_l2, teacher_forced)
 
 pytestmark = pytest.mark.gpu
 
@@ -61,20 +62,43 @@ def test_tiny_teacher_forced_parity(tiny_case):
     print(f"worst rel err over {len(steps)} steps: {worst}")
 
 
-def test_tiny_cache_rows_match_oracle(tiny_case):
+def test_tiny_poisoned_scratch(tiny_case):
+    """Working buffers start as NaN bytes: every value a step reads is written
+    earlier in the same step, so the results still match the oracle."""
     cfg, store, W, st0, steps, eng = tiny_case
     P = cfg.prompt_len
     _import_prefill(eng, cfg, st0, P)
-    st = st0.copy()
+    for j, (tok, ref) in enumerate(steps[:6]):
+        poison_scratch(eng)
+        am, lg = eng.decode(P + j, token=tok)
+        assert eng.status()[0] == 0
+        got = lg.cpu().numpy()
+        assert np.isfinite(got).all(), j
+        assert rel_l2(got, ref["logits"]) < REL_TOL, j
+        assert int(am.item()) == ref["argmax"], j
+        hid = eng.taps()["hidden"].cpu().numpy()
+        for l in range(cfg.n_layers):
+            assert rel_l2(hid[l], ref["hidden"][l]) < REL_TOL, (j, l)
+
+
+def test_tiny_cache_rows_match_oracle(tiny_case):
+    """Every appended cache row against the oracle's row for the same layer
+    input (isolated per layer), element by element."""
+    cfg, store, W, st0, steps, eng = tiny_case
+    P = cfg.prompt_len
+    _import_prefill(eng, cfg, st0, P)
+    n1 = 0
     for j, (tok, _) in enumerate(steps[:8]):
-        O.decode_step(W, st, P + j, token=tok)
-        eng.decode(P + j, token=tok)
-    torch.cuda.synchronize()
-    for l in range(cfg.n_layers):
-        got = eng.export_kv(l, P, 8).view(torch.bfloat16).float().cpu().numpy().astype(np.float64)
-        want = st.cache[l][P:P + 8]
-        n1 = assert_bf16_rows_match(got, want, f"layer {l}")
-        print(f"layer {l}: {n1} of {got.size} cache values one bf16 step apart")
+        pos = P + j
+        eng.decode(pos, token=tok)
+        assert eng.status()[0] == 0
+        hid = eng.taps()["hidden"].cpu().numpy()
+        caches = [eng.export_kv(l, 0, pos + 1).view(torch.bfloat16).float().cpu().numpy().astype(np.float64)
+                  for l in range(cfg.n_layers)]
+        want = isolated_cache_rows(W, cfg, pos, W.bf16_row("embed", tok), hid, caches)
+        for l in range(cfg.n_layers):
+            n1 += assert_bf16_rows_match(caches[l][pos], want[l], f"step {j} layer {l}")
+    print(f"{n1} cache values one bf16 step apart over 8 steps")
 
 
 def test_tiny_from_empty_cache(tiny_case):

@@ -48,6 +48,16 @@ def test_row_match_accepts_one_step_and_rejects_two():
         assert_bf16_rows_match(got2, want)
     with pytest.raises(AssertionError):   # not bf16 values at all
         bf16_ulps(want + 1e-9, want)
+    # near zero several steps are allowed within the absolute slack, not beyond
+    z = want.copy()
+    z[3] = _bf16([3e-6])[0]
+    zg = z.copy()
+    zg[3] = _bf16([3e-6 + 5e-6])[0]           # many bf16 steps, 5e-6 of a unit-rms row
+    assert bf16_ulps(zg, z)[3] > 1
+    assert_bf16_rows_match(zg, z)
+    zg[3] = _bf16([3e-6 + 5e-3])[0]
+    with pytest.raises(AssertionError):
+        assert_bf16_rows_match(zg, z)
 
 
 def test_rel_l2():
