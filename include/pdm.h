@@ -42,6 +42,8 @@ extern "C" {
 typedef struct ihipStream_t* pdm_stream_t; /* a hipStream_t; 0 is the null stream */
 
 #define PDM_MAX_LAYERS 128
+/* Size of the library's static per-device scratch array (pdm_bind_static). */
+#define PDM_STATIC_SCRATCH_BYTES (32u << 20)
 #define PDM_ABI_VERSION 2
 
 /* Error codes */
@@ -205,6 +207,21 @@ int pdm_get_sizes(const pdm_engine* e, pdm_sizes* out);
  * (synchronously). Rebinding replaces the previous buffers. */
 int pdm_bind(pdm_engine* e, void* weights_dev, uint64_t weight_bytes, void* kv_dev, uint64_t kv_bytes,
              void* scratch_dev, uint64_t scratch_bytes, void* trace_dev, uint64_t trace_bytes);
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): as pdm_bind,
+ * but the scratch workspace (plan, counters, flags, activations, partials,
+ * taps) is the library's own static device array of PDM_STATIC_SCRATCH_BYTES
+ * on the engine's device, and no trace buffer is bound. Allocates nothing.
+ * Returns PDM_ERR_SIZE when the engine needs more scratch than the array
+ * holds (pdm_get_sizes), PDM_ERR_DEVICE when the array's address cannot be
+ * obtained. Every engine bound this way on one device shares that device's
+ * array, which keeps the last step's contents: binding another engine this
+ * way takes the array over (the earlier engine must be rebound before its
+ * next call), and calls of two such engines on one device race if they
+ * overlap. The counters, flags and status word are cleared here and by
+ * pdm_reset_cache, as for pdm_bind. */
+int pdm_bind_static(pdm_engine* e, void* weights_dev, uint64_t weight_bytes, void* kv_dev, uint64_t kv_bytes);
 
 /* Offline packer for one FP8 matrix: reads its logical form (row-major e4m3
  * codes [N, K] and bf16 block scales [ceil(N/128), ceil(K/128)], device

@@ -5,6 +5,7 @@ import ctypes as C
 import os
 
 MAX_LAYERS = 128
+STATIC_SCRATCH_BYTES = 32 << 20
 ABI_VERSION = 2
 
 LIB_DIR = os.path.join(os.path.dirname(os.path.abspath(__file__)), "_lib")
@@ -70,6 +71,7 @@ _SIGS = {
     "pdm_create": (C.c_int, [C.POINTER(Dims), C.c_int32, C.c_int, C.POINTER(_P)]),
     "pdm_get_sizes": (C.c_int, [_P, C.POINTER(Sizes)]),
     "pdm_bind": (C.c_int, [_P, _P, C.c_uint64, _P, C.c_uint64, _P, C.c_uint64, _P, C.c_uint64]),
+    "pdm_bind_static": (C.c_int, [_P, _P, C.c_uint64, _P, C.c_uint64]),
     "pdm_load_fp8": (C.c_int, [_P, C.c_int32, C.c_int32, C.c_int32, _P, _P, _P]),
     "pdm_load_raw": (C.c_int, [_P, C.c_int32, C.c_int32, C.c_int32, _P, C.c_uint64, _P]),
     "pdm_load_packed_weights": (C.c_int, [_P, _P, C.c_uint64, C.c_int, _P]),

@@ -105,6 +105,9 @@ int check_engine(const pdm_engine* e, bool need_bound) {
   return PDM_OK;
 }
 
+int bind_buffers(pdm_engine* e, void* weights_dev, uint64_t weight_bytes, void* kv_dev, uint64_t kv_bytes,
+                 void* scratch_dev, uint64_t scratch_bytes, void* trace_dev, uint64_t trace_bytes);
+
 }  // namespace
 
 extern "C" {
@@ -188,6 +191,24 @@ int pdm_get_sizes(const pdm_engine* e, pdm_sizes* out) {
 
 int pdm_bind(pdm_engine* e, void* weights_dev, uint64_t weight_bytes, void* kv_dev, uint64_t kv_bytes,
              void* scratch_dev, uint64_t scratch_bytes, void* trace_dev, uint64_t trace_bytes) {
+  return bind_buffers(e, weights_dev, weight_bytes, kv_dev, kv_bytes, scratch_dev, scratch_bytes, trace_dev,
+                      trace_bytes);
+}
+
+int pdm_bind_static(pdm_engine* e, void* weights_dev, uint64_t weight_bytes, void* kv_dev, uint64_t kv_bytes) {
+  if (!e) return PDM_ERR_ARG;
+  if (e->lay.scratch_bytes > PDM_STATIC_SCRATCH_BYTES) return PDM_ERR_SIZE;
+  void* ws = nullptr;
+  if (static_scratch(e->device, &ws) != hipSuccess || !ws) return PDM_ERR_DEVICE;
+  return bind_buffers(e, weights_dev, weight_bytes, kv_dev, kv_bytes, ws, PDM_STATIC_SCRATCH_BYTES, nullptr, 0);
+}
+
+}  // extern "C"
+
+namespace {
+
+int bind_buffers(pdm_engine* e, void* weights_dev, uint64_t weight_bytes, void* kv_dev, uint64_t kv_bytes,
+                 void* scratch_dev, uint64_t scratch_bytes, void* trace_dev, uint64_t trace_bytes) {
   if (!e || !weights_dev || !kv_dev || !scratch_dev) return PDM_ERR_ARG;
   if (!aligned(weights_dev) || !aligned(kv_dev) || !aligned(scratch_dev) || (trace_dev && !aligned(trace_dev)))
     return PDM_ERR_ALIGN;
@@ -222,6 +243,10 @@ int pdm_bind(pdm_engine* e, void* weights_dev, uint64_t weight_bytes, void* kv_d
   e->bound = true;
   return PDM_OK;
 }
+
+}  // namespace
+
+extern "C" {
 
 int pdm_load_fp8(pdm_engine* e, int32_t tensor, int32_t layer, int32_t expert, const uint8_t* codes_dev,
                  const uint16_t* scales_dev, pdm_stream_t stream) {

@@ -31,5 +31,8 @@ hipError_t launch_rope_table(float* tab, int max_ctx, int rope, double base, hip
 hipError_t launch_pack(const uint8_t* src_codes, const uint16_t* src_scales, uint8_t* dst_codes,
                        uint16_t* dst_scales, const PackMap& m, hipStream_t stream);
 hipError_t launch_zero(void* p, size_t bytes, hipStream_t stream);
+// Device address of the library's static scratch array on `device`
+// (PDM_STATIC_SCRATCH_BYTES), looked up once per device.
+hipError_t static_scratch(int device, void** ptr);
 
 }  // namespace pdm

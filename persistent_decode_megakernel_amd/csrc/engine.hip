@@ -24,6 +24,8 @@
 // a dense contraction, so MFMA is not used there.
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 #include "pdm_internal.h"
 #include "engine.h"
 
@@ -2020,6 +2022,34 @@ __global__ void pack_scales_kernel(const uint16_t* __restrict__ src, uint16_t* _
 }  // namespace pdm
 
 namespace pdm {
+
+// Scratch workspace for callers that cannot allocate device memory: one
+// static array per device the library runs on, held until the process ends.
+// Host code must not use its name as a device address; its address on a
+// device comes from hipGetSymbolAddress with that device current, taken once
+// per device and kept.
+static __device__ __align__(256) uint8_t scratch[PDM_STATIC_SCRATCH_BYTES];
+
+hipError_t static_scratch(int device, void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  if (device < 0 || device >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[device]) {
+    int prev = -1;
+    hipError_t e = hipGetDevice(&prev);
+    if (e != hipSuccess) return e;
+    if (prev != device && (e = hipSetDevice(device)) != hipSuccess) return e;
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (prev != device) (void)hipSetDevice(prev);
+    if (e != hipSuccess) return e;
+    addr[device] = p;
+  }
+  *ptr = addr[device];
+  return hipSuccess;
+}
 
 hipError_t launch_engine(const Plan* plan_dev, const LaunchArgs& a, int G, hipStream_t stream, bool cooperative) {
   if (cooperative) {

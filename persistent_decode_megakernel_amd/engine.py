@@ -21,7 +21,9 @@ def _ptr(t: Optional[torch.Tensor]):
 class Engine:
     """One decode engine bound to torch-allocated device buffers."""
 
-    def __init__(self, cfg, max_ctx: int, device: int = 0, trace: bool = False):
+    def __init__(self, cfg, max_ctx: int, device: int = 0, trace: bool = False, static_scratch: bool = False):
+        """static_scratch: bind with pdm_bind_static (the library's own scratch
+        array; no trace buffer, no taps views)."""
         self.lib = L.load()
         if not torch.cuda.is_available():
             raise RuntimeError("the decode engine needs a HIP GPU")
@@ -36,14 +38,23 @@ class Engine:
         L.check("pdm_get_sizes", self.lib.pdm_get_sizes(h, C.byref(s)))
         self.sizes = s
         u8 = torch.uint8
+        self.static_scratch = bool(static_scratch)
         self.weights = torch.empty(s.weight_bytes, dtype=u8, device=self.device)
         self.kv = torch.zeros(s.kv_bytes, dtype=u8, device=self.device)
-        self.scratch = torch.zeros(s.scratch_bytes, dtype=u8, device=self.device)
-        self.trace = torch.zeros(s.trace_bytes, dtype=u8, device=self.device) if trace else None
-        torch.cuda.synchronize(self.device)
-        L.check("pdm_bind", self.lib.pdm_bind(
-            h, _ptr(self.weights), s.weight_bytes, _ptr(self.kv), s.kv_bytes, _ptr(self.scratch),
-            s.scratch_bytes, _ptr(self.trace), s.trace_bytes if trace else 0))
+        if self.static_scratch:
+            if trace:
+                raise ValueError("an engine on the static scratch array has no trace buffer")
+            self.scratch = self.trace = None
+            torch.cuda.synchronize(self.device)
+            L.check("pdm_bind_static", self.lib.pdm_bind_static(
+                h, _ptr(self.weights), s.weight_bytes, _ptr(self.kv), s.kv_bytes))
+        else:
+            self.scratch = torch.zeros(s.scratch_bytes, dtype=u8, device=self.device)
+            self.trace = torch.zeros(s.trace_bytes, dtype=u8, device=self.device) if trace else None
+            torch.cuda.synchronize(self.device)
+            L.check("pdm_bind", self.lib.pdm_bind(
+                h, _ptr(self.weights), s.weight_bytes, _ptr(self.kv), s.kv_bytes, _ptr(self.scratch),
+                s.scratch_bytes, _ptr(self.trace), s.trace_bytes if trace else 0))
         self.logits = torch.empty(max(cfg.vocab, 1), dtype=torch.float32, device=self.device)
         self.argmax = torch.zeros(1, dtype=torch.int32, device=self.device)
 
@@ -132,6 +143,8 @@ class Engine:
 
     def taps(self) -> dict:
         """Views of the last step's taps inside the scratch buffer."""
+        if self.static_scratch:
+            raise RuntimeError("taps of an engine on the static scratch array are not viewable from torch")
         t = L.Taps()
         L.check("pdm_get_taps", self.lib.pdm_get_taps(self.h, C.byref(t)))
         base = self.scratch.data_ptr()
