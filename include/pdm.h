@@ -130,10 +130,10 @@ enum pdm_tensor {
 
 /* Device-side status of the last decode step (pdm_sync_status). */
 typedef struct pdm_status {
-  int32_t code;          /* PDM_OK or PDM_ERR_WATCHDOG */
+  int32_t code;          /* PDM_OK, PDM_ERR_WATCHDOG or PDM_ERR_TOKEN */
   int32_t stage;         /* stage whose wait timed out, -1 if none */
-  int32_t workgroup;     /* workgroup that timed out first */
-  int32_t observed;      /* counter value it observed */
+  int32_t workgroup;     /* workgroup that failed first */
+  int32_t observed;      /* counter value it observed, or the bad token */
   uint32_t epoch;        /* epoch of the step that set the status */
   int32_t pad[3];
 } pdm_status;
@@ -266,8 +266,26 @@ int pdm_export_kv(const pdm_engine* e, int32_t layer, int32_t pos0, int32_t n, u
 int pdm_decode_step(pdm_engine* e, int32_t token, int32_t pos, const uint16_t* x_in_dev,
                     float* logits_dev, int32_t* argmax_dev, pdm_stream_t stream);
 
-/* Synchronise `stream` and read the device status word. Returns PDM_OK or
- * PDM_ERR_WATCHDOG (details in *out, which may be null). */
+/* Enqueue n_steps decode steps as ONE persistent launch: the engine stays
+ * resident on the device for the whole request and the host launches once
+ * (SemiAnalysis TileRT page, how-it-works section). Step j runs at position
+ * pos0 + j (pos0 must equal the cache length, pos0 + n_steps <= max_ctx) and
+ * appends its cache row. tokens_dev: int32 device array of the steps' input
+ * tokens (teacher forcing: n_steps entries); with greedy != 0 only
+ * tokens_dev[0] is read and step j > 0 takes the argmax of step j - 1, fed
+ * back on the device. argmax_dev: int32 [n_steps] device output (required
+ * when greedy), the argmax of every step; logits_dev: optional f32 [vocab],
+ * the last step's logits. Configs without a vocabulary return PDM_ERR_TOKEN.
+ * A token outside [0, vocab) found in tokens_dev stops the launch:
+ * pdm_sync_status then reports PDM_ERR_TOKEN. Taps and trace records hold the
+ * last step. Asynchronous on `stream`. */
+int pdm_decode_steps(pdm_engine* e, int32_t pos0, int32_t n_steps, const int32_t* tokens_dev, int greedy,
+                     float* logits_dev, int32_t* argmax_dev, pdm_stream_t stream);
+
+/* Synchronise `stream` and read the device status word. Returns PDM_OK,
+ * PDM_ERR_WATCHDOG (a dependency wait exceeded its spin limit) or
+ * PDM_ERR_TOKEN (a bad token in a multi-step launch); details in *out, which
+ * may be null. */
 int pdm_sync_status(pdm_engine* e, pdm_stream_t stream, pdm_status* out);
 
 int pdm_get_taps(const pdm_engine* e, pdm_taps* out);

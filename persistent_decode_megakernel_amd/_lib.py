@@ -79,6 +79,7 @@ _SIGS = {
     "pdm_import_kv": (C.c_int, [_P, C.c_int32, C.c_int32, C.c_int32, _P, _P]),
     "pdm_export_kv": (C.c_int, [_P, C.c_int32, C.c_int32, C.c_int32, _P, _P]),
     "pdm_decode_step": (C.c_int, [_P, C.c_int32, C.c_int32, _P, _P, _P, _P]),
+    "pdm_decode_steps": (C.c_int, [_P, C.c_int32, C.c_int32, _P, C.c_int, _P, _P, _P]),
     "pdm_sync_status": (C.c_int, [_P, _P, C.POINTER(Status)]),
     "pdm_get_taps": (C.c_int, [_P, C.POINTER(Taps)]),
     "pdm_cache_length": (C.c_int, [_P, C.POINTER(C.c_int32)]),

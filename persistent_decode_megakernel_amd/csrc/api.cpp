@@ -415,6 +415,7 @@ int pdm_decode_step(pdm_engine* e, int32_t token, int32_t pos, const uint16_t* x
   a.pos = pos;
   a.spin_limit = e->spin_limit > 0 ? e->spin_limit : kDefaultSpin;
   a.skip_stage = e->skip_stage;
+  a.n_steps = 1;
   a.x_in = x_in_dev;
   a.logits = d.vocab > 0 ? logits_dev : nullptr;
   a.argmax = d.vocab > 0 ? argmax_dev : nullptr;
@@ -424,6 +425,36 @@ int pdm_decode_step(pdm_engine* e, int32_t token, int32_t pos, const uint16_t* x
   if (err != hipSuccess) return PDM_ERR_LAUNCH;
   e->epoch = a.epoch;
   for (int l = 0; l < d.n_layers; ++l) e->layer_len[l] = pos + 1;
+  return PDM_OK;
+}
+
+int pdm_decode_steps(pdm_engine* e, int32_t pos0, int32_t n_steps, const int32_t* tokens_dev, int greedy,
+                     float* logits_dev, int32_t* argmax_dev, pdm_stream_t stream) {
+  int rc = check_engine(e, true);
+  if (rc) return rc;
+  const pdm_dims& d = e->dims;
+  if (d.vocab <= 0 || !tokens_dev) return PDM_ERR_TOKEN;
+  if (n_steps < 1 || (greedy && !argmax_dev)) return PDM_ERR_ARG;
+  if (pos0 < 0) return PDM_ERR_POS;
+  if ((int64_t)pos0 + n_steps > e->max_ctx) return PDM_ERR_CTX;
+  for (int l = 0; l < d.n_layers; ++l)
+    if (e->layer_len[l] != pos0) return PDM_ERR_POS;
+  LaunchArgs a{};
+  a.epoch = e->epoch + 1;
+  a.pos = pos0;
+  a.spin_limit = e->spin_limit > 0 ? e->spin_limit : kDefaultSpin;
+  a.skip_stage = e->skip_stage;
+  a.n_steps = n_steps;
+  a.greedy = greedy ? 1 : 0;
+  a.tokens = tokens_dev;
+  a.logits = logits_dev;
+  a.argmax = argmax_dev;
+  a.trace = e->trace_on ? e->trace : nullptr;
+  DeviceGuard g(e->device);
+  hipError_t err = launch_engine(e->plan_dev, a, e->G, (hipStream_t)stream, e->cooperative);
+  if (err != hipSuccess) return PDM_ERR_LAUNCH;
+  e->epoch += (uint32_t)n_steps;
+  for (int l = 0; l < d.n_layers; ++l) e->layer_len[l] = pos0 + n_steps;
   return PDM_OK;
 }
 
@@ -444,7 +475,7 @@ int pdm_sync_status(pdm_engine* e, pdm_stream_t stream, pdm_status* out) {
   st.observed = code ? raw[6] : 0;
   st.epoch = ep;
   if (out) *out = st;
-  return code ? PDM_ERR_WATCHDOG : PDM_OK;
+  return code ? -(int32_t)code : PDM_OK;
 }
 
 int pdm_get_taps(const pdm_engine* e, pdm_taps* out) {

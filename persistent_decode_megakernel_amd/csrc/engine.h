@@ -8,17 +8,22 @@
 namespace pdm {
 
 // Per-step arguments of the persistent kernel (passed by value).
+// A launch runs n_steps decode steps; step j has epoch epoch + j and
+// position pos + j.
 struct LaunchArgs {
-  uint32_t epoch;        // step counter since bind; counters target epoch * arrivals
-  int32_t token;         // input token (configs with a vocabulary)
-  int32_t pos;           // position of the new token == cache length
+  uint32_t epoch;        // epoch of the first step (steps since bind); counters target epoch * arrivals
+  int32_t token;         // input token of a single step (tokens == null)
+  int32_t pos;           // position of the first step's token == cache length
   int32_t spin_limit;    // polls before a dependency wait gives up
   int32_t skip_stage;    // debug: workgroup 0 does not signal this stage (-1 none)
+  int32_t n_steps;       // decode steps in this launch (>= 1)
+  int32_t greedy;        // step j > 0 takes the argmax of step j - 1 as its token
   int32_t pad;
+  const int32_t* tokens; // tokens of the steps (step 0 only when greedy), or null
   const uint16_t* x_in;  // bf16 hidden input of a bare layer stack
-  float* logits;         // optional logits output
-  int32_t* argmax;       // optional argmax output
-  uint64_t* trace;       // optional trace records
+  float* logits;         // optional logits output (the last step's)
+  int32_t* argmax;       // optional argmax output, one per step
+  uint64_t* trace;       // optional trace records (the last step's)
 };
 
 // Row/column map of the offline packer (see engine.hip, pack_codes_kernel).

@@ -226,22 +226,29 @@ __device__ __forceinline__ float silu(float g) { return g / (1.0f + __expf(-g));
 
 struct Ctx {
   const GLOBAL_AS Plan* P;  // plan in global memory: uniform reads become scalar loads
-  LaunchArgs A;
+  LaunchArgs A;             // with the current step's epoch, position, token and outputs
+  uint32_t epoch0;          // epoch of the launch's first step
   int G;
   int wg;
 };
+
+// The status word holds (epoch << 32) | -code of the first failure; a
+// failure of any step of this launch (epoch >= epoch0) aborts every wait.
+__device__ __forceinline__ bool status_aborts(const Ctx& c, unsigned long long v) {
+  return (uint32_t)v != 0u && (int)((uint32_t)(v >> 32) - c.epoch0) >= 0;
+}
 
 __device__ __forceinline__ int* counter_ptr(const Ctx& c, int stage, int stripe) {
   return reinterpret_cast<int*>(c.P->counters) + ((size_t)stage * kStripes + stripe) * kCounterStride;
 }
 __device__ __forceinline__ int stripe_count(int G, int stripe) { return (G - stripe + kStripes - 1) / kStripes; }
 
-// Record a dependency-wait timeout in the status word (first one wins).
-// Scalar arguments only: a by-reference argument of a non-inlined call would
-// force the caller's structs into scratch memory.
-__device__ __noinline__ void set_watchdog(uint64_t status, uint32_t epoch, int wg, int stage, int observed) {
+// Record a failure (a dependency-wait timeout, or a bad token) in the status
+// word (first one wins). Scalar arguments only: a by-reference argument of a
+// non-inlined call would force the caller's structs into scratch memory.
+__device__ __noinline__ void set_status(uint64_t status, uint32_t epoch, int code, int wg, int stage, int observed) {
   GLOBAL_AS unsigned long long* st = (GLOBAL_AS unsigned long long*)status;
-  unsigned long long mine = ((unsigned long long)epoch << 32) | (unsigned)(-PDM_ERR_WATCHDOG);
+  unsigned long long mine = ((unsigned long long)epoch << 32) | (unsigned)(-code);
   unsigned long long cur = __hip_atomic_load(st, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   if ((uint32_t)(cur >> 32) != epoch || (uint32_t)cur == 0u) {
     if (__hip_atomic_compare_exchange_strong(st, &cur, mine, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
@@ -279,12 +286,12 @@ __device__ __forceinline__ bool wait_stage(const Ctx& c, Smem& sm, int s, int my
       bool abort = false;
       if (lane == kStripes) {
         unsigned long long v = __hip_atomic_load(st, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        abort = (uint32_t)(v >> 32) == c.A.epoch && (uint32_t)v != 0u;
+        abort = status_aborts(c, v);
       }
       if (__any(abort)) { if (lane == 0) sm.abort = 1; break; }
       if (__all(ok)) break;
       if (++spins > c.A.spin_limit) {
-        if (!ok) set_watchdog(c.P->status, c.A.epoch, c.wg, my_stage, seen);
+        if (!ok) set_status(c.P->status, c.A.epoch, PDM_ERR_WATCHDOG, c.wg, my_stage, seen);
         if (lane == 0) sm.abort = 1;
         break;
       }
@@ -328,11 +335,11 @@ __device__ __forceinline__ bool wait_flags(const Ctx& c, Smem& sm, int s, int w0
         const uint32_t x = ld_coh_u(f + i);
         if ((int)(x - c.A.epoch) < 0) { ok = false; seen = x; }
       }
-      const bool abort = lane == 0 && (uint32_t)(sv >> 32) == c.A.epoch && (uint32_t)sv != 0u;
+      const bool abort = lane == 0 && status_aborts(c, sv);
       if (__any(abort)) { if (lane == 0) sm.abort = 1; break; }
       if (__all(ok)) break;
       if (++spins > c.A.spin_limit) {
-        if (!ok) set_watchdog(c.P->status, c.A.epoch, c.wg, my_stage, (int)seen);
+        if (!ok) set_status(c.P->status, c.A.epoch, PDM_ERR_WATCHDOG, c.wg, my_stage, (int)seen);
         if (lane == 0) sm.abort = 1;
         break;
       }
@@ -1909,22 +1916,14 @@ __device__ __forceinline__ bool stage_lm(const StageEnv& E, Smem& sm) {
       int oi = __shfl_xor(bi, off);
       if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
     }
-    if (lane == 0 && c.A.argmax) gst(c.A.argmax, bi);
+    if (lane == 0 && c.A.argmax) st_coh_i(c.A.argmax, bi);  // read back by the next step in greedy mode
   }
   return true;
 }
 
-}  // namespace
-
-__global__ void __launch_bounds__(kThreads, 1) engine_kernel(const Plan* __restrict__ P, LaunchArgs A) {
-  __shared__ Smem sm;
-  Ctx c;
-  c.P = (const GLOBAL_AS Plan*)P;
-  c.A = A;
-  c.G = c.P->G;
-  c.wg = blockIdx.x;
-  const int n = c.P->n_stages;
-  const int dpl = c.P->dims.kv_lora / 64;
+// All stages of one decode step, in plan order. Returns false when the step
+// was aborted (every workgroup leaves at its next wait).
+__device__ __forceinline__ bool run_step(const Ctx& c, Smem& sm, int n, int dpl) {
   for (int s = 0; s < n; ++s) {
     if (c.A.trace && threadIdx.x == 0) sm.t_entry = wall_clock64();
     StageEnv E{c, load_plan(&c.P->stages[s]), s};
@@ -1944,11 +1943,54 @@ __global__ void __launch_bounds__(kThreads, 1) engine_kernel(const Plan* __restr
       case PDM_ST_LM: ok = stage_lm(E, sm); break;
       default: ok = false; break;
     }
-    if (!ok) {  // watchdog abort: every workgroup leaves at its next wait
+    if (!ok) {
       mem_done();
-      return;
+      return false;
     }
     signal_stage(c, sm, s);
+  }
+  return true;
+}
+
+}  // namespace
+
+
+// One launch runs A.n_steps decode steps, so the engine can stay resident
+// for a whole request (SemiAnalysis TileRT page, how-it-works section: the
+// host launches once and execution stays on the device for the decode
+// lifecycle). Step j > 0 starts once every workgroup has finished step j - 1
+// (the counters of its last stage); its token comes from the token array, or
+// in greedy mode is the argmax step j - 1 wrote.
+__global__ void __launch_bounds__(kThreads, 1) engine_kernel(const Plan* __restrict__ P, LaunchArgs A) {
+  __shared__ Smem sm;
+  Ctx c;
+  c.P = (const GLOBAL_AS Plan*)P;
+  c.A = A;
+  c.epoch0 = A.epoch;
+  c.G = c.P->G;
+  c.wg = blockIdx.x;
+  const int n = c.P->n_stages;
+  const int dpl = c.P->dims.kv_lora / 64;
+  const int vocab = c.P->dims.vocab;
+  for (int step = 0; step < A.n_steps; ++step) {
+    if (step > 0) {
+      c.A.epoch = A.epoch + step - 1;  // the previous step's last stage, everywhere
+      if (!wait_stage(c, sm, n - 1, n - 1)) return;
+    }
+    c.A.epoch = A.epoch + step;
+    c.A.pos = A.pos + step;
+    if (A.tokens) {
+      const int t = step > 0 && A.greedy ? ld_coh_i(A.argmax + step - 1) : gld(A.tokens + step);
+      c.A.token = __builtin_amdgcn_readfirstlane(t);
+    }
+    if (vocab > 0 && (c.A.token < 0 || c.A.token >= vocab)) {
+      // every workgroup sees the same token and leaves; workgroup 0 reports it
+      if (c.wg == 0 && threadIdx.x == 0) set_status(c.P->status, c.A.epoch, PDM_ERR_TOKEN, 0, -1, c.A.token);
+      return;
+    }
+    c.A.argmax = A.argmax ? A.argmax + step : nullptr;
+    c.A.logits = step + 1 == A.n_steps ? A.logits : nullptr;
+    if (!run_step(c, sm, n, dpl)) return;
   }
 }
 

@@ -125,6 +125,26 @@ class Engine:
         L.check("pdm_decode_step", rc)
         return am, lg
 
+    def decode_steps(self, pos0: int, tokens: torch.Tensor, n_steps: Optional[int] = None, greedy: bool = False,
+                     logits: Optional[torch.Tensor] = None, argmax: Optional[torch.Tensor] = None):
+        """Enqueue n_steps decode steps as one resident launch (asynchronous).
+        tokens: int32 device tensor (n_steps teacher-forced tokens, or the first
+        token when greedy). Returns the per-step argmax tensor and the last
+        step's logits (or None)."""
+        assert tokens.dtype == torch.int32 and tokens.is_cuda
+        n = int(n_steps if n_steps is not None else tokens.numel())
+        if not greedy:
+            assert tokens.numel() >= n
+        am = argmax if argmax is not None else torch.zeros(n, dtype=torch.int32, device=self.device)
+        L.check("pdm_decode_steps", self.lib.pdm_decode_steps(self.h, int(pos0), n, _ptr(tokens), 1 if greedy else 0,
+                                                              _ptr(logits), _ptr(am), self.stream))
+        return am, logits
+
+    def decode_steps_raw(self, pos0, tokens, n_steps, greedy=False, logits=None, argmax=None) -> int:
+        """Like decode_steps but returns the ABI code instead of raising."""
+        return self.lib.pdm_decode_steps(self.h, int(pos0), int(n_steps), _ptr(tokens), 1 if greedy else 0,
+                                         _ptr(logits), _ptr(argmax), self.stream)
+
     def decode_raw(self, pos, token=None, x_in=None, logits=None, argmax=None) -> int:
         """Like decode but returns the ABI code instead of raising."""
         return self.lib.pdm_decode_step(self.h, -1 if token is None else int(token), int(pos), _ptr(x_in),
