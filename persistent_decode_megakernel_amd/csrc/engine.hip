@@ -1169,7 +1169,7 @@ __device__ __forceinline__ bool stage_qb(const StageEnv& E, Smem& sm) {
 // per attention unit and at most the planned count (one unit per workgroup
 // when the context allows it), which also sizes the partial buffer. The
 // attention and W_UV stages derive the same count from the position.
-constexpr int kChunkPos = 16;
+constexpr int kChunkPos = 64;
 __device__ __forceinline__ int attn_chunks(const Ctx& c, int ctx) {
   return min(c.P->nch, max(1, (ctx + kChunkPos - 1) / kChunkPos));
 }
@@ -1290,20 +1290,11 @@ __device__ __forceinline__ bool stage_attn(const StageEnv& E, Smem& sm) {
     uint32_t* trope = reinterpret_cast<uint32_t*>(tpart + hg * maxp * dc + 256);  // [2][hg][dr / 2]
     float* tkv = reinterpret_cast<float*>(trope + hg * dr + 256);    // [kvr]
     const float* raw = reinterpret_cast<const float*>(L.qkv_raw);
-    // slot k of head h holds a partial only if workgroup qb_first(h) + k
-    // owns rows (with fewer row groups than workgroups some own none)
+    // slot k of head h holds a partial only if q_b workgroup qb_first(h) + k
+    // owns rows (with fewer row groups than workgroups some own none): the
+    // planner's per-head slot mask
     uint64_t* qmask = reinterpret_cast<uint64_t*>(&sm.part[0][0]);
-    if ((int)threadIdx.x < hg) {
-      const int h = grp * hg + threadIdx.x, ng = qrows / gran;
-      const int first = qb_first(d, gran, c.G, h), np = qb_parts(d, gran, c.G, h);
-      uint64_t m = 0;
-      for (int k = 0; k < np; ++k) {
-        const int w = first + k;
-        if (ng * (w + 1) / c.G != ng * w / c.G) m |= 1ull << k;
-      }
-      sm.ired[threadIdx.x] = np;
-      qmask[threadIdx.x] = m;
-    }
+    if ((int)threadIdx.x < hg) qmask[threadIdx.x] = gld(&c.P->qb_mask[grp * hg + threadIdx.x]);
     dma_to_lds_wg(tpart, reinterpret_cast<const float*>(L.qlat_part) + (size_t)grp * hg * maxp * dc, hg * maxp * dc * 4);
     if (wave_id() == kPollWave) {
       dma_to_lds(trope, reinterpret_cast<const uint16_t*>(L.qrope) + (size_t)grp * 2 * hg * dr, 2 * hg * dr * 2);
@@ -1313,18 +1304,27 @@ __device__ __forceinline__ bool stage_attn(const StageEnv& E, Smem& sm) {
     __syncthreads();
     const float tau = 1.0f / sqrtf((float)qkh);
     const int lgdc = 31 - __builtin_clz(dc);
-    for (int i = threadIdx.x; i < hg * dc; i += kThreads) {
-      const int hh = i >> lgdc, col = i & (dc - 1);
-      const int np = sm.ired[hh];
+    for (int i = threadIdx.x; i < hg * dc / 4; i += kThreads) {
+      const int hh = (4 * i) >> lgdc, col = (4 * i) & (dc - 1);
       const uint64_t m = qmask[hh];
-      const float* pp = tpart + (size_t)hh * maxp * dc + col;
-      float sum = 0.f;
-      for (int k = 0; k < np; ++k)
-        if ((m >> k) & 1) sum += pp[k * dc];
-      __bf16 hi, lo;
-      split_bf16(sum * tau, hi, lo);
-      qh[hh * qstr + col] = hi;
-      ql[hh * qstr + col] = lo;
+      const float4* pp = reinterpret_cast<const float4*>(tpart + (size_t)hh * maxp * dc + col);
+      float4 sum = make_float4(0.f, 0.f, 0.f, 0.f);
+      for (int k = 0; k < maxp; ++k)
+        if ((m >> k) & 1) {
+          const float4 v = pp[k * (dc / 4)];
+          sum.x += v.x; sum.y += v.y; sum.z += v.z; sum.w += v.w;
+        }
+      __bf16 h0, l0, h1, l1, h2, l2, h3, l3;
+      split_bf16(sum.x * tau, h0, l0);
+      split_bf16(sum.y * tau, h1, l1);
+      split_bf16(sum.z * tau, h2, l2);
+      split_bf16(sum.w * tau, h3, l3);
+      uint32_t* qh2 = reinterpret_cast<uint32_t*>(qh + hh * qstr + col);
+      uint32_t* ql2 = reinterpret_cast<uint32_t*>(ql + hh * qstr + col);
+      qh2[0] = pack_bf16x2(h0, h1);
+      qh2[1] = pack_bf16x2(h2, h3);
+      ql2[0] = pack_bf16x2(l0, l1);
+      ql2[1] = pack_bf16x2(l2, l3);
     }
     for (int i = threadIdx.x; i < hg * (dr / 2); i += kThreads) {
       const int hh = i / (dr / 2), cp = i - hh * (dr / 2);
@@ -1465,21 +1465,36 @@ __device__ __forceinline__ bool stage_attn(const StageEnv& E, Smem& sm) {
   }
   __syncthreads();
   mark(c, sm, 1);
-  // ---- partials: acc[i][r] = O[head 4*lg + r][dim (w*DTILES + i)*16 + lr]
-  float* part = reinterpret_cast<float*>(L.attn_part);
+  // ---- partials: acc[i][r] = O[head 4*lg + r][dim (w*DTILES + i)*16 + lr].
+  // A head's partial row is [acc (d_c) ; max ; sum ; 0 ; 0] (a 16-byte
+  // multiple); the rows are transposed through LDS (the cache-row space is
+  // free now) so that every lane stores whole 16-byte pieces.
+  const int ps = dc + 4;
+  float* tout = reinterpret_cast<float*>(kvs);
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int hh = 4 * lg + r;
-    if (hh < hg) {
-      float* dst = part + ((size_t)(grp * hg + hh) * nch + ch) * (dc + 2);
 #pragma unroll
-      for (int i = 0; i < DTILES; ++i) st_coh(dst + (w * DTILES + i) * 16 + lr, acc[i][r]);
-    }
+    for (int i = 0; i < DTILES; ++i) tout[hh * ps + (w * DTILES + i) * 16 + lr] = acc[i][r];
   }
-  if (threadIdx.x < hg) {
-    float* dst = part + ((size_t)(grp * hg + threadIdx.x) * nch + ch) * (dc + 2);
-    st_coh(dst + dc, hm[threadIdx.x]);
-    st_coh(dst + dc + 1, hl[threadIdx.x]);
+  if (threadIdx.x < kMH) {
+    float* t = tout + threadIdx.x * ps + dc;
+    t[0] = hm[threadIdx.x];
+    t[1] = hl[threadIdx.x];
+    t[2] = t[3] = 0.f;
+  }
+  __syncthreads();
+  {
+    float* part = reinterpret_cast<float*>(L.attn_part) + ((size_t)grp * hg * nch + ch) * ps;
+    const int p4 = ps / 4;  // 16-byte pieces per head row
+    const __amdgpu_buffer_rsrc_t rp = vec_rsrc(part, (hg - 1) * nch * ps + ps);
+    for (int q = threadIdx.x; q < hg * p4; q += kThreads) {
+      const int hh = q / p4, c4 = q - hh * p4;
+      const float4 v = *reinterpret_cast<const float4*>(tout + hh * ps + 4 * c4);
+      // head hh's row of this chunk lies hh * nch rows further on
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rp, ((hh * nch) * ps + 4 * c4) * 4, 0,
+                                             kCpolSc1);
+    }
   }
   mark(c, sm, 2);
   return true;
@@ -1508,26 +1523,27 @@ __device__ __forceinline__ bool stage_uv(const StageEnv& E, Smem& sm) {
         if (ra >= rb) return wait_flags(c, sm, -1, 0, -1, E.s);
         if (!wait_flags(c, sm, E.st.wait, h0 / hg * nch, (h1 / hg + 1) * nch - 1, E.s)) return false;
         const int lane = lane_id();
-        const int hbytes = nch * (dc + 2) * 4;  // partials of one head
+        const int ps = dc + 4;                   // partial row: acc, max, sum, padding
+        const int hbytes = nch * ps * 4;         // partials of one head
         if (h0 == h1 && (hbytes & 15) == 0 && 4096 + hbytes + 1024 <= kXMax * 4) {
           // One head: all waves copy its partials into LDS with coherent
           // DMA; thread k then merges latent column k from LDS (chunk i's
           // maximum and sum in lane i of every wave).
-          const float* ph = part + (size_t)h0 * nch * (dc + 2);
+          const float* ph = part + (size_t)h0 * nch * ps;
           float* pr = sm.x + 1024;
           dma_to_lds_wg(pr, ph, hbytes);
           mem_done();
           __syncthreads();
           const bool lane_ch = lane < nch;
-          const float m = lane_ch ? pr[lane * (dc + 2) + dc] : -INFINITY;
-          const float sv = lane_ch ? pr[lane * (dc + 2) + dc + 1] : 0.f;
+          const float m = lane_ch ? pr[lane * ps + dc] : -INFINITY;
+          const float sv = lane_ch ? pr[lane * ps + dc + 1] : 0.f;
           const float mx = wave_max(m);
           const float e = m == -INFINITY ? 0.f : __expf(m - mx);
           const float fac = e / wave_sum(e * sv);
           if ((int)threadIdx.x < dc) {
             float num = 0.f;
             for (int i = 0; i < nch; ++i)
-              num += pr[i * (dc + 2) + threadIdx.x] *
+              num += pr[i * ps + threadIdx.x] *
                      __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, fac), i));
             sm.x[xperm(threadIdx.x)] = num;
           }
@@ -1540,14 +1556,14 @@ __device__ __forceinline__ bool stage_uv(const StageEnv& E, Smem& sm) {
         const int k = min((int)threadIdx.x, dc - 1);
         const bool lane_ch = lane < nch;
         for (int h = h0; h <= h1; ++h) {
-          const float* ph = part + (size_t)h * nch * (dc + 2);
-          const float* pl = ph + (size_t)(lane_ch ? lane : 0) * (dc + 2) + dc;
+          const float* ph = part + (size_t)h * nch * ps;
+          const float* pl = ph + (size_t)(lane_ch ? lane : 0) * ps + dc;
           const float mi = ld_coh(pl), si = ld_coh(pl + 1);
           float fac = 0.f, num = 0.f;
           for (int i0 = 0; i0 < nch; i0 += kMergeBatch) {
             float v[kMergeBatch];
 #pragma unroll
-            for (int b = 0; b < kMergeBatch; ++b) v[b] = ld_coh(ph + (size_t)min(i0 + b, nch - 1) * (dc + 2) + k);
+            for (int b = 0; b < kMergeBatch; ++b) v[b] = ld_coh(ph + (size_t)min(i0 + b, nch - 1) * ps + k);
             if (i0 == 0) {
               const float m = lane_ch ? mi : -INFINITY;
               const float mx = wave_max(m);

@@ -30,6 +30,7 @@ constexpr int kMaxSlots = 16;         // expert slots of one MoE stage
 constexpr int kMaxStages = PDM_MAX_LAYERS * 12 + 4;
 constexpr int kHeadGroup = 16;        // attention heads per work unit (at most)
 constexpr int kMaxChunks = 64;        // attention position chunks per head (one per lane when merged)
+constexpr int kMaxHeads = 256;        // attention heads
 constexpr uint32_t kMagic = 0x57444d50u;  // "PDMW"
 constexpr int kHeaderBytes = 256;
 constexpr int kTraceWords = 8;        // u64 words per (stage, workgroup) trace record
@@ -70,7 +71,7 @@ struct LayerPlan {
   uint64_t qkv_raw;    // [d_q + d_c + d_r]
   uint64_t qlat_part;  // [H][qb_maxparts][d_c]: per-workgroup partials of W_UK[h]^T q_nope[h]
   uint64_t qrope;      // bf16 [n_hg][high, residual][hg][d_r]: rotated rotary queries * tau
-  uint64_t attn_part;  // [H][chunks][d_c + 2]: acc, max, sum (chunks <= nch, chosen per step)
+  uint64_t attn_part;  // [H][chunks][d_c + 4]: acc, max, sum, 2 zeros (chunks <= nch, chosen per step)
   uint64_t o;          // [H * d_v]
   uint64_t xa;         // [D] residual after attention
   uint64_t act;        // [slots * F_e] or [F]: weighted SwiGLU activations
@@ -113,6 +114,8 @@ struct Plan {
   uint64_t logits_internal;             // scratch: f32 [vocab]
   uint64_t x0;                          // scratch: f32 [D] step input (tap)
   uint64_t trace;                       // trace buffer or 0
+  // per head: bit k set when q_b workgroup qb_first(h) + k owns rows (wrote partial slot k)
+  uint64_t qb_mask[kMaxHeads];
   LayerPlan layers[PDM_MAX_LAYERS];
   StagePlan stages[kMaxStages];
 };

@@ -22,7 +22,7 @@ int validate_dims(const pdm_dims& d, int32_t max_ctx) {
   if (d.rope <= 0 || d.rope % 16 != 0 || d.rope > 128) return PDM_ERR_CONFIG;
   if (!(d.kv_lora == 128 || d.kv_lora == 256 || d.kv_lora == 512)) return PDM_ERR_CONFIG;
   if (!is_pow2(d.v_head)) return PDM_ERR_CONFIG;
-  if (d.n_heads <= 0 || d.n_heads % 8 != 0) return PDM_ERR_CONFIG;
+  if (d.n_heads <= 0 || d.n_heads % 8 != 0 || d.n_heads > kMaxHeads) return PDM_ERR_CONFIG;
   if (d.hidden > kXMax || d.q_lora > kXMax || d.n_heads * d.v_head > kXMax) return PDM_ERR_CONFIG;
   bool any_dense = false, any_moe = false;
   for (int l = 0; l < d.n_layers; ++l) {
@@ -107,6 +107,16 @@ int build_plan(const pdm_dims& d, int32_t max_ctx, int32_t G, Plan* p, Layout* l
   p->qb_maxparts = 1;
   for (int h = 0; h < H; ++h) p->qb_maxparts = std::max(p->qb_maxparts, qb_parts(d, p->qb_gran, G, h));
   if (p->qb_maxparts > 64) return PDM_ERR_CONFIG;  // the attention stage keeps a 64-bit slot mask per head
+  for (int h = 0; h < H; ++h) {
+    const int first = qb_first(d, p->qb_gran, G, h), np = qb_parts(d, p->qb_gran, G, h);
+    uint64_t m = 0;
+    for (int k = 0; k < np; ++k) {
+      int ra, rb;
+      split_rows(H * qkh, p->qb_gran, G, first + k, ra, rb);
+      if (rb > ra) m |= 1ull << k;
+    }
+    p->qb_mask[h] = m;
+  }
   {
     // q_b LDS: staged c_q, the workgroup's q_nope values, its W_UK rows and
     // their scales (each DMA'd with 1 KB of slack), the absorb reduction
@@ -255,7 +265,7 @@ int build_plan(const pdm_dims& d, int32_t max_ctx, int32_t G, Plan* p, Layout* l
   const uint64_t qkv_raw = s.take((uint64_t)(d.q_lora + kvr) * 4);
   const uint64_t qlat_part = s.take((uint64_t)H * p->qb_maxparts * d.kv_lora * 4);
   const uint64_t qrope = s.take((uint64_t)p->n_hg * 2 * p->hg * d.rope * 2);
-  const uint64_t attn_part = s.take((uint64_t)H * p->nch * (d.kv_lora + 2) * 4);
+  const uint64_t attn_part = s.take((uint64_t)H * p->nch * (d.kv_lora + 4) * 4);
   const uint64_t o = s.take((uint64_t)H * d.v_head * 4);
   const uint64_t act_buf = s.take((uint64_t)act * 4);
   const uint64_t router_logits = s.take((uint64_t)std::max(d.n_experts, 1) * 4);
