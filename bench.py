@@ -12,8 +12,11 @@ measured in the same run on the same engine and weights.
 Each workload is timed two ways, both with HIP events on the launch stream and
 inputs resident in HBM: K back-to-back single-step launches, and one resident
 launch of the same K steps (the engine stays on the device for the whole
-request; this is the headline figure). Prints one JSON line with tok/s/user,
-TPOT, the HBM roofline fraction, a stage trace and the CPU oracle baseline.
+request; this is the headline figure). Then the bare DeepSeek-V3-shaped dense
+and MoE layers are timed per layer-step, alternating over two weight copies so
+that no step is served from the MALL. Prints one JSON line with tok/s/user,
+TPOT, the HBM roofline fraction, a stage trace, the single-layer timings and
+the CPU oracle baseline.
 """
 from __future__ import annotations
 
@@ -244,6 +247,59 @@ def run_workload(eng, cfg, K, Wm, do_trace, trace_detail):
     return out
 
 
+def layer_steps(name: str, copies: int, steps: int, warm: int = 2):
+    """Microseconds per step of one bare DeepSeek-V3-shaped layer (dense or
+    MoE, fed an N(0,1) bf16 hidden vector, 1024-position prompt cache).
+    Consecutive steps alternate over `copies` engines that hold their own
+    copies of the weights, so a step never finds the weights of the step
+    before it in the 256 MB MALL (one dense layer streams ~0.6 GB, a MoE layer
+    ~0.6 GB of its ~11 GB). Each step is one launch, timed with HIP events on
+    the launch stream; the launch gap between steps is included."""
+    import torch
+    from persistent_decode_megakernel_amd import Engine, roofline as R
+    from synth import configs, gen
+    cfg = configs.get(name)
+    P = cfg.prompt_len
+    n = steps + warm
+    per_engine = (n + copies - 1) // copies
+    engines = []
+    for _ in range(copies):
+        e = Engine(cfg, max_ctx=P + per_engine, device=0)
+        store = gen.LogicalWeights(cfg, SEED, "cuda", cache=False)
+        for spec in store.specs():
+            e.load_tensor(spec, store.get(spec.name, spec.layer, spec.expert))
+        del store
+        e.reset()
+        e.import_kv(0, 0, gen.latent_rows(cfg, 0, P, SEED, device="cuda"))
+        engines.append(e)
+    xs = [gen.layer_input(cfg, j, 0, SEED, device="cuda") for j in range(n)]
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+    ev[0].record(stream)
+    for j in range(n):
+        engines[j % copies].decode(P + j // copies, x_in=xs[j])
+        ev[j + 1].record(stream)
+    torch.cuda.synchronize()
+    for e in engines:
+        rc, st = e.status()
+        if rc != 0:
+            raise SystemExit(f"{name}: layer step failed: status {rc} stage {st.stage}")
+    us = sorted(ev[j].elapsed_time(ev[j + 1]) * 1e3 for j in range(warm, n))
+    mean_us = sum(us) / len(us)
+    ctx = P + per_engine // 2
+    nbytes = R.bytes_per_token(cfg, ctx)
+    del engines
+    torch.cuda.empty_cache()
+    log(f"{name}: {mean_us:.1f} us per layer-step (p50 {us[len(us) // 2]:.1f}) over {copies} weight copies, "
+        f"{nbytes / mean_us / 1e3:.0f} GB/s")
+    return {"workload": name, "weight_copies": copies, "steps": steps, "us_per_layer_step": round(mean_us, 2),
+            "p50_us": round(us[len(us) // 2], 2), "bytes_per_step": int(nbytes),
+            "GBps": round(nbytes / mean_us / 1e3, 1),
+            "frac_of_8TBps": round(nbytes / (mean_us * 1e-6) / R.HBM_PEAK_BYTES_PER_S, 4),
+            "timing": "one launch per step (launch gap included), steps alternate over the weight copies"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -256,6 +312,11 @@ def main():
     ap.add_argument("--no-trace", action="store_true")
     ap.add_argument("--trace-detail", action="store_true",
                     help="also print the per-stage phase breakdown of the fastest traced step (stderr)")
+    ap.add_argument("--layers", default="dsv3_dense_layer,dsv3_moe_layer",
+                    help="bare single-layer workloads timed after the stack ('' for none)")
+    ap.add_argument("--layer-copies", type=int, default=2,
+                    help="weight copies the single-layer steps alternate over")
+    ap.add_argument("--layer-steps", type=int, default=32)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a 1 GiB device copy three times (counter calibration for rocprofv3)")
     args = ap.parse_args()
@@ -340,6 +401,11 @@ def main():
         "git_head": git_head(),
         "engine_source_hash": engine_source_hash(),
     }
+    if args.layers:
+        del eng
+        torch.cuda.empty_cache()
+        out["layer_steps"] = [layer_steps(n, args.layer_copies, args.layer_steps)
+                              for n in args.layers.split(",") if n]
     if not args.no_cpu_baseline:
         try:
             out["cpu_baseline"] = cpu_baseline(head, store, head.prompt_len)

@@ -63,6 +63,11 @@ class StageInfo(C.Structure):
                 ("weight_bytes", C.c_uint64)]
 
 
+class PackedMatrix(C.Structure):
+    _fields_ = [("codes_offset", C.c_uint64), ("scales_offset", C.c_uint64), ("rows", C.c_int32),
+                ("K", C.c_int32), ("n_kblocks", C.c_int32), ("parts", C.c_int32)]
+
+
 _P = C.c_void_p
 _SIGS = {
     "pdm_query_sizes": (C.c_int, [C.POINTER(Dims), C.c_int32, C.c_int32, C.POINTER(Sizes)]),
@@ -75,6 +80,11 @@ _SIGS = {
     "pdm_load_fp8": (C.c_int, [_P, C.c_int32, C.c_int32, C.c_int32, _P, _P, _P]),
     "pdm_load_raw": (C.c_int, [_P, C.c_int32, C.c_int32, C.c_int32, _P, C.c_uint64, _P]),
     "pdm_load_packed_weights": (C.c_int, [_P, _P, C.c_uint64, C.c_int, _P]),
+    "pdm_pack_header": (C.c_int, [C.POINTER(Dims), _P, C.c_uint64]),
+    "pdm_pack_fp8": (C.c_int, [C.POINTER(Dims), C.c_int32, C.c_int32, C.c_int32, _P, _P, _P, C.c_uint64]),
+    "pdm_pack_raw": (C.c_int, [C.POINTER(Dims), C.c_int32, C.c_int32, C.c_int32, _P, C.c_uint64, _P, C.c_uint64]),
+    "pdm_packed_layout": (C.c_int, [C.POINTER(Dims), C.c_int32, C.c_int32, C.c_int32, C.c_int32,
+                                    C.POINTER(PackedMatrix)]),
     "pdm_reset_cache": (C.c_int, [_P, _P]),
     "pdm_import_kv": (C.c_int, [_P, C.c_int32, C.c_int32, C.c_int32, _P, _P]),
     "pdm_export_kv": (C.c_int, [_P, C.c_int32, C.c_int32, C.c_int32, _P, _P]),

@@ -108,6 +108,104 @@ int check_engine(const pdm_engine* e, bool need_bound) {
 int bind_buffers(pdm_engine* e, void* weights_dev, uint64_t weight_bytes, void* kv_dev, uint64_t kv_bytes,
                  void* scratch_dev, uint64_t scratch_bytes, void* trace_dev, uint64_t trace_bytes);
 
+// Where an FP8 tensor goes in the weight arena: one packed matrix, or two for
+// W_UKV (its key rows to W_UK, its value rows to W_UV). Offsets are relative
+// to the arena start (plan with relative addresses).
+struct PackTarget {
+  PackMap m;
+  uint64_t codes, scales;
+};
+int pack_targets(const pdm_dims& d, const Plan& p, int32_t tensor, int32_t layer, int32_t expert, PackTarget* t,
+                 int* n) {
+  if (layer < 0 || layer >= d.n_layers) return PDM_ERR_ARG;
+  const LayerPlan& L = p.layers[layer];
+  const int H = d.n_heads, D = d.hidden, qkh = d.qk_nope + d.rope, kvr = d.kv_lora + d.rope;
+  const bool moe = L.is_moe != 0;
+  *n = 1;
+  auto set = [&](PackTarget& x, int mode, int N, int K, const Fp8Mat& dst, uint64_t base, int row0, int which) {
+    x.m = PackMap{};
+    x.m.mode = mode; x.m.N = N; x.m.K = K; x.m.rows = dst.rows; x.m.Kp = dst.K; x.m.nkb = dst.nkb;
+    x.m.row0 = row0; x.m.which = which; x.m.dn = d.qk_nope; x.m.dv = d.v_head; x.m.dc = d.kv_lora;
+    x.codes = base + dst.codes;
+    x.scales = base + dst.scales;
+  };
+  if (expert >= 0) {
+    if (!moe || expert >= d.n_experts + d.n_shared) return PDM_ERR_ARG;
+    const uint64_t blk = L.expert_base + (uint64_t)expert * L.expert_stride;
+    switch (tensor) {
+      case PDM_T_W_GATE: set(t[0], 3, d.moe_ffn, D, L.egu, blk, 0, 0); return PDM_OK;
+      case PDM_T_W_UP: set(t[0], 3, d.moe_ffn, D, L.egu, blk, 0, 1); return PDM_OK;
+      case PDM_T_W_DOWN: set(t[0], 0, D, d.moe_ffn, L.edown, blk, 0, 0); return PDM_OK;
+      default: return PDM_ERR_ARG;
+    }
+  }
+  switch (tensor) {
+    case PDM_T_WQ_A: set(t[0], 0, d.q_lora, D, L.qkv, 0, 0, 0); return PDM_OK;
+    case PDM_T_WKV_A: set(t[0], 0, kvr, D, L.qkv, 0, d.q_lora, 0); return PDM_OK;
+    case PDM_T_WQ_B: set(t[0], 0, H * qkh, d.q_lora, L.qb, 0, 0, 0); return PDM_OK;
+    case PDM_T_WKV_B:
+      set(t[0], 1, H * (d.qk_nope + d.v_head), d.kv_lora, L.uk, 0, 0, 0);
+      set(t[1], 2, H * (d.qk_nope + d.v_head), d.kv_lora, L.uv, 0, 0, 0);
+      *n = 2;
+      return PDM_OK;
+    case PDM_T_WO: set(t[0], 0, D, H * d.v_head, L.wo, 0, 0, 0); return PDM_OK;
+    case PDM_T_W_GATE: if (moe) return PDM_ERR_ARG; set(t[0], 3, d.ffn, D, L.gu, 0, 0, 0); return PDM_OK;
+    case PDM_T_W_UP: if (moe) return PDM_ERR_ARG; set(t[0], 3, d.ffn, D, L.gu, 0, 0, 1); return PDM_OK;
+    case PDM_T_W_DOWN: if (moe) return PDM_ERR_ARG; set(t[0], 0, D, d.ffn, L.down, 0, 0, 0); return PDM_OK;
+    default: return PDM_ERR_ARG;
+  }
+}
+
+// Arena offset and byte size of a bf16 or f32 tensor.
+int raw_target(const pdm_dims& d, const Plan& p, int32_t tensor, int32_t layer, int32_t expert, uint64_t* off,
+               uint64_t* need) {
+  if (expert >= 0) return PDM_ERR_ARG;
+  if (tensor == PDM_T_EMBED || tensor == PDM_T_LM_HEAD || tensor == PDM_T_FINAL_NORM) {
+    if (d.vocab <= 0) return PDM_ERR_ARG;
+    if (tensor == PDM_T_EMBED) { *off = p.embed; *need = (uint64_t)d.vocab * d.hidden * 2; }
+    else if (tensor == PDM_T_LM_HEAD) { *off = p.lm_head; *need = (uint64_t)d.vocab * d.hidden * 2; }
+    else { *off = p.final_norm; *need = (uint64_t)d.hidden * 4; }
+    return PDM_OK;
+  }
+  if (layer < 0 || layer >= d.n_layers) return PDM_ERR_ARG;
+  const LayerPlan& L = p.layers[layer];
+  switch (tensor) {
+    case PDM_T_ATTN_NORM: *off = L.attn_norm; *need = (uint64_t)d.hidden * 4; return PDM_OK;
+    case PDM_T_Q_NORM: *off = L.q_norm; *need = (uint64_t)d.q_lora * 4; return PDM_OK;
+    case PDM_T_KV_NORM: *off = L.kv_norm; *need = (uint64_t)d.kv_lora * 4; return PDM_OK;
+    case PDM_T_FFN_NORM: *off = L.ffn_norm; *need = (uint64_t)d.hidden * 4; return PDM_OK;
+    case PDM_T_ROUTER:
+      if (!L.is_moe) return PDM_ERR_ARG;
+      *off = L.router; *need = (uint64_t)d.n_experts * d.hidden * 2;
+      return PDM_OK;
+    default: return PDM_ERR_ARG;
+  }
+}
+
+Header blob_header(const pdm_dims& d, uint64_t weight_bytes) {
+  Header h{};
+  h.magic = kMagic;
+  h.abi = PDM_ABI_VERSION;
+  h.dims_hash = dims_hash(d);
+  h.weight_bytes = weight_bytes;
+  return h;
+}
+
+// Relative plan of a model shape for the host packer (the weight arena
+// layout depends on neither the context length nor the workgroup count).
+struct HostPlan {
+  Plan* p = nullptr;
+  Layout lay;
+  int rc = PDM_OK;
+  explicit HostPlan(const pdm_dims* d) {
+    if (!d) { rc = PDM_ERR_ARG; return; }
+    p = new (std::nothrow) Plan;
+    if (!p) { rc = PDM_ERR_OOM; return; }
+    rc = build_plan(*d, 1, 256, p, &lay);
+  }
+  ~HostPlan() { delete p; }
+};
+
 }  // namespace
 
 extern "C" {
@@ -222,11 +320,7 @@ int bind_buffers(pdm_engine* e, void* weights_dev, uint64_t weight_bytes, void* 
   e->trace = static_cast<uint64_t*>(trace_dev);
   e->plan_dev = reinterpret_cast<Plan*>(e->scratch + e->lay.plan_off);
   absolutize(*e, &e->abs);
-  Header h{};
-  h.magic = kMagic;
-  h.abi = PDM_ABI_VERSION;
-  h.dims_hash = dims_hash(e->dims);
-  h.weight_bytes = e->lay.weight_bytes;
+  const Header h = blob_header(e->dims, e->lay.weight_bytes);
   hipError_t err = hipMemcpy(e->w, &h, sizeof(h), hipMemcpyHostToDevice);
   if (err == hipSuccess) err = hipMemcpy(e->plan_dev, &e->abs, sizeof(Plan), hipMemcpyHostToDevice);
   if (err == hipSuccess) {
@@ -253,82 +347,30 @@ int pdm_load_fp8(pdm_engine* e, int32_t tensor, int32_t layer, int32_t expert, c
   int rc = check_engine(e, true);
   if (rc) return rc;
   if (!codes_dev || !scales_dev) return PDM_ERR_ARG;
-  const pdm_dims& d = e->dims;
-  if (layer < 0 || layer >= d.n_layers) return PDM_ERR_ARG;
-  const LayerPlan& L = e->abs.layers[layer];
-  const int H = d.n_heads, D = d.hidden, qkh = d.qk_nope + d.rope, kvr = d.kv_lora + d.rope;
-  const bool moe = L.is_moe != 0;
-  PackMap m{};
-  m.dn = d.qk_nope; m.dv = d.v_head; m.dc = d.kv_lora;
-  // dst offsets are absolute addresses (base 0) or relative to an expert block
-  auto into = [&](const Fp8Mat& dst, uint64_t base) {
-    return hip_fail(launch_pack(codes_dev, scales_dev, reinterpret_cast<uint8_t*>(base + dst.codes),
-                                reinterpret_cast<uint16_t*>(base + dst.scales), m, (hipStream_t)stream));
-  };
-  auto set = [&](int mode, int N, int K, const Fp8Mat& dst, int row0, int which) {
-    m.mode = mode; m.N = N; m.K = K; m.rows = dst.rows; m.Kp = dst.K; m.nkb = dst.nkb; m.row0 = row0; m.which = which;
-  };
+  PackTarget t[2];
+  int n = 0;
+  rc = pack_targets(e->dims, e->plan, tensor, layer, expert, t, &n);
+  if (rc) return rc;
   DeviceGuard g(e->device);
-  const uint64_t zero = 0;
-  if (expert >= 0) {
-    if (!moe || expert >= d.n_experts + d.n_shared) return PDM_ERR_ARG;
-    const uint64_t blk = L.expert_base + (uint64_t)expert * L.expert_stride;
-    switch (tensor) {
-      case PDM_T_W_GATE: set(3, d.moe_ffn, D, L.egu, 0, 0); return into(L.egu, blk);
-      case PDM_T_W_UP: set(3, d.moe_ffn, D, L.egu, 0, 1); return into(L.egu, blk);
-      case PDM_T_W_DOWN: set(0, D, d.moe_ffn, L.edown, 0, 0); return into(L.edown, blk);
-      default: return PDM_ERR_ARG;
-    }
+  for (int i = 0; i < n; ++i) {
+    rc = hip_fail(launch_pack(codes_dev, scales_dev, e->w + t[i].codes, reinterpret_cast<uint16_t*>(e->w + t[i].scales),
+                              t[i].m, (hipStream_t)stream));
+    if (rc) return rc;
   }
-  switch (tensor) {
-    case PDM_T_WQ_A: set(0, d.q_lora, D, L.qkv, 0, 0); return into(L.qkv, zero);
-    case PDM_T_WKV_A: set(0, kvr, D, L.qkv, d.q_lora, 0); return into(L.qkv, zero);
-    case PDM_T_WQ_B: set(0, H * qkh, d.q_lora, L.qb, 0, 0); return into(L.qb, zero);
-    case PDM_T_WKV_B: {
-      set(1, H * (d.qk_nope + d.v_head), d.kv_lora, L.uk, 0, 0);
-      rc = into(L.uk, zero);
-      if (rc) return rc;
-      set(2, H * (d.qk_nope + d.v_head), d.kv_lora, L.uv, 0, 0);
-      return into(L.uv, zero);
-    }
-    case PDM_T_WO: set(0, D, H * d.v_head, L.wo, 0, 0); return into(L.wo, zero);
-    case PDM_T_W_GATE: if (moe) return PDM_ERR_ARG; set(3, d.ffn, D, L.gu, 0, 0); return into(L.gu, zero);
-    case PDM_T_W_UP: if (moe) return PDM_ERR_ARG; set(3, d.ffn, D, L.gu, 0, 1); return into(L.gu, zero);
-    case PDM_T_W_DOWN: if (moe) return PDM_ERR_ARG; set(0, D, d.ffn, L.down, 0, 0); return into(L.down, zero);
-    default: return PDM_ERR_ARG;
-  }
+  return PDM_OK;
 }
 
 int pdm_load_raw(pdm_engine* e, int32_t tensor, int32_t layer, int32_t expert, const void* src_dev, uint64_t bytes,
                  pdm_stream_t stream) {
   int rc = check_engine(e, true);
   if (rc) return rc;
-  if (!src_dev || expert >= 0) return PDM_ERR_ARG;
-  const pdm_dims& d = e->dims;
-  uint64_t dst = 0, need = 0;
-  if (tensor == PDM_T_EMBED || tensor == PDM_T_LM_HEAD || tensor == PDM_T_FINAL_NORM) {
-    if (d.vocab <= 0) return PDM_ERR_ARG;
-    if (tensor == PDM_T_EMBED) { dst = e->abs.embed; need = (uint64_t)d.vocab * d.hidden * 2; }
-    else if (tensor == PDM_T_LM_HEAD) { dst = e->abs.lm_head; need = (uint64_t)d.vocab * d.hidden * 2; }
-    else { dst = e->abs.final_norm; need = (uint64_t)d.hidden * 4; }
-  } else {
-    if (layer < 0 || layer >= d.n_layers) return PDM_ERR_ARG;
-    const LayerPlan& L = e->abs.layers[layer];
-    switch (tensor) {
-      case PDM_T_ATTN_NORM: dst = L.attn_norm; need = (uint64_t)d.hidden * 4; break;
-      case PDM_T_Q_NORM: dst = L.q_norm; need = (uint64_t)d.q_lora * 4; break;
-      case PDM_T_KV_NORM: dst = L.kv_norm; need = (uint64_t)d.kv_lora * 4; break;
-      case PDM_T_FFN_NORM: dst = L.ffn_norm; need = (uint64_t)d.hidden * 4; break;
-      case PDM_T_ROUTER:
-        if (!L.is_moe) return PDM_ERR_ARG;
-        dst = L.router; need = (uint64_t)d.n_experts * d.hidden * 2; break;
-      default: return PDM_ERR_ARG;
-    }
-  }
+  if (!src_dev) return PDM_ERR_ARG;
+  uint64_t off = 0, need = 0;
+  rc = raw_target(e->dims, e->plan, tensor, layer, expert, &off, &need);
+  if (rc) return rc;
   if (bytes != need) return PDM_ERR_SIZE;
   DeviceGuard g(e->device);
-  return hip_fail(hipMemcpyAsync(reinterpret_cast<void*>(dst), src_dev, bytes, hipMemcpyDeviceToDevice,
-                                 (hipStream_t)stream));
+  return hip_fail(hipMemcpyAsync(e->w + off, src_dev, bytes, hipMemcpyDeviceToDevice, (hipStream_t)stream));
 }
 
 int pdm_load_packed_weights(pdm_engine* e, const void* blob, uint64_t bytes, int blob_on_device, pdm_stream_t stream) {
@@ -348,6 +390,76 @@ int pdm_load_packed_weights(pdm_engine* e, const void* blob, uint64_t bytes, int
     return PDM_ERR_FORMAT;
   return hip_fail(hipMemcpyAsync(e->w, blob, e->lay.weight_bytes,
                                  blob_on_device ? hipMemcpyDeviceToDevice : hipMemcpyHostToDevice, (hipStream_t)stream));
+}
+
+int pdm_pack_header(const pdm_dims* dims, void* arena, uint64_t arena_bytes) {
+  HostPlan hp(dims);
+  if (hp.rc) return hp.rc;
+  if (!arena) return PDM_ERR_ARG;
+  if (arena_bytes < hp.lay.weight_bytes) return PDM_ERR_SIZE;
+  const Header h = blob_header(*dims, hp.lay.weight_bytes);
+  std::memcpy(arena, &h, sizeof(h));
+  return PDM_OK;
+}
+
+int pdm_pack_fp8(const pdm_dims* dims, int32_t tensor, int32_t layer, int32_t expert, const uint8_t* codes,
+                 const uint16_t* scales, void* arena, uint64_t arena_bytes) {
+  HostPlan hp(dims);
+  if (hp.rc) return hp.rc;
+  if (!codes || !scales || !arena) return PDM_ERR_ARG;
+  if (arena_bytes < hp.lay.weight_bytes) return PDM_ERR_SIZE;
+  PackTarget t[2];
+  int n = 0;
+  int rc = pack_targets(*dims, *hp.p, tensor, layer, expert, t, &n);
+  if (rc) return rc;
+  uint8_t* a = static_cast<uint8_t*>(arena);
+  for (int i = 0; i < n; ++i) {
+    const PackMap& m = t[i].m;
+    uint8_t* dc = a + t[i].codes;
+    uint16_t* ds = reinterpret_cast<uint16_t*>(a + t[i].scales);
+    int sr = 0, sc = 0;
+    // pack_src keeps columns (sc = k): a packed row is one logical row
+    for (int r = 0; r < m.rows; ++r)
+      if (pack_src(m, r, 0, sr, sc)) std::memcpy(dc + (size_t)r * m.Kp, codes + (size_t)sr * m.K, (size_t)m.Kp);
+    const int skb = (m.K + 127) / 128;
+    for (int rg = 0; rg < m.rows / 8; ++rg)
+      for (int kb = 0; kb < m.nkb; ++kb)
+        if (pack_src(m, rg * 8, kb * 128, sr, sc)) ds[(size_t)rg * m.nkb + kb] = scales[(size_t)(sr / 128) * skb + sc / 128];
+  }
+  return PDM_OK;
+}
+
+int pdm_pack_raw(const pdm_dims* dims, int32_t tensor, int32_t layer, int32_t expert, const void* src,
+                 uint64_t bytes, void* arena, uint64_t arena_bytes) {
+  HostPlan hp(dims);
+  if (hp.rc) return hp.rc;
+  if (!src || !arena) return PDM_ERR_ARG;
+  if (arena_bytes < hp.lay.weight_bytes) return PDM_ERR_SIZE;
+  uint64_t off = 0, need = 0;
+  int rc = raw_target(*dims, *hp.p, tensor, layer, expert, &off, &need);
+  if (rc) return rc;
+  if (bytes != need) return PDM_ERR_SIZE;
+  std::memcpy(static_cast<uint8_t*>(arena) + off, src, bytes);
+  return PDM_OK;
+}
+
+int pdm_packed_layout(const pdm_dims* dims, int32_t tensor, int32_t layer, int32_t expert, int32_t part,
+                      pdm_packed_matrix* out) {
+  HostPlan hp(dims);
+  if (hp.rc) return hp.rc;
+  if (!out) return PDM_ERR_ARG;
+  PackTarget t[2];
+  int n = 0;
+  int rc = pack_targets(*dims, *hp.p, tensor, layer, expert, t, &n);
+  if (rc) return rc;
+  if (part < 0 || part >= n) return PDM_ERR_ARG;
+  out->codes_offset = t[part].codes;
+  out->scales_offset = t[part].scales;
+  out->rows = t[part].m.rows;
+  out->K = t[part].m.Kp;
+  out->n_kblocks = t[part].m.nkb;
+  out->parts = n;
+  return PDM_OK;
 }
 
 int pdm_reset_cache(pdm_engine* e, pdm_stream_t stream) {

@@ -27,9 +27,6 @@ struct LaunchArgs {
 };
 
 // Row/column map of the offline packer (see engine.hip, pack_codes_kernel).
-struct PackMap {
-  int mode, N, K, rows, Kp, nkb, row0, dn, dv, dc, which;
-};
 
 hipError_t launch_engine(const Plan* plan_dev, const LaunchArgs& a, int G, hipStream_t stream, bool cooperative);
 hipError_t launch_rope_table(float* tab, int max_ctx, int rope, double base, hipStream_t stream);

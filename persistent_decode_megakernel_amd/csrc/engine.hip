@@ -2025,34 +2025,8 @@ __global__ void rope_table_kernel(float* tab, int max_ctx, int rope, double base
   }
 }
 
-// Offline packer: logical FP8 matrix (codes [N][K], scales [ceil(N/128)][ceil(K/128)])
-// into a packed matrix (codes [rows][Kp], scales [rows/8][nkb]) by a row/column map.
-//   mode 0: packed row r = logical row (r - row0) for r in [row0, row0 + N), same columns
-//   mode 1 (W_UK extract):   packed row (h, n), column c  <- logical (h*(dn+dv) + n, c)
-//   mode 2 (W_UV extract):   packed row (h, v), column c  <- logical (h*(dn+dv) + dn + v, c)
-//   mode 3 (gate/up interleave): packed row 16*i + j (j < 8) <- gate row 8*i + j (a0 = 0),
-//                                packed row 16*i + 8 + j     <- up row 8*i + j (a0 = 1)
-
-__device__ __forceinline__ bool pack_src(const PackMap& m, int r, int k, int& sr, int& sc) {
-  switch (m.mode) {
-    case 0:
-      if (r < m.row0 || r >= m.row0 + m.N) return false;
-      sr = r - m.row0; sc = k; return true;
-    case 1: {
-      int h = r / m.dn, n = r % m.dn;
-      sr = h * (m.dn + m.dv) + n; sc = k; return true;
-    }
-    case 2: {
-      int h = r / m.dv, v = r % m.dv;
-      sr = h * (m.dn + m.dv) + m.dn + v; sc = k; return true;
-    }
-    default: {
-      int i = r >> 4, j = r & 15;
-      if ((j >= 8) != (m.which == 1)) return false;
-      sr = 8 * i + (j & 7); sc = k; return true;
-    }
-  }
-}
+// Offline packer on the device: the logical-to-packed map of pack_src
+// (pdm_internal.h), one byte or scale per thread.
 
 __global__ void pack_codes_kernel(const uint8_t* __restrict__ src, uint8_t* __restrict__ dst, PackMap m) {
   const size_t n = (size_t)m.rows * m.Kp;

@@ -137,6 +137,42 @@ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // Balanced contiguous share of `rows` (whole groups of `gran` rows) for
 // workgroup wg of G: rows [ra, rb). Requires (rows / gran) * G < 2^31.
+// Packed FP8 matrix from a logical one (codes [N][K] row-major, bf16 block
+// scales [ceil(N/128)][ceil(K/128)]): packed codes [rows][Kp] (Kp = K) and
+// scales [rows / 8][nkb], one per 8 packed rows and 128 columns (the scale of
+// the logical block holding that tile's first element). Packed row r takes
+// logical row sr (columns unchanged) by mode:
+//   0: sr = r - row0 for r in [row0, row0 + N) (row concatenation; the rest
+//      of the packed rows come from other tensors)
+//   1: W_UK rows out of W_UKV: r = h * dn + n <- h * (dn + dv) + n
+//   2: W_UV rows out of W_UKV: r = h * dv + v <- h * (dn + dv) + dn + v
+//   3: gate/up interleave in groups of 8: r = 16 i + j <- gate row 8 i + j
+//      (j < 8, which = 0) or up row 8 i + (j - 8) (j >= 8, which = 1)
+struct PackMap {
+  int mode, N, K, rows, Kp, nkb, row0, dn, dv, dc, which;
+};
+PDM_HD inline bool pack_src(const PackMap& m, int r, int k, int& sr, int& sc) {
+  sc = k;
+  switch (m.mode) {
+    case 0:
+      if (r < m.row0 || r >= m.row0 + m.N) return false;
+      sr = r - m.row0;
+      return true;
+    case 1:
+      sr = r / m.dn * (m.dn + m.dv) + r % m.dn;
+      return true;
+    case 2:
+      sr = r / m.dv * (m.dn + m.dv) + m.dn + r % m.dv;
+      return true;
+    default: {
+      const int i = r >> 4, j = r & 15;
+      if ((j >= 8) != (m.which == 1)) return false;
+      sr = 8 * i + (j & 7);
+      return true;
+    }
+  }
+}
+
 PDM_HD inline void split_rows(int rows, int gran, int G, int wg, int& ra, int& rb) {
   const int ng = rows / gran;
   ra = ng * wg / G * gran;

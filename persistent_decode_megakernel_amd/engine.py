@@ -39,7 +39,8 @@ class Engine:
         self.sizes = s
         u8 = torch.uint8
         self.static_scratch = bool(static_scratch)
-        self.weights = torch.empty(s.weight_bytes, dtype=u8, device=self.device)
+        # zeroed, so that the gaps between packed tensors are reproducible bytes
+        self.weights = torch.zeros(s.weight_bytes, dtype=u8, device=self.device)
         self.kv = torch.zeros(s.kv_bytes, dtype=u8, device=self.device)
         if self.static_scratch:
             if trace:

@@ -186,6 +186,28 @@ def test_packed_blob_roundtrip(tiny_case):
     assert torch.equal(l1, l2)
 
 
+def test_host_packer_equals_device_packer(tiny_case):
+    """The host packer's blob (pdm_pack_*) is byte for byte the weight arena the
+    device packer (pdm_load_fp8 / pdm_load_raw) and pdm_bind produced, and an
+    engine loaded from it decodes like the original."""
+    from persistent_decode_megakernel_amd import Engine, pack
+    cfg, store, W, st0, steps, eng = tiny_case
+    blob = pack.pack_store(cfg, store)
+    dev = eng.weights.cpu().numpy()
+    assert dev.nbytes == blob.nbytes
+    diff = np.nonzero(dev != blob)[0]
+    assert diff.size == 0, f"{diff.size} bytes differ, first at {diff[:8].tolist()}"
+    eng2 = Engine(cfg, max_ctx=eng.max_ctx, device=0)
+    eng2.load_packed(torch.from_numpy(blob))
+    torch.cuda.synchronize()
+    for e in (eng, eng2):
+        _import_prefill(e, cfg, st0, cfg.prompt_len)
+    a1, l1 = eng.decode(cfg.prompt_len, token=steps[0][0])
+    a2, l2 = eng2.decode(cfg.prompt_len, token=steps[0][0])
+    torch.cuda.synchronize()
+    assert int(a1.item()) == int(a2.item()) and torch.equal(l1, l2)
+
+
 def test_trace_records(tiny_case):
     cfg, store, W, st0, steps, eng = tiny_case
     _import_prefill(eng, cfg, st0, cfg.prompt_len)
