@@ -21,8 +21,8 @@ What the TileRT pages fix and what is read into them:
     stream handed from one layer to the next is rounded to bf16. Everything
     else is exact float64 arithmetic of the dequantised weights.
 
-A dequantised FP8 weight is exactly code_value * block_scale; bf16 tensors
-widen exactly. Weights come from a store with a `numpy(name, layer, expert)`
+A dequantised FP8 or MXFP4 weight is exactly code_value * block_scale; bf16
+tensors widen exactly. Weights come from a store with a `numpy(name, layer, expert)`
 method returning the storage-form arrays (see synth.gen.LogicalWeights).
 """
 from __future__ import annotations
@@ -32,7 +32,7 @@ from typing import Dict, List, Optional
 
 import numpy as np
 
-from .numerics import bf16_bits_to_f64, bf16_round, dequant_fp8
+from .numerics import bf16_bits_to_f64, bf16_round, dequant_fp8, dequant_mxfp4
 
 
 # ---------------------------------------------------------------------------
@@ -56,6 +56,8 @@ class OracleWeights:
         t = self.store.numpy(name, layer, expert)
         if "codes" in t:
             w = dequant_fp8(t["codes"], t["scales"])
+        elif "mx_codes" in t:
+            w = dequant_mxfp4(t["mx_codes"], t["mx_scales"])
         elif t["data"].dtype == np.uint16:
             w = bf16_bits_to_f64(t["data"])
         else:

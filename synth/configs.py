@@ -39,6 +39,9 @@ class ModelConfig:
     # how the prompt cache is filled: "prefill" (full causal forward of the
     # prompt tokens) or "latent" (i.i.d. N(0,1) latents, rounded to bf16)
     prompt_fill: str = "prefill"
+    # storage of the routed and shared expert matrices: "fp8" (e4m3 with
+    # 128x128 bf16 block scales, like every other matrix) or "mxfp4"
+    expert_format: str = "fp8"
 
     @property
     def n_layers(self) -> int:
@@ -100,6 +103,13 @@ CONFIGS = {
         prompt_fill="latent"),
 }
 
+# The same models with MXFP4 expert matrices (OCP Microscaling: e2m1
+# elements, one power-of-two e8m0 scale per 32 consecutive elements of a row):
+# the 4-bit weights the pages' roofline figures assume, which halve the bytes
+# of every expert a token reads.
+for _n in ("tiny", "ragged", "dsv3_moe_layer", "dsv3_stack_1k", "dsv3_stack_8k"):
+    CONFIGS[_n + "_fp4"] = CONFIGS[_n].with_(name=_n + "_fp4", expert_format="mxfp4")
+
 # the workloads in the order the project's configuration list gives them
 CONFIG_ORDER = ("tiny", "dsv3_dense_layer", "dsv3_moe_layer", "dsv3_stack_1k", "dsv3_stack_8k")
 
@@ -113,10 +123,12 @@ def get(name: str) -> ModelConfig:
 # FP8 matrices carry one bf16 scale per 128x128 block (edge blocks partial).
 # ---------------------------------------------------------------------------
 FP8 = "fp8"      # uint8 e4m3 codes [N, K] + uint16 bf16 bit patterns [ceil(N/128), ceil(K/128)]
+MXFP4 = "mxfp4"  # uint8 codes [N, K/2] (element 2j in the low nibble of byte j, e2m1) + uint8 e8m0 scales [N, K/32]
 BF16 = "bf16"    # uint16 bf16 bit patterns
 F32 = "f32"      # float32 (norm gains)
 
 BLOCK = 128
+MX_BLOCK = 32
 
 
 @dataclass(frozen=True)
@@ -151,10 +163,11 @@ def layer_tensors(cfg: ModelConfig, l: int):
                 TensorSpec("w_down", FP8, (D, cfg.ffn), l)]
     else:
         out.append(TensorSpec("router", BF16, (cfg.n_experts, D), l))
+        ek = MXFP4 if cfg.expert_format == "mxfp4" else FP8
         for e in range(cfg.n_experts + cfg.n_shared):
-            out += [TensorSpec("w_gate", FP8, (cfg.moe_ffn, D), l, e),
-                    TensorSpec("w_up", FP8, (cfg.moe_ffn, D), l, e),
-                    TensorSpec("w_down", FP8, (D, cfg.moe_ffn), l, e)]
+            out += [TensorSpec("w_gate", ek, (cfg.moe_ffn, D), l, e),
+                    TensorSpec("w_up", ek, (cfg.moe_ffn, D), l, e),
+                    TensorSpec("w_down", ek, (D, cfg.moe_ffn), l, e)]
     return out
 
 

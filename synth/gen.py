@@ -13,6 +13,13 @@ Storage forms (the interface the decode step consumes):
     Pre-quantisation values are N(0, std^2); the scale is bf16(amax / 448)
     (1 for an all-zero block) and the code is the e4m3 encoding of
     clamp(w / scale, -448, 448), using torch's float8_e4m3fn conversion.
+  * MXFP4 matrix [N, K] (expert matrices of the *_fp4 configs): OCP
+    Microscaling FP4, e2m1 codes packed two per byte (element 2j in the low
+    nibble of byte j) [N, K/2] plus one e8m0 scale byte per 32 consecutive
+    elements of a row [N, K/32]. Pre-quantisation values are N(0, std^2); a
+    block's scale is 2^(floor(log2(amax)) - 2) (2 = exponent of the largest
+    e2m1 value, 6 = 1.5 * 2^2) and each element is w / scale rounded to the
+    nearest e2m1 value, ties to the even code, saturating at +-6.
   * bf16 tensors (router, embedding, LM head): N(0, std^2) rounded to bf16,
     stored as uint16 bit patterns.
   * norm gains: float32, all ones unless random gains are requested.
@@ -60,6 +67,26 @@ def quantize_blocks(w: torch.Tensor):
     return codes, s.view(torch.int16)
 
 
+def quantize_mxfp4(w: torch.Tensor):
+    """MXFP4 quantisation of an fp32 matrix [N, K], K a multiple of 32 (input
+    preparation only; the scale and rounding rules are in the module doc)."""
+    n, k = w.shape
+    blocks = w.reshape(n, k // C.MX_BLOCK, C.MX_BLOCK)
+    amax = blocks.abs().amax(dim=2)
+    e = torch.where(amax > 0, torch.floor(torch.log2(torch.where(amax > 0, amax, torch.ones_like(amax)))) - 2,
+                    torch.zeros_like(amax)).clamp(-127, 127)
+    a = (blocks / torch.exp2(e)[:, :, None]).abs()
+    # nearest e2m1 magnitude code (0, .5, 1, 1.5, 2, 3, 4, 6 -> 0..7); a tie
+    # goes to the even code: down at .25, 1.25, 2.5, 5 and up at .75, 1.75, 3.5
+    code = ((a > 0.25).int() + (a >= 0.75).int() + (a > 1.25).int() + (a >= 1.75).int() + (a > 2.5).int()
+            + (a >= 3.5).int() + (a > 5.0).int())
+    code = code | ((blocks < 0).int() << 3)
+    code = code.reshape(n, k).to(torch.uint8)
+    packed = code[:, 0::2] | (code[:, 1::2] << 4)
+    scales = (e + 127).to(torch.uint8)
+    return packed.contiguous(), scales.contiguous()
+
+
 def gen_tensor(spec: C.TensorSpec, master: int, device="cpu", std: float = 0.02,
                gains: str = "one") -> Dict[str, torch.Tensor]:
     seed = tensor_seed(master, spec.name, spec.layer, spec.expert)
@@ -72,6 +99,9 @@ def gen_tensor(spec: C.TensorSpec, master: int, device="cpu", std: float = 0.02,
     w = torch.randn(spec.shape, generator=g, device=device, dtype=torch.float32) * std
     if spec.kind == C.BF16:
         return {"data": w.to(torch.bfloat16).view(torch.int16)}
+    if spec.kind == C.MXFP4:
+        codes, scales = quantize_mxfp4(w)
+        return {"mx_codes": codes, "mx_scales": scales}
     codes, scales = quantize_blocks(w)
     return {"codes": codes, "scales": scales}
 

@@ -127,3 +127,19 @@ def test_blocked_lm_head_matches_step_logits(tiny_cfg, tiny_store):
         got = O.lm_logits(W, tiny_cfg, x, rows_per_block=rows)
         assert got.shape == out["logits"].shape
         assert _rel(got, out["logits"]) < 1e-13
+
+
+def test_decode_equals_causal_forward_mxfp4_experts():
+    """The same invariant with MXFP4 expert matrices (tiny_fp4): 40 positions."""
+    cfg = configs.get("tiny_fp4")
+    store = gen.LogicalWeights(cfg, 0, "cpu")
+    W = O.OracleWeights(store)
+    moe = cfg.layers.index("moe")
+    assert "mx_codes" in store.numpy("w_gate", moe, 0)
+    toks = gen.prompt_tokens(cfg)[:40]
+    full = O.forward_full(W, tokens=toks, parity=True, absorbed=False)
+    outs, _ = _decode_all(W, cfg, toks, True)
+    for t in range(len(toks)):
+        for l in range(cfg.n_layers):
+            assert _rel(outs[t]["hidden"][l], full["hidden"][l][t]) < 1e-12, (t, l)
+        assert outs[t]["argmax"] == int(np.argmax(full["logits"][t]))

@@ -114,3 +114,82 @@ def test_quantiser_ties_to_even():
     assert O.bf16_bits_to_f64(sbits.numpy().view(np.uint16))[0, 0] == 1.0
     assert N.E4M3[codes[0, 1].item()] == 1.0
     assert N.E4M3[codes[0, 2].item()] == 1.25
+
+
+# --- MXFP4 (OCP Microscaling v1.0: e2m1 elements, e8m0 block scales of 32)
+
+def _e2m1_as_e4m3_code(c: int) -> int:
+    """The e4m3 code of the same value: e2m1 is (sign, exponent bias 1,
+    1 mantissa bit), e4m3 (sign, exponent bias 7, 3 mantissa bits). Normal
+    e2m1 values move the exponent field by +6 and the mantissa bit to the top
+    of the 3-bit field; the e2m1 subnormal 0.5 is the e4m3 normal 2^-1."""
+    sign, exp, man = (c >> 3) & 1, (c >> 1) & 3, c & 1
+    if exp == 0:
+        mag = 0 if man == 0 else (6 << 3)
+    else:
+        mag = ((exp + 6) << 3) | (man << 2)
+    return (sign << 7) | mag
+
+
+def test_e2m1_table_matches_torch_float8_values():
+    # every e2m1 value is an e4m3 value: decode its e4m3 twin with torch
+    twins = torch.tensor([_e2m1_as_e4m3_code(c) for c in range(16)], dtype=torch.int32).to(torch.uint8)
+    ref = twins.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    np.testing.assert_array_equal(O.e2m1_decode(np.arange(16)), ref)
+
+
+def test_e2m1_invariants():
+    t = N.E2M1
+    assert t.shape == (16,) and np.isfinite(t).all()              # no inf / NaN codes
+    np.testing.assert_array_equal(t[8:], -t[:8])                   # sign bit
+    assert np.signbit(t[8]) and t[8] == 0.0
+    mags = t[:8]
+    assert (np.diff(mags) > 0).all() and mags.max() == 6.0         # monotone, largest 1.5 * 2^2
+    assert t[1] == 0.5 and t[2] == 1.0                             # subnormal step, exponent bias 1
+    # every magnitude is a multiple of the subnormal step 0.5 and below 8
+    assert (np.mod(mags, 0.5) == 0).all()
+
+
+def test_e8m0_scales():
+    np.testing.assert_array_equal(O.e8m0_decode(np.array([127, 128, 126, 0, 254])),
+                                  [1.0, 2.0, 0.5, 2.0 ** -127, 2.0 ** 127])
+    assert np.isnan(O.e8m0_decode(np.array([255]))[0])
+
+
+def test_mxfp4_dequant_bruteforce():
+    rng = np.random.default_rng(3)
+    n, k = 5, 96
+    codes = rng.integers(0, 256, size=(n, k // 2), dtype=np.uint8)
+    scales = rng.integers(100, 140, size=(n, k // 32), dtype=np.uint8)
+    got = O.dequant_mxfp4(codes, scales)
+    for i in range(n):
+        for j in range(k):
+            byte = int(codes[i, j // 2])
+            nib = byte & 0xF if j % 2 == 0 else byte >> 4
+            sign = -1.0 if nib & 8 else 1.0
+            e, m = (nib >> 1) & 3, nib & 1
+            v = sign * (m / 2.0 if e == 0 else (1 + m / 2.0) * 2.0 ** (e - 1))
+            assert got[i, j] == v * 2.0 ** (int(scales[i, j // 32]) - 127), (i, j)
+
+
+def test_generator_mxfp4_quantiser_is_nearest():
+    """The storage-form MXFP4 codes are a nearest e2m1 value of w / scale
+    (ties to the even code), with scale 2^(floor(log2(block amax)) - 2)."""
+    g = torch.Generator().manual_seed(7)
+    w = torch.randn(64, 256, generator=g) * 0.02
+    w[0, :32] = 0.0                       # an all-zero block
+    w[1, 0], w[1, 1] = 6.0 * 2.0 ** -5, 5.0 * 2.0 ** -5   # 5 is halfway between 4 and 6: even code (4)
+    codes, scales = gen.quantize_mxfp4(w)
+    codes, scales = codes.numpy(), scales.numpy()
+    deq = O.dequant_mxfp4(codes, scales)
+    s = O.e8m0_decode(np.repeat(scales, 32, axis=1))
+    wd = w.double().numpy()
+    amax = np.abs(wd).reshape(64, 8, 32).max(axis=2)
+    nz = amax > 0
+    np.testing.assert_array_equal(scales[nz].astype(np.int64) - 127, np.floor(np.log2(amax[nz])) - 2)
+    target = np.clip(wd / s, -6, 6)
+    dist = np.abs(target.reshape(-1)[:, None] - N.E2M1[None, :])
+    got = np.abs(target.reshape(-1) - deq.reshape(-1) / s.reshape(-1))
+    assert np.all(got <= dist.min(axis=1) * (1 + 1e-12) + 1e-300)
+    assert deq[1, 0] == 6.0 * 2.0 ** -5 and deq[1, 1] == 4.0 * 2.0 ** -5
+    assert (deq[0, :32] == 0).all()
