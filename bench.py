@@ -312,6 +312,8 @@ def main():
     ap.add_argument("--no-trace", action="store_true")
     ap.add_argument("--trace-detail", action="store_true",
                     help="also print the per-stage phase breakdown of the fastest traced step (stderr)")
+    ap.add_argument("--mxfp4", default="dsv3_stack_1k_fp4",
+                    help="the same stack with MXFP4 experts, timed on its own engine ('' for none)")
     ap.add_argument("--layers", default="dsv3_dense_layer,dsv3_moe_layer",
                     help="bare single-layer workloads timed after the stack ('' for none)")
     ap.add_argument("--layer-copies", type=int, default=2,
@@ -356,6 +358,21 @@ def main():
 
     results = [run_workload(eng, c, K, Wm, not args.no_trace, args.trace_detail and i == 0)
                for i, c in enumerate(cfgs)]
+    if args.mxfp4:
+        # a second engine: the expert matrices are MXFP4 (everything else as above)
+        c4 = configs.get(args.mxfp4)
+        e4 = Engine(c4, max_ctx=c4.prompt_len + c4.decode_steps, device=0, trace=not args.no_trace)
+        e4.set_trace(False)
+        s4 = gen.LogicalWeights(c4, SEED, "cuda", cache=False)
+        for spec in s4.specs():
+            e4.load_tensor(spec, s4.get(spec.name, spec.layer, spec.expert))
+        torch.cuda.synchronize()
+        log(f"{c4.name}: weights {e4.sizes.weight_bytes / 1e9:.2f} GB (MXFP4 experts)")
+        r4 = run_workload(e4, c4, K, Wm, not args.no_trace, False)
+        r4["weights"] = "MXFP4 routed and shared experts (e2m1, e8m0 scale per 32); everything else as the FP8 stack"
+        results.append(r4)
+        del e4, s4
+        torch.cuda.empty_cache()
     h = results[0]
     tpot = h["resident"]["ms_per_step"] / 1e3
     bytes_mean = h["bytes_per_token"]

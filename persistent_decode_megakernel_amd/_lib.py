@@ -6,7 +6,8 @@ import os
 
 MAX_LAYERS = 128
 STATIC_SCRATCH_BYTES = 32 << 20
-ABI_VERSION = 2
+ABI_VERSION = 3
+FMT_FP8, FMT_MXFP4 = 0, 1
 
 LIB_DIR = os.path.join(os.path.dirname(os.path.abspath(__file__)), "_lib")
 LIB_PATH = os.path.join(LIB_DIR, "libpdm.so")
@@ -37,7 +38,8 @@ class Dims(C.Structure):
                 ("v_head", C.c_int32), ("ffn", C.c_int32), ("n_experts", C.c_int32),
                 ("moe_ffn", C.c_int32), ("top_k", C.c_int32), ("n_shared", C.c_int32),
                 ("vocab", C.c_int32), ("n_layers", C.c_int32),
-                ("layer_moe", C.c_uint8 * MAX_LAYERS), ("rms_eps", C.c_float), ("rope_base", C.c_float)]
+                ("layer_moe", C.c_uint8 * MAX_LAYERS), ("rms_eps", C.c_float), ("rope_base", C.c_float),
+                ("expert_format", C.c_int32)]
 
 
 class Sizes(C.Structure):
@@ -65,7 +67,8 @@ class StageInfo(C.Structure):
 
 class PackedMatrix(C.Structure):
     _fields_ = [("codes_offset", C.c_uint64), ("scales_offset", C.c_uint64), ("rows", C.c_int32),
-                ("K", C.c_int32), ("n_kblocks", C.c_int32), ("parts", C.c_int32)]
+                ("K", C.c_int32), ("n_kblocks", C.c_int32), ("parts", C.c_int32), ("format", C.c_int32),
+                ("pad", C.c_int32)]
 
 
 _P = C.c_void_p
@@ -78,10 +81,12 @@ _SIGS = {
     "pdm_bind": (C.c_int, [_P, _P, C.c_uint64, _P, C.c_uint64, _P, C.c_uint64, _P, C.c_uint64]),
     "pdm_bind_static": (C.c_int, [_P, _P, C.c_uint64, _P, C.c_uint64]),
     "pdm_load_fp8": (C.c_int, [_P, C.c_int32, C.c_int32, C.c_int32, _P, _P, _P]),
+    "pdm_load_mxfp4": (C.c_int, [_P, C.c_int32, C.c_int32, C.c_int32, _P, _P, _P]),
     "pdm_load_raw": (C.c_int, [_P, C.c_int32, C.c_int32, C.c_int32, _P, C.c_uint64, _P]),
     "pdm_load_packed_weights": (C.c_int, [_P, _P, C.c_uint64, C.c_int, _P]),
     "pdm_pack_header": (C.c_int, [C.POINTER(Dims), _P, C.c_uint64]),
     "pdm_pack_fp8": (C.c_int, [C.POINTER(Dims), C.c_int32, C.c_int32, C.c_int32, _P, _P, _P, C.c_uint64]),
+    "pdm_pack_mxfp4": (C.c_int, [C.POINTER(Dims), C.c_int32, C.c_int32, C.c_int32, _P, _P, _P, C.c_uint64]),
     "pdm_pack_raw": (C.c_int, [C.POINTER(Dims), C.c_int32, C.c_int32, C.c_int32, _P, C.c_uint64, _P, C.c_uint64]),
     "pdm_packed_layout": (C.c_int, [C.POINTER(Dims), C.c_int32, C.c_int32, C.c_int32, C.c_int32,
                                     C.POINTER(PackedMatrix)]),
@@ -145,4 +150,5 @@ def dims_of(cfg) -> Dims:
     for i, kind in enumerate(cfg.layers):
         d.layer_moe[i] = 1 if kind == "moe" else 0
     d.rms_eps, d.rope_base = cfg.rms_eps, cfg.rope_base
+    d.expert_format = FMT_MXFP4 if getattr(cfg, "expert_format", "fp8") == "mxfp4" else FMT_FP8
     return d

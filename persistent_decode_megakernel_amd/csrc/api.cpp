@@ -114,6 +114,7 @@ int bind_buffers(pdm_engine* e, void* weights_dev, uint64_t weight_bytes, void* 
 struct PackTarget {
   PackMap m;
   uint64_t codes, scales;
+  int fmt;  // PDM_FMT_* of the packed matrix
 };
 int pack_targets(const pdm_dims& d, const Plan& p, int32_t tensor, int32_t layer, int32_t expert, PackTarget* t,
                  int* n) {
@@ -128,6 +129,7 @@ int pack_targets(const pdm_dims& d, const Plan& p, int32_t tensor, int32_t layer
     x.m.row0 = row0; x.m.which = which; x.m.dn = d.qk_nope; x.m.dv = d.v_head; x.m.dc = d.kv_lora;
     x.codes = base + dst.codes;
     x.scales = base + dst.scales;
+    x.fmt = dst.fmt;
   };
   if (expert >= 0) {
     if (!moe || expert >= d.n_experts + d.n_shared) return PDM_ERR_ARG;
@@ -351,6 +353,7 @@ int pdm_load_fp8(pdm_engine* e, int32_t tensor, int32_t layer, int32_t expert, c
   int n = 0;
   rc = pack_targets(e->dims, e->plan, tensor, layer, expert, t, &n);
   if (rc) return rc;
+  if (t[0].fmt != PDM_FMT_FP8) return PDM_ERR_ARG;
   DeviceGuard g(e->device);
   for (int i = 0; i < n; ++i) {
     rc = hip_fail(launch_pack(codes_dev, scales_dev, e->w + t[i].codes, reinterpret_cast<uint16_t*>(e->w + t[i].scales),
@@ -358,6 +361,23 @@ int pdm_load_fp8(pdm_engine* e, int32_t tensor, int32_t layer, int32_t expert, c
     if (rc) return rc;
   }
   return PDM_OK;
+}
+
+int pdm_load_mxfp4(pdm_engine* e, int32_t tensor, int32_t layer, int32_t expert, const uint8_t* codes_dev,
+                   const uint8_t* scales_dev, pdm_stream_t stream) {
+  int rc = check_engine(e, true);
+  if (rc) return rc;
+  if (!codes_dev || !scales_dev) return PDM_ERR_ARG;
+  PackTarget t[2];
+  int n = 0;
+  rc = pack_targets(e->dims, e->plan, tensor, layer, expert, t, &n);
+  if (rc) return rc;
+  if (t[0].fmt != PDM_FMT_MXFP4) return PDM_ERR_ARG;
+  DeviceGuard g(e->device);
+  const PackMap& m = t[0].m;
+  rc = hip_fail(launch_pack_rows(codes_dev, e->w + t[0].codes, m, m.Kp, (hipStream_t)stream));
+  if (!rc) rc = hip_fail(launch_pack_rows(scales_dev, e->w + t[0].scales, m, m.nkb, (hipStream_t)stream));
+  return rc;
 }
 
 int pdm_load_raw(pdm_engine* e, int32_t tensor, int32_t layer, int32_t expert, const void* src_dev, uint64_t bytes,
@@ -412,6 +432,7 @@ int pdm_pack_fp8(const pdm_dims* dims, int32_t tensor, int32_t layer, int32_t ex
   int n = 0;
   int rc = pack_targets(*dims, *hp.p, tensor, layer, expert, t, &n);
   if (rc) return rc;
+  if (t[0].fmt != PDM_FMT_FP8) return PDM_ERR_ARG;
   uint8_t* a = static_cast<uint8_t*>(arena);
   for (int i = 0; i < n; ++i) {
     const PackMap& m = t[i].m;
@@ -426,6 +447,29 @@ int pdm_pack_fp8(const pdm_dims* dims, int32_t tensor, int32_t layer, int32_t ex
       for (int kb = 0; kb < m.nkb; ++kb)
         if (pack_src(m, rg * 8, kb * 128, sr, sc)) ds[(size_t)rg * m.nkb + kb] = scales[(size_t)(sr / 128) * skb + sc / 128];
   }
+  return PDM_OK;
+}
+
+int pdm_pack_mxfp4(const pdm_dims* dims, int32_t tensor, int32_t layer, int32_t expert, const uint8_t* codes,
+                   const uint8_t* scales, void* arena, uint64_t arena_bytes) {
+  HostPlan hp(dims);
+  if (hp.rc) return hp.rc;
+  if (!codes || !scales || !arena) return PDM_ERR_ARG;
+  if (arena_bytes < hp.lay.weight_bytes) return PDM_ERR_SIZE;
+  PackTarget t[2];
+  int n = 0;
+  int rc = pack_targets(*dims, *hp.p, tensor, layer, expert, t, &n);
+  if (rc) return rc;
+  if (t[0].fmt != PDM_FMT_MXFP4) return PDM_ERR_ARG;
+  const PackMap& m = t[0].m;
+  uint8_t* a = static_cast<uint8_t*>(arena);
+  int sr = 0, sc = 0;
+  // whole rows: K / 2 code bytes and K / 32 scale bytes per row
+  for (int r = 0; r < m.rows; ++r)
+    if (pack_src(m, r, 0, sr, sc)) {
+      std::memcpy(a + t[0].codes + (size_t)r * m.Kp, codes + (size_t)sr * m.Kp, (size_t)m.Kp);
+      std::memcpy(a + t[0].scales + (size_t)r * m.nkb, scales + (size_t)sr * m.nkb, (size_t)m.nkb);
+    }
   return PDM_OK;
 }
 
@@ -459,6 +503,7 @@ int pdm_packed_layout(const pdm_dims* dims, int32_t tensor, int32_t layer, int32
   out->K = t[part].m.Kp;
   out->n_kblocks = t[part].m.nkb;
   out->parts = n;
+  out->format = t[part].fmt;
   return PDM_OK;
 }
 
@@ -533,7 +578,7 @@ int pdm_decode_step(pdm_engine* e, int32_t token, int32_t pos, const uint16_t* x
   a.argmax = d.vocab > 0 ? argmax_dev : nullptr;
   a.trace = e->trace_on ? e->trace : nullptr;
   DeviceGuard g(e->device);
-  hipError_t err = launch_engine(e->plan_dev, a, e->G, (hipStream_t)stream, e->cooperative);
+  hipError_t err = launch_engine(e->plan_dev, a, e->G, e->dims.expert_format, (hipStream_t)stream, e->cooperative);
   if (err != hipSuccess) return PDM_ERR_LAUNCH;
   e->epoch = a.epoch;
   for (int l = 0; l < d.n_layers; ++l) e->layer_len[l] = pos + 1;
@@ -563,7 +608,7 @@ int pdm_decode_steps(pdm_engine* e, int32_t pos0, int32_t n_steps, const int32_t
   a.argmax = argmax_dev;
   a.trace = e->trace_on ? e->trace : nullptr;
   DeviceGuard g(e->device);
-  hipError_t err = launch_engine(e->plan_dev, a, e->G, (hipStream_t)stream, e->cooperative);
+  hipError_t err = launch_engine(e->plan_dev, a, e->G, e->dims.expert_format, (hipStream_t)stream, e->cooperative);
   if (err != hipSuccess) return PDM_ERR_LAUNCH;
   e->epoch += (uint32_t)n_steps;
   for (int l = 0; l < d.n_layers; ++l) e->layer_len[l] = pos0 + n_steps;

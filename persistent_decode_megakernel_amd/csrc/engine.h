@@ -28,10 +28,14 @@ struct LaunchArgs {
 
 // Row/column map of the offline packer (see engine.hip, pack_codes_kernel).
 
-hipError_t launch_engine(const Plan* plan_dev, const LaunchArgs& a, int G, hipStream_t stream, bool cooperative);
+// One persistent launch; expert_format (PDM_FMT_*) picks the kernel instance.
+hipError_t launch_engine(const Plan* plan_dev, const LaunchArgs& a, int G, int expert_format, hipStream_t stream,
+                         bool cooperative);
 hipError_t launch_rope_table(float* tab, int max_ctx, int rope, double base, hipStream_t stream);
 hipError_t launch_pack(const uint8_t* src_codes, const uint16_t* src_scales, uint8_t* dst_codes,
                        uint16_t* dst_scales, const PackMap& m, hipStream_t stream);
+// Whole-row copy by the pack map (MXFP4 codes or scales): row_bytes per row.
+hipError_t launch_pack_rows(const uint8_t* src, uint8_t* dst, const PackMap& m, int row_bytes, hipStream_t stream);
 hipError_t launch_zero(void* p, size_t bytes, hipStream_t stream);
 // Device address of the library's static scratch array on `device`
 // (PDM_STATIC_SCRATCH_BYTES), looked up once per device.

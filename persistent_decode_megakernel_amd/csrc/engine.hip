@@ -33,6 +33,7 @@ namespace pdm {
 namespace {
 
 constexpr int kUnroll = 5;  // 1 KB units in flight per wave and buffer
+constexpr int kUnrollMx = 3;  // the same for MXFP4 units
 constexpr int kEarlyBatches = 1;       // unit batches per wave issued before a stage's dependency wait
 // The last wave of a workgroup polls the dependency counters and issues no
 // load before the wait: loads complete in order per wave, so a poll issued
@@ -77,7 +78,7 @@ __device__ __forceinline__ void gst(T* p, T v) { *gpw(p) = v; }
 // Weight matrix of one expert slot: FP8 codes and their block scales.
 struct __align__(16) SlotRef {
   const uint8_t* codes;
-  const uint16_t* scales;
+  const uint8_t* scales;  // bf16 block scales (FP8) or e8m0 bytes (MXFP4)
 };
 
 struct __align__(16) Smem {
@@ -102,6 +103,18 @@ struct __align__(16) Smem {
 // ------------------------------------------------------------------ helpers
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+// The thread and lane index as values the compiler cannot see through (an
+// empty asm that claims to change them): the MXFP4 stage code uses them so
+// that what it derives from them is computed in the stage, not hoisted out of
+// the step loop to the kernel entry, where each value would hold a register
+// for the whole kernel (the hoisting pays for the FP8 stages; for the two
+// MXFP4 stages it made the kernel run out of registers).
+__device__ __forceinline__ int opaque_tid() {
+  int t = threadIdx.x;
+  asm volatile("" : "+v"(t));
+  return t;
+}
+__device__ __forceinline__ int opaque_lane() { return opaque_tid() & 63; }
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
 __device__ __forceinline__ float ld_coh(const float* p) {
@@ -402,13 +415,22 @@ struct Gemv {
   int split;
 };
 
-// Address of the 16 bytes a lane reads for (row, byte offset b) and its scale.
+// Address of the 16 bytes a lane reads for (row, byte offset b) and of its
+// scale: FP8 (EB 1) a bf16 block scale, one per 8 rows and 128 bytes; MXFP4
+// (EB 0, slot matrices only) the e8m0 byte of its 32 elements (its 16 bytes).
+template <int EB>
+__device__ __forceinline__ const uint8_t* scale_ptr(const uint8_t* scales, int nkb, int row, int b) {
+  if constexpr (EB == 0) return scales + (size_t)row * nkb + (b >> 4);
+  return reinterpret_cast<const uint8_t*>(reinterpret_cast<const uint16_t*>(scales) + (size_t)(row >> 3) * nkb +
+                                          (b >> 7));
+}
 template <int EB, int SLOT>
 __device__ __forceinline__ void unit_ptr_t(const Gemv& g, const Smem& sm, int row, int b,
-                                           const uint8_t*& cp, const uint16_t*& sp) {
+                                           const uint8_t*& cp, const uint8_t*& sp) {
+  static_assert(EB != 0 || SLOT != 0, "MXFP4 matrices are expert slots");
   if constexpr (SLOT == 0) {
     cp = g.codes + (size_t)row * g.Kb + b;
-    if (EB == 1) sp = g.scales + (size_t)(row >> 3) * g.nkb + (b >> 7);
+    if (EB == 1) sp = scale_ptr<1>(reinterpret_cast<const uint8_t*>(g.scales), g.nkb, row, b);
   } else if constexpr (SLOT == 1 || SLOT == 3) {
     int pr = row;
     if constexpr (SLOT == 3) pr = row < g.seg_n1 ? g.seg_p1 + row : g.seg_p2 + (row - g.seg_n1);
@@ -416,13 +438,13 @@ __device__ __forceinline__ void unit_ptr_t(const Gemv& g, const Smem& sm, int ro
     int rr = pr & ((1 << g.lg_slot) - 1);
     const SlotRef sr = sm.slot[j];
     cp = sr.codes + (size_t)rr * g.slot_Kb + b;
-    if (EB == 1) sp = sr.scales + (size_t)(rr >> 3) * g.nkb + (b >> 7);
+    if (EB != 2) sp = scale_ptr<EB>(sr.scales, g.nkb, rr, b);
   } else {
     int j = b >> g.lg_slot;
     int bb = b & ((1 << g.lg_slot) - 1);
     const SlotRef sr = sm.slot[j];
     cp = sr.codes + (size_t)row * g.slot_Kb + bb;
-    if (EB == 1) sp = sr.scales + (size_t)(row >> 3) * g.nkb + (bb >> 7);
+    if (EB != 2) sp = scale_ptr<EB>(sr.scales, g.nkb, row, bb);
   }
 }
 
@@ -437,10 +459,20 @@ static_assert(kXMax % 1024 == 0, "staged vectors occupy whole 1024-float blocks"
 __device__ __forceinline__ int xperm(int k) {
   return (k & ~1023) | (((k >> 2) & 3) << 8) | (((k >> 4) & 63) << 2) | (k & 3);
 }
-// xperm of a group start: k a multiple of 16 (FP8 units) or of 8 (bf16 units)
+// MXFP4 stages stage their input in blocks of 2048 floats instead (a lane's
+// 16 code bytes hold 32 elements): float k = 32 l + 4 i + e of a block at
+// float 256 i + 4 l + e, so the lane's eight float4 reads are again 1 KB apart
+// and the lanes of a wave read consecutive float4s.
+static_assert(kXMax % 2048 == 0, "MXFP4-staged vectors occupy whole 2048-float blocks");
+__device__ __forceinline__ int xperm4(int k) {
+  return (k & ~2047) | (((k >> 2) & 7) << 8) | (((k >> 5) & 63) << 2) | (k & 3);
+}
+// xperm (xperm4 for EB 0) of a group start: k a multiple of 16 (FP8 units),
+// of 8 (bf16 units) or of 32 (MXFP4 units)
 template <int EB>
 __device__ __forceinline__ int xperm_group(int k) {
-  if constexpr (EB == 1) return (k & ~1023) | ((k >> 2) & 252);
+  if constexpr (EB == 0) return (k & ~2047) | ((k >> 3) & 252);
+  else if constexpr (EB == 1) return (k & ~1023) | ((k >> 2) & 252);
   else return (k & ~1023) | ((k & 8) << 6) | ((k >> 2) & 252);
 }
 
@@ -477,6 +509,42 @@ __device__ __forceinline__ float unit_dot(const u32x4& w, const float* xs) {
 }
 
 
+// dot of one lane's 16 MXFP4 code bytes (32 elements of one scale block,
+// element 2j in the low nibble of byte j) with the staged input (xperm4
+// order; xs = sm.x + xperm_group<0>(k0)). The hardware conversion applies the
+// block scale: each converted value is exactly e2m1 * 2^(s - 127).
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ float e8m0_value(uint32_t s) {
+  // 2^(s - 127) as an fp32 bit pattern; s = 0 is the subnormal 2^-127
+  return __builtin_bit_cast(float, s ? s << 23 : 0x00400000u);
+}
+__device__ __forceinline__ float unit_dot_mx(const u32x4& w, const float* xs, float scale) {
+  const float4* x4 = reinterpret_cast<const float4*>(xs);
+  const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+  // two accumulators: 32 products per lane would otherwise be one chain of
+  // dependent FMAs
+  float acc0 = 0.f, acc1 = 0.f;
+  // word q holds elements 8q .. 8q+7, two per byte (the byte index is an
+  // immediate of the conversion); they meet float4s 2q and 2q + 1
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const f32x2 e0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4((int)ws[q], scale, 0);
+    const f32x2 e1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4((int)ws[q], scale, 1);
+    const f32x2 e2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4((int)ws[q], scale, 2);
+    const f32x2 e3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4((int)ws[q], scale, 3);
+    const float4 xa = x4[64 * (2 * q)], xb = x4[64 * (2 * q + 1)];
+    acc0 = fmaf(e0[0], xa.x, acc0);
+    acc0 = fmaf(e0[1], xa.y, acc0);
+    acc0 = fmaf(e1[0], xa.z, acc0);
+    acc0 = fmaf(e1[1], xa.w, acc0);
+    acc1 = fmaf(e2[0], xb.x, acc1);
+    acc1 = fmaf(e2[1], xb.y, acc1);
+    acc1 = fmaf(e3[0], xb.z, acc1);
+    acc1 = fmaf(e3[1], xb.w, acc1);
+  }
+  return acc0 + acc1;
+}
+
 // Sum within aligned groups of 2^lg lanes (lg <= 6) without branches.
 __device__ __forceinline__ float group_sum_lg(float v, int lg) {
   v += lg >= 1 ? dpp<kDppXor1>(v) : 0.f;
@@ -509,11 +577,21 @@ struct NoLate {
 // input vector, so a unit's validity is the same for all lanes and its input
 // floats are at a lane-fixed LDS offset: every per-unit address term but the
 // lane's own is uniform (scalar arithmetic).
-template <int EB, bool LONG, int SLOT, bool FULL, class Prep, class Late>
+//
+// PAIR (MXFP4 only; rows of whole 512-byte pieces, an even row count, one
+// input vector): a unit is 512 bytes of each of two consecutive rows, lanes
+// 0-31 on the first and 32-63 on the second, at the same columns. Every lane
+// is valid for any such row length (MXFP4 gate/up rows of 3584 bytes are not
+// whole KB) and the two halves of a wave read the same staged inputs.
+template <int EB, bool LONG, int SLOT, bool FULL, bool PAIR, class Prep, class Late>
 __device__ __forceinline__ bool gemv_rows_t(const Gemv& g, Smem& sm, int ra, int rb, bool early, Prep&& prep,
                                             Late&& late) {
   static_assert(LONG || !FULL, "whole-KB rows are long rows");
-  const int lane = lane_id();
+  static_assert(!PAIR || (EB == 0 && LONG && !FULL), "row pairs are an MXFP4 long-row mode");
+  // units per batch: an MXFP4 unit carries twice the elements of an FP8 one
+  // (and twice the staged input reads), so its batches are shorter
+  constexpr int U = EB == 0 ? kUnrollMx : kUnroll;
+  const int lane = EB == 0 ? opaque_lane() : lane_id();
   const int w = wave_id();
   const int kb = g.Kb;
   int S = 1, m = 1, lg_lpr = 0;
@@ -522,14 +600,17 @@ __device__ __forceinline__ bool gemv_rows_t(const Gemv& g, Smem& sm, int ra, int
     m = 1024 / kb;
     lg_lpr = 31 - __builtin_clz(kb >> 4);
     nunits = (rb - ra) / m;
+  } else if constexpr (PAIR) {
+    S = kb >> 9;  // 512-byte pieces per row
+    nunits = ((rb - ra) >> 1) * S;
   } else {
     S = (kb + 1023) >> 10;
     nunits = (rb - ra) * S;
   }
-  // Units go out in batches of kUnroll. Wave w takes batch w first (issued
+  // Units go out in batches of U. Wave w takes batch w first (issued
   // before the dependency wait when early); later batches are claimed from an
   // LDS counter, so waves whose loads return sooner stream more of the rows.
-  const int nbat = (nunits + kUnroll - 1) / kUnroll;
+  const int nbat = (nunits + U - 1) / U;
   const int lpr_mask = (1 << lg_lpr) - 1;
   // u / S by multiply-high (exact for u < 2^32 / S)
   const uint32_t magic = S == 1 ? 0u : 0xFFFFFFFFu / (uint32_t)S + 1u;
@@ -540,20 +621,26 @@ __device__ __forceinline__ bool gemv_rows_t(const Gemv& g, Smem& sm, int ra, int
     return __builtin_amdgcn_readlane(v, 0);
   };
 
-  // A batch: each lane's 16 code bytes of kUnroll units and, for FP8, the
+  // A batch: each lane's 16 code bytes of U units and, for FP8, the
   // block scale each 16 bytes belong to, loaded alongside (the scale lines of
   // a row group are shared by its 8 rows and come from cache after the first).
-  u32x4 wa[kUnroll], wb[kUnroll];
-  uint32_t sa[kUnroll], sb[kUnroll];
+  u32x4 wa[U], wb[U];
+  uint32_t sa[U], sb[U];
   auto issue = [&](u32x4* W, uint32_t* SC, int bt) {
-    const int ub = bt * kUnroll;
+    const int ub = bt * U;
     int i_row = 0, i_seg = 0;
     if constexpr (LONG) { i_row = div_s(ub); i_seg = ub - i_row * S; }
 #pragma unroll
-    for (int j = 0; j < kUnroll; ++j) {
+    for (int j = 0; j < U; ++j) {
       const int u = ub + j;
       int row, b;
-      if constexpr (LONG) {
+      if constexpr (PAIR) {
+        row = ra + 2 * i_row + (lane >> 5);
+        b = (i_seg << 9) + ((lane & 31) << 4);
+        const bool wrap = i_seg + 1 == S;
+        i_row += wrap ? 1 : 0;
+        i_seg = wrap ? 0 : i_seg + 1;
+      } else if constexpr (LONG) {
         row = ra + i_row;
         b = (i_seg << 10) + (lane << 4);
         const bool wrap = i_seg + 1 == S;
@@ -563,30 +650,37 @@ __device__ __forceinline__ bool gemv_rows_t(const Gemv& g, Smem& sm, int ra, int
         row = ra + u * m + (lane >> lg_lpr);
         b = (lane & lpr_mask) << 4;
       }
-      const bool ok = u < nunits && (FULL || b < kb);
+      const bool ok = u < nunits && (FULL || PAIR || b < kb);
       const uint8_t* cp;
-      const uint16_t* sp = nullptr;
+      const uint8_t* sp = nullptr;
       unit_ptr_t<EB, SLOT>(g, sm, ok ? row : ra, ok ? b : 0, cp, sp);
       W[j] = __builtin_nontemporal_load(gp(reinterpret_cast<const u32x4*>(cp)));
-      if constexpr (EB == 1) SC[j] = gld(sp);
+      if constexpr (EB == 1) SC[j] = gld(reinterpret_cast<const uint16_t*>(sp));
+      if constexpr (EB == 0) SC[j] = gld(sp);
     }
   };
 
   // LONG rows span several units and possibly several batches (and waves):
   // each wave adds its share of a row into its own partial.
   auto compute = [&](const u32x4* W, const uint32_t* SC, int bt) {
-    const int ub = bt * kUnroll;
+    const int ub = bt * U;
     int c_row = 0, c_seg = 0;
     if constexpr (LONG) { c_row = div_s(ub); c_seg = ub - c_row * S; }
-    int cur_row = ra + c_row;
+    int cur_row = ra + (PAIR ? 2 * c_row : c_row);  // PAIR: the pair's first row
     float acc = 0.f;
 #pragma unroll
-    for (int j = 0; j < kUnroll; ++j) {
+    for (int j = 0; j < U; ++j) {
       const int u = ub + j;
       const bool uok = u < nunits;
       int row, b;
       const int seg = c_seg;
-      if constexpr (LONG) {
+      if constexpr (PAIR) {
+        row = ra + 2 * c_row;
+        b = (c_seg << 9) + ((lane & 31) << 4);
+        const bool wrap = c_seg + 1 == S;
+        c_row += wrap ? 1 : 0;
+        c_seg = wrap ? 0 : c_seg + 1;
+      } else if constexpr (LONG) {
         row = ra + c_row;
         b = (c_seg << 10) + (lane << 4);
         const bool wrap = c_seg + 1 == S;
@@ -596,20 +690,27 @@ __device__ __forceinline__ bool gemv_rows_t(const Gemv& g, Smem& sm, int ra, int
         row = ra + u * m + (lane >> lg_lpr);
         b = (lane & lpr_mask) << 4;
       }
-      const bool ok = uok && (FULL || b < kb);
+      const bool ok = uok && (FULL || PAIR || b < kb);
       const float* xs;
-      if constexpr (FULL) {
-        // xperm_group of (seg * 1024 + 16 * lane) (FP8) or (seg * 512 + 8 * lane) (bf16)
+      if constexpr (PAIR) {
+        // xperm4 of element 1024 seg + 32 (lane & 31)
+        xs = sm.x + ((seg >> 1) << 11) + ((((seg & 1) << 5) | (lane & 31)) << 2);
+      } else if constexpr (FULL) {
+        // xperm_group of (seg * 1024 + 16 * lane) (FP8), (seg * 512 + 8 * lane)
+        // (bf16) or xperm4 of (seg * 2048 + 32 * lane) (MXFP4)
         xs = sm.x + (EB == 1 ? (seg << 10) + (lane << 2)
-                             : ((seg >> 1) << 10) + ((lane & 1) << 9) + ((seg & 1) << 7) + ((lane >> 1) << 2));
+                     : EB == 0 ? (seg << 11) + (lane << 2)
+                               : ((seg >> 1) << 10) + ((lane & 1) << 9) + ((seg & 1) << 7) + ((lane >> 1) << 2));
       } else {
         const int bq = ok ? b : 0;
         const int rq = ok ? row : ra;
-        const int k0 = (EB == 1) ? bq : (bq >> 1);
+        const int k0 = (EB == 1) ? bq : (EB == 2) ? (bq >> 1) : (bq << 1);
         const int xoff = (g.lg_rpv >= 31) ? 0 : ((rq >> g.lg_rpv) - g.vbase) * g.xK;
         xs = sm.x + xperm_group<EB>(xoff + k0);
       }
-      float d = unit_dot<EB>(W[j], xs);
+      float d;
+      if constexpr (EB == 0) d = unit_dot_mx(W[j], xs, e8m0_value(SC[j]));
+      else d = unit_dot<EB>(W[j], xs);
       if constexpr (EB == 1) d *= bf16_val((uint16_t)SC[j]);
       d = ok ? d : 0.f;
       if constexpr (LONG) {
@@ -620,7 +721,8 @@ __device__ __forceinline__ bool gemv_rows_t(const Gemv& g, Smem& sm, int ra, int
         if (uok && row != cur_row) {
           const float t = row16_sum(acc);
           if ((lane & 15) == 0)
-            __hip_atomic_fetch_add(&sm.part[w][cur_row - ra], t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            __hip_atomic_fetch_add(&sm.part[w][cur_row - ra + (PAIR ? lane >> 5 : 0)], t, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_WORKGROUP);
           acc = 0.f;
           cur_row = row;
         }
@@ -633,7 +735,8 @@ __device__ __forceinline__ bool gemv_rows_t(const Gemv& g, Smem& sm, int ra, int
     if constexpr (LONG) {
       const float t = row16_sum(acc);
       if ((lane & 15) == 0)
-        __hip_atomic_fetch_add(&sm.part[w][cur_row - ra], t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        __hip_atomic_fetch_add(&sm.part[w][cur_row - ra + (PAIR ? lane >> 5 : 0)], t, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_WORKGROUP);
     }
   };
 
@@ -644,7 +747,9 @@ __device__ __forceinline__ bool gemv_rows_t(const Gemv& g, Smem& sm, int ra, int
   // go out before prep.
   constexpr int kStat = kWaves - 1;  // waves with static batches (not the polling wave)
   int bA = w < kStat ? w : nbat, bB = kEarlyBatches == 2 && w < kStat ? w + kStat : nbat;
-  const int ebat = !early ? 0 : !g.split ? nbat : min(nbat, (LONG ? g.seg_n1 * S : g.seg_n1 / m) / kUnroll);
+  // (first-segment units: S per row, S per row pair, or one per m rows)
+  const int ebat = !early ? 0 : !g.split ? nbat
+                 : min(nbat, (PAIR ? (g.seg_n1 >> 1) * S : LONG ? g.seg_n1 * S : g.seg_n1 / m) / U);
   if (bA < ebat) issue(wa, sa, bA);
   if (kEarlyBatches == 2 && bB < ebat) issue(wb, sb, bB);
   if (!prep()) return false;
@@ -698,9 +803,15 @@ template <int EB, int SLOT, class Prep, class Late>
 __device__ __forceinline__ bool gemv_rows(const Gemv& g, Smem& sm, int ra, int rb, bool early, Prep&& prep,
                                           Late&& late) {
   const bool small = g.Kb < 1024 && (1024 % g.Kb) == 0;
-  if (small) return gemv_rows_t<EB, false, SLOT, false>(g, sm, ra, rb, early, prep, late);
-  if ((g.Kb & 1023) == 0 && g.lg_rpv >= 31) return gemv_rows_t<EB, true, SLOT, true>(g, sm, ra, rb, early, prep, late);
-  return gemv_rows_t<EB, true, SLOT, false>(g, sm, ra, rb, early, prep, late);
+  if (small) return gemv_rows_t<EB, false, SLOT, false, false>(g, sm, ra, rb, early, prep, late);
+  if ((g.Kb & 1023) == 0 && g.lg_rpv >= 31)
+    return gemv_rows_t<EB, true, SLOT, true, false>(g, sm, ra, rb, early, prep, late);
+  if constexpr (EB == 0) {
+    // MXFP4 rows of whole 512-byte pieces (the gate/up rows): row pairs
+    if ((g.Kb & 511) == 0 && g.lg_rpv >= 31 && ((rb - ra) & 1) == 0 && (SLOT != 2 || (g.slot_Kb & 511) == 0))
+      return gemv_rows_t<EB, true, SLOT, false, true>(g, sm, ra, rb, early, prep, late);
+  }
+  return gemv_rows_t<EB, true, SLOT, false, false>(g, sm, ra, rb, early, prep, late);
 }
 
 // Balanced contiguous share of `rows` (in groups of `gran`) for workgroup wg.
@@ -804,10 +915,12 @@ __device__ __forceinline__ float4 ld_vec4(__amdgpu_buffer_rsrc_t r, int i4) {
 // x_lds = v (gain null) or v * gain, v = src[0, K) loaded coherently. Returns
 // this thread's sum of squares of v. Whether a batch slot has any element is
 // the same for the whole workgroup, so only the loads a vector needs are issued.
+template <bool MX = false>  // MX: xperm4 order (MXFP4 stages)
 __device__ __forceinline__ float stage_vec(Smem& sm, int K, const float* src, const float* gain) {
   const __amdgpu_buffer_rsrc_t rv = vec_rsrc(src, K);
   const __amdgpu_buffer_rsrc_t rg = vec_rsrc(gain ? gain : src, K);
   const int n4 = K / 4;
+  const int tid = MX ? opaque_tid() : (int)threadIdx.x;
   float ss = 0.f;
   for (int b0 = 0; b0 < n4; b0 += kStageVec * kThreads) {
     float4 v[kStageVec], g[kStageVec];
@@ -815,16 +928,16 @@ __device__ __forceinline__ float stage_vec(Smem& sm, int K, const float* src, co
     for (int i = 0; i < kStageVec; ++i) {
       v[i] = g[i] = make_float4(0.f, 0.f, 0.f, 0.f);
       if (b0 + i * kThreads < n4) {
-        v[i] = ld_vec4<kCpolSc1>(rv, b0 + i * kThreads + threadIdx.x);
-        if (gain) g[i] = ld_vec4<0>(rg, b0 + i * kThreads + threadIdx.x);
+        v[i] = ld_vec4<kCpolSc1>(rv, b0 + i * kThreads + tid);
+        if (gain) g[i] = ld_vec4<0>(rg, b0 + i * kThreads + tid);
       }
     }
 #pragma unroll
     for (int i = 0; i < kStageVec; ++i) {
-      const int i4 = b0 + i * kThreads + threadIdx.x;
+      const int i4 = b0 + i * kThreads + tid;
       float4 y = v[i];
       if (gain) { y.x *= g[i].x; y.y *= g[i].y; y.z *= g[i].z; y.w *= g[i].w; }
-      if (i4 < n4) *reinterpret_cast<float4*>(sm.x + xperm(4 * i4)) = y;
+      if (i4 < n4) *reinterpret_cast<float4*>(sm.x + (MX ? xperm4(4 * i4) : xperm(4 * i4))) = y;
       ss += v[i].x * v[i].x + v[i].y * v[i].y + v[i].z * v[i].z + v[i].w * v[i].w;
     }
   }
@@ -836,8 +949,9 @@ __device__ __forceinline__ float stage_vec(Smem& sm, int K, const float* src, co
 // GEMV is linear in its input), so the staging needs one barrier and no
 // second pass over LDS. The per-wave sums of squares stay in sm.nred for
 // rms_scale(), also in the next stage when it reuses the staged input.
+template <bool MX = false>
 __device__ __forceinline__ void stage_norm_vec(Smem& sm, int K, const float* gain, const float* src) {
-  const float w = wave_sum(stage_vec(sm, K, src, gain));
+  const float w = wave_sum(stage_vec<MX>(sm, K, src, gain));
   if (lane_id() == 0) sm.nred[wave_id()] = w;
   __syncthreads();
 }
@@ -848,8 +962,9 @@ __device__ __forceinline__ float rms_scale(const Smem& sm, int K, float eps) {
   return 1.0f / sqrtf(t / (float)K + eps);
 }
 // stage_plain of a contiguous coherent vector
+template <bool MX = false>
 __device__ __forceinline__ void stage_plain_vec(Smem& sm, int K, const float* src) {
-  stage_vec(sm, K, src, nullptr);
+  stage_vec<MX>(sm, K, src, nullptr);
   __syncthreads();
 }
 
@@ -898,6 +1013,7 @@ struct StageEnv {
 };
 
 __device__ __forceinline__ LayerPlan layer_of(const Ctx& c, int l) { return load_plan(&c.P->layers[l]); }
+
 
 // Input of layer l: the embedding row or external hidden vector for l == 0,
 // else the previous layer's output (written this step: coherent loads).
@@ -1294,7 +1410,10 @@ __device__ __forceinline__ bool stage_attn(const StageEnv& E, Smem& sm) {
     // owns rows (with fewer row groups than workgroups some own none): the
     // planner's per-head slot mask
     uint64_t* qmask = reinterpret_cast<uint64_t*>(&sm.part[0][0]);
-    if ((int)threadIdx.x < hg) qmask[threadIdx.x] = gld(&c.P->qb_mask[grp * hg + threadIdx.x]);
+    if ((int)threadIdx.x < hg) {
+      const int t = opaque_lane();  // threads < hg <= 64 are lanes of wave 0
+      qmask[t] = gld(&c.P->qb_mask[grp * hg + t]);
+    }
     dma_to_lds_wg(tpart, reinterpret_cast<const float*>(L.qlat_part) + (size_t)grp * hg * maxp * dc, hg * maxp * dc * 4);
     if (wave_id() == kPollWave) {
       dma_to_lds(trope, reinterpret_cast<const uint16_t*>(L.qrope) + (size_t)grp * 2 * hg * dr, 2 * hg * dr * 2);
@@ -1691,7 +1810,7 @@ __device__ __forceinline__ void route_wave_t(const pdm_dims& d, Smem& sm, const 
     }
     const int t = d.n_shared + lane;
     const uint8_t* base = reinterpret_cast<const uint8_t*>(L.expert_base) + (size_t)my_e * L.expert_stride;
-    sm.slot[t] = SlotRef{base + L.egu.codes, reinterpret_cast<const uint16_t*>(base + L.egu.scales)};
+    sm.slot[t] = SlotRef{base + L.egu.codes, base + L.egu.scales};
     sm.slot_w[t] = my_w;
     sm.slot_act[t] = lane * d.moe_ffn;
   }
@@ -1718,7 +1837,7 @@ __device__ __forceinline__ void set_slots(const pdm_dims& d, const LayerPlan& L,
     const int e = is_shared ? d.n_experts + i : sm.route_idx[i];
     const uint8_t* base = reinterpret_cast<const uint8_t*>(L.expert_base) + (size_t)e * L.expert_stride;
     const Fp8Mat& m = down ? L.edown : L.egu;
-    sm.slot[t] = SlotRef{base + m.codes, reinterpret_cast<const uint16_t*>(base + m.scales)};
+    sm.slot[t] = SlotRef{base + m.codes, base + m.scales};
     sm.slot_w[t] = down || is_shared ? 1.f : sm.route_w[i];
     sm.slot_act[t] = (is_shared ? k + i : i) * d.moe_ffn;
   }
@@ -1759,7 +1878,9 @@ __device__ __forceinline__ bool stage_gu(const StageEnv& E, Smem& sm) {
 // go out before the wait for the router logits and stream while this
 // workgroup computes the top-k. The router stage this workgroup ran last
 // already staged RMSNorm(x_attn) in LDS (kStXStaged).
-__device__ __forceinline__ bool stage_gu_moe(const StageEnv& E, Smem& sm) {
+// EB: 1 FP8 experts, 0 MXFP4 experts (input staged in xperm4 order).
+template <int EB>
+__device__ __forceinline__ bool stage_gu_moe_t(const StageEnv& E, Smem& sm) {
   const Ctx& c = E.c;
   const pdm_dims d = load_plan(&c.P->dims);
   const LayerPlan L = layer_of(c, E.st.layer);
@@ -1769,10 +1890,10 @@ __device__ __forceinline__ bool stage_gu_moe(const StageEnv& E, Smem& sm) {
   const int rows_sh = 2 * F * d.n_shared;  // row slots [0, n_shared) hold the shared experts
   Gemv g{};
   g.lg_rpv = 31;
-  g.Kb = d.hidden;
+  g.Kb = EB == 0 ? d.hidden / 2 : d.hidden;
   g.slot_mode = 1;
   g.lg_slot = 31 - __builtin_clz(2 * F);
-  g.slot_Kb = d.hidden;
+  g.slot_Kb = g.Kb;
   g.nkb = L.egu.nkb;
   int p1, e1, p2, e2;
   my_rows(rows_sh, E.st.gran, c.G, c.wg, p1, e1);
@@ -1787,10 +1908,10 @@ __device__ __forceinline__ bool stage_gu_moe(const StageEnv& E, Smem& sm) {
   if (threadIdx.x == 0) sm.slots_ready = 0;
   __syncthreads();
   float rs = 1.f;  // 1 / rms of x_attn, applied to the product
-  return run_gemv<1, 3>(E, sm, g, 0, n, true,
+  return run_gemv<EB, 3>(E, sm, g, 0, n, true,
       [&]() {
         if (!wait_stage(c, sm, E.st.wait, E.s)) return false;
-        if (!reuse) stage_norm_vec(sm, d.hidden, reinterpret_cast<const float*>(L.ffn_norm), xa);
+        if (!reuse) stage_norm_vec<EB == 0>(sm, d.hidden, reinterpret_cast<const float*>(L.ffn_norm), xa);
         rs = rms_scale(sm, d.hidden, d.rms_eps);  // with reuse: the router stage's sums
         return true;
       },
@@ -1810,8 +1931,11 @@ __device__ __forceinline__ bool stage_gu_moe(const StageEnv& E, Smem& sm) {
       [&]() { route_wave(d, sm, L, c.wg == 0); });
 }
 
+
 // --- DOWN: x_out = bf16(x_attn + sum_slots W_down[slot] act[slot])
-__device__ __forceinline__ bool stage_down(const StageEnv& E, Smem& sm) {
+// EB 0: the MoE layer's experts are MXFP4 (input staged in xperm4 order)
+template <int EB>
+__device__ __forceinline__ bool stage_down_t(const StageEnv& E, Smem& sm) {
   const Ctx& c = E.c;
   const pdm_dims d = load_plan(&c.P->dims);
   const LayerPlan L = layer_of(c, E.st.layer);
@@ -1825,10 +1949,10 @@ __device__ __forceinline__ bool stage_down(const StageEnv& E, Smem& sm) {
     K = d.ffn;
   } else {
     K = (d.top_k + d.n_shared) * d.moe_ffn;
-    g.Kb = K;
+    g.Kb = EB == 0 ? K / 2 : K;
     g.slot_mode = 2;
-    g.lg_slot = 31 - __builtin_clz(d.moe_ffn);
-    g.slot_Kb = d.moe_ffn;
+    g.slot_Kb = EB == 0 ? d.moe_ffn / 2 : d.moe_ffn;
+    g.lg_slot = 31 - __builtin_clz(g.slot_Kb);
     g.nkb = L.edown.nkb;
     g.lg_rpv = 31;
   }
@@ -1846,16 +1970,19 @@ __device__ __forceinline__ bool stage_down(const StageEnv& E, Smem& sm) {
   auto prep = [&]() {
         if (res_pre && (int)threadIdx.x < rb - ra) res = ld_coh(xa + ra + threadIdx.x);
         if (!wait_stage(c, sm, E.st.wait, E.s)) return false;
-        stage_plain_vec(sm, K, act);
+        if (EB == 0 && L.is_moe) stage_plain_vec<true>(sm, K, act);
+        else stage_plain_vec(sm, K, act);
         return true;
       };
   auto epi = [&](int ca, int n) {
         for (int t = threadIdx.x; t < n; t += kThreads)
           st_coh(out + ca + t, round_bf16((res_pre ? res : ld_coh(xa + ca + t)) + part_sum(sm, t)));
       };
+  if constexpr (EB == 0) return run_gemv<0, 2>(E, sm, g, ra, rb, true, prep, epi);
   if (L.is_moe) return run_gemv<1, 2>(E, sm, g, ra, rb, true, prep, epi);
   return run_gemv<1, 0>(E, sm, g, ra, rb, true, prep, epi);
 }
+
 
 // --- LM: logits = W_lm * RMSNorm(x), argmax over the vocabulary
 __device__ __forceinline__ bool stage_lm(const StageEnv& E, Smem& sm) {
@@ -1939,6 +2066,10 @@ __device__ __forceinline__ bool stage_lm(const StageEnv& E, Smem& sm) {
 
 // All stages of one decode step, in plan order. Returns false when the step
 // was aborted (every workgroup leaves at its next wait).
+// XF: the expert format (PDM_FMT_*) the kernel is built for. The MXFP4 stage
+// code lives only in that kernel's instance: kernel-wide register allocation
+// and instruction-cache footprint of the FP8 kernel stay as they are.
+template <int XF>
 __device__ __forceinline__ bool run_step(const Ctx& c, Smem& sm, int n, int dpl) {
   for (int s = 0; s < n; ++s) {
     if (c.A.trace && threadIdx.x == 0) sm.t_entry = wall_clock64();
@@ -1954,8 +2085,13 @@ __device__ __forceinline__ bool run_step(const Ctx& c, Smem& sm, int n, int dpl)
       case PDM_ST_WO: ok = stage_wo(E, sm); break;
       case PDM_ST_ROUTER: ok = stage_router(E, sm); break;
       case PDM_ST_GU: ok = stage_gu(E, sm); break;
-      case PDM_ST_GU_ROUTED: ok = stage_gu_moe(E, sm); break;
-      case PDM_ST_DOWN: ok = stage_down(E, sm); break;
+      case PDM_ST_GU_ROUTED:
+        ok = XF == PDM_FMT_MXFP4 ? stage_gu_moe_t<0>(E, sm) : stage_gu_moe_t<1>(E, sm);
+        break;
+      case PDM_ST_DOWN:
+        // (dense layers keep FP8 in either kernel)
+        ok = XF == PDM_FMT_MXFP4 && (E.st.flags & kStMx) ? stage_down_t<0>(E, sm) : stage_down_t<1>(E, sm);
+        break;
       case PDM_ST_LM: ok = stage_lm(E, sm); break;
       default: ok = false; break;
     }
@@ -1977,6 +2113,7 @@ __device__ __forceinline__ bool run_step(const Ctx& c, Smem& sm, int n, int dpl)
 // lifecycle). Step j > 0 starts once every workgroup has finished step j - 1
 // (the counters of its last stage); its token comes from the token array, or
 // in greedy mode is the argmax step j - 1 wrote.
+template <int XF>
 __global__ void __launch_bounds__(kThreads, 1) engine_kernel(const Plan* __restrict__ P, LaunchArgs A) {
   __shared__ Smem sm;
   Ctx c;
@@ -2006,7 +2143,7 @@ __global__ void __launch_bounds__(kThreads, 1) engine_kernel(const Plan* __restr
     }
     c.A.argmax = A.argmax ? A.argmax + step : nullptr;
     c.A.logits = step + 1 == A.n_steps ? A.logits : nullptr;
-    if (!run_step(c, sm, n, dpl)) return;
+    if (!run_step<XF>(c, sm, n, dpl)) return;
   }
 }
 
@@ -2034,6 +2171,18 @@ __global__ void pack_codes_kernel(const uint8_t* __restrict__ src, uint8_t* __re
     int r = (int)(i / m.Kp), k = (int)(i % m.Kp);
     int sr, sc;
     if (pack_src(m, r, k, sr, sc)) dst[i] = src[(size_t)sr * m.K + sc];
+  }
+}
+
+// Whole packed rows (MXFP4 codes or scales): packed row r is logical row sr
+// of the map, row_bytes bytes each.
+__global__ void pack_rows_kernel(const uint8_t* __restrict__ src, uint8_t* __restrict__ dst, PackMap m,
+                                 int row_bytes) {
+  const size_t n = (size_t)m.rows * row_bytes;
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) {
+    int r = (int)(i / row_bytes), c = (int)(i % row_bytes);
+    int sr, sc;
+    if (pack_src(m, r, 0, sr, sc)) dst[i] = src[(size_t)sr * row_bytes + c];
   }
 }
 
@@ -2083,14 +2232,20 @@ hipError_t static_scratch(int device, void** ptr) {
   return hipSuccess;
 }
 
-hipError_t launch_engine(const Plan* plan_dev, const LaunchArgs& a, int G, hipStream_t stream, bool cooperative) {
+hipError_t launch_engine(const Plan* plan_dev, const LaunchArgs& a, int G, int expert_format, hipStream_t stream,
+                         bool cooperative) {
+  const void* k = expert_format == PDM_FMT_MXFP4 ? (const void*)engine_kernel<PDM_FMT_MXFP4>
+                                                 : (const void*)engine_kernel<PDM_FMT_FP8>;
   if (cooperative) {
     const Plan* p = plan_dev;
     LaunchArgs args = a;
     void* kargs[] = {(void*)&p, (void*)&args};
-    return hipLaunchCooperativeKernel((const void*)engine_kernel, dim3(G), dim3(kThreads), kargs, 0, stream);
+    return hipLaunchCooperativeKernel(k, dim3(G), dim3(kThreads), kargs, 0, stream);
   }
-  hipLaunchKernelGGL(engine_kernel, dim3(G), dim3(kThreads), 0, stream, plan_dev, a);
+  if (expert_format == PDM_FMT_MXFP4)
+    hipLaunchKernelGGL(engine_kernel<PDM_FMT_MXFP4>, dim3(G), dim3(kThreads), 0, stream, plan_dev, a);
+  else
+    hipLaunchKernelGGL(engine_kernel<PDM_FMT_FP8>, dim3(G), dim3(kThreads), 0, stream, plan_dev, a);
   return hipGetLastError();
 }
 
@@ -2110,6 +2265,14 @@ hipError_t launch_rope_table(float* tab, int max_ctx, int rope, double base, hip
   size_t n = (size_t)max_ctx * (rope / 2);
   int blocks = (int)std::min<size_t>(4096, (n + 255) / 256);
   hipLaunchKernelGGL(rope_table_kernel, dim3(blocks), dim3(256), 0, stream, tab, max_ctx, rope, base);
+  return hipGetLastError();
+}
+
+hipError_t launch_pack_rows(const uint8_t* src, uint8_t* dst, const PackMap& m, int row_bytes, hipStream_t stream) {
+  size_t n = (size_t)m.rows * row_bytes;
+  int blocks = (int)std::min<size_t>(8192, (n + 255) / 256);
+  if (blocks < 1) return hipSuccess;
+  hipLaunchKernelGGL(pack_rows_kernel, dim3(blocks), dim3(256), 0, stream, src, dst, m, row_bytes);
   return hipGetLastError();
 }
 

@@ -39,13 +39,17 @@ constexpr int kTraceWords = 8;        // u64 words per (stage, workgroup) trace 
 // [rows / 8][nkb] with nkb = ceil(K / 128). A scale entry covers 8 packed rows
 // by 128 columns; the packer guarantees each such tile lies inside a single
 // 128x128 block of the logical matrix.
+// A packed weight matrix. FP8 (fmt PDM_FMT_FP8): e4m3 codes [rows][K] and
+// bf16 scales [rows / 8][nkb], nkb = ceil(K / 128). MXFP4 (PDM_FMT_MXFP4):
+// e2m1 codes [rows][K] bytes (2 elements each) and e8m0 scales [rows][nkb]
+// bytes, nkb = K / 16 (one per 32 elements). K is bytes per row in both.
 struct Fp8Mat {
   uint64_t codes;
   uint64_t scales;
   int32_t rows;
   int32_t K;
   int32_t nkb;
-  int32_t pad;
+  int32_t fmt;
 };
 
 struct LayerPlan {
@@ -94,6 +98,7 @@ struct StagePlan {
 
 // StagePlan flags. Consecutive stages of one workgroup share LDS:
 constexpr int kStXStaged = 1;  // the input the previous stage staged in LDS is this stage's input
+constexpr int kStMx = 2;       // the stage's expert matrices are MXFP4
 
 struct Plan {
   pdm_dims dims;

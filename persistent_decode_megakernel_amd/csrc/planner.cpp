@@ -41,6 +41,8 @@ int validate_dims(const pdm_dims& d, int32_t max_ctx) {
   if (d.qk_nope < 1024 && (!is_pow2(d.qk_nope) || 1024 / d.qk_nope > d.kv_lora)) return PDM_ERR_CONFIG;
   if (d.kv_lora < 1024 && 1024 / d.kv_lora > d.v_head) return PDM_ERR_CONFIG;
   if (!(d.rms_eps >= 0.f) || !(d.rope_base > 1.f)) return PDM_ERR_CONFIG;
+  if (d.expert_format != PDM_FMT_FP8 && d.expert_format != PDM_FMT_MXFP4) return PDM_ERR_CONFIG;
+  if (any_moe && d.expert_format == PDM_FMT_MXFP4 && (d.moe_ffn < 64 || d.hidden % 32 != 0)) return PDM_ERR_CONFIG;
   return PDM_OK;
 }
 
@@ -68,9 +70,26 @@ Fp8Mat fp8_mat(Cursor& c, int rows, int K) {
   m.rows = rows;
   m.K = K;
   m.nkb = (int)ceil_div(K, 128);
+  m.fmt = PDM_FMT_FP8;
   m.codes = c.take((uint64_t)rows * K);
   m.scales = c.take((uint64_t)(rows / 8) * m.nkb * 2);
   return m;
+}
+
+// K elements per row (a multiple of 32): K / 2 code bytes and K / 32 scale bytes per row
+Fp8Mat mxfp4_mat(Cursor& c, int rows, int K) {
+  Fp8Mat m{};
+  m.rows = rows;
+  m.K = K / 2;
+  m.nkb = K / 32;
+  m.fmt = PDM_FMT_MXFP4;
+  m.codes = c.take((uint64_t)rows * m.K);
+  m.scales = c.take((uint64_t)rows * m.nkb);
+  return m;
+}
+
+uint64_t mat_bytes(const Fp8Mat& m) {
+  return (uint64_t)m.rows * m.K + (m.fmt == PDM_FMT_MXFP4 ? (uint64_t)m.rows * m.nkb : (uint64_t)(m.rows / 8) * m.nkb * 2);
 }
 
 // rows covered by one 1 KB GEMV unit when a row is shorter than 1 KB
@@ -179,8 +198,9 @@ int build_plan(const pdm_dims& d, int32_t max_ctx, int32_t G, Plan* p, Layout* l
     } else {
       L.router = w.take((uint64_t)d.n_experts * D * 2);
       Cursor e;  // layout inside one expert block
-      L.egu = fp8_mat(e, 2 * d.moe_ffn, D);
-      L.edown = fp8_mat(e, D, d.moe_ffn);
+      auto emat = d.expert_format == PDM_FMT_MXFP4 ? mxfp4_mat : fp8_mat;
+      L.egu = emat(e, 2 * d.moe_ffn, D);
+      L.edown = emat(e, D, d.moe_ffn);
       L.expert_stride = align_up(e.off, 256);
       L.expert_base = w.take(L.expert_stride * (uint64_t)(d.n_experts + d.n_shared));
     }
@@ -216,11 +236,15 @@ int build_plan(const pdm_dims& d, int32_t max_ctx, int32_t G, Plan* p, Layout* l
       // Router and gate/up both read RMSNorm(x_attn): the router stage stages
       // it and the gate/up stage (shared and routed experts) reuses it from LDS.
       int s_rt = add(PDM_ST_ROUTER, l, s_wo, d.n_experts, D, unit_rows(D, 2));
+      // expert rows hold K bytes (FP8) or K / 2 bytes (MXFP4)
+      const bool fp4 = d.expert_format == PDM_FMT_MXFP4;
       int s_gr = add(PDM_ST_GU_ROUTED, l, s_rt, 2 * d.moe_ffn * (d.n_shared + d.top_k), D,
-                     std::max(16, unit_rows(D, 1)));
-      p->stages[s_gr].flags = kStXStaged;
+                     std::max(16, unit_rows(fp4 ? D / 2 : D, 1)));
+      // (the MXFP4 stage stages its input in its own order)
+      p->stages[s_gr].flags = fp4 ? kStMx : kStXStaged;
       int kslots = (d.top_k + d.n_shared) * d.moe_ffn;
-      last = add(PDM_ST_DOWN, l, s_gr, D, kslots, unit_rows(kslots, 1));
+      last = add(PDM_ST_DOWN, l, s_gr, D, kslots, unit_rows(fp4 ? kslots / 2 : kslots, 1));
+      if (fp4) p->stages[last].flags = kStMx;
     }
     if (ns > kMaxStages - 2) return PDM_ERR_CONFIG;
   }
@@ -302,7 +326,7 @@ void stage_info(const Plan& p, int s, pdm_stage_info* o) {
   const int l = st.layer;
   auto id = [&](int buf, int layer) { return buf + 16 * layer; };
   auto input = [&]() { return l == 0 ? id(PDM_BUF_INPUT, 0) : id(PDM_BUF_XOUT, l - 1); };
-  auto fp8b = [](const Fp8Mat& m) { return (uint64_t)m.rows * m.K + (uint64_t)(m.rows / 8) * m.nkb * 2; };
+  auto fp8b = [](const Fp8Mat& m) { return mat_bytes(m); };
   if (st.type == PDM_ST_LM) {
     o->reads[0] = id(PDM_BUF_XOUT, d.n_layers - 1);
     o->writes[0] = id(PDM_BUF_LOGITS, d.n_layers);

@@ -72,6 +72,12 @@ class Engine:
             L.check("pdm_load_fp8", self.lib.pdm_load_fp8(self.h, tid, spec.layer, spec.expert, _ptr(codes),
                                                           _ptr(scales), self.stream))
             return codes, scales
+        if "mx_codes" in t:
+            codes = t["mx_codes"].to(self.device).contiguous()
+            scales = t["mx_scales"].to(self.device).contiguous()
+            L.check("pdm_load_mxfp4", self.lib.pdm_load_mxfp4(self.h, tid, spec.layer, spec.expert, _ptr(codes),
+                                                              _ptr(scales), self.stream))
+            return codes, scales
         data = t["data"].to(self.device).contiguous()
         nbytes = data.numel() * data.element_size()
         L.check("pdm_load_raw", self.lib.pdm_load_raw(self.h, tid, spec.layer, spec.expert, _ptr(data), nbytes,

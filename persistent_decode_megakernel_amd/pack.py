@@ -42,6 +42,14 @@ def pack_fp8(cfg, name: str, layer: int, expert: int, codes: np.ndarray, scales:
                                                   _np_ptr(scales), _np_ptr(arena), arena.nbytes))
 
 
+def pack_mxfp4(cfg, name: str, layer: int, expert: int, codes: np.ndarray, scales: np.ndarray, arena: np.ndarray):
+    d = L.dims_of(cfg)
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    scales = np.ascontiguousarray(scales, dtype=np.uint8)
+    L.check("pdm_pack_mxfp4", L.load().pdm_pack_mxfp4(C.byref(d), L.TENSOR_IDS[name], layer, expert,
+                                                      _np_ptr(codes), _np_ptr(scales), _np_ptr(arena), arena.nbytes))
+
+
 def pack_raw(cfg, name: str, layer: int, expert: int, data: np.ndarray, arena: np.ndarray):
     d = L.dims_of(cfg)
     data = np.ascontiguousarray(data)
@@ -66,6 +74,8 @@ def pack_store(cfg, store) -> np.ndarray:
         t = store.numpy(spec.name, spec.layer, spec.expert)
         if "codes" in t:
             pack_fp8(cfg, spec.name, spec.layer, spec.expert, t["codes"], t["scales"], arena)
+        elif "mx_codes" in t:
+            pack_mxfp4(cfg, spec.name, spec.layer, spec.expert, t["mx_codes"], t["mx_scales"], arena)
         else:
             pack_raw(cfg, spec.name, spec.layer, spec.expert, t["data"], arena)
     return arena

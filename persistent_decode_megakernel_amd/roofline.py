@@ -12,6 +12,8 @@ Algorithmic bytes of one decode step (what the method must read):
     layer, the dense FFNs, and the top-k routed plus shared experts of every
     MoE layer (never all experts);
   * one bf16 scale per 128x128 block of those matrices;
+  * for MXFP4 experts (expert_format "mxfp4") half a byte per element and
+    one e8m0 scale byte per 32 elements instead;
   * bf16 router and LM head;
   * the latent cache: every layer reads ctx = pos + 1 rows of kv_lora + rope
     bf16 values.
@@ -29,20 +31,25 @@ def _blocks(n, k):
 def weight_bytes(cfg) -> dict:
     D, H = cfg.hidden, cfg.n_heads
     fp8 = []  # (rows, cols) of every active FP8 matrix of one token
+    mx = []   # the same for MXFP4 matrices
     bf16 = 0
+    experts = mx if getattr(cfg, "expert_format", "fp8") == "mxfp4" else fp8
     for kind in cfg.layers:
         fp8 += [(cfg.q_lora, D), (cfg.kv_row, D), (H * cfg.qk_head, cfg.q_lora),
                 (H * (cfg.qk_nope + cfg.v_head), cfg.kv_lora), (D, H * cfg.v_head)]
         if kind == "dense":
             fp8 += [(cfg.ffn, D), (cfg.ffn, D), (D, cfg.ffn)]
         else:
-            fp8 += [(cfg.moe_ffn, D), (cfg.moe_ffn, D), (D, cfg.moe_ffn)] * (cfg.top_k + cfg.n_shared)
+            experts += [(cfg.moe_ffn, D), (cfg.moe_ffn, D), (D, cfg.moe_ffn)] * (cfg.top_k + cfg.n_shared)
             bf16 += cfg.n_experts * D * 2
     if cfg.vocab:
         bf16 += cfg.vocab * D * 2
     codes = sum(n * k for n, k in fp8)
     scales = sum(_blocks(n, k) * 2 for n, k in fp8)
-    return {"fp8_codes": codes, "block_scales": scales, "bf16": bf16, "total": codes + scales + bf16}
+    mx_codes = sum(n * k // 2 for n, k in mx)
+    mx_scales = sum(n * k // 32 for n, k in mx)
+    return {"fp8_codes": codes, "block_scales": scales, "mxfp4_codes": mx_codes, "mxfp4_scales": mx_scales,
+            "bf16": bf16, "total": codes + scales + mx_codes + mx_scales + bf16}
 
 
 def kv_bytes(cfg, ctx: int) -> int:

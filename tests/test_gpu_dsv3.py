@@ -34,7 +34,7 @@ def _layer_case(name, steps):
     return cfg, eng, ref, st
 
 
-@pytest.mark.parametrize("name,steps", [("dsv3_dense_layer", 3), ("dsv3_moe_layer", 3)])
+@pytest.mark.parametrize("name,steps", [("dsv3_dense_layer", 3), ("dsv3_moe_layer", 3), ("dsv3_moe_layer_fp4", 3)])
 def test_dsv3_layer_parity(name, steps):
     cfg, eng, ref, st_ref = _layer_case(name, steps)
     P = cfg.prompt_len

@@ -34,6 +34,21 @@ def _logical_rows(cfg, name, part, rows):
     return r
 
 
+def _check_mx_tensor(cfg, arena, spec, t):
+    """An MXFP4 expert matrix: the same row map, codes and e8m0 scales per row."""
+    codes, scales = t["mx_codes"], t["mx_scales"]
+    m = pack.packed_layout(cfg, spec.name, spec.layer, spec.expert, 0)
+    assert m.format == L.FMT_MXFP4 and m.parts == 1
+    assert m.K == codes.shape[1] and m.n_kblocks == scales.shape[1] == m.K // 16
+    pc = arena[m.codes_offset:m.codes_offset + m.rows * m.K].reshape(m.rows, m.K)
+    ps = arena[m.scales_offset:m.scales_offset + m.rows * m.n_kblocks].reshape(m.rows, m.n_kblocks)
+    src = _logical_rows(cfg, spec.name, 0, m.rows)
+    mine = src >= 0
+    np.testing.assert_array_equal(pc[mine], codes[src[mine]], err_msg=f"{spec} codes")
+    np.testing.assert_array_equal(ps[mine], scales[src[mine]], err_msg=f"{spec} scales")
+    assert sorted(src[mine].tolist()) == list(range(codes.shape[0]))  # every row lands once
+
+
 def _check_tensor(cfg, arena, spec, t):
     codes, scales = t["codes"], t["scales"]
     first = pack.packed_layout(cfg, spec.name, spec.layer, spec.expert, 0)
@@ -57,18 +72,21 @@ def _check_tensor(cfg, arena, spec, t):
     np.testing.assert_array_equal(recovered, codes.astype(np.int32), err_msg=f"{spec} round trip")
 
 
-@pytest.mark.parametrize("name", ["tiny", "ragged"])
+@pytest.mark.parametrize("name", ["tiny", "ragged", "tiny_fp4", "ragged_fp4"])
 def test_host_packer_layout_byte_exact(name):
     cfg = configs.get(name)
     store = gen.LogicalWeights(cfg, 0, "cpu")
     arena = pack.pack_store(cfg, store)
-    n_fp8 = 0
+    n_fp8 = n_mx = 0
     for spec in store.specs():
         t = store.numpy(spec.name, spec.layer, spec.expert)
         if "codes" in t:
             _check_tensor(cfg, arena, spec, t)
             n_fp8 += 1
-    assert n_fp8 > 0
+        elif "mx_codes" in t:
+            _check_mx_tensor(cfg, arena, spec, t)
+            n_mx += 1
+    assert n_fp8 > 0 and (n_mx > 0) == (cfg.expert_format == "mxfp4")
 
 
 def test_host_packer_header_and_errors():

@@ -53,3 +53,34 @@ def test_single_layer_bytes():
     m = configs.get("dsv3_moe_layer")
     assert abs(R.bytes_per_token(d, 1025) / 1e6 - 584.7) < 0.1
     assert abs(R.bytes_per_token(m, 1025) / 1e6 - 588.4) < 0.1
+
+
+def test_mxfp4_expert_bytes():
+    """MXFP4 experts: half a byte per element plus one scale byte per 32."""
+    f8, f4 = configs.get("dsv3_stack_1k"), configs.get("dsv3_stack_1k_fp4")
+    w8, w4 = R.weight_bytes(f8), R.weight_bytes(f4)
+    expert_elems = 8 * 9 * 3 * 2048 * 7168
+    assert w4["mxfp4_codes"] == expert_elems // 2
+    assert w4["mxfp4_scales"] == expert_elems // 32
+    assert w8["fp8_codes"] - w4["fp8_codes"] == expert_elems
+    assert w4["bf16"] == w8["bf16"]
+
+
+def test_plan_weight_bytes_agree_with_roofline():
+    """The planner's per-stage weight bytes (scales included) add up to the
+    roofline's per-token weight bytes, for FP8 and MXFP4 experts."""
+    from persistent_decode_megakernel_amd import describe_plan
+    for name in ("dsv3_stack_1k", "dsv3_stack_1k_fp4", "tiny", "tiny_fp4"):
+        cfg = configs.get(name)
+        plan = describe_plan(cfg, cfg.prompt_len + 8)
+        gains = {"qkv": cfg.hidden * 4, "qb": cfg.q_lora * 4, "attn": cfg.kv_lora * 4, "router": cfg.hidden * 4,
+                 "lm": cfg.hidden * 4}
+        total = sum(s["weight_bytes"] - gains.get(s["type"], 0) for s in plan)
+        w = R.weight_bytes(cfg)
+        # the plan counts the scales it streams (an FP8 block scale is repeated
+        # for every 8 packed rows: 2 bytes per 1024 code bytes), the roofline
+        # one per 128x128 block (the algorithmic bytes); MXFP4 scales agree
+        fp8_scales_streamed = w["fp8_codes"] // 512
+        assert total - w["total"] >= 0, name
+        assert abs(total - w["total"] - fp8_scales_streamed + w["block_scales"]) / w["total"] < 1e-4, (
+            name, total, w["total"])
