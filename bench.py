@@ -157,9 +157,11 @@ def calibrate_copy(nbytes: int = 1 << 30):
     print(json.dumps({"calibration_copy_bytes": nbytes, "copies": 3}), flush=True)
 
 
-def run_workload(eng, cfg, K, Wm, do_trace, trace_detail):
+def run_workload(eng, cfg, K, Wm, do_trace, trace_detail, resident_only=False):
     """Time K teacher-forced steps of cfg on the bound engine, as K single-step
-    launches and as one resident launch. Returns a result dict."""
+    launches and as one resident launch (resident_only: only the resident
+    warm-up and timed launches, so that every engine launch of the process
+    runs many steps — for profiler runs). Returns a result dict."""
     import torch
     from persistent_decode_megakernel_amd import describe_plan, roofline as R, trace as T
     from synth import gen
@@ -175,12 +177,13 @@ def run_workload(eng, cfg, K, Wm, do_trace, trace_detail):
             eng.import_kv(l, 0, lat[l])
 
     stream = torch.cuda.current_stream()
-    fill()
-    for j in range(Wm):
-        eng.decode(P + j, token=toks[j])
-    rc, st = eng.status()
-    if rc != 0:
-        raise SystemExit(f"{cfg.name}: warm-up step failed: status {rc} stage {st.stage}")
+    if not resident_only:
+        fill()
+        for j in range(Wm):
+            eng.decode(P + j, token=toks[j])
+        rc, st = eng.status()
+        if rc != 0:
+            raise SystemExit(f"{cfg.name}: warm-up step failed: status {rc} stage {st.stage}")
     fill()
     eng.decode_steps(P, tok_dev[:Wm].clone(), argmax=am[:Wm])
     rc, st = eng.status()
@@ -188,19 +191,20 @@ def run_workload(eng, cfg, K, Wm, do_trace, trace_detail):
         raise SystemExit(f"{cfg.name}: resident warm-up failed: status {rc} stage {st.stage}")
 
     # K single-step launches
-    fill()
-    torch.cuda.synchronize()
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
-    ev[0].record(stream)
-    for j in range(K):
-        eng.decode(P + j, token=toks[j])
-        ev[j + 1].record(stream)
-    torch.cuda.synchronize()
-    rc, st = eng.status()
-    if rc != 0:
-        raise SystemExit(f"{cfg.name}: timed step failed: status {rc} stage {st.stage}")
-    per = sorted(ev[j].elapsed_time(ev[j + 1]) for j in range(K))
-    launch_s = ev[0].elapsed_time(ev[K]) / 1e3 / K
+    if not resident_only:
+        fill()
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
+        ev[0].record(stream)
+        for j in range(K):
+            eng.decode(P + j, token=toks[j])
+            ev[j + 1].record(stream)
+        torch.cuda.synchronize()
+        rc, st = eng.status()
+        if rc != 0:
+            raise SystemExit(f"{cfg.name}: timed step failed: status {rc} stage {st.stage}")
+        per = sorted(ev[j].elapsed_time(ev[j + 1]) for j in range(K))
+        launch_s = ev[0].elapsed_time(ev[K]) / 1e3 / K
 
     # one resident launch of the same K steps
     fill()
@@ -221,12 +225,14 @@ def run_workload(eng, cfg, K, Wm, do_trace, trace_detail):
         "bytes_per_token": int(bytes_mean),
         "resident": {"ms_per_step": round(resident_s * 1e3, 4), "tok_s_user": round(1 / resident_s, 3),
                      "frac_of_8TBps": round(bytes_mean / resident_s / R.HBM_PEAK_BYTES_PER_S, 4)},
-        "per_step_launch": {"ms_per_step": round(launch_s * 1e3, 4), "tok_s_user": round(1 / launch_s, 3),
-                            "p50_ms": round(per[K // 2], 4), "p99_ms": round(per[min(K - 1, int(0.99 * K))], 4),
-                            "frac_of_8TBps": round(bytes_mean / launch_s / R.HBM_PEAK_BYTES_PER_S, 4)},
     }
+    if not resident_only:
+        out["per_step_launch"] = {"ms_per_step": round(launch_s * 1e3, 4), "tok_s_user": round(1 / launch_s, 3),
+                                  "p50_ms": round(per[K // 2], 4), "p99_ms": round(per[min(K - 1, int(0.99 * K))], 4),
+                                  "frac_of_8TBps": round(bytes_mean / launch_s / R.HBM_PEAK_BYTES_PER_S, 4)}
     log(f"{cfg.name}: resident {resident_s * 1e3:.3f} ms/token ({1 / resident_s:.1f} tok/s/user, "
-        f"{bytes_mean / resident_s / 1e9:.0f} GB/s); single-step launches {launch_s * 1e3:.3f} ms/token")
+        f"{bytes_mean / resident_s / 1e9:.0f} GB/s)"
+        + ("" if resident_only else f"; single-step launches {launch_s * 1e3:.3f} ms/token"))
     if do_trace:
         plan = describe_plan(cfg, eng.max_ctx, eng.sizes.n_workgroups)
         fill()
@@ -319,6 +325,8 @@ def main():
     ap.add_argument("--layer-copies", type=int, default=2,
                     help="weight copies the single-layer steps alternate over")
     ap.add_argument("--layer-steps", type=int, default=32)
+    ap.add_argument("--resident-only", action="store_true",
+                    help="time only resident launches (no single-step launches): for profiler runs")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a 1 GiB device copy three times (counter calibration for rocprofv3)")
     args = ap.parse_args()
@@ -356,7 +364,7 @@ def main():
     ceiling = stream_ceiling(eng.weights)
     log(f"streaming-read ceiling (torch sum over 32 GB of the arena): {ceiling / 1e9:.0f} GB/s")
 
-    results = [run_workload(eng, c, K, Wm, not args.no_trace, args.trace_detail and i == 0)
+    results = [run_workload(eng, c, K, Wm, not args.no_trace, args.trace_detail and i == 0, args.resident_only)
                for i, c in enumerate(cfgs)]
     if args.mxfp4:
         # a second engine: the expert matrices are MXFP4 (everything else as above)
@@ -368,7 +376,7 @@ def main():
             e4.load_tensor(spec, s4.get(spec.name, spec.layer, spec.expert))
         torch.cuda.synchronize()
         log(f"{c4.name}: weights {e4.sizes.weight_bytes / 1e9:.2f} GB (MXFP4 experts)")
-        r4 = run_workload(e4, c4, K, Wm, not args.no_trace, False)
+        r4 = run_workload(e4, c4, K, Wm, not args.no_trace, False, args.resident_only)
         r4["weights"] = "MXFP4 routed and shared experts (e2m1, e8m0 scale per 32); everything else as the FP8 stack"
         results.append(r4)
         del e4, s4
