@@ -32,8 +32,7 @@
 namespace pdm {
 namespace {
 
-constexpr int kUnroll = 5;  // 1 KB units in flight per wave and buffer
-constexpr int kUnrollMx = 3;  // the same for MXFP4 units
+constexpr int kUnroll = 5;  // 1 KB units in flight per wave and buffer (FP8, bf16 and MXFP4 alike)
 constexpr int kEarlyBatches = 1;       // unit batches per wave issued before a stage's dependency wait
 // The last wave of a workgroup polls the dependency counters and issues no
 // load before the wait: loads complete in order per wave, so a poll issued
@@ -588,9 +587,7 @@ __device__ __forceinline__ bool gemv_rows_t(const Gemv& g, Smem& sm, int ra, int
                                             Late&& late) {
   static_assert(LONG || !FULL, "whole-KB rows are long rows");
   static_assert(!PAIR || (EB == 0 && LONG && !FULL), "row pairs are an MXFP4 long-row mode");
-  // units per batch: an MXFP4 unit carries twice the elements of an FP8 one
-  // (and twice the staged input reads), so its batches are shorter
-  constexpr int U = EB == 0 ? kUnrollMx : kUnroll;
+  constexpr int U = kUnroll;  // units per batch
   const int lane = EB == 0 ? opaque_lane() : lane_id();
   const int w = wave_id();
   const int kb = g.Kb;
