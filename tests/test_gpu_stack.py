@@ -138,7 +138,8 @@ def _oracle_base(eng, cfg, pos):
 
 
 @pytest.mark.timeout(1100)
-@pytest.mark.parametrize("name,checked", [("dsv3_stack_1k", (0, 255, 1023)), ("dsv3_stack_8k", (0, 1023))])
+@pytest.mark.parametrize("name,checked", [("dsv3_stack_1k", (0, 255, 1023)), ("dsv3_stack_8k", (0, 1023)),
+                                          ("dsv3_stack_1k_fp4", (0, 1023))])
 def test_stack_fullsize_own_cache(name, checked):
     from persistent_decode_megakernel_amd import Engine
     cfg = configs.get(name)
