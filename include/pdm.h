@@ -369,12 +369,13 @@ int pdm_export_kv(const pdm_engine* e, int32_t layer, int32_t pos0, int32_t n, u
  * "run inference" call of "What is TileRT" section 6.1; one kernel for the
  * whole step as in the SemiAnalysis TileRT page, how-it-works section).
  * token: input token id (configs with a vocabulary), else ignored;
- * x_in_dev: bf16 [hidden] input of a bare layer stack, else ignored;
+ * x_in_dev: bf16 [hidden] input of a bare layer stack (16-byte aligned, else
+ * PDM_ERR_ALIGN), else ignored;
  * pos: must equal the cache length and be < max_ctx; the step appends row pos.
  * logits_dev: optional f32 [vocab] output; argmax_dev: optional int32 output
  * (lowest index among equal maxima). Both written before the kernel ends.
  * Host-side errors: PDM_ERR_UNBOUND, PDM_ERR_POS, PDM_ERR_CTX, PDM_ERR_TOKEN,
- * PDM_ERR_LAUNCH; device-side failures go to the status word. */
+ * PDM_ERR_ALIGN, PDM_ERR_LAUNCH; device-side failures go to the status word. */
 int pdm_decode_step(pdm_engine* e, int32_t token, int32_t pos, const uint16_t* x_in_dev,
                     float* logits_dev, int32_t* argmax_dev, pdm_stream_t stream);
 

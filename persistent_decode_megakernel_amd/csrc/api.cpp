@@ -561,6 +561,8 @@ int pdm_decode_step(pdm_engine* e, int32_t token, int32_t pos, const uint16_t* x
     if (token < 0 || token >= d.vocab) return PDM_ERR_TOKEN;
   } else if (!x_in_dev) {
     return PDM_ERR_TOKEN;
+  } else if (reinterpret_cast<uintptr_t>(x_in_dev) & 15u) {
+    return PDM_ERR_ALIGN;  // the first stage reads it in 16-byte pieces
   }
   if (pos < 0) return PDM_ERR_POS;
   if (pos >= e->max_ctx) return PDM_ERR_CTX;

@@ -221,16 +221,6 @@ __device__ __forceinline__ float group_sum(float v, int gs) {
 }
 
 // block-wide sum (all 512 threads participate); result in every thread
-__device__ __forceinline__ float block_sum(Smem& sm, float v) {
-  float w = wave_sum(v);
-  if (lane_id() == 0) sm.red[wave_id()] = w;
-  __syncthreads();
-  float t = 0.f;
-#pragma unroll
-  for (int i = 0; i < kWaves; ++i) t += sm.red[i];
-  __syncthreads();
-  return t;
-}
 
 __device__ __forceinline__ float silu(float g) { return g / (1.0f + __expf(-g)); }
 
@@ -835,65 +825,6 @@ __device__ __forceinline__ void zero_part(Smem& sm) {
   if (threadIdx.x == 0) sm.claim = kEarlyBatches * (kWaves - 1);
 }
 
-// Copy K values get(k) into sm.x with all loads of a batch in flight at once
-// (a load-then-store loop would wait for each load in turn). Returns this
-// thread's sum of squares.
-constexpr int kStageBatch = 16;
-
-template <class Get>
-__device__ __forceinline__ float stage_values(Smem& sm, int K, Get&& get) {
-  float ss = 0.f;
-  for (int k0 = threadIdx.x; k0 < K; k0 += kStageBatch * kThreads) {
-    float v[kStageBatch];
-#pragma unroll
-    for (int i = 0; i < kStageBatch; ++i) {
-      int k = k0 + i * kThreads;
-      v[i] = k < K ? get(k) : 0.f;
-    }
-#pragma unroll
-    for (int i = 0; i < kStageBatch; ++i) {
-      int k = k0 + i * kThreads;
-      if (k < K) sm.x[xperm(k)] = v[i];
-      ss += v[i] * v[i];
-    }
-  }
-  return ss;
-}
-
-// Stage an input vector with fused RMSNorm: x_lds[k] = v[k] * g[k] / sqrt(mean(v^2) + eps).
-// `get(k)` returns v[k]. The gains are loaded in the same batches as the
-// input, so the whole staging costs one memory round trip per batch.
-// Contains barriers; all threads call it.
-template <class Get>
-__device__ __forceinline__ void stage_rmsnorm(Smem& sm, int K, const float* gain, float eps, Get&& get) {
-  float ss = 0.f;
-  for (int k0 = threadIdx.x; k0 < K; k0 += kStageBatch * kThreads) {
-    float v[kStageBatch], gv[kStageBatch];
-#pragma unroll
-    for (int i = 0; i < kStageBatch; ++i) {
-      int k = k0 + i * kThreads;
-      v[i] = k < K ? get(k) : 0.f;
-      gv[i] = gld(gain + min(k, K - 1));
-    }
-#pragma unroll
-    for (int i = 0; i < kStageBatch; ++i) {
-      int k = k0 + i * kThreads;
-      if (k < K) sm.x[xperm(k)] = v[i] * gv[i];
-      ss += v[i] * v[i];
-    }
-  }
-  float tot = block_sum(sm, ss);
-  float rs = 1.0f / sqrtf(tot / (float)K + eps);
-  for (int k = threadIdx.x; k < K; k += kThreads) sm.x[xperm(k)] *= rs;
-  __syncthreads();
-}
-
-template <class Get>
-__device__ __forceinline__ void stage_plain(Smem& sm, int K, Get&& get) {
-  stage_values(sm, K, get);
-  __syncthreads();
-}
-
 // Contiguous fp32 vectors written this step by other workgroups (K a multiple
 // of 4) are staged with 16-byte buffer loads under the sc1 policy, so every
 // vector of up to kStageVec * 4 * kThreads floats costs one round trip. The
@@ -952,6 +883,48 @@ __device__ __forceinline__ void stage_norm_vec(Smem& sm, int K, const float* gai
   if (lane_id() == 0) sm.nred[wave_id()] = w;
   __syncthreads();
 }
+// The same for a bf16 vector (the embedding row or a bare stack's input; K a
+// multiple of 8, src 16-byte aligned, not written this step): 16-byte loads
+// of 8 values, gain * v staged in xperm order, sums of squares to sm.nred.
+constexpr int kStageVecBf16 = 2;      // 8 values per load: 8192 per pass
+__device__ __forceinline__ void stage_norm_bf16(Smem& sm, int K, const float* gain, const uint16_t* src) {
+  const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(src), 0, K * 2, kBufDword3);
+  const __amdgpu_buffer_rsrc_t rg = vec_rsrc(gain, K);
+  const int n8 = K / 8;
+  float ss = 0.f;
+  for (int b0 = 0; b0 < n8; b0 += kStageVecBf16 * kThreads) {
+    u32x4 v[kStageVecBf16];
+    float4 g0[kStageVecBf16], g1[kStageVecBf16];
+#pragma unroll
+    for (int i = 0; i < kStageVecBf16; ++i) {
+      const int i8 = b0 + i * kThreads + (int)threadIdx.x;
+      v[i] = (u32x4){0u, 0u, 0u, 0u};
+      g0[i] = g1[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (b0 + i * kThreads < n8) {
+        v[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, i8 * 16, 0, 0);
+        g0[i] = ld_vec4<0>(rg, 2 * i8);
+        g1[i] = ld_vec4<0>(rg, 2 * i8 + 1);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kStageVecBf16; ++i) {
+      const int i8 = b0 + i * kThreads + (int)threadIdx.x;
+      const float a0 = bf16_lo(v[i].x), a1 = bf16_hi(v[i].x), a2 = bf16_lo(v[i].y), a3 = bf16_hi(v[i].y);
+      const float a4 = bf16_lo(v[i].z), a5 = bf16_hi(v[i].z), a6 = bf16_lo(v[i].w), a7 = bf16_hi(v[i].w);
+      if (i8 < n8) {
+        *reinterpret_cast<float4*>(sm.x + xperm(8 * i8)) =
+            make_float4(a0 * g0[i].x, a1 * g0[i].y, a2 * g0[i].z, a3 * g0[i].w);
+        *reinterpret_cast<float4*>(sm.x + xperm(8 * i8 + 4)) =
+            make_float4(a4 * g1[i].x, a5 * g1[i].y, a6 * g1[i].z, a7 * g1[i].w);
+      }
+      ss += a0 * a0 + a1 * a1 + a2 * a2 + a3 * a3 + a4 * a4 + a5 * a5 + a6 * a6 + a7 * a7;
+    }
+  }
+  const float w = wave_sum(ss);
+  if (lane_id() == 0) sm.nred[wave_id()] = w;
+  __syncthreads();
+}
+
 __device__ __forceinline__ float rms_scale(const Smem& sm, int K, float eps) {
   float t = 0.f;
 #pragma unroll
@@ -1119,7 +1092,8 @@ __device__ __forceinline__ bool stage_qkv(const StageEnv& E, Smem& sm) {
           stage_norm_vec(sm, D, reinterpret_cast<const float*>(L.attn_norm), in.prev);
           rs = rms_scale(sm, D, c.P->dims.rms_eps);
         } else {
-          stage_rmsnorm(sm, D, reinterpret_cast<const float*>(L.attn_norm), c.P->dims.rms_eps, in);
+          stage_norm_bf16(sm, D, reinterpret_cast<const float*>(L.attn_norm), in.bf16);
+          rs = rms_scale(sm, D, c.P->dims.rms_eps);
         }
         if (tapper) st_coh(reinterpret_cast<float*>(c.P->x0) + tk0 + threadIdx.x, tap);
         return true;

@@ -146,7 +146,7 @@ def test_plan_weight_bytes_match_active_parameters(lib):
 
 def test_engine_kernel_resource_usage():
     """The persistent kernel keeps one 512-thread workgroup per CU and does not
-    fall off a spill cliff: register spills turn into scratch traffic that every
+    spill vector registers: a spill turns into scratch traffic that every
     stage's completion wait then has to drain."""
     import json
     from persistent_decode_megakernel_amd import build
@@ -158,5 +158,8 @@ def test_engine_kernel_resource_usage():
     for k in ks:
         assert k["Occupancy [waves/SIMD]"] >= 2
         assert k["LDS Size [bytes/block]"] <= 160 * 1024
-        assert k["ScratchSize [bytes/lane]"] <= 512, k
-        assert k["VGPRs Spill"] <= 128, k
+        # no vector registers spilled to scratch; SGPR spills go to VGPR
+        # lanes (no memory traffic) and are bounded against a large jump
+        assert k["ScratchSize [bytes/lane]"] == 0, k
+        assert k["VGPRs Spill"] == 0, k
+        assert k["SGPRs Spill"] <= 1024, k
