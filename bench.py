@@ -14,9 +14,11 @@ inputs resident in HBM: K back-to-back single-step launches, and one resident
 launch of the same K steps (the engine stays on the device for the whole
 request; this is the headline figure). Then the bare DeepSeek-V3-shaped dense
 and MoE layers are timed per layer-step, alternating over two weight copies so
-that no step is served from the MALL. Prints one JSON line with tok/s/user,
-TPOT, the HBM roofline fraction, a stage trace, the single-layer timings and
-the CPU oracle baseline.
+that no step is served from the MALL, and the weight products of one MoE layer
+are timed at batch 1, 2, 4 and 8 (pdm_batch_gemm / pdm_batch_ffn, several
+sequences sharing every weight byte). Prints one JSON line with tok/s/user,
+TPOT, the HBM roofline fraction, a stage trace, the single-layer timings, the
+batch points and the CPU oracle baseline.
 """
 from __future__ import annotations
 
@@ -253,6 +255,71 @@ def run_workload(eng, cfg, K, Wm, do_trace, trace_detail, resident_only=False):
     return out
 
 
+def batch_points(eng, cfg, batches, reps: int = 20):
+    """Weight products of one DeepSeek-V3 MoE layer for B tokens at once
+    (pdm_batch_gemm on [W_DQ ; W_DKV], W_UQ and W_O, pdm_batch_ffn on the
+    union of the B tokens' routed experts plus the shared one), timed with HIP
+    events on the launch stream over `reps` back-to-back passes. W_UK / W_UV
+    (per-head products, about 1% of the layer's bytes), the bf16 router and
+    attention are not in it. Bytes are the FP8 codes and scales of every matrix
+    a pass reads; the union is counted from the seeded routing."""
+    import torch
+    from persistent_decode_megakernel_amd import _lib as L, pack, roofline as R
+    from synth import gen
+    layer = cfg.layers.index("moe")
+
+    def mat_bytes(name, expert=-1):
+        m = pack.packed_layout(cfg, name, layer, expert)
+        return m.rows * m.K + (m.rows // 8) * m.n_kblocks * 2
+
+    mats = [("wq_a", cfg.hidden), ("wq_b", cfg.q_lora), ("wo", cfg.n_heads * cfg.v_head)]
+    dense_bytes = sum(mat_bytes(n) for n, _ in mats)
+    expert_bytes = mat_bytes("w_gate", 0) + mat_bytes("w_down", 0)
+    stream = torch.cuda.current_stream()
+    pts = []
+    for B in batches:
+        xs = {n: torch.from_numpy(gen.batch_rows(B, K, SEED, tag=L.TENSOR_IDS[n])).cuda() for n, K in mats}
+        ys = {n: torch.empty(B, pack.packed_layout(cfg, n, layer).rows, device="cuda") for n, _ in mats}
+        h = torch.from_numpy(gen.batch_rows(B, cfg.hidden, SEED, tag=99)).cuda()
+        idx, w = gen.batch_routing(cfg, B, SEED)
+        idx_d, w_d = torch.from_numpy(idx).cuda(), torch.from_numpy(w).cuda()
+        yf = torch.empty(B, cfg.hidden, device="cuda")
+        n_u = len(set(idx.ravel().tolist())) + cfg.n_shared
+
+        def gemms():
+            for n, _ in mats:
+                eng.batch_gemm(L.TENSOR_IDS[n], layer, xs[n], out=ys[n])
+
+        def ffn():
+            eng.batch_ffn(layer, h, idx_d, w_d, out=yf)
+
+        def timed(fn):
+            for _ in range(3):
+                fn()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(reps):
+                fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / 1e3 / reps
+
+        t_g, t_f = timed(gemms), timed(ffn)
+        t = timed(lambda: (gemms(), ffn()))
+        nbytes = dense_bytes + n_u * expert_bytes
+        pts.append({"B": B, "us_per_layer_pass": round(t * 1e6, 1), "us_gemms": round(t_g * 1e6, 1),
+                    "us_ffn": round(t_f * 1e6, 1), "experts_read": n_u, "weight_bytes": int(nbytes),
+                    "GBps": round(nbytes / t / 1e9, 1), "frac_of_8TBps": round(nbytes / t / R.HBM_PEAK_BYTES_PER_S, 4),
+                    "tokens_per_s_per_layer": round(B / t, 1), "bytes_per_token": int(nbytes / B)})
+        log(f"batch {B}: one MoE layer's weight products {t * 1e6:.1f} us ({n_u} experts, "
+            f"{nbytes / 1e6:.0f} MB, {nbytes / t / 1e9:.0f} GB/s); qkv+q_b+W_O {t_g * 1e6:.1f} us, FFN {t_f * 1e6:.1f} us")
+    return {"workload": f"{cfg.name} layer {layer}: FP8 weight products of one MoE layer for B tokens "
+                        "([W_DQ ; W_DKV], W_UQ, W_O, union-of-experts SwiGLU), synthetic uniform top-8 routing",
+            "kernel": "pdm::batch_gemm_kernel (MFMA 16x16x32 bf16, FP8 weights read in place)",
+            "points": pts}
+
+
 def layer_steps(name: str, copies: int, steps: int, warm: int = 2):
     """Microseconds per step of one bare DeepSeek-V3-shaped layer (dense or
     MoE, fed an N(0,1) bf16 hidden vector, 1024-position prompt cache).
@@ -325,6 +392,8 @@ def main():
     ap.add_argument("--layer-copies", type=int, default=2,
                     help="weight copies the single-layer steps alternate over")
     ap.add_argument("--layer-steps", type=int, default=32)
+    ap.add_argument("--batch", default="1,2,4,8",
+                    help="batch sizes of the batched weight-product leg on the stack's engine ('' for none)")
     ap.add_argument("--resident-only", action="store_true",
                     help="time only resident launches (no single-step launches): for profiler runs")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -366,6 +435,7 @@ def main():
 
     results = [run_workload(eng, c, K, Wm, not args.no_trace, args.trace_detail and i == 0, args.resident_only)
                for i, c in enumerate(cfgs)]
+    batch = batch_points(eng, head, [int(b) for b in args.batch.split(",") if b]) if args.batch else None
     if args.mxfp4:
         # a second engine: the expert matrices are MXFP4 (everything else as above)
         c4 = configs.get(args.mxfp4)
@@ -426,6 +496,8 @@ def main():
         "git_head": git_head(),
         "engine_source_hash": engine_source_hash(),
     }
+    if batch is not None:
+        out["batch_points"] = batch
     if args.layers:
         del eng
         torch.cuda.empty_cache()

@@ -100,6 +100,10 @@ _SIGS = {
     "pdm_cache_length": (C.c_int, [_P, C.POINTER(C.c_int32)]),
     "pdm_set_debug": (C.c_int, [_P, C.c_int32, C.c_int32]),
     "pdm_set_trace": (C.c_int, [_P, C.c_int32]),
+    "pdm_batch_gemm": (C.c_int, [_P, C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_void_p, C.c_int32,
+                                 C.c_void_p, C.c_void_p]),
+    "pdm_batch_ffn": (C.c_int, [_P, C.c_int32, C.c_void_p, C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p,
+                                C.c_void_p]),
     "pdm_destroy": (C.c_int, [_P]),
     "pdm_strerror": (C.c_char_p, [C.c_int]),
 }

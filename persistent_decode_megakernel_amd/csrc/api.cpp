@@ -5,6 +5,7 @@
 // happens here.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdlib>
 #include <cstring>
 #include <new>
@@ -35,6 +36,7 @@ struct pdm_engine {
   int32_t skip_stage = -1;
   bool cooperative = false;
   bool trace_on = true;
+  uint8_t* batch_ws = nullptr;  // workspace of the batched feed-forward call (allocated on first use)
 };
 
 namespace {
@@ -677,8 +679,183 @@ int pdm_set_trace(pdm_engine* e, int32_t on) {
   return PDM_OK;
 }
 
+// ---- batched products
+
+namespace {
+
+constexpr size_t kWsList = 16;                                             // int32 [kMaxUnion] slot experts
+constexpr size_t kWsUw = 1280;                                             // f32 [kMaxUnion][kBatchMax]
+constexpr size_t kWsH = kWsUw + (size_t)kMaxUnion * kBatchMax * 4 + 256;   // f32 [slot][B][2 F]
+constexpr size_t kSlabBytes = 8 * 4 * 64 * 16;                             // staged activations of 512 columns
+static_assert(kWsList + kMaxUnion * 4 <= kWsUw, "workspace regions do not overlap");
+
+int64_t slabs_of(int64_t K) { return (K + 511) / 512; }
+
+// Most expert slots a batched MoE call can use.
+int batch_slots(const pdm_dims& d, int32_t B, bool moe) {
+  return moe ? std::min(B * d.top_k, d.n_experts) + d.n_shared : 1;
+}
+
+// Bytes of the gate/up output region and of the staged-activation region,
+// sized for the largest call (kBatchMax tokens, every matrix and layer kind).
+void ws_sizes(const pdm_dims& d, size_t* h_bytes, size_t* xg_bytes) {
+  const bool any_moe = std::any_of(d.layer_moe, d.layer_moe + d.n_layers, [](uint8_t m) { return m != 0; });
+  const int n_max = any_moe ? batch_slots(d, kBatchMax, true) : 1;
+  const size_t moe_h = any_moe ? (size_t)n_max * kBatchMax * 2 * d.moe_ffn : 0;
+  *h_bytes = 4 * std::max(moe_h, (size_t)kBatchMax * 2 * d.ffn);
+  const int64_t kmax = std::max({(int64_t)d.hidden, (int64_t)d.q_lora, (int64_t)d.kv_lora, (int64_t)d.ffn,
+                                 (int64_t)d.n_heads * d.v_head, (int64_t)d.moe_ffn});
+  *xg_bytes = kSlabBytes * std::max<size_t>(slabs_of(kmax), any_moe ? (size_t)n_max * slabs_of(d.moe_ffn) : 0);
+}
+
+int ensure_ws(pdm_engine* e) {
+  if (e->batch_ws) return PDM_OK;
+  size_t hb, xg;
+  ws_sizes(e->dims, &hb, &xg);
+  if (hipMalloc(&e->batch_ws, kWsH + ((hb + 255) & ~(size_t)255) + xg) != hipSuccess) {
+    e->batch_ws = nullptr;
+    return PDM_ERR_OOM;
+  }
+  return PDM_OK;
+}
+float* ws_h(pdm_engine* e) { return reinterpret_cast<float*>(e->batch_ws + kWsH); }
+bu32x4* ws_xg(pdm_engine* e) {
+  size_t hb, xg;
+  ws_sizes(e->dims, &hb, &xg);
+  return reinterpret_cast<bu32x4*>(e->batch_ws + kWsH + ((hb + 255) & ~(size_t)255));
+}
+
+int batch_args(const pdm_engine* e, int32_t B, const float* x_dev, const float* y_dev) {
+  int rc = check_engine(e, true);
+  if (rc) return rc;
+  if (B < 1 || B > kBatchMax || !x_dev || !y_dev) return PDM_ERR_ARG;
+  if (reinterpret_cast<uintptr_t>(x_dev) & 15u) return PDM_ERR_ALIGN;  // read in 16-byte pieces
+  return PDM_OK;
+}
+
+}  // namespace
+
+int pdm_batch_gemm(pdm_engine* e, int32_t tensor, int32_t layer, int32_t expert, int32_t part,
+                   const float* x_dev, int32_t B, float* y_dev, pdm_stream_t stream) {
+  int rc = batch_args(e, B, x_dev, y_dev);
+  if (rc) return rc;
+  PackTarget t[2];
+  int n = 0;
+  rc = pack_targets(e->dims, e->plan, tensor, layer, expert, t, &n);
+  if (rc) return rc;
+  if (part < 0 || part >= n) return PDM_ERR_ARG;
+  if (t[part].fmt != PDM_FMT_FP8) return PDM_ERR_CONFIG;
+  DeviceGuard dg(e->device);
+  if ((rc = ensure_ws(e))) return rc;
+  BatchGemm g{};
+  g.base = e->w;
+  g.codes_off = t[part].codes;
+  g.scales_off = t[part].scales;
+  g.rows = t[part].m.rows;
+  g.K = t[part].m.Kp;
+  g.nkb = t[part].m.nkb;
+  g.B = B;
+  g.xg = ws_xg(e);
+  g.y = y_dev;
+  g.ldy = g.rows;
+  batch_gemm_grid(g, 1);
+  BatchStage sa{};
+  sa.x = x_dev;
+  sa.xg = ws_xg(e);
+  sa.ldx = g.K;
+  sa.B = B;
+  sa.K = g.K;
+  sa.nwin = g.slabs * 8;
+  sa.z0 = y_dev;
+  sa.n0 = (size_t)B * g.rows;
+  const hipStream_t st = (hipStream_t)stream;
+  if (launch_batch_stage(sa, false, sa.nwin * 128, st) != hipSuccess) return PDM_ERR_LAUNCH;
+  return launch_batch_gemm(g, 0, 1, st) == hipSuccess ? PDM_OK : PDM_ERR_LAUNCH;
+}
+
+int pdm_batch_ffn(pdm_engine* e, int32_t layer, const float* h_dev, int32_t B, const int32_t* idx_dev,
+                  const float* w_dev, float* y_dev, pdm_stream_t stream) {
+  int rc = batch_args(e, B, h_dev, y_dev);
+  if (rc) return rc;
+  const pdm_dims& d = e->dims;
+  if (layer < 0 || layer >= d.n_layers) return PDM_ERR_ARG;
+  const LayerPlan& L = e->plan.layers[layer];
+  const bool moe = L.is_moe != 0;
+  if (moe && (!idx_dev || !w_dev)) return PDM_ERR_ARG;
+  if (moe && d.expert_format != PDM_FMT_FP8) return PDM_ERR_CONFIG;
+  DeviceGuard dg(e->device);
+  if ((rc = ensure_ws(e))) return rc;
+  int32_t* cnt = reinterpret_cast<int32_t*>(e->batch_ws);
+  int32_t* list = reinterpret_cast<int32_t*>(e->batch_ws + kWsList);
+  float* uw = reinterpret_cast<float*>(e->batch_ws + kWsUw);
+  float* hb = ws_h(e);
+  bu32x4* xg = ws_xg(e);
+  const hipStream_t st = (hipStream_t)stream;
+  const int n_slots = batch_slots(d, B, moe);
+  hipError_t err = moe ? launch_batch_union(idx_dev, w_dev, B, d.top_k, d.n_experts, d.n_shared, cnt, list, uw, st)
+                       : launch_batch_dense_slot(cnt, list, uw, st);
+  if (err != hipSuccess) return PDM_ERR_LAUNCH;
+  const Fp8Mat& gum = moe ? L.egu : L.gu;
+  const Fp8Mat& dnm = moe ? L.edown : L.down;
+  BatchGemm gu{};
+  gu.base = e->w + (moe ? L.expert_base : 0);
+  gu.stride = moe ? L.expert_stride : 0;
+  gu.codes_off = gum.codes;
+  gu.scales_off = gum.scales;
+  gu.rows = gum.rows;
+  gu.K = gum.K;
+  gu.nkb = gum.nkb;
+  gu.B = B;
+  gu.u_count = cnt;
+  gu.u_list = list;
+  gu.xg = xg;
+  gu.y = hb;
+  gu.ldy = gum.rows;
+  batch_gemm_grid(gu, n_slots);
+  BatchGemm dn = gu;
+  dn.codes_off = dnm.codes;
+  dn.scales_off = dnm.scales;
+  dn.rows = dnm.rows;
+  dn.K = dnm.K;
+  dn.nkb = dnm.nkb;
+  dn.y = y_dev;
+  dn.ldy = d.hidden;
+  batch_gemm_grid(dn, n_slots);
+  // stage the input, zero the gate/up outputs of the slots in use and y
+  BatchStage sx{};
+  sx.x = h_dev;
+  sx.xg = xg;
+  sx.ldx = d.hidden;
+  sx.B = B;
+  sx.K = gu.K;
+  sx.nwin = gu.slabs * 8;
+  sx.z0 = hb;
+  sx.c0 = cnt;
+  sx.n0 = (size_t)B * gum.rows;
+  sx.z1 = y_dev;
+  sx.n1 = (size_t)B * d.hidden;
+  if (launch_batch_stage(sx, false, sx.nwin * 128, st) != hipSuccess) return PDM_ERR_LAUNCH;
+  if (launch_batch_gemm(gu, 1, n_slots, st) != hipSuccess) return PDM_ERR_LAUNCH;
+  // stage the weighted SwiGLU activations of every slot for the down product
+  BatchStage sa{};
+  sa.x = hb;
+  sa.uw = uw;
+  sa.u_count = cnt;
+  sa.xg = xg;
+  sa.ldx = gum.rows;
+  sa.B = B;
+  sa.K = dn.K;
+  sa.nwin = dn.slabs * 8;
+  if (launch_batch_stage(sa, true, n_slots * sa.nwin * 128, st) != hipSuccess) return PDM_ERR_LAUNCH;
+  return launch_batch_gemm(dn, 2, n_slots, st) == hipSuccess ? PDM_OK : PDM_ERR_LAUNCH;
+}
+
 int pdm_destroy(pdm_engine* e) {
   if (!e) return PDM_ERR_ARG;
+  if (e->batch_ws) {
+    DeviceGuard g(e->device);
+    (void)hipFree(e->batch_ws);
+  }
   delete e;
   return PDM_OK;
 }

@@ -37,6 +37,56 @@ hipError_t launch_pack(const uint8_t* src_codes, const uint16_t* src_scales, uin
 // Whole-row copy by the pack map (MXFP4 codes or scales): row_bytes per row.
 hipError_t launch_pack_rows(const uint8_t* src, uint8_t* dst, const PackMap& m, int row_bytes, hipStream_t stream);
 hipError_t launch_zero(void* p, size_t bytes, hipStream_t stream);
+// ---- batched products (batch.hip)
+constexpr int kBatchMax = 16;                    // tokens per batched call (MFMA columns)
+constexpr int kMaxExpertsU = 1024;               // routed experts per layer (the dims limit)
+constexpr int kMaxUnion = kBatchMax * 16 + 16;   // union slots: B * top_k routed + shared (top_k + n_shared <= 16)
+
+typedef uint32_t bu32x4 __attribute__((ext_vector_type(4)));
+
+// One batched product. base: the matrix (mode 0) or expert block 0 (modes
+// 1, 2, slot s at base + u_list[s] * stride); codes_off / scales_off: the
+// packed FP8 matrix inside it. xg: the staged activations (whole K slabs;
+// mode 2: one run of slabs per slot, xg_slot u32x4 apart). The geometry
+// fields are set by batch_gemm_grid.
+struct BatchGemm {
+  const uint8_t* base;
+  uint64_t stride;
+  uint64_t codes_off, scales_off;
+  int32_t rows, K, nkb, B;
+  const int32_t* u_count;  // modes 1, 2: slots in use
+  const int32_t* u_list;   // modes 1, 2: expert of each slot
+  const bu32x4* xg;
+  int64_t xg_slot;
+  float* y;                // mode 0, 2: [B][ldy]; mode 1: [slot][B][ldy]
+  int32_t ldy;
+  int32_t tiles, slabs, groups;  // 16-row tiles, 512-column K slabs, 8-tile row groups
+  int32_t spw, splits;           // K slabs per workgroup, K splits per row group
+};
+// Geometry of a launch over n_slots slot matrices (1 for mode 0).
+void batch_gemm_grid(BatchGemm& g, int n_slots);
+hipError_t launch_batch_gemm(const BatchGemm& g, int mode, int n_slots, hipStream_t st);
+
+// A staging pass: x [B][ldx] over K columns (or, act, the SwiGLU activations
+// of every slot in use from gate/up outputs x [slot][B][ldx] with weights
+// uw), written to xg over nwin windows (per slot); it also zeroes n0 floats
+// at z0 (times *c0 when c0 is set) and n1 floats at z1.
+struct BatchStage {
+  const float* x;
+  const float* uw;
+  const int32_t* u_count;
+  bu32x4* xg;
+  int32_t ldx, B, K, nwin;
+  float* z0;
+  const int32_t* c0;
+  float* z1;
+  size_t n0, n1;
+};
+hipError_t launch_batch_stage(const BatchStage& a, bool act, int max_jobs, hipStream_t st);
+hipError_t launch_batch_union(const int32_t* idx, const float* wts, int B, int top_k, int E, int n_shared,
+                              int* u_count, int* u_list, float* uw, hipStream_t st);
+hipError_t launch_batch_dense_slot(int* u_count, int* u_list, float* uw, hipStream_t st);
+
 // Device address of the library's static scratch array on `device`
 // (PDM_STATIC_SCRATCH_BYTES), looked up once per device.
 hipError_t static_scratch(int device, void** ptr);

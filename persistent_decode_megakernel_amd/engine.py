@@ -157,6 +157,42 @@ class Engine:
         return self.lib.pdm_decode_step(self.h, -1 if token is None else int(token), int(pos), _ptr(x_in),
                                         _ptr(logits), _ptr(argmax), self.stream)
 
+    # ------------------------------------------------------------------ batched products
+    def batch_gemm_raw(self, tensor: int, layer: int, expert: int, part: int, x: Optional[torch.Tensor],
+                       B: int, y: Optional[torch.Tensor]) -> int:
+        """pdm_batch_gemm on the bound weights; returns the ABI code."""
+        return self.lib.pdm_batch_gemm(self.h, int(tensor), int(layer), int(expert), int(part), _ptr(x), int(B),
+                                       _ptr(y), self.stream)
+
+    def batch_gemm(self, tensor: int, layer: int, x: torch.Tensor, expert: int = -1, part: int = 0,
+                   out: Optional[torch.Tensor] = None) -> torch.Tensor:
+        """y[b] = W x[b] for the packed FP8 matrix holding (tensor, layer,
+        expert) (rows in packed order); x: f32 [B, K] on the device."""
+        assert x.dtype == torch.float32 and x.is_cuda and x.is_contiguous() and x.dim() == 2
+        lay = L.PackedMatrix()
+        L.check("pdm_packed_layout", self.lib.pdm_packed_layout(C.byref(self.dims), int(tensor), int(layer),
+                                                                int(expert), int(part), C.byref(lay)))
+        y = out if out is not None else torch.empty(x.shape[0], lay.rows, dtype=torch.float32, device=x.device)
+        L.check("pdm_batch_gemm", self.batch_gemm_raw(tensor, layer, expert, part, x, x.shape[0], y))
+        return y
+
+    def batch_ffn_raw(self, layer: int, h: Optional[torch.Tensor], B: int, idx: Optional[torch.Tensor],
+                      w: Optional[torch.Tensor], y: Optional[torch.Tensor]) -> int:
+        """pdm_batch_ffn; returns the ABI code."""
+        return self.lib.pdm_batch_ffn(self.h, int(layer), _ptr(h), int(B), _ptr(idx), _ptr(w), _ptr(y), self.stream)
+
+    def batch_ffn(self, layer: int, h: torch.Tensor, idx: Optional[torch.Tensor] = None,
+                  w: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+        """The SwiGLU / MoE block of `layer` for B tokens (no residual): h f32
+        [B, hidden] normalised inputs, idx int32 [B, top_k] and w f32 [B,
+        top_k] the routing of a MoE layer."""
+        assert h.dtype == torch.float32 and h.is_cuda and h.is_contiguous() and h.dim() == 2
+        if idx is not None:
+            assert idx.dtype == torch.int32 and idx.is_contiguous() and w.dtype == torch.float32 and w.is_contiguous()
+        y = out if out is not None else torch.empty_like(h)
+        L.check("pdm_batch_ffn", self.batch_ffn_raw(layer, h, h.shape[0], idx, w, y))
+        return y
+
     def status(self):
         st = L.Status()
         rc = self.lib.pdm_sync_status(self.h, self.stream, C.byref(st))

@@ -179,3 +179,21 @@ def layer_input(cfg: C.ModelConfig, step: int, attempt: int = 0, seed: int = 0, 
     g = _gen(tensor_seed(seed, "layer_input", step, attempt, extra=3), device)
     x = torch.randn(cfg.hidden, generator=g, device=device, dtype=torch.float32)
     return x.to(torch.bfloat16).view(torch.int16)
+
+
+def batch_rows(B: int, K: int, seed: int = 0, tag: int = 0) -> np.ndarray:
+    """B activation rows [B, K] drawn N(0,1) (float32): the normalised inputs
+    of a batch of B decode tokens."""
+    rng = np.random.default_rng(np.random.SeedSequence([seed, 4, tag, B, K]))
+    return rng.standard_normal((B, K)).astype(np.float32)
+
+
+def batch_routing(cfg: C.ModelConfig, B: int, seed: int = 0, tag: int = 0):
+    """Routing of B tokens: top_k distinct experts per token drawn uniformly
+    (idx int32 [B, top_k]) with positive weights that sum to 1 per token
+    (float32 [B, top_k]), the shape of sigmoid-scored, normalised top-k
+    routing on inputs that favour no expert."""
+    rng = np.random.default_rng(np.random.SeedSequence([seed, 5, tag, B]))
+    idx = np.stack([rng.choice(cfg.n_experts, cfg.top_k, replace=False) for _ in range(B)]).astype(np.int32)
+    w = rng.uniform(0.5, 1.5, size=(B, cfg.top_k))
+    return idx, (w / w.sum(axis=1, keepdims=True)).astype(np.float32)
