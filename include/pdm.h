@@ -473,6 +473,30 @@ int pdm_batch_gemm(pdm_engine* e, int32_t tensor, int32_t layer, int32_t expert,
 int pdm_batch_ffn(pdm_engine* e, int32_t layer, const float* h_dev, int32_t B, const int32_t* idx_dev,
                   const float* w_dev, float* y_dev, pdm_stream_t stream);
 
+/* One decode step of B sequences together (1 <= B <= PDM_BATCH_MAX), each at
+ * its own position with its own latent cache: the batch-1 step per sequence
+ * ("What is TileRT" section 5.2, the DeepSeek-V3 MLA + MoE layer), with every
+ * weight product run once for all B tokens (pdm_batch_gemm, the union of
+ * experts of pdm_batch_ffn) and the per-sequence parts (norms, RoPE, cache
+ * append, attention over the sequence's own cache, routing, argmax) run per
+ * token. Host-launched kernels on the engine's bound weights; the persistent
+ * kernel is not used and its cache is not touched.
+ * tokens: host int32 [B], in [0, vocab) (vocabulary models); positions: host
+ * int32 [B], position of each sequence's token == its cache length, in [0,
+ * max_ctx); x_in_dev: bf16 [B][hidden] inputs of a bare layer stack (vocab 0),
+ * else ignored; caches_dev: bf16 [B][n_layers][max_ctx][kv_lora + rope], the
+ * sequences' latent caches (caller-owned, 16-byte aligned), row positions[b]
+ * of every layer written by the step; logits_dev: f32 [B][vocab] (required
+ * with a vocabulary); argmax_dev: int32 [B] or null; hidden_dev: f32
+ * [n_layers][B][hidden] layer outputs or null. Needs expert_format
+ * PDM_FMT_FP8 when the model has MoE layers. The first call allocates the
+ * engine's batch workspaces (freed by pdm_destroy). Errors: PDM_ERR_UNBOUND,
+ * PDM_ERR_ARG, PDM_ERR_POS, PDM_ERR_CTX, PDM_ERR_TOKEN, PDM_ERR_ALIGN,
+ * PDM_ERR_CONFIG, PDM_ERR_OOM, PDM_ERR_LAUNCH. */
+int pdm_batch_decode_step(pdm_engine* e, int32_t B, const int32_t* tokens, const int32_t* positions,
+                          const uint16_t* x_in_dev, uint16_t* caches_dev, float* logits_dev, int32_t* argmax_dev,
+                          float* hidden_dev, pdm_stream_t stream);
+
 /* Release the engine handle ("What is TileRT" section 6.1, clean up). Never
  * frees caller buffers. Errors: PDM_ERR_ARG. */
 int pdm_destroy(pdm_engine* e);

@@ -104,6 +104,8 @@ _SIGS = {
                                  C.c_void_p, C.c_void_p]),
     "pdm_batch_ffn": (C.c_int, [_P, C.c_int32, C.c_void_p, C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p,
                                 C.c_void_p]),
+    "pdm_batch_decode_step": (C.c_int, [_P, C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
+                                        C.c_void_p, C.c_void_p, C.c_void_p]),
     "pdm_destroy": (C.c_int, [_P]),
     "pdm_strerror": (C.c_char_p, [C.c_int]),
 }

@@ -6,6 +6,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cmath>
 #include <cstdlib>
 #include <cstring>
 #include <new>
@@ -37,6 +38,7 @@ struct pdm_engine {
   bool cooperative = false;
   bool trace_on = true;
   uint8_t* batch_ws = nullptr;  // workspace of the batched feed-forward call (allocated on first use)
+  uint8_t* step_ws = nullptr;   // activations of the batched decode step (allocated on first use)
 };
 
 namespace {
@@ -850,11 +852,160 @@ int pdm_batch_ffn(pdm_engine* e, int32_t layer, const float* h_dev, int32_t B, c
   return launch_batch_gemm(dn, 2, n_slots, st) == hipSuccess ? PDM_OK : PDM_ERR_LAUNCH;
 }
 
+// ---- batched decode step
+
+namespace {
+
+// Activations of a batched step for kBatchMax tokens: offsets (bytes) of each
+// region in the step workspace.
+struct StepWs {
+  size_t x, h, t, qkv, cq, q, qlat, qpe, olat, o, rlog, idx, w, total;
+};
+StepWs step_ws_layout(const pdm_dims& d) {
+  StepWs o{};
+  size_t at = 0;
+  auto take = [&](size_t floats) {
+    const size_t r = at;
+    at += (floats * 4 + 255) & ~(size_t)255;
+    return r;
+  };
+  const size_t B = kBatchMax, H = d.n_heads;
+  o.x = take(B * d.hidden);
+  o.h = take(B * d.hidden);
+  o.t = take(B * d.hidden);
+  o.qkv = take(B * (d.q_lora + d.kv_lora + d.rope));
+  o.cq = take(B * d.q_lora);
+  o.q = take(B * H * (d.qk_nope + d.rope));
+  o.qlat = take(B * H * d.kv_lora);
+  o.qpe = take(B * H * d.rope);
+  o.olat = take(B * H * d.kv_lora);
+  o.o = take(B * H * d.v_head);
+  o.rlog = take(B * std::max(1, d.n_experts));
+  o.idx = take(B * 16);
+  o.w = take(B * 16);
+  o.total = at;
+  return o;
+}
+
+// One batched product over a packed FP8 matrix of the plan (relative offsets).
+int step_gemm(pdm_engine* e, const Fp8Mat& m, const float* x, int B, float* y, hipStream_t st) {
+  BatchGemm g{};
+  g.base = e->w;
+  g.codes_off = m.codes;
+  g.scales_off = m.scales;
+  g.rows = m.rows;
+  g.K = m.K;
+  g.nkb = m.nkb;
+  g.B = B;
+  g.xg = ws_xg(e);
+  g.y = y;
+  g.ldy = g.rows;
+  batch_gemm_grid(g, 1);
+  BatchStage sa{};
+  sa.x = x;
+  sa.xg = ws_xg(e);
+  sa.ldx = g.K;
+  sa.B = B;
+  sa.K = g.K;
+  sa.nwin = g.slabs * 8;
+  sa.z0 = y;
+  sa.n0 = (size_t)B * g.rows;
+  if (launch_batch_stage(sa, false, sa.nwin * 128, st) != hipSuccess) return PDM_ERR_LAUNCH;
+  return launch_batch_gemm(g, 0, 1, st) == hipSuccess ? PDM_OK : PDM_ERR_LAUNCH;
+}
+
+}  // namespace
+
+int pdm_batch_decode_step(pdm_engine* e, int32_t B, const int32_t* tokens, const int32_t* positions,
+                          const uint16_t* x_in_dev, uint16_t* caches_dev, float* logits_dev, int32_t* argmax_dev,
+                          float* hidden_dev, pdm_stream_t stream) {
+  int rc = check_engine(e, true);
+  if (rc) return rc;
+  const pdm_dims& d = e->dims;
+  if (B < 1 || B > kBatchMax || !positions || !caches_dev) return PDM_ERR_ARG;
+  if (reinterpret_cast<uintptr_t>(caches_dev) & 15u) return PDM_ERR_ALIGN;
+  const bool any_moe = std::any_of(d.layer_moe, d.layer_moe + d.n_layers, [](uint8_t m) { return m != 0; });
+  if (any_moe && d.expert_format != PDM_FMT_FP8) return PDM_ERR_CONFIG;
+  BatchTokens tk{};
+  for (int b = 0; b < B; ++b) {
+    if (positions[b] < 0) return PDM_ERR_POS;
+    if (positions[b] >= e->max_ctx) return PDM_ERR_CTX;
+    tk.pos[b] = positions[b];
+    if (d.vocab > 0) {
+      if (!tokens || tokens[b] < 0 || tokens[b] >= d.vocab) return PDM_ERR_TOKEN;
+      tk.token[b] = tokens[b];
+    }
+  }
+  if (d.vocab > 0 && !logits_dev) return PDM_ERR_ARG;
+  if (d.vocab <= 0 && !x_in_dev) return PDM_ERR_TOKEN;
+  DeviceGuard dg(e->device);
+  if ((rc = ensure_ws(e))) return rc;
+  const StepWs L0 = step_ws_layout(d);
+  if (!e->step_ws) {
+    if (hipMalloc(&e->step_ws, L0.total) != hipSuccess) {
+      e->step_ws = nullptr;
+      return PDM_ERR_OOM;
+    }
+  }
+  auto F = [&](size_t off) { return reinterpret_cast<float*>(e->step_ws + off); };
+  float *x = F(L0.x), *h = F(L0.h), *t = F(L0.t), *qkv = F(L0.qkv), *cq = F(L0.cq), *q = F(L0.q);
+  float *qlat = F(L0.qlat), *qpe = F(L0.qpe), *olat = F(L0.olat), *o = F(L0.o), *rlog = F(L0.rlog);
+  int32_t* idx = reinterpret_cast<int32_t*>(e->step_ws + L0.idx);
+  float* wts = F(L0.w);
+  const hipStream_t st = (hipStream_t)stream;
+  const uint8_t* W = e->w;
+  auto gain = [&](uint64_t off) { return reinterpret_cast<const float*>(W + off); };
+  const int D = d.hidden, H = d.n_heads, dc = d.kv_lora, dr = d.rope, kvr = dc + dr;
+  const int64_t seq_stride = (int64_t)d.n_layers * e->max_ctx * kvr;
+  const float tau = (float)(1.0 / std::sqrt((double)(d.qk_nope + d.rope)));
+  const Plan& P = e->plan;
+  auto ok = [](hipError_t x2) { return x2 == hipSuccess; };
+  if (!ok(bs_input(reinterpret_cast<const uint16_t*>(W + P.embed), d.vocab > 0 ? nullptr : x_in_dev, tk, B, D, x, st)))
+    return PDM_ERR_LAUNCH;
+  if (!ok(bs_norm(x, nullptr, false, gain(P.layers[0].attn_norm), d.rms_eps, B, D, h, st))) return PDM_ERR_LAUNCH;
+  for (int l = 0; l < d.n_layers; ++l) {
+    const LayerPlan& Lp = P.layers[l];
+    uint16_t* cache = caches_dev + (size_t)l * e->max_ctx * kvr;
+    if ((rc = step_gemm(e, Lp.qkv, h, B, qkv, st))) return rc;
+    if (!ok(bs_latent(qkv, Lp.qkv.rows, d.q_lora, dc, dr, gain(Lp.q_norm), gain(Lp.kv_norm), d.rms_eps,
+                      d.rope_base, tk, B, cache, seq_stride, cq, st)))
+      return PDM_ERR_LAUNCH;
+    if ((rc = step_gemm(e, Lp.qb, cq, B, q, st))) return rc;
+    if (!ok(bs_absorb(q, W + Lp.uk.codes, reinterpret_cast<const uint16_t*>(W + Lp.uk.scales), Lp.uk.nkb, H,
+                      d.qk_nope, dr, dc, B, d.rope_base, tk, qlat, qpe, st)))
+      return PDM_ERR_LAUNCH;
+    if (!ok(bs_attn(qlat, qpe, cache, seq_stride, H, dc, dr, tau, tk, B, olat, st))) return PDM_ERR_LAUNCH;
+    if (!ok(bs_uv(olat, W + Lp.uv.codes, reinterpret_cast<const uint16_t*>(W + Lp.uv.scales), Lp.uv.nkb, H,
+                  d.v_head, dc, B, o, st)))
+      return PDM_ERR_LAUNCH;
+    if ((rc = step_gemm(e, Lp.wo, o, B, t, st))) return rc;
+    if (!ok(bs_norm(x, t, false, gain(Lp.ffn_norm), d.rms_eps, B, D, h, st))) return PDM_ERR_LAUNCH;
+    if (Lp.is_moe) {
+      if (!ok(bs_bf16_rows(h, reinterpret_cast<const uint16_t*>(W + Lp.router), d.n_experts, D, B, rlog, st)))
+        return PDM_ERR_LAUNCH;
+      if (!ok(bs_topk(rlog, B, d.n_experts, d.top_k, idx, wts, st))) return PDM_ERR_LAUNCH;
+    }
+    if ((rc = pdm_batch_ffn(e, l, h, B, Lp.is_moe ? idx : nullptr, Lp.is_moe ? wts : nullptr, t, stream))) return rc;
+    const float* next = l + 1 < d.n_layers ? gain(P.layers[l + 1].attn_norm) : (d.vocab > 0 ? gain(P.final_norm) : nullptr);
+    if (!ok(bs_norm(x, t, true, next, d.rms_eps, B, D, next ? h : nullptr, st))) return PDM_ERR_LAUNCH;
+    if (hidden_dev && !ok(hipMemcpyAsync(hidden_dev + (size_t)l * B * D, x, (size_t)B * D * 4,
+                                         hipMemcpyDeviceToDevice, st)))
+      return PDM_ERR_LAUNCH;
+  }
+  if (d.vocab > 0) {
+    if (!ok(bs_bf16_rows(h, reinterpret_cast<const uint16_t*>(W + P.lm_head), d.vocab, D, B, logits_dev, st)))
+      return PDM_ERR_LAUNCH;
+    if (argmax_dev && !ok(bs_argmax(logits_dev, B, d.vocab, argmax_dev, st))) return PDM_ERR_LAUNCH;
+  }
+  return PDM_OK;
+}
+
 int pdm_destroy(pdm_engine* e) {
   if (!e) return PDM_ERR_ARG;
-  if (e->batch_ws) {
+  if (e->batch_ws || e->step_ws) {
     DeviceGuard g(e->device);
-    (void)hipFree(e->batch_ws);
+    if (e->batch_ws) (void)hipFree(e->batch_ws);
+    if (e->step_ws) (void)hipFree(e->step_ws);
   }
   delete e;
   return PDM_OK;

@@ -1,0 +1,480 @@
+// The per-token parts of a batched decode step for gfx950: B sequences, each
+// at its own position with its own latent cache, step through the layers
+// together. The weight products run as batched products (batch.hip: every
+// weight byte read once for all B tokens); the kernels here do what is per
+// sequence or per token: embedding rows, RMSNorms and residuals, the latent
+// norms, RoPE and cache append, the absorbed key projection, MLA attention
+// over each sequence's own cache, the per-head value projection, the router
+// and top-k, and the LM head's argmax. The layer computation is the batch-1
+// step of the pages' DeepSeek-V3 layer ("What is TileRT" section 5.2: MLA
+// attention and a routed + shared expert FFN) per token; the batching is the
+// next-step benchmark of the SemiAnalysis TileRT page (batch 2, 4 and 8).
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+
+#include "engine.h"
+
+namespace pdm {
+namespace {
+
+constexpr int kST = 256;  // threads of most kernels here
+typedef __bf16 sbf16x8 __attribute__((ext_vector_type(8)));
+typedef float sf32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t su32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bfv(uint16_t b) { return __builtin_bit_cast(float, (uint32_t)b << 16); }
+__device__ __forceinline__ uint16_t bf_rne(float v) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, v);
+  return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+__device__ __forceinline__ float bf_round(float v) { return bfv(bf_rne(v)); }
+
+// sum over the workgroup (blockDim.x a multiple of 64, <= 1024); red holds 16 floats
+__device__ __forceinline__ float wg_sum(float v, float* red) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  const int wv = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[wv] = v;
+  __syncthreads();
+  float t = 0.f;
+  for (int i = 0; i < nw; ++i) t += red[i];
+  return t;
+}
+
+// FP8 weight of a packed matrix (codes [rows][K], bf16 scales [rows / 8][nkb])
+__device__ __forceinline__ float fp8w(const uint8_t* codes, const uint16_t* scales, int K, int nkb, int r, int c) {
+  const auto f = __builtin_amdgcn_cvt_pk_f32_fp8((int)codes[(size_t)r * K + c], false);
+  return f[0] * bfv(scales[(size_t)(r >> 3) * nkb + (c >> 7)]);
+}
+
+// rotate pairs (2i, 2i + 1) of v[0 .. d) by pos * base^(-2i / d), in double
+__device__ __forceinline__ void rope_pair(float& a, float& b, int i, int d, int pos, double base) {
+  const double ang = (double)pos * pow(base, -2.0 * i / d);
+  const double cs = cos(ang), sn = sin(ang);
+  const double x = a, y = b;
+  a = (float)(x * cs - y * sn);
+  b = (float)(x * sn + y * cs);
+}
+
+}  // namespace
+
+// x[b] = embedding row tokens[b] (bf16 -> f32), or the bf16 input rows.
+__global__ void __launch_bounds__(kST) bs_input_kernel(const uint16_t* embed, const uint16_t* x_in, BatchTokens tk,
+                                                      int D, float* x) {
+  const int b = blockIdx.x;
+  const uint16_t* src = x_in ? x_in + (size_t)b * D : embed + (size_t)tk.token[b] * D;
+  for (int i = threadIdx.x; i < D; i += kST) x[(size_t)b * D + i] = bfv(src[i]);
+}
+
+// x[b] += add[b] (if add), rounded to bf16 (if round), then h[b] =
+// RMSNorm(x[b]) * gain (if h).
+__global__ void __launch_bounds__(kST) bs_norm_kernel(float* x, const float* add, int round, const float* gain,
+                                                     float eps, int D, float* h) {
+  __shared__ float red[16];
+  const int b = blockIdx.x;
+  float* xr = x + (size_t)b * D;
+  float ss = 0.f;
+  for (int i = threadIdx.x; i < D; i += kST) {
+    float v = xr[i];
+    if (add) v += add[(size_t)b * D + i];
+    if (round) v = bf_round(v);
+    xr[i] = v;
+    ss += v * v;
+  }
+  if (!h) return;
+  const float r = 1.0f / sqrtf(wg_sum(ss, red) / D + eps);
+  for (int i = threadIdx.x; i < D; i += kST) h[(size_t)b * D + i] = xr[i] * r * gain[i];
+}
+
+// From [c_q ; c_kv ; k_pe] of token b: RMSNorm(c_q) * q_norm for the query
+// product, and the new cache row [RMSNorm(c_kv) * kv_norm ; RoPE(k_pe)]
+// rounded to bf16 at position pos[b] of sequence b's cache of this layer.
+__global__ void __launch_bounds__(kST) bs_latent_kernel(const float* qkv, int ldq, int dq, int dc, int dr,
+                                                       const float* q_norm, const float* kv_norm, float eps,
+                                                       double base, BatchTokens tk, uint16_t* cache,
+                                                       int64_t seq_stride, float* cq) {
+  __shared__ float red[16];
+  const int b = blockIdx.x;
+  const float* in = qkv + (size_t)b * ldq;
+  float s1 = 0.f, s2 = 0.f;
+  for (int i = threadIdx.x; i < dq; i += kST) s1 += in[i] * in[i];
+  for (int i = threadIdx.x; i < dc; i += kST) s2 += in[dq + i] * in[dq + i];
+  const float r1 = 1.0f / sqrtf(wg_sum(s1, red) / dq + eps);
+  const float r2 = 1.0f / sqrtf(wg_sum(s2, red) / dc + eps);
+  for (int i = threadIdx.x; i < dq; i += kST) cq[(size_t)b * dq + i] = in[i] * r1 * q_norm[i];
+  uint16_t* row = cache + (size_t)b * seq_stride + (size_t)tk.pos[b] * (dc + dr);
+  for (int i = threadIdx.x; i < dc; i += kST) row[i] = bf_rne(in[dq + i] * r2 * kv_norm[i]);
+  for (int i = threadIdx.x; i < dr / 2; i += kST) {
+    float a = in[dq + dc + 2 * i], c = in[dq + dc + 2 * i + 1];
+    rope_pair(a, c, i, dr, tk.pos[b], base);
+    row[dc + 2 * i] = bf_rne(a);
+    row[dc + 2 * i + 1] = bf_rne(c);
+  }
+}
+
+// Head h: q_lat[b][h][c] = sum_n W_UK[h * dn + n][c] * q_nope[b][h][n] (the
+// key projection folded into the query) and the rotated rotary query
+// q_pe[b][h] = RoPE(q[b][h][dn ..], pos[b]). q: [B][H][dn + dr].
+__global__ void __launch_bounds__(kST) bs_absorb_kernel(const float* q, const uint8_t* codes, const uint16_t* scales,
+                                                       int nkb, int H, int dn, int dr, int dc, int B, double base,
+                                                       BatchTokens tk, float* qlat, float* qpe) {
+  extern __shared__ float qn[];  // [B][dn]
+  const int h = blockIdx.x, qkh = dn + dr;
+  for (int i = threadIdx.x; i < B * dn; i += kST) qn[i] = q[((size_t)(i / dn) * H + h) * qkh + i % dn];
+  for (int i = threadIdx.x; i < B * dr / 2; i += kST) {
+    const int b = i / (dr / 2), j = i % (dr / 2);
+    const float* src = q + ((size_t)b * H + h) * qkh + dn;
+    float a = src[2 * j], c = src[2 * j + 1];
+    rope_pair(a, c, j, dr, tk.pos[b], base);
+    qpe[((size_t)b * H + h) * dr + 2 * j] = a;
+    qpe[((size_t)b * H + h) * dr + 2 * j + 1] = c;
+  }
+  __syncthreads();
+  for (int c = threadIdx.x; c < dc; c += kST) {
+    float acc[kBatchMax];
+#pragma unroll
+    for (int b = 0; b < kBatchMax; ++b) acc[b] = 0.f;
+    for (int n = 0; n < dn; ++n) {
+      const float wt = fp8w(codes, scales, dc, nkb, h * dn + n, c);
+#pragma unroll
+      for (int b = 0; b < kBatchMax; ++b)
+        if (b < B) acc[b] += wt * qn[b * dn + n];
+    }
+    for (int b = 0; b < B; ++b) qlat[((size_t)b * H + h) * dc + c] = acc[b];
+  }
+}
+
+// MLA attention of sequence b over its cache positions 0 .. pos[b] for a group
+// of 16 heads (one workgroup of 4 waves): scores S[t][h] = tau * ([q_lat ;
+// q_pe][h] . row t) and values O[h] = sum_t softmax(S)[t][h] * c_t on the
+// matrix cores (v_mfma_f32_16x16x32_bf16: cache rows are bf16 already, the
+// fp32 queries and probabilities enter as a bf16 high part plus a bf16
+// residual), online softmax over blocks of 64 positions. Operand layout
+// (lane l, g = l / 16): A holds A[l % 16][8 g .. 8 g + 7], B holds B[8 g ..
+// 8 g + 7][l % 16], C holds C[4 g .. 4 g + 3][l % 16].
+constexpr int kBlk = 64;
+__global__ void __launch_bounds__(kST) bs_attn_kernel(const float* qlat, const float* qpe, const uint16_t* cache,
+                                                     int64_t seq_stride, int H, int dc, int dr, float tau,
+                                                     BatchTokens tk, float* olat) {
+  extern __shared__ __align__(16) unsigned char lds[];
+  const int kvr = dc + dr, rs = kvr + 8;  // cache-row stride in LDS (bf16), padded
+  const int ngrp = (H + 15) / 16;
+  const int b = blockIdx.x / ngrp, hg = blockIdx.x % ngrp, h0 = hg * 16;
+  const int ctx = tk.pos[b] + 1;
+  __bf16* qh = reinterpret_cast<__bf16*>(lds);                 // [16][rs]
+  __bf16* ql = qh + 16 * rs;                                   // [16][rs]
+  uint16_t* kv = reinterpret_cast<uint16_t*>(ql + 16 * rs);    // [kBlk][rs]
+  float* S = reinterpret_cast<float*>(kv + kBlk * rs);         // [16][kBlk]
+  float* hm = S + 16 * kBlk;                                   // running max, sum, rescale per head
+  float* hl = hm + 16;
+  float* ha = hl + 16;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, lr = lane & 15, lg = lane >> 4;
+  // queries of the group, scaled by tau, split hi / lo (heads past H are zero)
+  for (int i = threadIdx.x; i < 16 * kvr; i += kST) {
+    const int hh = i / kvr, d = i % kvr, hd = h0 + hh;
+    float v = 0.f;
+    if (hd < H) v = tau * (d < dc ? qlat[((size_t)b * H + hd) * dc + d] : qpe[((size_t)b * H + hd) * dr + d - dc]);
+    const float hi = bf_round(v);
+    qh[hh * rs + d] = __builtin_bit_cast(__bf16, bf_rne(v));
+    ql[hh * rs + d] = __builtin_bit_cast(__bf16, bf_rne(v - hi));
+  }
+  if (threadIdx.x < 16) { hm[threadIdx.x] = -INFINITY; hl[threadIdx.x] = 0.f; }
+  const int nt = dc / 64;  // value tiles of 16 dims per wave (dc in {128, 256, 512})
+  sf32x4 acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = (sf32x4){0.f, 0.f, 0.f, 0.f};
+  const uint16_t* seq = cache + (size_t)b * seq_stride;
+  const int q8 = kvr / 8;  // 16-byte pieces per row
+  for (int tb = 0; tb < ctx; tb += kBlk) {
+    const int nb = min(kBlk, ctx - tb);
+    __syncthreads();  // previous block's rows and probabilities are consumed
+    for (int i = threadIdx.x; i < kBlk * q8; i += kST) {
+      const int r = i / q8, p = i % q8;
+      su32x4 v = {0u, 0u, 0u, 0u};
+      if (r < nb) v = *reinterpret_cast<const su32x4*>(seq + (size_t)(tb + r) * kvr + p * 8);
+      *reinterpret_cast<su32x4*>(kv + r * rs + p * 8) = v;
+    }
+    __syncthreads();
+    // scores: wave w takes positions 16 w .. 16 w + 15 of the block
+    {
+      sf32x4 sc = {0.f, 0.f, 0.f, 0.f};
+      if (16 * w < nb) {
+        for (int kb = 0; kb < kvr / 32; ++kb) {
+          const sbf16x8 a = *reinterpret_cast<const sbf16x8*>(kv + (16 * w + lr) * rs + kb * 32 + lg * 8);
+          const sbf16x8 b1 = *reinterpret_cast<const sbf16x8*>(qh + lr * rs + kb * 32 + lg * 8);
+          const sbf16x8 b2 = *reinterpret_cast<const sbf16x8*>(ql + lr * rs + kb * 32 + lg * 8);
+          sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b1, sc, 0, 0, 0);
+          sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b2, sc, 0, 0, 0);
+        }
+      }
+      // sc[i] = S[position 16 w + 4 lg + i][head lr]
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = 16 * w + 4 * lg + i;
+        S[lr * kBlk + t] = t < nb ? sc[i] : -INFINITY;
+      }
+    }
+    __syncthreads();
+    // online softmax: 16 threads per head, 4 positions each
+    {
+      const int hh = threadIdx.x >> 4, sub = threadIdx.x & 15;
+      float* srow = S + hh * kBlk + sub * 4;
+      float mx = fmaxf(fmaxf(srow[0], srow[1]), fmaxf(srow[2], srow[3]));
+#pragma unroll
+      for (int o = 8; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 16));
+      const float mold = hm[hh], mn = fmaxf(mold, mx);
+      float ps = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float p = srow[i] == -INFINITY ? 0.f : __expf(srow[i] - mn);
+        srow[i] = p;
+        ps += p;
+      }
+#pragma unroll
+      for (int o = 8; o > 0; o >>= 1) ps += __shfl_xor(ps, o, 16);
+      __syncthreads();  // every thread has read hm before it changes
+      if (sub == 0) {
+        const float alpha = mold == -INFINITY ? 0.f : __expf(mold - mn);
+        ha[hh] = alpha;
+        hl[hh] = hl[hh] * alpha + ps;
+        hm[hh] = mn;
+      }
+    }
+    __syncthreads();
+    // values: wave w takes dims [w * nt * 16, (w + 1) * nt * 16)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if (i < nt) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[i][r] *= ha[4 * lg + r];
+      }
+    }
+    for (int pb = 0; pb < kBlk / 32; ++pb) {
+      if (pb * 32 >= nb) break;  // uniform
+      const float* prow = S + lr * kBlk + pb * 32 + 8 * lg;
+      sbf16x8 ah, al;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float v = prow[e], hi = bf_round(v);
+        ah[e] = __builtin_bit_cast(__bf16, bf_rne(v));
+        al[e] = __builtin_bit_cast(__bf16, bf_rne(v - hi));
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        if (i < nt) {
+          const int col = (w * nt + i) * 16 + lr;
+          const uint16_t* vcol = kv + (pb * 32 + 8 * lg) * rs + col;
+          sbf16x8 bv;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) bv[e] = __builtin_bit_cast(__bf16, vcol[e * rs]);
+          acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bv, acc[i], 0, 0, 0);
+          acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bv, acc[i], 0, 0, 0);
+        }
+      }
+    }
+  }
+  __syncthreads();
+  // acc[i][r] = O[head 4 lg + r][dim (w nt + i) 16 + lr]
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    if (i < nt) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int hd = h0 + 4 * lg + r;
+        if (hd < H) olat[((size_t)b * H + hd) * dc + (w * nt + i) * 16 + lr] = acc[i][r] / hl[4 * lg + r];
+      }
+    }
+  }
+}
+
+// Head h: o[b][h * dv + v] = sum_c W_UV[h * dv + v][c] * o_lat[b][h][c]; one
+// wave per row, lanes over c.
+__global__ void __launch_bounds__(kST) bs_uv_kernel(const float* olat, const uint8_t* codes, const uint16_t* scales,
+                                                   int nkb, int H, int dv, int dc, int B, float* o) {
+  extern __shared__ float ol[];  // [B][dc]
+  const int h = blockIdx.x, lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  for (int i = threadIdx.x; i < B * dc; i += kST) ol[i] = olat[((size_t)(i / dc) * H + h) * dc + i % dc];
+  __syncthreads();
+  for (int v = w; v < dv; v += kST / 64) {
+    const int r = h * dv + v;
+    float acc[kBatchMax];
+#pragma unroll
+    for (int b = 0; b < kBatchMax; ++b) acc[b] = 0.f;
+    for (int c = lane; c < dc; c += 64) {
+      const float wt = fp8w(codes, scales, dc, nkb, r, c);
+#pragma unroll
+      for (int b = 0; b < kBatchMax; ++b)
+        if (b < B) acc[b] += wt * ol[b * dc + c];
+    }
+    for (int b = 0; b < B; ++b) {
+      float s = acc[b];
+#pragma unroll
+      for (int o2 = 32; o2 > 0; o2 >>= 1) s += __shfl_xor(s, o2, 64);
+      if (lane == 0) o[(size_t)b * H * dv + r] = s;
+    }
+  }
+}
+
+// out[b][r] = sum_k M[r][k] * h[b][k] for a bf16 matrix M [N][K] (router, LM
+// head): one wave per row, 16-byte loads of 8 values, K a multiple of 8.
+__global__ void __launch_bounds__(kST) bs_bf16_rows_kernel(const float* h, const uint16_t* M, int N, int K, int B,
+                                                          float* out) {
+  const int lane = threadIdx.x & 63;
+  const int r = blockIdx.x * (kST / 64) + (threadIdx.x >> 6);
+  if (r >= N) return;  // wave-uniform
+  const uint16_t* row = M + (size_t)r * K;
+  float acc[kBatchMax];
+#pragma unroll
+  for (int b = 0; b < kBatchMax; ++b) acc[b] = 0.f;
+  for (int k8 = lane; k8 < K / 8; k8 += 64) {
+    const su32x4 v = *reinterpret_cast<const su32x4*>(row + k8 * 8);
+    float m[8];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      m[2 * e] = __builtin_bit_cast(float, v[e] << 16);
+      m[2 * e + 1] = __builtin_bit_cast(float, v[e] & 0xFFFF0000u);
+    }
+#pragma unroll
+    for (int b = 0; b < kBatchMax; ++b) {
+      if (b < B) {
+        const float4 x0 = *reinterpret_cast<const float4*>(h + (size_t)b * K + k8 * 8);
+        const float4 x1 = *reinterpret_cast<const float4*>(h + (size_t)b * K + k8 * 8 + 4);
+        acc[b] += m[0] * x0.x + m[1] * x0.y + m[2] * x0.z + m[3] * x0.w + m[4] * x1.x + m[5] * x1.y +
+                  m[6] * x1.z + m[7] * x1.w;
+      }
+    }
+  }
+  for (int b = 0; b < B; ++b) {
+    float s = acc[b];
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o, 64);
+    if (lane == 0) out[(size_t)b * N + r] = s;
+  }
+}
+
+// Token b's routing: sigmoid scores of its E router logits, the top_k (larger
+// first, lower index on ties) and their weights normalised to sum 1. One wave.
+__global__ void __launch_bounds__(64) bs_topk_kernel(const float* logits, int E, int top_k, int32_t* idx, float* wts) {
+  __shared__ float sg[kMaxExpertsU];
+  const int b = blockIdx.x, lane = threadIdx.x;
+  for (int e = lane; e < E; e += 64) sg[e] = 1.0f / (1.0f + __expf(-logits[(size_t)b * E + e]));
+  __syncthreads();
+  float total = 0.f;
+  for (int j = 0; j < top_k; ++j) {
+    float bv = -1.f;
+    int bi = 0x7fffffff;
+    for (int e = lane; e < E; e += 64) {
+      const float v = sg[e];
+      if (v > bv || (v == bv && e < bi)) { bv = v; bi = e; }
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      const float ov = __shfl_xor(bv, o, 64);
+      const int oi = __shfl_xor(bi, o, 64);
+      if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
+    }
+    if (lane == 0) {
+      idx[b * top_k + j] = bi;
+      wts[b * top_k + j] = bv;
+      sg[bi] = -2.f;  // taken
+    }
+    total += bv;
+    __syncthreads();
+  }
+  if (lane < top_k) wts[b * top_k + lane] /= total;
+}
+
+// argmax over V logits of token b (lowest index on ties)
+__global__ void __launch_bounds__(kST) bs_argmax_kernel(const float* logits, int V, int32_t* out) {
+  __shared__ float bvs[kST / 64];
+  __shared__ int bis[kST / 64];
+  const int b = blockIdx.x;
+  float bv = -INFINITY;
+  int bi = 0x7fffffff;
+  for (int i = threadIdx.x; i < V; i += kST) {
+    const float v = logits[(size_t)b * V + i];
+    if (v > bv || (v == bv && i < bi)) { bv = v; bi = i; }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float ov = __shfl_xor(bv, o, 64);
+    const int oi = __shfl_xor(bi, o, 64);
+    if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
+  }
+  if ((threadIdx.x & 63) == 0) { bvs[threadIdx.x >> 6] = bv; bis[threadIdx.x >> 6] = bi; }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    bv = bvs[0];
+    bi = bis[0];
+    for (int i = 1; i < kST / 64; ++i)
+      if (bvs[i] > bv || (bvs[i] == bv && bis[i] < bi)) { bv = bvs[i]; bi = bis[i]; }
+    out[b] = bi;
+  }
+}
+
+// ------------------------------------------------------------------ launchers
+
+hipError_t bs_input(const uint16_t* embed, const uint16_t* x_in, const BatchTokens& tk, int B, int D, float* x,
+                    hipStream_t st) {
+  hipLaunchKernelGGL(bs_input_kernel, dim3(B), dim3(kST), 0, st, embed, x_in, tk, D, x);
+  return hipGetLastError();
+}
+hipError_t bs_norm(float* x, const float* add, bool round, const float* gain, float eps, int B, int D, float* h,
+                   hipStream_t st) {
+  hipLaunchKernelGGL(bs_norm_kernel, dim3(B), dim3(kST), 0, st, x, add, round ? 1 : 0, gain, eps, D, h);
+  return hipGetLastError();
+}
+hipError_t bs_latent(const float* qkv, int ldq, int dq, int dc, int dr, const float* q_norm, const float* kv_norm,
+                     float eps, double base, const BatchTokens& tk, int B, uint16_t* cache, int64_t seq_stride,
+                     float* cq, hipStream_t st) {
+  hipLaunchKernelGGL(bs_latent_kernel, dim3(B), dim3(kST), 0, st, qkv, ldq, dq, dc, dr, q_norm, kv_norm, eps, base,
+                     tk, cache, seq_stride, cq);
+  return hipGetLastError();
+}
+hipError_t bs_absorb(const float* q, const uint8_t* codes, const uint16_t* scales, int nkb, int H, int dn, int dr,
+                     int dc, int B, double base, const BatchTokens& tk, float* qlat, float* qpe, hipStream_t st) {
+  hipLaunchKernelGGL(bs_absorb_kernel, dim3(H), dim3(kST), (size_t)B * dn * 4, st, q, codes, scales, nkb, H, dn, dr,
+                     dc, B, base, tk, qlat, qpe);
+  return hipGetLastError();
+}
+size_t bs_attn_lds(int dc, int dr) {
+  const int rs = dc + dr + 8;
+  return (size_t)2 * 16 * rs * 2 + (size_t)kBlk * rs * 2 + 16 * kBlk * 4 + 48 * 4;
+}
+hipError_t bs_attn(const float* qlat, const float* qpe, const uint16_t* cache, int64_t seq_stride, int H, int dc,
+                   int dr, float tau, const BatchTokens& tk, int B, float* olat, hipStream_t st) {
+  const size_t lds = bs_attn_lds(dc, dr);
+  static bool raised = false;  // more dynamic LDS than the default 64 KB (gfx950 has 160 KB)
+  if (!raised) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&bs_attn_kernel),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    if (e != hipSuccess) return e;
+    raised = true;
+  }
+  hipLaunchKernelGGL(bs_attn_kernel, dim3(B * ((H + 15) / 16)), dim3(kST), lds, st, qlat, qpe, cache, seq_stride, H,
+                     dc, dr, tau, tk, olat);
+  return hipGetLastError();
+}
+hipError_t bs_uv(const float* olat, const uint8_t* codes, const uint16_t* scales, int nkb, int H, int dv, int dc,
+                 int B, float* o, hipStream_t st) {
+  hipLaunchKernelGGL(bs_uv_kernel, dim3(H), dim3(kST), (size_t)B * dc * 4, st, olat, codes, scales, nkb, H, dv, dc,
+                     B, o);
+  return hipGetLastError();
+}
+hipError_t bs_bf16_rows(const float* h, const uint16_t* M, int N, int K, int B, float* out, hipStream_t st) {
+  hipLaunchKernelGGL(bs_bf16_rows_kernel, dim3((N + kST / 64 - 1) / (kST / 64)), dim3(kST), 0, st, h, M, N, K, B,
+                     out);
+  return hipGetLastError();
+}
+hipError_t bs_topk(const float* logits, int B, int E, int top_k, int32_t* idx, float* wts, hipStream_t st) {
+  hipLaunchKernelGGL(bs_topk_kernel, dim3(B), dim3(64), 0, st, logits, E, top_k, idx, wts);
+  return hipGetLastError();
+}
+hipError_t bs_argmax(const float* logits, int B, int V, int32_t* out, hipStream_t st) {
+  hipLaunchKernelGGL(bs_argmax_kernel, dim3(B), dim3(kST), 0, st, logits, V, out);
+  return hipGetLastError();
+}
+
+}  // namespace pdm

@@ -87,6 +87,28 @@ hipError_t launch_batch_union(const int32_t* idx, const float* wts, int B, int t
                               int* u_count, int* u_list, float* uw, hipStream_t st);
 hipError_t launch_batch_dense_slot(int* u_count, int* u_list, float* uw, hipStream_t st);
 
+// ---- per-token kernels of a batched decode step (batch_step.hip)
+struct BatchTokens {
+  int32_t token[kBatchMax];  // input token of each sequence (vocabulary models)
+  int32_t pos[kBatchMax];    // its position == its cache length before the step
+};
+hipError_t bs_input(const uint16_t* embed, const uint16_t* x_in, const BatchTokens& tk, int B, int D, float* x,
+                    hipStream_t st);
+hipError_t bs_norm(float* x, const float* add, bool round, const float* gain, float eps, int B, int D, float* h,
+                   hipStream_t st);
+hipError_t bs_latent(const float* qkv, int ldq, int dq, int dc, int dr, const float* q_norm, const float* kv_norm,
+                     float eps, double base, const BatchTokens& tk, int B, uint16_t* cache, int64_t seq_stride,
+                     float* cq, hipStream_t st);
+hipError_t bs_absorb(const float* q, const uint8_t* codes, const uint16_t* scales, int nkb, int H, int dn, int dr,
+                     int dc, int B, double base, const BatchTokens& tk, float* qlat, float* qpe, hipStream_t st);
+hipError_t bs_attn(const float* qlat, const float* qpe, const uint16_t* cache, int64_t seq_stride, int H, int dc,
+                   int dr, float tau, const BatchTokens& tk, int B, float* olat, hipStream_t st);
+hipError_t bs_uv(const float* olat, const uint8_t* codes, const uint16_t* scales, int nkb, int H, int dv, int dc,
+                 int B, float* o, hipStream_t st);
+hipError_t bs_bf16_rows(const float* h, const uint16_t* M, int N, int K, int B, float* out, hipStream_t st);
+hipError_t bs_topk(const float* logits, int B, int E, int top_k, int32_t* idx, float* wts, hipStream_t st);
+hipError_t bs_argmax(const float* logits, int B, int V, int32_t* out, hipStream_t st);
+
 // Device address of the library's static scratch array on `device`
 // (PDM_STATIC_SCRATCH_BYTES), looked up once per device.
 hipError_t static_scratch(int device, void** ptr);

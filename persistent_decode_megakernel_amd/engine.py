@@ -193,6 +193,33 @@ class Engine:
         L.check("pdm_batch_ffn", self.batch_ffn_raw(layer, h, h.shape[0], idx, w, y))
         return y
 
+    def batch_caches(self, B: int) -> torch.Tensor:
+        """Zeroed latent caches for B sequences: bf16 bits [B, n_layers, max_ctx, kv_lora + rope]."""
+        return torch.zeros(B, self.cfg.n_layers, self.max_ctx, self.cfg.kv_lora + self.cfg.rope, dtype=torch.int16,
+                           device=self.device)
+
+    def batch_decode_step_raw(self, tokens, positions, caches, x_in=None, logits=None, argmax=None,
+                              hidden=None) -> int:
+        """pdm_batch_decode_step; returns the ABI code."""
+        B = len(positions)
+        pos = (C.c_int32 * B)(*[int(p) for p in positions])
+        tok = None if tokens is None else (C.c_int32 * B)(*[int(t) for t in tokens])
+        return self.lib.pdm_batch_decode_step(self.h, B, tok, pos, _ptr(x_in), _ptr(caches), _ptr(logits),
+                                              _ptr(argmax), _ptr(hidden), self.stream)
+
+    def batch_decode_step(self, positions, caches: torch.Tensor, tokens=None, x_in: Optional[torch.Tensor] = None,
+                          hidden: Optional[torch.Tensor] = None):
+        """One decode step of B = len(positions) sequences (asynchronous).
+        Returns (argmax int32 [B], logits f32 [B, vocab]) device tensors, or
+        (None, None) for a bare layer stack."""
+        B = len(positions)
+        lg = am = None
+        if self.cfg.vocab > 0:
+            lg = torch.empty(B, self.cfg.vocab, dtype=torch.float32, device=self.device)
+            am = torch.empty(B, dtype=torch.int32, device=self.device)
+        L.check("pdm_batch_decode_step", self.batch_decode_step_raw(tokens, positions, caches, x_in, lg, am, hidden))
+        return am, lg
+
     def status(self):
         st = L.Status()
         rc = self.lib.pdm_sync_status(self.h, self.stream, C.byref(st))
