@@ -16,9 +16,10 @@ request; this is the headline figure). Then the bare DeepSeek-V3-shaped dense
 and MoE layers are timed per layer-step, alternating over two weight copies so
 that no step is served from the MALL, and the weight products of one MoE layer
 are timed at batch 1, 2, 4 and 8 (pdm_batch_gemm / pdm_batch_ffn, several
-sequences sharing every weight byte). Prints one JSON line with tok/s/user,
-TPOT, the HBM roofline fraction, a stage trace, the single-layer timings, the
-batch points and the CPU oracle baseline.
+sequences sharing every weight byte), as are whole batched decode steps of the
+stack (pdm_batch_decode_step). Prints one JSON line with tok/s/user, TPOT, the
+HBM roofline fraction, a stage trace, the single-layer timings, the batch
+points and the CPU oracle baseline.
 """
 from __future__ import annotations
 
@@ -320,6 +321,53 @@ def batch_points(eng, cfg, batches, reps: int = 20):
             "points": pts}
 
 
+def batch_step_points(eng, cfg, batches, steps: int = 16, warm: int = 2):
+    """Whole decode steps of B sequences at once on the stack
+    (pdm_batch_decode_step): each sequence has its own cache holding the
+    workload's prompt latents and steps through teacher-forced random tokens
+    at positions prompt_len + j. Timed with HIP events over `steps` steps after
+    `warm` untimed ones (which also append cache rows). Per-user speed is 1 /
+    step time, total throughput B / step time."""
+    import torch
+    from synth import gen
+    P = cfg.prompt_len
+    lat = [gen.latent_rows(cfg, l, P, SEED, device="cuda") for l in range(cfg.n_layers)]
+    stream = torch.cuda.current_stream()
+    pts = []
+    for B in batches:
+        caches = eng.batch_caches(B)
+        for b in range(B):
+            for l in range(cfg.n_layers):
+                caches[b, l, :P] = lat[l]
+        toks = [[gen.decode_token(cfg, j, 0, SEED + 1 + b) for b in range(B)] for j in range(warm + steps)]
+        lg = torch.empty(B, cfg.vocab, device="cuda")
+        am = torch.empty(B, dtype=torch.int32, device="cuda")
+
+        def step(j):
+            rc = eng.batch_decode_step_raw(toks[j], [P + j] * B, caches, logits=lg, argmax=am)
+            if rc != 0:
+                raise SystemExit(f"batched step failed: {rc}")
+        for j in range(warm):
+            step(j)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for j in range(warm, warm + steps):
+            step(j)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        t = e0.elapsed_time(e1) / 1e3 / steps
+        pts.append({"B": B, "ms_per_step": round(t * 1e3, 3), "tok_s_user": round(1 / t, 1),
+                    "tok_s_total": round(B / t, 1)})
+        log(f"batched step B={B}: {t * 1e3:.3f} ms/step, {1 / t:.1f} tok/s/user, {B / t:.1f} tok/s total")
+        del caches
+        torch.cuda.empty_cache()
+    return {"workload": f"{cfg.name}: B sequences per step, each with its own {P}-position prompt cache, "
+                        f"teacher-forced random tokens, context {P + warm + 1}..{P + warm + steps}",
+            "api": "pdm_batch_decode_step (host-launched kernels; batched MFMA weight products, union of experts)",
+            "points": pts}
+
+
 def layer_steps(name: str, copies: int, steps: int, warm: int = 2):
     """Microseconds per step of one bare DeepSeek-V3-shaped layer (dense or
     MoE, fed an N(0,1) bf16 hidden vector, 1024-position prompt cache).
@@ -436,6 +484,8 @@ def main():
     results = [run_workload(eng, c, K, Wm, not args.no_trace, args.trace_detail and i == 0, args.resident_only)
                for i, c in enumerate(cfgs)]
     batch = batch_points(eng, head, [int(b) for b in args.batch.split(",") if b]) if args.batch else None
+    bsteps = (batch_step_points(eng, head, [int(b) for b in args.batch.split(",") if b])
+              if args.batch and head.vocab > 0 else None)
     if args.mxfp4:
         # a second engine: the expert matrices are MXFP4 (everything else as above)
         c4 = configs.get(args.mxfp4)
@@ -498,6 +548,8 @@ def main():
     }
     if batch is not None:
         out["batch_points"] = batch
+    if bsteps is not None:
+        out["batch_step_points"] = bsteps
     if args.layers:
         del eng
         torch.cuda.empty_cache()

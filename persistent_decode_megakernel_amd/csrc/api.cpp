@@ -859,7 +859,7 @@ namespace {
 // Activations of a batched step for kBatchMax tokens: offsets (bytes) of each
 // region in the step workspace.
 struct StepWs {
-  size_t x, h, t, qkv, cq, q, qlat, qpe, olat, o, rlog, idx, w, total;
+  size_t x, h, t, qkv, cq, q, qlat, qpe, olat, o, rlog, idx, w, part, argv, argi, total;
 };
 StepWs step_ws_layout(const pdm_dims& d) {
   StepWs o{};
@@ -883,6 +883,9 @@ StepWs step_ws_layout(const pdm_dims& d) {
   o.rlog = take(B * std::max(1, d.n_experts));
   o.idx = take(B * 16);
   o.w = take(B * 16);
+  o.part = take(B * H * kAttnChunksMax * (d.kv_lora + 2));
+  o.argv = take(B * kArgPartsMax);
+  o.argi = take(B * kArgPartsMax);
   o.total = at;
   return o;
 }
@@ -951,6 +954,7 @@ int pdm_batch_decode_step(pdm_engine* e, int32_t B, const int32_t* tokens, const
   float *x = F(L0.x), *h = F(L0.h), *t = F(L0.t), *qkv = F(L0.qkv), *cq = F(L0.cq), *q = F(L0.q);
   float *qlat = F(L0.qlat), *qpe = F(L0.qpe), *olat = F(L0.olat), *o = F(L0.o), *rlog = F(L0.rlog);
   int32_t* idx = reinterpret_cast<int32_t*>(e->step_ws + L0.idx);
+  float* part = F(L0.part);
   float* wts = F(L0.w);
   const hipStream_t st = (hipStream_t)stream;
   const uint8_t* W = e->w;
@@ -974,7 +978,7 @@ int pdm_batch_decode_step(pdm_engine* e, int32_t B, const int32_t* tokens, const
     if (!ok(bs_absorb(q, W + Lp.uk.codes, reinterpret_cast<const uint16_t*>(W + Lp.uk.scales), Lp.uk.nkb, H,
                       d.qk_nope, dr, dc, B, d.rope_base, tk, qlat, qpe, st)))
       return PDM_ERR_LAUNCH;
-    if (!ok(bs_attn(qlat, qpe, cache, seq_stride, H, dc, dr, tau, tk, B, olat, st))) return PDM_ERR_LAUNCH;
+    if (!ok(bs_attn(qlat, qpe, cache, seq_stride, H, dc, dr, tau, tk, B, part, olat, st))) return PDM_ERR_LAUNCH;
     if (!ok(bs_uv(olat, W + Lp.uv.codes, reinterpret_cast<const uint16_t*>(W + Lp.uv.scales), Lp.uv.nkb, H,
                   d.v_head, dc, B, o, st)))
       return PDM_ERR_LAUNCH;
@@ -995,7 +999,9 @@ int pdm_batch_decode_step(pdm_engine* e, int32_t B, const int32_t* tokens, const
   if (d.vocab > 0) {
     if (!ok(bs_bf16_rows(h, reinterpret_cast<const uint16_t*>(W + P.lm_head), d.vocab, D, B, logits_dev, st)))
       return PDM_ERR_LAUNCH;
-    if (argmax_dev && !ok(bs_argmax(logits_dev, B, d.vocab, argmax_dev, st))) return PDM_ERR_LAUNCH;
+    if (argmax_dev && !ok(bs_argmax(logits_dev, B, d.vocab, F(L0.argv), reinterpret_cast<int32_t*>(e->step_ws + L0.argi),
+                                    argmax_dev, st)))
+      return PDM_ERR_LAUNCH;
   }
   return PDM_OK;
 }

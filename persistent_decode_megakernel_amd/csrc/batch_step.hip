@@ -11,6 +11,7 @@
 // next-step benchmark of the SemiAnalysis TileRT page (batch 2, 4 and 8).
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 
 #include "engine.h"
@@ -69,23 +70,35 @@ __global__ void __launch_bounds__(kST) bs_input_kernel(const uint16_t* embed, co
 }
 
 // x[b] += add[b] (if add), rounded to bf16 (if round), then h[b] =
-// RMSNorm(x[b]) * gain (if h).
-__global__ void __launch_bounds__(kST) bs_norm_kernel(float* x, const float* add, int round, const float* gain,
+// RMSNorm(x[b]) * gain (if h). D a multiple of 4, rows 16-byte aligned.
+constexpr int kNT = 1024;
+__global__ void __launch_bounds__(kNT) bs_norm_kernel(float* x, const float* add, int round, const float* gain,
                                                      float eps, int D, float* h) {
   __shared__ float red[16];
-  const int b = blockIdx.x;
-  float* xr = x + (size_t)b * D;
+  const int b = blockIdx.x, n4 = D / 4;
+  float4* xr = reinterpret_cast<float4*>(x + (size_t)b * D);
+  const float4* ar = add ? reinterpret_cast<const float4*>(add + (size_t)b * D) : nullptr;
   float ss = 0.f;
-  for (int i = threadIdx.x; i < D; i += kST) {
-    float v = xr[i];
-    if (add) v += add[(size_t)b * D + i];
-    if (round) v = bf_round(v);
+  for (int i = threadIdx.x; i < n4; i += kNT) {
+    float4 v = xr[i];
+    if (ar) {
+      const float4 a = ar[i];
+      v.x += a.x; v.y += a.y; v.z += a.z; v.w += a.w;
+    }
+    if (round) {
+      v.x = bf_round(v.x); v.y = bf_round(v.y); v.z = bf_round(v.z); v.w = bf_round(v.w);
+    }
     xr[i] = v;
-    ss += v * v;
+    ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
   }
-  if (!h) return;
+  if (!h) return;  // uniform
   const float r = 1.0f / sqrtf(wg_sum(ss, red) / D + eps);
-  for (int i = threadIdx.x; i < D; i += kST) h[(size_t)b * D + i] = xr[i] * r * gain[i];
+  const float4* g4 = reinterpret_cast<const float4*>(gain);
+  float4* h4 = reinterpret_cast<float4*>(h + (size_t)b * D);
+  for (int i = threadIdx.x; i < n4; i += kNT) {
+    const float4 v = xr[i], g = g4[i];
+    h4[i] = make_float4(v.x * r * g.x, v.y * r * g.y, v.z * r * g.z, v.w * r * g.w);
+  }
 }
 
 // From [c_q ; c_kv ; k_pe] of token b: RMSNorm(c_q) * q_norm for the query
@@ -116,14 +129,15 @@ __global__ void __launch_bounds__(kST) bs_latent_kernel(const float* qkv, int ld
 
 // Head h: q_lat[b][h][c] = sum_n W_UK[h * dn + n][c] * q_nope[b][h][n] (the
 // key projection folded into the query) and the rotated rotary query
-// q_pe[b][h] = RoPE(q[b][h][dn ..], pos[b]). q: [B][H][dn + dr].
-__global__ void __launch_bounds__(kST) bs_absorb_kernel(const float* q, const uint8_t* codes, const uint16_t* scales,
+// q_pe[b][h] = RoPE(q[b][h][dn ..], pos[b]). q: [B][H][dn + dr]. One thread
+// per 4 columns (dc / 4 threads), the rows' codes loaded 8 rows at a time.
+__global__ void __launch_bounds__(128) bs_absorb_kernel(const float* q, const uint8_t* codes, const uint16_t* scales,
                                                        int nkb, int H, int dn, int dr, int dc, int B, double base,
                                                        BatchTokens tk, float* qlat, float* qpe) {
   extern __shared__ float qn[];  // [B][dn]
-  const int h = blockIdx.x, qkh = dn + dr;
-  for (int i = threadIdx.x; i < B * dn; i += kST) qn[i] = q[((size_t)(i / dn) * H + h) * qkh + i % dn];
-  for (int i = threadIdx.x; i < B * dr / 2; i += kST) {
+  const int h = blockIdx.x, qkh = dn + dr, nt = blockDim.x;
+  for (int i = threadIdx.x; i < B * dn; i += nt) qn[i] = q[((size_t)(i / dn) * H + h) * qkh + i % dn];
+  for (int i = threadIdx.x; i < B * dr / 2; i += nt) {
     const int b = i / (dr / 2), j = i % (dr / 2);
     const float* src = q + ((size_t)b * H + h) * qkh + dn;
     float a = src[2 * j], c = src[2 * j + 1];
@@ -132,18 +146,39 @@ __global__ void __launch_bounds__(kST) bs_absorb_kernel(const float* q, const ui
     qpe[((size_t)b * H + h) * dr + 2 * j + 1] = c;
   }
   __syncthreads();
-  for (int c = threadIdx.x; c < dc; c += kST) {
-    float acc[kBatchMax];
+  const int c0 = threadIdx.x * 4;  // dc == 4 * blockDim.x
+  float acc[4][kBatchMax];
 #pragma unroll
-    for (int b = 0; b < kBatchMax; ++b) acc[b] = 0.f;
-    for (int n = 0; n < dn; ++n) {
-      const float wt = fp8w(codes, scales, dc, nkb, h * dn + n, c);
+  for (int e = 0; e < 4; ++e)
 #pragma unroll
-      for (int b = 0; b < kBatchMax; ++b)
-        if (b < B) acc[b] += wt * qn[b * dn + n];
+    for (int b = 0; b < kBatchMax; ++b) acc[e][b] = 0.f;
+  for (int n0 = 0; n0 < dn; n0 += 8) {
+    uint32_t cw[8];
+    float sc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int r = h * dn + n0 + i;
+      cw[i] = *reinterpret_cast<const uint32_t*>(codes + (size_t)r * dc + c0);
+      sc[i] = bfv(scales[(size_t)(r >> 3) * nkb + (c0 >> 7)]);
     }
-    for (int b = 0; b < B; ++b) qlat[((size_t)b * H + h) * dc + c] = acc[b];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)cw[i], false);
+      const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)cw[i], true);
+      const float wv[4] = {lo[0] * sc[i], lo[1] * sc[i], hi[0] * sc[i], hi[1] * sc[i]};
+#pragma unroll
+      for (int b = 0; b < kBatchMax; ++b) {
+        if (b < B) {
+          const float qv = qn[b * dn + n0 + i];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[e][b] += wv[e] * qv;
+        }
+      }
+    }
   }
+  for (int b = 0; b < B; ++b)
+    *reinterpret_cast<float4*>(qlat + ((size_t)b * H + h) * dc + c0) =
+        make_float4(acc[0][b], acc[1][b], acc[2][b], acc[3][b]);
 }
 
 // MLA attention of sequence b over its cache positions 0 .. pos[b] for a group
@@ -157,12 +192,14 @@ __global__ void __launch_bounds__(kST) bs_absorb_kernel(const float* q, const ui
 constexpr int kBlk = 64;
 __global__ void __launch_bounds__(kST) bs_attn_kernel(const float* qlat, const float* qpe, const uint16_t* cache,
                                                      int64_t seq_stride, int H, int dc, int dr, float tau,
-                                                     BatchTokens tk, float* olat) {
+                                                     BatchTokens tk, int nch, int chunk, float* part) {
   extern __shared__ __align__(16) unsigned char lds[];
   const int kvr = dc + dr, rs = kvr + 8;  // cache-row stride in LDS (bf16), padded
   const int ngrp = (H + 15) / 16;
-  const int b = blockIdx.x / ngrp, hg = blockIdx.x % ngrp, h0 = hg * 16;
-  const int ctx = tk.pos[b] + 1;
+  const int ch = blockIdx.x % nch, bh = blockIdx.x / nch;
+  const int b = bh / ngrp, hg = bh % ngrp, h0 = hg * 16;
+  const int ctx = tk.pos[b] + 1, t0 = ch * chunk, t1 = min(ctx, t0 + chunk);
+  if (t0 >= ctx) return;  // no positions in this chunk for this sequence (workgroup-uniform)
   __bf16* qh = reinterpret_cast<__bf16*>(lds);                 // [16][rs]
   __bf16* ql = qh + 16 * rs;                                   // [16][rs]
   uint16_t* kv = reinterpret_cast<uint16_t*>(ql + 16 * rs);    // [kBlk][rs]
@@ -187,8 +224,8 @@ __global__ void __launch_bounds__(kST) bs_attn_kernel(const float* qlat, const f
   for (int i = 0; i < 8; ++i) acc[i] = (sf32x4){0.f, 0.f, 0.f, 0.f};
   const uint16_t* seq = cache + (size_t)b * seq_stride;
   const int q8 = kvr / 8;  // 16-byte pieces per row
-  for (int tb = 0; tb < ctx; tb += kBlk) {
-    const int nb = min(kBlk, ctx - tb);
+  for (int tb = t0; tb < t1; tb += kBlk) {
+    const int nb = min(kBlk, t1 - tb);
     __syncthreads();  // previous block's rows and probabilities are consumed
     for (int i = threadIdx.x; i < kBlk * q8; i += kST) {
       const int r = i / q8, p = i % q8;
@@ -276,43 +313,93 @@ __global__ void __launch_bounds__(kST) bs_attn_kernel(const float* qlat, const f
     }
   }
   __syncthreads();
+  // the chunk's partial per head: [acc (dc) ; max ; sum] at part[b][h][ch];
   // acc[i][r] = O[head 4 lg + r][dim (w nt + i) 16 + lr]
+  const int ps = dc + 2;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     if (i < nt) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int hd = h0 + 4 * lg + r;
-        if (hd < H) olat[((size_t)b * H + hd) * dc + (w * nt + i) * 16 + lr] = acc[i][r] / hl[4 * lg + r];
+        if (hd < H) part[(((size_t)b * H + hd) * nch + ch) * ps + (w * nt + i) * 16 + lr] = acc[i][r];
       }
     }
+  }
+  if (threadIdx.x < 16 && h0 + (int)threadIdx.x < H) {
+    float* pm = part + (((size_t)b * H + h0 + threadIdx.x) * nch + ch) * ps + dc;
+    pm[0] = hm[threadIdx.x];
+    pm[1] = hl[threadIdx.x];
+  }
+}
+
+// Merge of sequence b's chunk partials for head h: o_lat = sum_i acc_i
+// e^(m_i - m) / sum_i l_i e^(m_i - m), m the largest m_i.
+__global__ void __launch_bounds__(kST) bs_attn_merge_kernel(const float* part, int H, int dc, int nch, int chunk,
+                                                           BatchTokens tk, float* olat) {
+  const int b = blockIdx.x / H, h = blockIdx.x % H, ps = dc + 2;
+  const int n = (tk.pos[b] + 1 + chunk - 1) / chunk;  // chunks with positions
+  const float* pb = part + ((size_t)b * H + h) * nch * ps;
+  float m = -INFINITY;
+  for (int i = 0; i < n; ++i) m = fmaxf(m, pb[i * ps + dc]);
+  float l = 0.f;
+  for (int i = 0; i < n; ++i) l += pb[i * ps + dc + 1] * __expf(pb[i * ps + dc] - m);
+  for (int c = threadIdx.x; c < dc; c += kST) {
+    float o = 0.f;
+    for (int i = 0; i < n; ++i) o += pb[i * ps + c] * __expf(pb[i * ps + dc] - m);
+    olat[((size_t)b * H + h) * dc + c] = o / l;
   }
 }
 
 // Head h: o[b][h * dv + v] = sum_c W_UV[h * dv + v][c] * o_lat[b][h][c]; one
-// wave per row, lanes over c.
+// wave per row, each lane 4 columns per pass (dword loads), rows in pairs.
 __global__ void __launch_bounds__(kST) bs_uv_kernel(const float* olat, const uint8_t* codes, const uint16_t* scales,
                                                    int nkb, int H, int dv, int dc, int B, float* o) {
   extern __shared__ float ol[];  // [B][dc]
   const int h = blockIdx.x, lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   for (int i = threadIdx.x; i < B * dc; i += kST) ol[i] = olat[((size_t)(i / dc) * H + h) * dc + i % dc];
   __syncthreads();
-  for (int v = w; v < dv; v += kST / 64) {
-    const int r = h * dv + v;
-    float acc[kBatchMax];
+  const int passes = (dc / 4 + 63) / 64;  // 1 or 2 (dc <= 512)
+  for (int v0 = 2 * w; v0 < dv; v0 += 2 * (kST / 64)) {
+    uint32_t cw[2][2];
+    float sc[2][2];
 #pragma unroll
-    for (int b = 0; b < kBatchMax; ++b) acc[b] = 0.f;
-    for (int c = lane; c < dc; c += 64) {
-      const float wt = fp8w(codes, scales, dc, nkb, r, c);
+    for (int rr = 0; rr < 2; ++rr) {
+      const int r = h * dv + v0 + rr;
 #pragma unroll
-      for (int b = 0; b < kBatchMax; ++b)
-        if (b < B) acc[b] += wt * ol[b * dc + c];
+      for (int p = 0; p < 2; ++p) {
+        const int c0 = (p * 64 + lane) * 4;
+        const bool in = p < passes && c0 < dc && v0 + rr < dv;
+        cw[rr][p] = in ? *reinterpret_cast<const uint32_t*>(codes + (size_t)r * dc + c0) : 0u;
+        sc[rr][p] = in ? bfv(scales[(size_t)(r >> 3) * nkb + (c0 >> 7)]) : 0.f;
+      }
     }
-    for (int b = 0; b < B; ++b) {
-      float s = acc[b];
 #pragma unroll
-      for (int o2 = 32; o2 > 0; o2 >>= 1) s += __shfl_xor(s, o2, 64);
-      if (lane == 0) o[(size_t)b * H * dv + r] = s;
+    for (int rr = 0; rr < 2; ++rr) {
+      float acc[kBatchMax];
+#pragma unroll
+      for (int b = 0; b < kBatchMax; ++b) acc[b] = 0.f;
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        const int c0 = (p * 64 + lane) * 4;
+        if (p < passes && c0 < dc) {
+          const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)cw[rr][p], false);
+          const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)cw[rr][p], true);
+#pragma unroll
+          for (int b = 0; b < kBatchMax; ++b) {
+            if (b < B) {
+              const float4 x4 = *reinterpret_cast<const float4*>(ol + b * dc + c0);
+              acc[b] += sc[rr][p] * (lo[0] * x4.x + lo[1] * x4.y + hi[0] * x4.z + hi[1] * x4.w);
+            }
+          }
+        }
+      }
+      for (int b = 0; b < B; ++b) {
+        float s2 = acc[b];
+#pragma unroll
+        for (int o2 = 32; o2 > 0; o2 >>= 1) s2 += __shfl_xor(s2, o2, 64);
+        if (lane == 0 && v0 + rr < dv) o[(size_t)b * H * dv + h * dv + v0 + rr] = s2;
+      }
     }
   }
 }
@@ -386,32 +473,38 @@ __global__ void __launch_bounds__(64) bs_topk_kernel(const float* logits, int E,
   if (lane < top_k) wts[b * top_k + lane] /= total;
 }
 
-// argmax over V logits of token b (lowest index on ties)
-__global__ void __launch_bounds__(kST) bs_argmax_kernel(const float* logits, int V, int32_t* out) {
+// argmax over V logits of token b (lowest index on ties), in two stages:
+// kArgParts workgroups per token each reduce a range, then one wave per token
+// reduces the parts.
+constexpr int kArgParts = kArgPartsMax;
+__device__ __forceinline__ void arg_better(float& bv, int& bi, float ov, int oi) {
+  if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
+}
+__global__ void __launch_bounds__(kST) bs_argmax_part_kernel(const float* logits, int V, float* pv, int32_t* pi) {
   __shared__ float bvs[kST / 64];
   __shared__ int bis[kST / 64];
-  const int b = blockIdx.x;
+  const int b = blockIdx.x / kArgParts, part = blockIdx.x % kArgParts;
+  const int per = (V + kArgParts - 1) / kArgParts, i0 = part * per, i1 = min(V, i0 + per);
   float bv = -INFINITY;
   int bi = 0x7fffffff;
-  for (int i = threadIdx.x; i < V; i += kST) {
-    const float v = logits[(size_t)b * V + i];
-    if (v > bv || (v == bv && i < bi)) { bv = v; bi = i; }
-  }
+  for (int i = i0 + threadIdx.x; i < i1; i += kST) arg_better(bv, bi, logits[(size_t)b * V + i], i);
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    const float ov = __shfl_xor(bv, o, 64);
-    const int oi = __shfl_xor(bi, o, 64);
-    if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
-  }
+  for (int o = 32; o > 0; o >>= 1) arg_better(bv, bi, __shfl_xor(bv, o, 64), __shfl_xor(bi, o, 64));
   if ((threadIdx.x & 63) == 0) { bvs[threadIdx.x >> 6] = bv; bis[threadIdx.x >> 6] = bi; }
   __syncthreads();
-  if (threadIdx.x == 0) {
-    bv = bvs[0];
-    bi = bis[0];
-    for (int i = 1; i < kST / 64; ++i)
-      if (bvs[i] > bv || (bvs[i] == bv && bis[i] < bi)) { bv = bvs[i]; bi = bis[i]; }
-    out[b] = bi;
+  if (threadIdx.x == 0) {  // holds wave 0's result already
+    for (int i = 1; i < kST / 64; ++i) arg_better(bv, bi, bvs[i], bis[i]);
+    pv[blockIdx.x] = bv;
+    pi[blockIdx.x] = bi;
   }
+}
+__global__ void __launch_bounds__(64) bs_argmax_final_kernel(const float* pv, const int32_t* pi, int32_t* out) {
+  const int b = blockIdx.x, lane = threadIdx.x;
+  float bv = pv[b * kArgParts + lane];
+  int bi = pi[b * kArgParts + lane];
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) arg_better(bv, bi, __shfl_xor(bv, o, 64), __shfl_xor(bi, o, 64));
+  if (lane == 0) out[b] = bi;
 }
 
 // ------------------------------------------------------------------ launchers
@@ -423,7 +516,7 @@ hipError_t bs_input(const uint16_t* embed, const uint16_t* x_in, const BatchToke
 }
 hipError_t bs_norm(float* x, const float* add, bool round, const float* gain, float eps, int B, int D, float* h,
                    hipStream_t st) {
-  hipLaunchKernelGGL(bs_norm_kernel, dim3(B), dim3(kST), 0, st, x, add, round ? 1 : 0, gain, eps, D, h);
+  hipLaunchKernelGGL(bs_norm_kernel, dim3(B), dim3(kNT), 0, st, x, add, round ? 1 : 0, gain, eps, D, h);
   return hipGetLastError();
 }
 hipError_t bs_latent(const float* qkv, int ldq, int dq, int dc, int dr, const float* q_norm, const float* kv_norm,
@@ -435,16 +528,22 @@ hipError_t bs_latent(const float* qkv, int ldq, int dq, int dc, int dr, const fl
 }
 hipError_t bs_absorb(const float* q, const uint8_t* codes, const uint16_t* scales, int nkb, int H, int dn, int dr,
                      int dc, int B, double base, const BatchTokens& tk, float* qlat, float* qpe, hipStream_t st) {
-  hipLaunchKernelGGL(bs_absorb_kernel, dim3(H), dim3(kST), (size_t)B * dn * 4, st, q, codes, scales, nkb, H, dn, dr,
-                     dc, B, base, tk, qlat, qpe);
+  hipLaunchKernelGGL(bs_absorb_kernel, dim3(H), dim3(dc / 4), (size_t)B * dn * 4, st, q, codes, scales, nkb, H, dn,
+                     dr, dc, B, base, tk, qlat, qpe);
   return hipGetLastError();
 }
 size_t bs_attn_lds(int dc, int dr) {
   const int rs = dc + dr + 8;
   return (size_t)2 * 16 * rs * 2 + (size_t)kBlk * rs * 2 + 16 * kBlk * 4 + 48 * 4;
 }
+// Position chunk of the attention workgroups for a longest context of ctx:
+// at least 128 positions, at most kAttnChunksMax chunks.
+int bs_attn_chunk(int ctx) {
+  const int c = std::max(128, (ctx + kAttnChunksMax - 1) / kAttnChunksMax);
+  return (c + kBlk - 1) / kBlk * kBlk;
+}
 hipError_t bs_attn(const float* qlat, const float* qpe, const uint16_t* cache, int64_t seq_stride, int H, int dc,
-                   int dr, float tau, const BatchTokens& tk, int B, float* olat, hipStream_t st) {
+                   int dr, float tau, const BatchTokens& tk, int B, float* part, float* olat, hipStream_t st) {
   const size_t lds = bs_attn_lds(dc, dr);
   static bool raised = false;  // more dynamic LDS than the default 64 KB (gfx950 has 160 KB)
   if (!raised) {
@@ -453,8 +552,12 @@ hipError_t bs_attn(const float* qlat, const float* qpe, const uint16_t* cache, i
     if (e != hipSuccess) return e;
     raised = true;
   }
-  hipLaunchKernelGGL(bs_attn_kernel, dim3(B * ((H + 15) / 16)), dim3(kST), lds, st, qlat, qpe, cache, seq_stride, H,
-                     dc, dr, tau, tk, olat);
+  int ctx = 1;
+  for (int b = 0; b < B; ++b) ctx = std::max(ctx, tk.pos[b] + 1);
+  const int chunk = bs_attn_chunk(ctx), nch = (ctx + chunk - 1) / chunk;
+  hipLaunchKernelGGL(bs_attn_kernel, dim3(B * ((H + 15) / 16) * nch), dim3(kST), lds, st, qlat, qpe, cache,
+                     seq_stride, H, dc, dr, tau, tk, nch, chunk, part);
+  hipLaunchKernelGGL(bs_attn_merge_kernel, dim3(B * H), dim3(kST), 0, st, part, H, dc, nch, chunk, tk, olat);
   return hipGetLastError();
 }
 hipError_t bs_uv(const float* olat, const uint8_t* codes, const uint16_t* scales, int nkb, int H, int dv, int dc,
@@ -472,8 +575,10 @@ hipError_t bs_topk(const float* logits, int B, int E, int top_k, int32_t* idx, f
   hipLaunchKernelGGL(bs_topk_kernel, dim3(B), dim3(64), 0, st, logits, E, top_k, idx, wts);
   return hipGetLastError();
 }
-hipError_t bs_argmax(const float* logits, int B, int V, int32_t* out, hipStream_t st) {
-  hipLaunchKernelGGL(bs_argmax_kernel, dim3(B), dim3(kST), 0, st, logits, V, out);
+hipError_t bs_argmax(const float* logits, int B, int V, float* part_v, int32_t* part_i, int32_t* out,
+                     hipStream_t st) {
+  hipLaunchKernelGGL(bs_argmax_part_kernel, dim3(B * kArgParts), dim3(kST), 0, st, logits, V, part_v, part_i);
+  hipLaunchKernelGGL(bs_argmax_final_kernel, dim3(B), dim3(64), 0, st, part_v, part_i, out);
   return hipGetLastError();
 }
 

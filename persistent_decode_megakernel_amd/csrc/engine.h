@@ -101,13 +101,18 @@ hipError_t bs_latent(const float* qkv, int ldq, int dq, int dc, int dr, const fl
                      float* cq, hipStream_t st);
 hipError_t bs_absorb(const float* q, const uint8_t* codes, const uint16_t* scales, int nkb, int H, int dn, int dr,
                      int dc, int B, double base, const BatchTokens& tk, float* qlat, float* qpe, hipStream_t st);
+constexpr int kAttnChunksMax = 32;  // position chunks per (sequence, head group) of the batched attention
+// part: f32 [B][H][kAttnChunksMax][kv_lora + 2] chunk partials
 hipError_t bs_attn(const float* qlat, const float* qpe, const uint16_t* cache, int64_t seq_stride, int H, int dc,
-                   int dr, float tau, const BatchTokens& tk, int B, float* olat, hipStream_t st);
+                   int dr, float tau, const BatchTokens& tk, int B, float* part, float* olat, hipStream_t st);
 hipError_t bs_uv(const float* olat, const uint8_t* codes, const uint16_t* scales, int nkb, int H, int dv, int dc,
                  int B, float* o, hipStream_t st);
 hipError_t bs_bf16_rows(const float* h, const uint16_t* M, int N, int K, int B, float* out, hipStream_t st);
 hipError_t bs_topk(const float* logits, int B, int E, int top_k, int32_t* idx, float* wts, hipStream_t st);
-hipError_t bs_argmax(const float* logits, int B, int V, int32_t* out, hipStream_t st);
+constexpr int kArgPartsMax = 64;    // argmax parts per token
+// part_v, part_i: [B][kArgPartsMax] scratch
+hipError_t bs_argmax(const float* logits, int B, int V, float* part_v, int32_t* part_i, int32_t* out,
+                     hipStream_t st);
 
 // Device address of the library's static scratch array on `device`
 // (PDM_STATIC_SCRATCH_BYTES), looked up once per device.
