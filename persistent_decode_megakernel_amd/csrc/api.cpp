@@ -963,6 +963,7 @@ int pdm_batch_decode_step(pdm_engine* e, int32_t B, const int32_t* tokens, const
   const int64_t seq_stride = (int64_t)d.n_layers * e->max_ctx * kvr;
   const float tau = (float)(1.0 / std::sqrt((double)(d.qk_nope + d.rope)));
   const Plan& P = e->plan;
+  const float* rope_tab = reinterpret_cast<const float*>(e->abs.rope_tab);
   auto ok = [](hipError_t x2) { return x2 == hipSuccess; };
   if (!ok(bs_input(reinterpret_cast<const uint16_t*>(W + P.embed), d.vocab > 0 ? nullptr : x_in_dev, tk, B, D, x, st)))
     return PDM_ERR_LAUNCH;
@@ -971,12 +972,12 @@ int pdm_batch_decode_step(pdm_engine* e, int32_t B, const int32_t* tokens, const
     const LayerPlan& Lp = P.layers[l];
     uint16_t* cache = caches_dev + (size_t)l * e->max_ctx * kvr;
     if ((rc = step_gemm(e, Lp.qkv, h, B, qkv, st))) return rc;
-    if (!ok(bs_latent(qkv, Lp.qkv.rows, d.q_lora, dc, dr, gain(Lp.q_norm), gain(Lp.kv_norm), d.rms_eps,
-                      d.rope_base, tk, B, cache, seq_stride, cq, st)))
+    if (!ok(bs_latent(qkv, Lp.qkv.rows, d.q_lora, dc, dr, gain(Lp.q_norm), gain(Lp.kv_norm), d.rms_eps, rope_tab, tk,
+                      B, cache, seq_stride, cq, st)))
       return PDM_ERR_LAUNCH;
     if ((rc = step_gemm(e, Lp.qb, cq, B, q, st))) return rc;
     if (!ok(bs_absorb(q, W + Lp.uk.codes, reinterpret_cast<const uint16_t*>(W + Lp.uk.scales), Lp.uk.nkb, H,
-                      d.qk_nope, dr, dc, B, d.rope_base, tk, qlat, qpe, st)))
+                      d.qk_nope, dr, dc, B, rope_tab, tk, qlat, qpe, st)))
       return PDM_ERR_LAUNCH;
     if (!ok(bs_attn(qlat, qpe, cache, seq_stride, H, dc, dr, tau, tk, B, part, olat, st))) return PDM_ERR_LAUNCH;
     if (!ok(bs_uv(olat, W + Lp.uv.codes, reinterpret_cast<const uint16_t*>(W + Lp.uv.scales), Lp.uv.nkb, H,

@@ -31,6 +31,23 @@ __device__ __forceinline__ uint16_t bf_rne(float v) {
 }
 __device__ __forceinline__ float bf_round(float v) { return bfv(bf_rne(v)); }
 
+// dst[i] = src(i) for i < n, by the NT threads of the workgroup, 8 loads per
+// thread in flight: the loads are unconditional (indices past n repeat the
+// last element), so no load waits for the one before it.
+template <int NT, class F>
+__device__ __forceinline__ void copy_in(float* dst, int n, F src) {
+  for (int i0 = 0; i0 < n; i0 += 8 * NT) {
+    float v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = src(min(i0 + j * NT + (int)threadIdx.x, n - 1));
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int i = i0 + j * NT + (int)threadIdx.x;
+      if (i < n) dst[i] = v[j];
+    }
+  }
+}
+
 // sum over the workgroup (blockDim.x a multiple of 64, <= 1024); red holds 16 floats
 __device__ __forceinline__ float wg_sum(float v, float* red) {
 #pragma unroll
@@ -50,13 +67,14 @@ __device__ __forceinline__ float fp8w(const uint8_t* codes, const uint16_t* scal
   return f[0] * bfv(scales[(size_t)(r >> 3) * nkb + (c >> 7)]);
 }
 
-// rotate pairs (2i, 2i + 1) of v[0 .. d) by pos * base^(-2i / d), in double
-__device__ __forceinline__ void rope_pair(float& a, float& b, int i, int d, int pos, double base) {
-  const double ang = (double)pos * pow(base, -2.0 * i / d);
-  const double cs = cos(ang), sn = sin(ang);
-  const double x = a, y = b;
-  a = (float)(x * cs - y * sn);
-  b = (float)(x * sn + y * cs);
+// rotate the pair (2i, 2i + 1) by pos * base^(-2i / d): tab_row is row pos
+// of the engine's RoPE table, (cos, sin) of each pair's angle (computed in
+// float64 when the engine was bound)
+__device__ __forceinline__ void rope_pair(float& a, float& b, const float* tab_row, int i) {
+  const float cs = tab_row[2 * i], sn = tab_row[2 * i + 1];
+  const float x = a, y = b;
+  a = x * cs - y * sn;
+  b = x * sn + y * cs;
 }
 
 }  // namespace
@@ -106,7 +124,7 @@ __global__ void __launch_bounds__(kNT) bs_norm_kernel(float* x, const float* add
 // rounded to bf16 at position pos[b] of sequence b's cache of this layer.
 __global__ void __launch_bounds__(kST) bs_latent_kernel(const float* qkv, int ldq, int dq, int dc, int dr,
                                                        const float* q_norm, const float* kv_norm, float eps,
-                                                       double base, BatchTokens tk, uint16_t* cache,
+                                                       const float* rope_tab, BatchTokens tk, uint16_t* cache,
                                                        int64_t seq_stride, float* cq) {
   __shared__ float red[16];
   const int b = blockIdx.x;
@@ -121,7 +139,7 @@ __global__ void __launch_bounds__(kST) bs_latent_kernel(const float* qkv, int ld
   for (int i = threadIdx.x; i < dc; i += kST) row[i] = bf_rne(in[dq + i] * r2 * kv_norm[i]);
   for (int i = threadIdx.x; i < dr / 2; i += kST) {
     float a = in[dq + dc + 2 * i], c = in[dq + dc + 2 * i + 1];
-    rope_pair(a, c, i, dr, tk.pos[b], base);
+    rope_pair(a, c, rope_tab + (size_t)tk.pos[b] * dr, i);
     row[dc + 2 * i] = bf_rne(a);
     row[dc + 2 * i + 1] = bf_rne(c);
   }
@@ -129,56 +147,94 @@ __global__ void __launch_bounds__(kST) bs_latent_kernel(const float* qkv, int ld
 
 // Head h: q_lat[b][h][c] = sum_n W_UK[h * dn + n][c] * q_nope[b][h][n] (the
 // key projection folded into the query) and the rotated rotary query
-// q_pe[b][h] = RoPE(q[b][h][dn ..], pos[b]). q: [B][H][dn + dr]. One thread
-// per 4 columns (dc / 4 threads), the rows' codes loaded 8 rows at a time.
-__global__ void __launch_bounds__(128) bs_absorb_kernel(const float* q, const uint8_t* codes, const uint16_t* scales,
-                                                       int nkb, int H, int dn, int dr, int dc, int B, double base,
-                                                       BatchTokens tk, float* qlat, float* qpe) {
-  extern __shared__ float qn[];  // [B][dn]
-  const int h = blockIdx.x, qkh = dn + dr, nt = blockDim.x;
-  for (int i = threadIdx.x; i < B * dn; i += nt) qn[i] = q[((size_t)(i / dn) * H + h) * qkh + i % dn];
-  for (int i = threadIdx.x; i < B * dr / 2; i += nt) {
-    const int b = i / (dr / 2), j = i % (dr / 2);
-    const float* src = q + ((size_t)b * H + h) * qkh + dn;
-    float a = src[2 * j], c = src[2 * j + 1];
-    rope_pair(a, c, j, dr, tk.pos[b], base);
-    qpe[((size_t)b * H + h) * dr + 2 * j] = a;
-    qpe[((size_t)b * H + h) * dr + 2 * j + 1] = c;
+// q_pe[b][h] = RoPE(q[b][h][dn ..], pos[b]). q: [B][H][dn + dr]. A workgroup
+// takes the columns of one column part (256 columns, or all of a narrower
+// latent) of one head: thread t handles 4 columns (t mod column threads) of
+// one group of rows (t / column threads), with every row's codes and scale of
+// its group loaded at once (one memory round trip), and the groups' sums meet
+// in LDS.
+constexpr int kAbT = 512;     // threads per absorb workgroup
+constexpr int kAbRows = 32;   // rows per thread and load batch
+__host__ __device__ __forceinline__ int ab_col_parts(int dc) { return dc >= 256 ? dc / 256 : 1; }
+__global__ void __launch_bounds__(kAbT) bs_absorb_kernel(const float* q, const uint8_t* codes, const uint16_t* scales,
+                                                        int nkb, int H, int dn, int dr, int dc, int B,
+                                                        const float* rope_tab, BatchTokens tk, float* qlat, float* qpe) {
+  extern __shared__ float ab_lds[];  // q_nope [B][dn], column sums [B][wcols]
+  const int cps = ab_col_parts(dc), h = blockIdx.x / cps, cpart = blockIdx.x % cps, qkh = dn + dr;
+  const int wcols = dc / cps, nct = wcols / 4, ng = kAbT / nct;
+  const int ct = threadIdx.x % nct, rg = threadIdx.x / nct;
+  float* qn = ab_lds;
+  float* red = ab_lds + B * dn;
+  const int rpg = (dn + ng - 1) / ng, n_beg = min(dn, rg * rpg), n_end = min(dn, n_beg + rpg);
+  const int c0 = cpart * wcols + ct * 4;
+  // the group's codes and scales first: they do not depend on the queries
+  uint32_t cw[kAbRows];
+  float sc[kAbRows];
+#pragma unroll
+  for (int i = 0; i < kAbRows; ++i) {  // unconditional loads (past the group: its first row, unused)
+    const int n = n_beg + i;
+    const int r = h * dn + (n < n_end ? n : min(n_beg, dn - 1));
+    cw[i] = *reinterpret_cast<const uint32_t*>(codes + (size_t)r * dc + c0);
+    sc[i] = bfv(scales[(size_t)(r >> 3) * nkb + (c0 >> 7)]);
+  }
+  copy_in<kAbT>(qn, B * dn, [&](int i) { return q[((size_t)(i / dn) * H + h) * qkh + i % dn]; });
+  for (int i = threadIdx.x; i < B * wcols; i += kAbT) red[i] = 0.f;
+  if (cpart == 0) {
+    for (int i = threadIdx.x; i < B * dr / 2; i += kAbT) {
+      const int b = i / (dr / 2), j = i % (dr / 2);
+      const float* src = q + ((size_t)b * H + h) * qkh + dn;
+      float a = src[2 * j], c = src[2 * j + 1];
+      rope_pair(a, c, rope_tab + (size_t)tk.pos[b] * dr, j);
+      qpe[((size_t)b * H + h) * dr + 2 * j] = a;
+      qpe[((size_t)b * H + h) * dr + 2 * j + 1] = c;
+    }
   }
   __syncthreads();
-  const int c0 = threadIdx.x * 4;  // dc == 4 * blockDim.x
   float acc[4][kBatchMax];
 #pragma unroll
   for (int e = 0; e < 4; ++e)
 #pragma unroll
     for (int b = 0; b < kBatchMax; ++b) acc[e][b] = 0.f;
-  for (int n0 = 0; n0 < dn; n0 += 8) {
-    uint32_t cw[8];
-    float sc[8];
+  for (int n0 = n_beg; n0 < n_end; n0 += kAbRows) {
+    if (n0 > n_beg) {  // rows past the first batch (a row group longer than kAbRows)
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int r = h * dn + n0 + i;
-      cw[i] = *reinterpret_cast<const uint32_t*>(codes + (size_t)r * dc + c0);
-      sc[i] = bfv(scales[(size_t)(r >> 3) * nkb + (c0 >> 7)]);
+      for (int i = 0; i < kAbRows; ++i) {
+        const int n = n0 + i;
+        const int r = h * dn + (n < n_end ? n : n0);
+        cw[i] = *reinterpret_cast<const uint32_t*>(codes + (size_t)r * dc + c0);
+        sc[i] = bfv(scales[(size_t)(r >> 3) * nkb + (c0 >> 7)]);
+      }
     }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)cw[i], false);
-      const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)cw[i], true);
-      const float wv[4] = {lo[0] * sc[i], lo[1] * sc[i], hi[0] * sc[i], hi[1] * sc[i]};
+    for (int i = 0; i < kAbRows; ++i) {
+      if (n0 + i < n_end) {
+        const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)cw[i], false);
+        const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)cw[i], true);
+        const float wv[4] = {lo[0] * sc[i], lo[1] * sc[i], hi[0] * sc[i], hi[1] * sc[i]};
 #pragma unroll
-      for (int b = 0; b < kBatchMax; ++b) {
-        if (b < B) {
-          const float qv = qn[b * dn + n0 + i];
+        for (int b = 0; b < kBatchMax; ++b) {
+          if (b < B) {
+            const float qv = qn[b * dn + n0 + i];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) acc[e][b] += wv[e] * qv;
+            for (int e = 0; e < 4; ++e) acc[e][b] = fmaf(wv[e], qv, acc[e][b]);
+          }
         }
       }
     }
   }
-  for (int b = 0; b < B; ++b)
-    *reinterpret_cast<float4*>(qlat + ((size_t)b * H + h) * dc + c0) =
-        make_float4(acc[0][b], acc[1][b], acc[2][b], acc[3][b]);
+  if (n_beg < n_end) {
+#pragma unroll
+    for (int b = 0; b < kBatchMax; ++b) {
+      if (b < B) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          __hip_atomic_fetch_add(&red[b * wcols + ct * 4 + e], acc[e][b], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      }
+    }
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < B * wcols; i += kAbT)
+    qlat[((size_t)(i / wcols) * H + h) * dc + cpart * wcols + i % wcols] = red[i];
 }
 
 // MLA attention of sequence b over its cache positions 0 .. pos[b] for a group
@@ -190,6 +246,9 @@ __global__ void __launch_bounds__(128) bs_absorb_kernel(const float* q, const ui
 // (lane l, g = l / 16): A holds A[l % 16][8 g .. 8 g + 7], B holds B[8 g ..
 // 8 g + 7][l % 16], C holds C[4 g .. 4 g + 3][l % 16].
 constexpr int kBlk = 64;
+constexpr int kAtMaxRow = 640;                              // kv_lora + rope, at most 512 + 128
+constexpr int kAtLd = (kBlk * (kAtMaxRow / 8) + kST - 1) / kST;  // 16-byte cache pieces per thread and block
+constexpr int kAtQ = (16 * kAtMaxRow + kST - 1) / kST;           // query values per thread
 __global__ void __launch_bounds__(kST) bs_attn_kernel(const float* qlat, const float* qpe, const uint16_t* cache,
                                                      int64_t seq_stride, int H, int dc, int dr, float tau,
                                                      BatchTokens tk, int nch, int chunk, float* part) {
@@ -208,32 +267,61 @@ __global__ void __launch_bounds__(kST) bs_attn_kernel(const float* qlat, const f
   float* hl = hm + 16;
   float* ha = hl + 16;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, lr = lane & 15, lg = lane >> 4;
-  // queries of the group, scaled by tau, split hi / lo (heads past H are zero)
-  for (int i = threadIdx.x; i < 16 * kvr; i += kST) {
-    const int hh = i / kvr, d = i % kvr, hd = h0 + hh;
-    float v = 0.f;
-    if (hd < H) v = tau * (d < dc ? qlat[((size_t)b * H + hd) * dc + d] : qpe[((size_t)b * H + hd) * dr + d - dc]);
-    const float hi = bf_round(v);
-    qh[hh * rs + d] = __builtin_bit_cast(__bf16, bf_rne(v));
-    ql[hh * rs + d] = __builtin_bit_cast(__bf16, bf_rne(v - hi));
+  const uint16_t* seq = cache + (size_t)b * seq_stride;
+  const int q8 = kvr / 8;  // 16-byte pieces per row
+  // A block's cache rows: every piece a thread copies is loaded at once into
+  // registers (one memory round trip), the next block's while this one is used.
+  // The loads are unconditional (pieces past the block read its first row and
+  // are zeroed when stored): no branch around them, so none waits for another.
+  su32x4 kvr_regs[kAtLd];
+  auto load_block = [&](int tb) {
+    const int nb = min(kBlk, t1 - tb);
+#pragma unroll
+    for (int j = 0; j < kAtLd; ++j) {
+      const int i = (int)threadIdx.x + j * kST, r = i / q8, p = i - r * q8;
+      const bool ok = i < kBlk * q8 && r < nb;
+      kvr_regs[j] = *reinterpret_cast<const su32x4*>(seq + (size_t)(tb + (ok ? r : 0)) * kvr + (ok ? p : 0) * 8);
+    }
+  };
+  load_block(t0);
+  // queries of the group, scaled by tau, split hi / lo (heads past H are zero):
+  // all of a thread's values are loaded before any is stored
+  {
+    float qv[kAtQ];
+#pragma unroll
+    for (int j = 0; j < kAtQ; ++j) {
+      const int i = (int)threadIdx.x + j * kST, hh = i / kvr, d = i - hh * kvr, hd = h0 + hh;
+      const bool ok = i < 16 * kvr && hd < H;
+      const int hq = ok ? hd : h0, dq = ok ? d : 0;
+      const float* src = dq < dc ? qlat + ((size_t)b * H + hq) * dc + dq : qpe + ((size_t)b * H + hq) * dr + dq - dc;
+      qv[j] = *src;
+    }
+#pragma unroll
+    for (int j = 0; j < kAtQ; ++j) {
+      const int i = (int)threadIdx.x + j * kST, hh = i / kvr, d = i - hh * kvr;
+      if (i < 16 * kvr) {
+        const float v = h0 + hh < H ? tau * qv[j] : 0.f, hi = bf_round(v);
+        qh[hh * rs + d] = __builtin_bit_cast(__bf16, bf_rne(v));
+        ql[hh * rs + d] = __builtin_bit_cast(__bf16, bf_rne(v - hi));
+      }
+    }
   }
   if (threadIdx.x < 16) { hm[threadIdx.x] = -INFINITY; hl[threadIdx.x] = 0.f; }
   const int nt = dc / 64;  // value tiles of 16 dims per wave (dc in {128, 256, 512})
   sf32x4 acc[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) acc[i] = (sf32x4){0.f, 0.f, 0.f, 0.f};
-  const uint16_t* seq = cache + (size_t)b * seq_stride;
-  const int q8 = kvr / 8;  // 16-byte pieces per row
   for (int tb = t0; tb < t1; tb += kBlk) {
     const int nb = min(kBlk, t1 - tb);
     __syncthreads();  // previous block's rows and probabilities are consumed
-    for (int i = threadIdx.x; i < kBlk * q8; i += kST) {
-      const int r = i / q8, p = i % q8;
-      su32x4 v = {0u, 0u, 0u, 0u};
-      if (r < nb) v = *reinterpret_cast<const su32x4*>(seq + (size_t)(tb + r) * kvr + p * 8);
-      *reinterpret_cast<su32x4*>(kv + r * rs + p * 8) = v;
+#pragma unroll
+    for (int j = 0; j < kAtLd; ++j) {
+      const int i = (int)threadIdx.x + j * kST, r = i / q8, p = i - r * q8;
+      if (i < kBlk * q8)
+        *reinterpret_cast<su32x4*>(kv + r * rs + p * 8) = r < nb ? kvr_regs[j] : (su32x4){0u, 0u, 0u, 0u};
     }
     __syncthreads();
+    if (tb + kBlk < t1) load_block(tb + kBlk);
     // scores: wave w takes positions 16 w .. 16 w + 15 of the block
     {
       sf32x4 sc = {0.f, 0.f, 0.f, 0.f};
@@ -334,110 +422,182 @@ __global__ void __launch_bounds__(kST) bs_attn_kernel(const float* qlat, const f
 }
 
 // Merge of sequence b's chunk partials for head h: o_lat = sum_i acc_i
-// e^(m_i - m) / sum_i l_i e^(m_i - m), m the largest m_i.
+// e^(m_i - m) / sum_i l_i e^(m_i - m), m the largest m_i. One wave reduces
+// the chunks' (m_i, l_i) (one chunk per lane), then every thread adds its
+// columns over the chunks.
 __global__ void __launch_bounds__(kST) bs_attn_merge_kernel(const float* part, int H, int dc, int nch, int chunk,
                                                            BatchTokens tk, float* olat) {
+  static_assert(kAttnChunksMax <= 64, "one lane per chunk");
+  __shared__ float wch[kAttnChunksMax];
+  __shared__ float linv;
   const int b = blockIdx.x / H, h = blockIdx.x % H, ps = dc + 2;
-  const int n = (tk.pos[b] + 1 + chunk - 1) / chunk;  // chunks with positions
+  const int n = (tk.pos[b] + 1 + chunk - 1) / chunk;  // chunks with positions (<= nch <= 64)
   const float* pb = part + ((size_t)b * H + h) * nch * ps;
-  float m = -INFINITY;
-  for (int i = 0; i < n; ++i) m = fmaxf(m, pb[i * ps + dc]);
-  float l = 0.f;
-  for (int i = 0; i < n; ++i) l += pb[i * ps + dc + 1] * __expf(pb[i * ps + dc] - m);
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    const float mi = lane < n ? pb[lane * ps + dc] : -INFINITY;
+    const float li = lane < n ? pb[lane * ps + dc + 1] : 0.f;
+    float m = mi;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+    const float wi = lane < n ? __expf(mi - m) : 0.f;
+    float l = li * wi;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) l += __shfl_xor(l, o, 64);
+    if (lane < n) wch[lane] = wi;
+    if (lane == 0) linv = 1.0f / l;
+  }
+  __syncthreads();
   for (int c = threadIdx.x; c < dc; c += kST) {
+    float v[kAttnChunksMax];
+#pragma unroll
+    for (int i = 0; i < kAttnChunksMax; ++i) v[i] = pb[min(i, n - 1) * ps + c];  // unconditional loads
     float o = 0.f;
-    for (int i = 0; i < n; ++i) o += pb[i * ps + c] * __expf(pb[i * ps + dc] - m);
-    olat[((size_t)b * H + h) * dc + c] = o / l;
+#pragma unroll
+    for (int i = 0; i < kAttnChunksMax; ++i)
+      if (i < n) o += v[i] * wch[i];
+    olat[((size_t)b * H + h) * dc + c] = o * linv;
   }
 }
 
-// Head h: o[b][h * dv + v] = sum_c W_UV[h * dv + v][c] * o_lat[b][h][c]; one
-// wave per row, each lane 4 columns per pass (dword loads), rows in pairs.
+// Head h: o[b][h * dv + v] = sum_c W_UV[h * dv + v][c] * o_lat[b][h][c]. A
+// workgroup takes 32 rows of one head (all of a narrower head), each of its 4
+// waves a quarter of them: a row's codes are 16-byte loads of dc / 16 lanes,
+// so one wave load covers 64 / (dc / 16) rows, and all of a wave's loads are
+// issued at once (one memory round trip). A row's per-token sums are added
+// across its lanes.
+constexpr int kUvRows = 32;  // rows per workgroup
+constexpr int kUvLd = 4;     // wave loads of codes: rows per wave (<= 8) / rows per load (>= 2)
+__host__ __device__ __forceinline__ int uv_row_parts(int dv) { return dv > kUvRows ? dv / kUvRows : 1; }
 __global__ void __launch_bounds__(kST) bs_uv_kernel(const float* olat, const uint8_t* codes, const uint16_t* scales,
                                                    int nkb, int H, int dv, int dc, int B, float* o) {
   extern __shared__ float ol[];  // [B][dc]
-  const int h = blockIdx.x, lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  for (int i = threadIdx.x; i < B * dc; i += kST) ol[i] = olat[((size_t)(i / dc) * H + h) * dc + i % dc];
+  const int rps = uv_row_parts(dv), h = blockIdx.x / rps, part = blockIdx.x % rps;
+  const int rw = dv / rps, rpw = rw / (kST / 64);
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int lpr = dc / 16, rpl = 64 / lpr, sub = lane / lpr, cl = lane % lpr, c0 = cl * 16;
+  const int r_w = h * dv + part * rw + w * rpw;  // first row of this wave
+  bu32x4 wv[kUvLd];
+  float sc[kUvLd];
+#pragma unroll
+  for (int j = 0; j < kUvLd; ++j) {
+    // unconditional loads: rows past the wave's read its first row, unused
+    const int ro = j * rpl + sub;
+    const int r = r_w + (ro < rpw ? ro : 0);
+    wv[j] = *reinterpret_cast<const bu32x4*>(codes + (size_t)r * dc + c0);
+    sc[j] = bfv(scales[(size_t)(r >> 3) * nkb + (c0 >> 7)]);
+  }
+  copy_in<kST>(ol, B * dc, [&](int i) { return olat[((size_t)(i / dc) * H + h) * dc + i % dc]; });
   __syncthreads();
-  const int passes = (dc / 4 + 63) / 64;  // 1 or 2 (dc <= 512)
-  for (int v0 = 2 * w; v0 < dv; v0 += 2 * (kST / 64)) {
-    uint32_t cw[2][2];
-    float sc[2][2];
 #pragma unroll
-    for (int rr = 0; rr < 2; ++rr) {
-      const int r = h * dv + v0 + rr;
+  for (int j = 0; j < kUvLd; ++j) {
+    if (j * rpl >= rpw) break;  // wave-uniform
+    const int ro = j * rpl + sub;
+    float f[16];
 #pragma unroll
-      for (int p = 0; p < 2; ++p) {
-        const int c0 = (p * 64 + lane) * 4;
-        const bool in = p < passes && c0 < dc && v0 + rr < dv;
-        cw[rr][p] = in ? *reinterpret_cast<const uint32_t*>(codes + (size_t)r * dc + c0) : 0u;
-        sc[rr][p] = in ? bfv(scales[(size_t)(r >> 3) * nkb + (c0 >> 7)]) : 0.f;
-      }
+    for (int e = 0; e < 4; ++e) {
+      const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)wv[j][e], false);
+      const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)wv[j][e], true);
+      f[4 * e + 0] = lo[0] * sc[j];
+      f[4 * e + 1] = lo[1] * sc[j];
+      f[4 * e + 2] = hi[0] * sc[j];
+      f[4 * e + 3] = hi[1] * sc[j];
     }
 #pragma unroll
-    for (int rr = 0; rr < 2; ++rr) {
-      float acc[kBatchMax];
+    for (int b = 0; b < kBatchMax; ++b) {
+      if (b < B) {
+        const float4* x4 = reinterpret_cast<const float4*>(ol + b * dc + c0);
+        float d = 0.f;
 #pragma unroll
-      for (int b = 0; b < kBatchMax; ++b) acc[b] = 0.f;
-#pragma unroll
-      for (int p = 0; p < 2; ++p) {
-        const int c0 = (p * 64 + lane) * 4;
-        if (p < passes && c0 < dc) {
-          const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)cw[rr][p], false);
-          const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)cw[rr][p], true);
-#pragma unroll
-          for (int b = 0; b < kBatchMax; ++b) {
-            if (b < B) {
-              const float4 x4 = *reinterpret_cast<const float4*>(ol + b * dc + c0);
-              acc[b] += sc[rr][p] * (lo[0] * x4.x + lo[1] * x4.y + hi[0] * x4.z + hi[1] * x4.w);
-            }
-          }
+        for (int e = 0; e < 4; ++e) {
+          const float4 x = x4[e];
+          d = fmaf(f[4 * e + 0], x.x, d);
+          d = fmaf(f[4 * e + 1], x.y, d);
+          d = fmaf(f[4 * e + 2], x.z, d);
+          d = fmaf(f[4 * e + 3], x.w, d);
         }
-      }
-      for (int b = 0; b < B; ++b) {
-        float s2 = acc[b];
-#pragma unroll
-        for (int o2 = 32; o2 > 0; o2 >>= 1) s2 += __shfl_xor(s2, o2, 64);
-        if (lane == 0 && v0 + rr < dv) o[(size_t)b * H * dv + h * dv + v0 + rr] = s2;
+        for (int off = lpr / 2; off > 0; off >>= 1) d += __shfl_xor(d, off, 64);
+        if (cl == 0 && ro < rpw) o[(size_t)b * H * dv + r_w + ro] = d;
       }
     }
   }
 }
 
 // out[b][r] = sum_k M[r][k] * h[b][k] for a bf16 matrix M [N][K] (router, LM
-// head): one wave per row, 16-byte loads of 8 values, K a multiple of 8.
+// head): one wave per kBrR consecutive rows, 16-byte loads of 8 values, K a
+// multiple of 8. A lane's loads of kBrP pieces of each of its rows go out
+// together, and every activation piece it loads serves all kBrR rows. BM (a
+// power of two >= B) bounds the tokens: activations are loaded 4 tokens at a
+// time, unconditionally (tokens past B repeat token B - 1, unused), so the
+// loads of a group do not wait for each other.
+constexpr int kBrR = 4;  // rows per wave
+constexpr int kBrP = 4;  // 16-byte pieces per lane and row in flight
+template <int BM>
 __global__ void __launch_bounds__(kST) bs_bf16_rows_kernel(const float* h, const uint16_t* M, int N, int K, int B,
                                                           float* out) {
   const int lane = threadIdx.x & 63;
-  const int r = blockIdx.x * (kST / 64) + (threadIdx.x >> 6);
-  if (r >= N) return;  // wave-uniform
-  const uint16_t* row = M + (size_t)r * K;
-  float acc[kBatchMax];
+  const int r0 = (blockIdx.x * (kST / 64) + (threadIdx.x >> 6)) * kBrR;
+  if (r0 >= N) return;  // wave-uniform
+  const int np = K / 8;
+  float acc[kBrR][BM];
 #pragma unroll
-  for (int b = 0; b < kBatchMax; ++b) acc[b] = 0.f;
-  for (int k8 = lane; k8 < K / 8; k8 += 64) {
-    const su32x4 v = *reinterpret_cast<const su32x4*>(row + k8 * 8);
-    float m[8];
+  for (int rr = 0; rr < kBrR; ++rr)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      m[2 * e] = __builtin_bit_cast(float, v[e] << 16);
-      m[2 * e + 1] = __builtin_bit_cast(float, v[e] & 0xFFFF0000u);
+    for (int b = 0; b < BM; ++b) acc[rr][b] = 0.f;
+  for (int p0 = 0; p0 < np; p0 += 64 * kBrP) {
+    su32x4 v[kBrR][kBrP];
+#pragma unroll
+    for (int rr = 0; rr < kBrR; ++rr) {
+      const int r = min(r0 + rr, N - 1);
+#pragma unroll
+      for (int j = 0; j < kBrP; ++j) {
+        const int k8 = min(p0 + 64 * j + lane, np - 1);  // unconditional; pieces past the row unused
+        v[rr][j] = *reinterpret_cast<const su32x4*>(M + (size_t)r * K + (size_t)k8 * 8);
+      }
     }
 #pragma unroll
-    for (int b = 0; b < kBatchMax; ++b) {
-      if (b < B) {
-        const float4 x0 = *reinterpret_cast<const float4*>(h + (size_t)b * K + k8 * 8);
-        const float4 x1 = *reinterpret_cast<const float4*>(h + (size_t)b * K + k8 * 8 + 4);
-        acc[b] += m[0] * x0.x + m[1] * x0.y + m[2] * x0.z + m[3] * x0.w + m[4] * x1.x + m[5] * x1.y +
-                  m[6] * x1.z + m[7] * x1.w;
+    for (int j = 0; j < kBrP; ++j) {
+      const int k8 = min(p0 + 64 * j + lane, np - 1);
+      const bool kin = p0 + 64 * j + lane < np;
+      float m[kBrR][8];
+#pragma unroll
+      for (int rr = 0; rr < kBrR; ++rr)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          m[rr][2 * e] = kin ? __builtin_bit_cast(float, v[rr][j][e] << 16) : 0.f;
+          m[rr][2 * e + 1] = kin ? __builtin_bit_cast(float, v[rr][j][e] & 0xFFFF0000u) : 0.f;
+        }
+#pragma unroll
+      for (int b0 = 0; b0 < BM; b0 += 4) {
+        float4 x[4][2];
+#pragma unroll
+        for (int i = 0; i < 4 && b0 + i < BM; ++i) {
+          const int bb = min(b0 + i, B - 1);
+          x[i][0] = *reinterpret_cast<const float4*>(h + (size_t)bb * K + k8 * 8);
+          x[i][1] = *reinterpret_cast<const float4*>(h + (size_t)bb * K + k8 * 8 + 4);
+        }
+#pragma unroll
+        for (int i = 0; i < 4 && b0 + i < BM; ++i) {
+          const float4 x0 = x[i][0], x1 = x[i][1];
+#pragma unroll
+          for (int rr = 0; rr < kBrR; ++rr)
+            acc[rr][b0 + i] += m[rr][0] * x0.x + m[rr][1] * x0.y + m[rr][2] * x0.z + m[rr][3] * x0.w +
+                               m[rr][4] * x1.x + m[rr][5] * x1.y + m[rr][6] * x1.z + m[rr][7] * x1.w;
+        }
       }
     }
   }
-  for (int b = 0; b < B; ++b) {
-    float s = acc[b];
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o, 64);
-    if (lane == 0) out[(size_t)b * N + r] = s;
+  for (int rr = 0; rr < kBrR; ++rr) {
+#pragma unroll
+    for (int b = 0; b < BM; ++b) {
+      if (b < B) {
+        float s = acc[rr][b];
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o, 64);
+        if (lane == 0 && r0 + rr < N) out[(size_t)b * N + r0 + rr] = s;
+      }
+    }
   }
 }
 
@@ -520,16 +680,18 @@ hipError_t bs_norm(float* x, const float* add, bool round, const float* gain, fl
   return hipGetLastError();
 }
 hipError_t bs_latent(const float* qkv, int ldq, int dq, int dc, int dr, const float* q_norm, const float* kv_norm,
-                     float eps, double base, const BatchTokens& tk, int B, uint16_t* cache, int64_t seq_stride,
-                     float* cq, hipStream_t st) {
-  hipLaunchKernelGGL(bs_latent_kernel, dim3(B), dim3(kST), 0, st, qkv, ldq, dq, dc, dr, q_norm, kv_norm, eps, base,
-                     tk, cache, seq_stride, cq);
+                     float eps, const float* rope_tab, const BatchTokens& tk, int B, uint16_t* cache,
+                     int64_t seq_stride, float* cq, hipStream_t st) {
+  hipLaunchKernelGGL(bs_latent_kernel, dim3(B), dim3(kST), 0, st, qkv, ldq, dq, dc, dr, q_norm, kv_norm, eps,
+                     rope_tab, tk, cache, seq_stride, cq);
   return hipGetLastError();
 }
 hipError_t bs_absorb(const float* q, const uint8_t* codes, const uint16_t* scales, int nkb, int H, int dn, int dr,
-                     int dc, int B, double base, const BatchTokens& tk, float* qlat, float* qpe, hipStream_t st) {
-  hipLaunchKernelGGL(bs_absorb_kernel, dim3(H), dim3(dc / 4), (size_t)B * dn * 4, st, q, codes, scales, nkb, H, dn,
-                     dr, dc, B, base, tk, qlat, qpe);
+                     int dc, int B, const float* rope_tab, const BatchTokens& tk, float* qlat, float* qpe,
+                     hipStream_t st) {
+  const int cps = ab_col_parts(dc);
+  hipLaunchKernelGGL(bs_absorb_kernel, dim3(H * cps), dim3(kAbT), (size_t)B * (dn + dc / cps) * 4, st, q, codes,
+                     scales, nkb, H, dn, dr, dc, B, rope_tab, tk, qlat, qpe);
   return hipGetLastError();
 }
 size_t bs_attn_lds(int dc, int dr) {
@@ -537,9 +699,9 @@ size_t bs_attn_lds(int dc, int dr) {
   return (size_t)2 * 16 * rs * 2 + (size_t)kBlk * rs * 2 + 16 * kBlk * 4 + 48 * 4;
 }
 // Position chunk of the attention workgroups for a longest context of ctx:
-// at least 128 positions, at most kAttnChunksMax chunks.
+// at least one block of kBlk positions, at most kAttnChunksMax chunks.
 int bs_attn_chunk(int ctx) {
-  const int c = std::max(128, (ctx + kAttnChunksMax - 1) / kAttnChunksMax);
+  const int c = std::max(kBlk, (ctx + kAttnChunksMax - 1) / kAttnChunksMax);
   return (c + kBlk - 1) / kBlk * kBlk;
 }
 hipError_t bs_attn(const float* qlat, const float* qpe, const uint16_t* cache, int64_t seq_stride, int H, int dc,
@@ -562,13 +724,18 @@ hipError_t bs_attn(const float* qlat, const float* qpe, const uint16_t* cache, i
 }
 hipError_t bs_uv(const float* olat, const uint8_t* codes, const uint16_t* scales, int nkb, int H, int dv, int dc,
                  int B, float* o, hipStream_t st) {
-  hipLaunchKernelGGL(bs_uv_kernel, dim3(H), dim3(kST), (size_t)B * dc * 4, st, olat, codes, scales, nkb, H, dv, dc,
-                     B, o);
+  hipLaunchKernelGGL(bs_uv_kernel, dim3(H * uv_row_parts(dv)), dim3(kST), (size_t)B * dc * 4, st, olat, codes, scales,
+                     nkb, H, dv, dc, B, o);
   return hipGetLastError();
 }
 hipError_t bs_bf16_rows(const float* h, const uint16_t* M, int N, int K, int B, float* out, hipStream_t st) {
-  hipLaunchKernelGGL(bs_bf16_rows_kernel, dim3((N + kST / 64 - 1) / (kST / 64)), dim3(kST), 0, st, h, M, N, K, B,
-                     out);
+  const int rows_per_wg = kBrR * (kST / 64);
+  const dim3 grid((N + rows_per_wg - 1) / rows_per_wg);
+  if (B <= 1) hipLaunchKernelGGL(bs_bf16_rows_kernel<1>, grid, dim3(kST), 0, st, h, M, N, K, B, out);
+  else if (B <= 2) hipLaunchKernelGGL(bs_bf16_rows_kernel<2>, grid, dim3(kST), 0, st, h, M, N, K, B, out);
+  else if (B <= 4) hipLaunchKernelGGL(bs_bf16_rows_kernel<4>, grid, dim3(kST), 0, st, h, M, N, K, B, out);
+  else if (B <= 8) hipLaunchKernelGGL(bs_bf16_rows_kernel<8>, grid, dim3(kST), 0, st, h, M, N, K, B, out);
+  else hipLaunchKernelGGL(bs_bf16_rows_kernel<kBatchMax>, grid, dim3(kST), 0, st, h, M, N, K, B, out);
   return hipGetLastError();
 }
 hipError_t bs_topk(const float* logits, int B, int E, int top_k, int32_t* idx, float* wts, hipStream_t st) {

@@ -96,11 +96,13 @@ hipError_t bs_input(const uint16_t* embed, const uint16_t* x_in, const BatchToke
                     hipStream_t st);
 hipError_t bs_norm(float* x, const float* add, bool round, const float* gain, float eps, int B, int D, float* h,
                    hipStream_t st);
+// rope_tab: the engine's RoPE table, f32 [max_ctx][rope / 2][2] (cos, sin)
 hipError_t bs_latent(const float* qkv, int ldq, int dq, int dc, int dr, const float* q_norm, const float* kv_norm,
-                     float eps, double base, const BatchTokens& tk, int B, uint16_t* cache, int64_t seq_stride,
-                     float* cq, hipStream_t st);
+                     float eps, const float* rope_tab, const BatchTokens& tk, int B, uint16_t* cache,
+                     int64_t seq_stride, float* cq, hipStream_t st);
 hipError_t bs_absorb(const float* q, const uint8_t* codes, const uint16_t* scales, int nkb, int H, int dn, int dr,
-                     int dc, int B, double base, const BatchTokens& tk, float* qlat, float* qpe, hipStream_t st);
+                     int dc, int B, const float* rope_tab, const BatchTokens& tk, float* qlat, float* qpe,
+                     hipStream_t st);
 constexpr int kAttnChunksMax = 32;  // position chunks per (sequence, head group) of the batched attention
 // part: f32 [B][H][kAttnChunksMax][kv_lora + 2] chunk partials
 hipError_t bs_attn(const float* qlat, const float* qpe, const uint16_t* cache, int64_t seq_stride, int H, int dc,
