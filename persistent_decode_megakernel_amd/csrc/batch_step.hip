@@ -249,6 +249,7 @@ constexpr int kBlk = 64;
 constexpr int kAtMaxRow = 640;                              // kv_lora + rope, at most 512 + 128
 constexpr int kAtLd = (kBlk * (kAtMaxRow / 8) + kST - 1) / kST;  // 16-byte cache pieces per thread and block
 constexpr int kAtQ = (16 * kAtMaxRow + kST - 1) / kST;           // query values per thread
+template <int NT>  // value tiles of 16 latent dims per wave: dc / 64 (2, 4 or 8)
 __global__ void __launch_bounds__(kST) bs_attn_kernel(const float* qlat, const float* qpe, const uint16_t* cache,
                                                      int64_t seq_stride, int H, int dc, int dr, float tau,
                                                      BatchTokens tk, int nch, int chunk, float* part) {
@@ -270,9 +271,9 @@ __global__ void __launch_bounds__(kST) bs_attn_kernel(const float* qlat, const f
   const uint16_t* seq = cache + (size_t)b * seq_stride;
   const int q8 = kvr / 8;  // 16-byte pieces per row
   // A block's cache rows: every piece a thread copies is loaded at once into
-  // registers (one memory round trip), the next block's while this one is used.
-  // The loads are unconditional (pieces past the block read its first row and
-  // are zeroed when stored): no branch around them, so none waits for another.
+  // registers (one memory round trip), then stored to LDS. The loads are
+  // unconditional (pieces past the block read its first row and are zeroed
+  // when stored): no branch around them, so none waits for another.
   su32x4 kvr_regs[kAtLd];
   auto load_block = [&](int tb) {
     const int nb = min(kBlk, t1 - tb);
@@ -307,12 +308,13 @@ __global__ void __launch_bounds__(kST) bs_attn_kernel(const float* qlat, const f
     }
   }
   if (threadIdx.x < 16) { hm[threadIdx.x] = -INFINITY; hl[threadIdx.x] = 0.f; }
-  const int nt = dc / 64;  // value tiles of 16 dims per wave (dc in {128, 256, 512})
+  constexpr int nt = NT;
   sf32x4 acc[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) acc[i] = (sf32x4){0.f, 0.f, 0.f, 0.f};
   for (int tb = t0; tb < t1; tb += kBlk) {
     const int nb = min(kBlk, t1 - tb);
+    if (tb > t0) load_block(tb);
     __syncthreads();  // previous block's rows and probabilities are consumed
 #pragma unroll
     for (int j = 0; j < kAtLd; ++j) {
@@ -321,7 +323,6 @@ __global__ void __launch_bounds__(kST) bs_attn_kernel(const float* qlat, const f
         *reinterpret_cast<su32x4*>(kv + r * rs + p * 8) = r < nb ? kvr_regs[j] : (su32x4){0u, 0u, 0u, 0u};
     }
     __syncthreads();
-    if (tb + kBlk < t1) load_block(tb + kBlk);
     // scores: wave w takes positions 16 w .. 16 w + 15 of the block
     {
       sf32x4 sc = {0.f, 0.f, 0.f, 0.f};
@@ -709,16 +710,26 @@ hipError_t bs_attn(const float* qlat, const float* qpe, const uint16_t* cache, i
   const size_t lds = bs_attn_lds(dc, dr);
   static bool raised = false;  // more dynamic LDS than the default 64 KB (gfx950 has 160 KB)
   if (!raised) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&bs_attn_kernel),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-    if (e != hipSuccess) return e;
+    for (const void* f : {reinterpret_cast<const void*>(&bs_attn_kernel<8>), reinterpret_cast<const void*>(&bs_attn_kernel<4>),
+                          reinterpret_cast<const void*>(&bs_attn_kernel<2>)}) {
+      const hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+      if (e != hipSuccess) return e;
+    }
     raised = true;
   }
   int ctx = 1;
   for (int b = 0; b < B; ++b) ctx = std::max(ctx, tk.pos[b] + 1);
   const int chunk = bs_attn_chunk(ctx), nch = (ctx + chunk - 1) / chunk;
-  hipLaunchKernelGGL(bs_attn_kernel, dim3(B * ((H + 15) / 16) * nch), dim3(kST), lds, st, qlat, qpe, cache,
-                     seq_stride, H, dc, dr, tau, tk, nch, chunk, part);
+  const dim3 grid(B * ((H + 15) / 16) * nch);
+  if (dc == 512)
+    hipLaunchKernelGGL(bs_attn_kernel<8>, grid, dim3(kST), lds, st, qlat, qpe, cache, seq_stride, H, dc, dr, tau, tk,
+                       nch, chunk, part);
+  else if (dc == 256)
+    hipLaunchKernelGGL(bs_attn_kernel<4>, grid, dim3(kST), lds, st, qlat, qpe, cache, seq_stride, H, dc, dr, tau, tk,
+                       nch, chunk, part);
+  else
+    hipLaunchKernelGGL(bs_attn_kernel<2>, grid, dim3(kST), lds, st, qlat, qpe, cache, seq_stride, H, dc, dr, tau, tk,
+                       nch, chunk, part);
   hipLaunchKernelGGL(bs_attn_merge_kernel, dim3(B * H), dim3(kST), 0, st, part, H, dc, nch, chunk, tk, olat);
   return hipGetLastError();
 }
