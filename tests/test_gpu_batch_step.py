@@ -6,6 +6,8 @@ margin-filtered teacher-forced inputs. Tolerances as the batch-1 engine's:
 1e-2 relative L2 on hidden states and logits against the oracle's chain, exact
 argmax, and every appended cache row equal, up to one bf16 step, to the row
 the oracle computes from this path's own input of that layer."""
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -43,7 +45,7 @@ def _case(name, prompt_lens, steps, x_inputs=False):
                 caches[b, l, :P] = rows
             st.length = P
         else:     # an oracle prefill of the sequence's own prompt
-            toks = gen.prompt_tokens(cfg, seed=b)[:P]
+            toks = gen.prompt_tokens(dataclasses.replace(cfg, prompt_len=max(P, cfg.prompt_len)), seed=b)[:P]
             st = O.prefill(W, toks, max_len=P + steps + 1)
             for l in range(cfg.n_layers):
                 caches[b, l, :P] = _bits(st.cache[l][:P]).cuda()
@@ -95,6 +97,17 @@ def _check(name, prompt_lens, steps, x_inputs=False):
 def test_batch_step_tiny():
     """Three sequences at different positions (prompts of 16, 40 and 7 tokens)."""
     _check("tiny", [16, 40, 7], 3)
+
+
+def test_batch_step_tiny_sixteen():
+    """The largest batch: 16 sequences with prompts of 1 to 60 tokens."""
+    _check("tiny", [1, 7, 16, 40, 60, 3, 22, 35, 9, 48, 13, 2, 57, 30, 5, 44], 2)
+
+
+def test_batch_step_tiny_long_context():
+    """Five sequences (a token bound of 8 with three unused slots), one of them
+    2100 positions long: attention chunks of two 64-position blocks."""
+    _check("tiny", [2100, 12, 300, 64, 65], 2)
 
 
 def test_batch_step_ragged():
