@@ -498,6 +498,10 @@ def main():
         log(f"{c4.name}: weights {e4.sizes.weight_bytes / 1e9:.2f} GB (MXFP4 experts)")
         r4 = run_workload(e4, c4, K, Wm, not args.no_trace, False, args.resident_only)
         r4["weights"] = "MXFP4 routed and shared experts (e2m1, e8m0 scale per 32); everything else as the FP8 stack"
+        if args.batch and c4.vocab > 0:
+            # batched steps over the same MXFP4 experts (B = 1 and the largest B asked for)
+            bl = [int(b) for b in args.batch.split(",") if b]
+            r4["batch_step_points"] = batch_step_points(e4, c4, sorted({min(bl), max(bl)}))
         results.append(r4)
         del e4, s4
         torch.cuda.empty_cache()

@@ -436,22 +436,24 @@ int pdm_set_trace(pdm_engine* e, int32_t on);
  * MoE layer reads the union of the experts its B tokens chose, which trades
  * per-user speed for total throughput (SemiAnalysis TileRT page, the section
  * on next steps: batch sizes 2, 4 and 8). These calls run those products on
- * the engine's bound FP8 weights, in place, on the matrix cores. They touch
+ * the engine's bound weights (FP8, or MXFP4 expert matrices), in place, on
+ * the matrix cores. They touch
  * neither the cache nor the persistent kernel's state. Outputs are sums of
  * per-slab partials added in no fixed order, so fp32 rounding may differ from
  * call to call. Stream-ordered; no host synchronisation. */
 #define PDM_BATCH_MAX 16
 
 /* y[b][r] = sum_k W[r][k] * x[b][k] for b < B and every row r of the packed
- * FP8 matrix that holds (tensor, layer, expert), part 1 being W_UV of
- * PDM_T_WKV_B, with W the dequantised weights (codes times block scales).
+ * matrix that holds (tensor, layer, expert), part 1 being W_UV of
+ * PDM_T_WKV_B, with W the dequantised weights (FP8 codes times 128 x 128
+ * block scales, or for MXFP4 expert matrices e2m1 codes times the e8m0 scale
+ * of each row's 32 columns).
  * Rows come in packed order (pdm_packed_layout): [W_DQ ; W_DKV] for
  * PDM_T_WQ_A and PDM_T_WKV_A alike, gate and up rows interleaved in eights for
  * PDM_T_W_GATE and PDM_T_W_UP. x_dev: f32 [B][K] (K the matrix's columns),
  * 16-byte aligned; y_dev: f32 [B][rows], overwritten; 1 <= B <= PDM_BATCH_MAX.
  * Errors: PDM_ERR_UNBOUND, PDM_ERR_ARG (null pointer, B out of range, unknown
- * tensor / layer / expert / part), PDM_ERR_CONFIG (an MXFP4 matrix),
- * PDM_ERR_ALIGN (x_dev), PDM_ERR_LAUNCH. */
+ * tensor / layer / expert / part), PDM_ERR_ALIGN (x_dev), PDM_ERR_LAUNCH. */
 int pdm_batch_gemm(pdm_engine* e, int32_t tensor, int32_t layer, int32_t expert, int32_t part,
                    const float* x_dev, int32_t B, float* y_dev, pdm_stream_t stream);
 
@@ -465,7 +467,7 @@ int pdm_batch_gemm(pdm_engine* e, int32_t tensor, int32_t layer, int32_t expert,
  * once for all B tokens. h_dev: f32 [B][hidden], the RMS-normalised FFN
  * input, 16-byte aligned; idx_dev: int32 [B][top_k], indices outside [0,
  * n_experts) are skipped; w_dev: f32 [B][top_k]; y_dev: f32 [B][hidden],
- * overwritten. A MoE layer needs expert_format PDM_FMT_FP8. The first call
+ * overwritten. Experts may be FP8 or MXFP4 (expert_format). The first call
  * allocates the engine's batch workspace (device memory, freed by
  * pdm_destroy); calls that overlap on the engine's device race on it.
  * Errors as pdm_batch_gemm, plus PDM_ERR_ARG for a MoE layer without
@@ -488,11 +490,10 @@ int pdm_batch_ffn(pdm_engine* e, int32_t layer, const float* h_dev, int32_t B, c
  * sequences' latent caches (caller-owned, 16-byte aligned), row positions[b]
  * of every layer written by the step; logits_dev: f32 [B][vocab] (required
  * with a vocabulary); argmax_dev: int32 [B] or null; hidden_dev: f32
- * [n_layers][B][hidden] layer outputs or null. Needs expert_format
- * PDM_FMT_FP8 when the model has MoE layers. The first call allocates the
- * engine's batch workspaces (freed by pdm_destroy). Errors: PDM_ERR_UNBOUND,
- * PDM_ERR_ARG, PDM_ERR_POS, PDM_ERR_CTX, PDM_ERR_TOKEN, PDM_ERR_ALIGN,
- * PDM_ERR_CONFIG, PDM_ERR_OOM, PDM_ERR_LAUNCH. */
+ * [n_layers][B][hidden] layer outputs or null. Experts may be FP8 or MXFP4.
+ * The first call allocates the engine's batch workspaces (freed by
+ * pdm_destroy). Errors: PDM_ERR_UNBOUND, PDM_ERR_ARG, PDM_ERR_POS,
+ * PDM_ERR_CTX, PDM_ERR_TOKEN, PDM_ERR_ALIGN, PDM_ERR_OOM, PDM_ERR_LAUNCH. */
 int pdm_batch_decode_step(pdm_engine* e, int32_t B, const int32_t* tokens, const int32_t* positions,
                           const uint16_t* x_in_dev, uint16_t* caches_dev, float* logits_dev, int32_t* argmax_dev,
                           float* hidden_dev, pdm_stream_t stream);

@@ -746,7 +746,7 @@ int pdm_batch_gemm(pdm_engine* e, int32_t tensor, int32_t layer, int32_t expert,
   rc = pack_targets(e->dims, e->plan, tensor, layer, expert, t, &n);
   if (rc) return rc;
   if (part < 0 || part >= n) return PDM_ERR_ARG;
-  if (t[part].fmt != PDM_FMT_FP8) return PDM_ERR_CONFIG;
+  const bool mx = t[part].fmt == PDM_FMT_MXFP4;
   DeviceGuard dg(e->device);
   if ((rc = ensure_ws(e))) return rc;
   BatchGemm g{};
@@ -754,8 +754,9 @@ int pdm_batch_gemm(pdm_engine* e, int32_t tensor, int32_t layer, int32_t expert,
   g.codes_off = t[part].codes;
   g.scales_off = t[part].scales;
   g.rows = t[part].m.rows;
-  g.K = t[part].m.Kp;
+  g.K = mx ? 2 * t[part].m.Kp : t[part].m.Kp;  // columns (MXFP4 rows hold two per byte)
   g.nkb = t[part].m.nkb;
+  g.fmt = t[part].fmt;
   g.B = B;
   g.xg = ws_xg(e);
   g.y = y_dev;
@@ -784,7 +785,6 @@ int pdm_batch_ffn(pdm_engine* e, int32_t layer, const float* h_dev, int32_t B, c
   const LayerPlan& L = e->plan.layers[layer];
   const bool moe = L.is_moe != 0;
   if (moe && (!idx_dev || !w_dev)) return PDM_ERR_ARG;
-  if (moe && d.expert_format != PDM_FMT_FP8) return PDM_ERR_CONFIG;
   DeviceGuard dg(e->device);
   if ((rc = ensure_ws(e))) return rc;
   int32_t* cnt = reinterpret_cast<int32_t*>(e->batch_ws);
@@ -802,11 +802,14 @@ int pdm_batch_ffn(pdm_engine* e, int32_t layer, const float* h_dev, int32_t B, c
   BatchGemm gu{};
   gu.base = e->w + (moe ? L.expert_base : 0);
   gu.stride = moe ? L.expert_stride : 0;
+  // columns per row: MXFP4 expert rows hold two per code byte
+  auto cols = [](const Fp8Mat& m) { return m.fmt == PDM_FMT_MXFP4 ? 2 * m.K : m.K; };
   gu.codes_off = gum.codes;
   gu.scales_off = gum.scales;
   gu.rows = gum.rows;
-  gu.K = gum.K;
+  gu.K = cols(gum);
   gu.nkb = gum.nkb;
+  gu.fmt = gum.fmt;
   gu.B = B;
   gu.u_count = cnt;
   gu.u_list = list;
@@ -818,8 +821,9 @@ int pdm_batch_ffn(pdm_engine* e, int32_t layer, const float* h_dev, int32_t B, c
   dn.codes_off = dnm.codes;
   dn.scales_off = dnm.scales;
   dn.rows = dnm.rows;
-  dn.K = dnm.K;
+  dn.K = cols(dnm);
   dn.nkb = dnm.nkb;
+  dn.fmt = dnm.fmt;
   dn.y = y_dev;
   dn.ldy = d.hidden;
   batch_gemm_grid(dn, n_slots);
@@ -927,8 +931,6 @@ int pdm_batch_decode_step(pdm_engine* e, int32_t B, const int32_t* tokens, const
   const pdm_dims& d = e->dims;
   if (B < 1 || B > kBatchMax || !positions || !caches_dev) return PDM_ERR_ARG;
   if (reinterpret_cast<uintptr_t>(caches_dev) & 15u) return PDM_ERR_ALIGN;
-  const bool any_moe = std::any_of(d.layer_moe, d.layer_moe + d.n_layers, [](uint8_t m) { return m != 0; });
-  if (any_moe && d.expert_format != PDM_FMT_FP8) return PDM_ERR_CONFIG;
   BatchTokens tk{};
   for (int b = 0; b < B; ++b) {
     if (positions[b] < 0) return PDM_ERR_POS;

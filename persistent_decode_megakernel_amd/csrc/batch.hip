@@ -23,7 +23,11 @@
 //   C: lane l holds rows 4 g .. 4 g + 3 of the tile for token l % 16.
 // A scale covers 8 packed rows and 128 columns, so the eight MFMAs of one
 // 128-column block accumulate apart and are scaled per lane before they join
-// the running sum.
+// the running sum. MXFP4 expert matrices (codes [rows][K / 2], element 2j in
+// the low nibble of byte j, one e8m0 scale per row and 32 columns) take the
+// same operand layout: a lane's 16 columns of a window are 8 code bytes under
+// one scale, converted straight to bf16 with the scale applied (e2m1 times a
+// power of two is exact in bf16), so their MFMAs join the sum unscaled.
 //
 // Work split: a workgroup (4 waves) owns 8 row tiles (128 rows) and a run of
 // K slabs (8 windows = 512 columns each). Per slab, each wave issues its two
@@ -82,6 +86,17 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ void fp8x4_to_bf16(uint32_t w, uint32_t& d0, uint32_t& d1) {
   d0 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false));
   d1 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true));
+}
+// 2^(e - 127) as an fp32 bit pattern (e = 0: the subnormal 2^-127)
+__device__ __forceinline__ float e8m0_f32(uint32_t e) { return __builtin_bit_cast(float, e ? e << 23 : 0x00400000u); }
+// eight e2m1 codes (one dword, element 2j in the low nibble of byte j) times
+// the block scale -> eight bf16 (four dwords), exact
+__device__ __forceinline__ void fp4x8_to_bf16(uint32_t w, float sc, uint32_t& d0, uint32_t& d1, uint32_t& d2,
+                                              uint32_t& d3) {
+  d0 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 0));
+  d1 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 1));
+  d2 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 2));
+  d3 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 3));
 }
 __device__ __forceinline__ float silu_f(float g) { return g / (1.0f + __expf(-g)); }
 
@@ -170,8 +185,9 @@ __global__ void __launch_bounds__(kBT) batch_stage_act_kernel(BatchStage a) {
 // u_list[s], output y + s * B * ldy ([slot][B][rows]). MODE 2: K slots, slot
 // s the down matrix of expert u_list[s], its staged activations at xg + s *
 // xg_slot (u32x4). Activations come staged (xg, whole slabs).
-template <int MODE>
+template <int MODE, int FMT>  // FMT: PDM_FMT_FP8 or PDM_FMT_MXFP4 codes
 __global__ void __launch_bounds__(kBT) batch_gemm_kernel(BatchGemm g) {
+  constexpr bool kMx = FMT == PDM_FMT_MXFP4;
   __shared__ u32x4_t xs[kSlabU4];  // [window][piece][lane]
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int per = g.splits * g.groups;
@@ -185,8 +201,12 @@ __global__ void __launch_bounds__(kBT) batch_gemm_kernel(BatchGemm g) {
   const uint16_t* scales = reinterpret_cast<const uint16_t*>(blk + g.scales_off);
   const u32x4_t* xg = g.xg + (MODE == 2 ? (size_t)slot * g.xg_slot : 0);
   const int rows = g.rows, K = g.K, B = g.B, nkb = g.nkb, nsc = rows >> 3;
+  const int rowb = kMx ? K / 2 : K;  // code bytes per row
   const __amdgpu_buffer_rsrc_t rc =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(codes), 0, (int)((uint64_t)rows * K), kBufWord3);
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(codes), 0, (int)((uint64_t)rows * rowb), kBufWord3);
+  // MXFP4: e8m0 scale bytes [rows][nkb], nkb = K / 32
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(scales), 0, kMx ? (int)((uint64_t)rows * nkb) : 0, kBufWord3);
   const int r16 = lane & 15, lg = lane >> 4;
   f32x4 acc[kTilesPerWave];
 #pragma unroll
@@ -202,8 +222,9 @@ __global__ void __launch_bounds__(kBT) batch_gemm_kernel(BatchGemm g) {
       __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(src + piece + lane),
                                        (__attribute__((address_space(3))) void*)(xs + piece), 16, 0, 0);
     }
-    // ---- this slab's weight codes for the wave's row tiles
+    // ---- this slab's weight codes (and MXFP4 scales) for the wave's row tiles
     u32x4_t wv[kTilesPerWave][kSlabW];
+    uint32_t ws[kMx ? kTilesPerWave : 1][kMx ? kSlabW : 1];
 #pragma unroll
     for (int t = 0; t < kTilesPerWave; ++t) {
       const int rt = q * kGroupT + w + t * kBWaves;
@@ -212,7 +233,13 @@ __global__ void __launch_bounds__(kBT) batch_gemm_kernel(BatchGemm g) {
       for (int i = 0; i < kSlabW; ++i) {
         const int k = (s * kSlabW + i) * 64 + lg * 16;
         const bool in = rt < g.tiles && row < rows && k < K;
-        wv[t][i] = __builtin_amdgcn_raw_buffer_load_b128(rc, in ? (uint32_t)(row * K + k) : kOob, 0, 0);
+        if constexpr (kMx) {
+          const auto c2 = __builtin_amdgcn_raw_buffer_load_b64(rc, in ? (uint32_t)(row * rowb + k / 2) : kOob, 0, 0);
+          wv[t][i] = (u32x4_t){c2[0], c2[1], 0u, 0u};
+          ws[t][i] = __builtin_amdgcn_raw_buffer_load_b8(rs, in ? (uint32_t)(row * nkb + k / 32) : kOob, 0, 0);
+        } else {
+          wv[t][i] = __builtin_amdgcn_raw_buffer_load_b128(rc, in ? (uint32_t)(row * K + k) : kOob, 0, 0);
+        }
       }
     }
     __builtin_amdgcn_s_waitcnt(0);  // the copies (and the codes) have landed
@@ -234,10 +261,16 @@ __global__ void __launch_bounds__(kBT) batch_gemm_kernel(BatchGemm g) {
           const int win = kb * 2 + i2;
           const u32x4_t c = wv[t][win];
           uint32_t p[8];
-          fp8x4_to_bf16(c[0], p[0], p[1]);
-          fp8x4_to_bf16(c[1], p[2], p[3]);
-          fp8x4_to_bf16(c[2], p[4], p[5]);
-          fp8x4_to_bf16(c[3], p[6], p[7]);
+          if constexpr (kMx) {
+            const float sc4 = e8m0_f32(ws[t][win]);
+            fp4x8_to_bf16(c[0], sc4, p[0], p[1], p[2], p[3]);
+            fp4x8_to_bf16(c[1], sc4, p[4], p[5], p[6], p[7]);
+          } else {
+            fp8x4_to_bf16(c[0], p[0], p[1]);
+            fp8x4_to_bf16(c[1], p[2], p[3]);
+            fp8x4_to_bf16(c[2], p[4], p[5]);
+            fp8x4_to_bf16(c[3], p[6], p[7]);
+          }
           const u32x4_t a1 = {p[0], p[1], p[2], p[3]}, a2 = {p[4], p[5], p[6], p[7]};
           const bf16x8 A1 = __builtin_bit_cast(bf16x8, a1), A2 = __builtin_bit_cast(bf16x8, a2);
           const bf16x8 H1 = __builtin_bit_cast(bf16x8, xs[win * kWinU4 + 0 * 64 + lane]);
@@ -249,8 +282,9 @@ __global__ void __launch_bounds__(kBT) batch_gemm_kernel(BatchGemm g) {
           tmp = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A2, H2, tmp, 0, 0, 0);
           tmp = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A2, L2, tmp, 0, 0, 0);
         }
-        const float sc =
-            srow < nsc ? __builtin_bit_cast(float, (uint32_t)scales[(size_t)srow * nkb + kbg] << 16) : 0.f;
+        const float sc = kMx ? 1.f  // (applied in the conversion)
+                         : srow < nsc ? __builtin_bit_cast(float, (uint32_t)scales[(size_t)srow * nkb + kbg] << 16)
+                                      : 0.f;
 #pragma unroll
         for (int i = 0; i < 4; ++i) acc[t][i] += sc * tmp[i];
       }
@@ -363,9 +397,13 @@ hipError_t launch_batch_gemm(const BatchGemm& g, int mode, int n_slots, hipStrea
   const int per = g.splits * g.groups;
   const int grid = per * (mode == 0 ? 1 : n_slots);
   if (grid <= 0) return hipSuccess;
-  if (mode == 0) hipLaunchKernelGGL(batch_gemm_kernel<0>, dim3(grid), dim3(kBT), 0, st, g);
-  else if (mode == 1) hipLaunchKernelGGL(batch_gemm_kernel<1>, dim3(grid), dim3(kBT), 0, st, g);
-  else hipLaunchKernelGGL(batch_gemm_kernel<2>, dim3(grid), dim3(kBT), 0, st, g);
+  const bool mx = g.fmt == PDM_FMT_MXFP4;
+  if (mode == 0 && !mx) hipLaunchKernelGGL((batch_gemm_kernel<0, PDM_FMT_FP8>), dim3(grid), dim3(kBT), 0, st, g);
+  else if (mode == 0) hipLaunchKernelGGL((batch_gemm_kernel<0, PDM_FMT_MXFP4>), dim3(grid), dim3(kBT), 0, st, g);
+  else if (mode == 1 && !mx) hipLaunchKernelGGL((batch_gemm_kernel<1, PDM_FMT_FP8>), dim3(grid), dim3(kBT), 0, st, g);
+  else if (mode == 1) hipLaunchKernelGGL((batch_gemm_kernel<1, PDM_FMT_MXFP4>), dim3(grid), dim3(kBT), 0, st, g);
+  else if (!mx) hipLaunchKernelGGL((batch_gemm_kernel<2, PDM_FMT_FP8>), dim3(grid), dim3(kBT), 0, st, g);
+  else hipLaunchKernelGGL((batch_gemm_kernel<2, PDM_FMT_MXFP4>), dim3(grid), dim3(kBT), 0, st, g);
   return hipGetLastError();
 }
 

@@ -62,6 +62,8 @@ struct BatchGemm {
   int32_t ldy;
   int32_t tiles, slabs, groups;  // 16-row tiles, 512-column K slabs, 8-tile row groups
   int32_t spw, splits;           // K slabs per workgroup, K splits per row group
+  int32_t fmt;                   // PDM_FMT_FP8 (K code bytes per row) or PDM_FMT_MXFP4 (K / 2; nkb = K / 32
+                                 // e8m0 scale bytes per row); K counts columns either way
 };
 // Geometry of a launch over n_slots slot matrices (1 for mode 0).
 void batch_gemm_grid(BatchGemm& g, int n_slots);

@@ -157,19 +157,25 @@ def test_batch_errors():
     torch.cuda.synchronize()
 
 
-def test_batch_mxfp4_experts_rejected():
-    from persistent_decode_megakernel_amd import Engine
-    cfg = configs.get("tiny_fp4")
-    eng = Engine(cfg, max_ctx=64, device=0)
-    x = torch.zeros(2, cfg.hidden, device="cuda")
-    y = torch.zeros(2, 4096, device="cuda")
-    idx = torch.zeros(2, cfg.top_k, dtype=torch.int32, device="cuda")
-    w = torch.zeros(2, cfg.top_k, device="cuda")
-    assert eng.batch_gemm_raw(L.T_W_GATE, 1, 2, 0, x, 2, y) == L.ERR_CONFIG
-    assert eng.batch_ffn_raw(1, x, 2, idx, w, y) == L.ERR_CONFIG
-    assert eng.batch_gemm_raw(L.T_WO, 1, -1, 0, x, 2, y) == L.OK            # non-expert matrices stay FP8
-    torch.cuda.synchronize()
-    eng.close()
+def test_batch_gemm_mxfp4_experts():
+    """MXFP4 expert matrices (e2m1 codes, an e8m0 scale per row and 32
+    columns) on the matrix cores: routed and shared gate/up and down of the
+    small model at B = 1, 3, 8, 16, and of the ragged one (hidden 1056: 33
+    scale bytes per row, a last 64-column window only half inside the row) at
+    B = 2, 7; the FP8 attention matrices of the same engines alongside."""
+    run_gemm("tiny_fp4", [("w_gate", 1, 3, 0), ("w_down", 1, 3, 0), ("w_gate", 1, 16, 0), ("w_down", 1, 16, 0),
+                          ("wo", 1, -1, 0)], (1, 3, 8, 16))
+    run_gemm("ragged_fp4", [("w_gate", 1, 11, 0), ("w_down", 2, 12, 0), ("w_gate", 2, 13, 0), ("wq_a", 1, -1, 0)],
+             (2, 7))
+
+
+@pytest.mark.parametrize("B", [1, 5, 16])
+def test_batch_ffn_mxfp4_experts(B):
+    """The union-of-experts block over MXFP4 experts (the dense layer of the
+    same model stays FP8)."""
+    run_ffn("tiny_fp4", 1, B, seed=20 + B)
+    run_ffn("tiny_fp4", 0, B, seed=20 + B)
+    run_ffn("ragged_fp4", 1, min(B, 8), seed=30 + B)
 
 
 def test_batch_dsv3_moe_layer():
