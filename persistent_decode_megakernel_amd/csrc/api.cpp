@@ -771,6 +771,7 @@ int pdm_batch_gemm(pdm_engine* e, int32_t tensor, int32_t layer, int32_t expert,
   sa.nwin = g.slabs * 8;
   sa.z0 = y_dev;
   sa.n0 = (size_t)B * g.rows;
+  sa.mx = mx ? 1 : 0;
   const hipStream_t st = (hipStream_t)stream;
   if (launch_batch_stage(sa, false, sa.nwin * 128, st) != hipSuccess) return PDM_ERR_LAUNCH;
   return launch_batch_gemm(g, 0, 1, st) == hipSuccess ? PDM_OK : PDM_ERR_LAUNCH;
@@ -840,6 +841,7 @@ int pdm_batch_ffn(pdm_engine* e, int32_t layer, const float* h_dev, int32_t B, c
   sx.n0 = (size_t)B * gum.rows;
   sx.z1 = y_dev;
   sx.n1 = (size_t)B * d.hidden;
+  sx.mx = gu.fmt == PDM_FMT_MXFP4 ? 1 : 0;
   if (launch_batch_stage(sx, false, sx.nwin * 128, st) != hipSuccess) return PDM_ERR_LAUNCH;
   if (launch_batch_gemm(gu, 1, n_slots, st) != hipSuccess) return PDM_ERR_LAUNCH;
   // stage the weighted SwiGLU activations of every slot for the down product
@@ -852,6 +854,7 @@ int pdm_batch_ffn(pdm_engine* e, int32_t layer, const float* h_dev, int32_t B, c
   sa.B = B;
   sa.K = dn.K;
   sa.nwin = dn.slabs * 8;
+  sa.mx = dn.fmt == PDM_FMT_MXFP4 ? 1 : 0;
   if (launch_batch_stage(sa, true, n_slots * sa.nwin * 128, st) != hipSuccess) return PDM_ERR_LAUNCH;
   return launch_batch_gemm(dn, 2, n_slots, st) == hipSuccess ? PDM_OK : PDM_ERR_LAUNCH;
 }

@@ -27,7 +27,11 @@
 // the low nibble of byte j, one e8m0 scale per row and 32 columns) take the
 // same operand layout: a lane's 16 columns of a window are 8 code bytes under
 // one scale, converted straight to bf16 with the scale applied (e2m1 times a
-// power of two is exact in bf16), so their MFMAs join the sum unscaled.
+// power of two is exact in bf16), so their MFMAs join the sum unscaled. For
+// MXFP4 products the columns of a window pair are interleaved so that one
+// 16-byte load of a lane is the 32 columns (one scale block) it needs for
+// both windows: window 2p + h, lane group g holds columns 128 p + 32 g + 16 h
+// .. + 15 (the activations are staged in the same order).
 //
 // Work split: a workgroup (4 waves) owns 8 row tiles (128 rows) and a run of
 // K slabs (8 windows = 512 columns each). Per slab, each wave issues its two
@@ -109,6 +113,12 @@ __device__ __forceinline__ float silu_f(float g) { return g / (1.0f + __expf(-g)
 constexpr int kWinU4 = 4 * 64;             // u32x4 per window
 constexpr int kSlabU4 = kSlabW * kWinU4;   // u32x4 per slab (32 KB)
 
+// first column of a staged piece: window win, lane jl, half (columns 0-7 or
+// 8-15 of the lane's 16); MXFP4 products interleave window pairs
+__device__ __forceinline__ int stage_col(int win, int jl, int half, int mx) {
+  return mx ? (win >> 1) * 128 + (jl >> 4) * 32 + (win & 1) * 16 + half * 8 : win * 64 + (jl >> 4) * 16 + half * 8;
+}
+
 __device__ __forceinline__ void stage_piece(u32x4_t* xw, int jl, int half, const float (&v)[8]) {
   uint32_t hb[8], lb[8];
 #pragma unroll
@@ -139,7 +149,7 @@ __global__ void __launch_bounds__(kBT) batch_stage_x_kernel(BatchStage a) {
   const int total = a.nwin * 2 * 64;
   for (int j = blockIdx.x * kBT + threadIdx.x; j < total; j += gridDim.x * kBT) {
     const int jl = j & 63, half = (j >> 6) & 1, win = j >> 7;
-    const int n = jl & 15, k = win * 64 + (jl >> 4) * 16 + half * 8;
+    const int n = jl & 15, k = stage_col(win, jl, half, a.mx);
     float v[8];
     if (n < a.B && k < a.K) {
       const float* xr = a.x + (size_t)n * a.ldx + k;
@@ -162,7 +172,7 @@ __global__ void __launch_bounds__(kBT) batch_stage_act_kernel(BatchStage a) {
   for (int j = blockIdx.x * kBT + threadIdx.x; j < total; j += gridDim.x * kBT) {
     const int slot = j / per, r = j - slot * per;
     const int jl = r & 63, half = (r >> 6) & 1, win = r >> 7;
-    const int n = jl & 15, k = win * 64 + (jl >> 4) * 16 + half * 8;
+    const int n = jl & 15, k = stage_col(win, jl, half, a.mx);
     float v[8];
     if (n < a.B && k < a.K) {
       const float* hr = a.x + ((size_t)slot * a.B + n) * a.ldx + (k >> 3) * 16;
@@ -222,22 +232,25 @@ __global__ void __launch_bounds__(kBT) batch_gemm_kernel(BatchGemm g) {
       __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(src + piece + lane),
                                        (__attribute__((address_space(3))) void*)(xs + piece), 16, 0, 0);
     }
-    // ---- this slab's weight codes (and MXFP4 scales) for the wave's row tiles
-    u32x4_t wv[kTilesPerWave][kSlabW];
-    uint32_t ws[kMx ? kTilesPerWave : 1][kMx ? kSlabW : 1];
+    // ---- this slab's weight codes (and MXFP4 scales) for the wave's row tiles:
+    // FP8, one 16-byte load per window; MXFP4, one per window pair (32 columns)
+    constexpr int kLd = kMx ? kSlabW / 2 : kSlabW;
+    u32x4_t wv[kTilesPerWave][kLd];
+    uint32_t ws[kMx ? kTilesPerWave : 1][kMx ? kLd : 1];
 #pragma unroll
     for (int t = 0; t < kTilesPerWave; ++t) {
       const int rt = q * kGroupT + w + t * kBWaves;
       const int row = rt * 16 + r16;
 #pragma unroll
-      for (int i = 0; i < kSlabW; ++i) {
-        const int k = (s * kSlabW + i) * 64 + lg * 16;
-        const bool in = rt < g.tiles && row < rows && k < K;
+      for (int i = 0; i < kLd; ++i) {
         if constexpr (kMx) {
-          const auto c2 = __builtin_amdgcn_raw_buffer_load_b64(rc, in ? (uint32_t)(row * rowb + k / 2) : kOob, 0, 0);
-          wv[t][i] = (u32x4_t){c2[0], c2[1], 0u, 0u};
+          const int k = (s * kLd + i) * 128 + lg * 32;
+          const bool in = rt < g.tiles && row < rows && k < K;
+          wv[t][i] = __builtin_amdgcn_raw_buffer_load_b128(rc, in ? (uint32_t)(row * rowb + k / 2) : kOob, 0, 0);
           ws[t][i] = __builtin_amdgcn_raw_buffer_load_b8(rs, in ? (uint32_t)(row * nkb + k / 32) : kOob, 0, 0);
         } else {
+          const int k = (s * kSlabW + i) * 64 + lg * 16;
+          const bool in = rt < g.tiles && row < rows && k < K;
           wv[t][i] = __builtin_amdgcn_raw_buffer_load_b128(rc, in ? (uint32_t)(row * K + k) : kOob, 0, 0);
         }
       }
@@ -259,13 +272,14 @@ __global__ void __launch_bounds__(kBT) batch_gemm_kernel(BatchGemm g) {
 #pragma unroll
         for (int i2 = 0; i2 < 2; ++i2) {
           const int win = kb * 2 + i2;
-          const u32x4_t c = wv[t][win];
           uint32_t p[8];
-          if constexpr (kMx) {
-            const float sc4 = e8m0_f32(ws[t][win]);
-            fp4x8_to_bf16(c[0], sc4, p[0], p[1], p[2], p[3]);
-            fp4x8_to_bf16(c[1], sc4, p[4], p[5], p[6], p[7]);
+          if constexpr (kMx) {  // window pair kb: bytes 8 i2 .. 8 i2 + 7 of its load
+            const u32x4_t c = wv[t][kb];
+            const float sc4 = e8m0_f32(ws[t][kb]);
+            fp4x8_to_bf16(c[2 * i2], sc4, p[0], p[1], p[2], p[3]);
+            fp4x8_to_bf16(c[2 * i2 + 1], sc4, p[4], p[5], p[6], p[7]);
           } else {
+            const u32x4_t c = wv[t][win];
             fp8x4_to_bf16(c[0], p[0], p[1]);
             fp8x4_to_bf16(c[1], p[2], p[3]);
             fp8x4_to_bf16(c[2], p[4], p[5]);

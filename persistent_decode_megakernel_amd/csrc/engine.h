@@ -83,6 +83,7 @@ struct BatchStage {
   const int32_t* c0;
   float* z1;
   size_t n0, n1;
+  int32_t mx;  // column order of an MXFP4 product (window pairs interleaved)
 };
 hipError_t launch_batch_stage(const BatchStage& a, bool act, int max_jobs, hipStream_t st);
 hipError_t launch_batch_union(const int32_t* idx, const float* wts, int B, int top_k, int E, int n_shared,
