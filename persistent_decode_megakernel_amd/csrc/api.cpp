@@ -924,6 +924,40 @@ int step_gemm(pdm_engine* e, const Fp8Mat& m, const float* x, int B, float* y, h
   return launch_batch_gemm(g, 0, 1, st) == hipSuccess ? PDM_OK : PDM_ERR_LAUNCH;
 }
 
+// y[b] = M x[b] for a bf16 matrix M [rows][K] at arena offset off (router, LM
+// head): on the matrix cores from kBf16MfmaMinB tokens on (no conversion of
+// the weights at all), else one wave per 4 rows on the vector ALUs. The
+// matrix cores' buffer addressing covers matrices below 2 GiB.
+constexpr int kBf16MfmaMinB = 2;
+int step_bf16(pdm_engine* e, uint64_t off, int rows, int K, const float* x, int B, float* y, hipStream_t st) {
+  if (B < kBf16MfmaMinB || (uint64_t)rows * K * 2 > 0x7FFFFFFFull)
+    return bs_bf16_rows(x, reinterpret_cast<const uint16_t*>(e->w + off), rows, K, B, y, st) == hipSuccess
+               ? PDM_OK
+               : PDM_ERR_LAUNCH;
+  BatchGemm g{};
+  g.base = e->w;
+  g.codes_off = off;
+  g.rows = rows;
+  g.K = K;
+  g.B = B;
+  g.fmt = kFmtBf16;
+  g.xg = ws_xg(e);
+  g.y = y;
+  g.ldy = rows;
+  batch_gemm_grid(g, 1);
+  BatchStage sa{};
+  sa.x = x;
+  sa.xg = ws_xg(e);
+  sa.ldx = K;
+  sa.B = B;
+  sa.K = K;
+  sa.nwin = g.slabs * 8;
+  sa.z0 = y;
+  sa.n0 = (size_t)B * rows;
+  if (launch_batch_stage(sa, false, sa.nwin * 128, st) != hipSuccess) return PDM_ERR_LAUNCH;
+  return launch_batch_gemm(g, 0, 1, st) == hipSuccess ? PDM_OK : PDM_ERR_LAUNCH;
+}
+
 }  // namespace
 
 int pdm_batch_decode_step(pdm_engine* e, int32_t B, const int32_t* tokens, const int32_t* positions,
@@ -991,8 +1025,7 @@ int pdm_batch_decode_step(pdm_engine* e, int32_t B, const int32_t* tokens, const
     if ((rc = step_gemm(e, Lp.wo, o, B, t, st))) return rc;
     if (!ok(bs_norm(x, t, false, gain(Lp.ffn_norm), d.rms_eps, B, D, h, st))) return PDM_ERR_LAUNCH;
     if (Lp.is_moe) {
-      if (!ok(bs_bf16_rows(h, reinterpret_cast<const uint16_t*>(W + Lp.router), d.n_experts, D, B, rlog, st)))
-        return PDM_ERR_LAUNCH;
+      if ((rc = step_bf16(e, Lp.router, d.n_experts, D, h, B, rlog, st))) return rc;
       if (!ok(bs_topk(rlog, B, d.n_experts, d.top_k, idx, wts, st))) return PDM_ERR_LAUNCH;
     }
     if ((rc = pdm_batch_ffn(e, l, h, B, Lp.is_moe ? idx : nullptr, Lp.is_moe ? wts : nullptr, t, stream))) return rc;
@@ -1003,8 +1036,7 @@ int pdm_batch_decode_step(pdm_engine* e, int32_t B, const int32_t* tokens, const
       return PDM_ERR_LAUNCH;
   }
   if (d.vocab > 0) {
-    if (!ok(bs_bf16_rows(h, reinterpret_cast<const uint16_t*>(W + P.lm_head), d.vocab, D, B, logits_dev, st)))
-      return PDM_ERR_LAUNCH;
+    if ((rc = step_bf16(e, P.lm_head, d.vocab, D, h, B, logits_dev, st))) return rc;
     if (argmax_dev && !ok(bs_argmax(logits_dev, B, d.vocab, F(L0.argv), reinterpret_cast<int32_t*>(e->step_ws + L0.argi),
                                     argmax_dev, st)))
       return PDM_ERR_LAUNCH;

@@ -31,7 +31,9 @@
 // MXFP4 products the columns of a window pair are interleaved so that one
 // 16-byte load of a lane is the 32 columns (one scale block) it needs for
 // both windows: window 2p + h, lane group g holds columns 128 p + 32 g + 16 h
-// .. + 15 (the activations are staged in the same order).
+// .. + 15 (the activations are staged in the same order). bf16 matrices (the
+// router and the LM head, kFmtBf16) need no conversion at all: a lane's 16
+// columns of a window are two 16-byte loads, A1 and A2 as they are.
 //
 // Work split: a workgroup (4 waves) owns 8 row tiles (128 rows) and a run of
 // K slabs (8 windows = 512 columns each). Per slab, each wave issues its two
@@ -195,9 +197,10 @@ __global__ void __launch_bounds__(kBT) batch_stage_act_kernel(BatchStage a) {
 // u_list[s], output y + s * B * ldy ([slot][B][rows]). MODE 2: K slots, slot
 // s the down matrix of expert u_list[s], its staged activations at xg + s *
 // xg_slot (u32x4). Activations come staged (xg, whole slabs).
-template <int MODE, int FMT>  // FMT: PDM_FMT_FP8 or PDM_FMT_MXFP4 codes
+template <int MODE, int FMT>  // FMT: PDM_FMT_FP8 or PDM_FMT_MXFP4 codes, or kFmtBf16 weights
 __global__ void __launch_bounds__(kBT) batch_gemm_kernel(BatchGemm g) {
   constexpr bool kMx = FMT == PDM_FMT_MXFP4;
+  constexpr bool kBf = FMT == kFmtBf16;
   __shared__ u32x4_t xs[kSlabU4];  // [window][piece][lane]
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int per = g.splits * g.groups;
@@ -211,7 +214,7 @@ __global__ void __launch_bounds__(kBT) batch_gemm_kernel(BatchGemm g) {
   const uint16_t* scales = reinterpret_cast<const uint16_t*>(blk + g.scales_off);
   const u32x4_t* xg = g.xg + (MODE == 2 ? (size_t)slot * g.xg_slot : 0);
   const int rows = g.rows, K = g.K, B = g.B, nkb = g.nkb, nsc = rows >> 3;
-  const int rowb = kMx ? K / 2 : K;  // code bytes per row
+  const int rowb = kBf ? 2 * K : kMx ? K / 2 : K;  // weight bytes per row
   const __amdgpu_buffer_rsrc_t rc =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(codes), 0, (int)((uint64_t)rows * rowb), kBufWord3);
   // MXFP4: e8m0 scale bytes [rows][nkb], nkb = K / 32
@@ -234,7 +237,7 @@ __global__ void __launch_bounds__(kBT) batch_gemm_kernel(BatchGemm g) {
     }
     // ---- this slab's weight codes (and MXFP4 scales) for the wave's row tiles:
     // FP8, one 16-byte load per window; MXFP4, one per window pair (32 columns)
-    constexpr int kLd = kMx ? kSlabW / 2 : kSlabW;
+    constexpr int kLd = kMx ? kSlabW / 2 : kBf ? 2 * kSlabW : kSlabW;
     u32x4_t wv[kTilesPerWave][kLd];
     uint32_t ws[kMx ? kTilesPerWave : 1][kMx ? kLd : 1];
 #pragma unroll
@@ -248,6 +251,10 @@ __global__ void __launch_bounds__(kBT) batch_gemm_kernel(BatchGemm g) {
           const bool in = rt < g.tiles && row < rows && k < K;
           wv[t][i] = __builtin_amdgcn_raw_buffer_load_b128(rc, in ? (uint32_t)(row * rowb + k / 2) : kOob, 0, 0);
           ws[t][i] = __builtin_amdgcn_raw_buffer_load_b8(rs, in ? (uint32_t)(row * nkb + k / 32) : kOob, 0, 0);
+        } else if constexpr (kBf) {  // window i / 2, columns 8 (i & 1) .. of the lane's 16
+          const int k = (s * kSlabW + (i >> 1)) * 64 + lg * 16 + (i & 1) * 8;
+          const bool in = rt < g.tiles && row < rows && k < K;
+          wv[t][i] = __builtin_amdgcn_raw_buffer_load_b128(rc, in ? (uint32_t)(row * rowb + 2 * k) : kOob, 0, 0);
         } else {
           const int k = (s * kSlabW + i) * 64 + lg * 16;
           const bool in = rt < g.tiles && row < rows && k < K;
@@ -273,7 +280,11 @@ __global__ void __launch_bounds__(kBT) batch_gemm_kernel(BatchGemm g) {
         for (int i2 = 0; i2 < 2; ++i2) {
           const int win = kb * 2 + i2;
           uint32_t p[8];
-          if constexpr (kMx) {  // window pair kb: bytes 8 i2 .. 8 i2 + 7 of its load
+          if constexpr (kBf) {
+            const u32x4_t c0 = wv[t][2 * win], c1 = wv[t][2 * win + 1];
+            p[0] = c0[0]; p[1] = c0[1]; p[2] = c0[2]; p[3] = c0[3];
+            p[4] = c1[0]; p[5] = c1[1]; p[6] = c1[2]; p[7] = c1[3];
+          } else if constexpr (kMx) {  // window pair kb: bytes 8 i2 .. 8 i2 + 7 of its load
             const u32x4_t c = wv[t][kb];
             const float sc4 = e8m0_f32(ws[t][kb]);
             fp4x8_to_bf16(c[2 * i2], sc4, p[0], p[1], p[2], p[3]);
@@ -296,7 +307,7 @@ __global__ void __launch_bounds__(kBT) batch_gemm_kernel(BatchGemm g) {
           tmp = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A2, H2, tmp, 0, 0, 0);
           tmp = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A2, L2, tmp, 0, 0, 0);
         }
-        const float sc = kMx ? 1.f  // (applied in the conversion)
+        const float sc = kMx || kBf ? 1.f  // (MXFP4: applied in the conversion; bf16: none)
                          : srow < nsc ? __builtin_bit_cast(float, (uint32_t)scales[(size_t)srow * nkb + kbg] << 16)
                                       : 0.f;
 #pragma unroll
@@ -412,7 +423,9 @@ hipError_t launch_batch_gemm(const BatchGemm& g, int mode, int n_slots, hipStrea
   const int grid = per * (mode == 0 ? 1 : n_slots);
   if (grid <= 0) return hipSuccess;
   const bool mx = g.fmt == PDM_FMT_MXFP4;
-  if (mode == 0 && !mx) hipLaunchKernelGGL((batch_gemm_kernel<0, PDM_FMT_FP8>), dim3(grid), dim3(kBT), 0, st, g);
+  if (mode == 0 && g.fmt == kFmtBf16)
+    hipLaunchKernelGGL((batch_gemm_kernel<0, kFmtBf16>), dim3(grid), dim3(kBT), 0, st, g);
+  else if (mode == 0 && !mx) hipLaunchKernelGGL((batch_gemm_kernel<0, PDM_FMT_FP8>), dim3(grid), dim3(kBT), 0, st, g);
   else if (mode == 0) hipLaunchKernelGGL((batch_gemm_kernel<0, PDM_FMT_MXFP4>), dim3(grid), dim3(kBT), 0, st, g);
   else if (mode == 1 && !mx) hipLaunchKernelGGL((batch_gemm_kernel<1, PDM_FMT_FP8>), dim3(grid), dim3(kBT), 0, st, g);
   else if (mode == 1) hipLaunchKernelGGL((batch_gemm_kernel<1, PDM_FMT_MXFP4>), dim3(grid), dim3(kBT), 0, st, g);

@@ -62,9 +62,11 @@ struct BatchGemm {
   int32_t ldy;
   int32_t tiles, slabs, groups;  // 16-row tiles, 512-column K slabs, 8-tile row groups
   int32_t spw, splits;           // K slabs per workgroup, K splits per row group
-  int32_t fmt;                   // PDM_FMT_FP8 (K code bytes per row) or PDM_FMT_MXFP4 (K / 2; nkb = K / 32
-                                 // e8m0 scale bytes per row); K counts columns either way
+  int32_t fmt;                   // PDM_FMT_FP8 (K code bytes per row), PDM_FMT_MXFP4 (K / 2; nkb = K / 32
+                                 // e8m0 scale bytes per row) or kFmtBf16 (2 K bytes, no scales, mode 0);
+                                 // K counts columns either way
 };
+constexpr int kFmtBf16 = 2;      // BatchGemm::fmt of a bf16 matrix (router, LM head)
 // Geometry of a launch over n_slots slot matrices (1 for mode 0).
 void batch_gemm_grid(BatchGemm& g, int n_slots);
 hipError_t launch_batch_gemm(const BatchGemm& g, int mode, int n_slots, hipStream_t st);

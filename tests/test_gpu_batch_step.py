@@ -99,6 +99,11 @@ def test_batch_step_tiny():
     _check("tiny", [16, 40, 7], 3)
 
 
+def test_batch_step_tiny_single():
+    """One sequence: the router and LM head rows take the vector-ALU path."""
+    _check("tiny", [33], 2)
+
+
 def test_batch_step_tiny_sixteen():
     """The largest batch: 16 sequences with prompts of 1 to 60 tokens."""
     _check("tiny", [1, 7, 16, 40, 60, 3, 22, 35, 9, 48, 13, 2, 57, 30, 5, 44], 2)
