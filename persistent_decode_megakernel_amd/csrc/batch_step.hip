@@ -238,21 +238,28 @@ __global__ void __launch_bounds__(kAbT) bs_absorb_kernel(const float* q, const u
 }
 
 // MLA attention of sequence b over its cache positions 0 .. pos[b] for a group
-// of 16 heads (one workgroup of 4 waves): scores S[t][h] = tau * ([q_lat ;
+// of 16 heads (one workgroup of 8 waves): scores S[t][h] = tau * ([q_lat ;
 // q_pe][h] . row t) and values O[h] = sum_t softmax(S)[t][h] * c_t on the
 // matrix cores (v_mfma_f32_16x16x32_bf16: cache rows are bf16 already, the
 // fp32 queries and probabilities enter as a bf16 high part plus a bf16
 // residual), online softmax over blocks of 64 positions. Operand layout
 // (lane l, g = l / 16): A holds A[l % 16][8 g .. 8 g + 7], B holds B[8 g ..
-// 8 g + 7][l % 16], C holds C[4 g .. 4 g + 3][l % 16].
+// 8 g + 7][l % 16], C holds C[4 g .. 4 g + 3][l % 16]. Scores: waves 0-3
+// take the block's four 16-position tiles over the first half of the latent
+// k-blocks, waves 4-7 the same tiles over the second half (two partial score
+// arrays, added by the softmax); values: wave w takes NT / 2 tiles of 16
+// latent dims.
 constexpr int kBlk = 64;
+constexpr int kAT = 512;                                    // threads of an attention workgroup
 constexpr int kAtMaxRow = 640;                              // kv_lora + rope, at most 512 + 128
-constexpr int kAtLd = (kBlk * (kAtMaxRow / 8) + kST - 1) / kST;  // 16-byte cache pieces per thread and block
-constexpr int kAtQ = (16 * kAtMaxRow + kST - 1) / kST;           // query values per thread
-template <int NT>  // value tiles of 16 latent dims per wave: dc / 64 (2, 4 or 8)
-__global__ void __launch_bounds__(kST) bs_attn_kernel(const float* qlat, const float* qpe, const uint16_t* cache,
+constexpr int kAtLd = (kBlk * (kAtMaxRow / 8) + kAT - 1) / kAT;  // 16-byte cache pieces per thread and block
+constexpr int kAtQ = (16 * kAtMaxRow + kAT - 1) / kAT;           // query values per thread
+template <int NT>  // value tiles of 16 latent dims per pair of waves: dc / 64 (2, 4 or 8)
+__global__ void __launch_bounds__(kAT) bs_attn_kernel(const float* qlat, const float* qpe, const uint16_t* cache,
                                                      int64_t seq_stride, int H, int dc, int dr, float tau,
                                                      BatchTokens tk, int nch, int chunk, float* part) {
+  static_assert(NT % 2 == 0, "value tiles split over two waves");
+  constexpr int kVT = NT / 2;  // value tiles per wave
   extern __shared__ __align__(16) unsigned char lds[];
   const int kvr = dc + dr, rs = kvr + 8;  // cache-row stride in LDS (bf16), padded
   const int ngrp = (H + 15) / 16;
@@ -263,8 +270,8 @@ __global__ void __launch_bounds__(kST) bs_attn_kernel(const float* qlat, const f
   __bf16* qh = reinterpret_cast<__bf16*>(lds);                 // [16][rs]
   __bf16* ql = qh + 16 * rs;                                   // [16][rs]
   uint16_t* kv = reinterpret_cast<uint16_t*>(ql + 16 * rs);    // [kBlk][rs]
-  float* S = reinterpret_cast<float*>(kv + kBlk * rs);         // [16][kBlk]
-  float* hm = S + 16 * kBlk;                                   // running max, sum, rescale per head
+  float* S = reinterpret_cast<float*>(kv + kBlk * rs);         // [2][16][kBlk] score partials
+  float* hm = S + 2 * 16 * kBlk;                               // running max, sum, rescale per head
   float* hl = hm + 16;
   float* ha = hl + 16;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, lr = lane & 15, lg = lane >> 4;
@@ -279,7 +286,7 @@ __global__ void __launch_bounds__(kST) bs_attn_kernel(const float* qlat, const f
     const int nb = min(kBlk, t1 - tb);
 #pragma unroll
     for (int j = 0; j < kAtLd; ++j) {
-      const int i = (int)threadIdx.x + j * kST, r = i / q8, p = i - r * q8;
+      const int i = (int)threadIdx.x + j * kAT, r = i / q8, p = i - r * q8;
       const bool ok = i < kBlk * q8 && r < nb;
       kvr_regs[j] = *reinterpret_cast<const su32x4*>(seq + (size_t)(tb + (ok ? r : 0)) * kvr + (ok ? p : 0) * 8);
     }
@@ -291,7 +298,7 @@ __global__ void __launch_bounds__(kST) bs_attn_kernel(const float* qlat, const f
     float qv[kAtQ];
 #pragma unroll
     for (int j = 0; j < kAtQ; ++j) {
-      const int i = (int)threadIdx.x + j * kST, hh = i / kvr, d = i - hh * kvr, hd = h0 + hh;
+      const int i = (int)threadIdx.x + j * kAT, hh = i / kvr, d = i - hh * kvr, hd = h0 + hh;
       const bool ok = i < 16 * kvr && hd < H;
       const int hq = ok ? hd : h0, dq = ok ? d : 0;
       const float* src = dq < dc ? qlat + ((size_t)b * H + hq) * dc + dq : qpe + ((size_t)b * H + hq) * dr + dq - dc;
@@ -299,7 +306,7 @@ __global__ void __launch_bounds__(kST) bs_attn_kernel(const float* qlat, const f
     }
 #pragma unroll
     for (int j = 0; j < kAtQ; ++j) {
-      const int i = (int)threadIdx.x + j * kST, hh = i / kvr, d = i - hh * kvr;
+      const int i = (int)threadIdx.x + j * kAT, hh = i / kvr, d = i - hh * kvr;
       if (i < 16 * kvr) {
         const float v = h0 + hh < H ? tau * qv[j] : 0.f, hi = bf_round(v);
         qh[hh * rs + d] = __builtin_bit_cast(__bf16, bf_rne(v));
@@ -308,58 +315,61 @@ __global__ void __launch_bounds__(kST) bs_attn_kernel(const float* qlat, const f
     }
   }
   if (threadIdx.x < 16) { hm[threadIdx.x] = -INFINITY; hl[threadIdx.x] = 0.f; }
-  constexpr int nt = NT;
-  sf32x4 acc[8];
+  sf32x4 acc[kVT];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) acc[i] = (sf32x4){0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < kVT; ++i) acc[i] = (sf32x4){0.f, 0.f, 0.f, 0.f};
+  const int nkb = kvr / 32;  // MFMA k-blocks of a score
   for (int tb = t0; tb < t1; tb += kBlk) {
     const int nb = min(kBlk, t1 - tb);
     if (tb > t0) load_block(tb);
     __syncthreads();  // previous block's rows and probabilities are consumed
 #pragma unroll
     for (int j = 0; j < kAtLd; ++j) {
-      const int i = (int)threadIdx.x + j * kST, r = i / q8, p = i - r * q8;
+      const int i = (int)threadIdx.x + j * kAT, r = i / q8, p = i - r * q8;
       if (i < kBlk * q8)
         *reinterpret_cast<su32x4*>(kv + r * rs + p * 8) = r < nb ? kvr_regs[j] : (su32x4){0u, 0u, 0u, 0u};
     }
     __syncthreads();
-    // scores: wave w takes positions 16 w .. 16 w + 15 of the block
+    // scores: wave w takes positions 16 (w & 3) .. + 15 over half (w >> 2) of the k-blocks
     {
+      const int tile = w & 3, half = w >> 2;
+      const int kb0 = half ? nkb / 2 : 0, kb1 = half ? nkb : nkb / 2;
       sf32x4 sc = {0.f, 0.f, 0.f, 0.f};
-      if (16 * w < nb) {
-        for (int kb = 0; kb < kvr / 32; ++kb) {
-          const sbf16x8 a = *reinterpret_cast<const sbf16x8*>(kv + (16 * w + lr) * rs + kb * 32 + lg * 8);
+      if (16 * tile < nb) {
+        for (int kb = kb0; kb < kb1; ++kb) {
+          const sbf16x8 a = *reinterpret_cast<const sbf16x8*>(kv + (16 * tile + lr) * rs + kb * 32 + lg * 8);
           const sbf16x8 b1 = *reinterpret_cast<const sbf16x8*>(qh + lr * rs + kb * 32 + lg * 8);
           const sbf16x8 b2 = *reinterpret_cast<const sbf16x8*>(ql + lr * rs + kb * 32 + lg * 8);
           sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b1, sc, 0, 0, 0);
           sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b2, sc, 0, 0, 0);
         }
       }
-      // sc[i] = S[position 16 w + 4 lg + i][head lr]
+      // sc[i] = partial S[position 16 tile + 4 lg + i][head lr]
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int t = 16 * w + 4 * lg + i;
-        S[lr * kBlk + t] = t < nb ? sc[i] : -INFINITY;
+        const int t = 16 * tile + 4 * lg + i;
+        S[(half * 16 + lr) * kBlk + t] = sc[i];
       }
     }
     __syncthreads();
-    // online softmax: 16 threads per head, 4 positions each
+    // online softmax: 32 threads per head, 2 positions each; the probabilities
+    // replace the first score partial
     {
-      const int hh = threadIdx.x >> 4, sub = threadIdx.x & 15;
-      float* srow = S + hh * kBlk + sub * 4;
-      float mx = fmaxf(fmaxf(srow[0], srow[1]), fmaxf(srow[2], srow[3]));
+      const int hh = threadIdx.x >> 5, sub = threadIdx.x & 31;
+      float* s0 = S + hh * kBlk + sub * 2;
+      const float* s1 = S + (16 + hh) * kBlk + sub * 2;
+      const float v0 = sub * 2 < nb ? s0[0] + s1[0] : -INFINITY;
+      const float v1 = sub * 2 + 1 < nb ? s0[1] + s1[1] : -INFINITY;
+      float mx = fmaxf(v0, v1);
 #pragma unroll
-      for (int o = 8; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 16));
+      for (int o = 16; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 32));
       const float mold = hm[hh], mn = fmaxf(mold, mx);
-      float ps = 0.f;
+      const float p0 = v0 == -INFINITY ? 0.f : __expf(v0 - mn), p1 = v1 == -INFINITY ? 0.f : __expf(v1 - mn);
+      s0[0] = p0;
+      s0[1] = p1;
+      float ps = p0 + p1;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float p = srow[i] == -INFINITY ? 0.f : __expf(srow[i] - mn);
-        srow[i] = p;
-        ps += p;
-      }
-#pragma unroll
-      for (int o = 8; o > 0; o >>= 1) ps += __shfl_xor(ps, o, 16);
+      for (int o = 16; o > 0; o >>= 1) ps += __shfl_xor(ps, o, 32);
       __syncthreads();  // every thread has read hm before it changes
       if (sub == 0) {
         const float alpha = mold == -INFINITY ? 0.f : __expf(mold - mn);
@@ -369,14 +379,11 @@ __global__ void __launch_bounds__(kST) bs_attn_kernel(const float* qlat, const f
       }
     }
     __syncthreads();
-    // values: wave w takes dims [w * nt * 16, (w + 1) * nt * 16)
+    // values: wave w takes dims [w * kVT * 16, (w + 1) * kVT * 16)
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      if (i < nt) {
+    for (int i = 0; i < kVT; ++i)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) acc[i][r] *= ha[4 * lg + r];
-      }
-    }
+      for (int r = 0; r < 4; ++r) acc[i][r] *= ha[4 * lg + r];
     for (int pb = 0; pb < kBlk / 32; ++pb) {
       if (pb * 32 >= nb) break;  // uniform
       const float* prow = S + lr * kBlk + pb * 32 + 8 * lg;
@@ -388,31 +395,27 @@ __global__ void __launch_bounds__(kST) bs_attn_kernel(const float* qlat, const f
         al[e] = __builtin_bit_cast(__bf16, bf_rne(v - hi));
       }
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        if (i < nt) {
-          const int col = (w * nt + i) * 16 + lr;
-          const uint16_t* vcol = kv + (pb * 32 + 8 * lg) * rs + col;
-          sbf16x8 bv;
+      for (int i = 0; i < kVT; ++i) {
+        const int col = (w * kVT + i) * 16 + lr;
+        const uint16_t* vcol = kv + (pb * 32 + 8 * lg) * rs + col;
+        sbf16x8 bv;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) bv[e] = __builtin_bit_cast(__bf16, vcol[e * rs]);
-          acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bv, acc[i], 0, 0, 0);
-          acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bv, acc[i], 0, 0, 0);
-        }
+        for (int e = 0; e < 8; ++e) bv[e] = __builtin_bit_cast(__bf16, vcol[e * rs]);
+        acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bv, acc[i], 0, 0, 0);
+        acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bv, acc[i], 0, 0, 0);
       }
     }
   }
   __syncthreads();
   // the chunk's partial per head: [acc (dc) ; max ; sum] at part[b][h][ch];
-  // acc[i][r] = O[head 4 lg + r][dim (w nt + i) 16 + lr]
+  // acc[i][r] = O[head 4 lg + r][dim (w kVT + i) 16 + lr]
   const int ps = dc + 2;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    if (i < nt) {
+  for (int i = 0; i < kVT; ++i) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int hd = h0 + 4 * lg + r;
-        if (hd < H) part[(((size_t)b * H + hd) * nch + ch) * ps + (w * nt + i) * 16 + lr] = acc[i][r];
-      }
+    for (int r = 0; r < 4; ++r) {
+      const int hd = h0 + 4 * lg + r;
+      if (hd < H) part[(((size_t)b * H + hd) * nch + ch) * ps + (w * kVT + i) * 16 + lr] = acc[i][r];
     }
   }
   if (threadIdx.x < 16 && h0 + (int)threadIdx.x < H) {
@@ -697,7 +700,7 @@ hipError_t bs_absorb(const float* q, const uint8_t* codes, const uint16_t* scale
 }
 size_t bs_attn_lds(int dc, int dr) {
   const int rs = dc + dr + 8;
-  return (size_t)2 * 16 * rs * 2 + (size_t)kBlk * rs * 2 + 16 * kBlk * 4 + 48 * 4;
+  return (size_t)2 * 16 * rs * 2 + (size_t)kBlk * rs * 2 + 2 * 16 * kBlk * 4 + 48 * 4;
 }
 // Position chunk of the attention workgroups for a longest context of ctx:
 // at least one block of kBlk positions, at most kAttnChunksMax chunks.
@@ -722,13 +725,13 @@ hipError_t bs_attn(const float* qlat, const float* qpe, const uint16_t* cache, i
   const int chunk = bs_attn_chunk(ctx), nch = (ctx + chunk - 1) / chunk;
   const dim3 grid(B * ((H + 15) / 16) * nch);
   if (dc == 512)
-    hipLaunchKernelGGL(bs_attn_kernel<8>, grid, dim3(kST), lds, st, qlat, qpe, cache, seq_stride, H, dc, dr, tau, tk,
+    hipLaunchKernelGGL(bs_attn_kernel<8>, grid, dim3(kAT), lds, st, qlat, qpe, cache, seq_stride, H, dc, dr, tau, tk,
                        nch, chunk, part);
   else if (dc == 256)
-    hipLaunchKernelGGL(bs_attn_kernel<4>, grid, dim3(kST), lds, st, qlat, qpe, cache, seq_stride, H, dc, dr, tau, tk,
+    hipLaunchKernelGGL(bs_attn_kernel<4>, grid, dim3(kAT), lds, st, qlat, qpe, cache, seq_stride, H, dc, dr, tau, tk,
                        nch, chunk, part);
   else
-    hipLaunchKernelGGL(bs_attn_kernel<2>, grid, dim3(kST), lds, st, qlat, qpe, cache, seq_stride, H, dc, dr, tau, tk,
+    hipLaunchKernelGGL(bs_attn_kernel<2>, grid, dim3(kAT), lds, st, qlat, qpe, cache, seq_stride, H, dc, dr, tau, tk,
                        nch, chunk, part);
   hipLaunchKernelGGL(bs_attn_merge_kernel, dim3(B * H), dim3(kST), 0, st, part, H, dc, nch, chunk, tk, olat);
   return hipGetLastError();
