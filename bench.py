@@ -222,6 +222,22 @@ def run_workload(eng, cfg, K, Wm, do_trace, trace_detail, resident_only=False):
         raise SystemExit(f"{cfg.name}: resident launch failed: status {rc} stage {st.stage}")
     resident_s = e0.elapsed_time(e1) / 1e3 / K
 
+    # the same resident launch decoding greedily: each step's token is the
+    # previous step's argmax, fed back on the device (autoregressive decode)
+    greedy_s = None
+    if cfg.vocab > 0 and not resident_only:
+        fill()
+        torch.cuda.synchronize()
+        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        g0.record(stream)
+        eng.decode_steps(P, tok_dev[:1].clone(), n_steps=K, greedy=True, argmax=am[:K])
+        g1.record(stream)
+        torch.cuda.synchronize()
+        rc, st = eng.status()
+        if rc != 0:
+            raise SystemExit(f"{cfg.name}: greedy resident launch failed: status {rc} stage {st.stage}")
+        greedy_s = g0.elapsed_time(g1) / 1e3 / K
+
     bytes_mean = R.mean_bytes_per_token(cfg, P, K)
     out = {
         "workload": cfg.name, "prompt_positions": P, "context_range": [P + 1, P + K], "steps": K,
@@ -229,13 +245,18 @@ def run_workload(eng, cfg, K, Wm, do_trace, trace_detail, resident_only=False):
         "resident": {"ms_per_step": round(resident_s * 1e3, 4), "tok_s_user": round(1 / resident_s, 3),
                      "frac_of_8TBps": round(bytes_mean / resident_s / R.HBM_PEAK_BYTES_PER_S, 4)},
     }
+    if greedy_s is not None:
+        out["resident_greedy"] = {"ms_per_step": round(greedy_s * 1e3, 4), "tok_s_user": round(1 / greedy_s, 3),
+                                  "frac_of_8TBps": round(bytes_mean / greedy_s / R.HBM_PEAK_BYTES_PER_S, 4),
+                                  "tokens": "each step's argmax, fed back on the device"}
     if not resident_only:
         out["per_step_launch"] = {"ms_per_step": round(launch_s * 1e3, 4), "tok_s_user": round(1 / launch_s, 3),
                                   "p50_ms": round(per[K // 2], 4), "p99_ms": round(per[min(K - 1, int(0.99 * K))], 4),
                                   "frac_of_8TBps": round(bytes_mean / launch_s / R.HBM_PEAK_BYTES_PER_S, 4)}
     log(f"{cfg.name}: resident {resident_s * 1e3:.3f} ms/token ({1 / resident_s:.1f} tok/s/user, "
         f"{bytes_mean / resident_s / 1e9:.0f} GB/s)"
-        + ("" if resident_only else f"; single-step launches {launch_s * 1e3:.3f} ms/token"))
+        + ("" if resident_only else f"; single-step launches {launch_s * 1e3:.3f} ms/token")
+        + ("" if greedy_s is None else f"; greedy resident {greedy_s * 1e3:.3f} ms/token"))
     if do_trace:
         plan = describe_plan(cfg, eng.max_ctx, eng.sizes.n_workgroups)
         fill()
