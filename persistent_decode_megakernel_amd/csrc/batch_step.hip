@@ -394,13 +394,31 @@ __global__ void __launch_bounds__(kAT) bs_attn_kernel(const float* qlat, const f
         ah[e] = __builtin_bit_cast(__bf16, bf_rne(v));
         al[e] = __builtin_bit_cast(__bf16, bf_rne(v - hi));
       }
+      // B of tile i = V[pb*32 + 8*lg + e][dim w*kVT*16 + kVT*lr + i]: a lane's
+      // kVT dims of one row are adjacent and come in one LDS read
+      const uint16_t* vrow = kv + (pb * 32 + 8 * lg) * rs + w * kVT * 16 + kVT * lr;
+      uint32_t vw[8][(kVT + 1) / 2];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        if constexpr (kVT == 4) {
+          const uint2 t = *reinterpret_cast<const uint2*>(vrow + e * rs);
+          vw[e][0] = t.x;
+          vw[e][1] = t.y;
+        } else if constexpr (kVT == 2) {
+          vw[e][0] = *reinterpret_cast<const uint32_t*>(vrow + e * rs);
+        } else {
+          vw[e][0] = vrow[e * rs];
+        }
+      }
 #pragma unroll
       for (int i = 0; i < kVT; ++i) {
-        const int col = (w * kVT + i) * 16 + lr;
-        const uint16_t* vcol = kv + (pb * 32 + 8 * lg) * rs + col;
-        sbf16x8 bv;
+        su32x4 bu;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) bv[e] = __builtin_bit_cast(__bf16, vcol[e * rs]);
+        for (int k = 0; k < 4; ++k) {
+          const uint32_t lo = vw[2 * k][i / 2], hi = vw[2 * k + 1][i / 2];
+          bu[k] = (i & 1) ? (lo >> 16) | (hi & 0xffff0000u) : (lo & 0xffffu) | (hi << 16);
+        }
+        const sbf16x8 bv = __builtin_bit_cast(sbf16x8, bu);
         acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bv, acc[i], 0, 0, 0);
         acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bv, acc[i], 0, 0, 0);
       }
@@ -408,14 +426,14 @@ __global__ void __launch_bounds__(kAT) bs_attn_kernel(const float* qlat, const f
   }
   __syncthreads();
   // the chunk's partial per head: [acc (dc) ; max ; sum] at part[b][h][ch];
-  // acc[i][r] = O[head 4 lg + r][dim (w kVT + i) 16 + lr]
+  // acc[i][r] = O[head 4 lg + r][dim w kVT 16 + kVT lr + i]
   const int ps = dc + 2;
 #pragma unroll
   for (int i = 0; i < kVT; ++i) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int hd = h0 + 4 * lg + r;
-      if (hd < H) part[(((size_t)b * H + hd) * nch + ch) * ps + (w * kVT + i) * 16 + lr] = acc[i][r];
+      if (hd < H) part[(((size_t)b * H + hd) * nch + ch) * ps + w * kVT * 16 + kVT * lr + i] = acc[i][r];
     }
   }
   if (threadIdx.x < 16 && h0 + (int)threadIdx.x < H) {

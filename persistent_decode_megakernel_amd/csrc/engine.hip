@@ -1539,14 +1539,33 @@ __device__ __forceinline__ bool stage_attn(const StageEnv& E, Smem& sm) {
           ah[e] = hi;
           al[e] = lo;
         }
+        // B of tile i = V[pb*32 + 8*lg + e][dim w*DTILES*16 + DTILES*lr + i]:
+        // the DTILES dims a lane needs from one row are adjacent, so one LDS
+        // read of 2*DTILES bytes per row serves every tile of the wave
+        const uint16_t* vrow =
+            reinterpret_cast<const uint16_t*>(kvs) + (pb * 32 + 8 * lg) * (2 * kstr) + w * DTILES * 16 + DTILES * lr;
+        uint32_t vw[8][(DTILES + 1) / 2];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          if constexpr (DTILES == 4) {
+            const uint2 t = *reinterpret_cast<const uint2*>(vrow + e * 2 * kstr);
+            vw[e][0] = t.x;
+            vw[e][1] = t.y;
+          } else if constexpr (DTILES == 2) {
+            vw[e][0] = *reinterpret_cast<const uint32_t*>(vrow + e * 2 * kstr);
+          } else {
+            vw[e][0] = vrow[e * 2 * kstr];
+          }
+        }
 #pragma unroll
         for (int i = 0; i < DTILES; ++i) {
-          // B = V[pb*32 + 8*lg + e][dim tile*16 + lr]: one bf16 from each of 8 rows
-          const int col = (w * DTILES + i) * 16 + lr;
-          const uint16_t* vcol = reinterpret_cast<const uint16_t*>(kvs) + (pb * 32 + 8 * lg) * (2 * kstr) + col;
-          bf16x8 b;
+          u32x4 bu;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) b[e] = __builtin_bit_cast(__bf16, vcol[e * 2 * kstr]);
+          for (int k = 0; k < 4; ++k) {
+            const uint32_t lo = vw[2 * k][i / 2], hi = vw[2 * k + 1][i / 2];
+            bu[k] = (i & 1) ? (lo >> 16) | (hi & 0xffff0000u) : (lo & 0xffffu) | (hi << 16);
+          }
+          const bf16x8 b = u32x4_as_bf16x8(bu);
           acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, b, acc[i], 0, 0, 0);
           acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, b, acc[i], 0, 0, 0);
         }
@@ -1555,7 +1574,7 @@ __device__ __forceinline__ bool stage_attn(const StageEnv& E, Smem& sm) {
   }
   __syncthreads();
   mark(c, sm, 1);
-  // ---- partials: acc[i][r] = O[head 4*lg + r][dim (w*DTILES + i)*16 + lr].
+  // ---- partials: acc[i][r] = O[head 4*lg + r][dim w*DTILES*16 + DTILES*lr + i].
   // A head's partial row is [acc (d_c) ; max ; sum ; 0 ; 0] (a 16-byte
   // multiple); the rows are transposed through LDS (the cache-row space is
   // free now) so that every lane stores whole 16-byte pieces.
@@ -1565,7 +1584,7 @@ __device__ __forceinline__ bool stage_attn(const StageEnv& E, Smem& sm) {
   for (int r = 0; r < 4; ++r) {
     const int hh = 4 * lg + r;
 #pragma unroll
-    for (int i = 0; i < DTILES; ++i) tout[hh * ps + (w * DTILES + i) * 16 + lr] = acc[i][r];
+    for (int i = 0; i < DTILES; ++i) tout[hh * ps + w * DTILES * 16 + DTILES * lr + i] = acc[i][r];
   }
   if (threadIdx.x < kMH) {
     float* t = tout + threadIdx.x * ps + dc;
