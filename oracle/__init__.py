@@ -18,3 +18,4 @@ from .model import (OracleWeights, DecodeState, decode_step, forward_full, prefi
                     rmsnorm, rope, softmax, route, topk_indices, mla_absorbed, mla_naive,
                     split_wkv_b, attention_decode, ffn_decode, lm_logits)
 from .batch import batch_gemm, batch_ffn  # noqa: F401
+from . import dsa  # noqa: F401
