@@ -12,7 +12,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OUT_DIR = os.path.join(HERE, "_lib")
 OUT = os.path.join(OUT_DIR, "libpdm.so")
-SOURCES = ["engine.hip", "batch.hip", "batch_step.hip", "api.cpp", "planner.cpp"]
+SOURCES = ["engine.hip", "batch.hip", "batch_step.hip", "dsa.hip", "api.cpp", "planner.cpp"]
 
 # Packed FP32 VALU forms stay off: plain float code only. The atomic
 # optimizer (which turns a few lanes' LDS or global atomics into a lane loop

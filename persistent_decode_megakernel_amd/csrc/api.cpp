@@ -1044,6 +1044,42 @@ int pdm_batch_decode_step(pdm_engine* e, int32_t B, const int32_t* tokens, const
   return PDM_OK;
 }
 
+int pdm_dsa_index_scores(const float* q_dev, const float* w_dev, const uint16_t* k_dev, int32_t n, int32_t HI,
+                         int32_t dI, float* scores_dev, pdm_stream_t stream) {
+  if (!q_dev || !w_dev || !k_dev || !scores_dev || n < 0) return PDM_ERR_ARG;
+  if (HI < 16 || HI > 64 || HI % 16 || dI < 32 || dI > 256 || dI % 32) return PDM_ERR_CONFIG;
+  if (reinterpret_cast<uintptr_t>(k_dev) & 15) return PDM_ERR_ALIGN;
+  return dsa_scores(q_dev, w_dev, k_dev, n, HI, dI, scores_dev, (hipStream_t)stream) == hipSuccess ? PDM_OK : PDM_ERR_LAUNCH;
+}
+
+int pdm_dsa_topk(const float* scores_dev, int32_t n, int32_t k, int32_t* idx_dev, pdm_stream_t stream) {
+  if (!scores_dev || !idx_dev || n < 0 || k < 0) return PDM_ERR_ARG;
+  return dsa_topk(scores_dev, n, k, idx_dev, (hipStream_t)stream) == hipSuccess ? PDM_OK : PDM_ERR_LAUNCH;
+}
+
+uint64_t pdm_dsa_attention_work_bytes(int32_t H, int32_t kv_lora) {
+  if (H < 1 || kv_lora < 1) return 0;
+  return (uint64_t)H * kAttnChunksMax * (kv_lora + 2) * 4;
+}
+
+int pdm_dsa_attention(const float* q_lat_dev, const float* q_pe_dev, const uint16_t* cache_dev, int32_t cache_rows,
+                      const int32_t* sel_dev, int32_t n_sel, int32_t H, int32_t kv_lora, int32_t rope, float tau,
+                      float* work_dev, uint64_t work_bytes, float* o_lat_dev, pdm_stream_t stream) {
+  if (!q_lat_dev || !q_pe_dev || !cache_dev || !sel_dev || !work_dev || !o_lat_dev) return PDM_ERR_ARG;
+  if (n_sel < 1 || H < 1 || cache_rows < 1) return PDM_ERR_ARG;
+  if (kv_lora != 128 && kv_lora != 256 && kv_lora != 512) return PDM_ERR_CONFIG;
+  const int kvr = kv_lora + rope;
+  if (rope < 0 || kvr % 32 || kvr > 640) return PDM_ERR_CONFIG;
+  if (reinterpret_cast<uintptr_t>(cache_dev) & 15) return PDM_ERR_ALIGN;
+  if (work_bytes < pdm_dsa_attention_work_bytes(H, kv_lora)) return PDM_ERR_SIZE;
+  BatchTokens tk{};
+  tk.pos[0] = n_sel - 1;  // the attention's positions are the list's entries
+  return bs_attn(q_lat_dev, q_pe_dev, cache_dev, 0, H, kv_lora, rope, tau, tk, 1, work_dev, o_lat_dev,
+                 (hipStream_t)stream, sel_dev, 0, cache_rows) == hipSuccess
+             ? PDM_OK
+             : PDM_ERR_LAUNCH;
+}
+
 int pdm_destroy(pdm_engine* e) {
   if (!e) return PDM_ERR_ARG;
   if (e->batch_ws || e->step_ws) {

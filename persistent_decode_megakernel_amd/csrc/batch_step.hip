@@ -254,10 +254,14 @@ constexpr int kAT = 512;                                    // threads of an att
 constexpr int kAtMaxRow = 640;                              // kv_lora + rope, at most 512 + 128
 constexpr int kAtLd = (kBlk * (kAtMaxRow / 8) + kAT - 1) / kAT;  // 16-byte cache pieces per thread and block
 constexpr int kAtQ = (16 * kAtMaxRow + kAT - 1) / kAT;           // query values per thread
-template <int NT>  // value tiles of 16 latent dims per pair of waves: dc / 64 (2, 4 or 8)
+// SP: sparse attention over a position list. Attention position t of
+// sequence b is then cache row sel[b * sel_stride + t] (clamped to
+// [0, sel_rows)), and tk.pos[b] + 1 is the list's length.
+template <int NT, bool SP>  // NT: value tiles of 16 latent dims per pair of waves: dc / 64 (2, 4 or 8)
 __global__ void __launch_bounds__(kAT) bs_attn_kernel(const float* qlat, const float* qpe, const uint16_t* cache,
                                                      int64_t seq_stride, int H, int dc, int dr, float tau,
-                                                     BatchTokens tk, int nch, int chunk, float* part) {
+                                                     BatchTokens tk, int nch, int chunk, float* part,
+                                                     const int32_t* sel, int sel_stride, int sel_rows) {
   static_assert(NT % 2 == 0, "value tiles split over two waves");
   constexpr int kVT = NT / 2;  // value tiles per wave
   extern __shared__ __align__(16) unsigned char lds[];
@@ -288,7 +292,9 @@ __global__ void __launch_bounds__(kAT) bs_attn_kernel(const float* qlat, const f
     for (int j = 0; j < kAtLd; ++j) {
       const int i = (int)threadIdx.x + j * kAT, r = i / q8, p = i - r * q8;
       const bool ok = i < kBlk * q8 && r < nb;
-      kvr_regs[j] = *reinterpret_cast<const su32x4*>(seq + (size_t)(tb + (ok ? r : 0)) * kvr + (ok ? p : 0) * 8);
+      const int t = tb + (ok ? r : 0);
+      const int row = SP ? min(max(sel[(size_t)b * sel_stride + t], 0), sel_rows - 1) : t;
+      kvr_regs[j] = *reinterpret_cast<const su32x4*>(seq + (size_t)row * kvr + (ok ? p : 0) * 8);
     }
   };
   load_block(t0);
@@ -726,31 +732,50 @@ int bs_attn_chunk(int ctx) {
   const int c = std::max(kBlk, (ctx + kAttnChunksMax - 1) / kAttnChunksMax);
   return (c + kBlk - 1) / kBlk * kBlk;
 }
-hipError_t bs_attn(const float* qlat, const float* qpe, const uint16_t* cache, int64_t seq_stride, int H, int dc,
-                   int dr, float tau, const BatchTokens& tk, int B, float* part, float* olat, hipStream_t st) {
-  const size_t lds = bs_attn_lds(dc, dr);
+template <int NT, bool SP>
+static hipError_t launch_attn(dim3 grid, size_t lds, hipStream_t st, const float* qlat, const float* qpe,
+                              const uint16_t* cache, int64_t seq_stride, int H, int dc, int dr, float tau,
+                              const BatchTokens& tk, int nch, int chunk, float* part, const int32_t* sel,
+                              int sel_stride, int sel_rows) {
   static bool raised = false;  // more dynamic LDS than the default 64 KB (gfx950 has 160 KB)
   if (!raised) {
-    for (const void* f : {reinterpret_cast<const void*>(&bs_attn_kernel<8>), reinterpret_cast<const void*>(&bs_attn_kernel<4>),
-                          reinterpret_cast<const void*>(&bs_attn_kernel<2>)}) {
-      const hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-      if (e != hipSuccess) return e;
-    }
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&bs_attn_kernel<NT, SP>),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    if (e != hipSuccess) return e;
     raised = true;
   }
+  hipLaunchKernelGGL((bs_attn_kernel<NT, SP>), grid, dim3(kAT), lds, st, qlat, qpe, cache, seq_stride, H, dc, dr,
+                     tau, tk, nch, chunk, part, sel, sel_stride, sel_rows);
+  return hipGetLastError();
+}
+template <bool SP>
+static hipError_t launch_attn_nt(dim3 grid, size_t lds, hipStream_t st, const float* qlat, const float* qpe,
+                                 const uint16_t* cache, int64_t seq_stride, int H, int dc, int dr, float tau,
+                                 const BatchTokens& tk, int nch, int chunk, float* part, const int32_t* sel,
+                                 int sel_stride, int sel_rows) {
+  if (dc == 512)
+    return launch_attn<8, SP>(grid, lds, st, qlat, qpe, cache, seq_stride, H, dc, dr, tau, tk, nch, chunk, part, sel,
+                              sel_stride, sel_rows);
+  if (dc == 256)
+    return launch_attn<4, SP>(grid, lds, st, qlat, qpe, cache, seq_stride, H, dc, dr, tau, tk, nch, chunk, part, sel,
+                              sel_stride, sel_rows);
+  return launch_attn<2, SP>(grid, lds, st, qlat, qpe, cache, seq_stride, H, dc, dr, tau, tk, nch, chunk, part, sel,
+                            sel_stride, sel_rows);
+}
+hipError_t bs_attn(const float* qlat, const float* qpe, const uint16_t* cache, int64_t seq_stride, int H, int dc,
+                   int dr, float tau, const BatchTokens& tk, int B, float* part, float* olat, hipStream_t st,
+                   const int32_t* sel, int sel_stride, int sel_rows) {
+  const size_t lds = bs_attn_lds(dc, dr);
   int ctx = 1;
   for (int b = 0; b < B; ++b) ctx = std::max(ctx, tk.pos[b] + 1);
   const int chunk = bs_attn_chunk(ctx), nch = (ctx + chunk - 1) / chunk;
   const dim3 grid(B * ((H + 15) / 16) * nch);
-  if (dc == 512)
-    hipLaunchKernelGGL(bs_attn_kernel<8>, grid, dim3(kAT), lds, st, qlat, qpe, cache, seq_stride, H, dc, dr, tau, tk,
-                       nch, chunk, part);
-  else if (dc == 256)
-    hipLaunchKernelGGL(bs_attn_kernel<4>, grid, dim3(kAT), lds, st, qlat, qpe, cache, seq_stride, H, dc, dr, tau, tk,
-                       nch, chunk, part);
-  else
-    hipLaunchKernelGGL(bs_attn_kernel<2>, grid, dim3(kAT), lds, st, qlat, qpe, cache, seq_stride, H, dc, dr, tau, tk,
-                       nch, chunk, part);
+  const hipError_t e =
+      sel ? launch_attn_nt<true>(grid, lds, st, qlat, qpe, cache, seq_stride, H, dc, dr, tau, tk, nch, chunk, part,
+                                 sel, sel_stride, sel_rows)
+          : launch_attn_nt<false>(grid, lds, st, qlat, qpe, cache, seq_stride, H, dc, dr, tau, tk, nch, chunk, part,
+                                  nullptr, 0, 0);
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL(bs_attn_merge_kernel, dim3(B * H), dim3(kST), 0, st, part, H, dc, nch, chunk, tk, olat);
   return hipGetLastError();
 }

@@ -109,9 +109,20 @@ hipError_t bs_absorb(const float* q, const uint8_t* codes, const uint16_t* scale
                      int dc, int B, const float* rope_tab, const BatchTokens& tk, float* qlat, float* qpe,
                      hipStream_t st);
 constexpr int kAttnChunksMax = 32;  // position chunks per (sequence, head group) of the batched attention
-// part: f32 [B][H][kAttnChunksMax][kv_lora + 2] chunk partials
+// part: f32 [B][H][kAttnChunksMax][kv_lora + 2] chunk partials. With sel set,
+// attention position t of sequence b is cache row sel[b * sel_stride + t]
+// (clamped to [0, sel_rows)) and tk.pos[b] + 1 is the number of positions.
 hipError_t bs_attn(const float* qlat, const float* qpe, const uint16_t* cache, int64_t seq_stride, int H, int dc,
-                   int dr, float tau, const BatchTokens& tk, int B, float* part, float* olat, hipStream_t st);
+                   int dr, float tau, const BatchTokens& tk, int B, float* part, float* olat, hipStream_t st,
+                   const int32_t* sel = nullptr, int sel_stride = 0, int sel_rows = 0);
+// Sparse attention's indexer scores and top-k selection (dsa.hip).
+// scores[s] = sum_j w[j] * max(0, q[j] . k[s]); q f32 [HI][dI], w f32 [HI],
+// k bf16 [n][dI]; HI a multiple of 16 up to 64, dI a multiple of 32 up to 256.
+hipError_t dsa_scores(const float* q, const float* w, const uint16_t* k, int n, int HI, int dI, float* scores,
+                      hipStream_t st);
+// idx: the min(kk, n) positions of largest score (ties: lower position) in
+// ascending order.
+hipError_t dsa_topk(const float* scores, int n, int kk, int32_t* idx, hipStream_t st);
 hipError_t bs_uv(const float* olat, const uint8_t* codes, const uint16_t* scales, int nkb, int H, int dv, int dc,
                  int B, float* o, hipStream_t st);
 hipError_t bs_bf16_rows(const float* h, const uint16_t* M, int N, int K, int B, float* out, hipStream_t st);

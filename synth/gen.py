@@ -197,3 +197,35 @@ def batch_routing(cfg: C.ModelConfig, B: int, seed: int = 0, tag: int = 0):
     idx = np.stack([rng.choice(cfg.n_experts, cfg.top_k, replace=False) for _ in range(B)]).astype(np.int32)
     w = rng.uniform(0.5, 1.5, size=(B, cfg.top_k))
     return idx, (w / w.sum(axis=1, keepdims=True)).astype(np.float32)
+
+
+def dsa_inputs(n: int, HI: int, dI: int, H: int, dc: int, dr: int, seed: int = 0, tag: int = 0):
+    """Inputs of one sparse-attention decode token over a cache of n rows:
+    indexer queries q [HI, dI] and head weights w [HI] (N(0,1) and
+    N(0, 1/HI), float32), indexer keys [n, dI] and latent cache rows
+    [n, dc + dr] (N(0,1), bf16 bit patterns as int16), absorbed latent
+    queries [H, dc] and rotary queries [H, dr] (N(0,1), float32)."""
+    rng = np.random.default_rng(np.random.SeedSequence([seed, 6, tag, n, HI, dI, H, dc, dr]))
+    f32 = np.float32
+    q = rng.standard_normal((HI, dI)).astype(f32)
+    w = (rng.standard_normal(HI) / np.sqrt(HI)).astype(f32)
+    keys = torch.from_numpy(rng.standard_normal((n, dI)).astype(f32)).to(torch.bfloat16).view(torch.int16)
+    rows = torch.from_numpy(rng.standard_normal((n, dc + dr)).astype(f32)).to(torch.bfloat16).view(torch.int16)
+    q_lat = rng.standard_normal((H, dc)).astype(f32)
+    q_pe = rng.standard_normal((H, dr)).astype(f32)
+    return q, w, keys, rows, q_lat, q_pe
+
+
+def dsa_scores_sample(n: int, kind: str, seed: int = 0) -> np.ndarray:
+    """Index scores [n] float32 for the selection: 'normal' N(0,1); 'ties'
+    values on a grid of 8 levels (many equal scores); 'zeros' +0.0 and -0.0
+    mixed with negatives; 'equal' one value everywhere."""
+    rng = np.random.default_rng(np.random.SeedSequence([seed, 7, n, len(kind)]))
+    if kind == "normal":
+        return rng.standard_normal(n).astype(np.float32)
+    if kind == "ties":
+        return (rng.integers(-4, 4, n) * 0.5).astype(np.float32)
+    if kind == "zeros":
+        v = rng.choice(np.array([0.0, -0.0, -1.0, -2.5], np.float32), n)
+        return v.astype(np.float32)
+    return np.full(n, 0.75, np.float32)

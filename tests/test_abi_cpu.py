@@ -22,7 +22,7 @@ def lib():
 
 def header_functions():
     text = open(os.path.join(ROOT, "include", "pdm.h")).read()
-    return sorted(set(re.findall(r"^\s*(?:int|const char\*)\s+(pdm_\w+)\s*\(", text, re.M)))
+    return sorted(set(re.findall(r"^\s*(?:int|uint64_t|const char\*)\s+(pdm_\w+)\s*\(", text, re.M)))
 
 
 def test_exports_every_declared_symbol(lib):
@@ -80,6 +80,33 @@ def test_invalid_shapes_rejected(lib):
     s = L.Sizes()
     assert lib.pdm_query_sizes(C.byref(d), 0, 256, C.byref(s)) == L.ERR_ARG
     assert lib.pdm_query_sizes(None, 64, 256, C.byref(s)) == L.ERR_ARG
+
+
+def test_dsa_argument_checks(lib):
+    """The sparse-attention calls reject bad arguments before any HIP call."""
+    from persistent_decode_megakernel_amd import _lib as L
+    fake = C.c_void_p(1 << 20)      # never dereferenced: every call below fails its checks first
+    odd = C.c_void_p((1 << 20) + 4)
+    assert lib.pdm_dsa_index_scores(None, fake, fake, 10, 64, 128, fake, None) == L.ERR_ARG
+    assert lib.pdm_dsa_index_scores(fake, fake, fake, -1, 64, 128, fake, None) == L.ERR_ARG
+    for HI, dI in ((8, 128), (80, 128), (24, 128), (64, 16), (64, 100), (64, 288)):
+        assert lib.pdm_dsa_index_scores(fake, fake, fake, 10, HI, dI, fake, None) == L.ERR_CONFIG, (HI, dI)
+    assert lib.pdm_dsa_index_scores(fake, fake, odd, 10, 64, 128, fake, None) == L.ERR_ALIGN
+    assert lib.pdm_dsa_topk(None, 10, 5, fake, None) == L.ERR_ARG
+    assert lib.pdm_dsa_topk(fake, 10, -1, fake, None) == L.ERR_ARG
+    assert lib.pdm_dsa_attention_work_bytes(128, 512) == 128 * 32 * 514 * 4
+    assert lib.pdm_dsa_attention_work_bytes(0, 512) == 0
+
+    def att(cache=fake, n_sel=4, H=16, dc=512, dr=64, wb=1 << 30, sel=fake, rows=10):
+        return lib.pdm_dsa_attention(fake, fake, cache, rows, sel, n_sel, H, dc, dr, 0.1, fake, wb, fake, None)
+    assert att(sel=None) == L.ERR_ARG
+    assert att(n_sel=0) == L.ERR_ARG
+    assert att(H=0) == L.ERR_ARG
+    assert att(rows=0) == L.ERR_ARG
+    for dc, dr in ((384, 64), (512, 65), (512, 160), (64, 32)):
+        assert att(dc=dc, dr=dr) == L.ERR_CONFIG, (dc, dr)
+    assert att(cache=odd) == L.ERR_ALIGN
+    assert att(wb=lib.pdm_dsa_attention_work_bytes(16, 512) - 1) == L.ERR_SIZE
 
 
 def _validate_dag(plan, cfg):
