@@ -17,14 +17,17 @@ and MoE layers are timed per layer-step, alternating over two weight copies so
 that no step is served from the MALL, and the weight products of one MoE layer
 are timed at batch 1, 2, 4 and 8 (pdm_batch_gemm / pdm_batch_ffn, several
 sequences sharing every weight byte), as are whole batched decode steps of the
-stack (pdm_batch_decode_step). Prints one JSON line with tok/s/user, TPOT, the
+stack (pdm_batch_decode_step). Sparse (DSA) attention of one DeepSeek-V3
+layer (indexer, top-2048, attention over the chosen rows) is timed at cache
+lengths 9216, 32768 and 131072. Prints one JSON line with tok/s/user, TPOT, the
 HBM roofline fraction, a stage trace, the single-layer timings, the batch
-points and the CPU oracle baseline.
+points, the sparse-attention points and the CPU oracle baseline.
 """
 from __future__ import annotations
 
 import argparse
 import hashlib
+import math
 import json
 import os
 import subprocess
@@ -442,6 +445,90 @@ def layer_steps(name: str, copies: int, steps: int, warm: int = 2):
             "timing": "one launch per step (launch gap included), steps alternate over the weight copies"}
 
 
+def dsa_points(contexts, k: int = 2048, reps: int = 20):
+    """Sparse (DSA) attention of one DeepSeek-V3-shaped layer at batch 1: the
+    indexer (64 heads x 128 over bf16 keys), the top-k of the scores and MLA
+    attention of 128 heads over the k chosen rows of the latent cache, timed
+    with HIP events on the launch stream, each call and the three together,
+    rotating over enough copies of the caches (>= 1 GB) that the last-level
+    cache holds none of them. Dense attention over all n rows through the same
+    attention kernel is timed beside it. Algorithmic bytes: the indexer reads
+    n keys, the top-k n scores, the attention k cache rows (1152 B each)."""
+    import torch
+    from persistent_decode_megakernel_amd import dsa as G
+    from synth import gen
+    HI, dI, H, dc, dr = 64, 128, 128, 512, 64
+    tau = 1.0 / math.sqrt(192.0)
+    stream = torch.cuda.current_stream()
+    pts = []
+    for n in contexts:
+        per = n * (dI + dc + dr) * 2
+        copies = max(2, -(-(1 << 30) // per))
+        q, w, keys, rows, q_lat, q_pe = gen.dsa_inputs(n, HI, dI, H, dc, dr, seed=SEED, tag=5)
+        qd, wd = torch.from_numpy(q).cuda(), torch.from_numpy(w).cuda()
+        ql, qp = torch.from_numpy(q_lat).cuda(), torch.from_numpy(q_pe).cuda()
+        kc = [keys.cuda() for _ in range(copies)]
+        cc = [rows.cuda() for _ in range(copies)]
+        sc = torch.empty(n, device="cuda")
+        sel = torch.empty(min(k, n), dtype=torch.int32, device="cuda")
+        allpos = torch.arange(n, dtype=torch.int32, device="cuda")
+        work = torch.empty(G.work_bytes(H, dc) // 4, device="cuda")
+        o = torch.empty(H, dc, device="cuda")
+        it = [0]
+
+        def nxt():
+            it[0] = (it[0] + 1) % copies
+            return it[0]
+
+        def f_idx():
+            G.index_scores(qd, wd, kc[nxt()], out=sc)
+
+        def f_topk():
+            G.topk(sc, k, out=sel)
+
+        def f_att():
+            G.attention(ql, qp, cc[nxt()], sel, tau, work=work, out=o)
+
+        def f_all():
+            c = nxt()
+            G.index_scores(qd, wd, kc[c], out=sc)
+            G.topk(sc, k, out=sel)
+            G.attention(ql, qp, cc[c], sel, tau, work=work, out=o)
+
+        def f_dense():
+            G.attention(ql, qp, cc[nxt()], allpos, tau, work=work, out=o)
+
+        def timed(fn):
+            for _ in range(3):
+                fn()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(reps):
+                fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / 1e3 / reps
+
+        f_idx()
+        t_i, t_k, t_a, t_all, t_d = timed(f_idx), timed(f_topk), timed(f_att), timed(f_all), timed(f_dense)
+        b_i, b_k, b_a = n * dI * 2, n * 4 + min(k, n) * 4, min(k, n) * (dc + dr) * 2
+        pt = {"context": n, "k": min(k, n), "cache_copies": copies,
+              "indexer_us": round(t_i * 1e6, 2), "indexer_GBps": round(b_i / t_i / 1e9, 1),
+              "topk_us": round(t_k * 1e6, 2),
+              "attention_us": round(t_a * 1e6, 2), "attention_GBps": round(b_a / t_a / 1e9, 1),
+              "sparse_layer_us": round(t_all * 1e6, 2),
+              "dense_attention_us": round(t_d * 1e6, 2),
+              "algorithmic_bytes": {"indexer": b_i, "topk": b_k, "attention": b_a}}
+        log(f"dsa n={n} k={pt['k']}: indexer {pt['indexer_us']} us, top-k {pt['topk_us']} us, attention "
+            f"{pt['attention_us']} us, all three {pt['sparse_layer_us']} us; dense attention over all n "
+            f"{pt['dense_attention_us']} us")
+        pts.append(pt)
+        del kc, cc
+        torch.cuda.empty_cache()
+    return pts
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -463,6 +550,8 @@ def main():
     ap.add_argument("--layer-steps", type=int, default=32)
     ap.add_argument("--batch", default="1,2,4,8",
                     help="batch sizes of the batched weight-product leg on the stack's engine ('' for none)")
+    ap.add_argument("--dsa", default="9216,32768,131072",
+                    help="cache lengths of the sparse-attention leg, top-2048 ('' for none)")
     ap.add_argument("--resident-only", action="store_true",
                     help="time only resident launches (no single-step launches): for profiler runs")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -575,6 +664,8 @@ def main():
         out["batch_points"] = batch
     if bsteps is not None:
         out["batch_step_points"] = bsteps
+    if args.dsa:
+        out["dsa_points"] = dsa_points([int(n) for n in args.dsa.split(",") if n])
     if args.layers:
         del eng
         torch.cuda.empty_cache()
