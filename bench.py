@@ -471,6 +471,7 @@ def dsa_points(contexts, k: int = 2048, reps: int = 20):
         cc = [rows.cuda() for _ in range(copies)]
         sc = torch.empty(n, device="cuda")
         sel = torch.empty(min(k, n), dtype=torch.int32, device="cuda")
+        tw = torch.empty(G.topk_work_bytes(n) // 4, dtype=torch.int32, device="cuda")
         allpos = torch.arange(n, dtype=torch.int32, device="cuda")
         work = torch.empty(G.work_bytes(H, dc) // 4, device="cuda")
         o = torch.empty(H, dc, device="cuda")
@@ -484,7 +485,7 @@ def dsa_points(contexts, k: int = 2048, reps: int = 20):
             G.index_scores(qd, wd, kc[nxt()], out=sc)
 
         def f_topk():
-            G.topk(sc, k, out=sel)
+            G.topk(sc, k, out=sel, work=tw)
 
         def f_att():
             G.attention(ql, qp, cc[nxt()], sel, tau, work=work, out=o)
@@ -492,7 +493,7 @@ def dsa_points(contexts, k: int = 2048, reps: int = 20):
         def f_all():
             c = nxt()
             G.index_scores(qd, wd, kc[c], out=sc)
-            G.topk(sc, k, out=sel)
+            G.topk(sc, k, out=sel, work=tw)
             G.attention(ql, qp, cc[c], sel, tau, work=work, out=o)
 
         def f_dense():

@@ -519,12 +519,20 @@ int pdm_batch_decode_step(pdm_engine* e, int32_t B, const int32_t* tokens, const
 int pdm_dsa_index_scores(const float* q_dev, const float* w_dev, const uint16_t* k_dev, int32_t n, int32_t HI,
                          int32_t dI, float* scores_dev, pdm_stream_t stream);
 
+/* Bytes of work_dev that pdm_dsa_topk needs for n scores. */
+uint64_t pdm_dsa_topk_work_bytes(int32_t n);
+
 /* Top-k selection: idx_dev (int32 [min(k, n)]) receives the positions of
  * the min(k, n) largest of scores_dev[0 .. n), equal scores going to the
  * lower position (-0.0 equals +0.0), in ascending position order. Scores
- * must not be NaN (their order is then unspecified). One workgroup.
- * Errors: PDM_ERR_ARG (null pointer, n < 0, k < 0), PDM_ERR_LAUNCH. */
-int pdm_dsa_topk(const float* scores_dev, int32_t n, int32_t k, int32_t* idx_dev, pdm_stream_t stream);
+ * must not be NaN (their order is then unspecified). Up to 16384 scores one
+ * workgroup selects; longer lists are spread over workgroups of 2048
+ * scores, with global histograms and counts in work_dev (device scratch of
+ * pdm_dsa_topk_work_bytes(n) bytes; calls sharing it must not overlap).
+ * Errors: PDM_ERR_ARG (null pointer, n < 0, k < 0), PDM_ERR_SIZE (work_bytes
+ * too small), PDM_ERR_LAUNCH. */
+int pdm_dsa_topk(const float* scores_dev, int32_t n, int32_t k, int32_t* idx_dev, void* work_dev,
+                 uint64_t work_bytes, pdm_stream_t stream);
 
 /* Bytes of work_dev that pdm_dsa_attention needs for H heads and a latent
  * width kv_lora (0 for a bad shape). */

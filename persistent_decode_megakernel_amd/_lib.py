@@ -107,7 +107,8 @@ _SIGS = {
     "pdm_batch_decode_step": (C.c_int, [_P, C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
                                         C.c_void_p, C.c_void_p, C.c_void_p]),
     "pdm_dsa_index_scores": (C.c_int, [_P, _P, _P, C.c_int32, C.c_int32, C.c_int32, _P, _P]),
-    "pdm_dsa_topk": (C.c_int, [_P, C.c_int32, C.c_int32, _P, _P]),
+    "pdm_dsa_topk_work_bytes": (C.c_uint64, [C.c_int32]),
+    "pdm_dsa_topk": (C.c_int, [_P, C.c_int32, C.c_int32, _P, _P, C.c_uint64, _P]),
     "pdm_dsa_attention_work_bytes": (C.c_uint64, [C.c_int32, C.c_int32]),
     "pdm_dsa_attention": (C.c_int, [_P, _P, _P, C.c_int32, _P, C.c_int32, C.c_int32, C.c_int32, C.c_int32,
                                     C.c_float, _P, C.c_uint64, _P, _P]),

@@ -1052,9 +1052,15 @@ int pdm_dsa_index_scores(const float* q_dev, const float* w_dev, const uint16_t*
   return dsa_scores(q_dev, w_dev, k_dev, n, HI, dI, scores_dev, (hipStream_t)stream) == hipSuccess ? PDM_OK : PDM_ERR_LAUNCH;
 }
 
-int pdm_dsa_topk(const float* scores_dev, int32_t n, int32_t k, int32_t* idx_dev, pdm_stream_t stream) {
-  if (!scores_dev || !idx_dev || n < 0 || k < 0) return PDM_ERR_ARG;
-  return dsa_topk(scores_dev, n, k, idx_dev, (hipStream_t)stream) == hipSuccess ? PDM_OK : PDM_ERR_LAUNCH;
+uint64_t pdm_dsa_topk_work_bytes(int32_t n) { return dsa_topk_work_bytes(n); }
+
+int pdm_dsa_topk(const float* scores_dev, int32_t n, int32_t k, int32_t* idx_dev, void* work_dev,
+                 uint64_t work_bytes, pdm_stream_t stream) {
+  if (!scores_dev || !idx_dev || !work_dev || n < 0 || k < 0) return PDM_ERR_ARG;
+  if (work_bytes < dsa_topk_work_bytes(n)) return PDM_ERR_SIZE;
+  return dsa_topk(scores_dev, n, k, idx_dev, static_cast<uint32_t*>(work_dev), (hipStream_t)stream) == hipSuccess
+             ? PDM_OK
+             : PDM_ERR_LAUNCH;
 }
 
 uint64_t pdm_dsa_attention_work_bytes(int32_t H, int32_t kv_lora) {

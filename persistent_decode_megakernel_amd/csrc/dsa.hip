@@ -225,6 +225,188 @@ __global__ void __launch_bounds__(kTkT) dsa_topk_kernel(const float* scores, int
   }
 }
 
+// ---------------------------------------------------------------- top-k, many workgroups
+// The same radix select spread over ceil(n / kMtTile) workgroups for long
+// lists: per digit one launch, where every workgroup derives the prefix so far
+// from the completed global histograms of the earlier digits (all derive the
+// same), counts its matching keys in LDS and adds the non-zero bins into the
+// global histogram of this digit; then one launch counts each workgroup's keys
+// above and equal to the threshold, and a last one writes each workgroup's
+// chosen positions at its offset (chosen keys of the workgroups before it,
+// equal keys capped by `need` in position order). Work buffer (u32):
+// hist[4][256], then cnt[G][2].
+constexpr int kMtT = 256;
+constexpr int kMtPer = 8;
+constexpr int kMtTile = kMtT * kMtPer;  // positions per workgroup
+
+// wave 0: the digit of hist (256 bins) that holds rank rem (1-based, largest
+// first) and the rank left inside it; result in out[0], out[1]
+__device__ __forceinline__ void mt_pick(const uint32_t* hist, uint32_t rem, uint32_t* out) {
+  const int lane = threadIdx.x & 63;
+  uint32_t c[4], t = 0u;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) { c[q] = hist[255 - 4 * lane - q]; t += c[q]; }
+  uint32_t incl = t;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t v = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += v;
+  }
+  const uint32_t excl = incl - t;
+  if (excl < rem && rem <= incl) {
+    uint32_t cum = excl;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if (cum + c[q] >= rem) {
+        out[0] = 255u - 4u * lane - q;
+        out[1] = rem - cum;
+        break;
+      }
+      cum += c[q];
+    }
+  }
+}
+
+// prefix of the first `digits` digits of the kk-th largest key, and the rank
+// left inside it, from the global histograms (every thread gets them)
+__device__ __forceinline__ void mt_derive(const uint32_t* ghist, int digits, int kk, uint32_t& prefix, uint32_t& rem,
+                                          uint32_t* sh) {
+  prefix = 0u;
+  rem = (uint32_t)kk;
+  for (int d = 0; d < digits; ++d) {
+    if (threadIdx.x < 64) mt_pick(ghist + 256 * d, rem, sh);
+    __syncthreads();
+    prefix |= sh[0] << (24 - 8 * d);
+    rem = sh[1];
+    __syncthreads();
+  }
+}
+
+__device__ __forceinline__ void mt_load(const float* scores, int n, uint32_t* keys) {
+  const int base = blockIdx.x * kMtTile + threadIdx.x;
+#pragma unroll
+  for (int j = 0; j < kMtPer; ++j) keys[j] = order_key(scores[min(base + j * kMtT, n - 1)]);
+}
+
+__global__ void __launch_bounds__(kMtT) dsa_mt_clear_kernel(uint32_t* work, int words) {
+  for (int i = blockIdx.x * kMtT + threadIdx.x; i < words; i += gridDim.x * kMtT) work[i] = 0u;
+}
+
+__global__ void __launch_bounds__(kMtT) dsa_mt_hist_kernel(const float* scores, int n, int kk, int digit,
+                                                          uint32_t* work) {
+  __shared__ uint32_t hist[256];
+  __shared__ uint32_t sh[2];
+  uint32_t keys[kMtPer];
+  mt_load(scores, n, keys);
+  hist[threadIdx.x] = 0u;
+  __syncthreads();
+  uint32_t prefix, rem;
+  mt_derive(work, digit, kk, prefix, rem, sh);
+  const uint32_t mask = digit ? 0xFFFFFFFFu << (32 - 8 * digit) : 0u;
+  const int shift = 24 - 8 * digit;
+#pragma unroll
+  for (int j = 0; j < kMtPer; ++j) {
+    const int i = blockIdx.x * kMtTile + threadIdx.x + j * kMtT;
+    if (i < n && (keys[j] & mask) == prefix) atomicAdd(&hist[(keys[j] >> shift) & 255u], 1u);
+  }
+  __syncthreads();
+  const uint32_t c = hist[threadIdx.x];
+  if (c) atomicAdd(&work[256 * digit + threadIdx.x], c);
+}
+
+__global__ void __launch_bounds__(kMtT) dsa_mt_count_kernel(const float* scores, int n, int kk, uint32_t* work) {
+  __shared__ uint32_t sh[2];
+  __shared__ uint32_t red[2][kMtT / 64];
+  uint32_t keys[kMtPer];
+  mt_load(scores, n, keys);
+  uint32_t T, need;
+  mt_derive(work, 4, kk, T, need, sh);
+  uint32_t gt = 0u, eq = 0u;
+#pragma unroll
+  for (int j = 0; j < kMtPer; ++j) {
+    const int i = blockIdx.x * kMtTile + threadIdx.x + j * kMtT;
+    gt += (i < n && keys[j] > T) ? 1u : 0u;
+    eq += (i < n && keys[j] == T) ? 1u : 0u;
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    gt += __shfl_xor(gt, o, 64);
+    eq += __shfl_xor(eq, o, 64);
+  }
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  if (lane == 0) { red[0][wv] = gt; red[1][wv] = eq; }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t a = 0u, b = 0u;
+    for (int v = 0; v < kMtT / 64; ++v) { a += red[0][v]; b += red[1][v]; }
+    work[1024 + 2 * blockIdx.x] = a;
+    work[1024 + 2 * blockIdx.x + 1] = b;
+  }
+}
+
+__global__ void __launch_bounds__(kMtT) dsa_mt_emit_kernel(const float* scores, int n, int kk, const uint32_t* work,
+                                                          int32_t* idx) {
+  __shared__ uint32_t sh[2];
+  __shared__ uint32_t red[2][kMtT / 64];
+  __shared__ uint32_t wsum[2][kMtT / 64];
+  uint32_t keys[kMtPer];
+  mt_load(scores, n, keys);
+  uint32_t T, need;
+  mt_derive(work, 4, kk, T, need, sh);
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  // keys above / equal to T in the workgroups before this one
+  uint32_t gp = 0u, ep = 0u;
+  for (int h = threadIdx.x; h < (int)blockIdx.x; h += kMtT) {
+    gp += work[1024 + 2 * h];
+    ep += work[1024 + 2 * h + 1];
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    gp += __shfl_xor(gp, o, 64);
+    ep += __shfl_xor(ep, o, 64);
+  }
+  if (lane == 0) { red[0][wv] = gp; red[1][wv] = ep; }
+  __syncthreads();
+  gp = 0u;
+  ep = 0u;
+#pragma unroll
+  for (int v = 0; v < kMtT / 64; ++v) { gp += red[0][v]; ep += red[1][v]; }
+  uint32_t eq_base = ep, out_base = gp + min(ep, need);
+  const uint64_t below = (1ull << lane) - 1ull;
+#pragma unroll
+  for (int j = 0; j < kMtPer; ++j) {
+    const int i = blockIdx.x * kMtTile + threadIdx.x + j * kMtT;
+    const bool valid = i < n;
+    const bool gt = valid && keys[j] > T, eq = valid && keys[j] == T;
+    const uint64_t be = __ballot(eq);
+    if (lane == 0) wsum[0][wv] = (uint32_t)__builtin_popcountll(be);
+    __syncthreads();
+    uint32_t eq_pre = 0u, eq_tot = 0u;
+#pragma unroll
+    for (int v = 0; v < kMtT / 64; ++v) {
+      const uint32_t c = wsum[0][v];
+      eq_pre += v < wv ? c : 0u;
+      eq_tot += c;
+    }
+    const bool take = gt || (eq && eq_base + eq_pre + (uint32_t)__builtin_popcountll(be & below) < need);
+    const uint64_t bt = __ballot(take);
+    if (lane == 0) wsum[1][wv] = (uint32_t)__builtin_popcountll(bt);
+    __syncthreads();
+    uint32_t tk_pre = 0u, tk_tot = 0u;
+#pragma unroll
+    for (int v = 0; v < kMtT / 64; ++v) {
+      const uint32_t c = wsum[1][v];
+      tk_pre += v < wv ? c : 0u;
+      tk_tot += c;
+    }
+    const uint32_t at = out_base + tk_pre + (uint32_t)__builtin_popcountll(bt & below);
+    if (take && at < (uint32_t)kk) idx[at] = i;  // at < kk always; the test keeps a slip inside idx
+    eq_base += eq_tot;
+    out_base += tk_tot;
+    __syncthreads();  // wsum is rewritten by the next tile
+  }
+}
+
 }  // namespace
 
 hipError_t dsa_scores(const float* q, const float* w, const uint16_t* k, int n, int HI, int dI, float* scores,
@@ -243,12 +425,25 @@ hipError_t dsa_scores(const float* q, const float* w, const uint16_t* k, int n, 
   return hipGetLastError();
 }
 
-hipError_t dsa_topk(const float* scores, int n, int kk, int32_t* idx, hipStream_t st) {
+size_t dsa_topk_work_bytes(int n) {
+  const int G = n > 0 ? (n + kMtTile - 1) / kMtTile : 0;
+  return ((size_t)1024 + 2 * (size_t)G) * 4;
+}
+
+hipError_t dsa_topk(const float* scores, int n, int kk, int32_t* idx, uint32_t* work, hipStream_t st) {
   if (n <= 0 || kk <= 0) return hipSuccess;
-  if (n <= kTkReg * kTkT)
+  if (n <= kTkReg * kTkT || kk >= n) {
     hipLaunchKernelGGL(dsa_topk_kernel<true>, dim3(1), dim3(kTkT), 0, st, scores, n, kk, idx);
-  else
-    hipLaunchKernelGGL(dsa_topk_kernel<false>, dim3(1), dim3(kTkT), 0, st, scores, n, kk, idx);
+    return hipGetLastError();
+  }
+  const int G = (n + kMtTile - 1) / kMtTile;
+  const int words = 1024 + 2 * G;
+  hipLaunchKernelGGL(dsa_mt_clear_kernel, dim3(std::min(64, (words + kMtT - 1) / kMtT)), dim3(kMtT), 0, st, work,
+                     words);
+  for (int d = 0; d < 4; ++d)
+    hipLaunchKernelGGL(dsa_mt_hist_kernel, dim3(G), dim3(kMtT), 0, st, scores, n, kk, d, work);
+  hipLaunchKernelGGL(dsa_mt_count_kernel, dim3(G), dim3(kMtT), 0, st, scores, n, kk, work);
+  hipLaunchKernelGGL(dsa_mt_emit_kernel, dim3(G), dim3(kMtT), 0, st, scores, n, kk, work, idx);
   return hipGetLastError();
 }
 

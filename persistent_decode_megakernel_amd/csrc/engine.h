@@ -121,8 +121,10 @@ hipError_t bs_attn(const float* qlat, const float* qpe, const uint16_t* cache, i
 hipError_t dsa_scores(const float* q, const float* w, const uint16_t* k, int n, int HI, int dI, float* scores,
                       hipStream_t st);
 // idx: the min(kk, n) positions of largest score (ties: lower position) in
-// ascending order.
-hipError_t dsa_topk(const float* scores, int n, int kk, int32_t* idx, hipStream_t st);
+// ascending order. work: dsa_topk_work_bytes(n) bytes of device scratch (used
+// only for lists longer than one workgroup's register-resident size).
+size_t dsa_topk_work_bytes(int n);
+hipError_t dsa_topk(const float* scores, int n, int kk, int32_t* idx, uint32_t* work, hipStream_t st);
 hipError_t bs_uv(const float* olat, const uint8_t* codes, const uint16_t* scales, int nkb, int H, int dv, int dc,
                  int B, float* o, hipStream_t st);
 hipError_t bs_bf16_rows(const float* h, const uint16_t* M, int N, int K, int B, float* out, hipStream_t st);

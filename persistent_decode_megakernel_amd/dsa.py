@@ -35,12 +35,19 @@ def index_scores(q: torch.Tensor, w: torch.Tensor, k: torch.Tensor, out: torch.T
     return out
 
 
-def topk(scores: torch.Tensor, k: int, out: torch.Tensor = None) -> torch.Tensor:
+def topk_work_bytes(n: int) -> int:
+    return int(L.load().pdm_dsa_topk_work_bytes(n))
+
+
+def topk(scores: torch.Tensor, k: int, out: torch.Tensor = None, work: torch.Tensor = None) -> torch.Tensor:
     """The min(k, n) positions of largest score, ascending, int32."""
     _dev(scores)
     n = scores.shape[0]
     out = torch.empty(min(k, n), dtype=torch.int32, device=scores.device) if out is None else out
-    L.check("pdm_dsa_topk", L.load().pdm_dsa_topk(_p(scores), n, int(k), _p(out), _stream()))
+    if work is None:
+        work = torch.empty(topk_work_bytes(n) // 4, dtype=torch.int32, device=scores.device)
+    L.check("pdm_dsa_topk", L.load().pdm_dsa_topk(_p(scores), n, int(k), _p(out), _p(work), work.numel() * 4,
+                                                  _stream()))
     return out
 
 

@@ -92,8 +92,12 @@ def test_dsa_argument_checks(lib):
     for HI, dI in ((8, 128), (80, 128), (24, 128), (64, 16), (64, 100), (64, 288)):
         assert lib.pdm_dsa_index_scores(fake, fake, fake, 10, HI, dI, fake, None) == L.ERR_CONFIG, (HI, dI)
     assert lib.pdm_dsa_index_scores(fake, fake, odd, 10, 64, 128, fake, None) == L.ERR_ALIGN
-    assert lib.pdm_dsa_topk(None, 10, 5, fake, None) == L.ERR_ARG
-    assert lib.pdm_dsa_topk(fake, 10, -1, fake, None) == L.ERR_ARG
+    assert lib.pdm_dsa_topk(None, 10, 5, fake, fake, 1 << 20, None) == L.ERR_ARG
+    assert lib.pdm_dsa_topk(fake, 10, -1, fake, fake, 1 << 20, None) == L.ERR_ARG
+    assert lib.pdm_dsa_topk(fake, 10, 5, fake, None, 1 << 20, None) == L.ERR_ARG
+    need = lib.pdm_dsa_topk_work_bytes(131072)
+    assert need == (1024 + 2 * 64) * 4
+    assert lib.pdm_dsa_topk(fake, 131072, 5, fake, fake, need - 1, None) == L.ERR_SIZE
     assert lib.pdm_dsa_attention_work_bytes(128, 512) == 128 * 32 * 514 * 4
     assert lib.pdm_dsa_attention_work_bytes(0, 512) == 0
 

@@ -52,7 +52,9 @@ def test_index_scores(n, HI, dI):
 TOPK_CASES = [(1, 1, "normal"), (5, 2, "normal"), (5, 9, "normal"), (100, 100, "ties"), (2047, 2048, "normal"),
               (2048, 2048, "normal"), (2049, 2048, "normal"), (9216, 2048, "normal"), (9216, 2048, "ties"),
               (9216, 64, "zeros"), (9216, 2048, "zeros"), (9216, 7, "equal"), (16384, 2048, "ties"),
-              (16385, 2048, "normal"), (131072, 2048, "normal"), (131072, 2048, "ties"), (40000, 1, "normal")]
+              (16385, 2048, "normal"), (131072, 2048, "normal"), (131072, 2048, "ties"), (40000, 1, "normal"),
+              (40000, 39999, "ties"), (20000, 20000, "normal"), (100000, 2048, "zeros"), (65537, 4096, "equal"),
+              (300000, 2048, "normal")]
 
 
 @pytest.mark.parametrize("n,k,kind", TOPK_CASES)
@@ -66,11 +68,24 @@ def test_topk_exact(n, k, kind):
 def test_topk_empty_and_arguments():
     s = torch.zeros(4, device=DEV)
     out = torch.full((4,), -7, dtype=torch.int32, device=DEV)
-    assert L.load().pdm_dsa_topk(G._p(s), 0, 5, G._p(out), G._stream()) == L.OK
-    assert L.load().pdm_dsa_topk(G._p(s), 4, 0, G._p(out), G._stream()) == L.OK
+    work = torch.zeros(G.topk_work_bytes(4) // 4, dtype=torch.int32, device=DEV)
+    call = lambda n, k: L.load().pdm_dsa_topk(G._p(s), n, k, G._p(out), G._p(work), work.numel() * 4,  # noqa: E731
+                                              G._stream())
+    assert call(0, 5) == L.OK
+    assert call(4, 0) == L.OK
     torch.cuda.synchronize()
     assert out.cpu().tolist() == [-7] * 4       # nothing written
-    assert L.load().pdm_dsa_topk(G._p(s), -1, 5, G._p(out), G._stream()) == L.ERR_ARG
+    assert call(-1, 5) == L.ERR_ARG
+
+
+def test_topk_reuses_its_work_buffer():
+    """Two long selections in a row through one work buffer (the histograms
+    are cleared by each call), the second shorter."""
+    work = torch.zeros(G.topk_work_bytes(131072) // 4, dtype=torch.int32, device=DEV)
+    for n, k, kind in ((131072, 2048, "normal"), (50000, 300, "ties")):
+        s = gen.dsa_scores_sample(n, kind, seed=7)
+        got = G.topk(torch.from_numpy(s).to(DEV), k, work=work).cpu().numpy().astype(np.int64)
+        np.testing.assert_array_equal(got, D.select_topk(s.astype(np.float64), k))
 
 
 ATT_CASES = [  # H, dc, dr, rows, n_sel
