@@ -103,8 +103,9 @@ __global__ void __launch_bounds__(kScT) dsa_scores_kernel(const float* q, const 
 // to T belong to the result (need). A final pass in position order writes
 // every position with key > T and the first `need` with key == T, at their
 // rank among the chosen (block prefix sums of ballots), so the output is the
-// chosen positions in ascending order. Up to kTkReg * kTkT scores the keys
-// stay in registers between passes; longer lists are read again per pass.
+// chosen positions in ascending order. The keys (up to kTkReg * kTkT, or
+// every position when kk >= n) stay in registers for all passes; longer
+// lists take the many-workgroup select below.
 constexpr int kTkT = 1024;
 constexpr int kTkReg = 16;
 __device__ __forceinline__ uint32_t order_key(float f) {
@@ -114,7 +115,6 @@ __device__ __forceinline__ uint32_t order_key(float f) {
 }
 __device__ __forceinline__ uint32_t popc64(uint64_t m) { return (uint32_t)__builtin_popcountll(m); }
 
-template <bool REG>
 __global__ void __launch_bounds__(kTkT) dsa_topk_kernel(const float* scores, int n, int kk, int32_t* idx) {
   __shared__ uint32_t hist[256];
   __shared__ uint32_t wsum[2][kTkT / 64];
@@ -125,26 +125,17 @@ __global__ void __launch_bounds__(kTkT) dsa_topk_kernel(const float* scores, int
     for (int i = tid; i < n; i += kTkT) idx[i] = i;
     return;
   }
-  uint32_t keys[REG ? kTkReg : 1];
-  if constexpr (REG) {
+  uint32_t keys[kTkReg];
 #pragma unroll
-    for (int j = 0; j < kTkReg; ++j) keys[j] = order_key(scores[min(tid + j * kTkT, n - 1)]);
-  }
+  for (int j = 0; j < kTkReg; ++j) keys[j] = order_key(scores[min(tid + j * kTkT, n - 1)]);
   uint32_t prefix = 0u, mask = 0u, rem = (uint32_t)kk;
   for (int shift = 24; shift >= 0; shift -= 8) {
     if (tid < 256) hist[tid] = 0u;
     __syncthreads();
-    if constexpr (REG) {
 #pragma unroll
-      for (int j = 0; j < kTkReg; ++j) {
-        const int i = tid + j * kTkT;
-        if (i < n && (keys[j] & mask) == prefix) atomicAdd(&hist[(keys[j] >> shift) & 255u], 1u);
-      }
-    } else {
-      for (int i = tid; i < n; i += kTkT) {
-        const uint32_t key = order_key(scores[i]);
-        if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
-      }
+    for (int j = 0; j < kTkReg; ++j) {
+      const int i = tid + j * kTkT;
+      if (i < n && (keys[j] & mask) == prefix) atomicAdd(&hist[(keys[j] >> shift) & 255u], 1u);
     }
     __syncthreads();
     if (wv == 0) {
@@ -211,17 +202,10 @@ __global__ void __launch_bounds__(kTkT) dsa_topk_kernel(const float* scores, int
     out_base += tk_tot;
     __syncthreads();  // wsum is rewritten by the next tile
   };
-  if constexpr (REG) {
 #pragma unroll
-    for (int j = 0; j < kTkReg; ++j) {
-      if (j >= nper) break;  // uniform
-      emit(tid + j * kTkT, keys[j]);
-    }
-  } else {
-    for (int j = 0; j < nper; ++j) {
-      const int i = tid + j * kTkT;
-      emit(i, order_key(scores[min(i, n - 1)]));
-    }
+  for (int j = 0; j < kTkReg; ++j) {
+    if (j >= nper) break;  // uniform
+    emit(tid + j * kTkT, keys[j]);
   }
 }
 
@@ -433,7 +417,7 @@ size_t dsa_topk_work_bytes(int n) {
 hipError_t dsa_topk(const float* scores, int n, int kk, int32_t* idx, uint32_t* work, hipStream_t st) {
   if (n <= 0 || kk <= 0) return hipSuccess;
   if (n <= kTkReg * kTkT || kk >= n) {
-    hipLaunchKernelGGL(dsa_topk_kernel<true>, dim3(1), dim3(kTkT), 0, st, scores, n, kk, idx);
+    hipLaunchKernelGGL(dsa_topk_kernel, dim3(1), dim3(kTkT), 0, st, scores, n, kk, idx);
     return hipGetLastError();
   }
   const int G = (n + kMtTile - 1) / kMtTile;
