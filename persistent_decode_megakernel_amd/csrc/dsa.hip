@@ -30,12 +30,15 @@ __device__ __forceinline__ float bf_val(uint16_t b) { return __builtin_bit_cast(
 // S[s][j] = k_s . q_j on the matrix cores: A = 16 cached keys (bf16, exact),
 // B = 16 indexer queries split into bf16 high and residual parts (two
 // products per k-block keep the query's float precision to ~2^-17). A
-// workgroup of 4 waves takes 64 positions, wave w the 16 from 16 w, all
-// head tiles; the queries are staged in LDS once per workgroup. Then
+// workgroup of 4 waves takes groups of 64 positions (wave w the 16 from
+// 16 w, all head tiles), striding over the groups when there are more than
+// kScGrid, so that the queries are staged in LDS once per workgroup; the
+// keys of its next group are loaded while the current one is computed. Then
 // relu, weight and a sum over heads: first over a lane's head tiles, then
 // over the 16 lanes of a row group.
 constexpr int kScT = 256;
-constexpr int kScPos = 64;        // positions per workgroup
+constexpr int kScPos = 64;        // positions per group
+constexpr int kScGrid = 512;      // workgroups at most
 constexpr int kScMaxHT = 4;       // head tiles of 16 (HI <= 64)
 constexpr int kScMaxKB = 8;       // k-blocks of 32 (dI <= 256)
 __global__ void __launch_bounds__(kScT) dsa_scores_kernel(const float* q, const float* w, const uint16_t* k, int n,
@@ -47,13 +50,17 @@ __global__ void __launch_bounds__(kScT) dsa_scores_kernel(const float* q, const 
   float* wl = reinterpret_cast<float*>(ql + HI * qs);
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, lr = lane & 15, lg = lane >> 4;
   const int nht = HI / 16, nkb = dI / 32;
-  // the wave's keys first (one memory round trip, unconditional: rows past n
-  // read row n - 1 and are not stored)
-  const int row = min(blockIdx.x * kScPos + 16 * wv + lr, n - 1);
-  du32x4 a[kScMaxKB];
+  const int ngroups = (n + kScPos - 1) / kScPos;
+  // a group's keys for this lane: one memory round trip, unconditional (rows
+  // past n read row n - 1 and are not stored)
+  du32x4 a[kScMaxKB], an[kScMaxKB];
+  auto load_keys = [&](int g, du32x4* dst) {
+    const int row = min(g * kScPos + 16 * wv + lr, n - 1);
 #pragma unroll
-  for (int kb = 0; kb < kScMaxKB; ++kb)
-    a[kb] = *reinterpret_cast<const du32x4*>(k + (size_t)row * dI + min(kb, nkb - 1) * 32 + lg * 8);
+    for (int kb = 0; kb < kScMaxKB; ++kb)
+      dst[kb] = *reinterpret_cast<const du32x4*>(k + (size_t)row * dI + min(kb, nkb - 1) * 32 + lg * 8);
+  };
+  load_keys(blockIdx.x, a);
   for (int i = threadIdx.x; i < HI * dI; i += kScT) {
     const int j = i / dI, c = i - j * dI;
     const float v = q[i];
@@ -63,36 +70,43 @@ __global__ void __launch_bounds__(kScT) dsa_scores_kernel(const float* q, const 
   }
   if ((int)threadIdx.x < HI) wl[threadIdx.x] = w[threadIdx.x];
   __syncthreads();
-  float tot[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int g = blockIdx.x; g < ngroups; g += gridDim.x) {
+    // unconditional (the last group reloads itself): a branch around the
+    // loads would make the compiler wait for them before computing
+    load_keys(min(g + (int)gridDim.x, ngroups - 1), an);
+    float tot[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int ht = 0; ht < kScMaxHT; ++ht) {
-    if (ht >= nht) break;  // uniform
-    df32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int ht = 0; ht < kScMaxHT; ++ht) {
+      if (ht >= nht) break;  // uniform
+      df32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int kb = 0; kb < kScMaxKB; ++kb) {
-      if (kb >= nkb) break;  // uniform
-      const dbf16x8 av = __builtin_bit_cast(dbf16x8, a[kb]);
-      const dbf16x8 bh = *reinterpret_cast<const dbf16x8*>(qh + (16 * ht + lr) * qs + kb * 32 + lg * 8);
-      const dbf16x8 bl = *reinterpret_cast<const dbf16x8*>(ql + (16 * ht + lr) * qs + kb * 32 + lg * 8);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bh, acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bl, acc, 0, 0, 0);
+      for (int kb = 0; kb < kScMaxKB; ++kb) {
+        if (kb >= nkb) break;  // uniform
+        const dbf16x8 av = __builtin_bit_cast(dbf16x8, a[kb]);
+        const dbf16x8 bh = *reinterpret_cast<const dbf16x8*>(qh + (16 * ht + lr) * qs + kb * 32 + lg * 8);
+        const dbf16x8 bl = *reinterpret_cast<const dbf16x8*>(ql + (16 * ht + lr) * qs + kb * 32 + lg * 8);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bh, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bl, acc, 0, 0, 0);
+      }
+      // acc[r] = S[position 16 wv + 4 lg + r][head 16 ht + lr]
+      const float wj = wl[16 * ht + lr];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) tot[r] += wj * fmaxf(acc[r], 0.f);
     }
-    // acc[r] = S[position 16 wv + 4 lg + r][head 16 ht + lr]
-    const float wj = wl[16 * ht + lr];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) tot[r] += wj * fmaxf(acc[r], 0.f);
-  }
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-#pragma unroll
-    for (int o = 8; o > 0; o >>= 1) tot[r] += __shfl_xor(tot[r], o, 16);
-  }
-  if (lr == 0) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int s = blockIdx.x * kScPos + 16 * wv + 4 * lg + r;
-      if (s < n) scores[s] = tot[r];
+#pragma unroll
+      for (int o = 8; o > 0; o >>= 1) tot[r] += __shfl_xor(tot[r], o, 16);
     }
+    if (lr == 0) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int s = g * kScPos + 16 * wv + 4 * lg + r;
+        if (s < n) scores[s] = tot[r];
+      }
+    }
+#pragma unroll
+    for (int kb = 0; kb < kScMaxKB; ++kb) a[kb] = an[kb];
   }
 }
 
@@ -404,8 +418,8 @@ hipError_t dsa_scores(const float* q, const float* w, const uint16_t* k, int n, 
     if (e != hipSuccess) return e;
     raised = true;
   }
-  hipLaunchKernelGGL(dsa_scores_kernel, dim3((n + kScPos - 1) / kScPos), dim3(kScT), lds, st, q, w, k, n, HI, dI,
-                     scores);
+  hipLaunchKernelGGL(dsa_scores_kernel, dim3(std::min((n + kScPos - 1) / kScPos, kScGrid)), dim3(kScT), lds, st, q,
+                     w, k, n, HI, dI, scores);
   return hipGetLastError();
 }
 

@@ -37,7 +37,7 @@ def _score_bound(q, w, K):
 
 
 @pytest.mark.parametrize("n,HI,dI", [(1, 64, 128), (63, 64, 128), (64, 16, 32), (65, 32, 64), (1000, 48, 96),
-                                     (9216, 64, 128), (5000, 64, 256)])
+                                     (9216, 64, 128), (5000, 64, 256), (70001, 64, 128), (33000, 16, 256)])
 def test_index_scores(n, HI, dI):
     print(f"index scores n={n} HI={HI} dI={dI}", flush=True)
     q, w, keys, _, _, _ = gen.dsa_inputs(n, HI, dI, 16, 128, 32, tag=1)
