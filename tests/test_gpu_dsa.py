@@ -168,3 +168,27 @@ def test_dsa_path_deepseek_v3_shape():
     assert ref_sc[rest].max() <= ref_sc[sel].min() + 2 * bound.max()
     C = _f64(cache)
     np.testing.assert_allclose(o, D.sparse_mla(q_lat, q_pe, C[:, :dc], C[:, dc:], sel, tau), rtol=0, atol=1e-4)
+
+
+def test_dsa_path_long_context():
+    """The whole path over a 131072-row cache: the indexer's workgroups stride
+    over several position groups and the selection runs over many
+    workgroups; the attention is checked on the chosen rows."""
+    n, HI, dI, H, dc, dr, k = 131072, 64, 128, 128, 512, 64, 2048
+    print(f"dsa path n={n}", flush=True)
+    q, w, keys, cache, q_lat, q_pe = gen.dsa_inputs(n, HI, dI, H, dc, dr, tag=5)
+    tau = 1.0 / np.sqrt(192.0)
+    sc = G.index_scores(torch.from_numpy(q).to(DEV), torch.from_numpy(w).to(DEV), keys.to(DEV))
+    sel = G.topk(sc, k)
+    o = G.attention(torch.from_numpy(q_lat).to(DEV), torch.from_numpy(q_pe).to(DEV), cache.to(DEV), sel, tau)
+    sc, sel, o = sc.cpu().numpy(), sel.cpu().numpy().astype(np.int64), o.cpu().numpy()
+    K = _f64(keys)
+    ref_sc = D.index_scores(q, w, K)
+    bound = _score_bound(q, w, K)
+    assert np.all(np.abs(sc - ref_sc) <= bound)
+    np.testing.assert_array_equal(sel, D.select_topk(sc.astype(np.float64), k))
+    rest = np.setdiff1d(np.arange(n), sel)
+    assert ref_sc[rest].max() <= ref_sc[sel].min() + 2 * bound.max()
+    rows = _f64(cache[torch.from_numpy(sel)])
+    np.testing.assert_allclose(o, D.sparse_mla(q_lat, q_pe, rows[:, :dc], rows[:, dc:], np.arange(k), tau),
+                               rtol=0, atol=1e-4)
